@@ -1,0 +1,132 @@
+"""The operations, written as their plain definitions in numpy (oracle side).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Source: "An Efficient Sparse Kernel Generator for O(3)-Equivariant Deep
+Networks" (sciencestack.ai page).  Abstract and Figure 1: the CG tensor
+product contracts the block-sparse tensor with two dense vectors and then
+applies a structured weight; Figure 4: use case A (a batch of independent
+rows) and use case B (graph convolution: node features combined with edge
+features, messages summed into the receiving node).  The abstract also names
+the gradient of the product.  The Sobek page (Abstract) states the same
+convolution without edge-sized intermediates; it does not change the values.
+
+Every function loops over paths and CG nonzeros in the order the paths are
+enumerated and is vectorised over rows/edges and channels only.  All
+arithmetic is float64.  For path p = (i1, i2, l3) with real CG block C_p and
+a nonzero C_p[i, j, k] (the readings are in ``oracle.irreps``/``oracle.cg``):
+
+uvu   out[r, o_q + u(2l3+1) + k] += W[r, w_p + u] * C x[s, a + u(2l1+1) + i] * y[r, b + j]
+uvw   out[r, o_q + w(2l3+1) + k] += sum_u W_p[u, w] * C x[s, a + u(2l1+1) + i] * y[r, b + j]
+
+For the batched product s = r; for the convolution the row r is an edge e in
+receiver-CSR order, s = col[e] its sender and the sum runs over the edges of
+each receiver n.  No extra path normalisation factor is applied.
+"""
+import numpy as np
+
+from .cg import nonzeros
+from .irreps import Problem, offsets
+
+
+def _layout(prob: Problem):
+    return offsets(prob.ins), offsets(prob.sh), offsets(prob.out)
+
+
+def _path_terms(prob: Problem):
+    """Yield (path, a, b, o, mul_in, mul_out, nz) with block offsets."""
+    oa, ob, oo = _layout(prob)
+    for p in prob.paths:
+        yield (p, oa[p.i1], ob[p.i2], oo[p.slot], prob.ins[p.i1].mul, prob.out[p.slot].mul,
+               nonzeros(p.l1, p.l2, p.l3))
+
+
+def edge_messages(prob: Problem, xs: np.ndarray, y: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Per-row tensor product: xs[r] is the input row used by row r (uvu only)."""
+    assert prob.mode == "uvu"
+    rows = xs.shape[0]
+    msg = np.zeros((rows, prob.d_out))
+    for p, a, b, o, mul, _, nz in _path_terms(prob):
+        n1, n3 = 2 * p.l1 + 1, 2 * p.l3 + 1
+        xb = xs[:, a:a + mul * n1].reshape(rows, mul, n1)
+        wb = w[:, p.w_off:p.w_off + mul]                        # (rows, mul)
+        ob = msg[:, o:o + mul * n3].reshape(rows, mul, n3)      # view into msg
+        for i, j, k, c in nz:
+            ob[:, :, k] += wb * (c * xb[:, :, i] * y[:, b + j][:, None])
+    return msg
+
+
+def tp_forward(prob: Problem, x, y, w):
+    """Batched CG tensor product, use case A.  uvu: w (B, P*mul); uvw: w shared, flat."""
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    w = np.asarray(w, np.float64)
+    if prob.mode == "uvu":
+        return edge_messages(prob, x, y, w)
+    rows = x.shape[0]
+    out = np.zeros((rows, prob.d_out))
+    for p, a, b, o, mul_in, mul_out, nz in _path_terms(prob):
+        n1, n3 = 2 * p.l1 + 1, 2 * p.l3 + 1
+        xb = x[:, a:a + mul_in * n1].reshape(rows, mul_in, n1)
+        wp = w[p.w_off:p.w_off + mul_in * mul_out].reshape(mul_in, mul_out)
+        t = np.zeros((rows, mul_in, n3))
+        for i, j, k, c in nz:
+            t[:, :, k] += c * xb[:, :, i] * y[:, b + j][:, None]
+        ob = out[:, o:o + mul_out * n3].reshape(rows, mul_out, n3)
+        ob += np.einsum("ruk,uw->rwk", t, wp)
+    return out
+
+
+def receivers_of(row_ptr: np.ndarray) -> np.ndarray:
+    """Receiver index of every edge of a receiver-sorted CSR."""
+    row_ptr = np.asarray(row_ptr, np.int64)
+    return np.repeat(np.arange(len(row_ptr) - 1), np.diff(row_ptr))
+
+
+def conv_forward(prob: Problem, row_ptr, col, x, y, w):
+    """Fused convolution, use case B: out[n] = sum over edges e of n of TP(x[col[e]], y[e], W[e])."""
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    w = np.asarray(w, np.float64)
+    col = np.asarray(col, np.int64)
+    n_nodes = len(row_ptr) - 1
+    msg = edge_messages(prob, x[col], y, w)
+    out = np.zeros((n_nodes, prob.d_out))
+    np.add.at(out, receivers_of(row_ptr), msg)
+    return out
+
+
+def conv_backward(prob: Problem, row_ptr, col, x, y, w, g):
+    """Gradients of sum(g * conv_forward(...)) with respect to x, y and W.
+
+    For each path and nonzero (i, j, k, c), with n the receiver and s the
+    sender of edge e:
+      dW[e, w_p + u]   += c * x[s,u,i] * y[e,j] * g[n,u,k]
+      dY[e, b + j]     += c * W[e,p,u] * x[s,u,i] * g[n,u,k]   (summed over u)
+      dx[s, a + u..+i] += c * W[e,p,u] * y[e,j] * g[n,u,k]     (summed over e)
+    """
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    w = np.asarray(w, np.float64)
+    g = np.asarray(g, np.float64)
+    col = np.asarray(col, np.int64)
+    dst = receivers_of(row_ptr)
+    n_edges = len(col)
+    xs, gs = x[col], g[dst]
+    dxs = np.zeros_like(xs)
+    dy = np.zeros_like(y)
+    dw = np.zeros_like(w)
+    for p, a, b, o, mul, _, nz in _path_terms(prob):
+        n1, n3 = 2 * p.l1 + 1, 2 * p.l3 + 1
+        xb = xs[:, a:a + mul * n1].reshape(n_edges, mul, n1)
+        dxb = dxs[:, a:a + mul * n1].reshape(n_edges, mul, n1)
+        gb = gs[:, o:o + mul * n3].reshape(n_edges, mul, n3)
+        wb = w[:, p.w_off:p.w_off + mul]
+        for i, j, k, c in nz:
+            yj = y[:, b + j][:, None]
+            dw[:, p.w_off:p.w_off + mul] += c * xb[:, :, i] * yj * gb[:, :, k]
+            dy[:, b + j] += np.sum(c * wb * xb[:, :, i] * gb[:, :, k], axis=1)
+            dxb[:, :, i] += c * wb * yj * gb[:, :, k]
+    dx = np.zeros_like(x)
+    np.add.at(dx, col, dxs)
+    return dx, dy, dw

@@ -1,0 +1,259 @@
+"""Pins of the oracle's operations (oracle/ref.py, oracle/cpu_loops.c).
+
+G8  equivariance under proper and improper rotations (forward and backward)
+G9  brute force: a dense einsum with the fully assembled coupling tensor
+G10 trilinear identity and finite differences for the backward
+plus: the explicit C loops agree with the numpy definitions, and planted
+mistakes in the oracle (a transposed index, a dropped term, a wrong sign)
+are caught by these pins.
+"""
+import numpy as np
+import pytest
+
+from oracle import irreps, loops, ref, wigner
+from oracle import sh as osh
+from oracle.cg import real_cg_block
+
+IN_MIXED = "2x0e+3x1o+2x2e+1x3o"
+
+
+def problem(in_irreps=IN_MIXED, lmax_sh=3, lmax_out=3, mode="uvu", out=None):
+    out = out or irreps.per_path_out_irreps(in_irreps, lmax_sh, lmax_out)
+    return irreps.build_problem(in_irreps, irreps.sh_irreps(lmax_sh), out, mode)
+
+
+def small_graph(rng, n_nodes, n_edges):
+    recv = rng.integers(0, n_nodes, n_edges)
+    send = rng.integers(0, n_nodes, n_edges)
+    order = np.argsort(recv, kind="stable")
+    row_ptr = np.concatenate([[0], np.cumsum(np.bincount(recv, minlength=n_nodes))])
+    return row_ptr, send[order]
+
+
+def conv_inputs(prob, rng, n_nodes=7, n_edges=30):
+    row_ptr, col = small_graph(rng, n_nodes, n_edges)
+    x = rng.standard_normal((n_nodes, prob.d_in))
+    vec = rng.standard_normal((n_edges, 3))
+    w = rng.standard_normal((n_edges, prob.weight_numel))
+    g = rng.standard_normal((n_nodes, prob.d_out))
+    return row_ptr, col, x, vec, w, g
+
+
+def dense_tensor(prob):
+    """The assembled coupling tensor P[x, y, w, out] (uvu) with P = C on every nonzero."""
+    oa, ob, oo = irreps.offsets(prob.ins), irreps.offsets(prob.sh), irreps.offsets(prob.out)
+    t = np.zeros((prob.d_in, prob.d_sh, prob.weight_numel, prob.d_out))
+    for p in prob.paths:
+        c = real_cg_block(p.l1, p.l2, p.l3)
+        n1, n2, n3 = c.shape
+        mi, mo = prob.ins[p.i1].mul, prob.out[p.slot].mul
+        for u in range(mi):
+            xs = slice(oa[p.i1] + u * n1, oa[p.i1] + (u + 1) * n1)
+            ys = slice(ob[p.i2], ob[p.i2] + n2)
+            if prob.mode == "uvu":
+                os_ = slice(oo[p.slot] + u * n3, oo[p.slot] + (u + 1) * n3)
+                t[xs, ys, p.w_off + u, os_] += c
+            else:
+                for w_ in range(mo):
+                    os_ = slice(oo[p.slot] + w_ * n3, oo[p.slot] + (w_ + 1) * n3)
+                    t[xs, ys, p.w_off + u * mo + w_, os_] += c
+    return t
+
+
+# ------------------------------------------------------------------------------ G9 brute force
+
+@pytest.mark.parametrize("in_irreps,lmax_sh,lmax_out", [
+    ("4x0e+4x1o", 2, 2), ("3x0e+3x1o+3x2e", 2, 2), (IN_MIXED, 3, 3), ("2x1o+1x2e", 1, 3)])
+def test_uvu_forward_and_backward_brute_force(in_irreps, lmax_sh, lmax_out):
+    prob = problem(in_irreps, lmax_sh, lmax_out)
+    rng = np.random.default_rng(0)
+    row_ptr, col, x, vec, w, g = conv_inputs(prob, rng)
+    y = rng.standard_normal((len(col), prob.d_sh))  # any y: the operation is bilinear in x, y
+    t = dense_tensor(prob)
+    dst = ref.receivers_of(row_ptr)
+    msg = np.einsum("abvo,ea,eb,ev->eo", t, x[col], y, w)
+    want = np.zeros((len(row_ptr) - 1, prob.d_out))
+    np.add.at(want, dst, msg)
+    assert np.allclose(ref.conv_forward(prob, row_ptr, col, x, y, w), want, atol=1e-12)
+    dx, dy, dw = ref.conv_backward(prob, row_ptr, col, x, y, w, g)
+    gd = g[dst]
+    want_dxs = np.einsum("abvo,eb,ev,eo->ea", t, y, w, gd)
+    want_dx = np.zeros_like(x)
+    np.add.at(want_dx, col, want_dxs)
+    assert np.allclose(dx, want_dx, atol=1e-12)
+    assert np.allclose(dy, np.einsum("abvo,ea,ev,eo->eb", t, x[col], w, gd), atol=1e-12)
+    assert np.allclose(dw, np.einsum("abvo,ea,eb,eo->ev", t, x[col], y, gd), atol=1e-12)
+
+
+def test_uvw_forward_brute_force():
+    ins = "3x0e+2x1o+2x2e"
+    prob = irreps.build_problem(ins, irreps.sh_irreps(2), "2x0e+3x1o+2x2e+1x1e+2x2o", "uvw")
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((11, prob.d_in))
+    y = rng.standard_normal((11, prob.d_sh))
+    w = rng.standard_normal(prob.weight_numel)
+    t = dense_tensor(prob)
+    want = np.einsum("abvo,ra,rb,v->ro", t, x, y, w)
+    assert np.allclose(ref.tp_forward(prob, x, y, w), want, atol=1e-12)
+
+
+def test_tp_uvu_is_conv_on_identity_graph():
+    prob = problem("4x0e+4x1o", 2, 2)
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((9, prob.d_in))
+    y = rng.standard_normal((9, prob.d_sh))
+    w = rng.standard_normal((9, prob.weight_numel))
+    ident = np.arange(10)
+    assert np.allclose(ref.tp_forward(prob, x, y, w),
+                       ref.conv_forward(prob, ident, np.arange(9), x, y, w), atol=1e-14)
+
+
+# ------------------------------------------------------------------------------ G8 equivariance
+
+def _rotate_case(prob, improper, seed=4):
+    rng = np.random.default_rng(seed)
+    row_ptr, col, x, vec, w, g = conv_inputs(prob, rng)
+    rot = wigner.random_rotation(rng)
+    lin = -rot if improper else rot
+    d_in = wigner.irreps_d(prob.ins, rot, improper)
+    d_sh = wigner.irreps_d(prob.sh, rot, improper)
+    d_out = wigner.irreps_d(prob.out, rot, improper)
+    y = osh.real_sh_all(prob.sh[-1].l, vec)
+    y_rot = osh.real_sh_all(prob.sh[-1].l, vec @ lin.T)
+    assert np.allclose(y_rot, y @ d_sh.T, atol=1e-11)
+    return row_ptr, col, x, y, w, g, d_in, d_sh, d_out, y_rot
+
+
+@pytest.mark.parametrize("improper", [False, True])
+def test_conv_equivariance(improper):
+    prob = problem()
+    row_ptr, col, x, y, w, g, d_in, d_sh, d_out, y_rot = _rotate_case(prob, improper)
+    out = ref.conv_forward(prob, row_ptr, col, x, y, w)
+    out_rot = ref.conv_forward(prob, row_ptr, col, x @ d_in.T, y_rot, w)
+    assert np.abs(out_rot - out @ d_out.T).max() < 1e-10 * max(1, np.abs(out).max())
+    dx, dy, dw = ref.conv_backward(prob, row_ptr, col, x, y, w, g)
+    dx2, dy2, dw2 = ref.conv_backward(prob, row_ptr, col, x @ d_in.T, y_rot, w, g @ d_out.T)
+    assert np.allclose(dx2, dx @ d_in.T, atol=1e-10)
+    assert np.allclose(dy2, dy @ d_sh.T, atol=1e-10)
+    assert np.allclose(dw2, dw, atol=1e-10)
+
+
+@pytest.mark.parametrize("improper", [False, True])
+def test_uvw_equivariance(improper):
+    ins = "2x0e+2x1o+2x2e+1x3o"
+    out_irreps = "3x0e+2x1o+2x2e+1x3o+2x1e+1x2o"
+    prob = irreps.build_problem(ins, irreps.sh_irreps(3), out_irreps, "uvw")
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((6, prob.d_in))
+    vec = rng.standard_normal((6, 3))
+    w = rng.standard_normal(prob.weight_numel)
+    rot = wigner.random_rotation(rng)
+    lin = -rot if improper else rot
+    d_in = wigner.irreps_d(prob.ins, rot, improper)
+    d_out = wigner.irreps_d(prob.out, rot, improper)
+    out = ref.tp_forward(prob, x, osh.real_sh_all(3, vec), w)
+    out_rot = ref.tp_forward(prob, x @ d_in.T, osh.real_sh_all(3, vec @ lin.T), w)
+    assert np.allclose(out_rot, out @ d_out.T, atol=1e-10)
+
+
+# ------------------------------------------------------------------------------ G10 backward
+
+def test_trilinear_identity():
+    prob = problem()
+    rng = np.random.default_rng(5)
+    row_ptr, col, x, vec, w, g = conv_inputs(prob, rng, 9, 40)
+    y = rng.standard_normal((len(col), prob.d_sh))
+    out = ref.conv_forward(prob, row_ptr, col, x, y, w)
+    dx, dy, dw = ref.conv_backward(prob, row_ptr, col, x, y, w, g)
+    s = np.sum(g * out)
+    for a, b in ((dx, x), (dy, y), (dw, w)):
+        assert abs(np.sum(a * b) - s) <= 1e-12 * max(1.0, abs(s)) * 10
+
+
+def test_finite_differences():
+    prob = problem("2x0e+2x1o+1x2e", 2, 2)
+    rng = np.random.default_rng(6)
+    row_ptr, col, x, vec, w, g = conv_inputs(prob, rng, 5, 14)
+    y = rng.standard_normal((len(col), prob.d_sh))
+    dx, dy, dw = ref.conv_backward(prob, row_ptr, col, x, y, w, g)
+
+    def loss(x_, y_, w_):
+        return np.sum(g * ref.conv_forward(prob, row_ptr, col, x_, y_, w_))
+
+    h = 1e-6
+    for arr, grad, which in ((x, dx, 0), (y, dy, 1), (w, dw, 2)):
+        for _ in range(6):
+            idx = tuple(rng.integers(0, s) for s in arr.shape)
+            ap, am = arr.copy(), arr.copy()
+            ap[idx] += h
+            am[idx] -= h
+            args_p = [x, y, w]
+            args_m = [x, y, w]
+            args_p[which], args_m[which] = ap, am
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - grad[idx]) < 1e-6 * max(1.0, abs(grad[idx]))
+
+
+# ------------------------------------------------------------------------------ C loops == numpy
+
+@pytest.mark.parametrize("in_f32", [False, True])
+def test_cpu_loops_match_numpy(in_f32):
+    prob = problem()
+    tab = loops.Tables(prob)
+    rng = np.random.default_rng(8)
+    row_ptr, col, x, vec, w, g = conv_inputs(prob, rng, 12, 70)
+    y = rng.standard_normal((len(col), prob.d_sh))
+    dt = np.float32 if in_f32 else np.float64
+    x, y, w, g = (a.astype(dt) for a in (x, y, w, g))
+    n = len(row_ptr) - 1
+    out = ref.conv_forward(prob, row_ptr, col, x, y, w)
+    dx, dy, dw = ref.conv_backward(prob, row_ptr, col, x, y, w, g)
+    assert np.allclose(loops.uvu_forward(tab, row_ptr, col, x, y, w), out, atol=1e-12)
+    rows = np.array([5, 0, 11, 3])
+    assert np.allclose(loops.conv_forward_rows(tab, row_ptr, col, x, y, w, rows), out[rows], atol=1e-12)
+    eidx, dy_s, dw_s = loops.conv_backward_edge_rows(tab, row_ptr, col, x, y, w, g, np.arange(n))
+    assert np.array_equal(eidx, np.arange(len(col)))
+    assert np.allclose(dy_s, dy, atol=1e-12) and np.allclose(dw_s, dw, atol=1e-12)
+    senders = np.array([2, 7, 0, 11])
+    assert np.allclose(loops.conv_backward_x_rows(tab, row_ptr, col, y, w, g, senders), dx[senders],
+                       atol=1e-12)
+
+
+def test_cpu_loops_uvw_match_numpy():
+    ins = "3x0e+2x1o+2x2e"
+    prob = irreps.build_problem(ins, irreps.sh_irreps(2), "2x0e+3x1o+2x2e+1x1e+2x2o", "uvw")
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((13, prob.d_in))
+    y = rng.standard_normal((13, prob.d_sh))
+    w = rng.standard_normal(prob.weight_numel)
+    assert np.allclose(loops.uvw_forward(loops.Tables(prob), x, y, w), ref.tp_forward(prob, x, y, w),
+                       atol=1e-12)
+
+
+# ------------------------------------------------------------------------------ planted mistakes
+
+def _mutated(kind):
+    real = ref.nonzeros
+
+    def nz(l1, l2, l3):
+        z = list(real(l1, l2, l3))
+        if (l1, l2, l3) != (1, 1, 2):
+            return z
+        if kind == "transpose":   # swap the roles of the input and output components
+            return [(k % (2 * l1 + 1), j, i % (2 * l3 + 1), c) for i, j, k, c in z]
+        if kind == "drop":
+            return z[1:]
+        if kind == "sign":
+            return [(i, j, k, -c if n == 0 else c) for n, (i, j, k, c) in enumerate(z)]
+        raise ValueError(kind)
+    return nz
+
+
+@pytest.mark.parametrize("kind", ["transpose", "drop", "sign"])
+def test_planted_mistake_is_caught_by_equivariance(monkeypatch, kind):
+    prob = problem("2x0e+2x1o", 2, 2)
+    row_ptr, col, x, y, w, g, d_in, d_sh, d_out, y_rot = _rotate_case(prob, False, seed=12)
+    monkeypatch.setattr(ref, "nonzeros", _mutated(kind))
+    out = ref.conv_forward(prob, row_ptr, col, x, y, w)
+    out_rot = ref.conv_forward(prob, row_ptr, col, x @ d_in.T, y_rot, w)
+    assert np.abs(out_rot - out @ d_out.T).max() > 1e-3
