@@ -1,0 +1,210 @@
+"""Benchmark of the fused CGTP convolution on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c5] [--no-cpu]
+
+One step = one pass of the hot path over the synthetic graph: the fused
+convolution forward (cgtp_conv_forward) followed by the fused backward
+(cgtp_conv_backward: grad_x, grad_y, grad_w).  Per-graph set-up (plan and
+hipRTC, spherical harmonics of the edge vectors, the sender transpose) runs
+before the timed region.  All inputs are resident in HBM when timing starts.
+
+Prints one JSON line with the throughput in edges/s (forward + backward per
+edge), the roofline of the dominant kernel (HIP events on the launch stream)
+and the CPU oracle's rate on the host cores (``cpu_baseline``).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "edges/sec fused CGTP conv fwd (+bwd) and % of HBM / FP32 roofline"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c5"])
+    ap.add_argument("--dtype", default="f32", choices=["f32", "f64"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(plan, N, E, es):
+    """Compulsory HBM bytes per launch: every input read once, every output written once."""
+    fwd = (N + 1) * 4 + E * 4 + es * (N * plan.d_x + E * plan.d_sh + E * plan.weight_numel + N * plan.d_out)
+    bwd = ((N + 1) * 4 + 2 * E * 4
+           + es * (N * plan.d_x + E * plan.d_sh + E * plan.weight_numel + N * plan.d_out)
+           + es * (N * plan.d_x + E * plan.d_sh + E * plan.weight_numel))
+    return fwd, bwd
+
+
+def make_inputs(spec, dtype, seed, device):
+    import torch
+    from clebsch_gordan_tensor_cgtp_amd import binding as cg
+    from clebsch_gordan_tensor_cgtp_amd import synth
+    st = synth.streams(seed)
+    row_ptr, col = synth.conv_graph(spec, seed)
+    N, E = len(row_ptr) - 1, len(col)
+    plan = cg.plan_for(spec, dtype)
+    npdt = np.float32 if dtype == "f32" else np.float64
+    fan_in = E / N
+
+    def dev(a):
+        if isinstance(a, np.ndarray):
+            return torch.from_numpy(a).to(device)
+        return a
+
+    d = {
+        "row_ptr": dev(row_ptr), "col": dev(col),
+        "x": dev(synth.normal(st["x"], (N, plan.d_x), dtype=npdt, device=device)),
+        "vec": dev(synth.normal(st["vec"], (E, 3), dtype=npdt, device=device)),
+        "w": dev(synth.normal(st["w"], (E, plan.weight_numel), 1.0 / np.sqrt(fan_in), dtype=npdt, device=device)),
+        "g": dev(synth.normal(st["sample"], (N, plan.d_out), dtype=npdt, device=device)),
+    }
+    return plan, d, (row_ptr, col)
+
+
+def cpu_baseline(spec, seed, host_graph, max_seconds=30.0):
+    """The oracle's explicit loops (fp64, OpenMP) on the host cores, on a bounded sample of
+    the same graph: forward and edge gradients of a contiguous receiver slice holding ~5% of
+    the edges, and grad_x of a contiguous sender range with about as many edges.  Values are
+    random (timing only); the rate is edges of the slice per second of the three passes."""
+    from oracle import irreps as oirreps
+    from oracle import loops
+    row_ptr, col = (np.asarray(a, dtype=np.int64) for a in host_graph)
+    N, E = len(row_ptr) - 1, len(col)
+    out_ir = oirreps.per_path_out_irreps(spec.in_irreps, spec.lmax_sh, spec.lmax_out)
+    prob = oirreps.build_problem(spec.in_irreps, oirreps.sh_irreps(spec.lmax_sh), out_ir, "uvu")
+    tab = loops.Tables(prob)
+    threads = loops.default_threads()
+    rng = np.random.default_rng(seed + 99)
+    target = max(2_000, E // 20)
+    start = int(rng.integers(0, max(1, N // 2)))
+    stop = min(max(int(np.searchsorted(row_ptr, row_ptr[start] + target)), start + 1), N)
+    e0, e1 = int(row_ptr[start]), int(row_ptr[stop])
+    n_e = e1 - e0
+    sub_ptr = row_ptr[start:stop + 1] - e0
+    uniq, inv = np.unique(col[e0:e1], return_inverse=True)
+    x_c = rng.standard_normal((len(uniq), prob.d_in))
+    y_s = rng.standard_normal((n_e, prob.d_sh))
+    w_s = rng.standard_normal((n_e, prob.weight_numel))
+    g_s = rng.standard_normal((stop - start, prob.d_out))
+    # senders [s0, s1) with about n_e outgoing edges, and their edges in sender order
+    order = np.argsort(col, kind="stable")
+    t_ptr = np.concatenate([[0], np.cumsum(np.bincount(col, minlength=N))])
+    s0 = int(rng.integers(0, max(1, N // 2)))
+    s1 = min(max(int(np.searchsorted(t_ptr, t_ptr[s0] + n_e)), s0 + 1), N)
+    t_edges = order[t_ptr[s0]:t_ptr[s1]]
+    dst = np.searchsorted(row_ptr, t_edges, side="right") - 1
+    guniq, ginv = np.unique(dst, return_inverse=True)
+    sptr = t_ptr[s0:s1 + 1] - t_ptr[s0]
+    g_c = rng.standard_normal((len(guniq), prob.d_out))
+    y_t = rng.standard_normal((len(t_edges), prob.d_sh))
+    w_t = rng.standard_normal((len(t_edges), prob.weight_numel))
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        loops.uvu_forward(tab, sub_ptr, inv, x_c, y_s, w_s, threads)
+        loops.uvu_backward_edges(tab, sub_ptr, inv, x_c, y_s, w_s, g_s, threads)
+        loops.uvu_backward_x(tab, sptr, ginv, y_t, w_t, g_c, threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or el * (reps + 1) / reps > max_seconds:
+            break
+    sec = (time.perf_counter() - t0) / reps
+    return {"value": n_e / sec, "unit": "edges/s", "cores": threads, "kind": "oracle",
+            "sample": f"receivers [{start},{stop}) = {n_e} of {E} edges: forward + grad_y/grad_w; "
+                      f"grad_x of senders [{s0},{s1}) = {len(t_edges)} edges; fp64 explicit loops, "
+                      f"mean of {reps} rep(s)"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    from clebsch_gordan_tensor_cgtp_amd import binding as cg
+    from clebsch_gordan_tensor_cgtp_amd import synth
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+    spec = synth.WORKLOADS[a.workload]
+    plan, d, host_graph = make_inputs(spec, a.dtype, a.seed, device)
+    N, E = d["row_ptr"].shape[0] - 1, d["col"].shape[0]
+    es = 4 if a.dtype == "f32" else 8
+    y = cg.spherical_harmonics(spec.lmax_sh, d["vec"])
+    tr = cg.graph_transpose(d["row_ptr"], d["col"])
+    out = torch.empty((N, plan.d_out), dtype=plan.torch_dtype, device=device)
+    gx = torch.empty_like(d["x"])
+    gy = torch.empty_like(y)
+    gw = torch.empty_like(d["w"])
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        cg.conv_forward(plan, d["row_ptr"], d["col"], d["x"], y, d["w"], out=out)
+        if ev is not None:
+            ev[1].record()
+        cg.conv_backward(plan, d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"], gx, gy, gw)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(a.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_per_step = wall * 1e3 / a.steps
+    fwd_b, bwd_b = algorithmic_bytes(plan, N, E, es)
+    dom = ("cgtp_conv_bwd", bwd_ms, bwd_b) if bwd_ms >= fwd_ms else ("cgtp_conv_fwd", fwd_ms, fwd_b)
+    achieved = dom[2] / (dom[1] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": E / (ms_per_step * 1e-3),
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": a.dtype,
+        "data": "synthetic",
+        "config": {"workload": spec.name, "N": N, "E": E, "in_irreps": spec.in_irreps,
+                   "sh_lmax": spec.lmax_sh, "paths": plan.num_paths, "d_out": plan.d_out,
+                   "step": "conv_forward + conv_backward (grad_x, grad_y, grad_w)",
+                   "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+                   "fwd_edges_per_s": E / (fwd_ms * 1e-3), "bwd_edges_per_s": E / (bwd_ms * 1e-3)},
+        "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": dom[2], "avg_launch_ms": dom[1],
+                     "other": {"kernel": "cgtp_conv_fwd" if dom[0] == "cgtp_conv_bwd" else "cgtp_conv_bwd",
+                               "achieved": (fwd_b / (fwd_ms * 1e-3) if dom[0] == "cgtp_conv_bwd"
+                                            else bwd_b / (bwd_ms * 1e-3)) / 1e9}},
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(spec, a.seed, host_graph)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,281 @@
+"""Thin ctypes binding of libcgtp (include/cgtp.h): same names, argument marshalling only.
+
+Every step runs in the library's HIP kernels.  Torch supplies device memory
+and the stream (``torch.cuda.current_stream().cuda_stream``); when an output
+tensor is not given, it is allocated here with ``torch.empty`` -- the only
+allocation on the path, and one the library itself never makes.  If
+``libcgtp.so`` is missing the first call raises: there is no fallback.
+"""
+import ctypes
+import os
+from functools import lru_cache
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcgtp.so")
+
+CGTP_UVU, CGTP_UVW = 0, 1
+CGTP_F32, CGTP_F64 = 0, 1
+STATUS = {0: "CGTP_OK", 1: "CGTP_ERR_INVALID_ARG", 2: "CGTP_ERR_IRREPS", 3: "CGTP_ERR_UNSUPPORTED",
+          4: "CGTP_ERR_COMPILE", 5: "CGTP_ERR_HIP", 6: "CGTP_ERR_INTERNAL"}
+
+EXPORTS = ("cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info_get", "cgtp_plan_path",
+           "cgtp_plan_path_coefficients", "cgtp_plan_source", "cgtp_tp_forward", "cgtp_conv_forward",
+           "cgtp_graph_transpose", "cgtp_conv_backward", "cgtp_spherical_harmonics", "cgtp_last_error")
+
+
+class CgtpError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("d_x", ctypes.c_int32), ("d_sh", ctypes.c_int32), ("d_out", ctypes.c_int32),
+                ("num_paths", ctypes.c_int32), ("weight_numel", ctypes.c_int64),
+                ("nnz_total", ctypes.c_int32), ("mode", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("fwd_tasks", ctypes.c_int32)]
+
+
+class PathInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("i1", "i2", "slot", "l1", "l2", "l3", "p3", "x_off", "y_off",
+                                              "out_off", "mul_in", "mul_out")] + \
+               [("w_off", ctypes.c_int64), ("nnz", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libcgtp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run `python -m clebsch_gordan_tensor_cgtp_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        L.cgtp_last_error.restype = ctypes.c_char_p
+        L.cgtp_plan_source.restype = ctypes.c_char_p
+        L.cgtp_plan_source.argtypes = [vp]
+        L.cgtp_plan_create.argtypes = [ctypes.c_char_p] * 3 + [ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp)]
+        L.cgtp_plan_destroy.argtypes = [vp]
+        L.cgtp_plan_info_get.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+        L.cgtp_plan_path.argtypes = [vp, i32, ctypes.POINTER(PathInfo)]
+        L.cgtp_plan_path_coefficients.argtypes = [vp, i32, i32, vp, vp, ctypes.POINTER(i32)]
+        L.cgtp_tp_forward.argtypes = [vp, i64, vp, vp, vp, ctypes.c_int, vp, vp]
+        L.cgtp_conv_forward.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+        L.cgtp_graph_transpose.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp]
+        L.cgtp_conv_backward.argtypes = [vp, i64, i64] + [vp] * 13
+        L.cgtp_spherical_harmonics.argtypes = [i32, ctypes.c_int, i64, vp, vp, vp]
+        for name in EXPORTS:
+            if name not in ("cgtp_last_error", "cgtp_plan_source"):
+                getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().cgtp_last_error().decode()
+
+
+def _check(status):
+    if status != 0:
+        raise CgtpError(status, last_error())
+
+
+# ------------------------------------------------------------------------------------ plans
+
+class Plan:
+    def __init__(self, in_irreps, sh_irreps, out_irreps, mode="uvu", dtype="f32"):
+        self._h = None
+        self.mode, self.dtype = mode, dtype
+        self.irreps = (in_irreps, sh_irreps, out_irreps)
+        h = ctypes.c_void_p()
+        _check(lib().cgtp_plan_create(in_irreps.encode(), sh_irreps.encode(), out_irreps.encode(),
+                                      {"uvu": CGTP_UVU, "uvw": CGTP_UVW}[mode],
+                                      {"f32": CGTP_F32, "f64": CGTP_F64}[dtype], ctypes.byref(h)))
+        self._h = h
+        info = PlanInfo()
+        _check(lib().cgtp_plan_info_get(h, ctypes.byref(info)))
+        self.info = info
+        self.d_x, self.d_sh, self.d_out = info.d_x, info.d_sh, info.d_out
+        self.num_paths, self.weight_numel, self.nnz_total = info.num_paths, info.weight_numel, info.nnz_total
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def torch_dtype(self):
+        import torch
+        return torch.float32 if self.dtype == "f32" else torch.float64
+
+    def path(self, p: int) -> dict:
+        pi = PathInfo()
+        _check(lib().cgtp_plan_path(self._h, p, ctypes.byref(pi)))
+        return {f: getattr(pi, f) for f, _ in PathInfo._fields_}
+
+    def coefficients(self, p: int):
+        """(ijk int32 [nnz,3], values float64 [nnz]) of path p, as the planner computed them."""
+        import numpy as np
+        n = ctypes.c_int32()
+        _check(lib().cgtp_plan_path_coefficients(self._h, p, 0, None, None, ctypes.byref(n)))
+        ijk = np.zeros((n.value, 3), dtype=np.int32)
+        vals = np.zeros(n.value, dtype=np.float64)
+        _check(lib().cgtp_plan_path_coefficients(self._h, p, n.value, ijk.ctypes.data, vals.ctypes.data,
+                                                 ctypes.byref(n)))
+        return ijk, vals
+
+    @property
+    def source(self) -> str:
+        return lib().cgtp_plan_source(self._h).decode()
+
+    def close(self):
+        if self._h is not None and _lib is not None:
+            lib().cgtp_plan_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def plan_create(in_irreps, sh_irreps, out_irreps, mode="uvu", dtype="f32") -> Plan:
+    return Plan(in_irreps, sh_irreps, out_irreps, mode, dtype)
+
+
+def sh_irreps(lmax: int) -> str:
+    return "+".join(f"1x{l}{'e' if l % 2 == 0 else 'o'}" for l in range(lmax + 1))
+
+
+def per_path_out_irreps(in_irreps: str, lmax_sh: int, lmax_out: int) -> str:
+    """One output block per coupling path, in path order (string bookkeeping only)."""
+    terms = []
+    for term in in_irreps.replace(" ", "").split("+"):
+        mul, lp = term.split("x")
+        l1, p1 = int(lp[:-1]), (1 if lp[-1] == "e" else -1)
+        for l2 in range(lmax_sh + 1):
+            p3 = p1 * (1 if l2 % 2 == 0 else -1)
+            for l3 in range(abs(l1 - l2), min(l1 + l2, lmax_out) + 1):
+                terms.append(f"{mul}x{l3}{'e' if p3 == 1 else 'o'}")
+    return "+".join(terms)
+
+
+@lru_cache(maxsize=None)
+def plan_for(spec, dtype="f32") -> Plan:
+    """The plan of a workload from ``synth.WORKLOADS`` (cached per process)."""
+    if hasattr(spec, "n_edges"):
+        out = per_path_out_irreps(spec.in_irreps, spec.lmax_sh, spec.lmax_out)
+        return Plan(spec.in_irreps, sh_irreps(spec.lmax_sh), out, "uvu", dtype)
+    if spec.mode == "uvu":
+        out = per_path_out_irreps(spec.in_irreps, spec.lmax_sh, spec.lmax_sh)
+        return Plan(spec.in_irreps, sh_irreps(spec.lmax_sh), out, "uvu", dtype)
+    return Plan(spec.in_irreps, sh_irreps(spec.lmax_sh), spec.out_irreps, "uvw", dtype)
+
+
+# ------------------------------------------------------------------------------------ calls
+
+def _stream(stream, device=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name, dtype=None, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) torch tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _ptr_or_null(t, name, dtype=None, shape=None):
+    return ctypes.c_void_p(0) if t is None else _dev(t, name, dtype, shape)
+
+
+def tp_forward(plan: Plan, x, y, w, out=None, stream=None):
+    import torch
+    B = x.shape[0]
+    dt = plan.torch_dtype
+    if out is None:
+        out = torch.empty((B, plan.d_out), dtype=dt, device=x.device)
+    shared = 1 if plan.mode == "uvw" else 0
+    wshape = (plan.weight_numel,) if shared else (B, plan.weight_numel)
+    _check(lib().cgtp_tp_forward(plan.handle, B, _dev(x, "x", dt, (B, plan.d_x)), _dev(y, "y", dt, (B, plan.d_sh)),
+                                 _dev(w, "w", dt, wshape), shared, _dev(out, "out", dt, (B, plan.d_out)),
+                                 _stream(stream, x.device)))
+    return out
+
+
+def conv_forward(plan: Plan, row_ptr, col, x, y, w, out=None, stream=None):
+    import torch
+    N, E = row_ptr.shape[0] - 1, col.shape[0]
+    dt = plan.torch_dtype
+    if out is None:
+        out = torch.empty((N, plan.d_out), dtype=dt, device=x.device)
+    _check(lib().cgtp_conv_forward(plan.handle, N, E, _dev(row_ptr, "row_ptr", torch.int32),
+                                   _dev(col, "col", torch.int32), _dev(x, "x", dt, (N, plan.d_x)),
+                                   _dev(y, "y", dt, (E, plan.d_sh)), _dev(w, "w", dt, (E, plan.weight_numel)),
+                                   _dev(out, "out", dt, (N, plan.d_out)), _stream(stream, x.device)))
+    return out
+
+
+def graph_transpose(row_ptr, col, t_row_ptr=None, t_edge=None, t_dst=None, stream=None):
+    import torch
+    N, E = row_ptr.shape[0] - 1, col.shape[0]
+    dev = row_ptr.device
+    t_row_ptr = torch.empty(N + 1, dtype=torch.int32, device=dev) if t_row_ptr is None else t_row_ptr
+    t_edge = torch.empty(E, dtype=torch.int32, device=dev) if t_edge is None else t_edge
+    t_dst = torch.empty(E, dtype=torch.int32, device=dev) if t_dst is None else t_dst
+    _check(lib().cgtp_graph_transpose(N, E, _dev(row_ptr, "row_ptr", torch.int32), _dev(col, "col", torch.int32),
+                                      _dev(t_row_ptr, "t_row_ptr", torch.int32, (N + 1,)),
+                                      _dev(t_edge, "t_edge", torch.int32, (E,)),
+                                      _dev(t_dst, "t_dst", torch.int32, (E,)), _stream(stream, dev)))
+    return t_row_ptr, t_edge, t_dst
+
+
+def conv_backward(plan: Plan, row_ptr, col, transpose, x, y, w, grad_out, grad_x=None, grad_y=None, grad_w=None,
+                  need=(True, True, True), stream=None):
+    """Returns (grad_x, grad_y, grad_w); entries not in ``need`` are None and not computed."""
+    import torch
+    N, E = row_ptr.shape[0] - 1, col.shape[0]
+    dt = plan.torch_dtype
+    dev = x.device
+    t_row_ptr, t_edge, t_dst = transpose
+    if need[0] and grad_x is None:
+        grad_x = torch.empty((N, plan.d_x), dtype=dt, device=dev)
+    if need[1] and grad_y is None:
+        grad_y = torch.empty((E, plan.d_sh), dtype=dt, device=dev)
+    if need[2] and grad_w is None:
+        grad_w = torch.empty((E, plan.weight_numel), dtype=dt, device=dev)
+    gx = grad_x if need[0] else None
+    gy = grad_y if need[1] else None
+    gw = grad_w if need[2] else None
+    _check(lib().cgtp_conv_backward(
+        plan.handle, N, E, _dev(row_ptr, "row_ptr", torch.int32), _dev(col, "col", torch.int32),
+        _dev(t_row_ptr, "t_row_ptr", torch.int32, (N + 1,)), _dev(t_edge, "t_edge", torch.int32, (E,)),
+        _dev(t_dst, "t_dst", torch.int32, (E,)), _dev(x, "x", dt, (N, plan.d_x)), _dev(y, "y", dt, (E, plan.d_sh)),
+        _dev(w, "w", dt, (E, plan.weight_numel)), _dev(grad_out, "grad_out", dt, (N, plan.d_out)),
+        _ptr_or_null(gx, "grad_x", dt, (N, plan.d_x)), _ptr_or_null(gy, "grad_y", dt, (E, plan.d_sh)),
+        _ptr_or_null(gw, "grad_w", dt, (E, plan.weight_numel)), _stream(stream, dev)))
+    return gx, gy, gw
+
+
+def spherical_harmonics(lmax: int, vec, out=None, stream=None):
+    import torch
+    E = vec.shape[0]
+    dt = vec.dtype
+    if dt not in (torch.float32, torch.float64):
+        raise TypeError("vec must be float32 or float64")
+    if out is None:
+        out = torch.empty((E, (lmax + 1) ** 2), dtype=dt, device=vec.device)
+    _check(lib().cgtp_spherical_harmonics(lmax, CGTP_F64 if dt == torch.float64 else CGTP_F32, E,
+                                          _dev(vec, "vec", dt, (E, 3)), _dev(out, "y", dt, (E, (lmax + 1) ** 2)),
+                                          _stream(stream, vec.device)))
+    return out

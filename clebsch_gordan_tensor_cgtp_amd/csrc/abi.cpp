@@ -1,0 +1,342 @@
+// extern "C" entry points of libcgtp (declared and documented in include/cgtp.h).
+// Argument checks happen here, before any HIP call; kernels are launched
+// asynchronously on the caller's stream; nothing is allocated on the device.
+#include <hip/hip_runtime_api.h>
+
+#include <climits>
+#include <cstring>
+#include <memory>
+#include <string>
+
+#include "plan.h"
+#include "static_kernels.h"
+
+struct cgtp_plan {
+    cgtp::Plan p;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+cgtp_status fail(cgtp_status code, const std::string &msg)
+{
+    g_last_error = msg;
+    return code;
+}
+
+template <class F> cgtp_status guarded(F &&f)
+{
+    try {
+        f();
+        return CGTP_OK;
+    } catch (const cgtp::Error &e) {
+        return fail(e.code, e.what());
+    } catch (const std::bad_alloc &) {
+        return fail(CGTP_ERR_INTERNAL, "host out of memory");
+    } catch (const std::exception &e) {
+        return fail(CGTP_ERR_INTERNAL, e.what());
+    } catch (...) {
+        return fail(CGTP_ERR_INTERNAL, "unknown failure");
+    }
+}
+
+void require(bool ok, const std::string &msg)
+{
+    if (!ok) throw cgtp::Error(CGTP_ERR_INVALID_ARG, msg);
+}
+
+void require_ptr(const void *p, const char *name, size_t align)
+{
+    require(p != nullptr, std::string(name) + " is NULL");
+    require(reinterpret_cast<uintptr_t>(p) % align == 0,
+            std::string(name) + " is not aligned to " + std::to_string(align) + " bytes");
+}
+
+// [a, a+na) and [b, b+nb) in bytes must not overlap
+void require_disjoint(const void *a, size_t na, const char *an, const void *b, size_t nb, const char *bn)
+{
+    if (!a || !b || !na || !nb) return;
+    auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    require(x + na <= y || y + nb <= x, std::string(an) + " overlaps " + bn);
+}
+
+void check_hip(hipError_t e, const char *what)
+{
+    if (e != hipSuccess) throw cgtp::Error(CGTP_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+void launch(hipFunction_t f, int64_t waves, void **args, void *stream)
+{
+    const int64_t blocks = (waves + 3) / 4;
+    require(blocks <= INT_MAX, "problem too large for one launch");
+    check_hip(hipModuleLaunchKernel(f, (unsigned)blocks, 1, 1, 256, 1, 1, 0, static_cast<hipStream_t>(stream), args,
+                                    nullptr),
+              "hipModuleLaunchKernel");
+}
+
+size_t elem(const cgtp::Plan &P) { return P.dtype == CGTP_F64 ? 8 : 4; }
+
+void check_graph_sizes(int64_t N, int64_t E)
+{
+    require(N >= 0 && N < INT_MAX, "N must be in [0, 2^31-1)");
+    require(E >= 0 && E < INT_MAX, "E must be in [0, 2^31-1)");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *cgtp_last_error(void) { return g_last_error.c_str(); }
+
+cgtp_status cgtp_plan_create(const char *in_irreps, const char *sh_irreps, const char *out_irreps, cgtp_mode mode,
+                             cgtp_dtype dtype, cgtp_plan **plan_out)
+{
+    return guarded([&] {
+        require(in_irreps && sh_irreps && out_irreps && plan_out, "NULL argument to cgtp_plan_create");
+        *plan_out = nullptr;
+        require(mode == CGTP_UVU || mode == CGTP_UVW, "mode must be CGTP_UVU or CGTP_UVW");
+        require(dtype == CGTP_F32 || dtype == CGTP_F64, "dtype must be CGTP_F32 or CGTP_F64");
+        auto h = std::make_unique<cgtp_plan>();
+        cgtp::Plan &P = h->p;
+        P.mode = mode;
+        P.dtype = dtype;
+        P.ins = cgtp::parse_irreps(in_irreps, "input");
+        P.sh = cgtp::parse_irreps(sh_irreps, "SH");
+        P.out = cgtp::parse_irreps(out_irreps, "output");
+        cgtp::build_paths(P);
+        cgtp::schedule(P);
+        P.source = cgtp::generate_source(P);
+        cgtp::compile_module(P);
+        *plan_out = h.release();
+    });
+}
+
+cgtp_status cgtp_plan_destroy(cgtp_plan *plan)
+{
+    return guarded([&] {
+        if (!plan) return;
+        int prev = 0;
+        bool have_prev = hipGetDevice(&prev) == hipSuccess;
+        for (auto &kv : plan->p.loaded) {
+            if (hipSetDevice(kv.first) == hipSuccess && kv.second.module) hipModuleUnload(kv.second.module);
+        }
+        if (have_prev && !plan->p.loaded.empty()) hipSetDevice(prev);
+        delete plan;
+    });
+}
+
+cgtp_status cgtp_plan_info_get(const cgtp_plan *plan, cgtp_plan_info *info)
+{
+    return guarded([&] {
+        require(plan && info, "NULL argument to cgtp_plan_info_get");
+        const cgtp::Plan &P = plan->p;
+        info->d_x = P.d_x;
+        info->d_sh = P.d_sh;
+        info->d_out = P.d_out;
+        info->num_paths = (int32_t)P.paths.size();
+        info->weight_numel = P.w_numel;
+        info->nnz_total = P.nnz_total;
+        info->mode = P.mode;
+        info->dtype = P.dtype;
+        info->fwd_tasks = P.fwd_tasks;
+    });
+}
+
+cgtp_status cgtp_plan_path(const cgtp_plan *plan, int32_t path, cgtp_path_info *info)
+{
+    return guarded([&] {
+        require(plan && info, "NULL argument to cgtp_plan_path");
+        require(path >= 0 && path < (int32_t)plan->p.paths.size(), "path index out of range");
+        const cgtp::Path &p = plan->p.paths[path];
+        info->i1 = p.i1;
+        info->i2 = p.i2;
+        info->slot = p.slot;
+        info->l1 = p.l1;
+        info->l2 = p.l2;
+        info->l3 = p.l3;
+        info->p3 = p.p3;
+        info->x_off = p.a;
+        info->y_off = p.b;
+        info->out_off = p.o;
+        info->mul_in = p.mul_in;
+        info->mul_out = p.mul_out;
+        info->w_off = p.w_off;
+        info->nnz = (int32_t)p.nz.size();
+    });
+}
+
+cgtp_status cgtp_plan_path_coefficients(const cgtp_plan *plan, int32_t path, int32_t cap, int32_t *ijk,
+                                        double *values, int32_t *nnz)
+{
+    return guarded([&] {
+        require(plan && nnz, "NULL argument to cgtp_plan_path_coefficients");
+        require(path >= 0 && path < (int32_t)plan->p.paths.size(), "path index out of range");
+        require(cap >= 0 && (cap == 0 || (ijk && values)), "cap > 0 needs ijk and values");
+        const auto &nz = plan->p.paths[path].nz;
+        *nnz = (int32_t)nz.size();
+        for (int32_t t = 0; t < cap && t < (int32_t)nz.size(); ++t) {
+            ijk[3 * t] = nz[t].i;
+            ijk[3 * t + 1] = nz[t].j;
+            ijk[3 * t + 2] = nz[t].k;
+            values[t] = nz[t].c;
+        }
+    });
+}
+
+const char *cgtp_plan_source(const cgtp_plan *plan) { return plan ? plan->p.source.c_str() : ""; }
+
+cgtp_status cgtp_tp_forward(const cgtp_plan *plan, int64_t B, const void *x, const void *y, const void *w,
+                            int shared_weights, void *out, void *stream)
+{
+    return guarded([&] {
+        require(plan != nullptr, "plan is NULL");
+        cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
+        require(B >= 0 && B < INT_MAX, "B must be in [0, 2^31-1)");
+        if (P.mode == CGTP_UVU)
+            require(shared_weights == 0, "uvu takes per-row weights: shared_weights must be 0");
+        else
+            require(shared_weights == 1, "uvw takes shared weights: shared_weights must be 1");
+        if (B == 0) return;
+        const size_t es = elem(P);
+        require_ptr(x, "x", es);
+        require_ptr(y, "y", es);
+        require_ptr(w, "w", es);
+        require_ptr(out, "out", es);
+        const size_t nw = (P.mode == CGTP_UVU ? (size_t)B : 1) * P.w_numel * es;
+        require_disjoint(out, B * P.d_out * es, "out", x, B * P.d_x * es, "x");
+        require_disjoint(out, B * P.d_out * es, "out", y, B * P.d_sh * es, "y");
+        require_disjoint(out, B * P.d_out * es, "out", w, nw, "w");
+        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw batched product is not built yet");
+        const auto &L = cgtp::module_for_current_device(P);
+        int es_max = 1;
+        for (const auto &g : P.fwd_groups) es_max = std::max(es_max, g.es);
+        int64_t blocks_of_rows = (B + es_max - 1) / es_max;
+        int64_t waves = blocks_of_rows * P.fwd_tasks;
+        const void *rp = nullptr, *cp = nullptr;
+        long nrows = (long)B, nwaves = (long)waves;
+        void *args[] = {&rp, &cp, &x, &y, &w, &out, &nrows, &nwaves};
+        launch(L.tp_fwd, waves, args, stream);
+    });
+}
+
+cgtp_status cgtp_conv_forward(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr, const int32_t *col,
+                              const void *x, const void *y, const void *w, void *out, void *stream)
+{
+    return guarded([&] {
+        require(plan != nullptr, "plan is NULL");
+        cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
+        check_graph_sizes(N, E);
+        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw convolution is not built yet");
+        if (N == 0) return;
+        const size_t es = elem(P);
+        require_ptr(row_ptr, "row_ptr", 4);
+        require_ptr(out, "out", es);
+        if (E > 0) {
+            require_ptr(col, "col", 4);
+            require_ptr(x, "x", es);
+            require_ptr(y, "y", es);
+            require_ptr(w, "w", es);
+        }
+        const size_t no = N * P.d_out * es;
+        require_disjoint(out, no, "out", x, N * P.d_x * es, "x");
+        require_disjoint(out, no, "out", y, E * P.d_sh * es, "y");
+        require_disjoint(out, no, "out", w, E * P.w_numel * es, "w");
+        require_disjoint(out, no, "out", row_ptr, (N + 1) * 4, "row_ptr");
+        require_disjoint(out, no, "out", col, E * 4, "col");
+        const auto &L = cgtp::module_for_current_device(P);
+        int64_t waves = N * P.fwd_tasks;
+        long nrows = (long)N, nwaves = (long)waves;
+        void *args[] = {&row_ptr, &col, &x, &y, &w, &out, &nrows, &nwaves};
+        launch(L.conv_fwd, waves, args, stream);
+    });
+}
+
+cgtp_status cgtp_graph_transpose(int64_t N, int64_t E, const int32_t *row_ptr, const int32_t *col, int32_t *t_row_ptr,
+                                 int32_t *t_edge, int32_t *t_dst, void *stream)
+{
+    return guarded([&] {
+        check_graph_sizes(N, E);
+        require_ptr(row_ptr, "row_ptr", 4);
+        require_ptr(t_row_ptr, "t_row_ptr", 4);
+        if (E > 0) {
+            require_ptr(col, "col", 4);
+            require_ptr(t_edge, "t_edge", 4);
+            require_ptr(t_dst, "t_dst", 4);
+        }
+        const void *outs[3] = {t_row_ptr, t_edge, t_dst};
+        const size_t outn[3] = {(size_t)(N + 1) * 4, (size_t)E * 4, (size_t)E * 4};
+        const char *names[3] = {"t_row_ptr", "t_edge", "t_dst"};
+        for (int a = 0; a < 3; ++a) {
+            require_disjoint(outs[a], outn[a], names[a], row_ptr, (N + 1) * 4, "row_ptr");
+            require_disjoint(outs[a], outn[a], names[a], col, E * 4, "col");
+            for (int b = a + 1; b < 3; ++b) require_disjoint(outs[a], outn[a], names[a], outs[b], outn[b], names[b]);
+        }
+        check_hip(cgtp::launch_transpose(N, E, row_ptr, col, t_row_ptr, t_edge, t_dst, static_cast<hipStream_t>(stream)),
+                  "transpose launch");
+    });
+}
+
+cgtp_status cgtp_conv_backward(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr, const int32_t *col,
+                               const int32_t *t_row_ptr, const int32_t *t_edge, const int32_t *t_dst, const void *x,
+                               const void *y, const void *w, const void *grad_out, void *grad_x, void *grad_y,
+                               void *grad_w, void *stream)
+{
+    return guarded([&] {
+        require(plan != nullptr, "plan is NULL");
+        cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
+        check_graph_sizes(N, E);
+        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw convolution is not built yet");
+        if (N == 0) return;
+        if (!grad_x && !grad_y && !grad_w) return;
+        const size_t es = elem(P);
+        require_ptr(row_ptr, "row_ptr", 4);
+        require_ptr(t_row_ptr, "t_row_ptr", 4);
+        require_ptr(x, "x", es);
+        if (E > 0) {
+            require_ptr(col, "col", 4);
+            require_ptr(t_edge, "t_edge", 4);
+            require_ptr(t_dst, "t_dst", 4);
+            require_ptr(y, "y", es);
+            require_ptr(w, "w", es);
+            require_ptr(grad_out, "grad_out", es);
+        }
+        if (grad_x) require_ptr(grad_x, "grad_x", es);
+        if (E > 0 && grad_y) require_ptr(grad_y, "grad_y", es);
+        if (E > 0 && grad_w) require_ptr(grad_w, "grad_w", es);
+        const void *ins[] = {x, y, w, grad_out, row_ptr, col, t_row_ptr, t_edge, t_dst};
+        const size_t inn[] = {N * P.d_x * es, E * P.d_sh * es, E * P.w_numel * es, N * P.d_out * es,
+                              (size_t)(N + 1) * 4, (size_t)E * 4, (size_t)(N + 1) * 4, (size_t)E * 4, (size_t)E * 4};
+        const char *inm[] = {"x", "y", "w", "grad_out", "row_ptr", "col", "t_row_ptr", "t_edge", "t_dst"};
+        void *outs[] = {grad_x, grad_y, grad_w};
+        const size_t outn[] = {N * P.d_x * es, E * P.d_sh * es, E * P.w_numel * es};
+        const char *outm[] = {"grad_x", "grad_y", "grad_w"};
+        for (int a = 0; a < 3; ++a) {
+            for (int b = 0; b < 9; ++b) require_disjoint(outs[a], outn[a], outm[a], ins[b], inn[b], inm[b]);
+            for (int b = a + 1; b < 3; ++b) require_disjoint(outs[a], outn[a], outm[a], outs[b], outn[b], outm[b]);
+        }
+        // with E == 0 the kernel still runs: every sender has an empty row and writes zeros to grad_x
+        const auto &L = cgtp::module_for_current_device(P);
+        long nnodes = (long)N;
+        void *args[] = {&t_row_ptr, &t_edge, &t_dst, &x, &y, &w, &grad_out, &grad_x, &grad_y, &grad_w, &nnodes};
+        launch(L.conv_bwd, N, args, stream);
+    });
+}
+
+cgtp_status cgtp_spherical_harmonics(int32_t lmax, cgtp_dtype dtype, int64_t E, const void *vec, void *y, void *stream)
+{
+    return guarded([&] {
+        require(lmax >= 0 && lmax <= 7, "lmax must be in [0, 7]");
+        require(dtype == CGTP_F32 || dtype == CGTP_F64, "dtype must be CGTP_F32 or CGTP_F64");
+        require(E >= 0 && E < INT_MAX, "E must be in [0, 2^31-1)");
+        if (E == 0) return;
+        const size_t es = dtype == CGTP_F64 ? 8 : 4;
+        require_ptr(vec, "vec", es);
+        require_ptr(y, "y", es);
+        require_disjoint(y, E * (lmax + 1) * (lmax + 1) * es, "y", vec, E * 3 * es, "vec");
+        check_hip(cgtp::launch_spherical_harmonics(lmax, dtype == CGTP_F64, E, vec, y, static_cast<hipStream_t>(stream)),
+                  "spherical harmonics launch");
+    });
+}
+
+}  // extern "C"

@@ -1,0 +1,529 @@
+// HIP source generator of libcgtp: one gfx950 module per plan, with the real
+// CG nonzeros written into the code as literal constants.
+//
+// Design sources: sciencestack.ai page (TL;DR, Abstract): JIT generation,
+// register-resident subkernels with long arithmetic streams, fusion of the
+// tensor product with the graph convolution; "The GPU memory optimization
+// with Larger angular momentum" discussion: nonzeros in the instruction
+// stream, no temporary device memory; Sobek page (Abstract): edge-local
+// products consumed directly into bounded receiver-side state; LunaTP page
+// (Abstract): node-centric execution with path-group parallelism.
+//
+// Kernels (all 64-lane wavefronts, 256-thread workgroups of independent waves):
+//  cgtp_conv_fwd  one wave per (receiver, path group, channel tile); lanes are
+//                 channels; when a group has fewer than 64 channels the wave
+//                 works on 64/ct edges at once (edge slots) and sums the slots
+//                 at the end.  Accumulators stay in registers across the
+//                 receiver's CSR row; each output element is written once.
+//  cgtp_conv_bwd  one wave per sender over the sender-sorted transpose; every
+//                 path in one wave.  Per edge it forms B_ij = sum_k C_ijk g_k,
+//                 then dF/dx_i = sum_j B_ij y_j and dF/dy_j = sum_i B_ij x_i,
+//                 writes dW once, reduces dY over the channel lanes, and keeps
+//                 dx in registers.  Channel tiles beyond 64 are walked in
+//                 sequence by the same wave; dY of later tiles is added to the
+//                 value the same lane wrote before, so the sum order is fixed.
+//  cgtp_tp_fwd    batched rows (use case A), same arithmetic as the forward.
+#include <algorithm>
+#include <cstdio>
+#include <map>
+#include <set>
+#include <sstream>
+
+#include "plan.h"
+
+namespace cgtp {
+
+namespace {
+
+struct Out {
+    std::ostringstream s;
+    int ind = 0;
+    template <class... A> Out &operator()(const A &...a)
+    {
+        for (int i = 0; i < ind; ++i) s << "  ";
+        (s << ... << a);
+        s << "\n";
+        return *this;
+    }
+};
+
+std::string lit(double v, bool f64)
+{
+    char buf[64];
+    if (f64)
+        std::snprintf(buf, sizeof buf, "%a", v);
+    else
+        std::snprintf(buf, sizeof buf, "%af", (double)(float)v);  // round to nearest float
+    return buf;
+}
+
+int log2i(int v)
+{
+    int r = 0;
+    while ((1 << r) < v) ++r;
+    return r;
+}
+
+// Input blocks, SH blocks and output slots touched by a set of paths.
+struct Touch {
+    std::set<int> i1, i2, slots;
+};
+Touch touched(const Plan &P, const std::vector<int> &paths)
+{
+    Touch t;
+    for (int i : paths) {
+        t.i1.insert(P.paths[i].i1);
+        t.i2.insert(P.paths[i].i2);
+        t.slots.insert(P.paths[i].slot);
+    }
+    return t;
+}
+
+int n_of(int l) { return 2 * l + 1; }
+
+// (i1, i2) pairs in order of their first path, each with its paths.
+std::vector<std::pair<std::pair<int, int>, std::vector<int>>> pairs_of(const Plan &P, const std::vector<int> &paths)
+{
+    std::vector<std::pair<std::pair<int, int>, std::vector<int>>> out;
+    std::map<std::pair<int, int>, int> at;
+    for (int i : paths) {
+        auto key = std::make_pair(P.paths[i].i1, P.paths[i].i2);
+        auto it = at.find(key);
+        if (it == at.end()) {
+            at[key] = (int)out.size();
+            out.push_back({key, {i}});
+        } else {
+            out[it->second].second.push_back(i);
+        }
+    }
+    return out;
+}
+
+// Is lane channel u possibly >= mul (masked) for a block of multiplicity mul?
+bool needs_mask(int mul, const Group &g) { return mul != g.tiles * g.ct; }
+
+// Emit loads of the sender row (x), the edge row (y) and the weights of edge index `ei`
+// and sender `si` into registers named <pre>x.., <pre>y.., <pre>w..
+void emit_edge_loads(Out &o, const Plan &P, const Group &g, const Touch &t, const std::string &pre,
+                     const std::string &si, const std::string &ei, bool declare)
+{
+    const std::string T = declare ? "T " : "";
+    for (int b : t.i1) {
+        const Irrep &ir = P.ins[b];
+        int off = 0;
+        for (int pi : g.paths)
+            if (P.paths[pi].i1 == b) off = P.paths[pi].a;
+        bool m = needs_mask(ir.mul, g);
+        for (int i = 0; i < n_of(ir.l); ++i) {
+            std::ostringstream addr;
+            addr << "x[(size_t)" << si << " * DX + " << off << " + u * " << n_of(ir.l) << " + " << i << "]";
+            if (m)
+                o(T, pre, "x", b, "_", i, " = (u < ", ir.mul, ") ? ", addr.str(), " : (T)0;");
+            else
+                o(T, pre, "x", b, "_", i, " = ", addr.str(), ";");
+        }
+    }
+    for (int b : t.i2) {
+        int off = 0;
+        for (int pi : g.paths)
+            if (P.paths[pi].i2 == b) off = P.paths[pi].b;
+        for (int j = 0; j < n_of(P.sh[b].l); ++j)
+            o(T, pre, "y", b, "_", j, " = __builtin_nontemporal_load(&y[(size_t)", ei, " * DSH + ", off + j, "]);");
+    }
+    for (int pi : g.paths) {
+        const Path &p = P.paths[pi];
+        std::ostringstream addr;
+        addr << "__builtin_nontemporal_load(&w[(size_t)" << ei << " * WROW + " << p.w_off << " + u])";
+        if (needs_mask(p.mul_in, g))
+            o(T, pre, "w", pi, " = (u < ", p.mul_in, ") ? ", addr.str(), " : (T)0;");
+        else
+            o(T, pre, "w", pi, " = ", addr.str(), ";");
+    }
+}
+
+void emit_copy(Out &o, const Plan &P, const Group &g, const Touch &t, const std::string &dst, const std::string &src)
+{
+    for (int b : t.i1)
+        for (int i = 0; i < n_of(P.ins[b].l); ++i) o(dst, "x", b, "_", i, " = ", src, "x", b, "_", i, ";");
+    for (int b : t.i2)
+        for (int j = 0; j < n_of(P.sh[b].l); ++j) o(dst, "y", b, "_", j, " = ", src, "y", b, "_", j, ";");
+    for (int pi : g.paths) o(dst, "w", pi, " = ", src, "w", pi, ";");
+}
+
+// acc[slot][k] += w_p * sum_{ij} C_ijk x_i y_j for every path of the group.
+void emit_forward_math(Out &o, const Plan &P, const Group &g, bool f64, const std::string &pre)
+{
+    for (auto &pr : pairs_of(P, g.paths)) {
+        int i1 = pr.first.first, i2 = pr.first.second;
+        std::set<std::pair<int, int>> used;
+        for (int pi : pr.second)
+            for (const Nonzero &z : P.paths[pi].nz) used.insert({z.i, z.j});
+        o("{");
+        o.ind++;
+        for (auto &ij : used)
+            o("const T q", ij.first, "_", ij.second, " = ", pre, "x", i1, "_", ij.first, " * ", pre, "y", i2, "_",
+              ij.second, ";");
+        for (int pi : pr.second) {
+            const Path &p = P.paths[pi];
+            std::map<int, std::vector<const Nonzero *>> byk;
+            for (const Nonzero &z : p.nz) byk[z.k].push_back(&z);
+            for (auto &kv : byk) {
+                const auto &v = kv.second;
+                std::ostringstream e;
+                e << lit(v[0]->c, f64) << " * q" << v[0]->i << "_" << v[0]->j;
+                for (size_t n = 1; n < v.size(); ++n) {
+                    std::ostringstream f;
+                    f << "FMA(" << lit(v[n]->c, f64) << ", q" << v[n]->i << "_" << v[n]->j << ", " << e.str() << ")";
+                    e.str(f.str());
+                }
+                o("a", p.slot, "_", kv.first, " = FMA(", pre, "w", pi, ", ", e.str(), ", a", p.slot, "_", kv.first,
+                  ");");
+            }
+        }
+        o.ind--;
+        o("}");
+    }
+}
+
+void emit_preamble(Out &o, const Plan &P)
+{
+    const bool f64 = P.dtype == CGTP_F64;
+    o("// generated by libcgtp for in=", P.ins.size(), " irreps, sh=", P.sh.size(), " irreps, out=", P.out.size(),
+      " irreps, ", P.paths.size(), " paths, ", P.nnz_total, " CG nonzeros");
+    o("typedef ", f64 ? "double" : "float", " T;");
+    o("#define FMA(a, b, c) ", f64 ? "__builtin_fma(a, b, c)" : "__builtin_fmaf(a, b, c)");
+    o("#define DX ", P.d_x);
+    o("#define DSH ", P.d_sh);
+    o("#define DOUT ", P.d_out);
+    o("#define WROW ", P.w_numel, "L");
+    o("typedef unsigned long size_t;");
+    o("");
+}
+
+// Forward body of one group; `n` is the receiver (conv) or -1 (rows mode).
+void emit_fwd_group(Out &o, const Plan &P, int gi, bool rows)
+{
+    const Group &g = P.fwd_groups[gi];
+    const bool f64 = P.dtype == CGTP_F64;
+    Touch t = touched(P, g.paths);
+    o("__device__ __forceinline__ void ", rows ? "tp" : "fwd", "_g", gi,
+      "(long n, int tile, int lane, const int* __restrict__ row_ptr, const int* __restrict__ col, "
+      "const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows)");
+    o("{");
+    o.ind++;
+    o("const int slot = lane >> ", log2i(g.ct), ";");
+    o("const int u = tile * ", g.ct, " + (lane & ", g.ct - 1, ");");
+    if (rows) {
+        int es_max = 1;
+        for (const Group &h : P.fwd_groups) es_max = std::max(es_max, h.es);
+        o("for (int sub = 0; sub < ", es_max / g.es, "; ++sub) {");
+        o.ind++;
+    }
+    for (int q : t.slots)
+        for (int k = 0; k < n_of(P.out[q].l); ++k) o("T a", q, "_", k, " = (T)0;");
+    if (rows) {
+        int es_max = 1;
+        for (const Group &h : P.fwd_groups) es_max = std::max(es_max, h.es);
+        o("const long r = n * ", es_max, " + sub * ", g.es, " + slot;");
+        o("if (r < nrows) {");
+        o.ind++;
+        emit_edge_loads(o, P, g, t, "c", "r", "r", true);
+        emit_forward_math(o, P, g, f64, "c");
+        o.ind--;
+        o("}");
+        o("if (r < nrows) {");
+        o.ind++;
+        o("T* orow = out + (size_t)r * DOUT;");
+    } else {
+        o("const int e0 = row_ptr[n], e1 = row_ptr[n + 1];");
+        o("if (e0 < e1) {");
+        o.ind++;
+        o("int e = e0 + slot;");
+        o("int ec = e < e1 ? e : e1 - 1;");
+        o("int s = col[ec];");
+        emit_edge_loads(o, P, g, t, "c", "s", "ec", true);
+        o("for (; e < e1; e += ", g.es, ") {");
+        o.ind++;
+        o("const int en = (e + ", g.es, " < e1) ? e + ", g.es, " : e1 - 1;");
+        o("const int sn = col[en];");
+        emit_edge_loads(o, P, g, t, "n", "sn", "en", true);
+        emit_forward_math(o, P, g, f64, "c");
+        emit_copy(o, P, g, t, "c", "n");
+        o.ind--;
+        o("}");
+        o.ind--;
+        o("}");
+        // sum the edge slots (fixed butterfly order, identical in every run)
+        for (int m = 32; m >= g.ct; m /= 2)
+            for (int q : t.slots)
+                for (int k = 0; k < n_of(P.out[q].l); ++k) o("a", q, "_", k, " += __shfl_xor(a", q, "_", k, ", ", m, ");");
+        o("if (slot == 0) {");
+        o.ind++;
+        o("T* orow = out + (size_t)n * DOUT;");
+    }
+    for (int q : t.slots) {
+        const Irrep &ir = P.out[q];
+        int off = 0;
+        for (int pi : g.paths)
+            if (P.paths[pi].slot == q) off = P.paths[pi].o;
+        std::string guard = needs_mask(ir.mul, g) ? "if (u < " + std::to_string(ir.mul) + ") " : "";
+        for (int k = 0; k < n_of(ir.l); ++k)
+            o(guard, "orow[", off, " + u * ", n_of(ir.l), " + ", k, "] = a", q, "_", k, ";");
+    }
+    o.ind--;
+    o("}");
+    if (rows) {
+        o.ind--;
+        o("}");  // sub-block loop
+    }
+    o.ind--;
+    o("}");
+    o("");
+}
+
+void emit_fwd_kernel(Out &o, const Plan &P, bool rows)
+{
+    o("extern \"C\" __global__ void __launch_bounds__(256, ", P.fwd_waves_per_eu, ") ", rows ? "cgtp_tp_fwd" : "cgtp_conv_fwd",
+      "(const int* __restrict__ row_ptr, const int* __restrict__ col, const T* __restrict__ x, "
+      "const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows, long nwaves)");
+    o("{");
+    o.ind++;
+    o("const long wave = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const int lane = threadIdx.x & 63;");
+    o("if (wave >= nwaves) return;");
+    o("const int task = (int)(wave % ", P.fwd_tasks, ");");
+    o("const long n = wave / ", P.fwd_tasks, ";");
+    o("switch (task) {");
+    int task = 0;
+    for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi)
+        for (int tile = 0; tile < P.fwd_groups[gi].tiles; ++tile, ++task)
+            o("case ", task, ": ", rows ? "tp" : "fwd", "_g", gi, "(n, ", tile,
+              ", lane, row_ptr, col, x, y, w, out, nrows); break;");
+    o("default: break;");
+    o("}");
+    o.ind--;
+    o("}");
+    o("");
+}
+
+// ------------------------------------------------------------------------------------------
+// Backward, sender pass.
+
+void emit_bwd_kernel(Out &o, const Plan &P)
+{
+    const Group &g = P.bwd_group;
+    const bool f64 = P.dtype == CGTP_F64;
+    Touch t = touched(P, g.paths);
+    o("extern \"C\" __global__ void __launch_bounds__(256, ", P.bwd_waves_per_eu, ") cgtp_conv_bwd(const int* __restrict__ t_row_ptr, "
+      "const int* __restrict__ t_edge, const int* __restrict__ t_dst, const T* __restrict__ x, "
+      "const T* __restrict__ y, const T* __restrict__ w, const T* __restrict__ g, T* __restrict__ dx, "
+      "T* __restrict__ dy, T* __restrict__ dw, long nnodes)");
+    o("{");
+    o.ind++;
+    o("const long s = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const int lane = threadIdx.x & 63;");
+    o("if (s >= nnodes) return;");
+    o("const int slot = lane >> ", log2i(g.ct), ";");
+    o("const int ul = lane & ", g.ct - 1, ";");
+    o("const int t0 = t_row_ptr[s], t1 = t_row_ptr[s + 1];");
+    o("for (int tile = 0; tile < ", g.tiles, "; ++tile) {");
+    o.ind++;
+    o("const int u = tile * ", g.ct, " + ul;");
+    // every input block: x values (zero for blocks without a path) and dx accumulators
+    for (int b = 0; b < (int)P.ins.size(); ++b) {
+        const Irrep &ir = P.ins[b];
+        int off = 0;
+        for (int bb = 0; bb < b; ++bb) off += P.ins[bb].dim();
+        bool used = t.i1.count(b) > 0;
+        for (int i = 0; i < n_of(ir.l); ++i) {
+            if (used) {
+                std::string addr = "x[(size_t)s * DX + " + std::to_string(off) + " + u * " + std::to_string(n_of(ir.l)) +
+                                   " + " + std::to_string(i) + "]";
+                if (needs_mask(ir.mul, g))
+                    o("const T x", b, "_", i, " = (u < ", ir.mul, ") ? ", addr, " : (T)0;");
+                else
+                    o("const T x", b, "_", i, " = ", addr, ";");
+            }
+            o("T d", b, "_", i, " = (T)0;");
+        }
+    }
+    o("for (int t = t0 + slot; t < t1; t += ", g.es, ") {");
+    o.ind++;
+    o("const int e = t_edge[t];");
+    o("const int n = t_dst[t];");
+    for (int b = 0; b < (int)P.sh.size(); ++b) {
+        int off = 0;
+        for (int bb = 0; bb < b; ++bb) off += P.sh[bb].dim();
+        for (int j = 0; j < n_of(P.sh[b].l); ++j) {
+            if (t.i2.count(b))
+                o("const T y", b, "_", j, " = __builtin_nontemporal_load(&y[(size_t)e * DSH + ", off + j, "]);");
+            o("T h", b, "_", j, " = (T)0;");  // dF/dy partial of this lane
+        }
+    }
+    for (int pi : g.paths) {
+        const Path &p = P.paths[pi];
+        std::string wa = "__builtin_nontemporal_load(&w[(size_t)e * WROW + " + std::to_string(p.w_off) + " + u])";
+        if (needs_mask(p.mul_in, g))
+            o("const T w", pi, " = (u < ", p.mul_in, ") ? ", wa, " : (T)0;");
+        else
+            o("const T w", pi, " = ", wa, ";");
+    }
+    // g rows of every slot
+    for (int q : t.slots) {
+        const Irrep &ir = P.out[q];
+        int off = 0;
+        for (int qq = 0; qq < q; ++qq) off += P.out[qq].dim();
+        for (int k = 0; k < n_of(ir.l); ++k) {
+            std::string ga = "g[(size_t)n * DOUT + " + std::to_string(off) + " + u * " + std::to_string(n_of(ir.l)) +
+                             " + " + std::to_string(k) + "]";
+            if (needs_mask(ir.mul, g))
+                o("const T g", q, "_", k, " = (u < ", ir.mul, ") ? ", ga, " : (T)0;");
+            else
+                o("const T g", q, "_", k, " = ", ga, ";");
+        }
+    }
+    for (int pi : g.paths) {
+        const Path &p = P.paths[pi];
+        // B_ij = sum_k C_ijk g_k
+        std::map<std::pair<int, int>, std::vector<const Nonzero *>> byij;
+        for (const Nonzero &z : p.nz) byij[{z.i, z.j}].push_back(&z);
+        o("{");
+        o.ind++;
+        for (auto &kv : byij) {
+            const auto &v = kv.second;
+            std::ostringstream e;
+            e << lit(v[0]->c, f64) << " * g" << p.slot << "_" << v[0]->k;
+            for (size_t n = 1; n < v.size(); ++n) {
+                std::ostringstream f;
+                f << "FMA(" << lit(v[n]->c, f64) << ", g" << p.slot << "_" << v[n]->k << ", " << e.str() << ")";
+                e.str(f.str());
+            }
+            o("const T B", kv.first.first, "_", kv.first.second, " = ", e.str(), ";");
+        }
+        // dF/dx_i = sum_j B_ij y_j ; dF/dy_j = sum_i B_ij x_i
+        std::map<int, std::vector<int>> rows, cols;
+        for (auto &kv : byij) {
+            rows[kv.first.first].push_back(kv.first.second);
+            cols[kv.first.second].push_back(kv.first.first);
+        }
+        for (auto &kv : rows) {
+            std::ostringstream e;
+            e << "B" << kv.first << "_" << kv.second[0] << " * y" << p.i2 << "_" << kv.second[0];
+            for (size_t n = 1; n < kv.second.size(); ++n) {
+                std::ostringstream f;
+                f << "FMA(B" << kv.first << "_" << kv.second[n] << ", y" << p.i2 << "_" << kv.second[n] << ", " << e.str()
+                  << ")";
+                e.str(f.str());
+            }
+            o("const T fx", kv.first, " = ", e.str(), ";");
+        }
+        for (auto &kv : cols) {
+            std::ostringstream e;
+            e << "B" << kv.second[0] << "_" << kv.first << " * x" << p.i1 << "_" << kv.second[0];
+            for (size_t n = 1; n < kv.second.size(); ++n) {
+                std::ostringstream f;
+                f << "FMA(B" << kv.second[n] << "_" << kv.first << ", x" << p.i1 << "_" << kv.second[n] << ", " << e.str()
+                  << ")";
+                e.str(f.str());
+            }
+            o("const T fy", kv.first, " = ", e.str(), ";");
+        }
+        // dW = sum_i x_i dF/dx_i
+        {
+            std::ostringstream e;
+            bool first = true;
+            for (auto &kv : rows) {
+                if (first) {
+                    e << "x" << p.i1 << "_" << kv.first << " * fx" << kv.first;
+                    first = false;
+                } else {
+                    std::ostringstream f;
+                    f << "FMA(x" << p.i1 << "_" << kv.first << ", fx" << kv.first << ", " << e.str() << ")";
+                    e.str(f.str());
+                }
+            }
+            std::string guard = needs_mask(p.mul_in, g) ? "(u < " + std::to_string(p.mul_in) + ") && " : "";
+            o("if (", guard, "dw) dw[(size_t)e * WROW + ", p.w_off, " + u] = ", e.str(), ";");
+        }
+        for (auto &kv : rows) o("d", p.i1, "_", kv.first, " = FMA(w", pi, ", fx", kv.first, ", d", p.i1, "_", kv.first, ");");
+        for (auto &kv : cols) o("h", p.i2, "_", kv.first, " = FMA(w", pi, ", fy", kv.first, ", h", p.i2, "_", kv.first, ");");
+        o.ind--;
+        o("}");
+    }
+    // dY: butterfly over the slot's channel lanes, then lane (j mod ct) of the slot writes j
+    o("if (dy) {");
+    o.ind++;
+    int j = 0;
+    std::vector<std::string> hs;
+    for (int b = 0; b < (int)P.sh.size(); ++b)
+        for (int jj = 0; jj < n_of(P.sh[b].l); ++jj) hs.push_back("h" + std::to_string(b) + "_" + std::to_string(jj));
+    for (auto &h : hs)
+        for (int m = g.ct / 2; m >= 1; m /= 2) o(h, " += __shfl_xor(", h, ", ", m, ");");
+    int per = (P.d_sh + g.ct - 1) / g.ct;
+    for (int r = 0; r < per; ++r) {
+        o("{");
+        o.ind++;
+        o("T v = (T)0;");
+        bool any = false;
+        for (j = r * g.ct; j < std::min(P.d_sh, (r + 1) * g.ct); ++j) {
+            o("if (ul == ", j - r * g.ct, ") v = ", hs[j], ";");
+            any = true;
+        }
+        if (any) {
+            o("const int jj = ", r * g.ct, " + ul;");
+            o("if (jj < DSH) {");
+            o.ind++;
+            o("T* p = &dy[(size_t)e * DSH + jj];");
+            o("if (tile == 0) *p = v; else *p += v;");
+            o.ind--;
+            o("}");
+        }
+        o.ind--;
+        o("}");
+    }
+    o.ind--;
+    o("}");
+    o.ind--;
+    o("}");  // edge loop
+    // sum the edge slots, write dx
+    for (int m = 32; m >= g.ct; m /= 2)
+        for (int b = 0; b < (int)P.ins.size(); ++b)
+            for (int i = 0; i < n_of(P.ins[b].l); ++i) o("d", b, "_", i, " += __shfl_xor(d", b, "_", i, ", ", m, ");");
+    o("if (dx && slot == 0) {");
+    o.ind++;
+    for (int b = 0; b < (int)P.ins.size(); ++b) {
+        const Irrep &ir = P.ins[b];
+        int off = 0;
+        for (int bb = 0; bb < b; ++bb) off += P.ins[bb].dim();
+        std::string guard = needs_mask(ir.mul, g) ? "if (u < " + std::to_string(ir.mul) + ") " : "";
+        for (int i = 0; i < n_of(ir.l); ++i)
+            o(guard, "dx[(size_t)s * DX + ", off, " + u * ", n_of(ir.l), " + ", i, "] = d", b, "_", i, ";");
+    }
+    o.ind--;
+    o("}");
+    o.ind--;
+    o("}");  // tile loop
+    o.ind--;
+    o("}");
+    o("");
+}
+
+}  // namespace
+
+std::string generate_source(const Plan &P)
+{
+    Out o;
+    emit_preamble(o, P);
+    if (P.mode == CGTP_UVU) {
+        for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi) emit_fwd_group(o, P, gi, false);
+        emit_fwd_kernel(o, P, false);
+        for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi) emit_fwd_group(o, P, gi, true);
+        emit_fwd_kernel(o, P, true);
+        emit_bwd_kernel(o, P);
+    } else {
+        o("// uvw plans: no kernels in this module yet");
+    }
+    return o.s.str();
+}
+
+}  // namespace cgtp

@@ -1,0 +1,127 @@
+// hipRTC compilation of the generated module for gfx950, an on-disk
+// content-addressed cache of code objects, and per-device module loading.
+//
+// sciencestack.ai page (TL;DR, Abstract): the kernels are generated and
+// JIT-compiled per model configuration.  Here the compiler is hipRTC, the
+// target is fixed to gfx950, and packed fp32 instructions are disabled.
+#include <dlfcn.h>
+#include <hip/hiprtc.h>
+#include <sys/stat.h>
+#include <unistd.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+#include <sstream>
+
+#include "plan.h"
+
+namespace cgtp {
+
+static const char *const kOptions[] = {
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+};
+
+static uint64_t fnv1a(const std::string &s, uint64_t h)
+{
+    for (unsigned char c : s) {
+        h ^= c;
+        h *= 1099511628211ull;
+    }
+    return h;
+}
+
+static std::string cache_dir()
+{
+    const char *env = std::getenv("CGTP_CACHE_DIR");
+    if (env && *env) return env;
+    Dl_info info;
+    if (dladdr(reinterpret_cast<void *>(&cache_dir), &info) && info.dli_fname) {
+        std::string p = info.dli_fname;
+        size_t slash = p.rfind('/');
+        if (slash != std::string::npos) return p.substr(0, slash) + "/jit_cache";
+    }
+    return "jit_cache";
+}
+
+static bool read_file(const std::string &path, std::vector<char> &out)
+{
+    std::ifstream f(path, std::ios::binary);
+    if (!f) return false;
+    out.assign(std::istreambuf_iterator<char>(f), std::istreambuf_iterator<char>());
+    return out.size() > 4 && std::memcmp(out.data(), "\x7f" "ELF", 4) == 0;
+}
+
+static void write_file_atomic(const std::string &path, const std::vector<char> &data)
+{
+    std::string tmp = path + ".tmp" + std::to_string(::getpid());
+    {
+        std::ofstream f(tmp, std::ios::binary);
+        if (!f) return;
+        f.write(data.data(), (std::streamsize)data.size());
+        if (!f) return;
+    }
+    std::rename(tmp.c_str(), path.c_str());
+}
+
+void compile_module(Plan &P)
+{
+    int major = 0, minor = 0;
+    hiprtcVersion(&major, &minor);
+    std::string opts;
+    for (const char *o : kOptions) opts += std::string(o) + " ";
+    std::string key_src = P.source + "\n//" + opts + std::to_string(major) + "." + std::to_string(minor);
+    char name[64];
+    std::snprintf(name, sizeof name, "cgtp_%016llx%016llx.hsaco",
+                  (unsigned long long)fnv1a(key_src, 1469598103934665603ull),
+                  (unsigned long long)fnv1a(key_src, 0x9e3779b97f4a7c15ull));
+    const std::string dir = cache_dir();
+    const std::string path = dir + "/" + name;
+    if (read_file(path, P.code)) return;
+
+    hiprtcProgram prog;
+    if (hiprtcCreateProgram(&prog, P.source.c_str(), "cgtp_module.hip", 0, nullptr, nullptr) != HIPRTC_SUCCESS)
+        throw Error(CGTP_ERR_COMPILE, "hiprtcCreateProgram failed");
+    hiprtcResult rc = hiprtcCompileProgram(prog, (int)(sizeof kOptions / sizeof kOptions[0]), kOptions);
+    if (rc != HIPRTC_SUCCESS) {
+        size_t n = 0;
+        hiprtcGetProgramLogSize(prog, &n);
+        std::string log(n, '\0');
+        if (n) hiprtcGetProgramLog(prog, &log[0]);
+        hiprtcDestroyProgram(&prog);
+        throw Error(CGTP_ERR_COMPILE, std::string("hipRTC: ") + hiprtcGetErrorString(rc) + "\n" + log);
+    }
+    size_t n = 0;
+    hiprtcGetCodeSize(prog, &n);
+    P.code.resize(n);
+    hiprtcGetCode(prog, P.code.data());
+    hiprtcDestroyProgram(&prog);
+    ::mkdir(dir.c_str(), 0755);
+    write_file_atomic(path, P.code);
+}
+
+static void check(hipError_t e, const char *what)
+{
+    if (e != hipSuccess) throw Error(CGTP_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+const Plan::Loaded &module_for_current_device(Plan &P)
+{
+    int dev = 0;
+    check(hipGetDevice(&dev), "hipGetDevice");
+    std::lock_guard<std::mutex> lock(P.mu);
+    auto it = P.loaded.find(dev);
+    if (it != P.loaded.end()) return it->second;
+    Plan::Loaded L;
+    check(hipModuleLoadData(&L.module, P.code.data()), "hipModuleLoadData");
+    if (P.mode == CGTP_UVU) {
+        check(hipModuleGetFunction(&L.conv_fwd, L.module, "cgtp_conv_fwd"), "hipModuleGetFunction(conv_fwd)");
+        check(hipModuleGetFunction(&L.conv_bwd, L.module, "cgtp_conv_bwd"), "hipModuleGetFunction(conv_bwd)");
+        check(hipModuleGetFunction(&L.tp_fwd, L.module, "cgtp_tp_fwd"), "hipModuleGetFunction(tp_fwd)");
+    }
+    return P.loaded.emplace(dev, L).first->second;
+}
+
+}  // namespace cgtp

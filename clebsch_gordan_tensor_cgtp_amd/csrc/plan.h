@@ -1,0 +1,90 @@
+// Internal plan representation shared by the planner, the code generator and
+// the ABI layer of libcgtp.  Nothing here is visible through include/cgtp.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <stdexcept>
+#include <string>
+#include <vector>
+
+#include "cgtp.h"
+
+namespace cgtp {
+
+// An error with a status code; converted to cgtp_status at the ABI edge.
+struct Error : std::runtime_error {
+    cgtp_status code;
+    Error(cgtp_status c, const std::string &m) : std::runtime_error(m), code(c) {}
+};
+
+struct Irrep {
+    int mul = 0, l = 0, p = 1;
+    int dim() const { return mul * (2 * l + 1); }
+};
+
+struct Nonzero {
+    int i, j, k;
+    double c;
+};
+
+struct Path {
+    int i1, i2, slot;
+    int l1, l2, l3, p3;
+    int a, b, o;           // offsets of the x, y and out blocks
+    int mul_in, mul_out;
+    int64_t w_off;
+    std::vector<Nonzero> nz;
+};
+
+// Work split of one generated kernel: a set of paths handled by one wave.
+struct Group {
+    std::vector<int> paths;  // indices into Plan::paths, canonical order
+    int mul = 0;             // channels of every path in the group
+    int ct = 64;             // lanes per edge slot (power of two <= 64)
+    int es = 1;              // edge slots per wave = 64 / ct
+    int tiles = 1;           // channel tiles of width ct covering mul
+};
+
+struct Plan {
+    std::vector<Irrep> ins, sh, out;
+    cgtp_mode mode = CGTP_UVU;
+    cgtp_dtype dtype = CGTP_F32;
+    std::vector<Path> paths;
+    int d_x = 0, d_sh = 0, d_out = 0;
+    int64_t w_numel = 0;
+    int nnz_total = 0;
+
+    std::vector<Group> fwd_groups;  // forward: one wave per (receiver, group, tile)
+    int fwd_tasks = 0;              // sum over groups of tiles
+    Group bwd_group;                // backward: one wave per sender covers every path
+    int fwd_waves_per_eu = 4;       // occupancy target given to the compiler (min waves per SIMD)
+    int bwd_waves_per_eu = 4;
+    std::string source;             // generated HIP source
+    std::vector<char> code;         // compiled gfx950 code object
+
+    std::mutex mu;                  // guards the per-device module table
+    struct Loaded {
+        hipModule_t module = nullptr;
+        hipFunction_t conv_fwd = nullptr, conv_bwd = nullptr, tp_fwd = nullptr;
+    };
+    std::map<int, Loaded> loaded;
+};
+
+// planner.cpp
+std::vector<Irrep> parse_irreps(const std::string &text, const char *what);
+void build_paths(Plan &plan);
+std::vector<Nonzero> real_cg_nonzeros(int l1, int l2, int l3);
+void schedule(Plan &plan);
+
+// codegen.cpp
+std::string generate_source(const Plan &plan);
+
+// jit.cpp
+void compile_module(Plan &plan);
+const Plan::Loaded &module_for_current_device(Plan &plan);
+
+}  // namespace cgtp

@@ -1,0 +1,310 @@
+// Host planner of libcgtp: irreps grammar, coupling paths, output slots, the
+// real CG blocks and the work split of the generated kernels.
+//
+// The CG values are computed here with the lowering-operator recursion (the
+// highest-weight state fixed by J+|J J> = 0, then J- applied M times), in long
+// double.  This is deliberately a different algorithm from a closed-form
+// Racah sum so that the two independent codes cross-check each other.  The
+// real basis, the Frobenius-1 normalisation, the sign rule and the zero
+// threshold are the conventions stated in include/cgtp.h.
+//
+// Pages: sciencestack.ai page (TL;DR, Abstract, Figures 1-3): static analysis
+// of the block-sparse CG tensor at model compile time, blocks that are
+// themselves sparse and repeated; "The GPU memory optimization with Larger
+// angular momentum" discussion: nonzeros coded into the instruction stream.
+#include <algorithm>
+#include <cctype>
+#include <cmath>
+#include <cstdlib>
+#include <complex>
+#include <map>
+#include <sstream>
+
+#include "plan.h"
+
+namespace cgtp {
+
+static constexpr int kLmax = 7;
+static constexpr long double kZeroTol = 1e-9L;
+
+std::vector<Irrep> parse_irreps(const std::string &text, const char *what)
+{
+    std::string s;
+    for (char ch : text)
+        if (!std::isspace(static_cast<unsigned char>(ch))) s.push_back(ch);
+    if (s.empty()) throw Error(CGTP_ERR_IRREPS, std::string(what) + " irreps: empty string");
+    std::vector<Irrep> out;
+    size_t pos = 0;
+    while (pos <= s.size()) {
+        size_t plus = s.find('+', pos);
+        std::string term = s.substr(pos, plus == std::string::npos ? std::string::npos : plus - pos);
+        auto bad = [&](const char *why) {
+            return Error(CGTP_ERR_IRREPS, std::string(what) + " irreps: term '" + term + "' " + why);
+        };
+        size_t x = term.find('x');
+        if (x == std::string::npos || x == 0) throw bad("must look like MULxLP");
+        for (size_t i = 0; i < x; ++i)
+            if (!std::isdigit(static_cast<unsigned char>(term[i]))) throw bad("has a bad multiplicity");
+        if (term.size() < x + 3) throw bad("lacks L or parity");
+        char par = term.back();
+        if (par != 'e' && par != 'o') throw bad("parity must be e or o");
+        std::string lstr = term.substr(x + 1, term.size() - x - 2);
+        for (char ch : lstr)
+            if (!std::isdigit(static_cast<unsigned char>(ch))) throw bad("has a bad L");
+        if (x > 9 || lstr.size() > 3) throw bad("is out of range");
+        Irrep ir;
+        ir.mul = std::stoi(term.substr(0, x));
+        ir.l = std::stoi(lstr);
+        ir.p = par == 'e' ? 1 : -1;
+        if (ir.mul < 1) throw bad("needs multiplicity >= 1");
+        if (ir.l > kLmax) throw bad("has L above 7");
+        out.push_back(ir);
+        if (plus == std::string::npos) break;
+        pos = plus + 1;
+    }
+    return out;
+}
+
+// ------------------------------------------------------------------------------------------
+// Complex CG by recursion.  table[m1 + j1][M + J] holds <j1 m1, j2 M-m1 | J M>.
+
+static long double raise_coef(int j, int m) { return std::sqrt((long double)(j - m) * (j + m + 1)); }
+static long double lower_coef(int j, int m) { return std::sqrt((long double)(j + m) * (j - m + 1)); }
+
+static std::vector<std::vector<long double>> complex_cg_table(int j1, int j2, int J)
+{
+    std::vector<std::vector<long double>> t(2 * j1 + 1, std::vector<long double>(2 * J + 1, 0.0L));
+    auto at = [&](int m1, int M) -> long double & { return t[m1 + j1][M + J]; };
+    auto valid = [&](int m1, int M) { return std::abs(m1) <= j1 && std::abs(M - m1) <= j2 && std::abs(M) <= J; };
+    // highest weight M = J: J+ |J J> = 0 gives
+    //   a(m1+1) raise_coef(j2, J-m1-1) + a(m1) raise_coef(j1, m1) = 0
+    // with a(j1) > 0 (Condon-Shortley).
+    int lo = std::max(-j1, J - j2);
+    at(j1, J) = 1.0L;
+    for (int m1 = j1 - 1; m1 >= lo; --m1) at(m1, J) = -at(m1 + 1, J) * raise_coef(j2, J - m1 - 1) / raise_coef(j1, m1);
+    long double nrm = 0.0L;
+    for (int m1 = lo; m1 <= j1; ++m1) nrm += at(m1, J) * at(m1, J);
+    nrm = std::sqrt(nrm);
+    for (int m1 = lo; m1 <= j1; ++m1) at(m1, J) /= nrm;
+    // lowering: lower_coef(J, M) |J M-1> = (J1- + J2-) |J M>
+    for (int M = J; M > -J; --M) {
+        for (int m1 = -j1; m1 <= j1; ++m1) {
+            int m2 = M - 1 - m1;
+            if (!valid(m1, M - 1)) continue;
+            long double v = 0.0L;
+            if (m1 + 1 <= j1 && valid(m1 + 1, M)) v += at(m1 + 1, M) * lower_coef(j1, m1 + 1);
+            if (m2 + 1 <= j2 && valid(m1, M)) v += at(m1, M) * lower_coef(j2, m2 + 1);
+            at(m1, M - 1) = v / lower_coef(J, M);
+        }
+    }
+    return t;
+}
+
+// Row r = m + l of the real-basis matrix Q_l (real = Q complex): up to two entries.
+struct QEntry {
+    int m;
+    std::complex<long double> v;
+};
+static std::vector<QEntry> q_row(int l, int m)
+{
+    const long double s = 1.0L / std::sqrt(2.0L);
+    const long double sg = (m % 2 == 0) ? 1.0L : -1.0L;
+    if (m > 0) return {{-m, {s, 0}}, {m, {sg * s, 0}}};
+    if (m < 0) return {{m, {0, s}}, {-m, {0, -sg * s}}};
+    return {{0, {1, 0}}};
+}
+
+std::vector<Nonzero> real_cg_nonzeros(int l1, int l2, int l3)
+{
+    if (l3 < std::abs(l1 - l2) || l3 > l1 + l2) throw Error(CGTP_ERR_INTERNAL, "triangle rule");
+    auto cg = complex_cg_table(l1, l2, l3);
+    const int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1, n3 = 2 * l3 + 1;
+    std::vector<long double> part(n1 * n2 * n3, 0.0L);
+    const bool take_real = (l1 + l2 + l3) % 2 == 0;
+    for (int i = 0; i < n1; ++i)
+        for (int j = 0; j < n2; ++j)
+            for (int k = 0; k < n3; ++k) {
+                std::complex<long double> acc = 0;
+                for (const auto &a : q_row(l1, i - l1))
+                    for (const auto &b : q_row(l2, j - l2))
+                        for (const auto &c : q_row(l3, k - l3)) {
+                            if (a.m + b.m != c.m) continue;
+                            acc += std::conj(a.v) * std::conj(b.v) * c.v * cg[a.m + l1][c.m + l3];
+                        }
+                part[(i * n2 + j) * n3 + k] = take_real ? acc.real() : acc.imag();
+            }
+    long double nrm = 0.0L;
+    for (long double v : part) nrm += v * v;
+    nrm = std::sqrt(nrm);
+    long double sign = 0.0L;
+    for (long double &v : part) {
+        v /= nrm;
+        if (std::fabs(v) <= kZeroTol) v = 0.0L;
+        if (sign == 0.0L && v != 0.0L) sign = v > 0 ? 1.0L : -1.0L;
+    }
+    std::vector<Nonzero> nz;
+    for (int i = 0; i < n1; ++i)
+        for (int j = 0; j < n2; ++j)
+            for (int k = 0; k < n3; ++k) {
+                long double v = part[(i * n2 + j) * n3 + k];
+                if (v != 0.0L) nz.push_back({i, j, k, static_cast<double>(sign * v)});
+            }
+    return nz;
+}
+
+// ------------------------------------------------------------------------------------------
+
+void build_paths(Plan &P)
+{
+    for (const Irrep &s : P.sh)
+        if (s.mul != 1) throw Error(CGTP_ERR_IRREPS, "every SH irrep must have multiplicity 1");
+    std::vector<int> xo, yo, oo;
+    int acc = 0;
+    for (const Irrep &r : P.ins) { xo.push_back(acc); acc += r.dim(); }
+    P.d_x = acc;
+    acc = 0;
+    for (const Irrep &r : P.sh) { yo.push_back(acc); acc += r.dim(); }
+    P.d_sh = acc;
+    acc = 0;
+    for (const Irrep &r : P.out) { oo.push_back(acc); acc += r.dim(); }
+    P.d_out = acc;
+
+    auto in_out = [&](int l, int p) {
+        for (const Irrep &o : P.out)
+            if (o.l == l && o.p == p) return true;
+        return false;
+    };
+    std::vector<Path> paths;
+    for (int i1 = 0; i1 < (int)P.ins.size(); ++i1)
+        for (int i2 = 0; i2 < (int)P.sh.size(); ++i2) {
+            const Irrep &a = P.ins[i1], &b = P.sh[i2];
+            for (int l3 = std::abs(a.l - b.l); l3 <= a.l + b.l; ++l3) {
+                int p3 = a.p * b.p;
+                if (!in_out(l3, p3)) continue;
+                Path p{};
+                p.i1 = i1; p.i2 = i2; p.l1 = a.l; p.l2 = b.l; p.l3 = l3; p.p3 = p3;
+                p.a = xo[i1]; p.b = yo[i2];
+                p.slot = -1;
+                paths.push_back(p);
+            }
+        }
+    // output slots: key (l, p) -> occurrences in out, producing paths in order
+    std::map<std::pair<int, int>, std::vector<int>> occ, prod;
+    for (int q = 0; q < (int)P.out.size(); ++q) occ[{P.out[q].l, P.out[q].p}].push_back(q);
+    for (int i = 0; i < (int)paths.size(); ++i) prod[{paths[i].l3, paths[i].p3}].push_back(i);
+    for (auto &kv : occ) {
+        auto it = prod.find(kv.first);
+        std::ostringstream key;
+        key << "l=" << kv.first.first << (kv.first.second > 0 ? "e" : "o");
+        if (it == prod.end()) throw Error(CGTP_ERR_IRREPS, "output irrep " + key.str() + " is produced by no path");
+        const auto &pr = it->second;
+        if (kv.second.size() == 1) {
+            for (int i : pr) paths[i].slot = kv.second[0];
+        } else if (kv.second.size() == pr.size()) {
+            for (size_t t = 0; t < pr.size(); ++t) paths[pr[t]].slot = kv.second[t];
+        } else {
+            std::ostringstream m;
+            m << "output irrep " << key.str() << " occurs " << kv.second.size() << " times but " << pr.size()
+              << " paths produce it";
+            throw Error(CGTP_ERR_IRREPS, m.str());
+        }
+    }
+    int64_t w = 0;
+    P.nnz_total = 0;
+    std::map<std::tuple<int, int, int>, std::vector<Nonzero>> cache;
+    for (Path &p : paths) {
+        p.o = oo[p.slot];
+        p.mul_in = P.ins[p.i1].mul;
+        p.mul_out = P.out[p.slot].mul;
+        if (P.mode == CGTP_UVU && p.mul_out != p.mul_in)
+            throw Error(CGTP_ERR_IRREPS, "uvu needs the output multiplicity to equal the input's on every path");
+        p.w_off = w;
+        w += P.mode == CGTP_UVU ? p.mul_in : (int64_t)p.mul_in * p.mul_out;
+        auto key = std::make_tuple(p.l1, p.l2, p.l3);
+        auto c = cache.find(key);
+        if (c == cache.end()) c = cache.emplace(key, real_cg_nonzeros(p.l1, p.l2, p.l3)).first;
+        p.nz = c->second;
+        P.nnz_total += (int)p.nz.size();
+    }
+    if (paths.empty()) throw Error(CGTP_ERR_IRREPS, "no coupling path connects the irreps");
+    P.w_numel = w;
+    P.paths = std::move(paths);
+}
+
+// ------------------------------------------------------------------------------------------
+// Work split.  Forward: output slots are packed greedily (in slot order, so
+// paths sharing an input block stay together) into groups whose accumulators
+// fit a register budget; each (receiver, group, channel tile) is one wave.
+// Backward: one group with every path (the sender pass keeps only the input
+// gradient resident, so it needs no split and no cross-wave reduction).
+
+static int lanes_for(int mul)
+{
+    int ct = 1;
+    while (ct < mul && ct < 64) ct *= 2;
+    return ct;
+}
+
+static void finish_group(Group &g)
+{
+    g.ct = lanes_for(g.mul);
+    g.es = 64 / g.ct;
+    g.tiles = (g.mul + g.ct - 1) / g.ct;
+}
+
+void schedule(Plan &P)
+{
+    const int word = P.dtype == CGTP_F64 ? 2 : 1;
+    const int budget = 64;  // 32-bit registers per lane for the forward accumulators
+    P.fwd_groups.clear();
+    if (P.mode == CGTP_UVU) {
+        std::vector<std::vector<int>> slot_paths(P.out.size());
+        for (int i = 0; i < (int)P.paths.size(); ++i) slot_paths[P.paths[i].slot].push_back(i);
+        // slots in order of their first path, so input blocks stay together
+        std::vector<int> order;
+        for (int q = 0; q < (int)P.out.size(); ++q) order.push_back(q);
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int a, int b) { return slot_paths[a].front() < slot_paths[b].front(); });
+        Group cur;
+        int regs = 0;
+        for (int q : order) {
+            int need = word * (2 * P.out[q].l + 1);
+            int mul = P.out[q].mul;
+            if (!cur.paths.empty() && (regs + need > budget || mul != cur.mul)) {
+                finish_group(cur);
+                P.fwd_groups.push_back(cur);
+                cur = Group();
+                regs = 0;
+            }
+            cur.mul = mul;
+            for (int i : slot_paths[q]) cur.paths.push_back(i);
+            regs += need;
+        }
+        if (!cur.paths.empty()) {
+            finish_group(cur);
+            P.fwd_groups.push_back(cur);
+        }
+        for (Group &g : P.fwd_groups) std::sort(g.paths.begin(), g.paths.end());
+    }
+    P.fwd_tasks = 0;
+    for (const Group &g : P.fwd_groups) P.fwd_tasks += g.tiles;
+
+    Group b;
+    for (int i = 0; i < (int)P.paths.size(); ++i) {
+        b.paths.push_back(i);
+        b.mul = std::max(b.mul, P.paths[i].mul_in);
+    }
+    finish_group(b);
+    P.bwd_group = b;
+
+    // Occupancy targets: 4 waves per SIMD (<= 128 VGPRs) keeps enough loads in
+    // flight to cover HBM latency in the forward; the backward holds a whole g
+    // row per edge and gets 2; fp64 doubles the register need of the same code
+    // and halves both.  CGTP_FWD_WAVES / CGTP_BWD_WAVES override (tuning).
+    P.fwd_waves_per_eu = P.dtype == CGTP_F64 ? 2 : 4;
+    P.bwd_waves_per_eu = P.dtype == CGTP_F64 ? 1 : 2;
+    if (const char *e = std::getenv("CGTP_FWD_WAVES")) P.fwd_waves_per_eu = std::max(1, std::atoi(e));
+    if (const char *e = std::getenv("CGTP_BWD_WAVES")) P.bwd_waves_per_eu = std::max(1, std::atoi(e));
+}
+
+}  // namespace cgtp

@@ -1,0 +1,235 @@
+// Fixed (not generated) kernels of libcgtp for gfx950: real spherical
+// harmonics of the edge vectors and the sender-sorted transpose of a
+// receiver CSR.
+//
+// Spherical harmonics: the edge features of the convolution (sciencestack.ai
+// page, Figure 4B).  Component normalisation, real basis with l = 1 ordered
+// (y, z, x).  Evaluated with the reduced associated Legendre recurrence
+// (no Condon-Shortley factor, which the real combination cancels) times the
+// Chebyshev-like recurrence of r_xy^m cos(m phi) and r_xy^m sin(m phi).
+//
+// Transpose: a stable counting sort of the edges by sender, needed by the
+// atomic-free backward (OpenEquivariance discussion: a deterministic fused
+// convolution next to the atomic one).  Counting uses integer atomics, whose
+// totals are exact; the placement inside a sender is then sorted by edge id,
+// so the result is unique and bit-exact.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "static_kernels.h"
+
+namespace cgtp {
+
+// ------------------------------------------------------------------------------------------
+// spherical harmonics
+
+template <typename T, int L>
+__global__ void __launch_bounds__(256) sh_kernel(int64_t E, const T *__restrict__ vec, T *__restrict__ y)
+{
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= E) return;
+    constexpr int D = (L + 1) * (L + 1);
+    T vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
+    T r2 = vx * vx + vy * vy + vz * vz;
+    T inv = r2 > (T)0 ? (T)1 / sqrt(r2) : (T)0;
+    T x = vx * inv, yy = vy * inv, z = vz * inv;
+    T c[L + 1], s[L + 1];
+    c[0] = (T)1;
+    s[0] = (T)0;
+#pragma unroll
+    for (int m = 0; m < L; ++m) {
+        c[m + 1] = x * c[m] - yy * s[m];
+        s[m + 1] = x * s[m] + yy * c[m];
+    }
+    T out[D];
+#pragma unroll
+    for (int m = 0; m <= L; ++m) {
+        // reduced Legendre Q_l^m(z), l = m..L
+        T dfact = (T)1;
+        for (int k = 1; k <= 2 * m - 1; k += 2) dfact *= (T)k;
+        T qmm = dfact, q_prev = (T)0, q = qmm;
+#pragma unroll
+        for (int l = m; l <= L; ++l) {
+            if (l == m) {
+                q = qmm;
+            } else if (l == m + 1) {
+                q_prev = qmm;
+                q = z * (T)(2 * m + 1) * qmm;
+            } else {
+                T qn = ((T)(2 * l - 1) * z * q - (T)(l + m - 1) * q_prev) / (T)(l - m);
+                q_prev = q;
+                q = qn;
+            }
+            // sqrt(2 (2l+1) (l-m)! / (l+m)!) for m > 0, sqrt(2l+1) for m = 0
+            T ratio = (T)1;
+            for (int k = l - m + 1; k <= l + m; ++k) ratio /= (T)k;
+            if (m == 0) {
+                out[l * l + l] = sqrt((T)(2 * l + 1)) * q;
+            } else {
+                T coef = sqrt((T)2 * (T)(2 * l + 1) * ratio) * q;
+                out[l * l + l + m] = coef * c[m];
+                out[l * l + l - m] = coef * s[m];
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i) y[(size_t)e * D + i] = out[i];
+}
+
+template <typename T>
+static hipError_t launch_sh_t(int lmax, int64_t E, const void *vec, void *y, hipStream_t st)
+{
+    dim3 grid((unsigned)((E + 255) / 256)), block(256);
+    const T *v = static_cast<const T *>(vec);
+    T *o = static_cast<T *>(y);
+    switch (lmax) {
+    case 0: hipLaunchKernelGGL((sh_kernel<T, 0>), grid, block, 0, st, E, v, o); break;
+    case 1: hipLaunchKernelGGL((sh_kernel<T, 1>), grid, block, 0, st, E, v, o); break;
+    case 2: hipLaunchKernelGGL((sh_kernel<T, 2>), grid, block, 0, st, E, v, o); break;
+    case 3: hipLaunchKernelGGL((sh_kernel<T, 3>), grid, block, 0, st, E, v, o); break;
+    case 4: hipLaunchKernelGGL((sh_kernel<T, 4>), grid, block, 0, st, E, v, o); break;
+    case 5: hipLaunchKernelGGL((sh_kernel<T, 5>), grid, block, 0, st, E, v, o); break;
+    case 6: hipLaunchKernelGGL((sh_kernel<T, 6>), grid, block, 0, st, E, v, o); break;
+    case 7: hipLaunchKernelGGL((sh_kernel<T, 7>), grid, block, 0, st, E, v, o); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_spherical_harmonics(int lmax, bool f64, int64_t E, const void *vec, void *y, hipStream_t st)
+{
+    if (E == 0) return hipSuccess;
+    return f64 ? launch_sh_t<double>(lmax, E, vec, y, st) : launch_sh_t<float>(lmax, E, vec, y, st);
+}
+
+// ------------------------------------------------------------------------------------------
+// transpose
+
+__global__ void __launch_bounds__(256) fill_zero(int32_t *a, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) a[i] = 0;
+}
+
+// count(s) lands at index s + 2 so that the inclusive scan leaves start(s) at s + 1
+__global__ void __launch_bounds__(256) count_senders(const int32_t *__restrict__ col, int64_t E, int64_t N,
+                                                     int32_t *t_row_ptr)
+{
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= E) return;
+    const int32_t s = col[e];
+    if (s >= 0 && s + 2 <= N) atomicAdd(&t_row_ptr[s + 2], 1);
+}
+
+// single-workgroup inclusive scan in place (once per graph, N + 1 entries)
+__global__ void __launch_bounds__(1024) scan_inclusive(int32_t *a, int64_t n)
+{
+    __shared__ int32_t part[1024];
+    const int tid = threadIdx.x;
+    const int64_t chunk = (n + 1023) / 1024;
+    const int64_t lo = tid * chunk, hi = lo + chunk < n ? lo + chunk : n;
+    int32_t sum = 0;
+    for (int64_t i = lo; i < hi; ++i) sum += a[i];
+    part[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < 1024; off *= 2) {
+        int32_t v = tid >= off ? part[tid - off] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    int32_t run = tid > 0 ? part[tid - 1] : 0;
+    for (int64_t i = lo; i < hi; ++i) {
+        run += a[i];
+        a[i] = run;
+    }
+}
+
+__global__ void __launch_bounds__(256) place_edges(const int32_t *__restrict__ col, int64_t E, int64_t N,
+                                                   int32_t *t_row_ptr, int32_t *t_edge)
+{
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= E) return;
+    const int32_t s = col[e];
+    if (s < 0 || s >= N) return;
+    const int32_t pos = atomicAdd(&t_row_ptr[s + 1], 1);
+    t_edge[pos] = (int32_t)e;
+}
+
+__device__ void sift_down(int32_t *a, int64_t root, int64_t n)
+{
+    for (;;) {
+        int64_t c = 2 * root + 1;
+        if (c >= n) return;
+        if (c + 1 < n && a[c + 1] > a[c]) ++c;
+        if (a[root] >= a[c]) return;
+        int32_t t = a[root];
+        a[root] = a[c];
+        a[c] = t;
+        root = c;
+    }
+}
+
+// ascending edge ids inside every sender segment (makes the order unique)
+__global__ void __launch_bounds__(256) sort_segments(const int32_t *__restrict__ t_row_ptr, int64_t N,
+                                                     int32_t *t_edge)
+{
+    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= N) return;
+    int32_t *a = t_edge + t_row_ptr[s];
+    const int64_t n = (int64_t)t_row_ptr[s + 1] - t_row_ptr[s];
+    if (n <= 32) {
+        for (int64_t i = 1; i < n; ++i) {
+            int32_t v = a[i];
+            int64_t j = i - 1;
+            while (j >= 0 && a[j] > v) {
+                a[j + 1] = a[j];
+                --j;
+            }
+            a[j + 1] = v;
+        }
+        return;
+    }
+    for (int64_t i = n / 2 - 1; i >= 0; --i) sift_down(a, i, n);
+    for (int64_t end = n - 1; end > 0; --end) {
+        int32_t t = a[0];
+        a[0] = a[end];
+        a[end] = t;
+        sift_down(a, 0, end);
+    }
+}
+
+// receiver of each transposed edge: binary search in the receiver CSR
+__global__ void __launch_bounds__(256) edge_receivers(const int32_t *__restrict__ row_ptr, int64_t N,
+                                                      const int32_t *__restrict__ t_edge, int64_t E,
+                                                      int32_t *t_dst)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= E) return;
+    const int32_t e = t_edge[t];
+    int64_t lo = 0, hi = N;  // find n with row_ptr[n] <= e < row_ptr[n + 1]
+    while (hi - lo > 1) {
+        int64_t mid = (lo + hi) / 2;
+        if (row_ptr[mid] <= e) lo = mid;
+        else hi = mid;
+    }
+    t_dst[t] = (int32_t)lo;
+}
+
+hipError_t launch_transpose(int64_t N, int64_t E, const int32_t *row_ptr, const int32_t *col, int32_t *t_row_ptr,
+                            int32_t *t_edge, int32_t *t_dst, hipStream_t st)
+{
+    auto blocks = [](int64_t n) { return dim3((unsigned)((n + 255) / 256)); };
+    hipLaunchKernelGGL(fill_zero, blocks(N + 1), dim3(256), 0, st, t_row_ptr, N + 1);
+    if (E > 0) {
+        hipLaunchKernelGGL(count_senders, blocks(E), dim3(256), 0, st, col, E, N, t_row_ptr);
+        hipLaunchKernelGGL(scan_inclusive, dim3(1), dim3(1024), 0, st, t_row_ptr, N + 1);
+        hipLaunchKernelGGL(place_edges, blocks(E), dim3(256), 0, st, col, E, N, t_row_ptr, t_edge);
+        if (N > 0) hipLaunchKernelGGL(sort_segments, blocks(N), dim3(256), 0, st, t_row_ptr, N, t_edge);
+        hipLaunchKernelGGL(edge_receivers, blocks(E), dim3(256), 0, st, row_ptr, N, t_edge, E, t_dst);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace cgtp

@@ -1,0 +1,184 @@
+/*
+ * cgtp.h -- C ABI of libcgtp: the O(3)-equivariant Clebsch-Gordan tensor
+ * product (CGTP), batched and fused with graph convolution, on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * What is computed (sources are the pages this library follows):
+ *  - "An Efficient Sparse Kernel Generator for O(3)-Equivariant Deep
+ *    Networks" (sciencestack.ai page), Abstract and Figure 1: a block-sparse
+ *    real CG tensor contracted with two dense vectors, followed by a
+ *    structured weight; Figure 4: use case A (batched rows) and use case B
+ *    (graph convolution, node features combined with edge features and
+ *    summed into the receiving node); the Abstract also names the gradient.
+ *  - Sobek (aiqbench.com page, Abstract): the convolution is evaluated with
+ *    bounded receiver-side state and no edge-sized intermediates, forward and
+ *    backward.
+ *  - LunaTP (readsearch.ai page, Abstract): node-centric execution.
+ *  - OpenEquivariance discussion "The GPU memory optimization with Larger
+ *    angular momentum": near-zero device memory overhead, only returned
+ *    buffers are new, a deterministic convolution exists next to an atomic one.
+ *
+ * Conventions (readings; the pages fix none of them):
+ *  - irreps strings "MULxLP" joined by '+', 0 <= L <= 7, P in {e,o}; blocks
+ *    concatenated in string order; element (channel u, component m) of a
+ *    block at offset + u*(2L+1) + (m+L);
+ *  - real basis with l = 1 ordered (y, z, x); every CG block has Frobenius
+ *    norm 1 and its first nonzero (row-major i, j, k) positive;
+ *  - paths: i1 over input irreps, i2 over SH irreps, l3 ascending, parity
+ *    p1*p2, kept if (l3, p3) occurs in the output; an output irrep that
+ *    occurs once receives the sum of all paths producing it, one that occurs
+ *    k > 1 times needs exactly k producing paths, taken in order;
+ *  - uvu weights: per row/edge, the concatenation over paths of [mul];
+ *    uvw weights (shared): the concatenation over paths of [mul_in][mul_out].
+ *
+ * Memory and streams: every device buffer is owned by the caller, must be a
+ * device pointer to contiguous row-major data of the plan's dtype, 16-byte
+ * aligned, and outputs must not alias inputs.  The library never allocates,
+ * frees or synchronises device memory.  `stream` is a hipStream_t (NULL =
+ * the default stream); all work is enqueued on it asynchronously.
+ * Index arrays are int32 and N, E < 2^31.
+ *
+ * Errors: every entry point returns a cgtp_status; the message of the last
+ * failure on the calling thread is cgtp_last_error().  Argument checks run
+ * before any GPU call.  A kernel fault surfaces at the caller's next
+ * synchronisation with the stream, not here.  No exception or abort crosses
+ * the ABI.
+ */
+#ifndef CGTP_H
+#define CGTP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum cgtp_status {
+    CGTP_OK = 0,
+    CGTP_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, aliasing */
+    CGTP_ERR_IRREPS = 2,      /* irreps string or path/slot rule violated      */
+    CGTP_ERR_UNSUPPORTED = 3, /* valid request this build does not implement   */
+    CGTP_ERR_COMPILE = 4,     /* hipRTC failed; the log is in cgtp_last_error  */
+    CGTP_ERR_HIP = 5,         /* a HIP runtime call failed                     */
+    CGTP_ERR_INTERNAL = 6
+} cgtp_status;
+
+typedef enum cgtp_mode { CGTP_UVU = 0, CGTP_UVW = 1 } cgtp_mode;
+typedef enum cgtp_dtype { CGTP_F32 = 0, CGTP_F64 = 1 } cgtp_dtype;
+
+typedef struct cgtp_plan cgtp_plan; /* opaque, immutable after creation */
+
+typedef struct cgtp_plan_info {
+    int32_t d_x;          /* width of one input row (node features)          */
+    int32_t d_sh;         /* width of one edge/row of y (spherical harmonics) */
+    int32_t d_out;        /* width of one output row                          */
+    int32_t num_paths;
+    int64_t weight_numel; /* uvu: weights per row/edge; uvw: shared total     */
+    int32_t nnz_total;    /* CG nonzeros summed over paths                    */
+    int32_t mode;         /* cgtp_mode                                        */
+    int32_t dtype;        /* cgtp_dtype                                       */
+    int32_t fwd_tasks;    /* waves per receiver in the forward convolution    */
+} cgtp_plan_info;
+
+typedef struct cgtp_path_info {
+    int32_t i1, i2, slot;         /* input irrep, SH irrep, output block       */
+    int32_t l1, l2, l3, p3;       /* degrees and output parity (+1/-1)         */
+    int32_t x_off, y_off, out_off;/* block offsets in x, y and out rows        */
+    int32_t mul_in, mul_out;
+    int64_t w_off;                /* offset of this path's weights             */
+    int32_t nnz;                  /* CG nonzeros of this path's block          */
+} cgtp_path_info;
+
+/*
+ * Plan: parse the three irreps strings, enumerate the paths, compute the real
+ * CG blocks (the planner's own exact code), drop the zeros (|C| <= 1e-9) and
+ * generate one gfx950 module with the nonzeros as compile-time constants
+ * (sciencestack.ai page, TL;DR and Abstract: JIT generation with static
+ * analysis; OpenEquivariance discussion: nonzeros in the instruction stream).
+ * The module is compiled with hipRTC (or taken from the on-disk cache,
+ * $CGTP_CACHE_DIR, default: a jit_cache folder next to the library) and
+ * loaded on a device at its first launch there.  Allocates no device memory.
+ * uvu needs mul_out == mul_in on every path; both modes need SH mul == 1.
+ * Errors: CGTP_ERR_INVALID_ARG (null), CGTP_ERR_IRREPS, CGTP_ERR_COMPILE.
+ */
+cgtp_status cgtp_plan_create(const char *in_irreps, const char *sh_irreps, const char *out_irreps,
+                             cgtp_mode mode, cgtp_dtype dtype, cgtp_plan **plan_out);
+cgtp_status cgtp_plan_destroy(cgtp_plan *plan);
+cgtp_status cgtp_plan_info_get(const cgtp_plan *plan, cgtp_plan_info *info);
+cgtp_status cgtp_plan_path(const cgtp_plan *plan, int32_t path, cgtp_path_info *info);
+/* Copies up to `cap` nonzeros of one path's real CG block: ijk[3*n] (i, j, k)
+ * and values[n] as float64.  *nnz receives the full count. */
+cgtp_status cgtp_plan_path_coefficients(const cgtp_plan *plan, int32_t path, int32_t cap,
+                                        int32_t *ijk, double *values, int32_t *nnz);
+/* The generated HIP source of the plan's module (owned by the plan). */
+const char *cgtp_plan_source(const cgtp_plan *plan);
+
+/*
+ * Batched tensor product, use case A (sciencestack.ai page, Figure 4A):
+ *   uvu: out[b, o + u(2l3+1) + k] = sum_paths W[b, w_p + u] *
+ *                                   sum_{i,j} C[i,j,k] x[b, a + u(2l1+1) + i] y[b, b_p + j]
+ *        w is [B][weight_numel], shared_weights must be 0;
+ *   uvw: out[b, o + v(2l3+1) + k] = sum_paths sum_u W_p[u][v] * (same contraction)
+ *        w is the shared [weight_numel] block, shared_weights must be 1.
+ * x [B][d_x], y [B][d_sh], out [B][d_out] (overwritten).  B = 0 is a no-op.
+ */
+cgtp_status cgtp_tp_forward(const cgtp_plan *plan, int64_t B, const void *x, const void *y,
+                            const void *w, int shared_weights, void *out, void *stream);
+
+/*
+ * Fused convolution forward, use case B (sciencestack.ai page, Figure 4B;
+ * Sobek page, Abstract): for every receiver n,
+ *   out[n] = sum_{e in [row_ptr[n], row_ptr[n+1])} TP_uvu(x[col[e]], y[e], W[e]).
+ * row_ptr [N+1] and col [E] form a receiver-sorted CSR (row_ptr[0] = 0,
+ * non-decreasing, row_ptr[N] = E, 0 <= col < N); y [E][d_sh] and w
+ * [E][weight_numel] are in CSR edge order; x [N][d_x]; out [N][d_out] is
+ * overwritten, receivers without edges get zeros.  One owner per output row:
+ * no atomics, bitwise deterministic.  uvu plans only (uvw returns
+ * CGTP_ERR_UNSUPPORTED).
+ */
+cgtp_status cgtp_conv_forward(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
+                              const int32_t *col, const void *x, const void *y, const void *w,
+                              void *out, void *stream);
+
+/*
+ * Sender-sorted transpose of a receiver CSR, once per graph: t_row_ptr [N+1],
+ * t_edge [E] (edge ids grouped by sender, ascending edge id inside a sender:
+ * a stable sort by col) and t_dst [E] (receiver of t_edge[t]).  Integer
+ * results, bit-exact and deterministic.  All outputs caller-owned.
+ */
+cgtp_status cgtp_graph_transpose(int64_t N, int64_t E, const int32_t *row_ptr, const int32_t *col,
+                                 int32_t *t_row_ptr, int32_t *t_edge, int32_t *t_dst, void *stream);
+
+/*
+ * Fused convolution backward (sciencestack.ai page, Abstract: gradient
+ * kernels; Sobek page: adjoints without edge-sized intermediates).  With
+ * g = grad_out [N][d_out], for each edge e = (s -> n) and path p:
+ *   grad_w[e, w_p + u] = sum_{ijk} C x[s,u,i] y[e,j] g[n,u,k]
+ *   grad_y[e, b_p + j] = sum_p sum_u W[e,p,u] sum_{ik} C x[s,u,i] g[n,u,k]
+ *   grad_x[s, a_p + u(2l1+1) + i] = sum_{e: col[e]=s} sum_p W[e,p,u] sum_{jk} C y[e,j] g[n,u,k]
+ * One pass in sender order over the transpose (cgtp_graph_transpose): each
+ * output row has one owner, no atomics, bitwise deterministic.  Any of
+ * grad_x / grad_y / grad_w may be NULL to skip it; outputs are overwritten.
+ */
+cgtp_status cgtp_conv_backward(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
+                               const int32_t *col, const int32_t *t_row_ptr, const int32_t *t_edge,
+                               const int32_t *t_dst, const void *x, const void *y, const void *w,
+                               const void *grad_out, void *grad_x, void *grad_y, void *grad_w,
+                               void *stream);
+
+/*
+ * Real spherical harmonics of the edge vectors, component normalisation
+ * (sum_m Y_lm^2 = 2l+1, Y_1 = sqrt3 (y, z, x)/|r|), degrees 0..lmax (<= 7):
+ * vec [E][3] (any nonzero length), y [E][(lmax+1)^2] overwritten.  These
+ * are the edge features of the convolution (sciencestack.ai page, Figure 4B).
+ */
+cgtp_status cgtp_spherical_harmonics(int32_t lmax, cgtp_dtype dtype, int64_t E, const void *vec,
+                                     void *y, void *stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *cgtp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CGTP_H */

@@ -1,0 +1,179 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: rel-L2 <= 1e-4 (fp32), <= 1e-10 (fp64) per output tensor; integer
+arrays bit-exact; outputs bitwise repeatable.
+"""
+import numpy as np
+import pytest
+
+from clebsch_gordan_tensor_cgtp_amd import binding as cg
+from clebsch_gordan_tensor_cgtp_amd import synth
+from oracle import irreps as oirreps
+from oracle import loops, ref
+from oracle import sh as osh
+
+from cases import TOL, ConvCase, edge_case_graph, rel_l2, to_device
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    # name: (spec, dtypes)
+    "nequip-small": (synth.scaled(synth.CONV_NEQUIP, 300, 12_001), ("f32", "f64")),
+    "stream-small": (synth.scaled(synth.CONV_STREAM, 257, 9_001), ("f32", "f64")),
+    "mace-small": (synth.scaled(synth.CONV_MACE, 97, 2_999), ("f32", "f64")),
+    "mixed-mul": (synth.ConvSpec("mixed", 61, 1_777, "5x0e+3x1o+7x2e+2x3o", 3, 3), ("f32", "f64")),
+    "mul4": (synth.ConvSpec("mul4", 53, 1_201, "4x0e+4x1o", 2, 2), ("f32",)),
+    "mul80": (synth.ConvSpec("mul80", 41, 997, "80x0e+80x1o", 1, 1), ("f32",)),
+}
+CASES = [(k, d) for k, (_, ds) in SMALL.items() for d in ds]
+
+
+def run_gpu(case, device, need=(True, True, True)):
+    import torch
+    plan = cg.plan_for(case.spec, case.dtype)
+    d = to_device(case, device)
+    y = cg.spherical_harmonics(case.spec.lmax_sh, d["vec"])
+    out = cg.conv_forward(plan, d["row_ptr"], d["col"], d["x"], y, d["w"])
+    tr = cg.graph_transpose(d["row_ptr"], d["col"])
+    grads = cg.conv_backward(plan, d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"], need=need)
+    torch.cuda.synchronize()
+    return d, y, out, tr, grads
+
+
+@pytest.mark.parametrize("lmax", range(8))
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_spherical_harmonics(device, lmax, dtype):
+    import torch
+    vec = synth.normal(synth.streams(lmax)["vec"], (4099, 3), dtype=np.float32 if dtype == "f32" else np.float64)
+    got = cg.spherical_harmonics(lmax, torch.from_numpy(vec).to(device)).cpu().numpy()
+    want = osh.real_sh_all(lmax, vec.astype(np.float64))
+    assert rel_l2(got, want) <= TOL[dtype]
+    assert np.abs(got - want).max() <= (1e-5 if dtype == "f32" else 1e-12) * max(1, lmax)
+
+
+@pytest.mark.parametrize("kind", ["uniform", "empty", "heavy", "isolated", "selfdup"])
+def test_transpose_bit_exact(device, kind):
+    import torch
+    rng = np.random.default_rng(3)
+    if kind == "uniform":
+        row_ptr, col = synth.uniform_graph(1000, 40_000, rng)
+    else:
+        row_ptr, col = edge_case_graph(kind, 700, rng)
+    t = lambda a: torch.from_numpy(a).to(device)
+    trp, te, td = (a.cpu().numpy() for a in cg.graph_transpose(t(row_ptr), t(col)))
+    order = np.argsort(col, kind="stable")
+    want_ptr = np.concatenate([[0], np.cumsum(np.bincount(col, minlength=len(row_ptr) - 1))])
+    dst = np.repeat(np.arange(len(row_ptr) - 1), np.diff(row_ptr))
+    assert np.array_equal(trp, want_ptr)
+    assert np.array_equal(te, order)
+    assert np.array_equal(td, dst[order])
+
+
+@pytest.mark.parametrize("name,dtype", CASES)
+def test_conv_forward_backward_small(device, name, dtype):
+    spec = SMALL[name][0]
+    case = ConvCase(spec, dtype, seed=1)
+    d, y, out, tr, (gx, gy, gw) = run_gpu(case, device)
+    assert rel_l2(y.cpu().numpy(), case.y_oracle()) <= TOL[dtype]
+    assert rel_l2(out.cpu().numpy(), case.oracle_forward()) <= TOL[dtype]
+    dx, eidx, dy, dw = case.oracle_backward()
+    assert np.array_equal(eidx, np.arange(case.E))
+    assert rel_l2(gx.cpu().numpy(), dx) <= TOL[dtype]
+    assert rel_l2(gy.cpu().numpy(), dy) <= TOL[dtype]
+    assert rel_l2(gw.cpu().numpy(), dw) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("kind", ["empty", "heavy", "isolated", "selfdup"])
+def test_conv_edge_cases(device, kind):
+    spec = synth.ConvSpec("edge-" + kind, 700, 0, "32x0e+32x1o+32x2e", 2, 2)
+    graph = edge_case_graph(kind, 700, np.random.default_rng(5))
+    case = ConvCase(spec, "f32", seed=2, graph=graph)
+    d, y, out, tr, (gx, gy, gw) = run_gpu(case, device)
+    out_h = out.cpu().numpy()
+    want = case.oracle_forward()
+    deg = np.diff(case.row_ptr)
+    assert np.all(out_h[deg == 0] == 0)
+    if case.E == 0:
+        assert np.all(out_h == 0) and np.all(gx.cpu().numpy() == 0)
+        return
+    assert rel_l2(out_h, want) <= TOL["f32"]
+    dx, eidx, dy, dw = case.oracle_backward()
+    assert rel_l2(gx.cpu().numpy(), dx) <= TOL["f32"]
+    assert rel_l2(gy.cpu().numpy(), dy) <= TOL["f32"]
+    assert rel_l2(gw.cpu().numpy(), dw) <= TOL["f32"]
+
+
+def test_backward_optional_outputs(device):
+    import torch
+    case = ConvCase(synth.scaled(synth.CONV_NEQUIP, 100, 3_000), "f32", seed=4)
+    d, y, out, tr, full = run_gpu(case, device)
+    for need in [(True, False, False), (False, True, False), (False, False, True)]:
+        part = cg.conv_backward(cg.plan_for(case.spec, "f32"), d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"],
+                                need=need)
+        torch.cuda.synchronize()
+        for a, b, n in zip(full, part, need):
+            if n:
+                assert torch.equal(a, b)
+            else:
+                assert b is None
+
+
+def test_determinism_bitwise(device):
+    import torch
+    case = ConvCase(synth.scaled(synth.CONV_NEQUIP, 400, 20_000), "f32", seed=6)
+    r1 = run_gpu(case, device)
+    r2 = run_gpu(case, device)
+    assert torch.equal(r1[2], r2[2])
+    for a, b in zip(r1[4], r2[4]):
+        assert torch.equal(a, b)
+
+
+def test_no_device_allocation(device):
+    """The library allocates nothing: with caller-owned outputs memory_allocated is unchanged."""
+    import torch
+    case = ConvCase(synth.scaled(synth.CONV_NEQUIP, 200, 8_000), "f32", seed=7)
+    plan = cg.plan_for(case.spec, "f32")
+    d = to_device(case, device)
+    y = torch.empty((case.E, plan.d_sh), dtype=torch.float32, device=device)
+    out = torch.empty((case.N, plan.d_out), dtype=torch.float32, device=device)
+    tr = (torch.empty(case.N + 1, dtype=torch.int32, device=device),
+          torch.empty(case.E, dtype=torch.int32, device=device), torch.empty(case.E, dtype=torch.int32, device=device))
+    gx, gy, gw = torch.empty_like(d["x"]), torch.empty_like(y), torch.empty_like(d["w"])
+
+    def calls():
+        cg.spherical_harmonics(2, d["vec"], out=y)
+        cg.conv_forward(plan, d["row_ptr"], d["col"], d["x"], y, d["w"], out=out)
+        cg.graph_transpose(d["row_ptr"], d["col"], *tr)
+        cg.conv_backward(plan, d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"], gx, gy, gw)
+
+    calls()  # first call on the device loads the plan's code object
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated(device)
+    free_before = torch.cuda.mem_get_info(device)[0]
+    for _ in range(3):
+        calls()
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated(device) == before
+    assert torch.cuda.mem_get_info(device)[0] >= free_before - (2 << 20)
+
+
+# --------------------------------------------------------------------------- batched product
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("in_irreps,lmax,B", [("4x0e+4x1o", 2, 1024), ("32x0e+32x1o+32x2e", 2, 777),
+                                              ("5x0e+3x1o+7x2e+2x3o", 3, 301)])
+def test_tp_forward_uvu(device, dtype, in_irreps, lmax, B):
+    import torch
+    out_ir = oirreps.per_path_out_irreps(in_irreps, lmax, lmax)
+    prob = oirreps.build_problem(in_irreps, oirreps.sh_irreps(lmax), out_ir, "uvu")
+    plan = cg.plan_create(in_irreps, oirreps.sh_irreps(lmax), out_ir, "uvu", dtype)
+    st = synth.streams(11)
+    npdt = np.float32 if dtype == "f32" else np.float64
+    x = synth.normal(st["x"], (B, prob.d_in), dtype=npdt)
+    vec = synth.normal(st["vec"], (B, 3), dtype=npdt)
+    w = synth.normal(st["w"], (B, prob.weight_numel), dtype=npdt)
+    t = lambda a: torch.from_numpy(a).to(device)
+    y = cg.spherical_harmonics(lmax, t(vec))
+    out = cg.tp_forward(plan, t(x), y, t(w)).cpu().numpy()
+    want = ref.tp_forward(prob, x, osh.real_sh_all(lmax, vec.astype(np.float64)), w)
+    assert rel_l2(out, want) <= TOL[dtype]
