@@ -36,7 +36,21 @@ def parse():
     ap.add_argument("--dtype", default="f32", choices=["f32", "f64"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (calibrates the HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_probe():
+    """A plain copy of known size: 1 GiB read + 1 GiB written per launch, 5 launches."""
+    import torch
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read_per_launch": a.numel() * 4,
+                      "copy_probe_bytes_written_per_launch": b.numel() * 4, "launches": 5}), flush=True)
 
 
 def algorithmic_bytes(plan, N, E, es):
@@ -133,6 +147,9 @@ def main():
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if a.copy_probe:
+        copy_probe()
+        return
     import torch
     from clebsch_gordan_tensor_cgtp_amd import binding as cg
     from clebsch_gordan_tensor_cgtp_amd import synth

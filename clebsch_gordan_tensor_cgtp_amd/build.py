@@ -18,6 +18,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libcgtp.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
+ROCM_INC = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "include")
 GPU_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
@@ -26,17 +27,41 @@ def sources():
     return sorted(glob.glob(os.path.join(csrc, "*.cpp"))) + sorted(glob.glob(os.path.join(csrc, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, "-O2", "-std=c++17", "-fPIC", "-shared", *GPU_FLAGS,
-           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           *sources(), "-lhiprtc", "-ldl", "-o", tmp]
+def _compile(args):
+    cmd, verbose = args
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libcgtp.so")
+    return r.returncode, r.stdout + r.stderr
+
+
+def build(verbose: bool = False) -> str:
+    """Host C++ sources are compiled as plain C++, the .hip sources for gfx950; then linked."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+    jobs, objs = [], []
+    for src in sources():
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        if src.endswith(".hip"):
+            cmd = [HIPCC, "-O2", "-std=c++17", "-fPIC", *GPU_FLAGS, *inc, "-c", src, "-o", obj]
+        else:
+            cmd = [HIPCC, "-O2", "-std=c++17", "-fPIC", "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", ROCM_INC, *inc, "-c", src,
+                   "-o", obj]
+        jobs.append((cmd, verbose))
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        for rc, log in ex.map(_compile, jobs):
+            if rc != 0:
+                sys.stderr.write(log)
+                raise RuntimeError("hipcc failed building libcgtp.so")
+    tmp = LIB + f".tmp{os.getpid()}"
+    rc, log = _compile(([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-lhiprtc", "-ldl", "-o", tmp],
+                        verbose))
+    if rc != 0:
+        sys.stderr.write(log)
+        raise RuntimeError("linking libcgtp.so failed")
     os.replace(tmp, LIB)
     return LIB
 

@@ -3,7 +3,10 @@
 // asynchronously on the caller's stream; nothing is allocated on the device.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <climits>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <memory>
 #include <string>
@@ -108,6 +111,20 @@ cgtp_status cgtp_plan_create(const char *in_irreps, const char *sh_irreps, const
         cgtp::schedule(P);
         P.source = cgtp::generate_source(P);
         cgtp::compile_module(P);
+        if (const char *log = std::getenv("CGTP_LOG"); log && *log && *log != '0') {
+            std::fprintf(stderr, "[cgtp] plan: %zu paths, %d nnz, d_x=%d d_sh=%d d_out=%d, module %zu bytes\n",
+                         P.paths.size(), P.nnz_total, P.d_x, P.d_sh, P.d_out, P.code.size());
+            for (size_t k = 0; k < P.fwd_groups.size(); ++k)
+                std::fprintf(stderr, "[cgtp]   fwd group %zu: %zu paths, mul %d, ct %d, tiles %d\n", k,
+                             P.fwd_groups[k].paths.size(), P.fwd_groups[k].mul, P.fwd_groups[k].ct,
+                             P.fwd_groups[k].tiles);
+            for (size_t k = 0; k < P.bwd_groups.size(); ++k)
+                std::fprintf(stderr, "[cgtp]   bwd group %zu: %zu paths, mul %d, ct %d, tiles %d, prefetch %d\n", k,
+                             P.bwd_groups[k].paths.size(), P.bwd_groups[k].mul, P.bwd_groups[k].ct,
+                             P.bwd_groups[k].tiles, (int)P.bwd_groups[k].prefetch);
+            std::fprintf(stderr, "[cgtp]   waves/SIMD targets: fwd %d, bwd %d\n", P.fwd_waves_per_eu,
+                         P.bwd_waves_per_eu);
+        }
         *plan_out = h.release();
     });
 }
@@ -318,8 +335,18 @@ cgtp_status cgtp_conv_backward(const cgtp_plan *plan, int64_t N, int64_t E, cons
         // with E == 0 the kernel still runs: every sender has an empty row and writes zeros to grad_x
         const auto &L = cgtp::module_for_current_device(P);
         long nnodes = (long)N;
-        void *args[] = {&t_row_ptr, &t_edge, &t_dst, &x, &y, &w, &grad_out, &grad_x, &grad_y, &grad_w, &nnodes};
-        launch(L.conv_bwd, N, args, stream);
+        // waves per sender: split the sender's edges when the mean out-degree leaves enough
+        // edge groups per wave (the dx partials are then summed in a fixed order in LDS)
+        for (int grp = 0; grp < (int)P.bwd_groups.size(); ++grp) {
+            const double groups = (double)E / (double)N / P.bwd_groups[grp].es;
+            int wpr = groups >= 16 ? 4 : groups >= 8 ? 2 : 1;
+            if (const char *env = std::getenv("CGTP_BWD_WPR")) wpr = std::max(1, std::min(4, std::atoi(env)));
+            void *args[] = {&t_row_ptr, &t_edge, &t_dst, &x, &y, &w, &grad_out, &grad_x, &grad_y, &grad_w,
+                            &nnodes, &wpr, &grp};
+            check_hip(hipModuleLaunchKernel(L.conv_bwd, (unsigned)N, 1, 1, 64 * wpr, 1, 1, 0,
+                                            static_cast<hipStream_t>(stream), args, nullptr),
+                      "hipModuleLaunchKernel");
+        }
     });
 }
 

@@ -238,17 +238,23 @@ void emit_fwd_group(Out &o, const Plan &P, int gi, bool rows)
         o("const int e0 = row_ptr[n], e1 = row_ptr[n + 1];");
         o("if (e0 < e1) {");
         o.ind++;
+        // pipeline: senders (col) two edge groups ahead, operands one ahead, so
+        // every wait is for loads issued a whole iteration earlier
         o("int e = e0 + slot;");
         o("int ec = e < e1 ? e : e1 - 1;");
         o("int s = col[ec];");
+        o("int en = (e + ", g.es, " < e1) ? e + ", g.es, " : e1 - 1;");
+        o("int sn = col[en];");
         emit_edge_loads(o, P, g, t, "c", "s", "ec", true);
         o("for (; e < e1; e += ", g.es, ") {");
         o.ind++;
-        o("const int en = (e + ", g.es, " < e1) ? e + ", g.es, " : e1 - 1;");
-        o("const int sn = col[en];");
+        o("const int enn = (e + ", 2 * g.es, " < e1) ? e + ", 2 * g.es, " : e1 - 1;");
+        o("const int snn = col[enn];");
         emit_edge_loads(o, P, g, t, "n", "sn", "en", true);
         emit_forward_math(o, P, g, f64, "c");
         emit_copy(o, P, g, t, "c", "n");
+        o("en = enn;");
+        o("sn = snn;");
         o.ind--;
         o("}");
         o.ind--;
@@ -309,34 +315,89 @@ void emit_fwd_kernel(Out &o, const Plan &P, bool rows)
 // ------------------------------------------------------------------------------------------
 // Backward, sender pass.
 
-void emit_bwd_kernel(Out &o, const Plan &P)
+// Sum over the CT channel lanes of one edge slot; every lane of the slot ends
+// with the same bits (each butterfly step adds the same two operands).
+void emit_slot_sum(Out &o, const Plan &P)
 {
-    const Group &g = P.bwd_group;
     const bool f64 = P.dtype == CGTP_F64;
-    Touch t = touched(P, g.paths);
-    o("extern \"C\" __global__ void __launch_bounds__(256, ", P.bwd_waves_per_eu, ") cgtp_conv_bwd(const int* __restrict__ t_row_ptr, "
-      "const int* __restrict__ t_edge, const int* __restrict__ t_dst, const T* __restrict__ x, "
-      "const T* __restrict__ y, const T* __restrict__ w, const T* __restrict__ g, T* __restrict__ dx, "
-      "T* __restrict__ dy, T* __restrict__ dw, long nnodes)");
+    o("template <int CT> __device__ __forceinline__ T slot_sum(T v)");
     o("{");
     o.ind++;
-    o("const long s = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
-    o("const int lane = threadIdx.x & 63;");
-    o("if (s >= nnodes) return;");
+    const int ctrls[4] = {0xB1, 0x4E, 0x141, 0x140};  // xor1, xor2, half-row mirror, row mirror
+    for (int st = 0, m = 2; st < 4; ++st, m *= 2) {
+        o("if constexpr (CT >= ", m, ") {");
+        o.ind++;
+        if (f64) {
+            o("long long b = __builtin_bit_cast(long long, v);");
+            o("int lo = __builtin_amdgcn_mov_dpp((int)b, ", ctrls[st], ", 15, 15, false);");
+            o("int hi = __builtin_amdgcn_mov_dpp((int)(b >> 32), ", ctrls[st], ", 15, 15, false);");
+            o("v += __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned)lo);");
+        } else {
+            o("v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ", ctrls[st],
+              ", 15, 15, false));");
+        }
+        o.ind--;
+        o("}");
+    }
+    o("if constexpr (CT >= 32) v += __shfl_xor(v, 16);");
+    o("if constexpr (CT >= 64) v += __shfl_xor(v, 32);");
+    o("return v;");
+    o.ind--;
+    o("}");
+    o("");
+}
+
+// Backward, sender pass, one path group (see the file comment).  dx blocks
+// and dY blocks are written by the first group that touches them (group 0 also
+// writes zeros for blocks no path touches) and accumulated by later groups;
+// the groups are separate launches in group order, so the sums are fixed.
+void emit_bwd_group(Out &o, const Plan &P, int gi)
+{
+    const Group &g = P.bwd_groups[gi];
+    const bool f64 = P.dtype == CGTP_F64;
+    const bool pf = g.prefetch;
+    Touch t = touched(P, g.paths);
+    // first group (in launch order) touching each input / SH block
+    auto first_i1 = [&](int b) {
+        for (int k = 0; k < (int)P.bwd_groups.size(); ++k)
+            for (int pi : P.bwd_groups[k].paths)
+                if (P.paths[pi].i1 == b) return k;
+        return -1;
+    };
+    auto first_i2 = [&](int b) {
+        for (int k = 0; k < (int)P.bwd_groups.size(); ++k)
+            for (int pi : P.bwd_groups[k].paths)
+                if (P.paths[pi].i2 == b) return k;
+        return -1;
+    };
+    std::vector<int> xb;  // input blocks this group writes or adds
+    for (int b = 0; b < (int)P.ins.size(); ++b)
+        if (t.i1.count(b) || (gi == 0 && first_i1(b) < 0)) xb.push_back(b);
+    int nx = 0;
+    for (int b : xb) nx += n_of(P.ins[b].l);
+    std::vector<int> yb;  // SH blocks this group writes or adds
+    for (int b = 0; b < (int)P.sh.size(); ++b)
+        if (t.i2.count(b) || (gi == 0 && first_i2(b) < 0)) yb.push_back(b);
+
+    o("__device__ __forceinline__ void bwd_g", gi,
+      "(long s, int wv, int lane, int wpr, T* red, const int* __restrict__ t_row_ptr, const int* __restrict__ t_edge, "
+      "const int* __restrict__ t_dst, const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, "
+      "const T* __restrict__ g, T* __restrict__ dx, T* __restrict__ dy, T* __restrict__ dw)");
+    o("{");
+    o.ind++;
     o("const int slot = lane >> ", log2i(g.ct), ";");
     o("const int ul = lane & ", g.ct - 1, ";");
     o("const int t0 = t_row_ptr[s], t1 = t_row_ptr[s + 1];");
+    o("const int stride = ", g.es, " * wpr;");
     o("for (int tile = 0; tile < ", g.tiles, "; ++tile) {");
     o.ind++;
     o("const int u = tile * ", g.ct, " + ul;");
-    // every input block: x values (zero for blocks without a path) and dx accumulators
-    for (int b = 0; b < (int)P.ins.size(); ++b) {
+    for (int b : xb) {
         const Irrep &ir = P.ins[b];
         int off = 0;
         for (int bb = 0; bb < b; ++bb) off += P.ins[bb].dim();
-        bool used = t.i1.count(b) > 0;
         for (int i = 0; i < n_of(ir.l); ++i) {
-            if (used) {
+            if (t.i1.count(b)) {
                 std::string addr = "x[(size_t)s * DX + " + std::to_string(off) + " + u * " + std::to_string(n_of(ir.l)) +
                                    " + " + std::to_string(i) + "]";
                 if (needs_mask(ir.mul, g))
@@ -347,41 +408,55 @@ void emit_bwd_kernel(Out &o, const Plan &P)
             o("T d", b, "_", i, " = (T)0;");
         }
     }
-    o("for (int t = t0 + slot; t < t1; t += ", g.es, ") {");
-    o.ind++;
-    o("const int e = t_edge[t];");
-    o("const int n = t_dst[t];");
-    for (int b = 0; b < (int)P.sh.size(); ++b) {
-        int off = 0;
-        for (int bb = 0; bb < b; ++bb) off += P.sh[bb].dim();
-        for (int j = 0; j < n_of(P.sh[b].l); ++j) {
-            if (t.i2.count(b))
-                o("const T y", b, "_", j, " = __builtin_nontemporal_load(&y[(size_t)e * DSH + ", off + j, "]);");
-            o("T h", b, "_", j, " = (T)0;");  // dF/dy partial of this lane
+    auto edge_loads = [&](const std::string &pre, const std::string &ev, const std::string &nv, bool declare) {
+        const std::string Ty = declare ? "T " : "";
+        for (int b : t.i2) {
+            int off = 0;
+            for (int bb = 0; bb < b; ++bb) off += P.sh[bb].dim();
+            for (int j = 0; j < n_of(P.sh[b].l); ++j)
+                o(Ty, pre, "y", b, "_", j, " = __builtin_nontemporal_load(&y[(size_t)", ev, " * DSH + ", off + j, "]);");
         }
-    }
-    for (int pi : g.paths) {
-        const Path &p = P.paths[pi];
-        std::string wa = "__builtin_nontemporal_load(&w[(size_t)e * WROW + " + std::to_string(p.w_off) + " + u])";
-        if (needs_mask(p.mul_in, g))
-            o("const T w", pi, " = (u < ", p.mul_in, ") ? ", wa, " : (T)0;");
-        else
-            o("const T w", pi, " = ", wa, ";");
-    }
-    // g rows of every slot
-    for (int q : t.slots) {
-        const Irrep &ir = P.out[q];
-        int off = 0;
-        for (int qq = 0; qq < q; ++qq) off += P.out[qq].dim();
-        for (int k = 0; k < n_of(ir.l); ++k) {
-            std::string ga = "g[(size_t)n * DOUT + " + std::to_string(off) + " + u * " + std::to_string(n_of(ir.l)) +
-                             " + " + std::to_string(k) + "]";
-            if (needs_mask(ir.mul, g))
-                o("const T g", q, "_", k, " = (u < ", ir.mul, ") ? ", ga, " : (T)0;");
+        for (int pi : g.paths) {
+            const Path &p = P.paths[pi];
+            std::string wa = "__builtin_nontemporal_load(&w[(size_t)" + ev + " * WROW + " + std::to_string(p.w_off) + " + u])";
+            if (needs_mask(p.mul_in, g))
+                o(Ty, pre, "w", pi, " = (u < ", p.mul_in, ") ? ", wa, " : (T)0;");
             else
-                o("const T g", q, "_", k, " = ", ga, ";");
+                o(Ty, pre, "w", pi, " = ", wa, ";");
         }
-    }
+        for (int q : t.slots) {
+            const Irrep &ir = P.out[q];
+            int off = 0;
+            for (int qq = 0; qq < q; ++qq) off += P.out[qq].dim();
+            for (int k = 0; k < n_of(ir.l); ++k) {
+                std::string ga = "g[(size_t)" + nv + " * DOUT + " + std::to_string(off) + " + u * " +
+                                 std::to_string(n_of(ir.l)) + " + " + std::to_string(k) + "]";
+                if (needs_mask(ir.mul, g))
+                    o(Ty, pre, "g", q, "_", k, " = (u < ", ir.mul, ") ? ", ga, " : (T)0;");
+                else
+                    o(Ty, pre, "g", q, "_", k, " = ", ga, ";");
+            }
+        }
+    };
+    // pipeline: edge and receiver ids two iterations ahead, operands one ahead
+    // (with prefetch) so every wait is for loads issued an iteration earlier
+    o("int t = t0 + wv * ", g.es, " + slot;");
+    o("if (t < t1) {");
+    o.ind++;
+    o("int e = t_edge[t], n = t_dst[t];");
+    o("int tn = (t + stride < t1) ? t + stride : t;");
+    o("int en = t_edge[tn], nn = t_dst[tn];");
+    if (pf) edge_loads("", "e", "n", true);
+    o("for (; t < t1; t += stride) {");
+    o.ind++;
+    o("const int tnn = (t + 2 * stride < t1) ? t + 2 * stride : tn;");
+    o("const int enn = t_edge[tnn], nnn = t_dst[tnn];");
+    if (pf)
+        edge_loads("n", "en", "nn", true);
+    else
+        edge_loads("", "e", "n", true);
+    for (int b : yb)
+        for (int j = 0; j < n_of(P.sh[b].l); ++j) o("T h", b, "_", j, " = (T)0;");  // dF/dy partial of this lane
     for (int pi : g.paths) {
         const Path &p = P.paths[pi];
         // B_ij = sum_k C_ijk g_k
@@ -428,8 +503,8 @@ void emit_bwd_kernel(Out &o, const Plan &P)
             }
             o("const T fy", kv.first, " = ", e.str(), ";");
         }
-        // dW = sum_i x_i dF/dx_i
         {
+            // dW = sum_i x_i dF/dx_i
             std::ostringstream e;
             bool first = true;
             for (auto &kv : rows) {
@@ -443,66 +518,165 @@ void emit_bwd_kernel(Out &o, const Plan &P)
                 }
             }
             std::string guard = needs_mask(p.mul_in, g) ? "(u < " + std::to_string(p.mul_in) + ") && " : "";
-            o("if (", guard, "dw) dw[(size_t)e * WROW + ", p.w_off, " + u] = ", e.str(), ";");
+            o("if (", guard, "dw) __builtin_nontemporal_store(", e.str(), ", &dw[(size_t)e * WROW + ", p.w_off, " + u]);");
         }
         for (auto &kv : rows) o("d", p.i1, "_", kv.first, " = FMA(w", pi, ", fx", kv.first, ", d", p.i1, "_", kv.first, ");");
         for (auto &kv : cols) o("h", p.i2, "_", kv.first, " = FMA(w", pi, ", fy", kv.first, ", h", p.i2, "_", kv.first, ");");
         o.ind--;
         o("}");
     }
-    // dY: butterfly over the slot's channel lanes, then lane (j mod ct) of the slot writes j
+    // dY: sum over the slot's channel lanes; lane (j mod ct) of the slot writes or adds j
     o("if (dy) {");
     o.ind++;
-    int j = 0;
-    std::vector<std::string> hs;
-    for (int b = 0; b < (int)P.sh.size(); ++b)
-        for (int jj = 0; jj < n_of(P.sh[b].l); ++jj) hs.push_back("h" + std::to_string(b) + "_" + std::to_string(jj));
-    for (auto &h : hs)
-        for (int m = g.ct / 2; m >= 1; m /= 2) o(h, " += __shfl_xor(", h, ", ", m, ");");
-    int per = (P.d_sh + g.ct - 1) / g.ct;
-    for (int r = 0; r < per; ++r) {
-        o("{");
-        o.ind++;
-        o("T v = (T)0;");
-        bool any = false;
-        for (j = r * g.ct; j < std::min(P.d_sh, (r + 1) * g.ct); ++j) {
-            o("if (ul == ", j - r * g.ct, ") v = ", hs[j], ";");
-            any = true;
-        }
-        if (any) {
-            o("const int jj = ", r * g.ct, " + ul;");
-            o("if (jj < DSH) {");
+    std::vector<std::pair<int, std::string>> hs;  // (column, register)
+    for (int b : yb) {
+        int off = 0;
+        for (int bb = 0; bb < b; ++bb) off += P.sh[bb].dim();
+        for (int jj = 0; jj < n_of(P.sh[b].l); ++jj)
+            hs.push_back({off + jj, "h" + std::to_string(b) + "_" + std::to_string(jj)});
+    }
+    for (auto &h : hs) o(h.second, " = slot_sum<", g.ct, ">(", h.second, ");");
+    for (size_t r = 0; r * g.ct < hs.size(); ++r) {
+        const size_t lo = r * g.ct, hi = std::min(hs.size(), (r + 1) * g.ct);
+        // split the chunk by write/add kind of the block its column belongs to
+        for (int add = 0; add < 2; ++add) {
+            std::vector<std::pair<size_t, int>> sel;  // (lane, column)
+            for (size_t c = lo; c < hi; ++c) {
+                int col = hs[c].first;
+                int blk = 0, acc = 0;
+                for (int b = 0; b < (int)P.sh.size(); ++b) {
+                    if (col < acc + P.sh[b].dim()) { blk = b; break; }
+                    acc += P.sh[b].dim();
+                }
+                bool is_add = first_i2(blk) >= 0 && first_i2(blk) < gi;
+                if ((int)is_add == add) sel.push_back({c - lo, col});
+            }
+            if (sel.empty()) continue;
+            o("{");
             o.ind++;
-            o("T* p = &dy[(size_t)e * DSH + jj];");
-            o("if (tile == 0) *p = v; else *p += v;");
+            o("T v = (T)0;");
+            o("int col = -1;");
+            for (auto &sc : sel) o("if (ul == ", sc.first, ") { v = ", hs[lo + sc.first].second, "; col = ", sc.second, "; }");
+            o("if (col >= 0) {");
+            o.ind++;
+            o("T* p = &dy[(size_t)e * DSH + col];");
+            if (add)
+                o("*p += v;");
+            else
+                o("if (tile == 0) *p = v; else *p += v;");
+            o.ind--;
+            o("}");
             o.ind--;
             o("}");
         }
-        o.ind--;
-        o("}");
+    }
+    o.ind--;
+    o("}");
+    if (P.bwd_sched_barrier) o("__builtin_amdgcn_sched_barrier(0);");
+    if (pf) {
+        for (int b : t.i2)
+            for (int j = 0; j < n_of(P.sh[b].l); ++j) o("y", b, "_", j, " = ny", b, "_", j, ";");
+        for (int pi : g.paths) o("w", pi, " = nw", pi, ";");
+        for (int q : t.slots)
+            for (int k = 0; k < n_of(P.out[q].l); ++k) o("g", q, "_", k, " = ng", q, "_", k, ";");
+    }
+    o("e = en;");
+    o("n = nn;");
+    o("en = enn;");
+    o("nn = nnn;");
+    o("tn = tnn;");
+    o.ind--;
+    o("}");  // edge loop
+    o.ind--;
+    o("}");  // t < t1
+    // sum the edge slots of the wave, then the waves of the workgroup (fixed order)
+    for (int m = 32; m >= g.ct; m /= 2)
+        for (int b : xb)
+            for (int i = 0; i < n_of(P.ins[b].l); ++i) o("d", b, "_", i, " += __shfl_xor(d", b, "_", i, ", ", m, ");");
+    o("if (wpr > 1) {");
+    o.ind++;
+    o("if (wv > 0 && slot == 0) {");
+    o.ind++;
+    {
+        int r = 0;
+        for (int b : xb)
+            for (int i = 0; i < n_of(P.ins[b].l); ++i, ++r)
+                o("red[(wv - 1) * ", nx * g.ct, " + ", r * g.ct, " + ul] = d", b, "_", i, ";");
+    }
+    o.ind--;
+    o("}");
+    o("__syncthreads();");
+    o("if (wv == 0) {");
+    o.ind++;
+    o("for (int v = 1; v < wpr; ++v) {");
+    o.ind++;
+    {
+        int r = 0;
+        for (int b : xb)
+            for (int i = 0; i < n_of(P.ins[b].l); ++i, ++r)
+                o("d", b, "_", i, " += red[(v - 1) * ", nx * g.ct, " + ", r * g.ct, " + ul];");
     }
     o.ind--;
     o("}");
     o.ind--;
-    o("}");  // edge loop
-    // sum the edge slots, write dx
-    for (int m = 32; m >= g.ct; m /= 2)
-        for (int b = 0; b < (int)P.ins.size(); ++b)
-            for (int i = 0; i < n_of(P.ins[b].l); ++i) o("d", b, "_", i, " += __shfl_xor(d", b, "_", i, ", ", m, ");");
-    o("if (dx && slot == 0) {");
+    o("}");
+    o("__syncthreads();");
+    o.ind--;
+    o("}");
+    o("if (dx && wv == 0 && slot == 0) {");
     o.ind++;
-    for (int b = 0; b < (int)P.ins.size(); ++b) {
+    for (int b : xb) {
         const Irrep &ir = P.ins[b];
         int off = 0;
         for (int bb = 0; bb < b; ++bb) off += P.ins[bb].dim();
+        bool add = first_i1(b) >= 0 && first_i1(b) < gi;
         std::string guard = needs_mask(ir.mul, g) ? "if (u < " + std::to_string(ir.mul) + ") " : "";
         for (int i = 0; i < n_of(ir.l); ++i)
-            o(guard, "dx[(size_t)s * DX + ", off, " + u * ", n_of(ir.l), " + ", i, "] = d", b, "_", i, ";");
+            o(guard, "dx[(size_t)s * DX + ", off, " + u * ", n_of(ir.l), " + ", i, "] ", add ? "+=" : "=", " d", b, "_", i,
+              ";");
     }
     o.ind--;
     o("}");
     o.ind--;
     o("}");  // tile loop
+    o.ind--;
+    o("}");
+    o("");
+}
+
+int bwd_red_size(const Plan &P)
+{
+    int m = 1;
+    for (const Group &g : P.bwd_groups) {
+        int nx = 0;
+        for (const Irrep &ir : P.ins) nx += n_of(ir.l);  // upper bound over the group's blocks
+        m = std::max(m, 3 * nx * g.ct);
+    }
+    return m;
+}
+
+void emit_bwd_kernel(Out &o, const Plan &P)
+{
+    emit_slot_sum(o, P);
+    for (int gi = 0; gi < (int)P.bwd_groups.size(); ++gi) emit_bwd_group(o, P, gi);
+    o("// one workgroup of 64*wpr threads per sender; `group` selects the path group (launched in order)");
+    o("extern \"C\" __global__ void __launch_bounds__(256, ", P.bwd_waves_per_eu,
+      ") cgtp_conv_bwd(const int* __restrict__ t_row_ptr, "
+      "const int* __restrict__ t_edge, const int* __restrict__ t_dst, const T* __restrict__ x, "
+      "const T* __restrict__ y, const T* __restrict__ w, const T* __restrict__ g, T* __restrict__ dx, "
+      "T* __restrict__ dy, T* __restrict__ dw, long nnodes, int wpr, int group)");
+    o("{");
+    o.ind++;
+    o("__shared__ T red[", bwd_red_size(P), "];  // partial dx of waves 1..3");
+    o("const long s = blockIdx.x;");
+    o("const int wv = threadIdx.x >> 6;");
+    o("const int lane = threadIdx.x & 63;");
+    o("if (s >= nnodes) return;");
+    o("switch (group) {");
+    for (int gi = 0; gi < (int)P.bwd_groups.size(); ++gi)
+        o("case ", gi, ": bwd_g", gi, "(s, wv, lane, wpr, red, t_row_ptr, t_edge, t_dst, x, y, w, g, dx, dy, dw); break;");
+    o("default: break;");
+    o("}");
     o.ind--;
     o("}");
     o("");

@@ -47,6 +47,7 @@ struct Group {
     int ct = 64;             // lanes per edge slot (power of two <= 64)
     int es = 1;              // edge slots per wave = 64 / ct
     int tiles = 1;           // channel tiles of width ct covering mul
+    bool prefetch = false;   // backward: double-buffer the next edge's operands in registers
 };
 
 struct Plan {
@@ -60,9 +61,12 @@ struct Plan {
 
     std::vector<Group> fwd_groups;  // forward: one wave per (receiver, group, tile)
     int fwd_tasks = 0;              // sum over groups of tiles
-    Group bwd_group;                // backward: one wave per sender covers every path
+    std::vector<Group> bwd_groups;  // backward: one launch per group, in order
     int fwd_waves_per_eu = 4;       // occupancy target given to the compiler (min waves per SIMD)
     int bwd_waves_per_eu = 4;
+    bool bwd_sched_barrier = true;  // keep path blocks of the backward from interleaving
+    int bwd_prefetch = -1;          // -1: per group by register estimate; 0/1 forced
+    bool fwd_split_inputs = false;  // forward groups follow input-irrep classes (measured slower)
     std::string source;             // generated HIP source
     std::vector<char> code;         // compiled gfx950 code object
 

@@ -18,6 +18,7 @@
 #include <cstdlib>
 #include <complex>
 #include <map>
+#include <set>
 #include <sstream>
 
 #include "plan.h"
@@ -232,11 +233,13 @@ void build_paths(Plan &P)
 }
 
 // ------------------------------------------------------------------------------------------
-// Work split.  Forward: output slots are packed greedily (in slot order, so
-// paths sharing an input block stay together) into groups whose accumulators
-// fit a register budget; each (receiver, group, channel tile) is one wave.
-// Backward: one group with every path (the sender pass keeps only the input
-// gradient resident, so it needs no split and no cross-wave reduction).
+// Work split.  Forward: output slots are grouped by the input blocks their
+// paths read (path-group parallelism, LunaTP page, Abstract), so each x
+// block is read by one group only; a class whose accumulators exceed the
+// register budget is split.  Each (receiver, group, channel tile) is one
+// wave.  Backward: one group with every path (the sender pass keeps only the
+// input gradient resident, so it needs no path split and each edge's dY is
+// complete inside one wave).
 
 static int lanes_for(int mul)
 {
@@ -254,29 +257,42 @@ static void finish_group(Group &g)
 
 void schedule(Plan &P)
 {
+    if (const char *e = std::getenv("CGTP_BWD_PREFETCH")) P.bwd_prefetch = std::atoi(e);
+    if (const char *e = std::getenv("CGTP_FWD_SPLIT_INPUTS")) P.fwd_split_inputs = std::atoi(e) != 0;
     const int word = P.dtype == CGTP_F64 ? 2 : 1;
     const int budget = 64;  // 32-bit registers per lane for the forward accumulators
     P.fwd_groups.clear();
     if (P.mode == CGTP_UVU) {
         std::vector<std::vector<int>> slot_paths(P.out.size());
         for (int i = 0; i < (int)P.paths.size(); ++i) slot_paths[P.paths[i].slot].push_back(i);
+        auto inputs_of = [&](int q) {
+            std::vector<int> v;
+            for (int i : slot_paths[q]) v.push_back(P.paths[i].i1);
+            std::sort(v.begin(), v.end());
+            v.erase(std::unique(v.begin(), v.end()), v.end());
+            return v;
+        };
         // slots in order of their first path, so input blocks stay together
         std::vector<int> order;
         for (int q = 0; q < (int)P.out.size(); ++q) order.push_back(q);
         std::stable_sort(order.begin(), order.end(),
                          [&](int a, int b) { return slot_paths[a].front() < slot_paths[b].front(); });
         Group cur;
+        std::vector<int> cur_inputs;
         int regs = 0;
         for (int q : order) {
             int need = word * (2 * P.out[q].l + 1);
             int mul = P.out[q].mul;
-            if (!cur.paths.empty() && (regs + need > budget || mul != cur.mul)) {
+            std::vector<int> ins = inputs_of(q);
+            if (!cur.paths.empty() &&
+                (regs + need > budget || mul != cur.mul || (P.fwd_split_inputs && ins != cur_inputs))) {
                 finish_group(cur);
                 P.fwd_groups.push_back(cur);
                 cur = Group();
                 regs = 0;
             }
             cur.mul = mul;
+            cur_inputs = ins;
             for (int i : slot_paths[q]) cur.paths.push_back(i);
             regs += need;
         }
@@ -289,22 +305,78 @@ void schedule(Plan &P)
     P.fwd_tasks = 0;
     for (const Group &g : P.fwd_groups) P.fwd_tasks += g.tiles;
 
-    Group b;
-    for (int i = 0; i < (int)P.paths.size(); ++i) {
-        b.paths.push_back(i);
-        b.mul = std::max(b.mul, P.paths[i].mul_in);
+    // Backward groups: paths sharing an SH block (so that block's dY is complete
+    // in one group), split when the register estimate exceeds the budget.
+    P.bwd_groups.clear();
+    {
+        auto nnz_b = [&](int pi) {
+            std::set<std::pair<int, int>> ij;
+            for (const Nonzero &z : P.paths[pi].nz) ij.insert({z.i, z.j});
+            return (int)ij.size();
+        };
+        auto estimate = [&](const std::vector<int> &ps, bool prefetch) {
+            std::set<int> i1s, i2s, slots;
+            int maxb = 0;
+            for (int pi : ps) {
+                i1s.insert(P.paths[pi].i1);
+                i2s.insert(P.paths[pi].i2);
+                slots.insert(P.paths[pi].slot);
+                maxb = std::max(maxb, nnz_b(pi) + 2 * P.paths[pi].l1 + 2 * P.paths[pi].l2 + 2);
+            }
+            int xs = 0, ys = 0, gs = 0;
+            for (int b : i1s) xs += 2 * P.ins[b].l + 1;
+            for (int b : i2s) ys += 2 * P.sh[b].l + 1;
+            for (int q : slots) gs += 2 * P.out[q].l + 1;
+            int edge = ys + (int)ps.size() + gs;
+            return word * (2 * xs + edge + ys + maxb + (prefetch ? edge : 0)) + 24;
+        };
+        // One group with every path is fastest when it fits (measured on the
+        // NequIP-like graph: fewer launches and index loads, the g row read in
+        // one pass); larger problems are split so that no group spills.
+        const int split_budget = 168;
+        std::vector<int> all_paths;
+        for (int i = 0; i < (int)P.paths.size(); ++i) all_paths.push_back(i);
+        bool split = estimate(all_paths, false) > 200;
+        if (const char *e = std::getenv("CGTP_BWD_SPLIT")) split = std::atoi(e) != 0;
+        if (!split) {
+            Group all;
+            for (int i = 0; i < (int)P.paths.size(); ++i) all.paths.push_back(i);
+            P.bwd_groups.push_back(all);
+        }
+        for (int b = 0; split && b < (int)P.sh.size(); ++b) {
+            Group cur;
+            for (int i = 0; i < (int)P.paths.size(); ++i) {
+                if (P.paths[i].i2 != b) continue;
+                std::vector<int> trial = cur.paths;
+                trial.push_back(i);
+                if (!cur.paths.empty() && estimate(trial, false) > split_budget) {
+                    P.bwd_groups.push_back(cur);
+                    cur = Group();
+                }
+                cur.paths.push_back(i);
+            }
+            if (!cur.paths.empty()) P.bwd_groups.push_back(cur);
+        }
+        int est_max = 0;
+        for (Group &g : P.bwd_groups) {
+            for (int pi : g.paths) g.mul = std::max(g.mul, P.paths[pi].mul_in);
+            finish_group(g);
+            // register double-buffering measured slower (it lowers occupancy and the
+            // backward is bound by outstanding L1 misses, not by issue latency)
+            g.prefetch = P.bwd_prefetch > 0;
+            est_max = std::max(est_max, estimate(g.paths, g.prefetch));
+        }
+        P.bwd_waves_per_eu = std::max(1, std::min(4, 512 * 4 / (5 * std::max(est_max, 1))));
     }
-    finish_group(b);
-    P.bwd_group = b;
 
     // Occupancy targets: 4 waves per SIMD (<= 128 VGPRs) keeps enough loads in
-    // flight to cover HBM latency in the forward; the backward holds a whole g
-    // row per edge and gets 2; fp64 doubles the register need of the same code
-    // and halves both.  CGTP_FWD_WAVES / CGTP_BWD_WAVES override (tuning).
+    // flight to cover HBM latency in the forward (fp64 doubles the register
+    // need and gets 2); the backward target follows its register estimate.
+    // CGTP_FWD_WAVES / CGTP_BWD_WAVES override (tuning).
     P.fwd_waves_per_eu = P.dtype == CGTP_F64 ? 2 : 4;
-    P.bwd_waves_per_eu = P.dtype == CGTP_F64 ? 1 : 2;
     if (const char *e = std::getenv("CGTP_FWD_WAVES")) P.fwd_waves_per_eu = std::max(1, std::atoi(e));
     if (const char *e = std::getenv("CGTP_BWD_WAVES")) P.bwd_waves_per_eu = std::max(1, std::atoi(e));
+    if (const char *e = std::getenv("CGTP_BWD_SCHED_BARRIER")) P.bwd_sched_barrier = std::atoi(e) != 0;
 }
 
 }  // namespace cgtp
