@@ -32,7 +32,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c5"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--dtype", default="f32", choices=["f32", "f64"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seed", type=int, default=0)
@@ -142,6 +142,63 @@ def cpu_baseline(spec, seed, host_graph, max_seconds=30.0):
                       f"mean of {reps} rep(s)"}
 
 
+def tp_flops(plan_paths, mul, mode):
+    """Counting convention: uvw per row sum_p [2 mul nnz_p + 2 mul_in mul_out (2l3+1)] (+ nnz_p);
+    uvu per row sum_p [mul (2 nnz_p + 2 (2l3+1)) + nnz_p]."""
+    f = 0
+    for p in plan_paths:
+        n3 = 2 * p["l3"] + 1
+        if mode == "uvw":
+            f += 2 * p["mul_in"] * p["nnz"] + 2 * p["mul_in"] * p["mul_out"] * n3 + p["nnz"]
+        else:
+            f += p["mul_in"] * (2 * p["nnz"] + 2 * n3) + p["nnz"]
+    return f
+
+
+def bench_tp(a, spec, device):
+    """Batched tensor product workloads: one step = one cgtp_tp_forward over the batch."""
+    import torch
+    from clebsch_gordan_tensor_cgtp_amd import binding as cg
+    from clebsch_gordan_tensor_cgtp_amd import synth
+    plan = cg.plan_for(spec, a.dtype)
+    st = synth.streams(a.seed)
+    npdt = np.float32 if a.dtype == "f32" else np.float64
+    B = spec.batch
+    x = torch.from_numpy(synth.normal(st["x"], (B, plan.d_x), dtype=npdt)).to(device)
+    vec = torch.from_numpy(synth.normal(st["vec"], (B, 3), dtype=npdt)).to(device)
+    wshape = (plan.weight_numel,) if spec.mode == "uvw" else (B, plan.weight_numel)
+    w = torch.from_numpy(synth.normal(st["w"], wshape, 0.25, dtype=npdt)).to(device)
+    y = cg.spherical_harmonics(spec.lmax_sh, vec)
+    out = torch.empty((B, plan.d_out), dtype=plan.torch_dtype, device=device)
+    for _ in range(a.warmup):
+        cg.tp_forward(plan, x, y, w, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(a.steps):
+        cg.tp_forward(plan, x, y, w, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / a.steps
+    paths = [plan.path(p) for p in range(plan.num_paths)]
+    flops = tp_flops(paths, None, spec.mode) * B
+    peak = 157.3 if a.dtype == "f32" else 78.6
+    achieved = flops / (ms * 1e-3) / 1e12
+    line = {"metric": "rows/sec batched CGTP forward and % of FP32 roofline", "value": B / (wall / a.steps),
+            "unit": "rows/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+            "ms_per_step": wall * 1e3 / a.steps, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": a.dtype, "data": "synthetic",
+            "config": {"workload": spec.name, "B": B, "in_irreps": spec.in_irreps, "mode": spec.mode,
+                       "paths": plan.num_paths, "nnz": plan.nnz_total, "kernel_ms": ms},
+            "roofline": {"bound": "mfma" if spec.mode == "uvw" else "hbm", "kernel": "cgtp_tp_forward",
+                         "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                         "traffic": None, "flops_per_launch": flops, "avg_launch_ms": ms},
+            "cpu_baseline": None}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -156,6 +213,8 @@ def main():
     device = "cuda:0"
     torch.cuda.set_device(0)
     spec = synth.WORKLOADS[a.workload]
+    if not hasattr(spec, "n_edges"):
+        return bench_tp(a, spec, device)
     plan, d, host_graph = make_inputs(spec, a.dtype, a.seed, device)
     N, E = d["row_ptr"].shape[0] - 1, d["col"].shape[0]
     es = 4 if a.dtype == "f32" else 8

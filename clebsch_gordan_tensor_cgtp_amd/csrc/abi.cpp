@@ -108,6 +108,11 @@ cgtp_status cgtp_plan_create(const char *in_irreps, const char *sh_irreps, const
         P.sh = cgtp::parse_irreps(sh_irreps, "SH");
         P.out = cgtp::parse_irreps(out_irreps, "output");
         cgtp::build_paths(P);
+        if (mode == CGTP_UVW)
+            for (const cgtp::Irrep &o : P.out)
+                if (o.mul > 16)
+                    throw cgtp::Error(CGTP_ERR_UNSUPPORTED,
+                                      "uvw: output multiplicities above 16 are not supported (one MFMA tile of 16)");
         cgtp::schedule(P);
         P.source = cgtp::generate_source(P);
         cgtp::compile_module(P);
@@ -224,7 +229,16 @@ cgtp_status cgtp_tp_forward(const cgtp_plan *plan, int64_t B, const void *x, con
         require_disjoint(out, B * P.d_out * es, "out", x, B * P.d_x * es, "x");
         require_disjoint(out, B * P.d_out * es, "out", y, B * P.d_sh * es, "y");
         require_disjoint(out, B * P.d_out * es, "out", w, nw, "w");
-        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw batched product is not built yet");
+        if (P.mode == CGTP_UVW) {
+            const auto &L = cgtp::module_for_current_device(P);
+            long nrows = (long)B;
+            const int64_t waves = (B + 15) / 16;
+            for (int grp = 0; grp < (int)P.uvw_groups.size(); ++grp) {
+                void *args[] = {&x, &y, &w, &out, &nrows, &grp};
+                launch(L.tp_uvw, waves, args, stream);
+            }
+            return;
+        }
         const auto &L = cgtp::module_for_current_device(P);
         int es_max = 1;
         for (const auto &g : P.fwd_groups) es_max = std::max(es_max, g.es);

@@ -682,6 +682,157 @@ void emit_bwd_kernel(Out &o, const Plan &P)
     o("");
 }
 
+// ------------------------------------------------------------------------------------------
+// uvw batched product: sparse CG contraction on VALU, dense multiplicity mixing
+// on MFMA (16x16x4).  One wave covers 16 rows; lane l works on row l % 16 and
+// input channel u = 4c + l / 16 for channel chunk c.  Per path and output
+// component k the B operand is t[row, u, k] straight from the VALU result and
+// the A operand is W_p[u][w] (w = l % 16), so
+//   D_{q,k}[w][row] += sum_u W_p[u][w] t_p[row, u, k]
+// accumulates the output block q = slot(p) in registers across paths and
+// chunks.  Lane l ends holding out[row = l % 16][w][k] in register v, with
+// w = 4 (l / 16) + v (fp32 instruction) or w = l / 16 + 4 v (fp64 instruction).
+void emit_uvw_group(Out &o, const Plan &P, int gi)
+{
+    const Group &g = P.uvw_groups[gi];
+    const bool f64 = P.dtype == CGTP_F64;
+    Touch t = touched(P, g.paths);
+    int chunks = 0;
+    for (int pi : g.paths) chunks = std::max(chunks, (P.paths[pi].mul_in + 3) / 4);
+    o("__device__ __forceinline__ void uvw_g", gi,
+      "(long blk, int lane, const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, "
+      "T* __restrict__ out, long nrows)");
+    o("{");
+    o.ind++;
+    o("const long row = blk * 16 + (lane & 15);");
+    o("const int usub = lane >> 4;");
+    o("const bool live = row < nrows;");
+    o("const long rr = live ? row : nrows - 1;  // rows past the end read row nrows-1 and are never stored");
+    for (int q : t.slots)
+        for (int k = 0; k < n_of(P.out[q].l); ++k) o("V4 a", q, "_", k, " = {0, 0, 0, 0};");
+    o("for (int c = 0; c < ", chunks, "; ++c) {");
+    o.ind++;
+    o("const int u = 4 * c + usub;");
+    for (int b : t.i1) {
+        const Irrep &ir = P.ins[b];
+        int off = 0;
+        for (int bb = 0; bb < b; ++bb) off += P.ins[bb].dim();
+        const bool mask = chunks * 4 > ir.mul;
+        if (mask) o("const int ux", b, " = u < ", ir.mul, " ? u : 0;");
+        std::string uu = mask ? "ux" + std::to_string(b) : "u";
+        for (int i = 0; i < n_of(ir.l); ++i) {
+            std::string ld = "x[(size_t)rr * DX + " + std::to_string(off) + " + " + uu + " * " + std::to_string(n_of(ir.l)) +
+                             " + " + std::to_string(i) + "]";
+            if (mask)
+                o("const T x", b, "_", i, " = u < ", ir.mul, " ? ", ld, " : (T)0;");
+            else
+                o("const T x", b, "_", i, " = ", ld, ";");
+        }
+    }
+    // SH blocks one at a time (rows of y are small and stay in L1), paths in (i2, i1) order
+    std::map<int, std::vector<int>> by_i2;
+    for (int pi : g.paths) by_i2[P.paths[pi].i2].push_back(pi);
+    for (auto &kv : by_i2) {
+        const int b = kv.first;
+        int off = 0;
+        for (int bb = 0; bb < b; ++bb) off += P.sh[bb].dim();
+        o("{");
+        o.ind++;
+        for (int j = 0; j < n_of(P.sh[b].l); ++j)
+            o("const T y", b, "_", j, " = y[(size_t)rr * DSH + ", off + j, "];");
+        for (int pi : kv.second) {
+            const Path &p = P.paths[pi];
+            o("{");
+            o.ind++;
+            // A operand: W_p[u][w] with w = lane % 16 (zero outside the block)
+            const bool wmask = chunks * 4 > p.mul_in || p.mul_out < 16;
+            if (wmask) {
+                o("const bool wok = u < ", p.mul_in, " && (lane & 15) < ", p.mul_out, ";");
+                o("const T wv = w[", p.w_off, " + (wok ? u * ", p.mul_out, " + (lane & 15) : 0)];");
+                o("const T wa = wok ? wv : (T)0;");
+            } else {
+                o("const T wa = w[", p.w_off, " + u * ", p.mul_out, " + (lane & 15)];");
+            }
+            std::map<int, std::vector<const Nonzero *>> byk;
+            for (const Nonzero &z : p.nz) byk[z.k].push_back(&z);
+            for (auto &kk : byk) {
+                const auto &v = kk.second;
+                std::ostringstream e;
+                e << lit(v[0]->c, f64) << " * (x" << p.i1 << "_" << v[0]->i << " * y" << p.i2 << "_" << v[0]->j << ")";
+                for (size_t n = 1; n < v.size(); ++n) {
+                    std::ostringstream f;
+                    f << "FMA(" << lit(v[n]->c, f64) << ", x" << p.i1 << "_" << v[n]->i << " * y" << p.i2 << "_" << v[n]->j
+                      << ", " << e.str() << ")";
+                    e.str(f.str());
+                }
+                o("a", p.slot, "_", kk.first, " = MFMA(wa, ", e.str(), ", a", p.slot, "_", kk.first, ");");
+            }
+            o.ind--;
+            o("}");
+        }
+        o.ind--;
+        o("}");
+    }
+    o.ind--;
+    o("}");  // chunk loop
+    o("if (live) {");
+    o.ind++;
+    o("T* orow = out + (size_t)row * DOUT;");
+    for (int q : t.slots) {
+        const Irrep &ir = P.out[q];
+        int off = 0;
+        for (int qq = 0; qq < q; ++qq) off += P.out[qq].dim();
+        for (int v = 0; v < 4; ++v) {
+            o("{");
+            o.ind++;
+            // D row held in register v of this lane: 4 (lane / 16) + v for the fp32
+            // instruction, lane / 16 + 4 v for the fp64 one
+            if (f64)
+                o("const int wo = usub + ", 4 * v, ";");
+            else
+                o("const int wo = 4 * usub + ", v, ";");
+            if (ir.mul < 16) o("if (wo < ", ir.mul, ") {");
+            for (int k = 0; k < n_of(ir.l); ++k)
+                o("orow[", off, " + wo * ", n_of(ir.l), " + ", k, "] = a", q, "_", k, "[", v, "];");
+            if (ir.mul < 16) o("}");
+            o.ind--;
+            o("}");
+        }
+    }
+    o.ind--;
+    o("}");
+    o.ind--;
+    o("}");
+    o("");
+}
+
+void emit_uvw_kernel(Out &o, const Plan &P)
+{
+    const bool f64 = P.dtype == CGTP_F64;
+    o("typedef ", f64 ? "double" : "float", " V4 __attribute__((ext_vector_type(4)));");
+    if (f64)
+        o("#define MFMA(a, b, c) __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0)");
+    else
+        o("#define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0)");
+    for (int gi = 0; gi < (int)P.uvw_groups.size(); ++gi) emit_uvw_group(o, P, gi);
+    o("// one wave per 16 rows; `group` selects the output slots (one launch per group)");
+    o("extern \"C\" __global__ void __launch_bounds__(256, ", P.uvw_waves_per_eu, ") cgtp_tp_uvw(const T* __restrict__ x, "
+      "const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows, int group)");
+    o("{");
+    o.ind++;
+    o("const long blk = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const int lane = threadIdx.x & 63;");
+    o("if (blk * 16 >= nrows) return;");
+    o("switch (group) {");
+    for (int gi = 0; gi < (int)P.uvw_groups.size(); ++gi)
+        o("case ", gi, ": uvw_g", gi, "(blk, lane, x, y, w, out, nrows); break;");
+    o("default: break;");
+    o("}");
+    o.ind--;
+    o("}");
+    o("");
+}
+
 }  // namespace
 
 std::string generate_source(const Plan &P)
@@ -695,7 +846,7 @@ std::string generate_source(const Plan &P)
         emit_fwd_kernel(o, P, true);
         emit_bwd_kernel(o, P);
     } else {
-        o("// uvw plans: no kernels in this module yet");
+        emit_uvw_kernel(o, P);
     }
     return o.s.str();
 }

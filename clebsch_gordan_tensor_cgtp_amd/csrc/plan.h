@@ -62,8 +62,10 @@ struct Plan {
     std::vector<Group> fwd_groups;  // forward: one wave per (receiver, group, tile)
     int fwd_tasks = 0;              // sum over groups of tiles
     std::vector<Group> bwd_groups;  // backward: one launch per group, in order
+    std::vector<Group> uvw_groups;  // uvw batched product: one launch per group of output slots
     int fwd_waves_per_eu = 4;       // occupancy target given to the compiler (min waves per SIMD)
     int bwd_waves_per_eu = 4;
+    int uvw_waves_per_eu = 2;
     bool bwd_sched_barrier = true;  // keep path blocks of the backward from interleaving
     int bwd_prefetch = -1;          // -1: per group by register estimate; 0/1 forced
     bool fwd_split_inputs = false;  // forward groups follow input-irrep classes (measured slower)
@@ -73,7 +75,7 @@ struct Plan {
     std::mutex mu;                  // guards the per-device module table
     struct Loaded {
         hipModule_t module = nullptr;
-        hipFunction_t conv_fwd = nullptr, conv_bwd = nullptr, tp_fwd = nullptr;
+        hipFunction_t conv_fwd = nullptr, conv_bwd = nullptr, tp_fwd = nullptr, tp_uvw = nullptr;
     };
     std::map<int, Loaded> loaded;
 };

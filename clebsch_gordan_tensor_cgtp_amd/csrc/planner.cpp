@@ -305,6 +305,32 @@ void schedule(Plan &P)
     P.fwd_tasks = 0;
     for (const Group &g : P.fwd_groups) P.fwd_tasks += g.tiles;
 
+    // uvw: output slots in order, packed while the MFMA accumulators (4 per lane
+    // per output component) fit 64 registers; all paths of a slot stay together.
+    P.uvw_groups.clear();
+    if (P.mode == CGTP_UVW) {
+        std::vector<std::vector<int>> slot_paths(P.out.size());
+        for (int i = 0; i < (int)P.paths.size(); ++i) slot_paths[P.paths[i].slot].push_back(i);
+        Group cur;
+        int regs = 0;
+        for (int q = 0; q < (int)P.out.size(); ++q) {
+            if (slot_paths[q].empty()) continue;
+            int need = 4 * word * (2 * P.out[q].l + 1);
+            if (!cur.paths.empty() && regs + need > 64) {
+                P.uvw_groups.push_back(cur);
+                cur = Group();
+                regs = 0;
+            }
+            for (int i : slot_paths[q]) cur.paths.push_back(i);
+            regs += need;
+        }
+        if (!cur.paths.empty()) P.uvw_groups.push_back(cur);
+        for (Group &g : P.uvw_groups) {
+            std::sort(g.paths.begin(), g.paths.end());
+            for (int pi : g.paths) g.mul = std::max(g.mul, P.paths[pi].mul_in);
+        }
+    }
+
     // Backward groups: paths sharing an SH block (so that block's dY is complete
     // in one group), split when the register estimate exceeds the budget.
     P.bwd_groups.clear();
@@ -376,6 +402,8 @@ void schedule(Plan &P)
     P.fwd_waves_per_eu = P.dtype == CGTP_F64 ? 2 : 4;
     if (const char *e = std::getenv("CGTP_FWD_WAVES")) P.fwd_waves_per_eu = std::max(1, std::atoi(e));
     if (const char *e = std::getenv("CGTP_BWD_WAVES")) P.bwd_waves_per_eu = std::max(1, std::atoi(e));
+    P.uvw_waves_per_eu = P.dtype == CGTP_F64 ? 1 : 2;
+    if (const char *e = std::getenv("CGTP_UVW_WAVES")) P.uvw_waves_per_eu = std::max(1, std::atoi(e));
     if (const char *e = std::getenv("CGTP_BWD_SCHED_BARRIER")) P.bwd_sched_barrier = std::atoi(e) != 0;
 }
 

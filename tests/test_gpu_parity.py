@@ -177,3 +177,57 @@ def test_tp_forward_uvu(device, dtype, in_irreps, lmax, B):
     out = cg.tp_forward(plan, t(x), y, t(w)).cpu().numpy()
     want = ref.tp_forward(prob, x, osh.real_sh_all(lmax, vec.astype(np.float64)), w)
     assert rel_l2(out, want) <= TOL[dtype]
+
+
+# --------------------------------------------------------------------------- uvw (dense mixing on MFMA)
+
+def _uvw_case(in_irreps, lmax, out_irreps, B, dtype, seed=13):
+    prob = oirreps.build_problem(in_irreps, oirreps.sh_irreps(lmax), out_irreps, "uvw")
+    st = synth.streams(seed)
+    npdt = np.float32 if dtype == "f32" else np.float64
+    x = synth.normal(st["x"], (B, prob.d_in), dtype=npdt)
+    vec = synth.normal(st["vec"], (B, 3), dtype=npdt)
+    # W_p ~ N(0,1)/sqrt(mul_in * paths into the output irrep)
+    fan = {}
+    for p in prob.paths:
+        fan[p.slot] = fan.get(p.slot, 0) + prob.ins[p.i1].mul
+    w = synth.normal(st["w"], (prob.weight_numel,), dtype=np.float64)
+    for p in prob.paths:
+        n = prob.ins[p.i1].mul * prob.out[p.slot].mul
+        w[p.w_off:p.w_off + n] /= np.sqrt(fan[p.slot])
+    return prob, x, vec, w.astype(npdt)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("in_irreps,lmax,out_irreps,B", [
+    (synth.TP_HIGHL.in_irreps, 7, synth.TP_HIGHL.out_irreps, 333),
+    ("3x0e+5x1o+2x2e", 2, "4x0e+7x1o+3x2e+2x1e+16x2o", 77),
+    ("16x0e+16x1o", 1, "16x0e+16x1o+16x1e", 1),
+])
+def test_tp_forward_uvw(device, dtype, in_irreps, lmax, out_irreps, B):
+    import torch
+    prob, x, vec, w = _uvw_case(in_irreps, lmax, out_irreps, B, dtype)
+    plan = cg.plan_create(in_irreps, oirreps.sh_irreps(lmax), out_irreps, "uvw", dtype)
+    t = lambda a: torch.from_numpy(a).to(device)
+    y = cg.spherical_harmonics(lmax, t(vec))
+    out = cg.tp_forward(plan, t(x), y, t(w)).cpu().numpy()
+    want = loops.uvw_forward(loops.Tables(prob), x.astype(np.float64),
+                             osh.real_sh_all(lmax, vec.astype(np.float64)), w.astype(np.float64))
+    assert rel_l2(out, want) <= TOL[dtype]
+
+
+def test_tp_forward_uvw_full_size_sampled(device):
+    """The high-L workload at its full batch (50,000 rows), checked on a seeded row sample."""
+    import torch
+    spec = synth.TP_HIGHL
+    prob, x, vec, w = _uvw_case(spec.in_irreps, spec.lmax_sh, spec.out_irreps, spec.batch, "f32", seed=0)
+    plan = cg.plan_for(spec, "f32")
+    t = lambda a: torch.from_numpy(a).to(device)
+    y = cg.spherical_harmonics(spec.lmax_sh, t(vec))
+    out = cg.tp_forward(plan, t(x), y, t(w))
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(1).choice(spec.batch, 2048, replace=False))
+    rows = np.unique(np.concatenate([rows, [0, spec.batch - 1]]))
+    want = loops.uvw_forward(loops.Tables(prob), x[rows].astype(np.float64),
+                             osh.real_sh_all(spec.lmax_sh, vec[rows].astype(np.float64)), w.astype(np.float64))
+    assert rel_l2(out.cpu().numpy()[rows], want) <= TOL["f32"]
