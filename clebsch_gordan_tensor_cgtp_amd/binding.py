@@ -17,6 +17,7 @@ CGTP_UVU, CGTP_UVW = 0, 1
 CGTP_F32, CGTP_F64 = 0, 1
 STATUS = {0: "CGTP_OK", 1: "CGTP_ERR_INVALID_ARG", 2: "CGTP_ERR_IRREPS", 3: "CGTP_ERR_UNSUPPORTED",
           4: "CGTP_ERR_COMPILE", 5: "CGTP_ERR_HIP", 6: "CGTP_ERR_INTERNAL"}
+STATUS_CODES = {v: k for k, v in STATUS.items()}
 
 EXPORTS = ("cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info_get", "cgtp_plan_path",
            "cgtp_plan_path_coefficients", "cgtp_plan_source", "cgtp_tp_forward", "cgtp_conv_forward",
