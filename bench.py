@@ -62,6 +62,23 @@ def algorithmic_bytes(plan, N, E, es):
     return fwd, bwd
 
 
+def measured_traffic(plan, spec, dtype, kernel):
+    """HBM-side bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE record, scaled
+    by the copy-kernel calibration; None when no record exists for this exact generated module."""
+    import glob
+    import hashlib
+    digest = hashlib.sha1(plan.source.encode()).hexdigest()
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*_hbm_counters.json")):
+        rec = json.load(open(path))
+        if rec.get("module_sha1") != digest or rec.get("dtype") != dtype or kernel not in rec.get("kernels", {}):
+            continue
+        k, cal = rec["kernels"][kernel], rec["calibration"]
+        kib = (k["FETCH_SIZE_kib_per_dispatch"] * cal["fetch_factor"]
+               + k["WRITE_SIZE_kib_per_dispatch"] * cal["write_factor"]) * k["dispatches_per_call"]
+        return kib * 1024
+    return None
+
+
 def make_inputs(spec, dtype, seed, device):
     import torch
     from clebsch_gordan_tensor_cgtp_amd import binding as cg
@@ -251,6 +268,7 @@ def main():
     fwd_b, bwd_b = algorithmic_bytes(plan, N, E, es)
     dom = ("cgtp_conv_bwd", bwd_ms, bwd_b) if bwd_ms >= fwd_ms else ("cgtp_conv_fwd", fwd_ms, fwd_b)
     achieved = dom[2] / (dom[1] * 1e-3) / 1e9
+    traffic = measured_traffic(plan, spec, a.dtype, dom[0])
     line = {
         "metric": METRIC,
         "value": E / (ms_per_step * 1e-3),
@@ -270,7 +288,7 @@ def main():
                    "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
                    "fwd_edges_per_s": E / (fwd_ms * 1e-3), "bwd_edges_per_s": E / (bwd_ms * 1e-3)},
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": dom[2], "avg_launch_ms": dom[1],
                      "other": {"kernel": "cgtp_conv_fwd" if dom[0] == "cgtp_conv_bwd" else "cgtp_conv_bwd",
                                "achieved": (fwd_b / (fwd_ms * 1e-3) if dom[0] == "cgtp_conv_bwd"
