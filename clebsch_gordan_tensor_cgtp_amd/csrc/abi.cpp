@@ -231,12 +231,9 @@ cgtp_status cgtp_tp_forward(const cgtp_plan *plan, int64_t B, const void *x, con
         require_disjoint(out, B * P.d_out * es, "out", w, nw, "w");
         if (P.mode == CGTP_UVW) {
             const auto &L = cgtp::module_for_current_device(P);
-            long nrows = (long)B;
-            const int64_t waves = (B + 15) / 16;
-            for (int grp = 0; grp < (int)P.uvw_groups.size(); ++grp) {
-                void *args[] = {&x, &y, &w, &out, &nrows, &grp};
-                launch(L.tp_uvw, waves, args, stream);
-            }
+            long nrows = (long)B, nblocks = (long)((B + 15) / 16);
+            void *args[] = {&x, &y, &w, &out, &nrows, &nblocks};
+            launch(L.tp_uvw, nblocks * (int64_t)P.uvw_groups.size(), args, stream);
             return;
         }
         const auto &L = cgtp::module_for_current_device(P);

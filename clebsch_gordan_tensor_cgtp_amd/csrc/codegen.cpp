@@ -684,10 +684,13 @@ void emit_bwd_kernel(Out &o, const Plan &P)
 
 // ------------------------------------------------------------------------------------------
 // uvw batched product: sparse CG contraction on VALU, dense multiplicity mixing
-// on MFMA (16x16x4).  One wave covers 16 rows; lane l works on row l % 16 and
-// input channel u = 4c + l / 16 for channel chunk c.  Per path and output
-// component k the B operand is t[row, u, k] straight from the VALU result and
-// the A operand is W_p[u][w] (w = l % 16), so
+// on MFMA (16x16x4).  One wave covers 16 rows; lane l works on row l % 16 and on
+// input channels u = 4c + l / 16 for the four channel chunks c.  The contraction
+// with y depends only on the row, so for each path and output component k the
+// column A[i] = sum_j C_ijk y_j is formed once (literal constants) and reused for
+// the four chunks: t_c = sum_i A[i] x[row, 4c + l/16, i] (LunaTP page, Abstract:
+// multi-level reuse).  t_c is directly the MFMA B operand and W_p[u][w = l % 16]
+// the A operand, so
 //   D_{q,k}[w][row] += sum_u W_p[u][w] t_p[row, u, k]
 // accumulates the output block q = slot(p) in registers across paths and
 // chunks.  Lane l ends holding out[row = l % 16][w][k] in register v, with
@@ -710,62 +713,84 @@ void emit_uvw_group(Out &o, const Plan &P, int gi)
     o("const long rr = live ? row : nrows - 1;  // rows past the end read row nrows-1 and are never stored");
     for (int q : t.slots)
         for (int k = 0; k < n_of(P.out[q].l); ++k) o("V4 a", q, "_", k, " = {0, 0, 0, 0};");
-    o("for (int c = 0; c < ", chunks, "; ++c) {");
-    o.ind++;
-    o("const int u = 4 * c + usub;");
-    for (int b : t.i1) {
+    for (int b : t.i2) {
+        int off = 0;
+        for (int bb = 0; bb < b; ++bb) off += P.sh[bb].dim();
+        for (int j = 0; j < n_of(P.sh[b].l); ++j) o("const T y", b, "_", j, " = y[(size_t)rr * DSH + ", off + j, "];");
+    }
+    // paths grouped by input block: that block's x is loaded for all chunks once
+    std::map<int, std::vector<int>> by_i1;
+    for (int pi : g.paths) by_i1[P.paths[pi].i1].push_back(pi);
+    for (auto &kv : by_i1) {
+        const int b = kv.first;
         const Irrep &ir = P.ins[b];
         int off = 0;
         for (int bb = 0; bb < b; ++bb) off += P.ins[bb].dim();
-        const bool mask = chunks * 4 > ir.mul;
-        if (mask) o("const int ux", b, " = u < ", ir.mul, " ? u : 0;");
-        std::string uu = mask ? "ux" + std::to_string(b) : "u";
-        for (int i = 0; i < n_of(ir.l); ++i) {
-            std::string ld = "x[(size_t)rr * DX + " + std::to_string(off) + " + " + uu + " * " + std::to_string(n_of(ir.l)) +
-                             " + " + std::to_string(i) + "]";
-            if (mask)
-                o("const T x", b, "_", i, " = u < ", ir.mul, " ? ", ld, " : (T)0;");
-            else
-                o("const T x", b, "_", i, " = ", ld, ";");
-        }
-    }
-    // SH blocks one at a time (rows of y are small and stay in L1), paths in (i2, i1) order
-    std::map<int, std::vector<int>> by_i2;
-    for (int pi : g.paths) by_i2[P.paths[pi].i2].push_back(pi);
-    for (auto &kv : by_i2) {
-        const int b = kv.first;
-        int off = 0;
-        for (int bb = 0; bb < b; ++bb) off += P.sh[bb].dim();
         o("{");
         o.ind++;
-        for (int j = 0; j < n_of(P.sh[b].l); ++j)
-            o("const T y", b, "_", j, " = y[(size_t)rr * DSH + ", off + j, "];");
+        for (int c = 0; c < chunks; ++c) {
+            const bool mask = 4 * c + 3 >= ir.mul;
+            std::string u = "(" + std::to_string(4 * c) + " + usub)";
+            for (int i = 0; i < n_of(ir.l); ++i) {
+                std::string addr = "(size_t)rr * DX + " + std::to_string(off) + " + " + (mask ? "(" + u + " < " +
+                                   std::to_string(ir.mul) + " ? " + u + " : 0)" : u) + " * " + std::to_string(n_of(ir.l)) +
+                                   " + " + std::to_string(i);
+                if (mask)
+                    o("const T x", c, "_", i, " = ", u, " < ", ir.mul, " ? x[", addr, "] : (T)0;");
+                else
+                    o("const T x", c, "_", i, " = x[", addr, "];");
+            }
+        }
         for (int pi : kv.second) {
             const Path &p = P.paths[pi];
             o("{");
             o.ind++;
-            // A operand: W_p[u][w] with w = lane % 16 (zero outside the block)
-            const bool wmask = chunks * 4 > p.mul_in || p.mul_out < 16;
-            if (wmask) {
-                o("const bool wok = u < ", p.mul_in, " && (lane & 15) < ", p.mul_out, ";");
-                o("const T wv = w[", p.w_off, " + (wok ? u * ", p.mul_out, " + (lane & 15) : 0)];");
-                o("const T wa = wok ? wv : (T)0;");
-            } else {
-                o("const T wa = w[", p.w_off, " + u * ", p.mul_out, " + (lane & 15)];");
-            }
-            std::map<int, std::vector<const Nonzero *>> byk;
-            for (const Nonzero &z : p.nz) byk[z.k].push_back(&z);
-            for (auto &kk : byk) {
-                const auto &v = kk.second;
-                std::ostringstream e;
-                e << lit(v[0]->c, f64) << " * (x" << p.i1 << "_" << v[0]->i << " * y" << p.i2 << "_" << v[0]->j << ")";
-                for (size_t n = 1; n < v.size(); ++n) {
-                    std::ostringstream f;
-                    f << "FMA(" << lit(v[n]->c, f64) << ", x" << p.i1 << "_" << v[n]->i << " * y" << p.i2 << "_" << v[n]->j
-                      << ", " << e.str() << ")";
-                    e.str(f.str());
+            // A operands: W_p[u][w] with u = 4c + lane/16, w = lane % 16 (zero outside the block)
+            for (int c = 0; c < chunks; ++c) {
+                std::string u = "(" + std::to_string(4 * c) + " + usub)";
+                const bool wmask = 4 * c + 3 >= p.mul_in || p.mul_out < 16;
+                if (wmask) {
+                    o("const bool wok", c, " = ", u, " < ", p.mul_in, " && (lane & 15) < ", p.mul_out, ";");
+                    o("const T wv", c, " = w[", p.w_off, " + (wok", c, " ? ", u, " * ", p.mul_out, " + (lane & 15) : 0)];");
+                    o("const T wa", c, " = wok", c, " ? wv", c, " : (T)0;");
+                } else {
+                    o("const T wa", c, " = w[", p.w_off, " + ", u, " * ", p.mul_out, " + (lane & 15)];");
                 }
-                o("a", p.slot, "_", kk.first, " = MFMA(wa, ", e.str(), ", a", p.slot, "_", kk.first, ");");
+            }
+            std::map<int, std::map<int, std::vector<const Nonzero *>>> byki;  // k -> i -> nonzeros
+            for (const Nonzero &z : p.nz) byki[z.k][z.i].push_back(&z);
+            for (auto &kk : byki) {
+                const int k = kk.first;
+                o("{");
+                o.ind++;
+                for (auto &ii : kk.second) {
+                    const auto &v = ii.second;
+                    std::ostringstream e;
+                    e << lit(v[0]->c, f64) << " * y" << p.i2 << "_" << v[0]->j;
+                    for (size_t n = 1; n < v.size(); ++n) {
+                        std::ostringstream f;
+                        f << "FMA(" << lit(v[n]->c, f64) << ", y" << p.i2 << "_" << v[n]->j << ", " << e.str() << ")";
+                        e.str(f.str());
+                    }
+                    o("const T A", ii.first, " = ", e.str(), ";");
+                }
+                for (int c = 0; c < chunks; ++c) {
+                    std::ostringstream e;
+                    bool first = true;
+                    for (auto &ii : kk.second) {
+                        if (first) {
+                            e << "A" << ii.first << " * x" << c << "_" << ii.first;
+                            first = false;
+                        } else {
+                            std::ostringstream f;
+                            f << "FMA(A" << ii.first << ", x" << c << "_" << ii.first << ", " << e.str() << ")";
+                            e.str(f.str());
+                        }
+                    }
+                    o("a", p.slot, "_", k, " = MFMA(wa", c, ", ", e.str(), ", a", p.slot, "_", k, ");");
+                }
+                o.ind--;
+                o("}");
             }
             o.ind--;
             o("}");
@@ -773,8 +798,6 @@ void emit_uvw_group(Out &o, const Plan &P, int gi)
         o.ind--;
         o("}");
     }
-    o.ind--;
-    o("}");  // chunk loop
     o("if (live) {");
     o.ind++;
     o("T* orow = out + (size_t)row * DOUT;");
@@ -815,14 +838,17 @@ void emit_uvw_kernel(Out &o, const Plan &P)
     else
         o("#define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0)");
     for (int gi = 0; gi < (int)P.uvw_groups.size(); ++gi) emit_uvw_group(o, P, gi);
-    o("// one wave per 16 rows; `group` selects the output slots (one launch per group)");
-    o("extern \"C\" __global__ void __launch_bounds__(256, ", P.uvw_waves_per_eu, ") cgtp_tp_uvw(const T* __restrict__ x, "
-      "const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows, int group)");
+    o("// one wave per (group, 16-row block), group-major so that the waves resident at any time");
+    o("// mostly run the same group's code");
+    o("extern \"C\" __global__ void __launch_bounds__(256, ", P.uvw_waves_per_eu,
+      ") cgtp_tp_uvw(const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, "
+      "T* __restrict__ out, long nrows, long nblocks)");
     o("{");
     o.ind++;
-    o("const long blk = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const long wave = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
     o("const int lane = threadIdx.x & 63;");
-    o("if (blk * 16 >= nrows) return;");
+    o("const int group = (int)(wave / nblocks);");
+    o("const long blk = wave - (long)group * nblocks;");
     o("switch (group) {");
     for (int gi = 0; gi < (int)P.uvw_groups.size(); ++gi)
         o("case ", gi, ": uvw_g", gi, "(blk, lane, x, y, w, out, nrows); break;");
