@@ -3,10 +3,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c5] [--no-cpu]
 
 One step = one pass of the hot path over the synthetic graph: the fused
-convolution forward (cgtp_conv_forward) followed by the fused backward
-(cgtp_conv_backward: grad_x, grad_y, grad_w).  Per-graph set-up (plan and
-hipRTC, spherical harmonics of the edge vectors, the sender transpose) runs
-before the timed region.  All inputs are resident in HBM when timing starts.
+convolution forward (cgtp_conv_forward_ordered, heavy-first receiver schedule)
+followed by the fused backward (cgtp_conv_backward: grad_x, grad_y, grad_w).
+Per-graph set-up (plan and hipRTC, spherical harmonics of the edge vectors,
+the sender transpose, the receiver schedule) runs before the timed region.  All inputs are resident in HBM when timing starts.
 
 Prints one JSON line with the throughput in edges/s (forward + backward per
 edge), the roofline of the dominant kernel (HIP events on the launch stream)
@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--dtype", default="f32", choices=["f32", "f64"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--natural-order", action="store_true",
+                    help="start receivers in node order instead of the heavy-first schedule")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -237,6 +239,7 @@ def main():
     es = 4 if a.dtype == "f32" else 8
     y = cg.spherical_harmonics(spec.lmax_sh, d["vec"])
     tr = cg.graph_transpose(d["row_ptr"], d["col"])
+    order = cg.graph_order(d["row_ptr"]) if not a.natural_order else None
     out = torch.empty((N, plan.d_out), dtype=plan.torch_dtype, device=device)
     gx = torch.empty_like(d["x"])
     gy = torch.empty_like(y)
@@ -245,7 +248,7 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        cg.conv_forward(plan, d["row_ptr"], d["col"], d["x"], y, d["w"], out=out)
+        cg.conv_forward(plan, d["row_ptr"], d["col"], d["x"], y, d["w"], out=out, order=order)
         if ev is not None:
             ev[1].record()
         cg.conv_backward(plan, d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"], gx, gy, gw)
@@ -285,6 +288,7 @@ def main():
         "config": {"workload": spec.name, "N": N, "E": E, "in_irreps": spec.in_irreps,
                    "sh_lmax": spec.lmax_sh, "paths": plan.num_paths, "d_out": plan.d_out,
                    "step": "conv_forward + conv_backward (grad_x, grad_y, grad_w)",
+                   "receiver_schedule": "natural" if a.natural_order else "heavy-first",
                    "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
                    "fwd_edges_per_s": E / (fwd_ms * 1e-3), "bwd_edges_per_s": E / (bwd_ms * 1e-3)},
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": achieved, "peak": HBM_PEAK_GBS,

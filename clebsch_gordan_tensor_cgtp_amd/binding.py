@@ -21,7 +21,8 @@ STATUS_CODES = {v: k for k, v in STATUS.items()}
 
 EXPORTS = ("cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info_get", "cgtp_plan_path",
            "cgtp_plan_path_coefficients", "cgtp_plan_source", "cgtp_tp_forward", "cgtp_conv_forward",
-           "cgtp_graph_transpose", "cgtp_conv_backward", "cgtp_spherical_harmonics", "cgtp_last_error")
+           "cgtp_graph_transpose", "cgtp_conv_backward", "cgtp_spherical_harmonics", "cgtp_last_error",
+           "cgtp_conv_forward_ordered", "cgtp_graph_order")
 
 
 class CgtpError(RuntimeError):
@@ -64,6 +65,8 @@ def lib():
         L.cgtp_plan_path_coefficients.argtypes = [vp, i32, i32, vp, vp, ctypes.POINTER(i32)]
         L.cgtp_tp_forward.argtypes = [vp, i64, vp, vp, vp, ctypes.c_int, vp, vp]
         L.cgtp_conv_forward.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+        L.cgtp_conv_forward_ordered.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.cgtp_graph_order.argtypes = [i64, vp, vp, vp]
         L.cgtp_graph_transpose.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp]
         L.cgtp_conv_backward.argtypes = [vp, i64, i64] + [vp] * 13
         L.cgtp_spherical_harmonics.argtypes = [i32, ctypes.c_int, i64, vp, vp, vp]
@@ -214,14 +217,25 @@ def tp_forward(plan: Plan, x, y, w, out=None, stream=None):
     return out
 
 
-def conv_forward(plan: Plan, row_ptr, col, x, y, w, out=None, stream=None):
+def graph_order(row_ptr, order=None, stream=None):
+    """Heavy-first receiver schedule (stable by log2 degree bucket, descending)."""
+    import torch
+    N = row_ptr.shape[0] - 1
+    order = torch.empty(N, dtype=torch.int32, device=row_ptr.device) if order is None else order
+    _check(lib().cgtp_graph_order(N, _dev(row_ptr, "row_ptr", torch.int32), _dev(order, "order", torch.int32, (N,)),
+                                  _stream(stream, row_ptr.device)))
+    return order
+
+
+def conv_forward(plan: Plan, row_ptr, col, x, y, w, out=None, order=None, stream=None):
     import torch
     N, E = row_ptr.shape[0] - 1, col.shape[0]
     dt = plan.torch_dtype
     if out is None:
         out = torch.empty((N, plan.d_out), dtype=dt, device=x.device)
-    _check(lib().cgtp_conv_forward(plan.handle, N, E, _dev(row_ptr, "row_ptr", torch.int32),
-                                   _dev(col, "col", torch.int32), _dev(x, "x", dt, (N, plan.d_x)),
+    _check(lib().cgtp_conv_forward_ordered(plan.handle, N, E, _dev(row_ptr, "row_ptr", torch.int32),
+                                   _dev(col, "col", torch.int32), _ptr_or_null(order, "order", torch.int32, (N,)),
+                                   _dev(x, "x", dt, (N, plan.d_x)),
                                    _dev(y, "y", dt, (E, plan.d_sh)), _dev(w, "w", dt, (E, plan.weight_numel)),
                                    _dev(out, "out", dt, (N, plan.d_out)), _stream(stream, x.device)))
     return out

@@ -241,15 +241,34 @@ cgtp_status cgtp_tp_forward(const cgtp_plan *plan, int64_t B, const void *x, con
         for (const auto &g : P.fwd_groups) es_max = std::max(es_max, g.es);
         int64_t blocks_of_rows = (B + es_max - 1) / es_max;
         int64_t waves = blocks_of_rows * P.fwd_tasks;
-        const void *rp = nullptr, *cp = nullptr;
+        const void *rp = nullptr, *cp = nullptr, *ord = nullptr;
         long nrows = (long)B, nwaves = (long)waves;
-        void *args[] = {&rp, &cp, &x, &y, &w, &out, &nrows, &nwaves};
+        void *args[] = {&rp, &cp, &x, &y, &w, &out, &nrows, &nwaves, &ord};
         launch(L.tp_fwd, waves, args, stream);
     });
 }
 
 cgtp_status cgtp_conv_forward(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr, const int32_t *col,
                               const void *x, const void *y, const void *w, void *out, void *stream)
+{
+    return cgtp_conv_forward_ordered(plan, N, E, row_ptr, col, nullptr, x, y, w, out, stream);
+}
+
+cgtp_status cgtp_graph_order(int64_t N, const int32_t *row_ptr, int32_t *order, void *stream)
+{
+    return guarded([&] {
+        require(N >= 0 && N < INT_MAX, "N must be in [0, 2^31-1)");
+        if (N == 0) return;
+        require_ptr(row_ptr, "row_ptr", 4);
+        require_ptr(order, "order", 4);
+        require_disjoint(order, N * 4, "order", row_ptr, (N + 1) * 4, "row_ptr");
+        check_hip(cgtp::launch_degree_order(N, row_ptr, order, static_cast<hipStream_t>(stream)), "order launch");
+    });
+}
+
+cgtp_status cgtp_conv_forward_ordered(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
+                                      const int32_t *col, const int32_t *order, const void *x, const void *y,
+                                      const void *w, void *out, void *stream)
 {
     return guarded([&] {
         require(plan != nullptr, "plan is NULL");
@@ -272,10 +291,14 @@ cgtp_status cgtp_conv_forward(const cgtp_plan *plan, int64_t N, int64_t E, const
         require_disjoint(out, no, "out", w, E * P.w_numel * es, "w");
         require_disjoint(out, no, "out", row_ptr, (N + 1) * 4, "row_ptr");
         require_disjoint(out, no, "out", col, E * 4, "col");
+        if (order) {
+            require_ptr(order, "order", 4);
+            require_disjoint(out, no, "out", order, N * 4, "order");
+        }
         const auto &L = cgtp::module_for_current_device(P);
         int64_t waves = N * P.fwd_tasks;
         long nrows = (long)N, nwaves = (long)waves;
-        void *args[] = {&row_ptr, &col, &x, &y, &w, &out, &nrows, &nwaves};
+        void *args[] = {&row_ptr, &col, &x, &y, &w, &out, &nrows, &nwaves, &order};
         launch(L.conv_fwd, waves, args, stream);
     });
 }

@@ -128,12 +128,12 @@ void emit_edge_loads(Out &o, const Plan &P, const Group &g, const Touch &t, cons
         for (int pi : g.paths)
             if (P.paths[pi].i2 == b) off = P.paths[pi].b;
         for (int j = 0; j < n_of(P.sh[b].l); ++j)
-            o(T, pre, "y", b, "_", j, " = __builtin_nontemporal_load(&y[(size_t)", ei, " * DSH + ", off + j, "]);");
+            o(T, pre, "y", b, "_", j, " = LD_STREAM(&y[(size_t)", ei, " * DSH + ", off + j, "]);");
     }
     for (int pi : g.paths) {
         const Path &p = P.paths[pi];
         std::ostringstream addr;
-        addr << "__builtin_nontemporal_load(&w[(size_t)" << ei << " * WROW + " << p.w_off << " + u])";
+        addr << "LD_STREAM(&w[(size_t)" << ei << " * WROW + " << p.w_off << " + u])";
         if (needs_mask(p.mul_in, g))
             o(T, pre, "w", pi, " = (u < ", p.mul_in, ") ? ", addr.str(), " : (T)0;");
         else
@@ -197,6 +197,14 @@ void emit_preamble(Out &o, const Plan &P)
     o("#define DOUT ", P.d_out);
     o("#define WROW ", P.w_numel, "L");
     o("typedef unsigned long size_t;");
+    // per-edge rows read or written once (y, W, dW): streaming hint on the memory instructions
+    if (P.stream_hint) {
+        o("#define LD_STREAM(p) __builtin_nontemporal_load(p)");
+        o("#define ST_STREAM(v, p) __builtin_nontemporal_store(v, p)");
+    } else {
+        o("#define LD_STREAM(p) (*(p))");
+        o("#define ST_STREAM(v, p) (*(p) = (v))");
+    }
     o("");
 }
 
@@ -291,14 +299,16 @@ void emit_fwd_kernel(Out &o, const Plan &P, bool rows)
 {
     o("extern \"C\" __global__ void __launch_bounds__(256, ", P.fwd_waves_per_eu, ") ", rows ? "cgtp_tp_fwd" : "cgtp_conv_fwd",
       "(const int* __restrict__ row_ptr, const int* __restrict__ col, const T* __restrict__ x, "
-      "const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows, long nwaves)");
+      "const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows, long nwaves, "
+      "const int* __restrict__ order)");
     o("{");
     o.ind++;
     o("const long wave = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
     o("const int lane = threadIdx.x & 63;");
     o("if (wave >= nwaves) return;");
     o("const int task = (int)(wave % ", P.fwd_tasks, ");");
-    o("const long n = wave / ", P.fwd_tasks, ";");
+    o("long n = wave / ", P.fwd_tasks, ";");
+    if (!rows) o("if (order) n = order[n];  // receiver schedule (heavy rows first), results unchanged");
     o("switch (task) {");
     int task = 0;
     for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi)
@@ -414,11 +424,11 @@ void emit_bwd_group(Out &o, const Plan &P, int gi)
             int off = 0;
             for (int bb = 0; bb < b; ++bb) off += P.sh[bb].dim();
             for (int j = 0; j < n_of(P.sh[b].l); ++j)
-                o(Ty, pre, "y", b, "_", j, " = __builtin_nontemporal_load(&y[(size_t)", ev, " * DSH + ", off + j, "]);");
+                o(Ty, pre, "y", b, "_", j, " = LD_STREAM(&y[(size_t)", ev, " * DSH + ", off + j, "]);");
         }
         for (int pi : g.paths) {
             const Path &p = P.paths[pi];
-            std::string wa = "__builtin_nontemporal_load(&w[(size_t)" + ev + " * WROW + " + std::to_string(p.w_off) + " + u])";
+            std::string wa = "LD_STREAM(&w[(size_t)" + ev + " * WROW + " + std::to_string(p.w_off) + " + u])";
             if (needs_mask(p.mul_in, g))
                 o(Ty, pre, "w", pi, " = (u < ", p.mul_in, ") ? ", wa, " : (T)0;");
             else
@@ -518,7 +528,7 @@ void emit_bwd_group(Out &o, const Plan &P, int gi)
                 }
             }
             std::string guard = needs_mask(p.mul_in, g) ? "(u < " + std::to_string(p.mul_in) + ") && " : "";
-            o("if (", guard, "dw) __builtin_nontemporal_store(", e.str(), ", &dw[(size_t)e * WROW + ", p.w_off, " + u]);");
+            o("if (", guard, "dw) ST_STREAM(", e.str(), ", &dw[(size_t)e * WROW + ", p.w_off, " + u]);");
         }
         for (auto &kv : rows) o("d", p.i1, "_", kv.first, " = FMA(w", pi, ", fx", kv.first, ", d", p.i1, "_", kv.first, ");");
         for (auto &kv : cols) o("h", p.i2, "_", kv.first, " = FMA(w", pi, ", fy", kv.first, ", h", p.i2, "_", kv.first, ");");

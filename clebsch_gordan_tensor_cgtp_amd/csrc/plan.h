@@ -66,6 +66,7 @@ struct Plan {
     int fwd_waves_per_eu = 4;       // occupancy target given to the compiler (min waves per SIMD)
     int bwd_waves_per_eu = 4;
     int uvw_waves_per_eu = 2;
+    bool stream_hint = true;        // nontemporal loads/stores for once-touched per-edge rows
     bool bwd_sched_barrier = true;  // keep path blocks of the backward from interleaving
     int bwd_prefetch = -1;          // -1: per group by register estimate; 0/1 forced
     bool fwd_split_inputs = false;  // forward groups follow input-irrep classes (measured slower)

@@ -8,6 +8,9 @@
 // (no Condon-Shortley factor, which the real combination cancels) times the
 // Chebyshev-like recurrence of r_xy^m cos(m phi) and r_xy^m sin(m phi).
 //
+// Receiver order: a stable bucket sort of the receivers by floor(log2(degree+1)),
+// heaviest bucket first, so that long CSR rows start early (power-law graphs).
+//
 // Transpose: a stable counting sort of the edges by sender, needed by the
 // atomic-free backward (OpenEquivariance discussion: a deterministic fused
 // convolution next to the atomic one).  Counting uses integer atomics, whose
@@ -215,6 +218,67 @@ __global__ void __launch_bounds__(256) edge_receivers(const int32_t *__restrict_
         else hi = mid;
     }
     t_dst[t] = (int32_t)lo;
+}
+
+// ------------------------------------------------------------------------------------------
+// heavy-first receiver order: stable bucket sort by floor(log2(degree + 1)), descending
+
+__device__ __forceinline__ int degree_bucket(const int32_t *row_ptr, int64_t i)
+{
+    const int32_t d = row_ptr[i + 1] - row_ptr[i];
+    return 31 - __clz(d + 1);  // floor(log2(d + 1)), 0..31
+}
+
+__global__ void __launch_bounds__(1024) degree_order(const int32_t *__restrict__ row_ptr, int64_t N,
+                                                     int32_t *__restrict__ order)
+{
+    __shared__ int32_t cnt[32];
+    __shared__ int32_t base[32];
+    __shared__ int32_t wcnt[16][32];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (tid < 32) cnt[tid] = 0;
+    __syncthreads();
+    for (int64_t i = tid; i < N; i += 1024) atomicAdd(&cnt[degree_bucket(row_ptr, i)], 1);
+    __syncthreads();
+    if (tid == 0) {
+        int32_t run = 0;
+        for (int b = 31; b >= 0; --b) {
+            base[b] = run;
+            run += cnt[b];
+        }
+    }
+    __syncthreads();
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int64_t c0 = 0; c0 < N; c0 += 1024) {
+        const int64_t i = c0 + tid;
+        const int b = i < N ? degree_bucket(row_ptr, i) : -1;
+        int rank = 0;
+        for (int bb = 0; bb < 32; ++bb) {
+            const unsigned long long m = __ballot(b == bb);
+            if (b == bb) rank = __popcll(m & below);
+            if (lane == 0) wcnt[wave][bb] = __popcll(m);
+        }
+        __syncthreads();
+        if (tid < 32) {
+            int32_t run = base[tid];
+            for (int w = 0; w < 16; ++w) {
+                const int32_t t = wcnt[w][tid];
+                wcnt[w][tid] = run;
+                run += t;
+            }
+            base[tid] = run;
+        }
+        __syncthreads();
+        if (b >= 0) order[wcnt[wave][b] + rank] = (int32_t)i;
+        __syncthreads();
+    }
+}
+
+hipError_t launch_degree_order(int64_t N, const int32_t *row_ptr, int32_t *order, hipStream_t st)
+{
+    if (N == 0) return hipSuccess;
+    hipLaunchKernelGGL(degree_order, dim3(1), dim3(1024), 0, st, row_ptr, N, order);
+    return hipGetLastError();
 }
 
 hipError_t launch_transpose(int64_t N, int64_t E, const int32_t *row_ptr, const int32_t *col, int32_t *t_row_ptr,

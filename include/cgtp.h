@@ -32,8 +32,8 @@
  *    uvw weights (shared): the concatenation over paths of [mul_in][mul_out].
  *
  * Memory and streams: every device buffer is owned by the caller, must be a
- * device pointer to contiguous row-major data of the plan's dtype, 16-byte
- * aligned, and outputs must not alias inputs.  The library never allocates,
+ * device pointer to contiguous row-major data of the plan's dtype, aligned
+ * to its element size, and outputs must not alias inputs.  The library never allocates,
  * frees or synchronises device memory.  `stream` is a hipStream_t (NULL =
  * the default stream); all work is enqueued on it asynchronously.
  * Index arrays are int32 and N, E < 2^31.
@@ -139,6 +139,25 @@ cgtp_status cgtp_tp_forward(const cgtp_plan *plan, int64_t B, const void *x, con
 cgtp_status cgtp_conv_forward(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
                               const int32_t *col, const void *x, const void *y, const void *w,
                               void *out, void *stream);
+
+/*
+ * Same as cgtp_conv_forward with a receiver schedule: order [N] is a
+ * permutation of the receivers giving the order in which their rows are
+ * started (NULL = natural order).  The result does not depend on it (each
+ * receiver is still summed by one owner in CSR edge order); a heavy-first
+ * order shortens the tail on power-law graphs (LunaTP page, Abstract:
+ * node-centric execution).  The caller must pass a permutation of 0..N-1.
+ */
+cgtp_status cgtp_conv_forward_ordered(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
+                                      const int32_t *col, const int32_t *order, const void *x, const void *y,
+                                      const void *w, void *out, void *stream);
+
+/*
+ * Heavy-first receiver schedule, once per graph: order [N] (caller-owned)
+ * receives the receivers stably sorted by floor(log2(in-degree + 1)),
+ * largest first (ties keep node order).  Integer result, deterministic.
+ */
+cgtp_status cgtp_graph_order(int64_t N, const int32_t *row_ptr, int32_t *order, void *stream);
 
 /*
  * Sender-sorted transpose of a receiver CSR, once per graph: t_row_ptr [N+1],

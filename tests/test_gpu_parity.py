@@ -69,6 +69,35 @@ def test_transpose_bit_exact(device, kind):
     assert np.array_equal(td, dst[order])
 
 
+@pytest.mark.parametrize("kind", ["uniform", "powerlaw", "heavy", "empty"])
+def test_graph_order_and_ordered_forward(device, kind):
+    """Heavy-first schedule: bit-exact vs a numpy stable sort; the forward result is unchanged bitwise."""
+    import torch
+    rng = np.random.default_rng(8)
+    if kind == "uniform":
+        graph = synth.uniform_graph(3000, 90_000, rng)
+    elif kind == "powerlaw":
+        graph = synth.powerlaw_graph(4000, 120_000, 2.0, 500, rng)
+    else:
+        graph = edge_case_graph(kind, 900, rng)
+    row_ptr, col = graph
+    deg = np.diff(row_ptr).astype(np.int64)
+    bucket = np.floor(np.log2(deg + 1)).astype(np.int64)
+    want = np.argsort(-bucket, kind="stable")
+    rp = torch.from_numpy(row_ptr).to(device)
+    order = cg.graph_order(rp).cpu().numpy()
+    assert np.array_equal(order, want)
+    spec = synth.ConvSpec("order-" + kind, len(row_ptr) - 1, len(col), "32x0e+32x1o+32x2e", 2, 2)
+    case = ConvCase(spec, "f32", seed=3, graph=graph)
+    plan = cg.plan_for(spec, "f32")
+    d = to_device(case, device)
+    y = cg.spherical_harmonics(2, d["vec"])
+    a = cg.conv_forward(plan, d["row_ptr"], d["col"], d["x"], y, d["w"])
+    b = cg.conv_forward(plan, d["row_ptr"], d["col"], d["x"], y, d["w"], order=torch.from_numpy(order).to(device))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("name,dtype", CASES)
 def test_conv_forward_backward_small(device, name, dtype):
     spec = SMALL[name][0]
