@@ -194,3 +194,27 @@ def conv_backward_x_rows(tab: Tables, row_ptr, col, y, w, g, senders, n_threads=
     uniq, inv = np.unique(gd, return_inverse=True)
     return uvu_backward_x(tab, sptr, inv, np.asarray(y)[eidx], np.asarray(w)[eidx],
                           np.asarray(g)[uniq], n_threads)
+
+
+def conv_double_backward_rows(tab: Tables, row_ptr, col, x, y, w, g, ggx, ggy, ggw, rows, senders,
+                              n_threads=None):
+    """Second-order gradients on a sample, from the explicit loops above.
+
+    The convolution is linear in each of x, y, W, so the derivatives of
+    L2 = <ggx, dx> + <ggy, dy> + <ggw, dW> are first-order passes with one operand
+    replaced by its upstream gradient:
+      d/dg = conv(ggx, y, W) + conv(x, ggy, W) + conv(x, y, ggw)        (receivers ``rows``)
+      d/dy = dY(ggx, y, W; g) + dY(x, y, ggw; g),  d/dW = dW(ggx, y, W; g) + dW(x, ggy, W; g)
+                                                                         (edges of ``rows``)
+      d/dx = dx(y -> ggy, W; g) + dx(y, W -> ggw; g)                    (nodes ``senders``)
+    Returns (edge ids, dx, dy, dw, dg) with dx for ``senders`` and dg for ``rows``.
+    """
+    dg = (conv_forward_rows(tab, row_ptr, col, ggx, y, w, rows, n_threads)
+          + conv_forward_rows(tab, row_ptr, col, x, ggy, w, rows, n_threads)
+          + conv_forward_rows(tab, row_ptr, col, x, y, ggw, rows, n_threads))
+    eidx, dy_a, dw_a = conv_backward_edge_rows(tab, row_ptr, col, ggx, y, w, g, rows, n_threads)
+    _, _, dw_b = conv_backward_edge_rows(tab, row_ptr, col, x, ggy, w, g, rows, n_threads)
+    _, dy_c, _ = conv_backward_edge_rows(tab, row_ptr, col, x, y, ggw, g, rows, n_threads)
+    dx = (conv_backward_x_rows(tab, row_ptr, col, ggy, w, g, senders, n_threads)
+          + conv_backward_x_rows(tab, row_ptr, col, y, ggw, g, senders, n_threads))
+    return eidx, dx, dy_a + dy_c, dw_a + dw_b, dg

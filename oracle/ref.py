@@ -130,3 +130,56 @@ def conv_backward(prob: Problem, row_ptr, col, x, y, w, g):
     dx = np.zeros_like(x)
     np.add.at(dx, col, dxs)
     return dx, dy, dw
+
+
+def conv_double_backward(prob: Problem, row_ptr, col, x, y, w, g, ggx, ggy, ggw):
+    """Second-order gradients of the convolution (uvu).
+
+    Sources: sciencestack.ai page, Abstract (the higher partial derivatives used
+    for interatomic forces); OpenEquivariance discussion page (a convolution
+    double backward with four results); Sobek page, Abstract (forward, backward
+    and double backward of the same operator).
+
+    With (dx, dy, dW) = conv_backward(x, y, W, g) and upstream gradients
+    (ggx, ggy, ggw) for them, the scalar is
+        L2 = <ggx, dx> + <ggy, dy> + <ggw, dW>
+           = sum over edges e = (s -> n), paths p, channels u, nonzeros (i, j, k, c) of
+             c * g[n,u,k] * (ggx[s,u,i] y[e,j] W[e,p,u] + x[s,u,i] ggy[e,j] W[e,p,u]
+                             + x[s,u,i] y[e,j] ggw[e,p,u])
+    and the four results are its derivatives, term by term:
+      d/dx[s,u,i]   = sum c g_k (ggy_j W + y_j ggw)          (summed over the edges of s)
+      d/dy[e,j]     = sum_u c g_k (ggx_i W + x_i ggw)
+      d/dW[e,p,u]   = sum c g_k (ggx_i y_j + x_i ggy_j)
+      d/dg[n,u,k]   = sum c (ggx_i y_j W + x_i ggy_j W + x_i y_j ggw)   (summed over the edges of n)
+    Returns (dx, dy, dw, dg), float64.
+    """
+    x, y, w, g, ggx, ggy, ggw = (np.asarray(a, np.float64) for a in (x, y, w, g, ggx, ggy, ggw))
+    col = np.asarray(col, np.int64)
+    dst = receivers_of(row_ptr)
+    n_edges = len(col)
+    xs, gxs, gs = x[col], ggx[col], g[dst]
+    dxs = np.zeros_like(xs)
+    dy = np.zeros_like(y)
+    dw = np.zeros_like(w)
+    dgs = np.zeros((n_edges, prob.d_out))
+    for p, a, b, o, mul, _, nz in _path_terms(prob):
+        n1, n3 = 2 * p.l1 + 1, 2 * p.l3 + 1
+        xb = xs[:, a:a + mul * n1].reshape(n_edges, mul, n1)
+        gxb = gxs[:, a:a + mul * n1].reshape(n_edges, mul, n1)
+        dxb = dxs[:, a:a + mul * n1].reshape(n_edges, mul, n1)
+        gb = gs[:, o:o + mul * n3].reshape(n_edges, mul, n3)
+        dgb = dgs[:, o:o + mul * n3].reshape(n_edges, mul, n3)
+        wb = w[:, p.w_off:p.w_off + mul]
+        gwb = ggw[:, p.w_off:p.w_off + mul]
+        for i, j, k, c in nz:
+            yj = y[:, b + j][:, None]
+            gyj = ggy[:, b + j][:, None]
+            dxb[:, :, i] += c * gb[:, :, k] * (gyj * wb + yj * gwb)
+            dy[:, b + j] += np.sum(c * gb[:, :, k] * (gxb[:, :, i] * wb + xb[:, :, i] * gwb), axis=1)
+            dw[:, p.w_off:p.w_off + mul] += c * gb[:, :, k] * (gxb[:, :, i] * yj + xb[:, :, i] * gyj)
+            dgb[:, :, k] += c * (gxb[:, :, i] * yj * wb + xb[:, :, i] * gyj * wb + xb[:, :, i] * yj * gwb)
+    dx = np.zeros_like(x)
+    np.add.at(dx, col, dxs)
+    dg = np.zeros_like(g)
+    np.add.at(dg, dst, dgs)
+    return dx, dy, dw, dg

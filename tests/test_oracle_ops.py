@@ -257,3 +257,111 @@ def test_planted_mistake_is_caught_by_equivariance(monkeypatch, kind):
     out = ref.conv_forward(prob, row_ptr, col, x, y, w)
     out_rot = ref.conv_forward(prob, row_ptr, col, x @ d_in.T, y_rot, w)
     assert np.abs(out_rot - out @ d_out.T).max() > 1e-3
+
+
+# ------------------------------------------------------------------------------ double backward
+
+def _dbl_inputs(prob, rng, n_nodes=6, n_edges=21):
+    row_ptr, col, x, vec, w, g = conv_inputs(prob, rng, n_nodes, n_edges)
+    y = rng.standard_normal((len(col), prob.d_sh))
+    ggx = rng.standard_normal(x.shape)
+    ggy = rng.standard_normal(y.shape)
+    ggw = rng.standard_normal(w.shape)
+    return row_ptr, col, x, y, w, g, ggx, ggy, ggw
+
+
+@pytest.mark.parametrize("in_irreps,lmax_sh,lmax_out", [("3x0e+3x1o+3x2e", 2, 2), ("2x1o+1x2e", 1, 3)])
+def test_double_backward_matches_autograd_of_dense_einsum(in_irreps, lmax_sh, lmax_out):
+    """Brute force: torch autograd (CPU, float64) differentiates twice through the dense coupling."""
+    import torch
+    prob = problem(in_irreps, lmax_sh, lmax_out)
+    rng = np.random.default_rng(11)
+    row_ptr, col, x, y, w, g, ggx, ggy, ggw = _dbl_inputs(prob, rng)
+    t = torch.from_numpy(dense_tensor(prob))
+    dst = torch.from_numpy(ref.receivers_of(row_ptr))
+    colt = torch.from_numpy(np.asarray(col, np.int64))
+    X, Y, W, G = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (x, y, w, g))
+
+    def forward(x_, y_, w_):
+        msg = torch.einsum("abvo,ea,eb,ev->eo", t, x_[colt], y_, w_)
+        return torch.zeros(len(row_ptr) - 1, prob.d_out, dtype=torch.float64).index_add(0, dst, msg)
+
+    first = torch.autograd.grad((G * forward(X, Y, W)).sum(), (X, Y, W), create_graph=True)
+    l2 = sum((torch.from_numpy(u) * v).sum() for u, v in zip((ggx, ggy, ggw), first))
+    want = torch.autograd.grad(l2, (X, Y, W, G))
+    got = ref.conv_double_backward(prob, row_ptr, col, x, y, w, g, ggx, ggy, ggw)
+    for a, b in zip(got, want):
+        assert np.allclose(a, b.numpy(), atol=1e-11, rtol=1e-11)
+
+
+def test_double_backward_finite_differences():
+    prob = problem("2x0e+2x1o+1x2e", 2, 2)
+    rng = np.random.default_rng(12)
+    row_ptr, col, x, y, w, g, ggx, ggy, ggw = _dbl_inputs(prob, rng, 5, 13)
+    got = ref.conv_double_backward(prob, row_ptr, col, x, y, w, g, ggx, ggy, ggw)
+
+    def l2(x_, y_, w_, g_):
+        dx, dy, dw = ref.conv_backward(prob, row_ptr, col, x_, y_, w_, g_)
+        return np.sum(ggx * dx) + np.sum(ggy * dy) + np.sum(ggw * dw)
+
+    h = 1e-6
+    base = [x, y, w, g]
+    for which in range(4):
+        for _ in range(5):
+            arr = base[which]
+            idx = tuple(rng.integers(0, s) for s in arr.shape)
+            args_p, args_m = list(base), list(base)
+            args_p[which], args_m[which] = arr.copy(), arr.copy()
+            args_p[which][idx] += h
+            args_m[which][idx] -= h
+            fd = (l2(*args_p) - l2(*args_m)) / (2 * h)
+            assert abs(fd - got[which][idx]) < 1e-6 * max(1.0, abs(got[which][idx]))
+
+
+def test_double_backward_euler_identities():
+    """L2 = A + B + C is linear in each operand: <d/dx, x> = B + C, <d/dy, y> = A + C,
+    <d/dW, W> = A + B, <d/dg, g> = A + B + C with A = <ggx, dx>, B = <ggy, dy>, C = <ggw, dW>."""
+    prob = problem()
+    rng = np.random.default_rng(13)
+    row_ptr, col, x, y, w, g, ggx, ggy, ggw = _dbl_inputs(prob, rng, 8, 33)
+    dx1, dy1, dw1 = ref.conv_backward(prob, row_ptr, col, x, y, w, g)
+    A, B, C = np.sum(ggx * dx1), np.sum(ggy * dy1), np.sum(ggw * dw1)
+    dx, dy, dw, dg = ref.conv_double_backward(prob, row_ptr, col, x, y, w, g, ggx, ggy, ggw)
+    scale = max(1.0, abs(A) + abs(B) + abs(C))
+    for got, want in ((np.sum(dx * x), B + C), (np.sum(dy * y), A + C), (np.sum(dw * w), A + B),
+                      (np.sum(dg * g), A + B + C)):
+        assert abs(got - want) <= 1e-11 * scale
+
+
+@pytest.mark.parametrize("improper", [False, True])
+def test_double_backward_equivariance(improper):
+    prob = problem()
+    row_ptr, col, x, y, w, g, d_in, d_sh, d_out, y_rot = _rotate_case(prob, improper)
+    rng = np.random.default_rng(14)
+    ggx = rng.standard_normal(x.shape)
+    ggy = rng.standard_normal(y.shape)
+    ggw = rng.standard_normal(w.shape)
+    base = ref.conv_double_backward(prob, row_ptr, col, x, y, w, g, ggx, ggy, ggw)
+    rot = ref.conv_double_backward(prob, row_ptr, col, x @ d_in.T, y_rot, w, g @ d_out.T, ggx @ d_in.T,
+                                   ggy @ d_sh.T, ggw)
+    for got, want in zip(rot, (base[0] @ d_in.T, base[1] @ d_sh.T, base[2], base[3] @ d_out.T)):
+        assert np.allclose(got, want, atol=1e-10)
+
+
+@pytest.mark.parametrize("in_f32", [False, True])
+def test_cpu_loops_double_backward_match_numpy(in_f32):
+    prob = problem()
+    rng = np.random.default_rng(15)
+    row_ptr, col, x, y, w, g, ggx, ggy, ggw = _dbl_inputs(prob, rng, 9, 40)
+    if in_f32:
+        x, y, w, g, ggx, ggy, ggw = (a.astype(np.float32) for a in (x, y, w, g, ggx, ggy, ggw))
+    want = ref.conv_double_backward(prob, row_ptr, col, x, y, w, g, ggx, ggy, ggw)
+    tab = loops.Tables(prob)
+    rows = np.array([4, 0, 7, 2])
+    senders = np.array([3, 8, 1])
+    eidx, dx, dy, dw, dg = loops.conv_double_backward_rows(tab, row_ptr, col, x, y, w, g, ggx, ggy, ggw,
+                                                           rows, senders)
+    assert np.allclose(dg, want[3][rows], atol=1e-12)
+    assert np.allclose(dy, want[1][eidx], atol=1e-12)
+    assert np.allclose(dw, want[2][eidx], atol=1e-12)
+    assert np.allclose(dx, want[0][senders], atol=1e-12)
