@@ -64,17 +64,31 @@ def algorithmic_bytes(plan, N, E, es):
     return fwd, bwd
 
 
+def kernel_digest(source, kernel):
+    """SHA-1 of the generated code one kernel runs: the module's shared preamble plus that
+    kernel's own section (the generator marks sections with '// @@section NAME' lines)."""
+    import hashlib
+    parts, name = {}, None
+    for line in source.splitlines(keepends=True):
+        if line.startswith("// @@section "):
+            name = line[len("// @@section "):].strip()
+        parts[name] = parts.get(name, "") + line
+    if "common" not in parts or kernel not in parts:
+        return None
+    return hashlib.sha1((parts["common"] + parts[kernel]).encode()).hexdigest()
+
+
 def measured_traffic(plan, spec, dtype, kernel):
     """HBM-side bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE record, scaled
-    by the copy-kernel calibration; None when no record exists for this exact generated module."""
+    by the copy-kernel calibration; None unless the record was taken on exactly this kernel's code."""
     import glob
-    import hashlib
-    digest = hashlib.sha1(plan.source.encode()).hexdigest()
+    digest = kernel_digest(plan.source, kernel)
     for path in glob.glob(os.path.join(ROOT, "profiles", "*_hbm_counters.json")):
         rec = json.load(open(path))
-        if rec.get("module_sha1") != digest or rec.get("dtype") != dtype or kernel not in rec.get("kernels", {}):
+        k = rec.get("kernels", {}).get(kernel)
+        if digest is None or k is None or k.get("code_sha1") != digest or rec.get("dtype") != dtype:
             continue
-        k, cal = rec["kernels"][kernel], rec["calibration"]
+        cal = rec["calibration"]
         kib = (k["FETCH_SIZE_kib_per_dispatch"] * cal["fetch_factor"]
                + k["WRITE_SIZE_kib_per_dispatch"] * cal["write_factor"]) * k["dispatches_per_call"]
         return kib * 1024

@@ -22,7 +22,7 @@ STATUS_CODES = {v: k for k, v in STATUS.items()}
 EXPORTS = ("cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info_get", "cgtp_plan_path",
            "cgtp_plan_path_coefficients", "cgtp_plan_source", "cgtp_tp_forward", "cgtp_conv_forward",
            "cgtp_graph_transpose", "cgtp_conv_backward", "cgtp_spherical_harmonics", "cgtp_last_error",
-           "cgtp_conv_forward_ordered", "cgtp_graph_order")
+           "cgtp_conv_forward_ordered", "cgtp_graph_order", "cgtp_conv_double_backward")
 
 
 class CgtpError(RuntimeError):
@@ -280,6 +280,33 @@ def conv_backward(plan: Plan, row_ptr, col, transpose, x, y, w, grad_out, grad_x
         _ptr_or_null(gx, "grad_x", dt, (N, plan.d_x)), _ptr_or_null(gy, "grad_y", dt, (E, plan.d_sh)),
         _ptr_or_null(gw, "grad_w", dt, (E, plan.weight_numel)), _stream(stream, dev)))
     return gx, gy, gw
+
+
+def conv_double_backward(plan: Plan, row_ptr, col, transpose, x, y, w, grad_out, gg_x, gg_y, gg_w, order=None,
+                         outs=(None, None, None, None), need=(True, True, True, True), stream=None):
+    """Second-order gradients (grad_x, grad_y, grad_w, grad_grad_out) of
+    <gg_x, dx> + <gg_y, dy> + <gg_w, dW>, where (dx, dy, dW) = conv_backward(x, y, w, grad_out).
+    An upstream gradient given as None is passed as zeros.  Entries not in ``need`` are None
+    and not computed."""
+    import torch
+    N, E = row_ptr.shape[0] - 1, col.shape[0]
+    dt = plan.torch_dtype
+    dev = x.device
+    shapes = ((N, plan.d_x), (E, plan.d_sh), (E, plan.weight_numel), (N, plan.d_out))
+    gg = [torch.zeros(sh, dtype=dt, device=dev) if t is None else t for t, sh in zip((gg_x, gg_y, gg_w), shapes)]
+    res = [None if not nd else (torch.empty(sh, dtype=dt, device=dev) if o is None else o)
+           for o, nd, sh in zip(outs, need, shapes)]
+    t_row_ptr, t_edge, t_dst = transpose
+    names = ("grad_x", "grad_y", "grad_w", "grad_grad_out")
+    _check(lib().cgtp_conv_double_backward(
+        plan.handle, N, E, _dev(row_ptr, "row_ptr", torch.int32), _dev(col, "col", torch.int32),
+        _ptr_or_null(order, "order", torch.int32, (N,)),
+        _dev(t_row_ptr, "t_row_ptr", torch.int32, (N + 1,)), _dev(t_edge, "t_edge", torch.int32, (E,)),
+        _dev(t_dst, "t_dst", torch.int32, (E,)), _dev(x, "x", dt, shapes[0]), _dev(y, "y", dt, shapes[1]),
+        _dev(w, "w", dt, shapes[2]), _dev(grad_out, "grad_out", dt, shapes[3]),
+        _dev(gg[0], "gg_x", dt, shapes[0]), _dev(gg[1], "gg_y", dt, shapes[1]), _dev(gg[2], "gg_w", dt, shapes[2]),
+        *[_ptr_or_null(r, nm, dt, sh) for r, nm, sh in zip(res, names, shapes)], _stream(stream, dev)))
+    return tuple(res)
 
 
 def spherical_harmonics(lmax: int, vec, out=None, stream=None):

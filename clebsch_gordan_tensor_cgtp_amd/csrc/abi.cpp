@@ -127,8 +127,12 @@ cgtp_status cgtp_plan_create(const char *in_irreps, const char *sh_irreps, const
                 std::fprintf(stderr, "[cgtp]   bwd group %zu: %zu paths, mul %d, ct %d, tiles %d, prefetch %d\n", k,
                              P.bwd_groups[k].paths.size(), P.bwd_groups[k].mul, P.bwd_groups[k].ct,
                              P.bwd_groups[k].tiles, (int)P.bwd_groups[k].prefetch);
-            std::fprintf(stderr, "[cgtp]   waves/SIMD targets: fwd %d, bwd %d\n", P.fwd_waves_per_eu,
-                         P.bwd_waves_per_eu);
+            for (size_t k = 0; k < P.dbl_groups.size(); ++k)
+                std::fprintf(stderr, "[cgtp]   double-backward sender group %zu: %zu paths, mul %d, ct %d, tiles %d\n", k,
+                             P.dbl_groups[k].paths.size(), P.dbl_groups[k].mul, P.dbl_groups[k].ct,
+                             P.dbl_groups[k].tiles);
+            std::fprintf(stderr, "[cgtp]   waves/SIMD targets: fwd %d, bwd %d, double backward %d / %d\n",
+                         P.fwd_waves_per_eu, P.bwd_waves_per_eu, P.dbl_fwd_waves_per_eu, P.dbl_bwd_waves_per_eu);
         }
         *plan_out = h.release();
     });
@@ -380,6 +384,81 @@ cgtp_status cgtp_conv_backward(const cgtp_plan *plan, int64_t N, int64_t E, cons
             check_hip(hipModuleLaunchKernel(L.conv_bwd, (unsigned)N, 1, 1, 64 * wpr, 1, 1, 0,
                                             static_cast<hipStream_t>(stream), args, nullptr),
                       "hipModuleLaunchKernel");
+        }
+    });
+}
+
+cgtp_status cgtp_conv_double_backward(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
+                                      const int32_t *col, const int32_t *order, const int32_t *t_row_ptr,
+                                      const int32_t *t_edge, const int32_t *t_dst, const void *x, const void *y,
+                                      const void *w, const void *grad_out, const void *gg_x, const void *gg_y,
+                                      const void *gg_w, void *grad_x, void *grad_y, void *grad_w,
+                                      void *grad_grad_out, void *stream)
+{
+    return guarded([&] {
+        require(plan != nullptr, "plan is NULL");
+        cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
+        check_graph_sizes(N, E);
+        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw convolution is not built yet");
+        if (N == 0) return;
+        const bool send = grad_x || grad_y || grad_w;
+        if (!send && !grad_grad_out) return;
+        const size_t es = elem(P);
+        require_ptr(row_ptr, "row_ptr", 4);
+        require_ptr(x, "x", es);
+        require_ptr(gg_x, "gg_x", es);
+        if (send) require_ptr(t_row_ptr, "t_row_ptr", 4);
+        if (E > 0) {
+            require_ptr(col, "col", 4);
+            require_ptr(y, "y", es);
+            require_ptr(w, "w", es);
+            require_ptr(gg_y, "gg_y", es);
+            require_ptr(gg_w, "gg_w", es);
+            if (send) {
+                require_ptr(t_edge, "t_edge", 4);
+                require_ptr(t_dst, "t_dst", 4);
+                require_ptr(grad_out, "grad_out", es);
+            }
+        }
+        if (order) require_ptr(order, "order", 4);
+        if (grad_x) require_ptr(grad_x, "grad_x", es);
+        if (E > 0 && grad_y) require_ptr(grad_y, "grad_y", es);
+        if (E > 0 && grad_w) require_ptr(grad_w, "grad_w", es);
+        if (grad_grad_out) require_ptr(grad_grad_out, "grad_grad_out", es);
+        const void *ins[] = {x, y, w, grad_out, gg_x, gg_y, gg_w, row_ptr, col, order, t_row_ptr, t_edge, t_dst};
+        const size_t inn[] = {N * P.d_x * es, E * P.d_sh * es, E * P.w_numel * es, N * P.d_out * es,
+                              N * P.d_x * es, E * P.d_sh * es, E * P.w_numel * es, (size_t)(N + 1) * 4,
+                              (size_t)E * 4, (size_t)N * 4, (size_t)(N + 1) * 4, (size_t)E * 4, (size_t)E * 4};
+        const char *inm[] = {"x", "y", "w", "grad_out", "gg_x", "gg_y", "gg_w", "row_ptr", "col", "order",
+                             "t_row_ptr", "t_edge", "t_dst"};
+        void *outs[] = {grad_x, grad_y, grad_w, grad_grad_out};
+        const size_t outn[] = {N * P.d_x * es, E * P.d_sh * es, E * P.w_numel * es, N * P.d_out * es};
+        const char *outm[] = {"grad_x", "grad_y", "grad_w", "grad_grad_out"};
+        for (int a = 0; a < 4; ++a) {
+            for (int b = 0; b < 13; ++b) require_disjoint(outs[a], outn[a], outm[a], ins[b], inn[b], inm[b]);
+            for (int b = a + 1; b < 4; ++b) require_disjoint(outs[a], outn[a], outm[a], outs[b], outn[b], outm[b]);
+        }
+        const auto &L = cgtp::module_for_current_device(P);
+        if (grad_grad_out) {
+            // receiver pass: d/dg = conv(gg_x, y, w) + conv(x, gg_y, w) + conv(x, y, gg_w)
+            int64_t waves = N * P.fwd_tasks;
+            long nrows = (long)N, nwaves = (long)waves;
+            void *args[] = {&row_ptr, &col, &x, &y, &w, &gg_x, &gg_y, &gg_w, &grad_grad_out, &nrows, &nwaves, &order};
+            launch(L.dbwd_recv, waves, args, stream);
+        }
+        if (send) {
+            // sender pass over the transpose: d/dx, d/dy, d/dW (one owner per output row)
+            long nnodes = (long)N;
+            for (int grp = 0; grp < (int)P.dbl_groups.size(); ++grp) {
+                const double groups = (double)E / (double)N / P.dbl_groups[grp].es;
+                int wpr = groups >= 16 ? 4 : groups >= 8 ? 2 : 1;
+                if (const char *env = std::getenv("CGTP_BWD_WPR")) wpr = std::max(1, std::min(4, std::atoi(env)));
+                void *args[] = {&t_row_ptr, &t_edge, &t_dst, &x, &y, &w, &grad_out, &gg_x, &gg_y, &gg_w,
+                                &grad_x, &grad_y, &grad_w, &nnodes, &wpr, &grp};
+                check_hip(hipModuleLaunchKernel(L.dbwd_send, (unsigned)N, 1, 1, 64 * wpr, 1, 1, 0,
+                                                static_cast<hipStream_t>(stream), args, nullptr),
+                          "hipModuleLaunchKernel");
+            }
         }
     });
 }

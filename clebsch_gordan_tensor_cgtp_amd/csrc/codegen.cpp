@@ -105,7 +105,7 @@ bool needs_mask(int mul, const Group &g) { return mul != g.tiles * g.ct; }
 // Emit loads of the sender row (x), the edge row (y) and the weights of edge index `ei`
 // and sender `si` into registers named <pre>x.., <pre>y.., <pre>w..
 void emit_edge_loads(Out &o, const Plan &P, const Group &g, const Touch &t, const std::string &pre,
-                     const std::string &si, const std::string &ei, bool declare)
+                     const std::string &si, const std::string &ei, bool declare, bool dbl = false)
 {
     const std::string T = declare ? "T " : "";
     for (int b : t.i1) {
@@ -139,15 +139,99 @@ void emit_edge_loads(Out &o, const Plan &P, const Group &g, const Touch &t, cons
         else
             o(T, pre, "w", pi, " = ", addr.str(), ";");
     }
+    if (!dbl) return;
+    // double backward: the upstream gradients for dx (gathered like x), dY and dW
+    for (int b : t.i1) {
+        const Irrep &ir = P.ins[b];
+        int off = 0;
+        for (int pi : g.paths)
+            if (P.paths[pi].i1 == b) off = P.paths[pi].a;
+        bool m = needs_mask(ir.mul, g);
+        for (int i = 0; i < n_of(ir.l); ++i) {
+            std::ostringstream addr;
+            addr << "ggx[(size_t)" << si << " * DX + " << off << " + u * " << n_of(ir.l) << " + " << i << "]";
+            if (m)
+                o(T, pre, "gx", b, "_", i, " = (u < ", ir.mul, ") ? ", addr.str(), " : (T)0;");
+            else
+                o(T, pre, "gx", b, "_", i, " = ", addr.str(), ";");
+        }
+    }
+    for (int b : t.i2) {
+        int off = 0;
+        for (int pi : g.paths)
+            if (P.paths[pi].i2 == b) off = P.paths[pi].b;
+        for (int j = 0; j < n_of(P.sh[b].l); ++j)
+            o(T, pre, "gy", b, "_", j, " = LD_STREAM(&ggy[(size_t)", ei, " * DSH + ", off + j, "]);");
+    }
+    for (int pi : g.paths) {
+        const Path &p = P.paths[pi];
+        std::ostringstream addr;
+        addr << "LD_STREAM(&ggw[(size_t)" << ei << " * WROW + " << p.w_off << " + u])";
+        if (needs_mask(p.mul_in, g))
+            o(T, pre, "gw", pi, " = (u < ", p.mul_in, ") ? ", addr.str(), " : (T)0;");
+        else
+            o(T, pre, "gw", pi, " = ", addr.str(), ";");
+    }
 }
 
-void emit_copy(Out &o, const Plan &P, const Group &g, const Touch &t, const std::string &dst, const std::string &src)
+void emit_copy(Out &o, const Plan &P, const Group &g, const Touch &t, const std::string &dst, const std::string &src,
+               bool dbl = false)
 {
     for (int b : t.i1)
         for (int i = 0; i < n_of(P.ins[b].l); ++i) o(dst, "x", b, "_", i, " = ", src, "x", b, "_", i, ";");
     for (int b : t.i2)
         for (int j = 0; j < n_of(P.sh[b].l); ++j) o(dst, "y", b, "_", j, " = ", src, "y", b, "_", j, ";");
     for (int pi : g.paths) o(dst, "w", pi, " = ", src, "w", pi, ";");
+    if (!dbl) return;
+    for (int b : t.i1)
+        for (int i = 0; i < n_of(P.ins[b].l); ++i) o(dst, "gx", b, "_", i, " = ", src, "gx", b, "_", i, ";");
+    for (int b : t.i2)
+        for (int j = 0; j < n_of(P.sh[b].l); ++j) o(dst, "gy", b, "_", j, " = ", src, "gy", b, "_", j, ";");
+    for (int pi : g.paths) o(dst, "gw", pi, " = ", src, "gw", pi, ";");
+}
+
+// Linear combination sum_n c_n * <reg prefix><i>_<j> of the nonzeros in v, as nested FMAs.
+std::string cg_sum(const std::vector<const Nonzero *> &v, const std::string &reg, bool f64)
+{
+    std::ostringstream e;
+    e << lit(v[0]->c, f64) << " * " << reg << v[0]->i << "_" << v[0]->j;
+    for (size_t n = 1; n < v.size(); ++n) {
+        std::ostringstream f;
+        f << "FMA(" << lit(v[n]->c, f64) << ", " << reg << v[n]->i << "_" << v[n]->j << ", " << e.str() << ")";
+        e.str(f.str());
+    }
+    return e.str();
+}
+
+// Double backward, receiver pass: d/dg of <ggx,dx> + <ggy,dy> + <ggw,dW> is the
+// convolution of (ggx, y, W) + (x, ggy, W) + (x, y, ggw), so per path and k
+//   acc[k] += w * sum C (ggx_i y_j + x_i ggy_j) + ggw * sum C x_i y_j.
+void emit_dbl_recv_math(Out &o, const Plan &P, const Group &g, bool f64, const std::string &pre)
+{
+    for (auto &pr : pairs_of(P, g.paths)) {
+        int i1 = pr.first.first, i2 = pr.first.second;
+        std::set<std::pair<int, int>> used;
+        for (int pi : pr.second)
+            for (const Nonzero &z : P.paths[pi].nz) used.insert({z.i, z.j});
+        o("{");
+        o.ind++;
+        for (auto &ij : used) {
+            const int i = ij.first, j = ij.second;
+            o("const T q", i, "_", j, " = ", pre, "x", i1, "_", i, " * ", pre, "y", i2, "_", j, ";");
+            o("const T r", i, "_", j, " = FMA(", pre, "x", i1, "_", i, ", ", pre, "gy", i2, "_", j, ", ", pre, "gx", i1,
+              "_", i, " * ", pre, "y", i2, "_", j, ");");
+        }
+        for (int pi : pr.second) {
+            const Path &p = P.paths[pi];
+            std::map<int, std::vector<const Nonzero *>> byk;
+            for (const Nonzero &z : p.nz) byk[z.k].push_back(&z);
+            for (auto &kv : byk)
+                o("a", p.slot, "_", kv.first, " = FMA(", pre, "w", pi, ", ", cg_sum(kv.second, "r", f64), ", FMA(", pre,
+                  "gw", pi, ", ", cg_sum(kv.second, "q", f64), ", a", p.slot, "_", kv.first, "));");
+        }
+        o.ind--;
+        o("}");
+    }
 }
 
 // acc[slot][k] += w_p * sum_{ij} C_ijk x_i y_j for every path of the group.
@@ -208,15 +292,19 @@ void emit_preamble(Out &o, const Plan &P)
     o("");
 }
 
-// Forward body of one group; `n` is the receiver (conv) or -1 (rows mode).
-void emit_fwd_group(Out &o, const Plan &P, int gi, bool rows)
+// Forward body of one group; `n` is the receiver (conv) or the row block (rows
+// mode).  With dbl, the same receiver-owned stream computes the double
+// backward's d/dg (emit_dbl_recv_math) from the extra operands ggx, ggy, ggw.
+void emit_fwd_group(Out &o, const Plan &P, int gi, bool rows, bool dbl = false)
 {
     const Group &g = P.fwd_groups[gi];
     const bool f64 = P.dtype == CGTP_F64;
     Touch t = touched(P, g.paths);
-    o("__device__ __forceinline__ void ", rows ? "tp" : "fwd", "_g", gi,
+    o("__device__ __forceinline__ void ", rows ? "tp" : dbl ? "dbr" : "fwd", "_g", gi,
       "(long n, int tile, int lane, const int* __restrict__ row_ptr, const int* __restrict__ col, "
-      "const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows)");
+      "const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, ",
+      dbl ? "const T* __restrict__ ggx, const T* __restrict__ ggy, const T* __restrict__ ggw, " : "",
+      "T* __restrict__ out, long nrows)");
     o("{");
     o.ind++;
     o("const int slot = lane >> ", log2i(g.ct), ";");
@@ -253,14 +341,17 @@ void emit_fwd_group(Out &o, const Plan &P, int gi, bool rows)
         o("int s = col[ec];");
         o("int en = (e + ", g.es, " < e1) ? e + ", g.es, " : e1 - 1;");
         o("int sn = col[en];");
-        emit_edge_loads(o, P, g, t, "c", "s", "ec", true);
+        emit_edge_loads(o, P, g, t, "c", "s", "ec", true, dbl);
         o("for (; e < e1; e += ", g.es, ") {");
         o.ind++;
         o("const int enn = (e + ", 2 * g.es, " < e1) ? e + ", 2 * g.es, " : e1 - 1;");
         o("const int snn = col[enn];");
-        emit_edge_loads(o, P, g, t, "n", "sn", "en", true);
-        emit_forward_math(o, P, g, f64, "c");
-        emit_copy(o, P, g, t, "c", "n");
+        emit_edge_loads(o, P, g, t, "n", "sn", "en", true, dbl);
+        if (dbl)
+            emit_dbl_recv_math(o, P, g, f64, "c");
+        else
+            emit_forward_math(o, P, g, f64, "c");
+        emit_copy(o, P, g, t, "c", "n", dbl);
         o("en = enn;");
         o("sn = snn;");
         o.ind--;
@@ -295,12 +386,14 @@ void emit_fwd_group(Out &o, const Plan &P, int gi, bool rows)
     o("");
 }
 
-void emit_fwd_kernel(Out &o, const Plan &P, bool rows)
+void emit_fwd_kernel(Out &o, const Plan &P, bool rows, bool dbl = false)
 {
-    o("extern \"C\" __global__ void __launch_bounds__(256, ", P.fwd_waves_per_eu, ") ", rows ? "cgtp_tp_fwd" : "cgtp_conv_fwd",
+    o("extern \"C\" __global__ void __launch_bounds__(256, ", dbl ? P.dbl_fwd_waves_per_eu : P.fwd_waves_per_eu, ") ",
+      rows ? "cgtp_tp_fwd" : dbl ? "cgtp_conv_dbwd_recv" : "cgtp_conv_fwd",
       "(const int* __restrict__ row_ptr, const int* __restrict__ col, const T* __restrict__ x, "
-      "const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows, long nwaves, "
-      "const int* __restrict__ order)");
+      "const T* __restrict__ y, const T* __restrict__ w, ",
+      dbl ? "const T* __restrict__ ggx, const T* __restrict__ ggy, const T* __restrict__ ggw, " : "",
+      "T* __restrict__ out, long nrows, long nwaves, const int* __restrict__ order)");
     o("{");
     o.ind++;
     o("const long wave = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
@@ -313,8 +406,8 @@ void emit_fwd_kernel(Out &o, const Plan &P, bool rows)
     int task = 0;
     for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi)
         for (int tile = 0; tile < P.fwd_groups[gi].tiles; ++tile, ++task)
-            o("case ", task, ": ", rows ? "tp" : "fwd", "_g", gi, "(n, ", tile,
-              ", lane, row_ptr, col, x, y, w, out, nrows); break;");
+            o("case ", task, ": ", rows ? "tp" : dbl ? "dbr" : "fwd", "_g", gi, "(n, ", tile,
+              ", lane, row_ptr, col, x, y, w, ", dbl ? "ggx, ggy, ggw, " : "", "out, nrows); break;");
     o("default: break;");
     o("}");
     o.ind--;
@@ -361,22 +454,23 @@ void emit_slot_sum(Out &o, const Plan &P)
 // and dY blocks are written by the first group that touches them (group 0 also
 // writes zeros for blocks no path touches) and accumulated by later groups;
 // the groups are separate launches in group order, so the sums are fixed.
-void emit_bwd_group(Out &o, const Plan &P, int gi)
+void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false)
 {
-    const Group &g = P.bwd_groups[gi];
+    const std::vector<Group> &groups = dbl ? P.dbl_groups : P.bwd_groups;
+    const Group &g = groups[gi];
     const bool f64 = P.dtype == CGTP_F64;
     const bool pf = g.prefetch;
     Touch t = touched(P, g.paths);
     // first group (in launch order) touching each input / SH block
     auto first_i1 = [&](int b) {
-        for (int k = 0; k < (int)P.bwd_groups.size(); ++k)
-            for (int pi : P.bwd_groups[k].paths)
+        for (int k = 0; k < (int)groups.size(); ++k)
+            for (int pi : groups[k].paths)
                 if (P.paths[pi].i1 == b) return k;
         return -1;
     };
     auto first_i2 = [&](int b) {
-        for (int k = 0; k < (int)P.bwd_groups.size(); ++k)
-            for (int pi : P.bwd_groups[k].paths)
+        for (int k = 0; k < (int)groups.size(); ++k)
+            for (int pi : groups[k].paths)
                 if (P.paths[pi].i2 == b) return k;
         return -1;
     };
@@ -389,10 +483,12 @@ void emit_bwd_group(Out &o, const Plan &P, int gi)
     for (int b = 0; b < (int)P.sh.size(); ++b)
         if (t.i2.count(b) || (gi == 0 && first_i2(b) < 0)) yb.push_back(b);
 
-    o("__device__ __forceinline__ void bwd_g", gi,
+    o("__device__ __forceinline__ void ", dbl ? "dbs" : "bwd", "_g", gi,
       "(long s, int wv, int lane, int wpr, T* red, const int* __restrict__ t_row_ptr, const int* __restrict__ t_edge, "
       "const int* __restrict__ t_dst, const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, "
-      "const T* __restrict__ g, T* __restrict__ dx, T* __restrict__ dy, T* __restrict__ dw)");
+      "const T* __restrict__ g, ",
+      dbl ? "const T* __restrict__ ggx, const T* __restrict__ ggy, const T* __restrict__ ggw, " : "",
+      "T* __restrict__ dx, T* __restrict__ dy, T* __restrict__ dw)");
     o("{");
     o.ind++;
     o("const int slot = lane >> ", log2i(g.ct), ";");
@@ -414,6 +510,13 @@ void emit_bwd_group(Out &o, const Plan &P, int gi)
                     o("const T x", b, "_", i, " = (u < ", ir.mul, ") ? ", addr, " : (T)0;");
                 else
                     o("const T x", b, "_", i, " = ", addr, ";");
+                if (dbl) {
+                    std::string gaddr = "ggx" + addr.substr(1);
+                    if (needs_mask(ir.mul, g))
+                        o("const T gx", b, "_", i, " = (u < ", ir.mul, ") ? ", gaddr, " : (T)0;");
+                    else
+                        o("const T gx", b, "_", i, " = ", gaddr, ";");
+                }
             }
             o("T d", b, "_", i, " = (T)0;");
         }
@@ -446,6 +549,21 @@ void emit_bwd_group(Out &o, const Plan &P, int gi)
                 else
                     o(Ty, pre, "g", q, "_", k, " = ", ga, ";");
             }
+        }
+        if (!dbl) return;
+        for (int b : t.i2) {
+            int off = 0;
+            for (int bb = 0; bb < b; ++bb) off += P.sh[bb].dim();
+            for (int j = 0; j < n_of(P.sh[b].l); ++j)
+                o(Ty, pre, "gy", b, "_", j, " = LD_STREAM(&ggy[(size_t)", ev, " * DSH + ", off + j, "]);");
+        }
+        for (int pi : g.paths) {
+            const Path &p = P.paths[pi];
+            std::string wa = "LD_STREAM(&ggw[(size_t)" + ev + " * WROW + " + std::to_string(p.w_off) + " + u])";
+            if (needs_mask(p.mul_in, g))
+                o(Ty, pre, "gw", pi, " = (u < ", p.mul_in, ") ? ", wa, " : (T)0;");
+            else
+                o(Ty, pre, "gw", pi, " = ", wa, ";");
         }
     };
     // pipeline: edge and receiver ids two iterations ahead, operands one ahead
@@ -491,47 +609,68 @@ void emit_bwd_group(Out &o, const Plan &P, int gi)
             rows[kv.first.first].push_back(kv.first.second);
             cols[kv.first.second].push_back(kv.first.first);
         }
-        for (auto &kv : rows) {
-            std::ostringstream e;
-            e << "B" << kv.first << "_" << kv.second[0] << " * y" << p.i2 << "_" << kv.second[0];
-            for (size_t n = 1; n < kv.second.size(); ++n) {
-                std::ostringstream f;
-                f << "FMA(B" << kv.first << "_" << kv.second[n] << ", y" << p.i2 << "_" << kv.second[n] << ", " << e.str()
-                  << ")";
-                e.str(f.str());
+        // f<name>_i = sum_j B_ij <v>_j over the row i (or the column j when by_col)
+        auto contract = [&](const std::map<int, std::vector<int>> &lines, bool by_col, const std::string &v, int blk,
+                            const std::string &name) {
+            for (auto &kv : lines) {
+                auto bij = [&](int m) {
+                    return by_col ? "B" + std::to_string(m) + "_" + std::to_string(kv.first)
+                                  : "B" + std::to_string(kv.first) + "_" + std::to_string(m);
+                };
+                std::ostringstream e;
+                e << bij(kv.second[0]) << " * " << v << blk << "_" << kv.second[0];
+                for (size_t n = 1; n < kv.second.size(); ++n) {
+                    std::ostringstream f;
+                    f << "FMA(" << bij(kv.second[n]) << ", " << v << blk << "_" << kv.second[n] << ", " << e.str() << ")";
+                    e.str(f.str());
+                }
+                o("const T ", name, kv.first, " = ", e.str(), ";");
             }
-            o("const T fx", kv.first, " = ", e.str(), ";");
-        }
-        for (auto &kv : cols) {
-            std::ostringstream e;
-            e << "B" << kv.second[0] << "_" << kv.first << " * x" << p.i1 << "_" << kv.second[0];
-            for (size_t n = 1; n < kv.second.size(); ++n) {
-                std::ostringstream f;
-                f << "FMA(B" << kv.second[n] << "_" << kv.first << ", x" << p.i1 << "_" << kv.second[n] << ", " << e.str()
-                  << ")";
-                e.str(f.str());
-            }
-            o("const T fy", kv.first, " = ", e.str(), ";");
-        }
+        };
+        contract(rows, false, "y", p.i2, "fx");
+        if (dbl) contract(rows, false, "gy", p.i2, "fxg");  // d/dx of the ggy term
+        contract(cols, true, "x", p.i1, "fy");
+        if (dbl) contract(cols, true, "gx", p.i1, "fyg");   // d/dy of the ggx term
         {
-            // dW = sum_i x_i dF/dx_i
+            // dW = sum_i x_i dF/dx_i   (double backward: sum_i ggx_i fx_i + x_i fxg_i)
             std::ostringstream e;
             bool first = true;
-            for (auto &kv : rows) {
+            auto term = [&](const std::string &a, const std::string &b) {
                 if (first) {
-                    e << "x" << p.i1 << "_" << kv.first << " * fx" << kv.first;
+                    e << a << " * " << b;
                     first = false;
                 } else {
                     std::ostringstream f;
-                    f << "FMA(x" << p.i1 << "_" << kv.first << ", fx" << kv.first << ", " << e.str() << ")";
+                    f << "FMA(" << a << ", " << b << ", " << e.str() << ")";
                     e.str(f.str());
+                }
+            };
+            for (auto &kv : rows) {
+                const std::string i = std::to_string(kv.first), b1 = std::to_string(p.i1);
+                if (dbl) {
+                    term("gx" + b1 + "_" + i, "fx" + i);
+                    term("x" + b1 + "_" + i, "fxg" + i);
+                } else {
+                    term("x" + b1 + "_" + i, "fx" + i);
                 }
             }
             std::string guard = needs_mask(p.mul_in, g) ? "(u < " + std::to_string(p.mul_in) + ") && " : "";
             o("if (", guard, "dw) ST_STREAM(", e.str(), ", &dw[(size_t)e * WROW + ", p.w_off, " + u]);");
         }
-        for (auto &kv : rows) o("d", p.i1, "_", kv.first, " = FMA(w", pi, ", fx", kv.first, ", d", p.i1, "_", kv.first, ");");
-        for (auto &kv : cols) o("h", p.i2, "_", kv.first, " = FMA(w", pi, ", fy", kv.first, ", h", p.i2, "_", kv.first, ");");
+        if (dbl) {
+            // d/dx = W fxg + ggw fx ; d/dy = W fyg + ggw fy
+            for (auto &kv : rows)
+                o("d", p.i1, "_", kv.first, " = FMA(w", pi, ", fxg", kv.first, ", FMA(gw", pi, ", fx", kv.first, ", d", p.i1,
+                  "_", kv.first, "));");
+            for (auto &kv : cols)
+                o("h", p.i2, "_", kv.first, " = FMA(w", pi, ", fyg", kv.first, ", FMA(gw", pi, ", fy", kv.first, ", h", p.i2,
+                  "_", kv.first, "));");
+        } else {
+            for (auto &kv : rows)
+                o("d", p.i1, "_", kv.first, " = FMA(w", pi, ", fx", kv.first, ", d", p.i1, "_", kv.first, ");");
+            for (auto &kv : cols)
+                o("h", p.i2, "_", kv.first, " = FMA(w", pi, ", fy", kv.first, ", h", p.i2, "_", kv.first, ");");
+        }
         o.ind--;
         o("}");
     }
@@ -589,6 +728,11 @@ void emit_bwd_group(Out &o, const Plan &P, int gi)
         for (int pi : g.paths) o("w", pi, " = nw", pi, ";");
         for (int q : t.slots)
             for (int k = 0; k < n_of(P.out[q].l); ++k) o("g", q, "_", k, " = ng", q, "_", k, ";");
+        if (dbl) {
+            for (int b : t.i2)
+                for (int j = 0; j < n_of(P.sh[b].l); ++j) o("gy", b, "_", j, " = ngy", b, "_", j, ";");
+            for (int pi : g.paths) o("gw", pi, " = ngw", pi, ";");
+        }
     }
     o("e = en;");
     o("n = nn;");
@@ -654,10 +798,10 @@ void emit_bwd_group(Out &o, const Plan &P, int gi)
     o("");
 }
 
-int bwd_red_size(const Plan &P)
+int bwd_red_size(const std::vector<Group> &groups, const Plan &P)
 {
     int m = 1;
-    for (const Group &g : P.bwd_groups) {
+    for (const Group &g : groups) {
         int nx = 0;
         for (const Irrep &ir : P.ins) nx += n_of(ir.l);  // upper bound over the group's blocks
         m = std::max(m, 3 * nx * g.ct);
@@ -665,26 +809,31 @@ int bwd_red_size(const Plan &P)
     return m;
 }
 
-void emit_bwd_kernel(Out &o, const Plan &P)
+// Sender-pass kernel: the backward (dbl = false) or the double backward's
+// d/dx, d/dy, d/dW (dbl = true); slot_sum comes from the preamble.
+void emit_bwd_kernel(Out &o, const Plan &P, bool dbl = false)
 {
-    emit_slot_sum(o, P);
-    for (int gi = 0; gi < (int)P.bwd_groups.size(); ++gi) emit_bwd_group(o, P, gi);
+    const std::vector<Group> &groups = dbl ? P.dbl_groups : P.bwd_groups;
+    for (int gi = 0; gi < (int)groups.size(); ++gi) emit_bwd_group(o, P, gi, dbl);
     o("// one workgroup of 64*wpr threads per sender; `group` selects the path group (launched in order)");
-    o("extern \"C\" __global__ void __launch_bounds__(256, ", P.bwd_waves_per_eu,
-      ") cgtp_conv_bwd(const int* __restrict__ t_row_ptr, "
+    o("extern \"C\" __global__ void __launch_bounds__(256, ", dbl ? P.dbl_bwd_waves_per_eu : P.bwd_waves_per_eu, ") ",
+      dbl ? "cgtp_conv_dbwd_send" : "cgtp_conv_bwd",
+      "(const int* __restrict__ t_row_ptr, "
       "const int* __restrict__ t_edge, const int* __restrict__ t_dst, const T* __restrict__ x, "
-      "const T* __restrict__ y, const T* __restrict__ w, const T* __restrict__ g, T* __restrict__ dx, "
-      "T* __restrict__ dy, T* __restrict__ dw, long nnodes, int wpr, int group)");
+      "const T* __restrict__ y, const T* __restrict__ w, const T* __restrict__ g, ",
+      dbl ? "const T* __restrict__ ggx, const T* __restrict__ ggy, const T* __restrict__ ggw, " : "",
+      "T* __restrict__ dx, T* __restrict__ dy, T* __restrict__ dw, long nnodes, int wpr, int group)");
     o("{");
     o.ind++;
-    o("__shared__ T red[", bwd_red_size(P), "];  // partial dx of waves 1..3");
+    o("__shared__ T red[", bwd_red_size(groups, P), "];  // partial dx of waves 1..3");
     o("const long s = blockIdx.x;");
     o("const int wv = threadIdx.x >> 6;");
     o("const int lane = threadIdx.x & 63;");
     o("if (s >= nnodes) return;");
     o("switch (group) {");
-    for (int gi = 0; gi < (int)P.bwd_groups.size(); ++gi)
-        o("case ", gi, ": bwd_g", gi, "(s, wv, lane, wpr, red, t_row_ptr, t_edge, t_dst, x, y, w, g, dx, dy, dw); break;");
+    for (int gi = 0; gi < (int)groups.size(); ++gi)
+        o("case ", gi, ": ", dbl ? "dbs" : "bwd", "_g", gi, "(s, wv, lane, wpr, red, t_row_ptr, t_edge, t_dst, x, y, w, g, ",
+          dbl ? "ggx, ggy, ggw, " : "", "dx, dy, dw); break;");
     o("default: break;");
     o("}");
     o.ind--;
@@ -873,15 +1022,29 @@ void emit_uvw_kernel(Out &o, const Plan &P)
 
 std::string generate_source(const Plan &P)
 {
+    // "// @@section NAME" lines split the module into the shared preamble and one part per
+    // kernel (with its helpers), so a measurement taken on one kernel can be matched to the
+    // exact code it ran even after other kernels of the module change.
     Out o;
+    o("// @@section common");
     emit_preamble(o, P);
     if (P.mode == CGTP_UVU) {
+        emit_slot_sum(o, P);
+        o("// @@section cgtp_conv_fwd");
         for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi) emit_fwd_group(o, P, gi, false);
         emit_fwd_kernel(o, P, false);
+        o("// @@section cgtp_tp_fwd");
         for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi) emit_fwd_group(o, P, gi, true);
         emit_fwd_kernel(o, P, true);
+        o("// @@section cgtp_conv_bwd");
         emit_bwd_kernel(o, P);
+        o("// @@section cgtp_conv_dbwd_recv");
+        for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi) emit_fwd_group(o, P, gi, false, true);
+        emit_fwd_kernel(o, P, false, true);
+        o("// @@section cgtp_conv_dbwd_send");
+        emit_bwd_kernel(o, P, true);
     } else {
+        o("// @@section cgtp_tp_uvw");
         emit_uvw_kernel(o, P);
     }
     return o.s.str();

@@ -120,6 +120,8 @@ const Plan::Loaded &module_for_current_device(Plan &P)
         check(hipModuleGetFunction(&L.conv_fwd, L.module, "cgtp_conv_fwd"), "hipModuleGetFunction(conv_fwd)");
         check(hipModuleGetFunction(&L.conv_bwd, L.module, "cgtp_conv_bwd"), "hipModuleGetFunction(conv_bwd)");
         check(hipModuleGetFunction(&L.tp_fwd, L.module, "cgtp_tp_fwd"), "hipModuleGetFunction(tp_fwd)");
+        check(hipModuleGetFunction(&L.dbwd_recv, L.module, "cgtp_conv_dbwd_recv"), "hipModuleGetFunction(dbwd_recv)");
+        check(hipModuleGetFunction(&L.dbwd_send, L.module, "cgtp_conv_dbwd_send"), "hipModuleGetFunction(dbwd_send)");
     } else {
         check(hipModuleGetFunction(&L.tp_uvw, L.module, "cgtp_tp_uvw"), "hipModuleGetFunction(tp_uvw)");
     }

@@ -332,68 +332,77 @@ void schedule(Plan &P)
         }
     }
 
-    // Backward groups: paths sharing an SH block (so that block's dY is complete
-    // in one group), split when the register estimate exceeds the budget.
-    P.bwd_groups.clear();
+    // Sender-pass groups (backward, and the double backward's d/dx, d/dy, d/dW):
+    // paths sharing an SH block (so that block's dY is complete in one group),
+    // split when the register estimate exceeds the budget.
     {
         auto nnz_b = [&](int pi) {
             std::set<std::pair<int, int>> ij;
             for (const Nonzero &z : P.paths[pi].nz) ij.insert({z.i, z.j});
             return (int)ij.size();
         };
-        auto estimate = [&](const std::vector<int> &ps, bool prefetch) {
+        // 32-bit registers per lane: dx accumulators and x per sender, the edge
+        // operands (y, W, g), dY partials, the B block and its contractions; the
+        // double backward adds ggx, ggy, ggw and a second contraction per line.
+        auto estimate = [&](const std::vector<int> &ps, bool prefetch, bool dbl) {
             std::set<int> i1s, i2s, slots;
             int maxb = 0;
             for (int pi : ps) {
                 i1s.insert(P.paths[pi].i1);
                 i2s.insert(P.paths[pi].i2);
                 slots.insert(P.paths[pi].slot);
-                maxb = std::max(maxb, nnz_b(pi) + 2 * P.paths[pi].l1 + 2 * P.paths[pi].l2 + 2);
+                maxb = std::max(maxb, nnz_b(pi) + (dbl ? 2 : 1) * (2 * P.paths[pi].l1 + 2 * P.paths[pi].l2 + 2));
             }
             int xs = 0, ys = 0, gs = 0;
             for (int b : i1s) xs += 2 * P.ins[b].l + 1;
             for (int b : i2s) ys += 2 * P.sh[b].l + 1;
             for (int q : slots) gs += 2 * P.out[q].l + 1;
-            int edge = ys + (int)ps.size() + gs;
-            return word * (2 * xs + edge + ys + maxb + (prefetch ? edge : 0)) + 24;
+            int edge = ys + (int)ps.size() + gs + (dbl ? ys + (int)ps.size() : 0);
+            return word * ((dbl ? 3 : 2) * xs + edge + ys + maxb + (prefetch ? edge : 0)) + 24;
         };
         // One group with every path is fastest when it fits (measured on the
         // NequIP-like graph: fewer launches and index loads, the g row read in
         // one pass); larger problems are split so that no group spills.
-        const int split_budget = 168;
-        std::vector<int> all_paths;
-        for (int i = 0; i < (int)P.paths.size(); ++i) all_paths.push_back(i);
-        bool split = estimate(all_paths, false) > 200;
-        if (const char *e = std::getenv("CGTP_BWD_SPLIT")) split = std::atoi(e) != 0;
-        if (!split) {
-            Group all;
-            for (int i = 0; i < (int)P.paths.size(); ++i) all.paths.push_back(i);
-            P.bwd_groups.push_back(all);
-        }
-        for (int b = 0; split && b < (int)P.sh.size(); ++b) {
-            Group cur;
-            for (int i = 0; i < (int)P.paths.size(); ++i) {
-                if (P.paths[i].i2 != b) continue;
-                std::vector<int> trial = cur.paths;
-                trial.push_back(i);
-                if (!cur.paths.empty() && estimate(trial, false) > split_budget) {
-                    P.bwd_groups.push_back(cur);
-                    cur = Group();
-                }
-                cur.paths.push_back(i);
+        auto make_groups = [&](bool dbl, std::vector<Group> &groups, int &waves) {
+            const int split_budget = 168, one_group_limit = 200;
+            groups.clear();
+            std::vector<int> all_paths;
+            for (int i = 0; i < (int)P.paths.size(); ++i) all_paths.push_back(i);
+            bool split = estimate(all_paths, false, dbl) > one_group_limit;
+            if (const char *e = std::getenv(dbl ? "CGTP_DBL_SPLIT" : "CGTP_BWD_SPLIT")) split = std::atoi(e) != 0;
+            if (!split) {
+                Group all;
+                all.paths = all_paths;
+                groups.push_back(all);
             }
-            if (!cur.paths.empty()) P.bwd_groups.push_back(cur);
-        }
-        int est_max = 0;
-        for (Group &g : P.bwd_groups) {
-            for (int pi : g.paths) g.mul = std::max(g.mul, P.paths[pi].mul_in);
-            finish_group(g);
-            // register double-buffering measured slower (it lowers occupancy and the
-            // backward is bound by outstanding L1 misses, not by issue latency)
-            g.prefetch = P.bwd_prefetch > 0;
-            est_max = std::max(est_max, estimate(g.paths, g.prefetch));
-        }
-        P.bwd_waves_per_eu = std::max(1, std::min(4, 512 * 4 / (5 * std::max(est_max, 1))));
+            for (int b = 0; split && b < (int)P.sh.size(); ++b) {
+                Group cur;
+                for (int i = 0; i < (int)P.paths.size(); ++i) {
+                    if (P.paths[i].i2 != b) continue;
+                    std::vector<int> trial = cur.paths;
+                    trial.push_back(i);
+                    if (!cur.paths.empty() && estimate(trial, false, dbl) > split_budget) {
+                        groups.push_back(cur);
+                        cur = Group();
+                    }
+                    cur.paths.push_back(i);
+                }
+                if (!cur.paths.empty()) groups.push_back(cur);
+            }
+            int est_max = 0;
+            for (Group &g : groups) {
+                for (int pi : g.paths) g.mul = std::max(g.mul, P.paths[pi].mul_in);
+                finish_group(g);
+                // register double-buffering measured slower (it lowers occupancy and the
+                // backward is bound by outstanding L1 misses, not by issue latency)
+                g.prefetch = !dbl && P.bwd_prefetch > 0;
+                est_max = std::max(est_max, estimate(g.paths, g.prefetch, dbl));
+            }
+            waves = std::max(1, std::min(4, 512 * 4 / (5 * std::max(est_max, 1))));
+        };
+        make_groups(false, P.bwd_groups, P.bwd_waves_per_eu);
+        make_groups(P.mode == CGTP_UVU, P.dbl_groups, P.dbl_bwd_waves_per_eu);
+        if (P.mode != CGTP_UVU) P.dbl_groups.clear();
     }
 
     // Occupancy targets: 4 waves per SIMD (<= 128 VGPRs) keeps enough loads in
@@ -402,6 +411,10 @@ void schedule(Plan &P)
     // CGTP_FWD_WAVES / CGTP_BWD_WAVES override (tuning).
     P.fwd_waves_per_eu = P.dtype == CGTP_F64 ? 2 : 4;
     if (const char *e = std::getenv("CGTP_FWD_WAVES")) P.fwd_waves_per_eu = std::max(1, std::atoi(e));
+    // the double backward's receiver pass holds twice the forward's operands
+    P.dbl_fwd_waves_per_eu = std::max(1, P.fwd_waves_per_eu / 2);
+    if (const char *e = std::getenv("CGTP_DBL_FWD_WAVES")) P.dbl_fwd_waves_per_eu = std::max(1, std::atoi(e));
+    if (const char *e = std::getenv("CGTP_DBL_BWD_WAVES")) P.dbl_bwd_waves_per_eu = std::max(1, std::atoi(e));
     if (const char *e = std::getenv("CGTP_BWD_WAVES")) P.bwd_waves_per_eu = std::max(1, std::atoi(e));
     P.uvw_waves_per_eu = P.dtype == CGTP_F64 ? 1 : 2;
     if (const char *e = std::getenv("CGTP_UVW_WAVES")) P.uvw_waves_per_eu = std::max(1, std::atoi(e));

@@ -9,9 +9,11 @@ Recipe (the pages name no dataset; these stand in for the molecular graphs
 NequIP/MACE run on, sciencestack.ai page Figures 4-5, and for the
 edge-scaling regimes of the Sobek page):
 
-* seeds: ``np.random.SeedSequence(seed)`` spawns five children in the order
-  graph, x, vec, w, sample; each drives its own PCG64 ``default_rng``.  Draws
-  are float64 and cast to the run's dtype afterwards.
+* seeds: ``np.random.SeedSequence(seed)`` spawns six children in the order
+  graph, x, vec, w, sample, upstream; each drives its own PCG64
+  ``default_rng`` (``upstream`` spawns three more, for the double backward's
+  upstream gradients of dx, dY and dW, all ~ N(0, 1)).  Draws are float64 and
+  cast to the run's dtype afterwards.
 * uniform graph: E receivers drawn uniformly from [0, N) (so the in-degree is
   Binomial(E, 1/N) ~ Poisson(E/N) with an exact total), E senders drawn
   uniformly with replacement (self-loops and duplicates allowed), a stable
@@ -33,12 +35,19 @@ from typing import Optional
 import numpy as np
 
 HOST_LIMIT = 400_000_000
-STREAMS = ("graph", "x", "vec", "w", "sample")
+STREAMS = ("graph", "x", "vec", "w", "sample", "upstream")
 
 
 def streams(seed: int = 0):
     children = np.random.SeedSequence(seed).spawn(len(STREAMS))
     return {name: child for name, child in zip(STREAMS, children)}
+
+
+def upstream_streams(seed: int = 0):
+    """Three independent children (for the upstream gradients of dx, dY and dW in the
+    double backward); adding them left the first five streams unchanged."""
+    gx, gy, gw = streams(seed)["upstream"].spawn(3)
+    return {"gg_x": gx, "gg_y": gy, "gg_w": gw}
 
 
 def rng(child: np.random.SeedSequence) -> np.random.Generator:

@@ -186,6 +186,37 @@ cgtp_status cgtp_conv_backward(const cgtp_plan *plan, int64_t N, int64_t E, cons
                                void *stream);
 
 /*
+ * Fused convolution double backward: the higher partial derivatives used for
+ * interatomic forces (sciencestack.ai page, Abstract; OpenEquivariance
+ * discussion: a convolution double backward with four results; Sobek page,
+ * Abstract: the same operator through double backward; LunaTP page,
+ * Abstract: higher-order derivatives).  With (dx, dy, dW) the results of
+ * cgtp_conv_backward for (x, y, w, grad_out) and upstream gradients gg_x
+ * [N][d_x], gg_y [E][d_sh], gg_w [E][weight_numel] for them, the scalar
+ *   L2 = <gg_x, dx> + <gg_y, dy> + <gg_w, dW>
+ * is differentiated:
+ *   grad_grad_out [N][d_out] = conv(gg_x, y, w) + conv(x, gg_y, w) + conv(x, y, gg_w)
+ *   grad_x [N][d_x]          = sum over e = (s -> n): sum_p sum_{jk} C g[n,u,k] (W gg_y_j + gg_w y_j)
+ *   grad_y [E][d_sh]         = sum_p sum_u sum_{ik} C g[n,u,k] (W gg_x[s,u,i] + gg_w x[s,u,i])
+ *   grad_w [E][weight_numel] = sum_{ijk} C g[n,u,k] (gg_x[s,u,i] y_j + x[s,u,i] gg_y_j)
+ * (conv(.) is cgtp_conv_forward; sums per path p and channel u as in
+ * cgtp_conv_backward.)  grad_grad_out comes from one receiver-ordered pass
+ * (schedule `order` as in cgtp_conv_forward_ordered, NULL = natural); the
+ * other three from one sender-ordered pass over the transpose.  Any output may
+ * be NULL to skip it (a pass with no requested output is not launched);
+ * outputs are overwritten, each row has one owner, no atomics, bitwise
+ * deterministic.  Every input named in a requested pass must be non-NULL
+ * (pass zeros for an absent upstream gradient); x and gg_x always.  uvu plans
+ * only.
+ */
+cgtp_status cgtp_conv_double_backward(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
+                                      const int32_t *col, const int32_t *order, const int32_t *t_row_ptr,
+                                      const int32_t *t_edge, const int32_t *t_dst, const void *x, const void *y,
+                                      const void *w, const void *grad_out, const void *gg_x, const void *gg_y,
+                                      const void *gg_w, void *grad_x, void *grad_y, void *grad_w,
+                                      void *grad_grad_out, void *stream);
+
+/*
  * Real spherical harmonics of the edge vectors, component normalisation
  * (sum_m Y_lm^2 = 2l+1, Y_1 = sqrt3 (y, z, x)/|r|), degrees 0..lmax (<= 7):
  * vec [E][3] (any nonzero length), y [E][(lmax+1)^2] overwritten.  These
