@@ -1,6 +1,7 @@
 """Benchmark of the fused CGTP convolution on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c5] [--no-cpu]
+                    [--double-backward]
 
 One step = one pass of the hot path over the synthetic graph: the fused
 convolution forward (cgtp_conv_forward_ordered, heavy-first receiver schedule)
@@ -38,6 +39,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--natural-order", action="store_true",
                     help="start receivers in node order instead of the heavy-first schedule")
+    ap.add_argument("--double-backward", action="store_true",
+                    help="time the convolution double backward (both passes) instead of forward + backward")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -62,6 +65,126 @@ def algorithmic_bytes(plan, N, E, es):
            + es * (N * plan.d_x + E * plan.d_sh + E * plan.weight_numel + N * plan.d_out)
            + es * (N * plan.d_x + E * plan.d_sh + E * plan.weight_numel))
     return fwd, bwd
+
+
+def algorithmic_bytes_dbl(plan, N, E, es):
+    """Compulsory bytes of the two double-backward passes: inputs read once, outputs written once.
+    Receiver pass: row_ptr, col, x, gg_x, y, gg_y, w, gg_w -> grad_grad_out.  Sender pass:
+    t_row_ptr, t_edge, t_dst, x, gg_x, y, gg_y, w, gg_w, grad_out -> grad_x, grad_y, grad_w."""
+    ops = 2 * N * plan.d_x + 2 * E * plan.d_sh + 2 * E * plan.weight_numel
+    recv = (N + 1) * 4 + E * 4 + es * (ops + N * plan.d_out)
+    send = (N + 1) * 4 + 2 * E * 4 + es * (ops + N * plan.d_out) + es * (N * plan.d_x + E * plan.d_sh
+                                                                         + E * plan.weight_numel)
+    return recv, send
+
+
+def cpu_baseline_dbl(spec, seed, host_graph, max_seconds=30.0):
+    """The oracle's double backward (explicit fp64 loops, OpenMP) on the sub-graph of a contiguous
+    receiver slice holding ~5% of the edges, random values (timing only): all four results of the
+    sub-graph, i.e. the same per-edge work as the full operation.  Rate = sub-graph edges per second."""
+    from oracle import irreps as oirreps
+    from oracle import loops
+    row_ptr, col = (np.asarray(a, dtype=np.int64) for a in host_graph)
+    N, E = len(row_ptr) - 1, len(col)
+    out_ir = oirreps.per_path_out_irreps(spec.in_irreps, spec.lmax_sh, spec.lmax_out)
+    prob = oirreps.build_problem(spec.in_irreps, oirreps.sh_irreps(spec.lmax_sh), out_ir, "uvu")
+    tab = loops.Tables(prob)
+    threads = loops.default_threads()
+    rng = np.random.default_rng(seed + 98)
+    target = max(2_000, E // 20)
+    start = int(rng.integers(0, max(1, N // 2)))
+    stop = min(max(int(np.searchsorted(row_ptr, row_ptr[start] + target)), start + 1), N)
+    e0, e1 = int(row_ptr[start]), int(row_ptr[stop])
+    n_e = e1 - e0
+    sub_ptr = row_ptr[start:stop + 1] - e0
+    uniq, inv = np.unique(col[e0:e1], return_inverse=True)
+    x, ggx = rng.standard_normal((2, len(uniq), prob.d_in))
+    y, ggy = rng.standard_normal((2, n_e, prob.d_sh))
+    w, ggw = rng.standard_normal((2, n_e, prob.weight_numel))
+    g = rng.standard_normal((stop - start, prob.d_out))
+    rows, senders = np.arange(stop - start), np.arange(len(uniq))
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        loops.conv_double_backward_rows(tab, sub_ptr, inv, x, y, w, g, ggx, ggy, ggw, rows, senders, threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or el >= max_seconds:
+            break
+    return {"value": n_e * reps / el, "unit": "edges/s", "cores": threads, "kind": "oracle",
+            "sample": f"receivers [{start},{stop}) = {n_e} of {E} edges and their {len(uniq)} senders: all four "
+                      f"double-backward results of that sub-graph; fp64 explicit loops, mean of {reps} rep(s)"}
+
+
+def bench_double_backward(a, spec, plan, d, host_graph, device):
+    import torch
+    from clebsch_gordan_tensor_cgtp_amd import binding as cg
+    from clebsch_gordan_tensor_cgtp_amd import synth
+    N, E = d["row_ptr"].shape[0] - 1, d["col"].shape[0]
+    es = 4 if a.dtype == "f32" else 8
+    npdt = np.float32 if a.dtype == "f32" else np.float64
+    up = synth.upstream_streams(a.seed)
+
+    def dev(t):
+        return torch.from_numpy(np.ascontiguousarray(t)).to(device) if isinstance(t, np.ndarray) else t
+
+    gg = [dev(synth.normal(up["gg_x"], (N, plan.d_x), dtype=npdt, device=device)),
+          dev(synth.normal(up["gg_y"], (E, plan.d_sh), dtype=npdt, device=device)),
+          dev(synth.normal(up["gg_w"], (E, plan.weight_numel), dtype=npdt, device=device))]
+    y = cg.spherical_harmonics(spec.lmax_sh, d["vec"])
+    tr = cg.graph_transpose(d["row_ptr"], d["col"])
+    order = cg.graph_order(d["row_ptr"]) if not a.natural_order else None
+    outs = (torch.empty_like(d["x"]), torch.empty_like(y), torch.empty_like(d["w"]),
+            torch.empty((N, plan.d_out), dtype=plan.torch_dtype, device=device))
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        cg.conv_double_backward(plan, d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"], *gg, order=order,
+                                outs=outs, need=(False, False, False, True))
+        if ev is not None:
+            ev[1].record()
+        cg.conv_double_backward(plan, d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"], *gg, order=order,
+                                outs=outs, need=(True, True, True, False))
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    t0 = time.perf_counter()
+    for k in range(a.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    recv_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    send_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_per_step = wall * 1e3 / a.steps
+    recv_b, send_b = algorithmic_bytes_dbl(plan, N, E, es)
+    dom = ("cgtp_conv_dbwd_send", send_ms, send_b) if send_ms >= recv_ms else ("cgtp_conv_dbwd_recv", recv_ms, recv_b)
+    oth = ("cgtp_conv_dbwd_recv", recv_ms, recv_b) if dom[0] == "cgtp_conv_dbwd_send" else \
+        ("cgtp_conv_dbwd_send", send_ms, send_b)
+    achieved = dom[2] / (dom[1] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC, "value": E / (ms_per_step * 1e-3), "unit": "edges/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": a.dtype, "data": "synthetic",
+        "config": {"workload": spec.name, "N": N, "E": E, "in_irreps": spec.in_irreps, "sh_lmax": spec.lmax_sh,
+                   "paths": plan.num_paths, "d_out": plan.d_out,
+                   "step": "conv_double_backward (grad_x, grad_y, grad_w, grad_grad_out)",
+                   "receiver_schedule": "natural" if a.natural_order else "heavy-first",
+                   "recv_ms": recv_ms, "send_ms": send_ms},
+        "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(plan, spec, a.dtype, dom[0]),
+                     "algorithmic_bytes_per_launch": dom[2], "avg_launch_ms": dom[1],
+                     "other": {"kernel": oth[0], "achieved": oth[2] / (oth[1] * 1e-3) / 1e9}},
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_dbl(spec, a.seed, host_graph)
+    print(json.dumps(line), flush=True)
 
 
 def kernel_digest(source, kernel):
@@ -249,6 +372,8 @@ def main():
     if not hasattr(spec, "n_edges"):
         return bench_tp(a, spec, device)
     plan, d, host_graph = make_inputs(spec, a.dtype, a.seed, device)
+    if a.double_backward:
+        return bench_double_backward(a, spec, plan, d, host_graph, device)
     N, E = d["row_ptr"].shape[0] - 1, d["col"].shape[0]
     es = 4 if a.dtype == "f32" else 8
     y = cg.spherical_harmonics(spec.lmax_sh, d["vec"])

@@ -144,3 +144,96 @@ def test_full_stream_powerlaw_sampled(device):
     check_sampled(case, 256, 256)
     del case
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------------------ double backward
+
+class DoubleBackwardCase(DeviceCase):
+    """Full-size inputs plus the upstream gradients gg_x, gg_y, gg_w (seeded, drawn like x, y, w)."""
+
+    def __init__(self, spec, dtype, device, seed=0):
+        super().__init__(spec, dtype, device, seed)
+        npdt = np.float32 if dtype == "f32" else np.float64
+        up = synth.upstream_streams(seed)
+        import torch
+
+        def dev(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device) if isinstance(a, np.ndarray) else a
+
+        self.gg = [dev(synth.normal(up["gg_x"], (self.N, self.plan.d_x), dtype=npdt, device=device)),
+                   dev(synth.normal(up["gg_y"], (self.E, self.plan.d_sh), dtype=npdt, device=device)),
+                   dev(synth.normal(up["gg_w"], (self.E, self.plan.weight_numel), dtype=npdt, device=device))]
+
+    def run_dbl(self):
+        import torch
+        d = self.d
+        y = cg.spherical_harmonics(self.spec.lmax_sh, d["vec"])
+        tr = cg.graph_transpose(d["row_ptr"], d["col"])
+        order = cg.graph_order(d["row_ptr"])
+        res = cg.conv_double_backward(self.plan, d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"], *self.gg,
+                                      order=order)
+        torch.cuda.synchronize()
+        return res
+
+    def oracle_on(self, rp, col_local, senders_global, edges, recv_global, rows, senders):
+        """The oracle on a sub-graph: rp/col_local index local senders, whose global ids are
+        senders_global; edges are global edge ids in sub-CSR order, recv_global the receivers."""
+        f64 = lambda a: np.asarray(a, np.float64)
+        x = f64(self.rows(self.d["x"], senders_global))
+        ggx = f64(self.rows(self.gg[0], senders_global))
+        y = self.y_of(edges)
+        ggy = f64(self.rows(self.gg[1], edges))
+        w = f64(self.rows(self.d["w"], edges))
+        ggw = f64(self.rows(self.gg[2], edges))
+        g = f64(self.rows(self.d["g"], recv_global))
+        return loops.conv_double_backward_rows(self.tab, rp, col_local, x, y, w, g, ggx, ggy, ggw, rows, senders)
+
+    def oracle_receivers_dbl(self, recv):
+        rp = self.row_ptr.astype(np.int64)
+        deg = rp[recv + 1] - rp[recv]
+        sub_ptr = np.concatenate([[0], np.cumsum(deg)])
+        edges = np.concatenate([np.arange(rp[r], rp[r + 1]) for r in recv])
+        uniq, inv = np.unique(self.col[edges], return_inverse=True)
+        _, _, dy, dw, dg = self.oracle_on(sub_ptr, inv, uniq, edges, recv, np.arange(len(recv)), np.zeros(0, np.int64))
+        return edges, dy, dw, dg
+
+    def oracle_senders_dbl(self, send):
+        col = self.col.astype(np.int64)
+        edges = np.nonzero(np.isin(col, send))[0]              # ascending edge id = receiver order
+        dst = np.searchsorted(self.row_ptr.astype(np.int64), edges, side="right") - 1
+        runiq, rinv = np.unique(dst, return_inverse=True)
+        sub_ptr = np.concatenate([[0], np.cumsum(np.bincount(rinv, minlength=len(runiq)))])
+        s_local = np.searchsorted(send, col[edges])
+        _, dx, _, _, _ = self.oracle_on(sub_ptr, s_local, send, edges, runiq, np.zeros(0, np.int64),
+                                        np.arange(len(send)))
+        return dx
+
+
+def test_full_nequip_double_backward_all_rows(device):
+    case = DoubleBackwardCase(synth.CONV_NEQUIP, "f32", device)
+    gx, gy, gw, gg = case.run_dbl()
+    allr = np.arange(case.N)
+    edges, dy, dw, dg = case.oracle_receivers_dbl(allr)
+    assert np.array_equal(edges, np.arange(case.E))
+    assert rel_l2(gg.cpu().numpy(), dg) <= TOL["f32"]
+    assert rel_l2(gy.cpu().numpy(), dy) <= TOL["f32"]
+    assert rel_l2(gw.cpu().numpy(), dw) <= TOL["f32"]
+    assert rel_l2(gx.cpu().numpy(), case.oracle_senders_dbl(allr)) <= TOL["f32"]
+
+
+def test_full_mace_double_backward_sampled(device):
+    import torch
+    case = DoubleBackwardCase(synth.CONV_MACE, "f32", device)
+    gx, gy, gw, gg = case.run_dbl()
+    rng = np.random.default_rng(31)
+    deg = np.diff(case.row_ptr)
+    outdeg = np.bincount(case.col, minlength=case.N)
+    recv = np.unique(np.concatenate([rng.choice(case.N, 96, replace=False), [int(np.argmax(deg))]]))
+    send = np.unique(np.concatenate([rng.choice(case.N, 64, replace=False), [int(np.argmax(outdeg))]]))
+    edges, dy, dw, dg = case.oracle_receivers_dbl(recv)
+    assert rel_l2(case.rows(gg, recv), dg) <= TOL["f32"]
+    assert rel_l2(case.rows(gy, edges), dy) <= TOL["f32"]
+    assert rel_l2(case.rows(gw, edges), dw) <= TOL["f32"]
+    assert rel_l2(case.rows(gx, send), case.oracle_senders_dbl(send)) <= TOL["f32"]
+    del case, gx, gy, gw, gg
+    torch.cuda.empty_cache()
