@@ -218,3 +218,20 @@ def conv_double_backward_rows(tab: Tables, row_ptr, col, x, y, w, g, ggx, ggy, g
     dx = (conv_backward_x_rows(tab, row_ptr, col, ggy, w, g, senders, n_threads)
           + conv_backward_x_rows(tab, row_ptr, col, y, ggw, g, senders, n_threads))
     return eidx, dx, dy_a + dy_c, dw_a + dw_b, dg
+
+
+def conv_forward_uvw_rows(tab: Tables, row_ptr, col, x, y, w, rows, n_threads=None) -> np.ndarray:
+    """uvw convolution output of the receivers ``rows``: the explicit uvw loops on every edge
+    of those receivers (x gathered by sender), summed per receiver in CSR edge order."""
+    row_ptr = np.asarray(row_ptr, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    deg = row_ptr[rows + 1] - row_ptr[rows]
+    eidx = np.concatenate([np.arange(row_ptr[r], row_ptr[r + 1]) for r in rows]) if len(rows) else \
+        np.zeros(0, np.int64)
+    out = np.zeros((len(rows), tab.prob.d_out))
+    if len(eidx) == 0:
+        return out
+    msg = uvw_forward(tab, np.asarray(x)[np.asarray(col)[eidx]], np.asarray(y)[eidx], w, n_threads)
+    seg = np.repeat(np.arange(len(rows)), deg)
+    np.add.at(out, seg, msg)
+    return out

@@ -84,13 +84,17 @@ def receivers_of(row_ptr: np.ndarray) -> np.ndarray:
 
 
 def conv_forward(prob: Problem, row_ptr, col, x, y, w):
-    """Fused convolution, use case B: out[n] = sum over edges e of n of TP(x[col[e]], y[e], W[e])."""
+    """Fused convolution, use case B: out[n] = sum over edges e of n of TP(x[col[e]], y[e], W_e).
+
+    uvu: W_e = W[e] (per-edge weights).  uvw: W_e = W, the shared [P][mul_in][mul_out] block for
+    every edge (the fully connected multiplicity mixing of the Sobek page, Abstract, inside the
+    convolution)."""
     x = np.asarray(x, np.float64)
     y = np.asarray(y, np.float64)
     w = np.asarray(w, np.float64)
     col = np.asarray(col, np.int64)
     n_nodes = len(row_ptr) - 1
-    msg = edge_messages(prob, x[col], y, w)
+    msg = edge_messages(prob, x[col], y, w) if prob.mode == "uvu" else tp_forward(prob, x[col], y, w)
     out = np.zeros((n_nodes, prob.d_out))
     np.add.at(out, receivers_of(row_ptr), msg)
     return out

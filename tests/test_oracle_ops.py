@@ -365,3 +365,85 @@ def test_cpu_loops_double_backward_match_numpy(in_f32):
     assert np.allclose(dy, want[1][eidx], atol=1e-12)
     assert np.allclose(dw, want[2][eidx], atol=1e-12)
     assert np.allclose(dx, want[0][senders], atol=1e-12)
+
+
+
+# ------------------------------------------------------------------------------ uvw convolution
+
+def _uvw_conv_problem():
+    return irreps.build_problem("3x0e+2x1o+2x2e", irreps.sh_irreps(2), "2x0e+3x1o+2x2e+1x1e+2x2o", "uvw")
+
+
+def test_uvw_conv_brute_force_and_identity_graph():
+    prob = _uvw_conv_problem()
+    rng = np.random.default_rng(16)
+    row_ptr, col = small_graph(rng, 7, 31)
+    x = rng.standard_normal((7, prob.d_in))
+    y = rng.standard_normal((31, prob.d_sh))
+    w = rng.standard_normal(prob.weight_numel)
+    t = dense_tensor(prob)
+    msg = np.einsum("abvo,ea,eb,v->eo", t, x[col], y, w)
+    want = np.zeros((7, prob.d_out))
+    np.add.at(want, ref.receivers_of(row_ptr), msg)
+    assert np.allclose(ref.conv_forward(prob, row_ptr, col, x, y, w), want, atol=1e-12)
+    ident = np.arange(32)
+    assert np.allclose(ref.conv_forward(prob, ident, np.arange(31), x[col], y, w),
+                       ref.tp_forward(prob, x[col], y, w), atol=1e-13)
+
+
+def test_uvw_conv_is_mixing_of_unit_weight_uvu_messages():
+    """Linearity: the uvw convolution equals W applied to the per-path sums of unit-weight messages."""
+    prob = _uvw_conv_problem()
+    rng = np.random.default_rng(17)
+    row_ptr, col = small_graph(rng, 6, 25)
+    x = rng.standard_normal((6, prob.d_in))
+    y = rng.standard_normal((25, prob.d_sh))
+    w = rng.standard_normal(prob.weight_numel)
+    got = ref.conv_forward(prob, row_ptr, col, x, y, w)
+    dst = ref.receivers_of(row_ptr)
+    oa, ob, oo = irreps.offsets(prob.ins), irreps.offsets(prob.sh), irreps.offsets(prob.out)
+    want = np.zeros_like(got)
+    for p in prob.paths:
+        c = real_cg_block(p.l1, p.l2, p.l3)
+        mi, mo = prob.ins[p.i1].mul, prob.out[p.slot].mul
+        n1, n2, n3 = c.shape
+        xb = x[col][:, oa[p.i1]:oa[p.i1] + mi * n1].reshape(-1, mi, n1)
+        yb = y[:, ob[p.i2]:ob[p.i2] + n2]
+        t = np.zeros((6, mi, n3))
+        np.add.at(t, dst, np.einsum("ijk,eui,ej->euk", c, xb, yb))
+        wp = w[p.w_off:p.w_off + mi * mo].reshape(mi, mo)
+        want[:, oo[p.slot]:oo[p.slot] + mo * n3] += np.einsum("nuk,uv->nvk", t, wp).reshape(6, -1)
+    assert np.allclose(got, want, atol=1e-12)
+
+
+@pytest.mark.parametrize("improper", [False, True])
+def test_uvw_conv_equivariance(improper):
+    prob = irreps.build_problem("2x0e+2x1o+2x2e+1x3o", irreps.sh_irreps(3), "3x0e+2x1o+2x2e+1x3o+2x1e+1x2o", "uvw")
+    rng = np.random.default_rng(18)
+    row_ptr, col = small_graph(rng, 6, 20)
+    x = rng.standard_normal((6, prob.d_in))
+    vec = rng.standard_normal((20, 3))
+    w = rng.standard_normal(prob.weight_numel)
+    rot = wigner.random_rotation(rng)
+    lin = -rot if improper else rot
+    d_in = wigner.irreps_d(prob.ins, rot, improper)
+    d_out = wigner.irreps_d(prob.out, rot, improper)
+    out = ref.conv_forward(prob, row_ptr, col, x, osh.real_sh_all(3, vec), w)
+    out_rot = ref.conv_forward(prob, row_ptr, col, x @ d_in.T, osh.real_sh_all(3, vec @ lin.T), w)
+    assert np.allclose(out_rot, out @ d_out.T, atol=1e-10)
+
+
+@pytest.mark.parametrize("in_f32", [False, True])
+def test_cpu_loops_uvw_conv_match_numpy(in_f32):
+    prob = _uvw_conv_problem()
+    rng = np.random.default_rng(19)
+    row_ptr, col = small_graph(rng, 9, 44)
+    x = rng.standard_normal((9, prob.d_in))
+    y = rng.standard_normal((44, prob.d_sh))
+    w = rng.standard_normal(prob.weight_numel)
+    if in_f32:
+        x, y, w = (a.astype(np.float32) for a in (x, y, w))
+    want = ref.conv_forward(prob, row_ptr, col, x, y, w)
+    rows = np.array([5, 0, 8, 3])
+    got = loops.conv_forward_uvw_rows(loops.Tables(prob), row_ptr, col, x, y, w, rows)
+    assert np.allclose(got, want[rows], atol=1e-12)
