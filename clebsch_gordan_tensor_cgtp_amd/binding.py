@@ -233,10 +233,11 @@ def conv_forward(plan: Plan, row_ptr, col, x, y, w, out=None, order=None, stream
     dt = plan.torch_dtype
     if out is None:
         out = torch.empty((N, plan.d_out), dtype=dt, device=x.device)
+    wshape = (plan.weight_numel,) if plan.mode == "uvw" else (E, plan.weight_numel)  # uvw: shared weights
     _check(lib().cgtp_conv_forward_ordered(plan.handle, N, E, _dev(row_ptr, "row_ptr", torch.int32),
                                    _dev(col, "col", torch.int32), _ptr_or_null(order, "order", torch.int32, (N,)),
                                    _dev(x, "x", dt, (N, plan.d_x)),
-                                   _dev(y, "y", dt, (E, plan.d_sh)), _dev(w, "w", dt, (E, plan.weight_numel)),
+                                   _dev(y, "y", dt, (E, plan.d_sh)), _dev(w, "w", dt, wshape),
                                    _dev(out, "out", dt, (N, plan.d_out)), _stream(stream, x.device)))
     return out
 

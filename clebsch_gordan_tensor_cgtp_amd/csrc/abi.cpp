@@ -108,11 +108,6 @@ cgtp_status cgtp_plan_create(const char *in_irreps, const char *sh_irreps, const
         P.sh = cgtp::parse_irreps(sh_irreps, "SH");
         P.out = cgtp::parse_irreps(out_irreps, "output");
         cgtp::build_paths(P);
-        if (mode == CGTP_UVW)
-            for (const cgtp::Irrep &o : P.out)
-                if (o.mul > 16)
-                    throw cgtp::Error(CGTP_ERR_UNSUPPORTED,
-                                      "uvw: output multiplicities above 16 are not supported (one MFMA tile of 16)");
         cgtp::schedule(P);
         P.source = cgtp::generate_source(P);
         cgtp::compile_module(P);
@@ -127,6 +122,10 @@ cgtp_status cgtp_plan_create(const char *in_irreps, const char *sh_irreps, const
                 std::fprintf(stderr, "[cgtp]   bwd group %zu: %zu paths, mul %d, ct %d, tiles %d, prefetch %d\n", k,
                              P.bwd_groups[k].paths.size(), P.bwd_groups[k].mul, P.bwd_groups[k].ct,
                              P.bwd_groups[k].tiles, (int)P.bwd_groups[k].prefetch);
+            for (size_t k = 0; k < P.uvc_groups.size(); ++k)
+                std::fprintf(stderr, "[cgtp]   uvw convolution group %zu: %zu paths, mul %d, ct %d, tiles %d\n", k,
+                             P.uvc_groups[k].paths.size(), P.uvc_groups[k].mul, P.uvc_groups[k].ct,
+                             P.uvc_groups[k].tiles);
             for (size_t k = 0; k < P.dbl_groups.size(); ++k)
                 std::fprintf(stderr, "[cgtp]   double-backward sender group %zu: %zu paths, mul %d, ct %d, tiles %d\n", k,
                              P.dbl_groups[k].paths.size(), P.dbl_groups[k].mul, P.dbl_groups[k].ct,
@@ -234,6 +233,11 @@ cgtp_status cgtp_tp_forward(const cgtp_plan *plan, int64_t B, const void *x, con
         require_disjoint(out, B * P.d_out * es, "out", y, B * P.d_sh * es, "y");
         require_disjoint(out, B * P.d_out * es, "out", w, nw, "w");
         if (P.mode == CGTP_UVW) {
+            for (const cgtp::Irrep &o : P.out)
+                if (o.mul > 16)
+                    throw cgtp::Error(CGTP_ERR_UNSUPPORTED,
+                                      "uvw batched product: output multiplicities above 16 are not supported (one "
+                                      "MFMA tile of 16 output channels); the uvw convolution supports them");
             const auto &L = cgtp::module_for_current_device(P);
             long nrows = (long)B, nblocks = (long)((B + 15) / 16);
             void *args[] = {&x, &y, &w, &out, &nrows, &nblocks};
@@ -278,8 +282,8 @@ cgtp_status cgtp_conv_forward_ordered(const cgtp_plan *plan, int64_t N, int64_t 
         require(plan != nullptr, "plan is NULL");
         cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
         check_graph_sizes(N, E);
-        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw convolution is not built yet");
         if (N == 0) return;
+        const bool uvw = P.mode == CGTP_UVW;
         const size_t es = elem(P);
         require_ptr(row_ptr, "row_ptr", 4);
         require_ptr(out, "out", es);
@@ -287,12 +291,12 @@ cgtp_status cgtp_conv_forward_ordered(const cgtp_plan *plan, int64_t N, int64_t 
             require_ptr(col, "col", 4);
             require_ptr(x, "x", es);
             require_ptr(y, "y", es);
-            require_ptr(w, "w", es);
         }
+        if (E > 0 || uvw) require_ptr(w, "w", es);
         const size_t no = N * P.d_out * es;
         require_disjoint(out, no, "out", x, N * P.d_x * es, "x");
         require_disjoint(out, no, "out", y, E * P.d_sh * es, "y");
-        require_disjoint(out, no, "out", w, E * P.w_numel * es, "w");
+        require_disjoint(out, no, "out", w, (uvw ? 1 : E) * P.w_numel * es, "w");
         require_disjoint(out, no, "out", row_ptr, (N + 1) * 4, "row_ptr");
         require_disjoint(out, no, "out", col, E * 4, "col");
         if (order) {
@@ -300,6 +304,18 @@ cgtp_status cgtp_conv_forward_ordered(const cgtp_plan *plan, int64_t N, int64_t 
             require_disjoint(out, no, "out", order, N * 4, "order");
         }
         const auto &L = cgtp::module_for_current_device(P);
+        if (uvw) {
+            // one workgroup of 4 waves per 16 receivers, one launch per path group, in order
+            long nrows = (long)N;
+            const unsigned tiles = (unsigned)((N + 15) / 16);
+            for (int grp = 0; grp < (int)P.uvc_groups.size(); ++grp) {
+                void *args[] = {&row_ptr, &col, &x, &y, &w, &out, &nrows, &order, &grp};
+                check_hip(hipModuleLaunchKernel(L.conv_uvw, tiles, 1, 1, 256, 1, 1, 0, static_cast<hipStream_t>(stream),
+                                                args, nullptr),
+                          "hipModuleLaunchKernel");
+            }
+            return;
+        }
         int64_t waves = N * P.fwd_tasks;
         long nrows = (long)N, nwaves = (long)waves;
         void *args[] = {&row_ptr, &col, &x, &y, &w, &out, &nrows, &nwaves, &order};

@@ -988,7 +988,7 @@ void emit_uvw_group(Out &o, const Plan &P, int gi)
     o("");
 }
 
-void emit_uvw_kernel(Out &o, const Plan &P)
+void emit_mfma_defs(Out &o, const Plan &P)
 {
     const bool f64 = P.dtype == CGTP_F64;
     o("typedef ", f64 ? "double" : "float", " V4 __attribute__((ext_vector_type(4)));");
@@ -996,6 +996,10 @@ void emit_uvw_kernel(Out &o, const Plan &P)
         o("#define MFMA(a, b, c) __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0)");
     else
         o("#define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0)");
+}
+
+void emit_uvw_kernel(Out &o, const Plan &P)
+{
     for (int gi = 0; gi < (int)P.uvw_groups.size(); ++gi) emit_uvw_group(o, P, gi);
     o("// one wave per (group, 16-row block), group-major so that the waves resident at any time");
     o("// mostly run the same group's code");
@@ -1011,6 +1015,248 @@ void emit_uvw_kernel(Out &o, const Plan &P)
     o("switch (group) {");
     for (int gi = 0; gi < (int)P.uvw_groups.size(); ++gi)
         o("case ", gi, ": uvw_g", gi, "(blk, lane, x, y, w, out, nrows); break;");
+    o("default: break;");
+    o("}");
+    o.ind--;
+    o("}");
+    o("");
+}
+
+// ------------------------------------------------------------------------------------------
+// uvw convolution (shared weights): one workgroup of 4 waves per tile of 16
+// receivers and one launch per path group.  Edge stream: lanes are input
+// channels (edge slots when there are fewer than 64), and per receiver the
+// unweighted sums T_p[u][k] = sum over its edges of sum_ij C_ijk x[s,u,i] y[e,j]
+// stay in registers (Sobek page, Abstract: edge-local products consumed into
+// bounded receiver-side state).  T is staged in LDS as [p,k][u][row].  Mixing:
+// out[n, q, w, k] (+)= sum_p sum_u W_p[u][w] T_p[n][u][k] on MFMA 16x16x4 with
+// the 16 receivers as the B columns (A = W_p[u][w = lane % 16], B = T[row =
+// lane % 16][u = 4c + lane / 16][k]).  A slot's first group writes it, later
+// groups (later launches) add, so every sum has a fixed order.
+int uvc_mu_pad(const Path &p) { return (p.mul_in + 3) / 4 * 4; }
+
+void emit_uvc_group(Out &o, const Plan &P, int gi)
+{
+    const Group &g = P.uvc_groups[gi];
+    const bool f64 = P.dtype == CGTP_F64;
+    Touch t = touched(P, g.paths);
+    auto first_group_of_slot = [&](int q) {
+        for (int k = 0; k < (int)P.uvc_groups.size(); ++k)
+            for (int pi : P.uvc_groups[k].paths)
+                if (P.paths[pi].slot == q) return k;
+        return -1;
+    };
+    // LDS offset (in elements) of each path's T block
+    std::map<int, int> loff;
+    int lds_elems = 0;
+    for (int pi : g.paths) {
+        loff[pi] = lds_elems;
+        lds_elems += 16 * uvc_mu_pad(P.paths[pi]) * n_of(P.paths[pi].l3);
+    }
+    o("__device__ __forceinline__ void uvc_g", gi,
+      "(long tile, int wv, int lane, const int* __restrict__ row_ptr, const int* __restrict__ col, "
+      "const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows, "
+      "const int* __restrict__ order, T* lds)");
+    o("{");
+    o.ind++;
+    o("const int slot = lane >> ", log2i(g.ct), ";");
+    o("const int ul = lane & ", g.ct - 1, ";");
+    o("for (int m = 0; m < 4; ++m) {");
+    o.ind++;
+    o("const int r = wv + 4 * m;  // receiver of the tile handled by this wave");
+    o("const long idx = tile * 16 + r;");
+    o("const bool live = idx < nrows;");
+    o("const long n = live ? (order ? (long)order[idx] : idx) : 0;");
+    o("for (int ctile = 0; ctile < ", g.tiles, "; ++ctile) {");
+    o.ind++;
+    o("const int u = ctile * ", g.ct, " + ul;");
+    for (int pi : g.paths)
+        for (int k = 0; k < n_of(P.paths[pi].l3); ++k) o("T t", pi, "_", k, " = (T)0;");
+    o("const int e0 = live ? row_ptr[n] : 0, e1 = live ? row_ptr[n + 1] : 0;");
+    o("if (e0 < e1) {");
+    o.ind++;
+    // operands: x of the sender (gathered), y of the edge; senders two ahead, operands one ahead
+    auto loads = [&](const std::string &pre, const std::string &si, const std::string &ei, bool declare) {
+        const std::string Ty = declare ? "T " : "";
+        for (int b : t.i1) {
+            const Irrep &ir = P.ins[b];
+            int off = 0;
+            for (int pi : g.paths)
+                if (P.paths[pi].i1 == b) off = P.paths[pi].a;
+            const bool m = needs_mask(ir.mul, g);
+            for (int i = 0; i < n_of(ir.l); ++i) {
+                std::ostringstream addr;
+                addr << "x[(size_t)" << si << " * DX + " << off << " + " << (m ? "(u < " + std::to_string(ir.mul) + " ? u : 0)" : "u")
+                     << " * " << n_of(ir.l) << " + " << i << "]";
+                if (m)
+                    o(Ty, pre, "x", b, "_", i, " = (u < ", ir.mul, ") ? ", addr.str(), " : (T)0;");
+                else
+                    o(Ty, pre, "x", b, "_", i, " = ", addr.str(), ";");
+            }
+        }
+        for (int b : t.i2) {
+            int off = 0;
+            for (int pi : g.paths)
+                if (P.paths[pi].i2 == b) off = P.paths[pi].b;
+            for (int j = 0; j < n_of(P.sh[b].l); ++j)
+                o(Ty, pre, "y", b, "_", j, " = y[(size_t)", ei, " * DSH + ", off + j, "];");
+        }
+    };
+    auto copy = [&]() {
+        for (int b : t.i1)
+            for (int i = 0; i < n_of(P.ins[b].l); ++i) o("cx", b, "_", i, " = nx", b, "_", i, ";");
+        for (int b : t.i2)
+            for (int j = 0; j < n_of(P.sh[b].l); ++j) o("cy", b, "_", j, " = ny", b, "_", j, ";");
+    };
+    o("int e = e0 + slot;");
+    o("int ec = e < e1 ? e : e1 - 1;");
+    o("int s = col[ec];");
+    o("int en = (e + ", g.es, " < e1) ? e + ", g.es, " : e1 - 1;");
+    o("int sn = col[en];");
+    loads("c", "s", "ec", true);
+    o("for (; e < e1; e += ", g.es, ") {");
+    o.ind++;
+    o("const int enn = (e + ", 2 * g.es, " < e1) ? e + ", 2 * g.es, " : e1 - 1;");
+    o("const int snn = col[enn];");
+    loads("n", "sn", "en", true);
+    for (auto &pr : pairs_of(P, g.paths)) {
+        int i1 = pr.first.first, i2 = pr.first.second;
+        std::set<std::pair<int, int>> used;
+        for (int pi : pr.second)
+            for (const Nonzero &z : P.paths[pi].nz) used.insert({z.i, z.j});
+        o("{");
+        o.ind++;
+        for (auto &ij : used)
+            o("const T q", ij.first, "_", ij.second, " = cx", i1, "_", ij.first, " * cy", i2, "_", ij.second, ";");
+        for (int pi : pr.second) {
+            std::map<int, std::vector<const Nonzero *>> byk;
+            for (const Nonzero &z : P.paths[pi].nz) byk[z.k].push_back(&z);
+            for (auto &kv : byk) o("t", pi, "_", kv.first, " += ", cg_sum(kv.second, "q", f64), ";");
+        }
+        o.ind--;
+        o("}");
+    }
+    copy();
+    o("en = enn;");
+    o("sn = snn;");
+    o.ind--;
+    o("}");  // edge loop
+    o.ind--;
+    o("}");  // e0 < e1
+    for (int m = 32; m >= g.ct; m /= 2)
+        for (int pi : g.paths)
+            for (int k = 0; k < n_of(P.paths[pi].l3); ++k) o("t", pi, "_", k, " += __shfl_xor(t", pi, "_", k, ", ", m, ");");
+    o("if (slot == 0) {");
+    o.ind++;
+    for (int pi : g.paths) {
+        const Path &p = P.paths[pi];
+        const int mp = uvc_mu_pad(p);
+        for (int k = 0; k < n_of(p.l3); ++k)
+            o("if (u < ", mp, ") lds[", loff[pi] + 16 * mp * k, " + u * 16 + r] = t", pi, "_", k, ";");
+    }
+    o.ind--;
+    o("}");
+    o.ind--;
+    o("}");  // channel tiles
+    o.ind--;
+    o("}");  // receivers of the wave
+    o("__syncthreads();");
+    // mixing on MFMA: items (slot q, 16-wide block of output channels), round-robin over the waves
+    o("const int usub = lane >> 4;");
+    o("const int row = lane & 15;");
+    o("const long oidx = tile * 16 + row;");
+    o("const bool olive = oidx < nrows;");
+    o("const long on = olive ? (order ? (long)order[oidx] : oidx) : 0;");
+    o("T* orow = out + (size_t)on * DOUT;");
+    int item = 0;
+    for (int q : t.slots) {
+        const Irrep &ir = P.out[q];
+        int ooff = 0;
+        for (int qq = 0; qq < q; ++qq) ooff += P.out[qq].dim();
+        const bool add = first_group_of_slot(q) < gi;
+        const int wtiles = (ir.mul + 15) / 16;
+        for (int wt = 0; wt < wtiles; ++wt, ++item) {
+            o("if (wv == ", item % 4, ") {");
+            o.ind++;
+            for (int k = 0; k < n_of(ir.l); ++k) o("V4 d", k, " = {0, 0, 0, 0};");
+            for (int pi : g.paths) {
+                const Path &p = P.paths[pi];
+                if (p.slot != q) continue;
+                const int mp = uvc_mu_pad(p);
+                o("{");
+                o.ind++;
+                for (int c = 0; c < mp / 4; ++c) {
+                    std::string u = "(" + std::to_string(4 * c) + " + usub)";
+                    std::string wcol = "(" + std::to_string(16 * wt) + " + row)";
+                    const bool wmask = 4 * c + 3 >= p.mul_in || 16 * wt + 15 >= p.mul_out;
+                    if (wmask) {
+                        o("const bool wok", c, " = ", u, " < ", p.mul_in, " && ", wcol, " < ", p.mul_out, ";");
+                        o("const T wv", c, " = w[", p.w_off, " + (wok", c, " ? ", u, " * ", p.mul_out, " + ", wcol, " : 0)];");
+                        o("const T wa", c, " = wok", c, " ? wv", c, " : (T)0;");
+                    } else {
+                        o("const T wa", c, " = w[", p.w_off, " + ", u, " * ", p.mul_out, " + ", wcol, "];");
+                    }
+                }
+                for (int k = 0; k < n_of(p.l3); ++k)
+                    for (int c = 0; c < mp / 4; ++c) {
+                        const int base = loff[pi] + 16 * mp * k + 16 * 4 * c;
+                        if (4 * c + 3 >= p.mul_in)
+                            o("d", k, " = MFMA(wa", c, ", (", 4 * c, " + usub < ", p.mul_in, ") ? lds[", base, " + lane] : (T)0, d", k,
+                              ");");
+                        else
+                            o("d", k, " = MFMA(wa", c, ", lds[", base, " + lane], d", k, ");");
+                    }
+                o.ind--;
+                o("}");
+            }
+            o("if (olive) {");
+            o.ind++;
+            for (int v = 0; v < 4; ++v) {
+                std::string wo = f64 ? "(" + std::to_string(16 * wt + 4 * v) + " + usub)"
+                                     : "(" + std::to_string(16 * wt + v) + " + 4 * usub)";
+                std::string guard = 16 * wt + 15 >= ir.mul ? "if (" + wo + " < " + std::to_string(ir.mul) + ") " : "";
+                for (int k = 0; k < n_of(ir.l); ++k)
+                    o(guard, "orow[", ooff, " + ", wo, " * ", n_of(ir.l), " + ", k, "] ", add ? "+=" : "=", " d", k, "[", v, "];");
+            }
+            o.ind--;
+            o("}");
+            o.ind--;
+            o("}");
+        }
+    }
+    o.ind--;
+    o("}");
+    o("");
+}
+
+int uvc_lds_elems(const Plan &P)
+{
+    int m = 1;
+    for (const Group &g : P.uvc_groups) {
+        int e = 0;
+        for (int pi : g.paths) e += 16 * uvc_mu_pad(P.paths[pi]) * n_of(P.paths[pi].l3);
+        m = std::max(m, e);
+    }
+    return m;
+}
+
+void emit_uvc_kernel(Out &o, const Plan &P)
+{
+    for (int gi = 0; gi < (int)P.uvc_groups.size(); ++gi) emit_uvc_group(o, P, gi);
+    o("// one workgroup of 4 waves per 16 receivers; `group` selects the path group (launched in order)");
+    o("extern \"C\" __global__ void __launch_bounds__(256, ", P.uvc_waves_per_eu,
+      ") cgtp_conv_uvw(const int* __restrict__ row_ptr, const int* __restrict__ col, const T* __restrict__ x, "
+      "const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows, "
+      "const int* __restrict__ order, int group)");
+    o("{");
+    o.ind++;
+    o("__shared__ T lds[", uvc_lds_elems(P), "];  // T of the tile's 16 receivers, [p,k][u][row]");
+    o("const long tile = blockIdx.x;");
+    o("const int wv = threadIdx.x >> 6;");
+    o("const int lane = threadIdx.x & 63;");
+    o("switch (group) {");
+    for (int gi = 0; gi < (int)P.uvc_groups.size(); ++gi)
+        o("case ", gi, ": uvc_g", gi, "(tile, wv, lane, row_ptr, col, x, y, w, out, nrows, order, lds); break;");
     o("default: break;");
     o("}");
     o.ind--;
@@ -1044,8 +1290,11 @@ std::string generate_source(const Plan &P)
         o("// @@section cgtp_conv_dbwd_send");
         emit_bwd_kernel(o, P, true);
     } else {
+        emit_mfma_defs(o, P);
         o("// @@section cgtp_tp_uvw");
         emit_uvw_kernel(o, P);
+        o("// @@section cgtp_conv_uvw");
+        emit_uvc_kernel(o, P);
     }
     return o.s.str();
 }

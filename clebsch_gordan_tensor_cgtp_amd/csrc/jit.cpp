@@ -124,6 +124,7 @@ const Plan::Loaded &module_for_current_device(Plan &P)
         check(hipModuleGetFunction(&L.dbwd_send, L.module, "cgtp_conv_dbwd_send"), "hipModuleGetFunction(dbwd_send)");
     } else {
         check(hipModuleGetFunction(&L.tp_uvw, L.module, "cgtp_tp_uvw"), "hipModuleGetFunction(tp_uvw)");
+        check(hipModuleGetFunction(&L.conv_uvw, L.module, "cgtp_conv_uvw"), "hipModuleGetFunction(conv_uvw)");
     }
     return P.loaded.emplace(dev, L).first->second;
 }

@@ -64,11 +64,13 @@ struct Plan {
     std::vector<Group> bwd_groups;  // backward: one launch per group, in order
     std::vector<Group> uvw_groups;  // uvw batched product: one launch per group of output slots
     std::vector<Group> dbl_groups;  // double backward, sender pass: one launch per group, in order
+    std::vector<Group> uvc_groups;  // uvw convolution: one launch per group, in order (a slot may span groups)
     int fwd_waves_per_eu = 4;       // occupancy target given to the compiler (min waves per SIMD)
     int bwd_waves_per_eu = 4;
     int uvw_waves_per_eu = 2;
     int dbl_fwd_waves_per_eu = 2;   // double backward, receiver pass (twice the forward's operands)
     int dbl_bwd_waves_per_eu = 2;   // double backward, sender pass
+    int uvc_waves_per_eu = 2;       // uvw convolution
     bool stream_hint = true;        // nontemporal loads/stores for once-touched per-edge rows
     bool bwd_sched_barrier = true;  // keep path blocks of the backward from interleaving
     int bwd_prefetch = -1;          // -1: per group by register estimate; 0/1 forced
@@ -80,7 +82,7 @@ struct Plan {
     struct Loaded {
         hipModule_t module = nullptr;
         hipFunction_t conv_fwd = nullptr, conv_bwd = nullptr, tp_fwd = nullptr, tp_uvw = nullptr;
-        hipFunction_t dbwd_recv = nullptr, dbwd_send = nullptr;
+        hipFunction_t dbwd_recv = nullptr, dbwd_send = nullptr, conv_uvw = nullptr;
     };
     std::map<int, Loaded> loaded;
 };

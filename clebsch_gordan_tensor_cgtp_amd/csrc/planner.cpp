@@ -332,6 +332,39 @@ void schedule(Plan &P)
         }
     }
 
+    // uvw convolution: paths in slot order, packed while the per-lane sums T_p
+    // (2l3+1 per path) fit 64 registers and the workgroup's staging of T for 16
+    // receivers (16 * mul_in rounded to 4 * (2l3+1) per path) fits 64 KB of LDS.
+    P.uvc_groups.clear();
+    if (P.mode == CGTP_UVW) {
+        std::vector<int> order;
+        for (int q = 0; q < (int)P.out.size(); ++q)
+            for (int i = 0; i < (int)P.paths.size(); ++i)
+                if (P.paths[i].slot == q) order.push_back(i);
+        Group cur;
+        int regs = 0;
+        long lds = 0;
+        for (int i : order) {
+            const Path &p = P.paths[i];
+            int need = word * (2 * p.l3 + 1);
+            long bytes = 16L * ((p.mul_in + 3) / 4 * 4) * (2 * p.l3 + 1) * 4 * word;
+            if (!cur.paths.empty() && (regs + need > 64 || lds + bytes > 65536)) {
+                P.uvc_groups.push_back(cur);
+                cur = Group();
+                regs = 0;
+                lds = 0;
+            }
+            cur.paths.push_back(i);
+            regs += need;
+            lds += bytes;
+        }
+        if (!cur.paths.empty()) P.uvc_groups.push_back(cur);
+        for (Group &g : P.uvc_groups) {
+            for (int pi : g.paths) g.mul = std::max(g.mul, P.paths[pi].mul_in);
+            finish_group(g);
+        }
+    }
+
     // Sender-pass groups (backward, and the double backward's d/dx, d/dy, d/dW):
     // paths sharing an SH block (so that block's dY is complete in one group),
     // split when the register estimate exceeds the budget.
@@ -417,6 +450,8 @@ void schedule(Plan &P)
     if (const char *e = std::getenv("CGTP_DBL_BWD_WAVES")) P.dbl_bwd_waves_per_eu = std::max(1, std::atoi(e));
     if (const char *e = std::getenv("CGTP_BWD_WAVES")) P.bwd_waves_per_eu = std::max(1, std::atoi(e));
     P.uvw_waves_per_eu = P.dtype == CGTP_F64 ? 1 : 2;
+    P.uvc_waves_per_eu = P.dtype == CGTP_F64 ? 1 : 2;
+    if (const char *e = std::getenv("CGTP_UVC_WAVES")) P.uvc_waves_per_eu = std::max(1, std::atoi(e));
     if (const char *e = std::getenv("CGTP_UVW_WAVES")) P.uvw_waves_per_eu = std::max(1, std::atoi(e));
     if (const char *e = std::getenv("CGTP_BWD_SCHED_BARRIER")) P.bwd_sched_barrier = std::atoi(e) != 0;
 }

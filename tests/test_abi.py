@@ -109,7 +109,6 @@ def test_plan_errors():
         ("8x1o", "1x1o", "8x0e+8x0e", 0, 0, cg.STATUS_CODES["CGTP_ERR_IRREPS"]),  # 2 slots, 1 path
         ("32x0e", "1x0e", "32x0e", 7, 0, cg.STATUS_CODES["CGTP_ERR_INVALID_ARG"]),
         ("32x0e", "1x0e", "32x0e", 0, 9, cg.STATUS_CODES["CGTP_ERR_INVALID_ARG"]),
-        ("16x0e", "1x0e", "32x0e", 1, 0, cg.STATUS_CODES["CGTP_ERR_UNSUPPORTED"]),  # uvw mul_out > 16
     ]
     for a, b, c, mode, dt, want in bad:
         st = L.cgtp_plan_create(a.encode(), b.encode(), c.encode(), mode, dt, ctypes.byref(h))
@@ -137,7 +136,16 @@ def test_call_errors_before_any_gpu_work():
     # output overlapping an input
     assert L.cgtp_conv_forward(plan.handle, 4, 4, fake, ctypes.c_void_p(1 << 22), ctypes.c_void_p(1 << 24),
                                fake, fake, ctypes.c_void_p((1 << 24) + 64), s) == inval
-    assert L.cgtp_conv_forward(uvw.handle, 4, 4, fake, fake, fake, fake, fake, fake, s) == unsup
+    # uvw convolution: shared weights must be given, outputs must not overlap them
+    assert L.cgtp_conv_forward(uvw.handle, 4, 4, fake, fake, fake, fake, null, fake, s) == inval
+    assert L.cgtp_conv_forward(uvw.handle, 4, 0, fake, null, null, null, null, fake, s) == inval
+    assert L.cgtp_conv_forward(uvw.handle, 4, 4, fake, fake, ctypes.c_void_p(1 << 22), ctypes.c_void_p(1 << 24),
+                               ctypes.c_void_p(1 << 26), ctypes.c_void_p((1 << 26) + 64), s) == inval
+    # the batched uvw product covers one 16-wide MFMA tile of output channels
+    wide = ctypes.c_void_p()
+    assert L.cgtp_plan_create(b"16x0e", b"1x0e", b"32x0e", 1, 0, ctypes.byref(wide)) == 0
+    assert L.cgtp_tp_forward(wide, 4, fake, fake, fake, 1, ctypes.c_void_p(1 << 26), s) == unsup
+    assert L.cgtp_plan_destroy(wide) == 0
     assert L.cgtp_tp_forward(plan.handle, 4, fake, fake, fake, 1, fake, s) == inval   # uvu needs shared=0
     assert L.cgtp_tp_forward(uvw.handle, 4, fake, fake, fake, 0, fake, s) == inval    # uvw needs shared=1
     assert L.cgtp_spherical_harmonics(8, 0, 4, fake, fake, s) == inval
