@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c2uvw"])
     ap.add_argument("--dtype", default="f32", choices=["f32", "f64"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seed", type=int, default=0)
@@ -187,6 +187,95 @@ def bench_double_backward(a, spec, plan, d, host_graph, device):
     print(json.dumps(line), flush=True)
 
 
+def uvw_conv_flops(plan, N, E):
+    """Fixed counting convention for the uvw convolution: per edge the sparse contraction
+    sum_p mul_in * 2 * nnz_p (VALU), per receiver the mixing sum_p 2 * mul_in * mul_out * (2l3+1)
+    (MFMA)."""
+    sparse = dense = 0
+    for p in range(plan.num_paths):
+        info = plan.path(p)
+        sparse += info["mul_in"] * 2 * info["nnz"]
+        dense += 2 * info["mul_in"] * info["mul_out"] * (2 * info["l3"] + 1)
+    return E * sparse, N * dense
+
+
+def cpu_baseline_uvw_conv(plan_prob, spec, seed, host_graph, max_seconds=30.0):
+    """The oracle's explicit uvw loops on every edge of a contiguous receiver slice (~5% of the
+    edges), summed per receiver; random values (timing only).  Rate = slice edges per second."""
+    from oracle import irreps as oirreps
+    from oracle import loops
+    row_ptr, col = (np.asarray(a, dtype=np.int64) for a in host_graph)
+    N, E = len(row_ptr) - 1, len(col)
+    prob = oirreps.build_problem(spec.in_irreps, oirreps.sh_irreps(spec.lmax_sh), spec.out_irreps, "uvw")
+    tab = loops.Tables(prob)
+    threads = loops.default_threads()
+    rng = np.random.default_rng(seed + 97)
+    target = max(2_000, E // 20)
+    start = int(rng.integers(0, max(1, N // 2)))
+    stop = min(max(int(np.searchsorted(row_ptr, row_ptr[start] + target)), start + 1), N)
+    x = rng.standard_normal((N, prob.d_in))
+    y = rng.standard_normal((E, prob.d_sh))
+    w = rng.standard_normal(prob.weight_numel)
+    rows = np.arange(start, stop)
+    n_e = int(row_ptr[stop] - row_ptr[start])
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        loops.conv_forward_uvw_rows(tab, row_ptr, col, x, y, w, rows, threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or el >= max_seconds:
+            break
+    return {"value": n_e * reps / el, "unit": "edges/s", "cores": threads, "kind": "oracle",
+            "sample": f"receivers [{start},{stop}) = {n_e} of {E} edges: uvw convolution output of that slice; "
+                      f"fp64 explicit loops, mean of {reps} rep(s)"}
+
+
+def bench_conv_uvw(a, spec, plan, d, host_graph, device):
+    import torch
+    from clebsch_gordan_tensor_cgtp_amd import binding as cg
+    N, E = d["row_ptr"].shape[0] - 1, d["col"].shape[0]
+    y = cg.spherical_harmonics(spec.lmax_sh, d["vec"])
+    order = cg.graph_order(d["row_ptr"]) if not a.natural_order else None
+    out = torch.empty((N, plan.d_out), dtype=plan.torch_dtype, device=device)
+
+    def step():
+        cg.conv_forward(plan, d["row_ptr"], d["col"], d["x"], y, d["w"], out=out, order=order)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for _ in range(a.steps):
+        step()
+    ev[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev[0].elapsed_time(ev[1]) / a.steps
+    sparse, dense = uvw_conv_flops(plan, N, E)
+    tflops = (sparse + dense) / (ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC, "value": E / (wall / a.steps), "unit": "edges/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": wall * 1e3 / a.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": a.dtype, "data": "synthetic",
+        "config": {"workload": spec.name, "N": N, "E": E, "in_irreps": spec.in_irreps, "out_irreps": spec.out_irreps,
+                   "sh_lmax": spec.lmax_sh, "paths": plan.num_paths, "d_out": plan.d_out,
+                   "step": "conv_forward (uvw: shared weights, MFMA mixing per 16-receiver tile)",
+                   "receiver_schedule": "natural" if a.natural_order else "heavy-first", "fwd_ms": ms},
+        "roofline": {"bound": "alu", "kernel": "cgtp_conv_uvw", "achieved": tflops, "peak": 157.3, "unit": "TFLOP/s",
+                     "frac": tflops / 157.3, "traffic": measured_traffic(plan, spec, a.dtype, "cgtp_conv_uvw"),
+                     "flops_per_launch": {"sparse_valu": sparse, "mixing_mfma": dense}, "avg_launch_ms": ms,
+                     "hbm_algorithmic_bytes_per_launch": (N + 1) * 4 + E * 4 + (4 if a.dtype == "f32" else 8) * (
+                         N * plan.d_x + E * plan.d_sh + plan.weight_numel + N * plan.d_out)},
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_uvw_conv(None, spec, a.seed, host_graph)
+    print(json.dumps(line), flush=True)
+
+
 def kernel_digest(source, kernel):
     """SHA-1 of the generated code one kernel runs: the module's shared preamble plus that
     kernel's own section (the generator marks sections with '// @@section NAME' lines)."""
@@ -238,7 +327,8 @@ def make_inputs(spec, dtype, seed, device):
         "row_ptr": dev(row_ptr), "col": dev(col),
         "x": dev(synth.normal(st["x"], (N, plan.d_x), dtype=npdt, device=device)),
         "vec": dev(synth.normal(st["vec"], (E, 3), dtype=npdt, device=device)),
-        "w": dev(synth.normal(st["w"], (E, plan.weight_numel), 1.0 / np.sqrt(fan_in), dtype=npdt, device=device)),
+        "w": dev(synth.normal(st["w"], (E, plan.weight_numel), 1.0 / np.sqrt(fan_in), dtype=npdt, device=device))
+        if spec.mode == "uvu" else dev(synth.normal(st["w"], (plan.weight_numel,), 1.0 / np.sqrt(32.0), dtype=npdt)),
         "g": dev(synth.normal(st["sample"], (N, plan.d_out), dtype=npdt, device=device)),
     }
     return plan, d, (row_ptr, col)
@@ -368,10 +458,12 @@ def main():
     from clebsch_gordan_tensor_cgtp_amd import synth
     device = "cuda:0"
     torch.cuda.set_device(0)
-    spec = synth.WORKLOADS[a.workload]
+    spec = {**synth.WORKLOADS, **synth.EXTRA_WORKLOADS}[a.workload]
     if not hasattr(spec, "n_edges"):
         return bench_tp(a, spec, device)
     plan, d, host_graph = make_inputs(spec, a.dtype, a.seed, device)
+    if spec.mode == "uvw":
+        return bench_conv_uvw(a, spec, plan, d, host_graph, device)
     if a.double_backward:
         return bench_double_backward(a, spec, plan, d, host_graph, device)
     N, E = d["row_ptr"].shape[0] - 1, d["col"].shape[0]

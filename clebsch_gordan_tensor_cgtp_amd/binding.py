@@ -170,6 +170,8 @@ def per_path_out_irreps(in_irreps: str, lmax_sh: int, lmax_out: int) -> str:
 def plan_for(spec, dtype="f32") -> Plan:
     """The plan of a workload from ``synth.WORKLOADS`` (cached per process)."""
     if hasattr(spec, "n_edges"):
+        if spec.mode == "uvw":
+            return Plan(spec.in_irreps, sh_irreps(spec.lmax_sh), spec.out_irreps, "uvw", dtype)
         out = per_path_out_irreps(spec.in_irreps, spec.lmax_sh, spec.lmax_out)
         return Plan(spec.in_irreps, sh_irreps(spec.lmax_sh), out, "uvu", dtype)
     if spec.mode == "uvu":

@@ -71,7 +71,7 @@ def warm(names):
     from clebsch_gordan_tensor_cgtp_amd import binding, synth
     for name in names:
         for dtype in ("f32", "f64"):
-            spec = synth.WORKLOADS[name]
+            spec = {**synth.WORKLOADS, **synth.EXTRA_WORKLOADS}[name]
             binding.plan_for(spec, dtype)
 
 

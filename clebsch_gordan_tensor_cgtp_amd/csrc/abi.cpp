@@ -123,9 +123,9 @@ cgtp_status cgtp_plan_create(const char *in_irreps, const char *sh_irreps, const
                              P.bwd_groups[k].paths.size(), P.bwd_groups[k].mul, P.bwd_groups[k].ct,
                              P.bwd_groups[k].tiles, (int)P.bwd_groups[k].prefetch);
             for (size_t k = 0; k < P.uvc_groups.size(); ++k)
-                std::fprintf(stderr, "[cgtp]   uvw convolution group %zu: %zu paths, mul %d, ct %d, tiles %d\n", k,
-                             P.uvc_groups[k].paths.size(), P.uvc_groups[k].mul, P.uvc_groups[k].ct,
-                             P.uvc_groups[k].tiles);
+                std::fprintf(stderr, "[cgtp]   uvw convolution group %zu: %zu paths, mul %d, ct %d, tiles %d, %d receivers "
+                             "per wave\n", k, P.uvc_groups[k].paths.size(), P.uvc_groups[k].mul, P.uvc_groups[k].ct,
+                             P.uvc_groups[k].tiles, P.uvc_rpw);
             for (size_t k = 0; k < P.dbl_groups.size(); ++k)
                 std::fprintf(stderr, "[cgtp]   double-backward sender group %zu: %zu paths, mul %d, ct %d, tiles %d\n", k,
                              P.dbl_groups[k].paths.size(), P.dbl_groups[k].mul, P.dbl_groups[k].ct,
@@ -305,13 +305,14 @@ cgtp_status cgtp_conv_forward_ordered(const cgtp_plan *plan, int64_t N, int64_t 
         }
         const auto &L = cgtp::module_for_current_device(P);
         if (uvw) {
-            // one workgroup of 4 waves per 16 receivers, one launch per path group, in order
+            // one workgroup of 16 / rpw waves per 16 receivers, one launch per path group, in order
             long nrows = (long)N;
             const unsigned tiles = (unsigned)((N + 15) / 16);
+            const unsigned threads = 1024u / (unsigned)P.uvc_rpw;
             for (int grp = 0; grp < (int)P.uvc_groups.size(); ++grp) {
                 void *args[] = {&row_ptr, &col, &x, &y, &w, &out, &nrows, &order, &grp};
-                check_hip(hipModuleLaunchKernel(L.conv_uvw, tiles, 1, 1, 256, 1, 1, 0, static_cast<hipStream_t>(stream),
-                                                args, nullptr),
+                check_hip(hipModuleLaunchKernel(L.conv_uvw, tiles, 1, 1, threads, 1, 1, 0,
+                                                static_cast<hipStream_t>(stream), args, nullptr),
                           "hipModuleLaunchKernel");
             }
             return;

@@ -1023,8 +1023,8 @@ void emit_uvw_kernel(Out &o, const Plan &P)
 }
 
 // ------------------------------------------------------------------------------------------
-// uvw convolution (shared weights): one workgroup of 4 waves per tile of 16
-// receivers and one launch per path group.  Edge stream: lanes are input
+// uvw convolution (shared weights): one workgroup per tile of 16 receivers
+// (16 / rpw waves, rpw receivers each) and one launch per path group.  Edge stream: lanes are input
 // channels (edge slots when there are fewer than 64), and per receiver the
 // unweighted sums T_p[u][k] = sum over its edges of sum_ij C_ijk x[s,u,i] y[e,j]
 // stay in registers (Sobek page, Abstract: edge-local products consumed into
@@ -1061,9 +1061,10 @@ void emit_uvc_group(Out &o, const Plan &P, int gi)
     o.ind++;
     o("const int slot = lane >> ", log2i(g.ct), ";");
     o("const int ul = lane & ", g.ct - 1, ";");
-    o("for (int m = 0; m < 4; ++m) {");
+    const int nw = 16 / P.uvc_rpw;  // waves per workgroup
+    o("for (int m = 0; m < ", P.uvc_rpw, "; ++m) {");
     o.ind++;
-    o("const int r = wv + 4 * m;  // receiver of the tile handled by this wave");
+    o("const int r = wv + ", nw, " * m;  // receiver of the tile handled by this wave");
     o("const long idx = tile * 16 + r;");
     o("const bool live = idx < nrows;");
     o("const long n = live ? (order ? (long)order[idx] : idx) : 0;");
@@ -1176,7 +1177,7 @@ void emit_uvc_group(Out &o, const Plan &P, int gi)
         const bool add = first_group_of_slot(q) < gi;
         const int wtiles = (ir.mul + 15) / 16;
         for (int wt = 0; wt < wtiles; ++wt, ++item) {
-            o("if (wv == ", item % 4, ") {");
+            o("if (wv == ", item % nw, ") {");
             o.ind++;
             for (int k = 0; k < n_of(ir.l); ++k) o("V4 d", k, " = {0, 0, 0, 0};");
             for (int pi : g.paths) {
@@ -1243,8 +1244,8 @@ int uvc_lds_elems(const Plan &P)
 void emit_uvc_kernel(Out &o, const Plan &P)
 {
     for (int gi = 0; gi < (int)P.uvc_groups.size(); ++gi) emit_uvc_group(o, P, gi);
-    o("// one workgroup of 4 waves per 16 receivers; `group` selects the path group (launched in order)");
-    o("extern \"C\" __global__ void __launch_bounds__(256, ", P.uvc_waves_per_eu,
+    o("// one workgroup of ", 16 / P.uvc_rpw, " waves per 16 receivers; `group` selects the path group (launched in order)");
+    o("extern \"C\" __global__ void __launch_bounds__(", 1024 / P.uvc_rpw, ", ", P.uvc_waves_per_eu,
       ") cgtp_conv_uvw(const int* __restrict__ row_ptr, const int* __restrict__ col, const T* __restrict__ x, "
       "const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows, "
       "const int* __restrict__ order, int group)");

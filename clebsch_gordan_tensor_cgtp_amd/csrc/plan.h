@@ -71,6 +71,7 @@ struct Plan {
     int dbl_fwd_waves_per_eu = 2;   // double backward, receiver pass (twice the forward's operands)
     int dbl_bwd_waves_per_eu = 2;   // double backward, sender pass
     int uvc_waves_per_eu = 2;       // uvw convolution
+    int uvc_rpw = 4;                // uvw convolution: receivers per wave (16 / waves per workgroup)
     bool stream_hint = true;        // nontemporal loads/stores for once-touched per-edge rows
     bool bwd_sched_barrier = true;  // keep path blocks of the backward from interleaving
     int bwd_prefetch = -1;          // -1: per group by register estimate; 0/1 forced

@@ -334,34 +334,66 @@ void schedule(Plan &P)
 
     // uvw convolution: paths in slot order, packed while the per-lane sums T_p
     // (2l3+1 per path) fit 64 registers and the workgroup's staging of T for 16
-    // receivers (16 * mul_in rounded to 4 * (2l3+1) per path) fits 64 KB of LDS.
+    // receivers (16 * mul_in rounded to 4 * (2l3+1) per path) fits the LDS budget.
+    // Workgroup shape: one receiver per wave (16 waves, 4 per SIMD, <= 128 VGPRs)
+    // when the per-lane estimate fits, else 2 or 4 receivers per wave.  A 16-wave
+    // workgroup fills a CU alone, so it may stage up to 120 KB; smaller ones keep
+    // 64 KB so that two fit.
     P.uvc_groups.clear();
     if (P.mode == CGTP_UVW) {
-        std::vector<int> order;
-        for (int q = 0; q < (int)P.out.size(); ++q)
-            for (int i = 0; i < (int)P.paths.size(); ++i)
-                if (P.paths[i].slot == q) order.push_back(i);
-        Group cur;
-        int regs = 0;
-        long lds = 0;
-        for (int i : order) {
-            const Path &p = P.paths[i];
-            int need = word * (2 * p.l3 + 1);
-            long bytes = 16L * ((p.mul_in + 3) / 4 * 4) * (2 * p.l3 + 1) * 4 * word;
-            if (!cur.paths.empty() && (regs + need > 64 || lds + bytes > 65536)) {
-                P.uvc_groups.push_back(cur);
-                cur = Group();
-                regs = 0;
-                lds = 0;
+        auto make = [&](long lds_budget, std::vector<Group> &groups) {
+            groups.clear();
+            std::vector<int> order;
+            for (int q = 0; q < (int)P.out.size(); ++q)
+                for (int i = 0; i < (int)P.paths.size(); ++i)
+                    if (P.paths[i].slot == q) order.push_back(i);
+            Group cur;
+            int regs = 0;
+            long lds = 0;
+            for (int i : order) {
+                const Path &p = P.paths[i];
+                int need = word * (2 * p.l3 + 1);
+                long bytes = 16L * ((p.mul_in + 3) / 4 * 4) * (2 * p.l3 + 1) * 4 * word;
+                if (!cur.paths.empty() && (regs + need > 64 || lds + bytes > lds_budget)) {
+                    groups.push_back(cur);
+                    cur = Group();
+                    regs = 0;
+                    lds = 0;
+                }
+                cur.paths.push_back(i);
+                regs += need;
+                lds += bytes;
             }
-            cur.paths.push_back(i);
-            regs += need;
-            lds += bytes;
-        }
-        if (!cur.paths.empty()) P.uvc_groups.push_back(cur);
-        for (Group &g : P.uvc_groups) {
-            for (int pi : g.paths) g.mul = std::max(g.mul, P.paths[pi].mul_in);
-            finish_group(g);
+            if (!cur.paths.empty()) groups.push_back(cur);
+            int est_max = 0;
+            for (Group &g : groups) {
+                for (int pi : g.paths) g.mul = std::max(g.mul, P.paths[pi].mul_in);
+                finish_group(g);
+                std::set<int> i1s, i2s;
+                int acc = 0;
+                for (int pi : g.paths) {
+                    i1s.insert(P.paths[pi].i1);
+                    i2s.insert(P.paths[pi].i2);
+                    acc += 2 * P.paths[pi].l3 + 1;
+                }
+                int ops = 0;
+                for (int b : i1s) ops += 2 * P.ins[b].l + 1;
+                for (int b : i2s) ops += 2 * P.sh[b].l + 1;
+                // x_i * y_j products of the largest (input block, SH block) pair, live together
+                std::map<std::pair<int, int>, std::set<std::pair<int, int>>> pair_ij;
+                for (int pi : g.paths)
+                    for (const Nonzero &z : P.paths[pi].nz) pair_ij[{P.paths[pi].i1, P.paths[pi].i2}].insert({z.i, z.j});
+                int maxpair = 0;
+                for (auto &kv : pair_ij) maxpair = std::max(maxpair, (int)kv.second.size());
+                // fp64: register pairs and 64-bit address arithmetic measured ~30% above the count
+                est_max = std::max(est_max, (word * (acc + 3 * ops / 2 + maxpair) + 24) * (word == 2 ? 13 : 10) / 10);
+            }
+            return est_max <= 128 ? 1 : est_max <= 256 ? 2 : 4;
+        };
+        P.uvc_rpw = make(65536, P.uvc_groups);
+        if (P.uvc_rpw == 1) {
+            std::vector<Group> wide;
+            if (make(122880, wide) == 1) P.uvc_groups = wide;
         }
     }
 
@@ -450,8 +482,8 @@ void schedule(Plan &P)
     if (const char *e = std::getenv("CGTP_DBL_BWD_WAVES")) P.dbl_bwd_waves_per_eu = std::max(1, std::atoi(e));
     if (const char *e = std::getenv("CGTP_BWD_WAVES")) P.bwd_waves_per_eu = std::max(1, std::atoi(e));
     P.uvw_waves_per_eu = P.dtype == CGTP_F64 ? 1 : 2;
-    P.uvc_waves_per_eu = P.dtype == CGTP_F64 ? 1 : 2;
-    if (const char *e = std::getenv("CGTP_UVC_WAVES")) P.uvc_waves_per_eu = std::max(1, std::atoi(e));
+    if (const char *e = std::getenv("CGTP_UVC_RPW")) P.uvc_rpw = std::atoi(e) >= 4 ? 4 : std::atoi(e) >= 2 ? 2 : 1;
+    P.uvc_waves_per_eu = 4 / P.uvc_rpw;  // the workgroup's 16 / rpw waves spread over 4 SIMDs
     if (const char *e = std::getenv("CGTP_UVW_WAVES")) P.uvw_waves_per_eu = std::max(1, std::atoi(e));
     if (const char *e = std::getenv("CGTP_BWD_SCHED_BARRIER")) P.bwd_sched_barrier = std::atoi(e) != 0;
 }

@@ -140,6 +140,8 @@ class ConvSpec:
     graph: str = "uniform"      # or "powerlaw"
     zipf_a: float = 2.0
     cap: int = 2000
+    mode: str = "uvu"           # "uvw": shared [P][mul_in][mul_out] weights, outputs ``out_irreps``
+    out_irreps: Optional[str] = None
 
 
 @dataclass(frozen=True)
@@ -167,6 +169,13 @@ CONV_STREAM = ConvSpec("conv-N200k-E10M-powerlaw-64x(0e,1o,2e)-sh2", 200_000, 10
                        _ladder(64, 2), 2, 2, graph="powerlaw", zipf_a=2.0, cap=2000)
 
 WORKLOADS = {"c1": TP_SMALL, "c2": CONV_NEQUIP, "c3": CONV_MACE, "c4": TP_HIGHL, "c5": CONV_STREAM}
+
+# The NequIP-like graph and inputs with fully connected multiplicity mixing (uvw, shared
+# weights) into every reachable output irrep at 32 channels (Sobek page, Abstract: the fully
+# connected operator family).
+CONV_NEQUIP_UVW = ConvSpec("conv-uvw-N5000-E200k-32x(0e,1o,2e)-sh2", 5000, 200_000, _ladder(32, 2), 2, 2,
+                           mode="uvw", out_irreps="32x0e+32x1o+32x2e+32x1e+32x2o")
+EXTRA_WORKLOADS = {"c2uvw": CONV_NEQUIP_UVW}
 
 
 def conv_graph(spec: ConvSpec, seed: int = 0):
