@@ -22,7 +22,7 @@ STATUS_CODES = {v: k for k, v in STATUS.items()}
 EXPORTS = ("cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info_get", "cgtp_plan_path",
            "cgtp_plan_path_coefficients", "cgtp_plan_source", "cgtp_tp_forward", "cgtp_conv_forward",
            "cgtp_graph_transpose", "cgtp_conv_backward", "cgtp_spherical_harmonics", "cgtp_last_error",
-           "cgtp_conv_forward_ordered", "cgtp_graph_order", "cgtp_conv_double_backward")
+           "cgtp_conv_forward_ordered", "cgtp_graph_order", "cgtp_conv_double_backward", "cgtp_tp_backward")
 
 
 class CgtpError(RuntimeError):
@@ -217,6 +217,26 @@ def tp_forward(plan: Plan, x, y, w, out=None, stream=None):
                                  _dev(w, "w", dt, wshape), shared, _dev(out, "out", dt, (B, plan.d_out)),
                                  _stream(stream, x.device)))
     return out
+
+
+def tp_backward(plan: Plan, x, y, w, grad_out, grad_x=None, grad_y=None, grad_w=None, need=(True, True, True),
+                stream=None):
+    """Batched product backward (uvu): returns (grad_x, grad_y, grad_w); entries not in ``need`` are None."""
+    import torch
+    B = x.shape[0]
+    dt = plan.torch_dtype
+    dev = x.device
+    shapes = ((B, plan.d_x), (B, plan.d_sh), (B, plan.weight_numel))
+    res = [None if not nd else (torch.empty(sh, dtype=dt, device=dev) if o is None else o)
+           for o, nd, sh in zip((grad_x, grad_y, grad_w), need, shapes)]
+    shared = 1 if plan.mode == "uvw" else 0
+    wshape = (plan.weight_numel,) if shared else shapes[2]
+    _check(lib().cgtp_tp_backward(plan.handle, B, _dev(x, "x", dt, shapes[0]), _dev(y, "y", dt, shapes[1]),
+                                  _dev(w, "w", dt, wshape), shared, _dev(grad_out, "grad_out", dt, (B, plan.d_out)),
+                                  *[_ptr_or_null(r, n, dt, sh) for r, n, sh in zip(res, ("grad_x", "grad_y", "grad_w"),
+                                                                                   shapes)],
+                                  _stream(stream, dev)))
+    return tuple(res)
 
 
 def graph_order(row_ptr, order=None, stream=None):

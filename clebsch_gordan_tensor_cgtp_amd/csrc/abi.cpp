@@ -262,6 +262,48 @@ cgtp_status cgtp_conv_forward(const cgtp_plan *plan, int64_t N, int64_t E, const
     return cgtp_conv_forward_ordered(plan, N, E, row_ptr, col, nullptr, x, y, w, out, stream);
 }
 
+cgtp_status cgtp_tp_backward(const cgtp_plan *plan, int64_t B, const void *x, const void *y, const void *w,
+                             int shared_weights, const void *grad_out, void *grad_x, void *grad_y, void *grad_w,
+                             void *stream)
+{
+    return guarded([&] {
+        require(plan != nullptr, "plan is NULL");
+        cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
+        require(B >= 0 && B < INT_MAX, "B must be in [0, 2^31-1)");
+        if (P.mode == CGTP_UVU)
+            require(shared_weights == 0, "uvu takes per-row weights: shared_weights must be 0");
+        else
+            throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw batched backward is not built yet");
+        if (B == 0 || (!grad_x && !grad_y && !grad_w)) return;
+        const size_t es = elem(P);
+        require_ptr(x, "x", es);
+        require_ptr(y, "y", es);
+        require_ptr(w, "w", es);
+        require_ptr(grad_out, "grad_out", es);
+        if (grad_x) require_ptr(grad_x, "grad_x", es);
+        if (grad_y) require_ptr(grad_y, "grad_y", es);
+        if (grad_w) require_ptr(grad_w, "grad_w", es);
+        const void *ins[] = {x, y, w, grad_out};
+        const size_t inn[] = {B * P.d_x * es, B * P.d_sh * es, B * P.w_numel * es, B * P.d_out * es};
+        const char *inm[] = {"x", "y", "w", "grad_out"};
+        void *outs[] = {grad_x, grad_y, grad_w};
+        const size_t outn[] = {B * P.d_x * es, B * P.d_sh * es, B * P.w_numel * es};
+        const char *outm[] = {"grad_x", "grad_y", "grad_w"};
+        for (int a = 0; a < 3; ++a) {
+            for (int b = 0; b < 4; ++b) require_disjoint(outs[a], outn[a], outm[a], ins[b], inn[b], inm[b]);
+            for (int b = a + 1; b < 3; ++b) require_disjoint(outs[a], outn[a], outm[a], outs[b], outn[b], outm[b]);
+        }
+        const auto &L = cgtp::module_for_current_device(P);
+        long nrows = (long)B;
+        // one launch per path group, in order (later groups add to blocks an earlier one wrote)
+        for (int grp = 0; grp < (int)P.bwd_groups.size(); ++grp) {
+            long nblocks = (long)((B + P.bwd_groups[grp].es - 1) / P.bwd_groups[grp].es);
+            void *args[] = {&x, &y, &w, &grad_out, &grad_x, &grad_y, &grad_w, &nrows, &nblocks, &grp};
+            launch(L.tp_bwd, nblocks, args, stream);
+        }
+    });
+}
+
 cgtp_status cgtp_graph_order(int64_t N, const int32_t *row_ptr, int32_t *order, void *stream)
 {
     return guarded([&] {

@@ -454,12 +454,12 @@ void emit_slot_sum(Out &o, const Plan &P)
 // and dY blocks are written by the first group that touches them (group 0 also
 // writes zeros for blocks no path touches) and accumulated by later groups;
 // the groups are separate launches in group order, so the sums are fixed.
-void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false)
+void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmode = false)
 {
     const std::vector<Group> &groups = dbl ? P.dbl_groups : P.bwd_groups;
     const Group &g = groups[gi];
     const bool f64 = P.dtype == CGTP_F64;
-    const bool pf = g.prefetch;
+    const bool pf = g.prefetch && !rowmode;
     Touch t = touched(P, g.paths);
     // first group (in launch order) touching each input / SH block
     auto first_i1 = [&](int b) {
@@ -483,6 +483,19 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false)
     for (int b = 0; b < (int)P.sh.size(); ++b)
         if (t.i2.count(b) || (gi == 0 && first_i2(b) < 0)) yb.push_back(b);
 
+    if (rowmode) {
+        // batched rows: edge slot = row; the row is its own sender, edge and receiver
+        o("__device__ __forceinline__ void tpb_g", gi,
+          "(long blk, int lane, const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, "
+          "const T* __restrict__ g, T* __restrict__ dx, T* __restrict__ dy, T* __restrict__ dw, long nrows)");
+        o("{");
+        o.ind++;
+        o("const int slot = lane >> ", log2i(g.ct), ";");
+        o("const int ul = lane & ", g.ct - 1, ";");
+        o("const long row = blk * ", g.es, " + slot;");
+        o("const bool live = row < nrows;");
+        o("const long s = live ? row : nrows - 1;  // rows past the end read row nrows-1 and store nothing");
+    } else {
     o("__device__ __forceinline__ void ", dbl ? "dbs" : "bwd", "_g", gi,
       "(long s, int wv, int lane, int wpr, T* red, const int* __restrict__ t_row_ptr, const int* __restrict__ t_edge, "
       "const int* __restrict__ t_dst, const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, "
@@ -495,6 +508,7 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false)
     o("const int ul = lane & ", g.ct - 1, ";");
     o("const int t0 = t_row_ptr[s], t1 = t_row_ptr[s + 1];");
     o("const int stride = ", g.es, " * wpr;");
+    }
     o("for (int tile = 0; tile < ", g.tiles, "; ++tile) {");
     o.ind++;
     o("const int u = tile * ", g.ct, " + ul;");
@@ -568,6 +582,14 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false)
     };
     // pipeline: edge and receiver ids two iterations ahead, operands one ahead
     // (with prefetch) so every wait is for loads issued an iteration earlier
+    if (rowmode) {
+        o("{");
+        o.ind++;
+        o("{");
+        o.ind++;
+        o("const long e = s, n = s;");
+        edge_loads("", "e", "n", true);
+    } else {
     o("int t = t0 + wv * ", g.es, " + slot;");
     o("if (t < t1) {");
     o.ind++;
@@ -583,6 +605,7 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false)
         edge_loads("n", "en", "nn", true);
     else
         edge_loads("", "e", "n", true);
+    }
     for (int b : yb)
         for (int j = 0; j < n_of(P.sh[b].l); ++j) o("T h", b, "_", j, " = (T)0;");  // dF/dy partial of this lane
     for (int pi : g.paths) {
@@ -655,6 +678,7 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false)
                 }
             }
             std::string guard = needs_mask(p.mul_in, g) ? "(u < " + std::to_string(p.mul_in) + ") && " : "";
+            if (rowmode) guard = "live && " + guard;
             o("if (", guard, "dw) ST_STREAM(", e.str(), ", &dw[(size_t)e * WROW + ", p.w_off, " + u]);");
         }
         if (dbl) {
@@ -706,7 +730,7 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false)
             o("T v = (T)0;");
             o("int col = -1;");
             for (auto &sc : sel) o("if (ul == ", sc.first, ") { v = ", hs[lo + sc.first].second, "; col = ", sc.second, "; }");
-            o("if (col >= 0) {");
+            o(rowmode ? "if (live && col >= 0) {" : "if (col >= 0) {");
             o.ind++;
             o("T* p = &dy[(size_t)e * DSH + col];");
             if (add)
@@ -734,6 +758,12 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false)
             for (int pi : g.paths) o("gw", pi, " = ngw", pi, ";");
         }
     }
+    if (rowmode) {
+        o.ind--;
+        o("}");
+        o.ind--;
+        o("}");
+    } else {
     o("e = en;");
     o("n = nn;");
     o("en = enn;");
@@ -743,6 +773,11 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false)
     o("}");  // edge loop
     o.ind--;
     o("}");  // t < t1
+    }
+    if (rowmode) {
+        // each slot is its own row: no sum over slots or waves
+        o("if (dx && live) {");
+    } else {
     // sum the edge slots of the wave, then the waves of the workgroup (fixed order)
     for (int m = 32; m >= g.ct; m /= 2)
         for (int b : xb)
@@ -778,6 +813,7 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false)
     o.ind--;
     o("}");
     o("if (dx && wv == 0 && slot == 0) {");
+    }
     o.ind++;
     for (int b : xb) {
         const Irrep &ir = P.ins[b];
@@ -807,6 +843,31 @@ int bwd_red_size(const std::vector<Group> &groups, const Plan &P)
         m = std::max(m, 3 * nx * g.ct);
     }
     return m;
+}
+
+// Batched backward (use case A): rows-mode groups of the sender pass; one wave
+// covers es rows, one launch per group (later groups add to dx / dY blocks an
+// earlier group wrote), so every sum has a fixed order.
+void emit_tpb_kernel(Out &o, const Plan &P)
+{
+    for (int gi = 0; gi < (int)P.bwd_groups.size(); ++gi) emit_bwd_group(o, P, gi, false, true);
+    o("extern \"C\" __global__ void __launch_bounds__(256, ", P.bwd_waves_per_eu,
+      ") cgtp_tp_bwd(const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, "
+      "const T* __restrict__ g, T* __restrict__ dx, T* __restrict__ dy, T* __restrict__ dw, long nrows, long nblocks, "
+      "int group)");
+    o("{");
+    o.ind++;
+    o("const long blk = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const int lane = threadIdx.x & 63;");
+    o("if (blk >= nblocks) return;");
+    o("switch (group) {");
+    for (int gi = 0; gi < (int)P.bwd_groups.size(); ++gi)
+        o("case ", gi, ": tpb_g", gi, "(blk, lane, x, y, w, g, dx, dy, dw, nrows); break;");
+    o("default: break;");
+    o("}");
+    o.ind--;
+    o("}");
+    o("");
 }
 
 // Sender-pass kernel: the backward (dbl = false) or the double backward's
@@ -1285,6 +1346,8 @@ std::string generate_source(const Plan &P)
         emit_fwd_kernel(o, P, true);
         o("// @@section cgtp_conv_bwd");
         emit_bwd_kernel(o, P);
+        o("// @@section cgtp_tp_bwd");
+        emit_tpb_kernel(o, P);
         o("// @@section cgtp_conv_dbwd_recv");
         for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi) emit_fwd_group(o, P, gi, false, true);
         emit_fwd_kernel(o, P, false, true);

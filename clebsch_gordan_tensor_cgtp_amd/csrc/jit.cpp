@@ -122,6 +122,7 @@ const Plan::Loaded &module_for_current_device(Plan &P)
         check(hipModuleGetFunction(&L.tp_fwd, L.module, "cgtp_tp_fwd"), "hipModuleGetFunction(tp_fwd)");
         check(hipModuleGetFunction(&L.dbwd_recv, L.module, "cgtp_conv_dbwd_recv"), "hipModuleGetFunction(dbwd_recv)");
         check(hipModuleGetFunction(&L.dbwd_send, L.module, "cgtp_conv_dbwd_send"), "hipModuleGetFunction(dbwd_send)");
+        check(hipModuleGetFunction(&L.tp_bwd, L.module, "cgtp_tp_bwd"), "hipModuleGetFunction(tp_bwd)");
     } else {
         check(hipModuleGetFunction(&L.tp_uvw, L.module, "cgtp_tp_uvw"), "hipModuleGetFunction(tp_uvw)");
         check(hipModuleGetFunction(&L.conv_uvw, L.module, "cgtp_conv_uvw"), "hipModuleGetFunction(conv_uvw)");

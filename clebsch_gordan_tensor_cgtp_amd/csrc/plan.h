@@ -83,7 +83,7 @@ struct Plan {
     struct Loaded {
         hipModule_t module = nullptr;
         hipFunction_t conv_fwd = nullptr, conv_bwd = nullptr, tp_fwd = nullptr, tp_uvw = nullptr;
-        hipFunction_t dbwd_recv = nullptr, dbwd_send = nullptr, conv_uvw = nullptr;
+        hipFunction_t dbwd_recv = nullptr, dbwd_send = nullptr, conv_uvw = nullptr, tp_bwd = nullptr;
     };
     std::map<int, Loaded> loaded;
 };

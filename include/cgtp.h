@@ -119,11 +119,28 @@ const char *cgtp_plan_source(const cgtp_plan *plan);
  *                                   sum_{i,j} C[i,j,k] x[b, a + u(2l1+1) + i] y[b, b_p + j]
  *        w is [B][weight_numel], shared_weights must be 0;
  *   uvw: out[b, o + v(2l3+1) + k] = sum_paths sum_u W_p[u][v] * (same contraction)
- *        w is the shared [weight_numel] block, shared_weights must be 1.
+ *        w is the shared [weight_numel] block, shared_weights must be 1; every
+ *        output multiplicity must be <= 16 (one MFMA tile), else
+ *        CGTP_ERR_UNSUPPORTED.
  * x [B][d_x], y [B][d_sh], out [B][d_out] (overwritten).  B = 0 is a no-op.
  */
 cgtp_status cgtp_tp_forward(const cgtp_plan *plan, int64_t B, const void *x, const void *y,
                             const void *w, int shared_weights, void *out, void *stream);
+
+/*
+ * Batched tensor product backward, use case A (sciencestack.ai page, Abstract:
+ * gradient kernels; Figure 4A): with g = grad_out [B][d_out], per row b
+ *   grad_w[b, w_p + u] = sum_{ijk} C x[b,u,i] y[b,j] g[b,u,k]
+ *   grad_y[b, b_p + j] = sum_p sum_u W[b,p,u] sum_{ik} C x[b,u,i] g[b,u,k]
+ *   grad_x[b, a_p + u(2l1+1) + i] = sum_p W[b,p,u] sum_{jk} C y[b,j] g[b,u,k]
+ * (the convolution backward with every row its own sender and receiver).
+ * uvu only (shared_weights must be 0); uvw returns CGTP_ERR_UNSUPPORTED.  Any
+ * of grad_x / grad_y / grad_w may be NULL to skip it; outputs are overwritten,
+ * one owner per element, no atomics, bitwise deterministic.  B = 0 is a no-op.
+ */
+cgtp_status cgtp_tp_backward(const cgtp_plan *plan, int64_t B, const void *x, const void *y, const void *w,
+                             int shared_weights, const void *grad_out, void *grad_x, void *grad_y, void *grad_w,
+                             void *stream);
 
 /*
  * Fused convolution forward, use case B (sciencestack.ai page, Figure 4B;
@@ -133,8 +150,10 @@ cgtp_status cgtp_tp_forward(const cgtp_plan *plan, int64_t B, const void *x, con
  * non-decreasing, row_ptr[N] = E, 0 <= col < N); y [E][d_sh] and w
  * [E][weight_numel] are in CSR edge order; x [N][d_x]; out [N][d_out] is
  * overwritten, receivers without edges get zeros.  One owner per output row:
- * no atomics, bitwise deterministic.  uvu plans only (uvw returns
- * CGTP_ERR_UNSUPPORTED).
+ * no atomics, bitwise deterministic.  uvw plans (fully connected multiplicity
+ * mixing inside the convolution; Sobek page, Abstract): w is the shared
+ * [weight_numel] block instead, out[n] = sum_e TP_uvw(x[col[e]], y[e], W),
+ * the mixing running on MFMA per tile of 16 receivers.
  */
 cgtp_status cgtp_conv_forward(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
                               const int32_t *col, const void *x, const void *y, const void *w,

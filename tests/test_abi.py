@@ -145,6 +145,11 @@ def test_call_errors_before_any_gpu_work():
     wide = ctypes.c_void_p()
     assert L.cgtp_plan_create(b"16x0e", b"1x0e", b"32x0e", 1, 0, ctypes.byref(wide)) == 0
     assert L.cgtp_tp_forward(wide, 4, fake, fake, fake, 1, ctypes.c_void_p(1 << 26), s) == unsup
+    # batched backward: uvu needs shared=0; the uvw backward is not built
+    assert L.cgtp_tp_backward(plan.handle, 4, fake, fake, fake, 1, fake, fake, fake, fake, s) == inval
+    assert L.cgtp_tp_backward(uvw.handle, 4, fake, fake, fake, 1, fake, fake, fake, fake, s) == unsup
+    assert L.cgtp_tp_backward(plan.handle, 4, fake, fake, fake, 0, null, fake, null, null, s) == inval
+    assert L.cgtp_tp_backward(plan.handle, 0, null, null, null, 0, null, null, null, null, s) == 0
     assert L.cgtp_plan_destroy(wide) == 0
     assert L.cgtp_tp_forward(plan.handle, 4, fake, fake, fake, 1, fake, s) == inval   # uvu needs shared=0
     assert L.cgtp_tp_forward(uvw.handle, 4, fake, fake, fake, 0, fake, s) == inval    # uvw needs shared=1

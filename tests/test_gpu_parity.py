@@ -208,6 +208,37 @@ def test_tp_forward_uvu(device, dtype, in_irreps, lmax, B):
     assert rel_l2(out, want) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("in_irreps,lmax,B", [("4x0e+4x1o", 2, 1024), ("32x0e+32x1o+32x2e", 2, 777),
+                                              ("5x0e+3x1o+7x2e+2x3o", 3, 301), ("128x0e+128x1o+128x2e+128x3o", 3, 97),
+                                              ("80x0e+80x1o", 1, 33)])
+def test_tp_backward_uvu(device, dtype, in_irreps, lmax, B):
+    """Batched backward vs the oracle's convolution backward on the identity graph (row b is its
+    own sender and receiver); optional outputs give the same bits."""
+    import torch
+    out_ir = oirreps.per_path_out_irreps(in_irreps, lmax, lmax)
+    prob = oirreps.build_problem(in_irreps, oirreps.sh_irreps(lmax), out_ir, "uvu")
+    plan = cg.plan_create(in_irreps, oirreps.sh_irreps(lmax), out_ir, "uvu", dtype)
+    st = synth.streams(12)
+    npdt = np.float32 if dtype == "f32" else np.float64
+    x = synth.normal(st["x"], (B, prob.d_in), dtype=npdt)
+    vec = synth.normal(st["vec"], (B, 3), dtype=npdt)
+    w = synth.normal(st["w"], (B, prob.weight_numel), dtype=npdt)
+    g = synth.normal(st["sample"], (B, prob.d_out), dtype=npdt)
+    t = lambda a: torch.from_numpy(a).to(device)
+    y = cg.spherical_harmonics(lmax, t(vec))
+    gx, gy, gw = cg.tp_backward(plan, t(x), y, t(w), t(g))
+    torch.cuda.synchronize()
+    ident = np.arange(B + 1)
+    want = ref.conv_backward(prob, ident, np.arange(B), x, osh.real_sh_all(lmax, vec.astype(np.float64)), w, g)
+    for got, exp in zip((gx, gy, gw), want):
+        assert rel_l2(got.cpu().numpy(), exp) <= TOL[dtype]
+    for k in range(3):
+        part = cg.tp_backward(plan, t(x), y, t(w), t(g), need=tuple(i == k for i in range(3)))
+        torch.cuda.synchronize()
+        assert torch.equal(part[k], (gx, gy, gw)[k])
+
+
 # --------------------------------------------------------------------------- uvw (dense mixing on MFMA)
 
 def _uvw_case(in_irreps, lmax, out_irreps, B, dtype, seed=13):
