@@ -33,7 +33,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c2uvw"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c2uvw", "c1big"])
+    ap.add_argument("--backward", action="store_true", help="batched uvu workloads: also time cgtp_tp_backward")
     ap.add_argument("--dtype", default="f32", choices=["f32", "f64"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seed", type=int, default=0)
@@ -401,47 +402,116 @@ def tp_flops(plan_paths, mul, mode):
     return f
 
 
+def cpu_baseline_tp(spec, plan_paths, seed, max_seconds=30.0):
+    """The oracle's explicit loops (fp64, OpenMP) on a bounded sample of rows of the same batch
+    (random values, timing only): the uvu forward (and backward with ``backward``) or the uvw
+    forward.  Rate = rows per second."""
+    from oracle import irreps as oirreps
+    from oracle import loops
+    out_ir = spec.out_irreps if spec.mode == "uvw" else oirreps.per_path_out_irreps(spec.in_irreps, spec.lmax_sh,
+                                                                                     spec.lmax_sh)
+    prob = oirreps.build_problem(spec.in_irreps, oirreps.sh_irreps(spec.lmax_sh), out_ir, spec.mode)
+    tab = loops.Tables(prob)
+    threads = loops.default_threads()
+    rng = np.random.default_rng(seed + 96)
+    n = max(1, min(spec.batch, 20_000 if spec.mode == "uvu" else 500))
+    x = rng.standard_normal((n, prob.d_in))
+    y = rng.standard_normal((n, prob.d_sh))
+    w = rng.standard_normal(prob.weight_numel if spec.mode == "uvw" else (n, prob.weight_numel))
+    g = rng.standard_normal((n, prob.d_out))
+    ident = np.arange(n + 1)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        if spec.mode == "uvw":
+            loops.uvw_forward(tab, x, y, w, threads)
+        else:
+            loops.uvu_forward(tab, ident, np.arange(n), x, y, w, threads)
+            if plan_paths == "backward":
+                loops.uvu_backward_edges(tab, ident, np.arange(n), x, y, w, g, threads)
+                loops.uvu_backward_x(tab, ident, np.arange(n), y, w, g, threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or el >= max_seconds:
+            break
+    what = "uvw forward" if spec.mode == "uvw" else ("uvu forward + backward" if plan_paths == "backward"
+                                                      else "uvu forward")
+    return {"value": n * reps / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {spec.batch} rows, {what}; fp64 explicit loops, mean of {reps} rep(s)"}
+
+
 def bench_tp(a, spec, device):
-    """Batched tensor product workloads: one step = one cgtp_tp_forward over the batch."""
+    """Batched tensor product workloads: one step = one cgtp_tp_forward over the batch (with
+    --backward, uvu only: cgtp_tp_forward + cgtp_tp_backward)."""
     import torch
     from clebsch_gordan_tensor_cgtp_amd import binding as cg
     from clebsch_gordan_tensor_cgtp_amd import synth
     plan = cg.plan_for(spec, a.dtype)
     st = synth.streams(a.seed)
     npdt = np.float32 if a.dtype == "f32" else np.float64
+    es = 4 if a.dtype == "f32" else 8
     B = spec.batch
+    backward = a.backward and spec.mode == "uvu"
     x = torch.from_numpy(synth.normal(st["x"], (B, plan.d_x), dtype=npdt)).to(device)
     vec = torch.from_numpy(synth.normal(st["vec"], (B, 3), dtype=npdt)).to(device)
     wshape = (plan.weight_numel,) if spec.mode == "uvw" else (B, plan.weight_numel)
     w = torch.from_numpy(synth.normal(st["w"], wshape, 0.25, dtype=npdt)).to(device)
+    g = torch.from_numpy(synth.normal(st["sample"], (B, plan.d_out), dtype=npdt)).to(device) if backward else None
     y = cg.spherical_harmonics(spec.lmax_sh, vec)
     out = torch.empty((B, plan.d_out), dtype=plan.torch_dtype, device=device)
+    grads = (torch.empty_like(x), torch.empty_like(y), torch.empty_like(w)) if backward else None
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        cg.tp_forward(plan, x, y, w, out=out)
+        if ev is not None:
+            ev[1].record()
+        if backward:
+            cg.tp_backward(plan, x, y, w, g, *grads)
+        if ev is not None:
+            ev[2].record()
+
     for _ in range(a.warmup):
-        cg.tp_forward(plan, x, y, w, out=out)
+        step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
     t0 = time.perf_counter()
-    e0.record()
-    for _ in range(a.steps):
-        cg.tp_forward(plan, x, y, w, out=out)
-    e1.record()
+    for k in range(a.steps):
+        step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / a.steps
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) if backward else 0.0
     paths = [plan.path(p) for p in range(plan.num_paths)]
-    flops = tp_flops(paths, None, spec.mode) * B
-    peak = 157.3 if a.dtype == "f32" else 78.6
-    achieved = flops / (ms * 1e-3) / 1e12
+    config = {"workload": spec.name, "B": B, "in_irreps": spec.in_irreps, "mode": spec.mode,
+              "paths": plan.num_paths, "nnz": plan.nnz_total, "fwd_ms": fwd_ms,
+              "step": "tp_forward + tp_backward" if backward else "tp_forward"}
+    if spec.mode == "uvw":
+        flops = tp_flops(paths, None, spec.mode) * B
+        peak = 157.3 if a.dtype == "f32" else 78.6
+        achieved = flops / (fwd_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "cgtp_tp_uvw", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None, "flops_per_launch": flops, "avg_launch_ms": fwd_ms}
+    else:
+        # uvu is HBM-bound: every row reads x, y, W once and writes out once (backward: reads
+        # x, y, W, grad_out, writes grad_x, grad_y, grad_w)
+        fwd_b = B * es * (plan.d_x + plan.d_sh + plan.weight_numel + plan.d_out)
+        bwd_b = B * es * (2 * plan.d_x + 2 * plan.d_sh + 2 * plan.weight_numel + plan.d_out)
+        dom = ("cgtp_tp_bwd", bwd_ms, bwd_b) if backward and bwd_ms >= fwd_ms else ("cgtp_tp_fwd", fwd_ms, fwd_b)
+        achieved = dom[2] / (dom[1] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": dom[0], "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(plan, spec, a.dtype, dom[0]),
+                "algorithmic_bytes_per_launch": dom[2], "avg_launch_ms": dom[1]}
+        if backward:
+            config["bwd_ms"] = bwd_ms
     line = {"metric": "rows/sec batched CGTP forward and % of FP32 roofline", "value": B / (wall / a.steps),
             "unit": "rows/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
             "ms_per_step": wall * 1e3 / a.steps, "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": a.dtype, "data": "synthetic",
-            "config": {"workload": spec.name, "B": B, "in_irreps": spec.in_irreps, "mode": spec.mode,
-                       "paths": plan.num_paths, "nnz": plan.nnz_total, "kernel_ms": ms},
-            "roofline": {"bound": "mfma" if spec.mode == "uvw" else "hbm", "kernel": "cgtp_tp_forward",
-                         "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                         "traffic": None, "flops_per_launch": flops, "avg_launch_ms": ms},
+            "vs_baseline": None, "dtype": a.dtype, "data": "synthetic", "config": config, "roofline": roof,
             "cpu_baseline": None}
+    if not a.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_tp(spec, "backward" if backward else None, a.seed)
     print(json.dumps(line), flush=True)
 
 

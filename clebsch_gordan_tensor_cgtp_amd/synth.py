@@ -175,7 +175,10 @@ WORKLOADS = {"c1": TP_SMALL, "c2": CONV_NEQUIP, "c3": CONV_MACE, "c4": TP_HIGHL,
 # connected operator family).
 CONV_NEQUIP_UVW = ConvSpec("conv-uvw-N5000-E200k-32x(0e,1o,2e)-sh2", 5000, 200_000, _ladder(32, 2), 2, 2,
                            mode="uvw", out_irreps="32x0e+32x1o+32x2e+32x1e+32x2o")
-EXTRA_WORKLOADS = {"c2uvw": CONV_NEQUIP_UVW}
+# A batched uvu product over as many rows as the streaming graph has nodes, with the NequIP-like
+# irreps (HBM-bound, unlike the 1,024-row batch that is launch-bound).
+TP_BIG = TPSpec("tp-uvu-B200k-32x(0e,1o,2e)-sh2", 200_000, _ladder(32, 2), 2, "uvu")
+EXTRA_WORKLOADS = {"c2uvw": CONV_NEQUIP_UVW, "c1big": TP_BIG}
 
 
 def conv_graph(spec: ConvSpec, seed: int = 0):
