@@ -235,3 +235,17 @@ def conv_forward_uvw_rows(tab: Tables, row_ptr, col, x, y, w, rows, n_threads=No
     seg = np.repeat(np.arange(len(rows)), deg)
     np.add.at(out, seg, msg)
     return out
+
+
+def conv_forward_radial_rows(tab: Tables, row_ptr, col, x, y, rho, theta, rows, n_threads=None) -> np.ndarray:
+    """Radial-projection convolution output of the receivers ``rows``: W_e = rho[e] @ Theta formed
+    for their edges only (a library matmul), then the explicit uvu loops."""
+    row_ptr = np.asarray(row_ptr, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    deg = row_ptr[rows + 1] - row_ptr[rows]
+    sub_ptr = np.concatenate([[0], np.cumsum(deg)])
+    eidx = np.concatenate([np.arange(row_ptr[r], row_ptr[r + 1]) for r in rows]) if len(rows) else \
+        np.zeros(0, np.int64)
+    w = np.asarray(rho, np.float64)[eidx] @ np.asarray(theta, np.float64)
+    return uvu_forward(tab, sub_ptr, np.asarray(col)[eidx], np.asarray(x, np.float64),
+                       np.asarray(y, np.float64)[eidx], w, n_threads)

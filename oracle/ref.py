@@ -187,3 +187,14 @@ def conv_double_backward(prob: Problem, row_ptr, col, x, y, w, g, ggx, ggy, ggw)
     dg = np.zeros_like(g)
     np.add.at(dg, dst, dgs)
     return dx, dy, dw, dg
+
+
+def conv_forward_radial(prob: Problem, row_ptr, col, x, y, rho, theta):
+    """Convolution whose per-edge weights are a radial projection: W_e = rho[e] @ Theta.
+
+    Source: Sobek page, Abstract (edge-conditioned weights from a radial projection, which the
+    streaming formulation reassociates with the coupling and the aggregation so that W_e is
+    never stored).  rho [E][R] holds each edge's radial features, Theta [R][weight_numel] is
+    shared.  The plain definition: form W = rho @ Theta, then the uvu convolution."""
+    w = np.asarray(rho, np.float64) @ np.asarray(theta, np.float64)
+    return conv_forward(prob, row_ptr, col, x, y, w)

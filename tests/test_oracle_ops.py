@@ -447,3 +447,43 @@ def test_cpu_loops_uvw_conv_match_numpy(in_f32):
     rows = np.array([5, 0, 8, 3])
     got = loops.conv_forward_uvw_rows(loops.Tables(prob), row_ptr, col, x, y, w, rows)
     assert np.allclose(got, want[rows], atol=1e-12)
+
+
+
+# ------------------------------------------------------------------------------ radial projection
+
+def test_radial_conv_brute_force_and_linearity():
+    """W_e = rho_e Theta: equals the dense einsum with that W, is linear in Theta, and a rho that is
+    one-hot on radial channel r selects Theta's row r as every edge's weights."""
+    prob = problem("3x0e+3x1o+3x2e", 2, 2)
+    rng = np.random.default_rng(20)
+    row_ptr, col, x, vec, w, g = conv_inputs(prob, rng, 7, 29)
+    y = rng.standard_normal((29, prob.d_sh))
+    rho = rng.standard_normal((29, 5))
+    theta = rng.standard_normal((5, prob.weight_numel))
+    got = ref.conv_forward_radial(prob, row_ptr, col, x, y, rho, theta)
+    t = dense_tensor(prob)
+    msg = np.einsum("abvo,ea,eb,er,rv->eo", t, x[col], y, rho, theta)
+    want = np.zeros((7, prob.d_out))
+    np.add.at(want, ref.receivers_of(row_ptr), msg)
+    assert np.allclose(got, want, atol=1e-12)
+    theta2 = rng.standard_normal(theta.shape)
+    both = ref.conv_forward_radial(prob, row_ptr, col, x, y, rho, theta + 2.0 * theta2)
+    assert np.allclose(both, got + 2.0 * ref.conv_forward_radial(prob, row_ptr, col, x, y, rho, theta2), atol=1e-11)
+    onehot = np.zeros_like(rho)
+    onehot[:, 3] = 1.0
+    assert np.allclose(ref.conv_forward_radial(prob, row_ptr, col, x, y, onehot, theta),
+                       ref.conv_forward(prob, row_ptr, col, x, y, np.tile(theta[3], (29, 1))), atol=1e-12)
+
+
+def test_cpu_loops_radial_match_numpy():
+    prob = problem()
+    rng = np.random.default_rng(21)
+    row_ptr, col, x, vec, w, g = conv_inputs(prob, rng, 9, 41)
+    y = rng.standard_normal((41, prob.d_sh))
+    rho = rng.standard_normal((41, 8))
+    theta = rng.standard_normal((8, prob.weight_numel))
+    rows = np.array([2, 8, 0, 5])
+    want = ref.conv_forward_radial(prob, row_ptr, col, x, y, rho, theta)[rows]
+    got = loops.conv_forward_radial_rows(loops.Tables(prob), row_ptr, col, x, y, rho, theta, rows)
+    assert np.allclose(got, want, atol=1e-12)
