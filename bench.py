@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--natural-order", action="store_true",
                     help="start receivers in node order instead of the heavy-first schedule")
+    ap.add_argument("--radial", type=int, default=0, metavar="R",
+                    help="time the forward with radially projected weights W_e = rho_e Theta (R features per edge)")
     ap.add_argument("--double-backward", action="store_true",
                     help="time the convolution double backward (both passes) instead of forward + backward")
     ap.add_argument("--copy-probe", action="store_true",
@@ -274,6 +276,97 @@ def bench_conv_uvw(a, spec, plan, d, host_graph, device):
     }
     if not a.no_cpu:
         line["cpu_baseline"] = cpu_baseline_uvw_conv(None, spec, a.seed, host_graph)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_radial(spec, seed, host_graph, R, max_seconds=30.0):
+    """The oracle (W = rho @ Theta for the slice's edges, then the explicit uvu loops) on a
+    contiguous receiver slice with ~5% of the edges; random values.  Rate = slice edges/s."""
+    from oracle import irreps as oirreps
+    from oracle import loops
+    row_ptr, col = (np.asarray(a, dtype=np.int64) for a in host_graph)
+    N, E = len(row_ptr) - 1, len(col)
+    out_ir = oirreps.per_path_out_irreps(spec.in_irreps, spec.lmax_sh, spec.lmax_out)
+    prob = oirreps.build_problem(spec.in_irreps, oirreps.sh_irreps(spec.lmax_sh), out_ir, "uvu")
+    tab = loops.Tables(prob)
+    threads = loops.default_threads()
+    rng = np.random.default_rng(seed + 95)
+    target = max(2_000, E // 20)
+    start = int(rng.integers(0, max(1, N // 2)))
+    stop = min(max(int(np.searchsorted(row_ptr, row_ptr[start] + target)), start + 1), N)
+    e0, e1 = int(row_ptr[start]), int(row_ptr[stop])
+    sub_ptr = row_ptr[start:stop + 1] - e0
+    uniq, inv = np.unique(col[e0:e1], return_inverse=True)
+    x = rng.standard_normal((len(uniq), prob.d_in))
+    y = rng.standard_normal((e1 - e0, prob.d_sh))
+    rho = rng.standard_normal((e1 - e0, R))
+    theta = rng.standard_normal((R, prob.weight_numel))
+    rows = np.arange(stop - start)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        loops.conv_forward_radial_rows(tab, sub_ptr, inv, x, y, rho, theta, rows, threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or el >= max_seconds:
+            break
+    return {"value": (e1 - e0) * reps / el, "unit": "edges/s", "cores": threads, "kind": "oracle",
+            "sample": f"receivers [{start},{stop}) = {e1 - e0} of {E} edges, R = {R}: W = rho @ Theta for those "
+                      f"edges, then the fp64 explicit loops; mean of {reps} rep(s)"}
+
+
+def bench_radial(a, spec, plan, d, host_graph, device):
+    import torch
+    from clebsch_gordan_tensor_cgtp_amd import binding as cg
+    from clebsch_gordan_tensor_cgtp_amd import synth
+    R = a.radial
+    N, E = d["row_ptr"].shape[0] - 1, d["col"].shape[0]
+    es = 4 if a.dtype == "f32" else 8
+    npdt = np.float32 if a.dtype == "f32" else np.float64
+    up = synth.upstream_streams(a.seed)
+    rho = synth.normal(up["gg_y"], (E, R), dtype=npdt, device=device)
+    theta = synth.normal(up["gg_w"], (R, plan.weight_numel), 1.0 / np.sqrt(R * E / N), dtype=npdt)
+    rho = torch.from_numpy(rho).to(device) if isinstance(rho, np.ndarray) else rho
+    theta = torch.from_numpy(theta).to(device)
+    y = cg.spherical_harmonics(spec.lmax_sh, d["vec"])
+    order = cg.graph_order(d["row_ptr"]) if not a.natural_order else None
+    out = torch.empty((N, plan.d_out), dtype=plan.torch_dtype, device=device)
+    plan.radial_source(R)  # JIT outside the timed region
+
+    def timed(fn):
+        for _ in range(a.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(a.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / a.steps, (time.perf_counter() - t0) / a.steps
+
+    ms, wall = timed(lambda: cg.conv_forward_radial(plan, d["row_ptr"], d["col"], d["x"], y, rho, theta, out=out,
+                                                     order=order))
+    ms_w, _ = timed(lambda: cg.conv_forward(plan, d["row_ptr"], d["col"], d["x"], y, d["w"], out=out, order=order))
+    alg = (N + 1) * 4 + E * 4 + es * (N * plan.d_x + E * plan.d_sh + E * R + R * plan.weight_numel + N * plan.d_out)
+    achieved = alg / (ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC, "value": E / wall, "unit": "edges/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": wall * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": a.dtype, "data": "synthetic",
+        "config": {"workload": spec.name, "N": N, "E": E, "in_irreps": spec.in_irreps, "sh_lmax": spec.lmax_sh,
+                   "paths": plan.num_paths, "d_out": plan.d_out, "radial_features": R,
+                   "step": "conv_forward_radial (W_e = rho_e Theta rebuilt in registers, never stored)",
+                   "receiver_schedule": "natural" if a.natural_order else "heavy-first", "fwd_ms": ms,
+                   "materialised_weights_fwd_ms": ms_w},
+        "roofline": {"bound": "hbm", "kernel": "cgtp_conv_fwd_radial", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": alg, "avg_launch_ms": ms},
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_radial(spec, a.seed, host_graph, R)
     print(json.dumps(line), flush=True)
 
 
@@ -534,6 +627,8 @@ def main():
     plan, d, host_graph = make_inputs(spec, a.dtype, a.seed, device)
     if spec.mode == "uvw":
         return bench_conv_uvw(a, spec, plan, d, host_graph, device)
+    if a.radial:
+        return bench_radial(a, spec, plan, d, host_graph, device)
     if a.double_backward:
         return bench_double_backward(a, spec, plan, d, host_graph, device)
     N, E = d["row_ptr"].shape[0] - 1, d["col"].shape[0]

@@ -22,7 +22,8 @@ STATUS_CODES = {v: k for k, v in STATUS.items()}
 EXPORTS = ("cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info_get", "cgtp_plan_path",
            "cgtp_plan_path_coefficients", "cgtp_plan_source", "cgtp_tp_forward", "cgtp_conv_forward",
            "cgtp_graph_transpose", "cgtp_conv_backward", "cgtp_spherical_harmonics", "cgtp_last_error",
-           "cgtp_conv_forward_ordered", "cgtp_graph_order", "cgtp_conv_double_backward", "cgtp_tp_backward")
+           "cgtp_conv_forward_ordered", "cgtp_graph_order", "cgtp_conv_double_backward", "cgtp_tp_backward",
+           "cgtp_conv_forward_radial", "cgtp_plan_radial_prepare", "cgtp_plan_radial_source")
 
 
 class CgtpError(RuntimeError):
@@ -57,6 +58,7 @@ def lib():
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
         L.cgtp_last_error.restype = ctypes.c_char_p
         L.cgtp_plan_source.restype = ctypes.c_char_p
+        L.cgtp_plan_radial_source.restype = ctypes.c_char_p
         L.cgtp_plan_source.argtypes = [vp]
         L.cgtp_plan_create.argtypes = [ctypes.c_char_p] * 3 + [ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp)]
         L.cgtp_plan_destroy.argtypes = [vp]
@@ -71,7 +73,7 @@ def lib():
         L.cgtp_conv_backward.argtypes = [vp, i64, i64] + [vp] * 13
         L.cgtp_spherical_harmonics.argtypes = [i32, ctypes.c_int, i64, vp, vp, vp]
         for name in EXPORTS:
-            if name not in ("cgtp_last_error", "cgtp_plan_source"):
+            if name not in ("cgtp_last_error", "cgtp_plan_source", "cgtp_plan_radial_source"):
                 getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -132,6 +134,11 @@ class Plan:
     @property
     def source(self) -> str:
         return lib().cgtp_plan_source(self._h).decode()
+
+    def radial_source(self, R: int) -> str:
+        """Generate and compile the radial-projection module for R (host only); its source."""
+        _check(lib().cgtp_plan_radial_prepare(self._h, R))
+        return lib().cgtp_plan_radial_source(self._h, R).decode()
 
     def close(self):
         if self._h is not None and _lib is not None:
@@ -261,6 +268,22 @@ def conv_forward(plan: Plan, row_ptr, col, x, y, w, out=None, order=None, stream
                                    _dev(x, "x", dt, (N, plan.d_x)),
                                    _dev(y, "y", dt, (E, plan.d_sh)), _dev(w, "w", dt, wshape),
                                    _dev(out, "out", dt, (N, plan.d_out)), _stream(stream, x.device)))
+    return out
+
+
+def conv_forward_radial(plan: Plan, row_ptr, col, x, y, rho, theta, out=None, order=None, stream=None):
+    """Convolution with W_e = rho[e] @ theta built in the kernel (rho [E][R], theta [R][weight_numel])."""
+    import torch
+    N, E = row_ptr.shape[0] - 1, col.shape[0]
+    R = theta.shape[0]
+    dt = plan.torch_dtype
+    if out is None:
+        out = torch.empty((N, plan.d_out), dtype=dt, device=x.device)
+    _check(lib().cgtp_conv_forward_radial(plan.handle, N, E, _dev(row_ptr, "row_ptr", torch.int32),
+                                          _dev(col, "col", torch.int32), _ptr_or_null(order, "order", torch.int32, (N,)),
+                                          _dev(x, "x", dt, (N, plan.d_x)), _dev(y, "y", dt, (E, plan.d_sh)), R,
+                                          _dev(rho, "rho", dt, (E, R)), _dev(theta, "theta", dt, (R, plan.weight_numel)),
+                                          _dev(out, "out", dt, (N, plan.d_out)), _stream(stream, x.device)))
     return out
 
 

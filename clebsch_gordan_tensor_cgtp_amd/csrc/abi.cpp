@@ -366,6 +366,68 @@ cgtp_status cgtp_conv_forward_ordered(const cgtp_plan *plan, int64_t N, int64_t 
     });
 }
 
+cgtp_status cgtp_plan_radial_prepare(const cgtp_plan *plan, int32_t R)
+{
+    return guarded([&] {
+        require(plan != nullptr, "plan is NULL");
+        cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
+        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "the radial projection takes uvu plans");
+        require(R >= 1 && R <= 64, "R (radial features per edge) must be in [1, 64]");
+        if ((size_t)R * P.w_numel * elem(P) > 65536)
+            throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "R * weight_numel must fit 64 KB of LDS (Theta is staged there)");
+        cgtp::prepare_radial(P, R);
+    });
+}
+
+const char *cgtp_plan_radial_source(const cgtp_plan *plan, int32_t R)
+{
+    if (!plan) return nullptr;
+    cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
+    std::lock_guard<std::mutex> lock(P.mu);
+    auto it = P.radial.find(R);
+    return it == P.radial.end() ? nullptr : it->second.source.c_str();
+}
+
+cgtp_status cgtp_conv_forward_radial(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
+                                     const int32_t *col, const int32_t *order, const void *x, const void *y, int32_t R,
+                                     const void *rho, const void *theta, void *out, void *stream)
+{
+    return guarded([&] {
+        require(plan != nullptr, "plan is NULL");
+        cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
+        check_graph_sizes(N, E);
+        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "the radial projection takes uvu plans");
+        require(R >= 1 && R <= 64, "R (radial features per edge) must be in [1, 64]");
+        const size_t es = elem(P);
+        if ((size_t)R * P.w_numel * es > 65536)
+            throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "R * weight_numel must fit 64 KB of LDS (Theta is staged there)");
+        if (N == 0) return;
+        require_ptr(row_ptr, "row_ptr", 4);
+        require_ptr(out, "out", es);
+        require_ptr(theta, "theta", es);
+        if (E > 0) {
+            require_ptr(col, "col", 4);
+            require_ptr(x, "x", es);
+            require_ptr(y, "y", es);
+            require_ptr(rho, "rho", es);
+        }
+        if (order) require_ptr(order, "order", 4);
+        const size_t no = N * P.d_out * es;
+        require_disjoint(out, no, "out", x, N * P.d_x * es, "x");
+        require_disjoint(out, no, "out", y, E * P.d_sh * es, "y");
+        require_disjoint(out, no, "out", rho, E * (size_t)R * es, "rho");
+        require_disjoint(out, no, "out", theta, (size_t)R * P.w_numel * es, "theta");
+        require_disjoint(out, no, "out", row_ptr, (N + 1) * 4, "row_ptr");
+        require_disjoint(out, no, "out", col, E * 4, "col");
+        require_disjoint(out, no, "out", order, N * 4, "order");
+        hipFunction_t f = cgtp::radial_function_for_current_device(P, R);
+        int64_t waves = N * P.fwd_tasks;
+        long nrows = (long)N, nwaves = (long)waves;
+        void *args[] = {&row_ptr, &col, &x, &y, &rho, &theta, &out, &nrows, &nwaves, &order};
+        launch(f, waves, args, stream);
+    });
+}
+
 cgtp_status cgtp_graph_transpose(int64_t N, int64_t E, const int32_t *row_ptr, const int32_t *col, int32_t *t_row_ptr,
                                  int32_t *t_edge, int32_t *t_dst, void *stream)
 {

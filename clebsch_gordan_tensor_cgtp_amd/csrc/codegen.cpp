@@ -105,7 +105,7 @@ bool needs_mask(int mul, const Group &g) { return mul != g.tiles * g.ct; }
 // Emit loads of the sender row (x), the edge row (y) and the weights of edge index `ei`
 // and sender `si` into registers named <pre>x.., <pre>y.., <pre>w..
 void emit_edge_loads(Out &o, const Plan &P, const Group &g, const Touch &t, const std::string &pre,
-                     const std::string &si, const std::string &ei, bool declare, bool dbl = false)
+                     const std::string &si, const std::string &ei, bool declare, bool dbl = false, int radial = 0)
 {
     const std::string T = declare ? "T " : "";
     for (int b : t.i1) {
@@ -129,6 +129,11 @@ void emit_edge_loads(Out &o, const Plan &P, const Group &g, const Touch &t, cons
             if (P.paths[pi].i2 == b) off = P.paths[pi].b;
         for (int j = 0; j < n_of(P.sh[b].l); ++j)
             o(T, pre, "y", b, "_", j, " = LD_STREAM(&y[(size_t)", ei, " * DSH + ", off + j, "]);");
+    }
+    if (radial) {
+        // radial features of the edge (the weights are rebuilt from them, see emit_radial_weights)
+        for (int r = 0; r < radial; ++r) o(T, pre, "rho", r, " = LD_STREAM(&rho[(size_t)", ei, " * NRAD + ", r, "]);");
+        return;
     }
     for (int pi : g.paths) {
         const Path &p = P.paths[pi];
@@ -175,12 +180,16 @@ void emit_edge_loads(Out &o, const Plan &P, const Group &g, const Touch &t, cons
 }
 
 void emit_copy(Out &o, const Plan &P, const Group &g, const Touch &t, const std::string &dst, const std::string &src,
-               bool dbl = false)
+               bool dbl = false, int radial = 0)
 {
     for (int b : t.i1)
         for (int i = 0; i < n_of(P.ins[b].l); ++i) o(dst, "x", b, "_", i, " = ", src, "x", b, "_", i, ";");
     for (int b : t.i2)
         for (int j = 0; j < n_of(P.sh[b].l); ++j) o(dst, "y", b, "_", j, " = ", src, "y", b, "_", j, ";");
+    if (radial) {
+        for (int r = 0; r < radial; ++r) o(dst, "rho", r, " = ", src, "rho", r, ";");
+        return;
+    }
     for (int pi : g.paths) o(dst, "w", pi, " = ", src, "w", pi, ";");
     if (!dbl) return;
     for (int b : t.i1)
@@ -234,8 +243,36 @@ void emit_dbl_recv_math(Out &o, const Plan &P, const Group &g, bool f64, const s
     }
 }
 
-// acc[slot][k] += w_p * sum_{ij} C_ijk x_i y_j for every path of the group.
-void emit_forward_math(Out &o, const Plan &P, const Group &g, bool f64, const std::string &pre)
+// Radial projection (Sobek page, Abstract: reassociated radial projection): the edge's weights
+// W[p][u] = sum_r rho_r Theta[r][w_p + u] are rebuilt in registers from the R radial
+// features and the LDS copy of Theta ([r][w] layout: consecutive lanes read consecutive
+// words), never stored.
+void emit_radial_weights(Out &o, const Plan &P, const Group &g, const std::string &pre, int R, int only = -1)
+{
+    for (int pi : g.paths) {
+        if (only >= 0 && pi != only) continue;
+        const Path &p = P.paths[pi];
+        const bool m = needs_mask(p.mul_in, g);
+        // lanes past the block read column 0 (in bounds) and their weight is set to 0
+        const std::string uu = m ? "(u < " + std::to_string(p.mul_in) + " ? u : 0)" : "u";
+        std::ostringstream e;
+        e << pre << "rho0 * th[" << p.w_off << " + " << uu << "]";
+        for (int r = 1; r < R; ++r) {
+            std::ostringstream f;
+            f << "FMA(" << pre << "rho" << r << ", th[" << (long)r * P.w_numel + p.w_off << " + " << uu << "], " << e.str()
+              << ")";
+            e.str(f.str());
+        }
+        if (m)
+            o("const T ", pre, "w", pi, " = (u < ", p.mul_in, ") ? ", e.str(), " : (T)0;");
+        else
+            o("const T ", pre, "w", pi, " = ", e.str(), ";");
+    }
+}
+
+// acc[slot][k] += w_p * sum_{ij} C_ijk x_i y_j for every path of the group (radial > 0: each
+// path's weight is rebuilt from the radial features right before its use).
+void emit_forward_math(Out &o, const Plan &P, const Group &g, bool f64, const std::string &pre, int radial = 0)
 {
     for (auto &pr : pairs_of(P, g.paths)) {
         int i1 = pr.first.first, i2 = pr.first.second;
@@ -249,6 +286,7 @@ void emit_forward_math(Out &o, const Plan &P, const Group &g, bool f64, const st
               ij.second, ";");
         for (int pi : pr.second) {
             const Path &p = P.paths[pi];
+            if (radial) emit_radial_weights(o, P, g, pre, radial, pi);
             std::map<int, std::vector<const Nonzero *>> byk;
             for (const Nonzero &z : p.nz) byk[z.k].push_back(&z);
             for (auto &kv : byk) {
@@ -295,14 +333,15 @@ void emit_preamble(Out &o, const Plan &P)
 // Forward body of one group; `n` is the receiver (conv) or the row block (rows
 // mode).  With dbl, the same receiver-owned stream computes the double
 // backward's d/dg (emit_dbl_recv_math) from the extra operands ggx, ggy, ggw.
-void emit_fwd_group(Out &o, const Plan &P, int gi, bool rows, bool dbl = false)
+void emit_fwd_group(Out &o, const Plan &P, int gi, bool rows, bool dbl = false, int radial = 0)
 {
     const Group &g = P.fwd_groups[gi];
     const bool f64 = P.dtype == CGTP_F64;
     Touch t = touched(P, g.paths);
-    o("__device__ __forceinline__ void ", rows ? "tp" : dbl ? "dbr" : "fwd", "_g", gi,
+    o("__device__ __forceinline__ void ", rows ? "tp" : dbl ? "dbr" : radial ? "rad" : "fwd", "_g", gi,
       "(long n, int tile, int lane, const int* __restrict__ row_ptr, const int* __restrict__ col, "
-      "const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, ",
+      "const T* __restrict__ x, const T* __restrict__ y, ",
+      radial ? "const T* __restrict__ rho, const T* thl, " : "const T* __restrict__ w, ",
       dbl ? "const T* __restrict__ ggx, const T* __restrict__ ggy, const T* __restrict__ ggw, " : "",
       "T* __restrict__ out, long nrows)");
     o("{");
@@ -341,17 +380,26 @@ void emit_fwd_group(Out &o, const Plan &P, int gi, bool rows, bool dbl = false)
         o("int s = col[ec];");
         o("int en = (e + ", g.es, " < e1) ? e + ", g.es, " : e1 - 1;");
         o("int sn = col[en];");
-        emit_edge_loads(o, P, g, t, "c", "s", "ec", true, dbl);
+        emit_edge_loads(o, P, g, t, "c", "s", "ec", true, dbl, radial);
         o("for (; e < e1; e += ", g.es, ") {");
         o.ind++;
         o("const int enn = (e + ", 2 * g.es, " < e1) ? e + ", 2 * g.es, " : e1 - 1;");
         o("const int snn = col[enn];");
-        emit_edge_loads(o, P, g, t, "n", "sn", "en", true, dbl);
-        if (dbl)
+        emit_edge_loads(o, P, g, t, "n", "sn", "en", true, dbl, radial);
+        if (radial) {
+            // The Theta reads do not depend on the edge: left alone, the compiler hoists all
+            // R * paths of them out of the loop and spills them.  An empty asm makes the base
+            // offset (always 0) opaque per iteration, so each read stays next to its use.
+            o("int zo = 0;");
+            o("asm volatile(\"\" : \"+v\"(zo));");
+            o("const T* th = thl + zo;");
+            emit_forward_math(o, P, g, f64, "c", radial);
+        } else if (dbl) {
             emit_dbl_recv_math(o, P, g, f64, "c");
-        else
+        } else {
             emit_forward_math(o, P, g, f64, "c");
-        emit_copy(o, P, g, t, "c", "n", dbl);
+        }
+        emit_copy(o, P, g, t, "c", "n", dbl, radial);
         o("en = enn;");
         o("sn = snn;");
         o.ind--;
@@ -1327,6 +1375,43 @@ void emit_uvc_kernel(Out &o, const Plan &P)
 }
 
 }  // namespace
+
+std::string generate_radial_source(const Plan &P, int R)
+{
+    Out o;
+    emit_preamble(o, P);
+    o("#define NRAD ", R);
+    for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi) emit_fwd_group(o, P, gi, false, false, R);
+    o("// one wave per (receiver, path group, channel tile); the workgroup first stages Theta in LDS");
+    // the rebuilt weights and the double-buffered radial features need more registers than the
+    // forward's target leaves (measured: spills at 4 waves per SIMD)
+    const int waves = std::max(1, P.fwd_waves_per_eu - 1 - (R > 8 ? 1 : 0));
+    o("extern \"C\" __global__ void __launch_bounds__(256, ", waves, ") cgtp_conv_fwd_radial("
+      "const int* __restrict__ row_ptr, const int* __restrict__ col, const T* __restrict__ x, const T* __restrict__ y, "
+      "const T* __restrict__ rho, const T* __restrict__ theta, T* __restrict__ out, long nrows, long nwaves, "
+      "const int* __restrict__ order)");
+    o("{");
+    o.ind++;
+    o("__shared__ T thl[", (long)R * P.w_numel, "];  // Theta [r][w]");
+    o("for (int i = threadIdx.x; i < ", (long)R * P.w_numel, "; i += 256) thl[i] = theta[i];");
+    o("__syncthreads();");
+    o("const long wave = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const int lane = threadIdx.x & 63;");
+    o("if (wave >= nwaves) return;");
+    o("const int task = (int)(wave % ", P.fwd_tasks, ");");
+    o("long n = wave / ", P.fwd_tasks, ";");
+    o("if (order) n = order[n];  // receiver schedule (heavy rows first), results unchanged");
+    o("switch (task) {");
+    int task = 0;
+    for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi)
+        for (int tile = 0; tile < P.fwd_groups[gi].tiles; ++tile, ++task)
+            o("case ", task, ": rad_g", gi, "(n, ", tile, ", lane, row_ptr, col, x, y, rho, thl, out, nrows); break;");
+    o("default: break;");
+    o("}");
+    o.ind--;
+    o("}");
+    return o.s.str();
+}
 
 std::string generate_source(const Plan &P)
 {

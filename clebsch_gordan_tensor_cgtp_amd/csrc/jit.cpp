@@ -66,23 +66,26 @@ static void write_file_atomic(const std::string &path, const std::vector<char> &
     std::rename(tmp.c_str(), path.c_str());
 }
 
-void compile_module(Plan &P)
+void compile_module(Plan &P) { P.code = compile_source(P.source); }
+
+std::vector<char> compile_source(const std::string &source)
 {
+    std::vector<char> code;
     int major = 0, minor = 0;
     hiprtcVersion(&major, &minor);
     std::string opts;
     for (const char *o : kOptions) opts += std::string(o) + " ";
-    std::string key_src = P.source + "\n//" + opts + std::to_string(major) + "." + std::to_string(minor);
+    std::string key_src = source + "\n//" + opts + std::to_string(major) + "." + std::to_string(minor);
     char name[64];
     std::snprintf(name, sizeof name, "cgtp_%016llx%016llx.hsaco",
                   (unsigned long long)fnv1a(key_src, 1469598103934665603ull),
                   (unsigned long long)fnv1a(key_src, 0x9e3779b97f4a7c15ull));
     const std::string dir = cache_dir();
     const std::string path = dir + "/" + name;
-    if (read_file(path, P.code)) return;
+    if (read_file(path, code)) return code;
 
     hiprtcProgram prog;
-    if (hiprtcCreateProgram(&prog, P.source.c_str(), "cgtp_module.hip", 0, nullptr, nullptr) != HIPRTC_SUCCESS)
+    if (hiprtcCreateProgram(&prog, source.c_str(), "cgtp_module.hip", 0, nullptr, nullptr) != HIPRTC_SUCCESS)
         throw Error(CGTP_ERR_COMPILE, "hiprtcCreateProgram failed");
     hiprtcResult rc = hiprtcCompileProgram(prog, (int)(sizeof kOptions / sizeof kOptions[0]), kOptions);
     if (rc != HIPRTC_SUCCESS) {
@@ -95,11 +98,12 @@ void compile_module(Plan &P)
     }
     size_t n = 0;
     hiprtcGetCodeSize(prog, &n);
-    P.code.resize(n);
-    hiprtcGetCode(prog, P.code.data());
+    code.resize(n);
+    hiprtcGetCode(prog, code.data());
     hiprtcDestroyProgram(&prog);
     ::mkdir(dir.c_str(), 0755);
-    write_file_atomic(path, P.code);
+    write_file_atomic(path, code);
+    return code;
 }
 
 static void check(hipError_t e, const char *what)
@@ -128,6 +132,39 @@ const Plan::Loaded &module_for_current_device(Plan &P)
         check(hipModuleGetFunction(&L.conv_uvw, L.module, "cgtp_conv_uvw"), "hipModuleGetFunction(conv_uvw)");
     }
     return P.loaded.emplace(dev, L).first->second;
+}
+
+// Generate and compile the radial module for R (no device needed); caller holds P.mu.
+static Plan::Radial &radial_locked(Plan &P, int R)
+{
+    Plan::Radial &rv = P.radial[R];
+    if (rv.code.empty()) {
+        rv.source = generate_radial_source(P, R);
+        rv.code = compile_source(rv.source);
+    }
+    return rv;
+}
+
+const std::string &prepare_radial(Plan &P, int R)
+{
+    std::lock_guard<std::mutex> lock(P.mu);
+    return radial_locked(P, R).source;
+}
+
+hipFunction_t radial_function_for_current_device(Plan &P, int R)
+{
+    int dev = 0;
+    check(hipGetDevice(&dev), "hipGetDevice");
+    std::lock_guard<std::mutex> lock(P.mu);
+    Plan::Radial &rv = radial_locked(P, R);
+    auto it = rv.loaded.find(dev);
+    if (it != rv.loaded.end()) return it->second.second;
+    hipModule_t m = nullptr;
+    hipFunction_t f = nullptr;
+    check(hipModuleLoadData(&m, rv.code.data()), "hipModuleLoadData");
+    check(hipModuleGetFunction(&f, m, "cgtp_conv_fwd_radial"), "hipModuleGetFunction(conv_fwd_radial)");
+    rv.loaded[dev] = {m, f};
+    return f;
 }
 
 }  // namespace cgtp

@@ -86,6 +86,14 @@ struct Plan {
         hipFunction_t dbwd_recv = nullptr, dbwd_send = nullptr, conv_uvw = nullptr, tp_bwd = nullptr;
     };
     std::map<int, Loaded> loaded;
+
+    // Radial-projection forward, one module per number of radial features R (built on first use).
+    struct Radial {
+        std::string source;
+        std::vector<char> code;
+        std::map<int, std::pair<hipModule_t, hipFunction_t>> loaded;  // per device
+    };
+    std::map<int, Radial> radial;
 };
 
 // planner.cpp
@@ -96,9 +104,13 @@ void schedule(Plan &plan);
 
 // codegen.cpp
 std::string generate_source(const Plan &plan);
+std::string generate_radial_source(const Plan &plan, int R);
 
 // jit.cpp
 void compile_module(Plan &plan);
+std::vector<char> compile_source(const std::string &source);
 const Plan::Loaded &module_for_current_device(Plan &plan);
+hipFunction_t radial_function_for_current_device(Plan &plan, int R);
+const std::string &prepare_radial(Plan &plan, int R);
 
 }  // namespace cgtp

@@ -172,6 +172,27 @@ cgtp_status cgtp_conv_forward_ordered(const cgtp_plan *plan, int64_t N, int64_t 
                                       const void *w, void *out, void *stream);
 
 /*
+ * Fused convolution with radially projected weights (Sobek page, Abstract:
+ * the radial projection reassociated with the coupling and the aggregation,
+ * so that edge-sized weights are never stored): for a uvu plan,
+ *   W_e = rho[e] @ Theta,   out[n] = sum_e TP_uvu(x[col[e]], y[e], W_e),
+ * with rho [E][R] the edges' radial features (CSR edge order) and Theta
+ * [R][weight_numel] shared.  Each edge reads R values instead of weight_numel;
+ * Theta is staged in LDS (R * weight_numel elements must fit 64 KB, else
+ * CGTP_ERR_UNSUPPORTED).  1 <= R <= 64.  The kernel for a given R is generated
+ * and compiled on the first call with that R (then cached).  Everything else
+ * (CSR, schedule `order`, layouts, determinism) as cgtp_conv_forward_ordered.
+ */
+/* Generate and compile the radial kernel for R now (host only, no device needed), e.g. to
+ * move the JIT cost out of the first call; its source is then cgtp_plan_radial_source (owned
+ * by the plan; NULL before the module for R exists). */
+cgtp_status cgtp_plan_radial_prepare(const cgtp_plan *plan, int32_t R);
+const char *cgtp_plan_radial_source(const cgtp_plan *plan, int32_t R);
+cgtp_status cgtp_conv_forward_radial(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
+                                     const int32_t *col, const int32_t *order, const void *x, const void *y, int32_t R,
+                                     const void *rho, const void *theta, void *out, void *stream);
+
+/*
  * Heavy-first receiver schedule, once per graph: order [N] (caller-owned)
  * receives the receivers stably sorted by floor(log2(in-degree + 1)),
  * largest first (ties keep node order).  Integer result, deterministic.
