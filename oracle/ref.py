@@ -198,3 +198,37 @@ def conv_forward_radial(prob: Problem, row_ptr, col, x, y, rho, theta):
     shared.  The plain definition: form W = rho @ Theta, then the uvu convolution."""
     w = np.asarray(rho, np.float64) @ np.asarray(theta, np.float64)
     return conv_forward(prob, row_ptr, col, x, y, w)
+
+
+def tp_backward(prob: Problem, x, y, w, g):
+    """Gradients of sum(g * tp_forward(x, y, W)) for the batched product (use case A).
+
+    sciencestack.ai page, Abstract (gradient kernels) and Figure 4A.  uvu: per row, as the
+    convolution backward on the identity graph.  uvw (shared W_p [mul_in][mul_out]), for each path
+    and nonzero (i, j, k, c):
+      dx[b, u, i]   += c * y[b, j] * sum_w W_p[u, w] g[b, w, k]
+      dy[b, j]      += c * sum_u x[b, u, i] * sum_w W_p[u, w] g[b, w, k]
+      dW_p[u, w]    += c * sum_b x[b, u, i] y[b, j] g[b, w, k]
+    Returns (dx, dy, dw) with dw shaped like w."""
+    x, y, w, g = (np.asarray(a, np.float64) for a in (x, y, w, g))
+    rows = x.shape[0]
+    if prob.mode == "uvu":
+        ident = np.arange(rows + 1)
+        return conv_backward(prob, ident, np.arange(rows), x, y, w, g)
+    dx = np.zeros_like(x)
+    dy = np.zeros_like(y)
+    dw = np.zeros_like(w)
+    for p, a, b, o, mul_in, mul_out, nz in _path_terms(prob):
+        n1, n3 = 2 * p.l1 + 1, 2 * p.l3 + 1
+        xb = x[:, a:a + mul_in * n1].reshape(rows, mul_in, n1)
+        dxb = dx[:, a:a + mul_in * n1].reshape(rows, mul_in, n1)
+        gb = g[:, o:o + mul_out * n3].reshape(rows, mul_out, n3)
+        wp = w[p.w_off:p.w_off + mul_in * mul_out].reshape(mul_in, mul_out)
+        gw = np.einsum("uw,rwk->ruk", wp, gb)               # sum_w W_p[u, w] g[b, w, k]
+        dwp = dw[p.w_off:p.w_off + mul_in * mul_out].reshape(mul_in, mul_out)
+        for i, j, k, c in nz:
+            yj = y[:, b + j][:, None]
+            dxb[:, :, i] += c * yj * gw[:, :, k]
+            dy[:, b + j] += c * np.sum(xb[:, :, i] * gw[:, :, k], axis=1)
+            dwp += c * np.einsum("ru,r,rw->uw", xb[:, :, i], y[:, b + j], gb[:, :, k])
+    return dx, dy, dw

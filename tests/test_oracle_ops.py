@@ -487,3 +487,52 @@ def test_cpu_loops_radial_match_numpy():
     want = ref.conv_forward_radial(prob, row_ptr, col, x, y, rho, theta)[rows]
     got = loops.conv_forward_radial_rows(loops.Tables(prob), row_ptr, col, x, y, rho, theta, rows)
     assert np.allclose(got, want, atol=1e-12)
+
+
+
+# ------------------------------------------------------------------------------ batched backward
+
+def _uvw_tp_problem():
+    return irreps.build_problem("3x0e+2x1o+2x2e", irreps.sh_irreps(2), "2x0e+3x1o+2x2e+1x1e+2x2o", "uvw")
+
+
+def test_tp_backward_uvw_matches_autograd_of_dense_einsum():
+    import torch
+    prob = _uvw_tp_problem()
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((9, prob.d_in))
+    y = rng.standard_normal((9, prob.d_sh))
+    w = rng.standard_normal(prob.weight_numel)
+    g = rng.standard_normal((9, prob.d_out))
+    t = torch.from_numpy(dense_tensor(prob))
+    X, Y, W = (torch.tensor(a, requires_grad=True) for a in (x, y, w))
+    out = torch.einsum("abvo,ra,rb,v->ro", t, X, Y, W)
+    want = torch.autograd.grad((torch.from_numpy(g) * out).sum(), (X, Y, W))
+    got = ref.tp_backward(prob, x, y, w, g)
+    for a, b in zip(got, want):
+        assert np.allclose(a, b.numpy(), atol=1e-11)
+
+
+def test_tp_backward_uvw_trilinear_and_finite_differences():
+    prob = _uvw_tp_problem()
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((7, prob.d_in))
+    y = rng.standard_normal((7, prob.d_sh))
+    w = rng.standard_normal(prob.weight_numel)
+    g = rng.standard_normal((7, prob.d_out))
+    dx, dy, dw = ref.tp_backward(prob, x, y, w, g)
+    s = np.sum(g * ref.tp_forward(prob, x, y, w))
+    for a, b in ((dx, x), (dy, y), (dw, w)):
+        assert abs(np.sum(a * b) - s) <= 1e-11 * max(1.0, abs(s))
+    h = 1e-6
+    base = [x, y, w]
+    for which, grad in enumerate((dx, dy, dw)):
+        for _ in range(4):
+            arr = base[which]
+            idx = tuple(rng.integers(0, n) for n in arr.shape)
+            ap, am = list(base), list(base)
+            ap[which], am[which] = arr.copy(), arr.copy()
+            ap[which][idx] += h
+            am[which][idx] -= h
+            fd = (np.sum(g * ref.tp_forward(prob, *ap)) - np.sum(g * ref.tp_forward(prob, *am))) / (2 * h)
+            assert abs(fd - grad[idx]) < 1e-6 * max(1.0, abs(grad[idx]))
