@@ -21,6 +21,7 @@
  */
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #include <omp.h>
 
@@ -154,6 +155,86 @@ int oracle_uvw_forward(int n_paths, const int *pt, const int *nzi, const int *nz
             }
         }
     }
+    return 0;
+}
+
+/*
+ * uvw batched backward: the derivatives of sum(g * out) written as loops.  For every row, path,
+ * input channel u and nonzero (i, j, k, c):
+ *   gw[k]  = sum_w W_p[u][w] g[row, o + w*n3 + k]
+ *   dx[row, a + u*n1 + i] += c * y[row, b + j] * gw[k]
+ *   dy[row, b + j]        += c * x[row, a + u*n1 + i] * gw[k]
+ *   t[k] (= sum of c * x * y)  then  dW_p[u][w] += sum_k t[k] * g[row, o + w*n3 + k]
+ * dx and dy are written for the n_rows rows; dW sums over the rows `wrows` (n_wrows of them), each
+ * thread into its own array, the arrays then added in thread order.
+ */
+int oracle_uvw_backward(int n_paths, const int *pt, const int *nzi, const int *nzj, const int *nzk,
+                        const double *nzc, int d_x, int d_sh, int d_out, int64_t weight_numel, int64_t n_rows,
+                        const int64_t *rows, int64_t n_wrows, const int64_t *wrows, const void *x, const void *y,
+                        const void *w, const void *g, int in_f32, double *dx, double *dy, double *dw,
+                        int n_threads)
+{
+#pragma omp parallel for schedule(dynamic, 4) num_threads(n_threads)
+    for (int64_t s = 0; s < n_rows; ++s) {
+        const int64_t r = rows[s];
+        double *ox = dx + (size_t)s * d_x, *oy = dy + (size_t)s * d_sh;
+        double gw[64];
+        memset(ox, 0, sizeof(double) * (size_t)d_x);
+        memset(oy, 0, sizeof(double) * (size_t)d_sh);
+        for (int p = 0; p < n_paths; ++p) {
+            const int *q = pt + p * PT_FIELDS;
+            int mi = q[PT_MUL_IN], mo = q[PT_MUL_OUT], n3 = q[PT_N3];
+            for (int u = 0; u < mi; ++u) {
+                for (int k = 0; k < n3; ++k) {
+                    gw[k] = 0.0;
+                    for (int ww = 0; ww < mo; ++ww)
+                        gw[k] += ld(w, (size_t)q[PT_WOFF] + (size_t)u * mo + ww, in_f32) *
+                                 ld(g, (size_t)r * d_out + q[PT_O] + ww * n3 + k, in_f32);
+                }
+                for (int z = q[PT_NZ0]; z < q[PT_NZ0] + q[PT_NZN]; ++z) {
+                    double xv = ld(x, (size_t)r * d_x + q[PT_A] + u * q[PT_N1] + nzi[z], in_f32);
+                    double yv = ld(y, (size_t)r * d_sh + q[PT_B] + nzj[z], in_f32);
+                    ox[q[PT_A] + u * q[PT_N1] + nzi[z]] += nzc[z] * yv * gw[nzk[z]];
+                    oy[q[PT_B] + nzj[z]] += nzc[z] * xv * gw[nzk[z]];
+                }
+            }
+        }
+    }
+    int nt = n_threads > 0 ? n_threads : 1;
+    double *part = (double *)calloc((size_t)nt * (size_t)weight_numel, sizeof(double));
+    if (!part) return 1;
+#pragma omp parallel num_threads(nt)
+    {
+        double *mine = part + (size_t)omp_get_thread_num() * (size_t)weight_numel;
+        double t[64];
+#pragma omp for schedule(static)
+        for (int64_t s = 0; s < n_wrows; ++s) {
+            const int64_t r = wrows[s];
+            for (int p = 0; p < n_paths; ++p) {
+                const int *q = pt + p * PT_FIELDS;
+                int mi = q[PT_MUL_IN], mo = q[PT_MUL_OUT], n3 = q[PT_N3];
+                for (int u = 0; u < mi; ++u) {
+                    for (int k = 0; k < n3; ++k) t[k] = 0.0;
+                    for (int z = q[PT_NZ0]; z < q[PT_NZ0] + q[PT_NZN]; ++z) {
+                        double xv = ld(x, (size_t)r * d_x + q[PT_A] + u * q[PT_N1] + nzi[z], in_f32);
+                        double yv = ld(y, (size_t)r * d_sh + q[PT_B] + nzj[z], in_f32);
+                        t[nzk[z]] += nzc[z] * xv * yv;
+                    }
+                    for (int ww = 0; ww < mo; ++ww) {
+                        double acc = 0.0;
+                        for (int k = 0; k < n3; ++k) acc += t[k] * ld(g, (size_t)r * d_out + q[PT_O] + ww * n3 + k, in_f32);
+                        mine[(size_t)q[PT_WOFF] + (size_t)u * mo + ww] += acc;
+                    }
+                }
+            }
+        }
+    }
+    for (int64_t i = 0; i < weight_numel; ++i) {
+        double acc = 0.0;
+        for (int th = 0; th < nt; ++th) acc += part[(size_t)th * (size_t)weight_numel + i];
+        dw[i] = acc;
+    }
+    free(part);
     return 0;
 }
 

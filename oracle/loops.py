@@ -150,6 +150,25 @@ def uvw_forward(tab: Tables, x, y, w, n_threads=None) -> np.ndarray:
     return out
 
 
+def uvw_backward(tab: Tables, x, y, w, g, rows, wrows, n_threads=None):
+    """uvw batched backward: (dx, dy) of the rows ``rows`` and dW summed over the rows ``wrows``."""
+    prob = tab.prob
+    x, y, w, g = _input(x), _input(y), _input(w), _input(g)
+    f32 = _same_kind(x, y, w, g)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    wrows = np.ascontiguousarray(wrows, dtype=np.int64)
+    dx = np.empty((len(rows), prob.d_in))
+    dy = np.empty((len(rows), prob.d_sh))
+    dw = np.empty(prob.weight_numel)
+    rc = _load().oracle_uvw_backward(*tab.head(), prob.d_in, prob.d_sh, prob.d_out,
+                                     ctypes.c_int64(prob.weight_numel), ctypes.c_int64(len(rows)), _p(rows),
+                                     ctypes.c_int64(len(wrows)), _p(wrows), _p(x), _p(y), _p(w), _p(g), f32,
+                                     _p(dx), _p(dy), _p(dw), n_threads or default_threads())
+    if rc != 0:
+        raise MemoryError("oracle_uvw_backward: allocation failed")
+    return dx, dy, dw
+
+
 # ----------------------------------------------------------------------------------------------
 # Convenience wrappers on whole or sampled graphs (index bookkeeping only, no arithmetic).
 

@@ -536,3 +536,22 @@ def test_tp_backward_uvw_trilinear_and_finite_differences():
             am[which][idx] -= h
             fd = (np.sum(g * ref.tp_forward(prob, *ap)) - np.sum(g * ref.tp_forward(prob, *am))) / (2 * h)
             assert abs(fd - grad[idx]) < 1e-6 * max(1.0, abs(grad[idx]))
+
+
+
+@pytest.mark.parametrize("in_f32", [False, True])
+def test_cpu_loops_uvw_backward_match_numpy(in_f32):
+    prob = irreps.build_problem("2x0e+3x1o+2x2e+1x3o", irreps.sh_irreps(3), "3x0e+2x1o+2x2e+1x3o+2x1e+1x2o", "uvw")
+    rng = np.random.default_rng(24)
+    x = rng.standard_normal((13, prob.d_in))
+    y = rng.standard_normal((13, prob.d_sh))
+    w = rng.standard_normal(prob.weight_numel)
+    g = rng.standard_normal((13, prob.d_out))
+    if in_f32:
+        x, y, w, g = (a.astype(np.float32) for a in (x, y, w, g))
+    want = ref.tp_backward(prob, x, y, w, g)
+    rows = np.array([4, 0, 12, 7])
+    dx, dy, dw = loops.uvw_backward(loops.Tables(prob), x, y, w, g, rows, np.arange(13))
+    assert np.allclose(dx, want[0][rows], atol=1e-12)
+    assert np.allclose(dy, want[1][rows], atol=1e-12)
+    assert np.allclose(dw, want[2], atol=1e-11)
