@@ -23,7 +23,8 @@ EXPORTS = ("cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info_get", "cgtp_
            "cgtp_plan_path_coefficients", "cgtp_plan_source", "cgtp_tp_forward", "cgtp_conv_forward",
            "cgtp_graph_transpose", "cgtp_conv_backward", "cgtp_spherical_harmonics", "cgtp_last_error",
            "cgtp_conv_forward_ordered", "cgtp_graph_order", "cgtp_conv_double_backward", "cgtp_tp_backward",
-           "cgtp_conv_forward_radial", "cgtp_plan_radial_prepare", "cgtp_plan_radial_source")
+           "cgtp_conv_forward_radial", "cgtp_plan_radial_prepare", "cgtp_plan_radial_source",
+           "cgtp_tp_backward_workspace_size", "cgtp_plan_uvw_backward_prepare", "cgtp_plan_uvw_backward_source")
 
 
 class CgtpError(RuntimeError):
@@ -59,6 +60,7 @@ def lib():
         L.cgtp_last_error.restype = ctypes.c_char_p
         L.cgtp_plan_source.restype = ctypes.c_char_p
         L.cgtp_plan_radial_source.restype = ctypes.c_char_p
+        L.cgtp_plan_uvw_backward_source.restype = ctypes.c_char_p
         L.cgtp_plan_source.argtypes = [vp]
         L.cgtp_plan_create.argtypes = [ctypes.c_char_p] * 3 + [ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp)]
         L.cgtp_plan_destroy.argtypes = [vp]
@@ -73,7 +75,8 @@ def lib():
         L.cgtp_conv_backward.argtypes = [vp, i64, i64] + [vp] * 13
         L.cgtp_spherical_harmonics.argtypes = [i32, ctypes.c_int, i64, vp, vp, vp]
         for name in EXPORTS:
-            if name not in ("cgtp_last_error", "cgtp_plan_source", "cgtp_plan_radial_source"):
+            if name not in ("cgtp_last_error", "cgtp_plan_source", "cgtp_plan_radial_source",
+                            "cgtp_plan_uvw_backward_source"):
                 getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -134,6 +137,11 @@ class Plan:
     @property
     def source(self) -> str:
         return lib().cgtp_plan_source(self._h).decode()
+
+    def uvw_backward_source(self) -> str:
+        """Generate and compile the uvw batched-backward module (host only); its source."""
+        _check(lib().cgtp_plan_uvw_backward_prepare(self._h))
+        return lib().cgtp_plan_uvw_backward_source(self._h).decode()
 
     def radial_source(self, R: int) -> str:
         """Generate and compile the radial-projection module for R (host only); its source."""
@@ -226,23 +234,35 @@ def tp_forward(plan: Plan, x, y, w, out=None, stream=None):
     return out
 
 
+def tp_backward_workspace_size(plan: Plan, B: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().cgtp_tp_backward_workspace_size(plan.handle, B, ctypes.byref(n)))
+    return n.value
+
+
 def tp_backward(plan: Plan, x, y, w, grad_out, grad_x=None, grad_y=None, grad_w=None, need=(True, True, True),
-                stream=None):
-    """Batched product backward (uvu): returns (grad_x, grad_y, grad_w); entries not in ``need`` are None."""
+                workspace=None, stream=None):
+    """Batched product backward: returns (grad_x, grad_y, grad_w); entries not in ``need`` are None.
+    uvu: per-row weights; uvw: shared weights (a workspace is allocated here unless given)."""
     import torch
     B = x.shape[0]
     dt = plan.torch_dtype
     dev = x.device
-    shapes = ((B, plan.d_x), (B, plan.d_sh), (B, plan.weight_numel))
+    shared = 1 if plan.mode == "uvw" else 0
+    wshape = (plan.weight_numel,) if shared else (B, plan.weight_numel)
+    shapes = ((B, plan.d_x), (B, plan.d_sh), wshape)
     res = [None if not nd else (torch.empty(sh, dtype=dt, device=dev) if o is None else o)
            for o, nd, sh in zip((grad_x, grad_y, grad_w), need, shapes)]
-    shared = 1 if plan.mode == "uvw" else 0
-    wshape = (plan.weight_numel,) if shared else shapes[2]
+    nbytes = tp_backward_workspace_size(plan, B) if res[2] is not None else 0
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes // (4 if plan.dtype == "f32" else 8), dtype=dt, device=dev)
+    ws = ctypes.c_void_p(0) if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().cgtp_tp_backward(plan.handle, B, _dev(x, "x", dt, shapes[0]), _dev(y, "y", dt, shapes[1]),
                                   _dev(w, "w", dt, wshape), shared, _dev(grad_out, "grad_out", dt, (B, plan.d_out)),
                                   *[_ptr_or_null(r, n, dt, sh) for r, n, sh in zip(res, ("grad_x", "grad_y", "grad_w"),
                                                                                    shapes)],
-                                  _stream(stream, dev)))
+                                  ws, ctypes.c_size_t(wsb), _stream(stream, dev)))
     return tuple(res)
 
 

@@ -262,18 +262,45 @@ cgtp_status cgtp_conv_forward(const cgtp_plan *plan, int64_t N, int64_t E, const
     return cgtp_conv_forward_ordered(plan, N, E, row_ptr, col, nullptr, x, y, w, out, stream);
 }
 
+// uvw batched backward: chunks of 16-row blocks whose dW partials the workspace holds
+static void uvb_chunks(int64_t B, long &nblocks, long &bpc, long &nchunks)
+{
+    nblocks = (long)((B + 15) / 16);
+    nchunks = std::min<long>(nblocks, 256);
+    bpc = nchunks > 0 ? (nblocks + nchunks - 1) / nchunks : 1;
+    nchunks = nchunks > 0 ? (nblocks + bpc - 1) / bpc : 0;
+}
+
+cgtp_status cgtp_tp_backward_workspace_size(const cgtp_plan *plan, int64_t B, size_t *bytes)
+{
+    return guarded([&] {
+        require(plan != nullptr && bytes != nullptr, "plan and bytes must be non-NULL");
+        const cgtp::Plan &P = plan->p;
+        require(B >= 0 && B < INT_MAX, "B must be in [0, 2^31-1)");
+        *bytes = 0;
+        if (P.mode == CGTP_UVW) {
+            long nblocks, bpc, nchunks;
+            uvb_chunks(B, nblocks, bpc, nchunks);
+            *bytes = (size_t)nchunks * P.w_numel * elem(P);
+        }
+    });
+}
+
 cgtp_status cgtp_tp_backward(const cgtp_plan *plan, int64_t B, const void *x, const void *y, const void *w,
                              int shared_weights, const void *grad_out, void *grad_x, void *grad_y, void *grad_w,
-                             void *stream)
+                             void *workspace, size_t workspace_bytes, void *stream)
 {
     return guarded([&] {
         require(plan != nullptr, "plan is NULL");
         cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
         require(B >= 0 && B < INT_MAX, "B must be in [0, 2^31-1)");
-        if (P.mode == CGTP_UVU)
+        const bool uvw = P.mode == CGTP_UVW;
+        if (!uvw)
             require(shared_weights == 0, "uvu takes per-row weights: shared_weights must be 0");
         else
-            throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw batched backward is not built yet");
+            require(shared_weights == 1, "uvw takes shared weights: shared_weights must be 1");
+        if (uvw && !P.uvb_ok)
+            throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw batched backward: every multiplicity must be <= 16");
         if (B == 0 || (!grad_x && !grad_y && !grad_w)) return;
         const size_t es = elem(P);
         require_ptr(x, "x", es);
@@ -283,23 +310,51 @@ cgtp_status cgtp_tp_backward(const cgtp_plan *plan, int64_t B, const void *x, co
         if (grad_x) require_ptr(grad_x, "grad_x", es);
         if (grad_y) require_ptr(grad_y, "grad_y", es);
         if (grad_w) require_ptr(grad_w, "grad_w", es);
-        const void *ins[] = {x, y, w, grad_out};
-        const size_t inn[] = {B * P.d_x * es, B * P.d_sh * es, B * P.w_numel * es, B * P.d_out * es};
-        const char *inm[] = {"x", "y", "w", "grad_out"};
-        void *outs[] = {grad_x, grad_y, grad_w};
-        const size_t outn[] = {B * P.d_x * es, B * P.d_sh * es, B * P.w_numel * es};
-        const char *outm[] = {"grad_x", "grad_y", "grad_w"};
-        for (int a = 0; a < 3; ++a) {
-            for (int b = 0; b < 4; ++b) require_disjoint(outs[a], outn[a], outm[a], ins[b], inn[b], inm[b]);
-            for (int b = a + 1; b < 3; ++b) require_disjoint(outs[a], outn[a], outm[a], outs[b], outn[b], outm[b]);
+        const size_t nw = (uvw ? 1 : (size_t)B) * P.w_numel * es;
+        long nblocks, bpc, nchunks;
+        uvb_chunks(B, nblocks, bpc, nchunks);
+        const size_t ws_need = uvw && grad_w ? (size_t)nchunks * P.w_numel * es : 0;
+        if (ws_need) {
+            require_ptr(workspace, "workspace", es);
+            require(workspace_bytes >= ws_need, "workspace too small (see cgtp_tp_backward_workspace_size)");
         }
-        const auto &L = cgtp::module_for_current_device(P);
+        const void *ins[] = {x, y, w, grad_out};
+        const size_t inn[] = {B * P.d_x * es, B * P.d_sh * es, nw, B * P.d_out * es};
+        const char *inm[] = {"x", "y", "w", "grad_out"};
+        void *outs[] = {grad_x, grad_y, grad_w, ws_need ? workspace : nullptr};
+        const size_t outn[] = {B * P.d_x * es, B * P.d_sh * es, nw, ws_need};
+        const char *outm[] = {"grad_x", "grad_y", "grad_w", "workspace"};
+        for (int a = 0; a < 4; ++a) {
+            for (int b = 0; b < 4; ++b) require_disjoint(outs[a], outn[a], outm[a], ins[b], inn[b], inm[b]);
+            for (int b = a + 1; b < 4; ++b) require_disjoint(outs[a], outn[a], outm[a], outs[b], outn[b], outm[b]);
+        }
         long nrows = (long)B;
-        // one launch per path group, in order (later groups add to blocks an earlier one wrote)
-        for (int grp = 0; grp < (int)P.bwd_groups.size(); ++grp) {
-            long nblocks = (long)((B + P.bwd_groups[grp].es - 1) / P.bwd_groups[grp].es);
-            void *args[] = {&x, &y, &w, &grad_out, &grad_x, &grad_y, &grad_w, &nrows, &nblocks, &grp};
-            launch(L.tp_bwd, nblocks, args, stream);
+        if (!uvw) {
+            const auto &L = cgtp::module_for_current_device(P);
+            // one launch per path group, in order (later groups add to blocks an earlier one wrote)
+            for (int grp = 0; grp < (int)P.bwd_groups.size(); ++grp) {
+                long nb = (long)((B + P.bwd_groups[grp].es - 1) / P.bwd_groups[grp].es);
+                void *args[] = {&x, &y, &w, &grad_out, &grad_x, &grad_y, &grad_w, &nrows, &nb, &grp};
+                launch(L.tp_bwd, nb, args, stream);
+            }
+            return;
+        }
+        const auto &F = cgtp::uvw_backward_for_current_device(P);
+        if (grad_x || grad_y) {
+            // one launch per input block, in order (dY is added over the launches)
+            for (int grp = 0; grp < (int)P.uvb_x_groups.size(); ++grp) {
+                void *args[] = {&x, &y, &w, &grad_out, &grad_x, &grad_y, &nrows, &nblocks, &grp};
+                launch(F.xy, nblocks, args, stream);
+            }
+        }
+        if (grad_w) {
+            long nwaves = nchunks * (long)P.uvb_w_groups.size();
+            void *args[] = {&x, &y, &grad_out, &workspace, &nrows, &nblocks, &bpc, &nchunks, &nwaves};
+            launch(F.w, nwaves, args, stream);
+            void *rargs[] = {&workspace, &nchunks, &grad_w};
+            check_hip(hipModuleLaunchKernel(F.reduce, (unsigned)((P.w_numel + 255) / 256), 1, 1, 256, 1, 1, 0,
+                                            static_cast<hipStream_t>(stream), rargs, nullptr),
+                      "hipModuleLaunchKernel");
         }
     });
 }
@@ -364,6 +419,25 @@ cgtp_status cgtp_conv_forward_ordered(const cgtp_plan *plan, int64_t N, int64_t 
         void *args[] = {&row_ptr, &col, &x, &y, &w, &out, &nrows, &nwaves, &order};
         launch(L.conv_fwd, waves, args, stream);
     });
+}
+
+cgtp_status cgtp_plan_uvw_backward_prepare(const cgtp_plan *plan)
+{
+    return guarded([&] {
+        require(plan != nullptr, "plan is NULL");
+        cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
+        if (P.mode != CGTP_UVW || !P.uvb_ok)
+            throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw batched backward: uvw plans with multiplicities <= 16");
+        cgtp::prepare_uvw_backward(P);
+    });
+}
+
+const char *cgtp_plan_uvw_backward_source(const cgtp_plan *plan)
+{
+    if (!plan) return nullptr;
+    cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
+    std::lock_guard<std::mutex> lock(P.mu);
+    return P.uvb.code.empty() ? nullptr : P.uvb.source.c_str();
 }
 
 cgtp_status cgtp_plan_radial_prepare(const cgtp_plan *plan, int32_t R)

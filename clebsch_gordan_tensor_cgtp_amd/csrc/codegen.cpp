@@ -1374,7 +1374,342 @@ void emit_uvc_kernel(Out &o, const Plan &P)
     o("");
 }
 
+// ------------------------------------------------------------------------------------------
+// uvw batched backward (every mul_in, mul_out <= 16).  One wave per 16-row block; lane l works
+// on row l % 16.  With G_p[row][u][k] = sum_w W_p[u][w] g[row][w][k] (MFMA: A = W_p[u = l%16][w],
+// B = g[row = l%16][w][k], the lane ending with u = U(v) of its row):
+//   dx[row][u][i] = sum_p sum_k A_p[i][k] G_p[row][u][k],  A_p[i][k] = sum_j C_ijk y[row][j]
+//   dy[row][j]    = sum_p sum_{u,i,k} C_ijk x[row][u][i] G_p[row][u][k]
+// (cgtp_tp_uvw_bwd_xy, one launch per input block; dY summed over the launches in order), and
+//   dW_p[u][w] = sum_rows sum_k t_p[row][u][k] g[row][w][k],  t_p = sum_i A_p[i][k] x[row][u][i]
+// as per-chunk MFMA partials over row blocks (t transposed through LDS so that the rows are the
+// MFMA K dimension), summed in chunk order by cgtp_reduce_chunks.
+std::string uvb_u(bool f64, int v) { return f64 ? "(usub + " + std::to_string(4 * v) + ")" : "(4 * usub + " + std::to_string(v) + ")"; }
+
+void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
+{
+    const Group &g = P.uvb_x_groups[gi];
+    const bool f64 = P.dtype == CGTP_F64;
+    Touch t = touched(P, g.paths);
+    const int b1 = P.paths[g.paths[0]].i1;
+    const Irrep &ir = P.ins[b1];
+    const int n1 = n_of(ir.l);
+    const int a = P.paths[g.paths[0]].a;
+    o("__device__ __forceinline__ void uvbx_g", gi, "(long blk, int wv, int lane, const T* __restrict__ x, "
+      "const T* __restrict__ y, const T* __restrict__ w, const T* __restrict__ g, T* __restrict__ dx, "
+      "T* __restrict__ dy, long nrows, T* dyl)");
+    o("{");
+    o.ind++;
+    o("const int rl = lane & 15;");
+    o("const int usub = lane >> 4;");
+    o("const long row = blk * 16 + rl;");
+    o("const bool live = row < nrows;");
+    o("const long rr = live ? row : nrows - 1;  // rows past the end read row nrows-1 and store nothing");
+    o("T* dyw = dyl + wv * ", 16 * P.d_sh, ";  // this wave's dY rows");
+    o("for (int c = lane; c < ", 16 * P.d_sh, "; c += 64) dyw[c] = (T)0;");
+    o("WAVE_SYNC();");
+    for (int b : t.i2) {
+        int off = 0;
+        for (int bb = 0; bb < b; ++bb) off += P.sh[bb].dim();
+        for (int j = 0; j < n_of(P.sh[b].l); ++j) o("const T y", b, "_", j, " = y[(size_t)rr * DSH + ", off + j, "];");
+    }
+    for (int v = 0; v < 4; ++v) {
+        const std::string u = uvb_u(f64, v);
+        for (int i = 0; i < n1; ++i) {
+            o("const T x", v, "_", i, " = ", u, " < ", ir.mul, " ? x[(size_t)rr * DX + ", a, " + (", u, " < ", ir.mul, " ? ", u,
+              " : 0) * ", n1, " + ", i, "] : (T)0;");
+            o("T d", v, "_", i, " = (T)0;");
+        }
+    }
+    for (int pi : g.paths) {
+        const Path &p = P.paths[pi];
+        const int n3 = n_of(p.l3), n2 = n_of(p.l2);
+        o("{");
+        o.ind++;
+        // A operands of G: W_p[u = lane % 16][w = 4c + lane / 16]
+        const int wch = (p.mul_out + 3) / 4;
+        for (int c = 0; c < wch; ++c) {
+            o("const bool wok", c, " = rl < ", p.mul_in, " && ", 4 * c, " + usub < ", p.mul_out, ";");
+            o("const T wv", c, " = w[", p.w_off, " + (wok", c, " ? rl * ", p.mul_out, " + ", 4 * c, " + usub : 0)];");
+            o("const T wa", c, " = wok", c, " ? wv", c, " : (T)0;");
+        }
+        for (int j = 0; j < n2; ++j) o("T h", j, " = (T)0;");
+        std::map<int, std::map<int, std::vector<const Nonzero *>>> byki;  // k -> i -> nonzeros
+        for (const Nonzero &z : p.nz) byki[z.k][z.i].push_back(&z);
+        for (auto &kk : byki) {
+            const int k = kk.first;
+            o("{");
+            o.ind++;
+            for (int c = 0; c < wch; ++c)
+                o("const T gb", c, " = ", 4 * c, " + usub < ", p.mul_out, " ? g[(size_t)rr * DOUT + ", p.o, " + (", 4 * c,
+                  " + usub < ", p.mul_out, " ? ", 4 * c, " + usub : 0) * ", n3, " + ", k, "] : (T)0;");
+            o("V4 G = {0, 0, 0, 0};");
+            for (int c = 0; c < wch; ++c) o("G = MFMA(wa", c, ", gb", c, ", G);");
+            for (auto &ii : kk.second) {
+                const int i = ii.first;
+                const auto &v = ii.second;
+                std::ostringstream e;
+                e << lit(v[0]->c, f64) << " * y" << p.i2 << "_" << v[0]->j;
+                for (size_t n = 1; n < v.size(); ++n) {
+                    std::ostringstream f;
+                    f << "FMA(" << lit(v[n]->c, f64) << ", y" << p.i2 << "_" << v[n]->j << ", " << e.str() << ")";
+                    e.str(f.str());
+                }
+                o("{");
+                o.ind++;
+                o("const T A = ", e.str(), ";");
+                for (int vv = 0; vv < 4; ++vv) o("d", vv, "_", i, " = FMA(A, G[", vv, "], d", vv, "_", i, ");");
+                o("const T si = FMA(x0_", i, ", G[0], FMA(x1_", i, ", G[1], FMA(x2_", i, ", G[2], x3_", i, " * G[3])));");
+                for (const Nonzero *z : v) o("h", z->j, " = FMA(", lit(z->c, f64), ", si, h", z->j, ");");
+                o.ind--;
+                o("}");
+            }
+            // one output component at a time: without this the loads and MFMAs of every k of the
+            // path are issued together and all of their results stay live
+            o("__builtin_amdgcn_sched_barrier(0);");
+            o.ind--;
+            o("}");
+        }
+        // dY of this path: sum the row's four lanes, then lane usub == 0 adds into the wave's LDS rows
+        for (int j = 0; j < n2; ++j) {
+            o("h", j, " += __shfl_xor(h", j, ", 16);");
+            o("h", j, " += __shfl_xor(h", j, ", 32);");
+        }
+        o("if (usub == 0) {");
+        o.ind++;
+        for (int j = 0; j < n2; ++j) o("dyw[rl * DSH + ", p.b + j, "] += h", j, ";");
+        o.ind--;
+        o("}");
+        // The dx sums are only read by the conditional store at the end; left alone the compiler
+        // sinks every update there and keeps each (path, k) result of G live until then.  An
+        // empty asm consumes and redefines them here, so each path's updates happen in place.
+        for (int v = 0; v < 4; ++v)
+            for (int i = 0; i < n1; ++i) o("asm volatile(\"\" : \"+v\"(d", v, "_", i, "));");
+        o("__builtin_amdgcn_sched_barrier(0);");
+        o.ind--;
+        o("}");
+    }
+    o("if (live && dx) {");
+    o.ind++;
+    for (int v = 0; v < 4; ++v) {
+        const std::string u = uvb_u(f64, v);
+        o("if (", u, " < ", ir.mul, ") {");
+        o.ind++;
+        for (int i = 0; i < n1; ++i) o("dx[(size_t)rr * DX + ", a, " + ", u, " * ", n1, " + ", i, "] = d", v, "_", i, ";");
+        o.ind--;
+        o("}");
+    }
+    if (gi == 0) {
+        // input blocks that no path uses get zero gradients
+        int off = 0;
+        for (int b = 0; b < (int)P.ins.size(); ++b) {
+            bool used = false;
+            for (const Path &q : P.paths) used = used || q.i1 == b;
+            if (!used) o("for (int c = lane >> 4; c < ", P.ins[b].dim(), "; c += 4) dx[(size_t)rr * DX + ", off, " + c] = (T)0;");
+            off += P.ins[b].dim();
+        }
+    }
+    o.ind--;
+    o("}");
+    o("WAVE_SYNC();");
+    // dY of the rows: the first launch writes every column, later launches add theirs
+    o("if (live && dy) {");
+    o.ind++;
+    o("for (int j = usub; j < DSH; j += 4) dy[(size_t)rr * DSH + j] ", gi == 0 ? "=" : "+=", " dyw[rl * DSH + j];");
+    o.ind--;
+    o("}");
+    o.ind--;
+    o("}");
+    o("");
+}
+
+void emit_uvb_w_group(Out &o, const Plan &P, int gi)
+{
+    const Group &g = P.uvb_w_groups[gi];
+    const bool f64 = P.dtype == CGTP_F64;
+    Touch t = touched(P, g.paths);
+    o("__device__ __forceinline__ void uvbw_g", gi, "(long chunk, int wv, int lane, const T* __restrict__ x, "
+      "const T* __restrict__ y, const T* __restrict__ g, T* __restrict__ ws, long nrows, long nblocks, long bpc, T* tl)");
+    o("{");
+    o.ind++;
+    o("const int rl = lane & 15;");
+    o("const int usub = lane >> 4;");
+    o("T* tw = tl + wv * ", 16 * 17, ";  // this wave's transpose tile [row][u], rows padded to 17");
+    for (int pi : g.paths) o("V4 D", pi, " = {0, 0, 0, 0};");
+    o("const long b0 = chunk * bpc;");
+    o("const long b1 = b0 + bpc < nblocks ? b0 + bpc : nblocks;");
+    o("for (long blk = b0; blk < b1; ++blk) {");
+    o.ind++;
+    o("const long row = blk * 16 + rl;");
+    o("const bool live = row < nrows;");
+    o("const long rr = live ? row : nrows - 1;");
+    for (int b : t.i2) {
+        int off = 0;
+        for (int bb = 0; bb < b; ++bb) off += P.sh[bb].dim();
+        for (int j = 0; j < n_of(P.sh[b].l); ++j) o("const T y", b, "_", j, " = y[(size_t)rr * DSH + ", off + j, "];");
+    }
+    std::map<int, std::vector<int>> by_i1;
+    for (int pi : g.paths) by_i1[P.paths[pi].i1].push_back(pi);
+    for (auto &kv : by_i1) {
+        const Irrep &ir = P.ins[kv.first];
+        const int n1 = n_of(ir.l);
+        const int a = P.paths[kv.second[0]].a;
+        o("{");
+        o.ind++;
+        // x in the forward's layout: lane holds u = 4c + lane / 16
+        for (int c = 0; c < 4; ++c)
+            for (int i = 0; i < n1; ++i)
+                o("const T x", c, "_", i, " = ", 4 * c, " + usub < ", ir.mul, " ? x[(size_t)rr * DX + ", a, " + (", 4 * c, " + usub < ",
+                  ir.mul, " ? ", 4 * c, " + usub : 0) * ", n1, " + ", i, "] : (T)0;");
+        for (int pi : kv.second) {
+            const Path &p = P.paths[pi];
+            const int n3 = n_of(p.l3);
+            std::map<int, std::map<int, std::vector<const Nonzero *>>> byki;
+            for (const Nonzero &z : p.nz) byki[z.k][z.i].push_back(&z);
+            for (auto &kk : byki) {
+                const int k = kk.first;
+                o("{");
+                o.ind++;
+                for (auto &ii : kk.second) {
+                    const auto &v = ii.second;
+                    std::ostringstream e;
+                    e << lit(v[0]->c, f64) << " * y" << p.i2 << "_" << v[0]->j;
+                    for (size_t n = 1; n < v.size(); ++n) {
+                        std::ostringstream f;
+                        f << "FMA(" << lit(v[n]->c, f64) << ", y" << p.i2 << "_" << v[n]->j << ", " << e.str() << ")";
+                        e.str(f.str());
+                    }
+                    o("const T A", ii.first, " = ", e.str(), ";");
+                }
+                o("WAVE_SYNC();");
+                for (int c = 0; c < 4; ++c) {
+                    std::ostringstream e;
+                    bool first = true;
+                    for (auto &ii : kk.second) {
+                        if (first) {
+                            e << "A" << ii.first << " * x" << c << "_" << ii.first;
+                            first = false;
+                        } else {
+                            std::ostringstream f;
+                            f << "FMA(A" << ii.first << ", x" << c << "_" << ii.first << ", " << e.str() << ")";
+                            e.str(f.str());
+                        }
+                    }
+                    o("tw[rl * 17 + ", 4 * c, " + usub] = live ? ", e.str(), " : (T)0;");
+                }
+                o("WAVE_SYNC();");
+                // rows are the MFMA K dimension: A = t[row = 4m + lane/16][u = lane%16], B = g[row][w = lane%16][k]
+                for (int m = 0; m < 4; ++m) {
+                    o("{");
+                    o.ind++;
+                    o("const long br = blk * 16 + ", 4 * m, " + usub;");
+                    o("const bool bok = br < nrows && rl < ", p.mul_out, ";");
+                    o("const T gv = g[bok ? (size_t)br * DOUT + ", p.o, " + rl * ", n3, " + ", k, " : 0];");
+                    o("D", pi, " = MFMA(tw[(", 4 * m, " + usub) * 17 + rl], bok ? gv : (T)0, D", pi, ");");
+                    o.ind--;
+                    o("}");
+                }
+                o("__builtin_amdgcn_sched_barrier(0);");
+                o.ind--;
+                o("}");
+            }
+        }
+        o.ind--;
+        o("}");
+    }
+    o.ind--;
+    o("}");  // row blocks
+    // lane holds D[u = U(v)][w = lane % 16]
+    for (int pi : g.paths) {
+        const Path &p = P.paths[pi];
+        for (int v = 0; v < 4; ++v) {
+            const std::string u = uvb_u(f64, v);
+            o("if (", u, " < ", p.mul_in, " && rl < ", p.mul_out, ") ws[(size_t)chunk * WN + ", p.w_off, " + ", u, " * ", p.mul_out,
+              " + rl] = D", pi, "[", v, "];");
+        }
+    }
+    o.ind--;
+    o("}");
+    o("");
+}
+
+void emit_uvb_kernels(Out &o, const Plan &P)
+{
+    if (!P.uvb_ok) {
+        o("// uvw batched backward not generated: some multiplicity exceeds 16");
+        return;
+    }
+    o("#define WN ", P.w_numel, "L");
+    o("#define WAVE_SYNC() do { __builtin_amdgcn_fence(__ATOMIC_RELEASE, \"wavefront\"); "
+      "__builtin_amdgcn_wave_barrier(); __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, \"wavefront\"); } while (0)");
+    for (int gi = 0; gi < (int)P.uvb_x_groups.size(); ++gi) emit_uvb_xy_group(o, P, gi);
+    o("extern \"C\" __global__ void __launch_bounds__(256, 1) cgtp_tp_uvw_bwd_xy(const T* __restrict__ x, "
+      "const T* __restrict__ y, const T* __restrict__ w, const T* __restrict__ g, T* __restrict__ dx, "
+      "T* __restrict__ dy, long nrows, long nblocks, int group)");
+    o("{");
+    o.ind++;
+    o("__shared__ T dyl[", 4 * 16 * P.d_sh, "];");
+    o("const long blk = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const int wv = threadIdx.x >> 6;");
+    o("const int lane = threadIdx.x & 63;");
+    o("if (blk >= nblocks) return;");
+    o("switch (group) {");
+    for (int gi = 0; gi < (int)P.uvb_x_groups.size(); ++gi)
+        o("case ", gi, ": uvbx_g", gi, "(blk, wv, lane, x, y, w, g, dx, dy, nrows, dyl); break;");
+    o("default: break;");
+    o("}");
+    o.ind--;
+    o("}");
+    o("");
+    for (int gi = 0; gi < (int)P.uvb_w_groups.size(); ++gi) emit_uvb_w_group(o, P, gi);
+    o("// one wave per (path group, chunk of row blocks), chunk-major within a group");
+    o("extern \"C\" __global__ void __launch_bounds__(256, 1) cgtp_tp_uvw_bwd_w(const T* __restrict__ x, "
+      "const T* __restrict__ y, const T* __restrict__ g, T* __restrict__ ws, long nrows, long nblocks, long bpc, "
+      "long nchunks, long nwaves)");
+    o("{");
+    o.ind++;
+    o("__shared__ T tl[", 4 * 16 * 17, "];");
+    o("const long wave = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const int wv = threadIdx.x >> 6;");
+    o("const int lane = threadIdx.x & 63;");
+    o("if (wave >= nwaves) return;");
+    o("const int group = (int)(wave / nchunks);");
+    o("const long chunk = wave - (long)group * nchunks;");
+    o("switch (group) {");
+    for (int gi = 0; gi < (int)P.uvb_w_groups.size(); ++gi)
+        o("case ", gi, ": uvbw_g", gi, "(chunk, wv, lane, x, y, g, ws, nrows, nblocks, bpc, tl); break;");
+    o("default: break;");
+    o("}");
+    o.ind--;
+    o("}");
+    o("");
+    o("// dW[i] = sum over chunks of the partials, in chunk order");
+    o("extern \"C\" __global__ void __launch_bounds__(256) cgtp_reduce_chunks(const T* __restrict__ ws, long nchunks, "
+      "T* __restrict__ out)");
+    o("{");
+    o.ind++;
+    o("const long i = (long)blockIdx.x * 256 + threadIdx.x;");
+    o("if (i >= WN) return;");
+    o("T s = (T)0;");
+    o("for (long c = 0; c < nchunks; ++c) s += ws[(size_t)c * WN + i];");
+    o("out[i] = s;");
+    o.ind--;
+    o("}");
+    o("");
+}
+
 }  // namespace
+
+std::string generate_uvw_backward_source(const Plan &P)
+{
+    Out o;
+    o("// @@section common");
+    emit_preamble(o, P);
+    emit_mfma_defs(o, P);
+    o("// @@section cgtp_tp_uvw_bwd");
+    emit_uvb_kernels(o, P);
+    return o.s.str();
+}
 
 std::string generate_radial_source(const Plan &P, int R)
 {

@@ -130,6 +130,7 @@ const Plan::Loaded &module_for_current_device(Plan &P)
     } else {
         check(hipModuleGetFunction(&L.tp_uvw, L.module, "cgtp_tp_uvw"), "hipModuleGetFunction(tp_uvw)");
         check(hipModuleGetFunction(&L.conv_uvw, L.module, "cgtp_conv_uvw"), "hipModuleGetFunction(conv_uvw)");
+
     }
     return P.loaded.emplace(dev, L).first->second;
 }
@@ -165,6 +166,41 @@ hipFunction_t radial_function_for_current_device(Plan &P, int R)
     check(hipModuleGetFunction(&f, m, "cgtp_conv_fwd_radial"), "hipModuleGetFunction(conv_fwd_radial)");
     rv.loaded[dev] = {m, f};
     return f;
+}
+
+}  // namespace cgtp
+
+namespace cgtp {
+
+static void uvb_locked(Plan &P)
+{
+    if (P.uvb.code.empty()) {
+        P.uvb.source = generate_uvw_backward_source(P);
+        P.uvb.code = compile_source(P.uvb.source);
+    }
+}
+
+const std::string &prepare_uvw_backward(Plan &P)
+{
+    std::lock_guard<std::mutex> lock(P.mu);
+    uvb_locked(P);
+    return P.uvb.source;
+}
+
+const Plan::UvwBackward::Fns &uvw_backward_for_current_device(Plan &P)
+{
+    int dev = 0;
+    check(hipGetDevice(&dev), "hipGetDevice");
+    std::lock_guard<std::mutex> lock(P.mu);
+    uvb_locked(P);
+    auto it = P.uvb.loaded.find(dev);
+    if (it != P.uvb.loaded.end()) return it->second;
+    Plan::UvwBackward::Fns F;
+    check(hipModuleLoadData(&F.module, P.uvb.code.data()), "hipModuleLoadData");
+    check(hipModuleGetFunction(&F.xy, F.module, "cgtp_tp_uvw_bwd_xy"), "hipModuleGetFunction(uvw_bwd_xy)");
+    check(hipModuleGetFunction(&F.w, F.module, "cgtp_tp_uvw_bwd_w"), "hipModuleGetFunction(uvw_bwd_w)");
+    check(hipModuleGetFunction(&F.reduce, F.module, "cgtp_reduce_chunks"), "hipModuleGetFunction(reduce)");
+    return P.uvb.loaded.emplace(dev, F).first->second;
 }
 
 }  // namespace cgtp

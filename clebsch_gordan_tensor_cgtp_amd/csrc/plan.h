@@ -65,6 +65,9 @@ struct Plan {
     std::vector<Group> uvw_groups;  // uvw batched product: one launch per group of output slots
     std::vector<Group> dbl_groups;  // double backward, sender pass: one launch per group, in order
     std::vector<Group> uvc_groups;  // uvw convolution: one launch per group, in order (a slot may span groups)
+    std::vector<Group> uvb_x_groups;  // uvw batched backward, dx/dy: one input block per group (launched in order)
+    std::vector<Group> uvb_w_groups;  // uvw batched backward, dW partials: up to 16 paths per group
+    bool uvb_ok = false;            // uvw batched backward supported (every mul_in, mul_out <= 16)
     int fwd_waves_per_eu = 4;       // occupancy target given to the compiler (min waves per SIMD)
     int bwd_waves_per_eu = 4;
     int uvw_waves_per_eu = 2;
@@ -94,6 +97,17 @@ struct Plan {
         std::map<int, std::pair<hipModule_t, hipFunction_t>> loaded;  // per device
     };
     std::map<int, Radial> radial;
+
+    // uvw batched backward: its own module, built on first use (large at high L).
+    struct UvwBackward {
+        std::string source;
+        std::vector<char> code;
+        struct Fns {
+            hipModule_t module = nullptr;
+            hipFunction_t xy = nullptr, w = nullptr, reduce = nullptr;
+        };
+        std::map<int, Fns> loaded;  // per device
+    } uvb;
 };
 
 // planner.cpp
@@ -112,5 +126,8 @@ std::vector<char> compile_source(const std::string &source);
 const Plan::Loaded &module_for_current_device(Plan &plan);
 hipFunction_t radial_function_for_current_device(Plan &plan, int R);
 const std::string &prepare_radial(Plan &plan, int R);
+std::string generate_uvw_backward_source(const Plan &plan);
+const std::string &prepare_uvw_backward(Plan &plan);
+const Plan::UvwBackward::Fns &uvw_backward_for_current_device(Plan &plan);
 
 }  // namespace cgtp

@@ -255,6 +255,12 @@ static void finish_group(Group &g)
     g.tiles = (g.mul + g.ct - 1) / g.ct;
 }
 
+static int getenv_int(const char *name, int dflt)
+{
+    const char *e = std::getenv(name);
+    return e && *e ? std::max(1, std::atoi(e)) : dflt;
+}
+
 void schedule(Plan &P)
 {
     if (const char *e = std::getenv("CGTP_BWD_PREFETCH")) P.bwd_prefetch = std::atoi(e);
@@ -395,6 +401,31 @@ void schedule(Plan &P)
             std::vector<Group> wide;
             if (make(122880, wide) == 1) P.uvc_groups = wide;
         }
+    }
+
+    // uvw batched backward: dx/dy groups are the input blocks (each block's dx is complete in one
+    // launch; dY is accumulated over the launches in order); dW groups pack 8 paths (a 16x16
+    // MFMA accumulator, 4 registers per lane, per path; 16 spilled at l = 7).
+    P.uvb_x_groups.clear();
+    P.uvb_w_groups.clear();
+    P.uvb_ok = P.mode == CGTP_UVW;
+    if (P.mode == CGTP_UVW) {
+        for (const Path &p : P.paths) P.uvb_ok = P.uvb_ok && p.mul_in <= 16 && p.mul_out <= 16;
+        for (int b = 0; b < (int)P.ins.size(); ++b) {
+            Group g;
+            for (int i = 0; i < (int)P.paths.size(); ++i)
+                if (P.paths[i].i1 == b) g.paths.push_back(i);
+            if (!g.paths.empty()) P.uvb_x_groups.push_back(g);
+        }
+        Group cur;
+        for (int i = 0; i < (int)P.paths.size(); ++i) {
+            if ((int)cur.paths.size() == (getenv_int("CGTP_UVB_W_PATHS", 8))) {
+                P.uvb_w_groups.push_back(cur);
+                cur = Group();
+            }
+            cur.paths.push_back(i);
+        }
+        if (!cur.paths.empty()) P.uvb_w_groups.push_back(cur);
     }
 
     // Sender-pass groups (backward, and the double backward's d/dx, d/dy, d/dW):

@@ -34,7 +34,8 @@
  * Memory and streams: every device buffer is owned by the caller, must be a
  * device pointer to contiguous row-major data of the plan's dtype, aligned
  * to its element size, and outputs must not alias inputs.  The library never allocates,
- * frees or synchronises device memory.  `stream` is a hipStream_t (NULL =
+ * frees or synchronises device memory; the one entry point that needs
+ * temporary memory (cgtp_tp_backward, uvw) takes it from the caller.  `stream` is a hipStream_t (NULL =
  * the default stream); all work is enqueued on it asynchronously.
  * Index arrays are int32 and N, E < 2^31.
  *
@@ -129,18 +130,32 @@ cgtp_status cgtp_tp_forward(const cgtp_plan *plan, int64_t B, const void *x, con
 
 /*
  * Batched tensor product backward, use case A (sciencestack.ai page, Abstract:
- * gradient kernels; Figure 4A): with g = grad_out [B][d_out], per row b
- *   grad_w[b, w_p + u] = sum_{ijk} C x[b,u,i] y[b,j] g[b,u,k]
- *   grad_y[b, b_p + j] = sum_p sum_u W[b,p,u] sum_{ik} C x[b,u,i] g[b,u,k]
- *   grad_x[b, a_p + u(2l1+1) + i] = sum_p W[b,p,u] sum_{jk} C y[b,j] g[b,u,k]
- * (the convolution backward with every row its own sender and receiver).
- * uvu only (shared_weights must be 0); uvw returns CGTP_ERR_UNSUPPORTED.  Any
- * of grad_x / grad_y / grad_w may be NULL to skip it; outputs are overwritten,
- * one owner per element, no atomics, bitwise deterministic.  B = 0 is a no-op.
+ * gradient kernels; Figure 4A): with g = grad_out [B][d_out],
+ *   uvu (shared_weights = 0), per row b:
+ *     grad_w[b, w_p + u] = sum_{ijk} C x[b,u,i] y[b,j] g[b,u,k]
+ *     grad_y[b, b_p + j] = sum_p sum_u W[b,p,u] sum_{ik} C x[b,u,i] g[b,u,k]
+ *     grad_x[b, a_p + u(2l1+1) + i] = sum_p W[b,p,u] sum_{jk} C y[b,j] g[b,u,k]
+ *   uvw (shared_weights = 1, every mul_in and mul_out <= 16, else
+ *   CGTP_ERR_UNSUPPORTED), with G_p[b,u,k] = sum_w W_p[u][w] g[b, o_p + w(2l3+1) + k]:
+ *     grad_x[b, a_p + u(2l1+1) + i] = sum_p sum_{jk} C y[b,j] G_p[b,u,k]
+ *     grad_y[b, b_p + j] = sum_p sum_u sum_{ik} C x[b,u,i] G_p[b,u,k]
+ *     grad_w[w_p + u*mul_out + w] = sum_b sum_{ijk} C x[b,u,i] y[b,j] g[b, o_p + w(2l3+1) + k]
+ *   The shared-weight gradient sums over all rows: per-chunk partials go to
+ *   the caller's `workspace` (workspace_bytes >= cgtp_tp_backward_workspace_size;
+ *   0 for uvu, where workspace may be NULL) and are summed in chunk order.
+ * Any of grad_x / grad_y / grad_w may be NULL to skip it; outputs are
+ * overwritten, one owner per element, no atomics, bitwise deterministic.
+ * B = 0 is a no-op.
  */
+cgtp_status cgtp_tp_backward_workspace_size(const cgtp_plan *plan, int64_t B, size_t *bytes);
+/* uvw: the backward kernels form their own module, generated and compiled on the first call;
+ * this builds it ahead of time (host only) and cgtp_plan_uvw_backward_source returns its source
+ * (owned by the plan; NULL before it exists). */
+cgtp_status cgtp_plan_uvw_backward_prepare(const cgtp_plan *plan);
+const char *cgtp_plan_uvw_backward_source(const cgtp_plan *plan);
 cgtp_status cgtp_tp_backward(const cgtp_plan *plan, int64_t B, const void *x, const void *y, const void *w,
                              int shared_weights, const void *grad_out, void *grad_x, void *grad_y, void *grad_w,
-                             void *stream);
+                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Fused convolution forward, use case B (sciencestack.ai page, Figure 4B;

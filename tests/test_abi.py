@@ -146,10 +146,22 @@ def test_call_errors_before_any_gpu_work():
     assert L.cgtp_plan_create(b"16x0e", b"1x0e", b"32x0e", 1, 0, ctypes.byref(wide)) == 0
     assert L.cgtp_tp_forward(wide, 4, fake, fake, fake, 1, ctypes.c_void_p(1 << 26), s) == unsup
     # batched backward: uvu needs shared=0; the uvw backward is not built
-    assert L.cgtp_tp_backward(plan.handle, 4, fake, fake, fake, 1, fake, fake, fake, fake, s) == inval
-    assert L.cgtp_tp_backward(uvw.handle, 4, fake, fake, fake, 1, fake, fake, fake, fake, s) == unsup
-    assert L.cgtp_tp_backward(plan.handle, 4, fake, fake, fake, 0, null, fake, null, null, s) == inval
-    assert L.cgtp_tp_backward(plan.handle, 0, null, null, null, 0, null, null, null, null, s) == 0
+    z = ctypes.c_size_t(0)
+    assert L.cgtp_tp_backward(plan.handle, 4, fake, fake, fake, 1, fake, fake, fake, fake, null, z, s) == inval
+    assert L.cgtp_tp_backward(uvw.handle, 4, fake, fake, fake, 0, fake, fake, fake, fake, null, z, s) == inval
+    assert L.cgtp_tp_backward(plan.handle, 4, fake, fake, fake, 0, null, fake, null, null, null, z, s) == inval
+    assert L.cgtp_tp_backward(plan.handle, 0, null, null, null, 0, null, null, null, null, null, z, s) == 0
+    # uvw: the shared-weight gradient needs the workspace, sized by the query
+    nb = ctypes.c_size_t()
+    assert L.cgtp_tp_backward_workspace_size(uvw.handle, 50_000, ctypes.byref(nb)) == 0
+    nblocks = (50_000 + 15) // 16
+    bpc = -(-nblocks // 256)
+    assert nb.value == -(-nblocks // bpc) * uvw.weight_numel * 4   # at most 256 chunks of 16-row blocks
+    assert L.cgtp_tp_backward_workspace_size(plan.handle, 50_000, ctypes.byref(nb)) == 0 and nb.value == 0
+    assert L.cgtp_tp_backward(uvw.handle, 4, fake, fake, fake, 1, ctypes.c_void_p(1 << 26), null, null,
+                              ctypes.c_void_p(1 << 28), null, z, s) == inval
+    assert L.cgtp_tp_backward(wide, 4, fake, fake, fake, 1, fake, fake, fake, fake, null, z, s) == unsup
+    assert L.cgtp_plan_destroy(wide) == 0
     assert L.cgtp_plan_destroy(wide) == 0
     assert L.cgtp_tp_forward(plan.handle, 4, fake, fake, fake, 1, fake, s) == inval   # uvu needs shared=0
     assert L.cgtp_tp_forward(uvw.handle, 4, fake, fake, fake, 0, fake, s) == inval    # uvw needs shared=1

@@ -291,3 +291,71 @@ def test_tp_forward_uvw_full_size_sampled(device):
     want = loops.uvw_forward(loops.Tables(prob), x[rows].astype(np.float64),
                              osh.real_sh_all(spec.lmax_sh, vec[rows].astype(np.float64)), w.astype(np.float64))
     assert rel_l2(out.cpu().numpy()[rows], want) <= TOL["f32"]
+
+
+# --------------------------------------------------------------------------- uvw batched backward
+
+UVB_CASES = [
+    ("3x0e+2x1o+2x2e", 2, "2x0e+3x1o+2x2e+1x1e+2x2o", 1000, ("f32", "f64")),
+    ("16x0e+16x1o+16x2e", 2, "16x0e+16x1o+16x2e+16x1e+16x2o", 777, ("f32", "f64")),
+    ("5x0e+3x1o+7x2e+2x3o", 3, "6x0e+4x1o+3x2e+2x1e+1x3o+9x2o", 301, ("f32",)),
+    ("+".join(f"16x{l}{'e' if l % 2 == 0 else 'o'}" for l in range(6)), 5,
+     "+".join(f"16x{l}{'e' if l % 2 == 0 else 'o'}" for l in range(6)), 200, ("f32",)),
+]
+
+
+def _uvb_run(device, ins, lmax, outs, B, dtype, seed=61, need=(True, True, True)):
+    import torch
+    prob = oirreps.build_problem(ins, oirreps.sh_irreps(lmax), outs, "uvw")
+    plan = cg.plan_create(ins, oirreps.sh_irreps(lmax), outs, "uvw", dtype)
+    st = synth.streams(seed)
+    npdt = np.float32 if dtype == "f32" else np.float64
+    x = synth.normal(st["x"], (B, prob.d_in), dtype=npdt)
+    vec = synth.normal(st["vec"], (B, 3), dtype=npdt)
+    w = synth.normal(st["w"], (prob.weight_numel,), 0.25, dtype=npdt)
+    g = synth.normal(st["sample"], (B, prob.d_out), dtype=npdt)
+    t = lambda a: torch.from_numpy(a).to(device)
+    y = cg.spherical_harmonics(lmax, t(vec))
+    got = cg.tp_backward(plan, t(x), y, t(w), t(g), need=need)
+    torch.cuda.synchronize()
+    return prob, plan, x, vec, w, g, got
+
+
+@pytest.mark.parametrize("ins,lmax,outs,B,dtype", [(c[0], c[1], c[2], c[3], d) for c in UVB_CASES for d in c[4]])
+def test_tp_backward_uvw(device, ins, lmax, outs, B, dtype):
+    prob, plan, x, vec, w, g, (gx, gy, gw) = _uvb_run(device, ins, lmax, outs, B, dtype)
+    y = osh.real_sh_all(lmax, vec.astype(np.float64))
+    f64 = lambda a: np.asarray(a, np.float64)
+    dx, dy, dw = loops.uvw_backward(loops.Tables(prob), f64(x), y, f64(w), f64(g), np.arange(B), np.arange(B))
+    assert rel_l2(gx.cpu().numpy(), dx) <= TOL[dtype]
+    assert rel_l2(gy.cpu().numpy(), dy) <= TOL[dtype]
+    assert rel_l2(gw.cpu().numpy(), dw) <= TOL[dtype]
+
+
+def test_tp_backward_uvw_outputs_and_repeat_bitwise(device):
+    import torch
+    ins, lmax, outs = "16x0e+16x1o+16x2e", 2, "16x0e+16x1o+16x2e+16x1e+16x2o"
+    full = _uvb_run(device, ins, lmax, outs, 4097, "f32")[-1]
+    again = _uvb_run(device, ins, lmax, outs, 4097, "f32")[-1]
+    for a, b in zip(full, again):
+        assert torch.equal(a, b)
+    for k in range(3):
+        part = _uvb_run(device, ins, lmax, outs, 4097, "f32", need=tuple(i == k for i in range(3)))[-1]
+        assert torch.equal(part[k], full[k])
+        assert all(part[i] is None for i in range(3) if i != k)
+
+
+def test_tp_backward_uvw_full_size_sampled(device):
+    """The high-L batch (50,000 rows, l <= 7): dx, dY on sampled rows, dW over every row."""
+    spec = synth.TP_HIGHL
+    prob = oirreps.build_problem(spec.in_irreps, oirreps.sh_irreps(spec.lmax_sh), spec.out_irreps, "uvw")
+    B = spec.batch
+    _, plan, x, vec, w, g, (gx, gy, gw) = _uvb_run(device, spec.in_irreps, spec.lmax_sh, spec.out_irreps, B, "f32",
+                                                   seed=62)
+    rows = np.unique(np.concatenate([np.random.default_rng(63).choice(B, 200, replace=False), [0, B - 1]]))
+    f64 = lambda a: np.asarray(a, np.float64)
+    y = osh.real_sh_all(spec.lmax_sh, vec.astype(np.float64))
+    dx, dy, dw = loops.uvw_backward(loops.Tables(prob), f64(x), y, f64(w), f64(g), rows, np.arange(B))
+    assert rel_l2(gx.cpu().numpy()[rows], dx) <= TOL["f32"]
+    assert rel_l2(gy.cpu().numpy()[rows], dy) <= TOL["f32"]
+    assert rel_l2(gw.cpu().numpy(), dw) <= TOL["f32"]
