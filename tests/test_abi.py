@@ -162,7 +162,6 @@ def test_call_errors_before_any_gpu_work():
                               ctypes.c_void_p(1 << 28), null, z, s) == inval
     assert L.cgtp_tp_backward(wide, 4, fake, fake, fake, 1, fake, fake, fake, fake, null, z, s) == unsup
     assert L.cgtp_plan_destroy(wide) == 0
-    assert L.cgtp_plan_destroy(wide) == 0
     assert L.cgtp_tp_forward(plan.handle, 4, fake, fake, fake, 1, fake, s) == inval   # uvu needs shared=0
     assert L.cgtp_tp_forward(uvw.handle, 4, fake, fake, fake, 0, fake, s) == inval    # uvw needs shared=1
     assert L.cgtp_spherical_harmonics(8, 0, 4, fake, fake, s) == inval
