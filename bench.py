@@ -544,7 +544,7 @@ def bench_tp(a, spec, device):
     npdt = np.float32 if a.dtype == "f32" else np.float64
     es = 4 if a.dtype == "f32" else 8
     B = spec.batch
-    backward = a.backward and spec.mode == "uvu"
+    backward = a.backward
     x = torch.from_numpy(synth.normal(st["x"], (B, plan.d_x), dtype=npdt)).to(device)
     vec = torch.from_numpy(synth.normal(st["vec"], (B, 3), dtype=npdt)).to(device)
     wshape = (plan.weight_numel,) if spec.mode == "uvw" else (B, plan.weight_numel)
@@ -553,6 +553,10 @@ def bench_tp(a, spec, device):
     y = cg.spherical_harmonics(spec.lmax_sh, vec)
     out = torch.empty((B, plan.d_out), dtype=plan.torch_dtype, device=device)
     grads = (torch.empty_like(x), torch.empty_like(y), torch.empty_like(w)) if backward else None
+    ws = None
+    if backward and spec.mode == "uvw":
+        plan.uvw_backward_source()  # JIT outside the timed region
+        ws = torch.empty(cg.tp_backward_workspace_size(plan, B) // es, dtype=plan.torch_dtype, device=device)
 
     def step(ev=None):
         if ev is not None:
@@ -561,7 +565,7 @@ def bench_tp(a, spec, device):
         if ev is not None:
             ev[1].record()
         if backward:
-            cg.tp_backward(plan, x, y, w, g, *grads)
+            cg.tp_backward(plan, x, y, w, g, *grads, workspace=ws)
         if ev is not None:
             ev[2].record()
 
@@ -583,9 +587,13 @@ def bench_tp(a, spec, device):
     if spec.mode == "uvw":
         flops = tp_flops(paths, None, spec.mode) * B
         peak = 157.3 if a.dtype == "f32" else 78.6
-        achieved = flops / (fwd_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "cgtp_tp_uvw", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": None, "flops_per_launch": flops, "avg_launch_ms": fwd_ms}
+        # fixed counting convention: the backward (dx, dY, dW) counts 3x the forward's flops
+        dom = ("cgtp_tp_uvw_bwd", bwd_ms, 3 * flops) if backward and bwd_ms >= fwd_ms else ("cgtp_tp_uvw", fwd_ms, flops)
+        achieved = dom[2] / (dom[1] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom[0], "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None, "flops_per_launch": dom[2], "avg_launch_ms": dom[1]}
+        if backward:
+            config["bwd_ms"] = bwd_ms
     else:
         # uvu is HBM-bound: every row reads x, y, W once and writes out once (backward: reads
         # x, y, W, grad_out, writes grad_x, grad_y, grad_w)
