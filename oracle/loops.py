@@ -268,3 +268,27 @@ def conv_forward_radial_rows(tab: Tables, row_ptr, col, x, y, rho, theta, rows, 
     w = np.asarray(rho, np.float64)[eidx] @ np.asarray(theta, np.float64)
     return uvu_forward(tab, sub_ptr, np.asarray(col)[eidx], np.asarray(x, np.float64),
                        np.asarray(y, np.float64)[eidx], w, n_threads)
+
+
+def conv_backward_uvw_rows(tab: Tables, row_ptr, col, x, y, w, g, edges, senders, n_threads=None):
+    """uvw convolution backward on a sample: dY of the edges ``edges``, dx of the nodes
+    ``senders`` (all their edges) and dW over every edge, from the explicit uvw backward loops
+    applied to the edges as rows (x gathered by sender, g by receiver)."""
+    row_ptr = np.asarray(row_ptr, dtype=np.int64)
+    col = np.asarray(col, dtype=np.int64)
+    senders = np.asarray(senders, dtype=np.int64)
+    dst = np.repeat(np.arange(len(row_ptr) - 1), np.diff(row_ptr))
+    E = len(col)
+    xe, ge = np.asarray(x)[col], np.asarray(g)[dst]
+    order = np.argsort(col, kind="stable")
+    starts = np.searchsorted(col[order], senders, side="left")
+    ends = np.searchsorted(col[order], senders, side="right")
+    sedges = np.concatenate([order[a:b] for a, b in zip(starts, ends)]) if len(senders) else np.zeros(0, np.int64)
+    rows = np.concatenate([np.asarray(edges, np.int64), sedges])
+    dxr, dyr, dw = uvw_backward(tab, xe, np.asarray(y), np.asarray(w), ge, rows, np.arange(E), n_threads)
+    dy = dyr[:len(edges)]
+    dxs = dxr[len(edges):]
+    dx = np.zeros((len(senders), tab.prob.d_in))
+    seg = np.repeat(np.arange(len(senders)), ends - starts)
+    np.add.at(dx, seg, dxs)
+    return dx, dy, dw

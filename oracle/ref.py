@@ -100,6 +100,18 @@ def conv_forward(prob: Problem, row_ptr, col, x, y, w):
     return out
 
 
+def conv_backward_uvw(prob: Problem, row_ptr, col, x, y, w, g):
+    """Gradients of sum(g * conv_forward(...)) for a uvw plan (shared W): every edge is a row of
+    the batched product with x[col[e]], y[e] and g[receiver(e)]; dY is that row's gradient, dW the
+    sum over the edges and dx the sum over each sender's edges."""
+    x, y, w, g = (np.asarray(a, np.float64) for a in (x, y, w, g))
+    col = np.asarray(col, np.int64)
+    dxs, dy, dw = tp_backward(prob, x[col], y, w, g[receivers_of(row_ptr)])
+    dx = np.zeros_like(x)
+    np.add.at(dx, col, dxs)
+    return dx, dy, dw
+
+
 def conv_backward(prob: Problem, row_ptr, col, x, y, w, g):
     """Gradients of sum(g * conv_forward(...)) with respect to x, y and W.
 

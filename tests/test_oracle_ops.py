@@ -555,3 +555,30 @@ def test_cpu_loops_uvw_backward_match_numpy(in_f32):
     assert np.allclose(dx, want[0][rows], atol=1e-12)
     assert np.allclose(dy, want[1][rows], atol=1e-12)
     assert np.allclose(dw, want[2], atol=1e-11)
+
+
+
+def test_uvw_conv_backward_matches_autograd_and_loops():
+    import torch
+    prob = _uvw_conv_problem()
+    rng = np.random.default_rng(25)
+    row_ptr, col = small_graph(rng, 7, 27)
+    x = rng.standard_normal((7, prob.d_in))
+    y = rng.standard_normal((27, prob.d_sh))
+    w = rng.standard_normal(prob.weight_numel)
+    g = rng.standard_normal((7, prob.d_out))
+    t = torch.from_numpy(dense_tensor(prob))
+    dst = torch.from_numpy(ref.receivers_of(row_ptr))
+    colt = torch.from_numpy(np.asarray(col, np.int64))
+    X, Y, W = (torch.tensor(a, requires_grad=True) for a in (x, y, w))
+    msg = torch.einsum("abvo,ea,eb,v->eo", t, X[colt], Y, W)
+    out = torch.zeros(7, prob.d_out, dtype=torch.float64).index_add(0, dst, msg)
+    want = torch.autograd.grad((torch.from_numpy(g) * out).sum(), (X, Y, W))
+    got = ref.conv_backward_uvw(prob, row_ptr, col, x, y, w, g)
+    for a, b in zip(got, want):
+        assert np.allclose(a, b.numpy(), atol=1e-11)
+    edges, senders = np.array([3, 0, 26, 11]), np.array([6, 1, 4])
+    dx, dy, dw = loops.conv_backward_uvw_rows(loops.Tables(prob), row_ptr, col, x, y, w, g, edges, senders)
+    assert np.allclose(dx, got[0][senders], atol=1e-12)
+    assert np.allclose(dy, got[1][edges], atol=1e-12)
+    assert np.allclose(dw, got[2], atol=1e-11)
