@@ -1144,30 +1144,13 @@ void emit_uvw_kernel(Out &o, const Plan &P)
 // groups (later launches) add, so every sum has a fixed order.
 int uvc_mu_pad(const Path &p) { return (p.mul_in + 3) / 4 * 4; }
 
-void emit_uvc_group(Out &o, const Plan &P, int gi)
+// uvw convolution, edge stream of one path group: each wave accumulates the unweighted per-path
+// sums T_p[u][k] of its receivers' edges (rows r of the tile `tile`) and stages them in LDS as
+// [p,k][u][row] at the offsets `loff`.  Shared by the forward and the dW pass.
+void emit_uvc_phase_a(Out &o, const Plan &P, const Group &g, std::map<int, int> &loff)
 {
-    const Group &g = P.uvc_groups[gi];
-    const bool f64 = P.dtype == CGTP_F64;
     Touch t = touched(P, g.paths);
-    auto first_group_of_slot = [&](int q) {
-        for (int k = 0; k < (int)P.uvc_groups.size(); ++k)
-            for (int pi : P.uvc_groups[k].paths)
-                if (P.paths[pi].slot == q) return k;
-        return -1;
-    };
-    // LDS offset (in elements) of each path's T block
-    std::map<int, int> loff;
-    int lds_elems = 0;
-    for (int pi : g.paths) {
-        loff[pi] = lds_elems;
-        lds_elems += 16 * uvc_mu_pad(P.paths[pi]) * n_of(P.paths[pi].l3);
-    }
-    o("__device__ __forceinline__ void uvc_g", gi,
-      "(long tile, int wv, int lane, const int* __restrict__ row_ptr, const int* __restrict__ col, "
-      "const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows, "
-      "const int* __restrict__ order, T* lds)");
-    o("{");
-    o.ind++;
+    const bool f64 = P.dtype == CGTP_F64;
     o("const int slot = lane >> ", log2i(g.ct), ";");
     o("const int ul = lane & ", g.ct - 1, ";");
     const int nw = 16 / P.uvc_rpw;  // waves per workgroup
@@ -1270,6 +1253,34 @@ void emit_uvc_group(Out &o, const Plan &P, int gi)
     o("}");  // channel tiles
     o.ind--;
     o("}");  // receivers of the wave
+}
+
+void emit_uvc_group(Out &o, const Plan &P, int gi)
+{
+    const Group &g = P.uvc_groups[gi];
+    const bool f64 = P.dtype == CGTP_F64;
+    Touch t = touched(P, g.paths);
+    auto first_group_of_slot = [&](int q) {
+        for (int k = 0; k < (int)P.uvc_groups.size(); ++k)
+            for (int pi : P.uvc_groups[k].paths)
+                if (P.paths[pi].slot == q) return k;
+        return -1;
+    };
+    // LDS offset (in elements) of each path's T block
+    std::map<int, int> loff;
+    int lds_elems = 0;
+    for (int pi : g.paths) {
+        loff[pi] = lds_elems;
+        lds_elems += 16 * uvc_mu_pad(P.paths[pi]) * n_of(P.paths[pi].l3);
+    }
+    o("__device__ __forceinline__ void uvc_g", gi,
+      "(long tile, int wv, int lane, const int* __restrict__ row_ptr, const int* __restrict__ col, "
+      "const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows, "
+      "const int* __restrict__ order, T* lds)");
+    o("{");
+    o.ind++;
+    const int nw = 16 / P.uvc_rpw;  // waves per workgroup
+    emit_uvc_phase_a(o, P, g, loff);
     o("__syncthreads();");
     // mixing on MFMA: items (slot q, 16-wide block of output channels), round-robin over the waves
     o("const int usub = lane >> 4;");
