@@ -34,7 +34,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c2uvw", "c1big"])
-    ap.add_argument("--backward", action="store_true", help="batched uvu workloads: also time cgtp_tp_backward")
+    ap.add_argument("--backward", action="store_true",
+                    help="batched workloads: also time cgtp_tp_backward; uvw convolution: also cgtp_conv_backward_ws")
     ap.add_argument("--dtype", default="f32", choices=["f32", "f64"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seed", type=int, default=0)
@@ -202,9 +203,11 @@ def uvw_conv_flops(plan, N, E):
     return E * sparse, N * dense
 
 
-def cpu_baseline_uvw_conv(plan_prob, spec, seed, host_graph, max_seconds=30.0):
+def cpu_baseline_uvw_conv(plan_prob, spec, seed, host_graph, max_seconds=30.0, backward=False):
     """The oracle's explicit uvw loops on every edge of a contiguous receiver slice (~5% of the
-    edges), summed per receiver; random values (timing only).  Rate = slice edges per second."""
+    edges), summed per receiver; with ``backward`` also the explicit uvw backward loops on the
+    slice's edges as rows (dx and dY per edge, dW over the slice).  Random values (timing only).
+    Rate = slice edges per second."""
     from oracle import irreps as oirreps
     from oracle import loops
     row_ptr, col = (np.asarray(a, dtype=np.int64) for a in host_graph)
@@ -221,61 +224,105 @@ def cpu_baseline_uvw_conv(plan_prob, spec, seed, host_graph, max_seconds=30.0):
     w = rng.standard_normal(prob.weight_numel)
     rows = np.arange(start, stop)
     n_e = int(row_ptr[stop] - row_ptr[start])
+    edges = np.arange(row_ptr[start], row_ptr[stop])
+    dst = np.repeat(np.arange(N), np.diff(row_ptr))
+    g = rng.standard_normal((N, prob.d_out))
     t0 = time.perf_counter()
     reps = 0
     while True:
         loops.conv_forward_uvw_rows(tab, row_ptr, col, x, y, w, rows, threads)
+        if backward:
+            xe, ye, ge = x[col[edges]], y[edges], g[dst[edges]]
+            loops.uvw_backward(tab, xe, ye, w, ge, np.arange(n_e), np.arange(n_e), threads)
         reps += 1
         el = time.perf_counter() - t0
         if el >= 10.0 or el >= max_seconds:
             break
+    what = "uvw convolution output and backward (dx, dY, dW) of the slice's edges" if backward else \
+        "uvw convolution output of that slice"
     return {"value": n_e * reps / el, "unit": "edges/s", "cores": threads, "kind": "oracle",
-            "sample": f"receivers [{start},{stop}) = {n_e} of {E} edges: uvw convolution output of that slice; "
+            "sample": f"receivers [{start},{stop}) = {n_e} of {E} edges: {what}; "
                       f"fp64 explicit loops, mean of {reps} rep(s)"}
 
 
 def bench_conv_uvw(a, spec, plan, d, host_graph, device):
+    """uvw convolution: one step = conv_forward (with --backward: + the backward's dx/dY pass,
+    G = W^T g and the unit-weight sender pass, and its dW pass, per-tile partials and their
+    reduction; both through cgtp_conv_backward_ws with a preallocated workspace)."""
     import torch
     from clebsch_gordan_tensor_cgtp_amd import binding as cg
     N, E = d["row_ptr"].shape[0] - 1, d["col"].shape[0]
+    es = 4 if a.dtype == "f32" else 8
     y = cg.spherical_harmonics(spec.lmax_sh, d["vec"])
     order = cg.graph_order(d["row_ptr"]) if not a.natural_order else None
     out = torch.empty((N, plan.d_out), dtype=plan.torch_dtype, device=device)
+    backward = a.backward
+    if backward:
+        plan.conv_uvw_backward_source(0)  # JIT outside the timed region
+        tr = cg.graph_transpose(d["row_ptr"], d["col"])
+        ws = torch.empty(cg.conv_backward_workspace_size(plan, N, E), dtype=torch.uint8, device=device)
+        gx, gy, gw = torch.empty_like(d["x"]), torch.empty_like(y), torch.empty_like(d["w"])
 
-    def step():
+    def step(ev):
+        ev[0].record()
         cg.conv_forward(plan, d["row_ptr"], d["col"], d["x"], y, d["w"], out=out, order=order)
+        ev[1].record()
+        if backward:
+            cg.conv_backward(plan, d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"], gx, gy, gw,
+                             need=(True, True, False), order=order, workspace=ws)
+            ev[2].record()
+            cg.conv_backward(plan, d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"], gx, gy, gw,
+                             need=(False, False, True), order=order, workspace=ws)
+            ev[3].record()
 
-    for _ in range(a.warmup):
-        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(max(a.steps, a.warmup))]
+    for k in range(a.warmup):
+        step(evs[k])
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     t0 = time.perf_counter()
-    ev[0].record()
-    for _ in range(a.steps):
-        step()
-    ev[1].record()
+    for k in range(a.steps):
+        step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = ev[0].elapsed_time(ev[1]) / a.steps
+    evs = evs[:a.steps]
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     sparse, dense = uvw_conv_flops(plan, N, E)
-    tflops = (sparse + dense) / (ms * 1e-3) / 1e12
+    # fixed counting convention of the backward: dx/dY pass = G (dense) + dx and dY contractions
+    # (2 x sparse); dW pass = T again (sparse) + the dW contraction (dense)
+    phases = [("cgtp_conv_uvw", ms, sparse + dense)]
+    config = {"workload": spec.name, "N": N, "E": E, "in_irreps": spec.in_irreps, "out_irreps": spec.out_irreps,
+              "sh_lmax": spec.lmax_sh, "paths": plan.num_paths, "d_out": plan.d_out,
+              "step": "conv_forward (uvw: shared weights, MFMA mixing per 16-receiver tile)",
+              "receiver_schedule": "natural" if a.natural_order else "heavy-first", "fwd_ms": ms}
+    if backward:
+        xy_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        w_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+        phases += [("dx/dY pass (cgtp_conv_uvw_bwd_g + cgtp_conv_uvw_bwd_xy)", xy_ms, dense + 2 * sparse),
+                   ("dW pass (cgtp_conv_uvw_bwd_w + cgtp_reduce_chunks)", w_ms, sparse + dense)]
+        config.update({"step": "conv_forward + conv_backward_ws (grad_x, grad_y, grad_w; uvw)",
+                       "bwd_xy_ms": xy_ms, "bwd_w_ms": w_ms, "bwd_ms": xy_ms + w_ms,
+                       "workspace_bytes": int(ws.numel())})
+    dom = max(phases, key=lambda p: p[1])
+    tflops = dom[2] / (dom[1] * 1e-3) / 1e12
+    peak = 157.3 if a.dtype == "f32" else 78.6
+    roof = {"bound": "alu", "kernel": dom[0], "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+            "frac": tflops / peak, "traffic": None, "flops_per_launch": dom[2], "avg_launch_ms": dom[1]}
+    if dom[0] == "cgtp_conv_uvw":
+        roof.update({"traffic": measured_traffic(plan, spec, a.dtype, "cgtp_conv_uvw"),
+                     "flops_per_launch": {"sparse_valu": sparse, "mixing_mfma": dense},
+                     "hbm_algorithmic_bytes_per_launch": (N + 1) * 4 + E * 4 + es * (
+                         N * plan.d_x + E * plan.d_sh + plan.weight_numel + N * plan.d_out)})
+    if backward:
+        roof["phases"] = [{"kernel": p[0], "avg_ms": p[1], "flops": p[2],
+                           "tflops": p[2] / (p[1] * 1e-3) / 1e12} for p in phases]
     line = {
         "metric": METRIC, "value": E / (wall / a.steps), "unit": "edges/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": wall * 1e3 / a.steps, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": a.dtype, "data": "synthetic",
-        "config": {"workload": spec.name, "N": N, "E": E, "in_irreps": spec.in_irreps, "out_irreps": spec.out_irreps,
-                   "sh_lmax": spec.lmax_sh, "paths": plan.num_paths, "d_out": plan.d_out,
-                   "step": "conv_forward (uvw: shared weights, MFMA mixing per 16-receiver tile)",
-                   "receiver_schedule": "natural" if a.natural_order else "heavy-first", "fwd_ms": ms},
-        "roofline": {"bound": "alu", "kernel": "cgtp_conv_uvw", "achieved": tflops, "peak": 157.3, "unit": "TFLOP/s",
-                     "frac": tflops / 157.3, "traffic": measured_traffic(plan, spec, a.dtype, "cgtp_conv_uvw"),
-                     "flops_per_launch": {"sparse_valu": sparse, "mixing_mfma": dense}, "avg_launch_ms": ms,
-                     "hbm_algorithmic_bytes_per_launch": (N + 1) * 4 + E * 4 + (4 if a.dtype == "f32" else 8) * (
-                         N * plan.d_x + E * plan.d_sh + plan.weight_numel + N * plan.d_out)},
+        "vs_baseline": None, "dtype": a.dtype, "data": "synthetic", "config": config, "roofline": roof,
         "cpu_baseline": None,
     }
     if not a.no_cpu:
-        line["cpu_baseline"] = cpu_baseline_uvw_conv(None, spec, a.seed, host_graph)
+        line["cpu_baseline"] = cpu_baseline_uvw_conv(None, spec, a.seed, host_graph, backward=backward)
     print(json.dumps(line), flush=True)
 
 

@@ -24,7 +24,11 @@ EXPORTS = ("cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info_get", "cgtp_
            "cgtp_graph_transpose", "cgtp_conv_backward", "cgtp_spherical_harmonics", "cgtp_last_error",
            "cgtp_conv_forward_ordered", "cgtp_graph_order", "cgtp_conv_double_backward", "cgtp_tp_backward",
            "cgtp_conv_forward_radial", "cgtp_plan_radial_prepare", "cgtp_plan_radial_source",
-           "cgtp_tp_backward_workspace_size", "cgtp_plan_uvw_backward_prepare", "cgtp_plan_uvw_backward_source")
+           "cgtp_tp_backward_workspace_size", "cgtp_plan_uvw_backward_prepare", "cgtp_plan_uvw_backward_source",
+           "cgtp_conv_backward_workspace_size", "cgtp_conv_backward_ws", "cgtp_plan_conv_uvw_backward_prepare",
+           "cgtp_plan_conv_uvw_backward_source")
+_STRING_RESULTS = ("cgtp_last_error", "cgtp_plan_source", "cgtp_plan_radial_source", "cgtp_plan_uvw_backward_source",
+                   "cgtp_plan_conv_uvw_backward_source")
 
 
 class CgtpError(RuntimeError):
@@ -61,6 +65,10 @@ def lib():
         L.cgtp_plan_source.restype = ctypes.c_char_p
         L.cgtp_plan_radial_source.restype = ctypes.c_char_p
         L.cgtp_plan_uvw_backward_source.restype = ctypes.c_char_p
+        L.cgtp_plan_conv_uvw_backward_source.restype = ctypes.c_char_p
+        L.cgtp_plan_conv_uvw_backward_source.argtypes = [vp, i32]
+        L.cgtp_conv_backward_workspace_size.argtypes = [vp, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+        L.cgtp_conv_backward_ws.argtypes = [vp, i64, i64] + [vp] * 14 + [ctypes.c_size_t, vp]
         L.cgtp_plan_source.argtypes = [vp]
         L.cgtp_plan_create.argtypes = [ctypes.c_char_p] * 3 + [ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp)]
         L.cgtp_plan_destroy.argtypes = [vp]
@@ -75,8 +83,7 @@ def lib():
         L.cgtp_conv_backward.argtypes = [vp, i64, i64] + [vp] * 13
         L.cgtp_spherical_harmonics.argtypes = [i32, ctypes.c_int, i64, vp, vp, vp]
         for name in EXPORTS:
-            if name not in ("cgtp_last_error", "cgtp_plan_source", "cgtp_plan_radial_source",
-                            "cgtp_plan_uvw_backward_source"):
+            if name not in _STRING_RESULTS:
                 getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -142,6 +149,12 @@ class Plan:
         """Generate and compile the uvw batched-backward module (host only); its source."""
         _check(lib().cgtp_plan_uvw_backward_prepare(self._h))
         return lib().cgtp_plan_uvw_backward_source(self._h).decode()
+
+    def conv_uvw_backward_source(self, module: int = 0) -> str:
+        """Generate and compile the uvw convolution-backward modules (host only); the source of
+        module 0 (G and dW kernels) or 1 (the unit-weight sender pass)."""
+        _check(lib().cgtp_plan_conv_uvw_backward_prepare(self._h))
+        return lib().cgtp_plan_conv_uvw_backward_source(self._h, module).decode()
 
     def radial_source(self, R: int) -> str:
         """Generate and compile the radial-projection module for R (host only); its source."""
@@ -321,23 +334,48 @@ def graph_transpose(row_ptr, col, t_row_ptr=None, t_edge=None, t_dst=None, strea
     return t_row_ptr, t_edge, t_dst
 
 
+def conv_backward_workspace_size(plan: Plan, N: int, E: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().cgtp_conv_backward_workspace_size(plan.handle, N, E, ctypes.byref(n)))
+    return n.value
+
+
 def conv_backward(plan: Plan, row_ptr, col, transpose, x, y, w, grad_out, grad_x=None, grad_y=None, grad_w=None,
-                  need=(True, True, True), stream=None):
-    """Returns (grad_x, grad_y, grad_w); entries not in ``need`` are None and not computed."""
+                  need=(True, True, True), order=None, workspace=None, stream=None):
+    """Returns (grad_x, grad_y, grad_w); entries not in ``need`` are None and not computed.
+    uvw plans: shared weights, a workspace (allocated here unless given) and an optional
+    receiver schedule ``order`` for the weight-gradient pass."""
     import torch
     N, E = row_ptr.shape[0] - 1, col.shape[0]
     dt = plan.torch_dtype
     dev = x.device
     t_row_ptr, t_edge, t_dst = transpose
+    uvw = plan.mode == "uvw"
+    wshape = (plan.weight_numel,) if uvw else (E, plan.weight_numel)
     if need[0] and grad_x is None:
         grad_x = torch.empty((N, plan.d_x), dtype=dt, device=dev)
     if need[1] and grad_y is None:
         grad_y = torch.empty((E, plan.d_sh), dtype=dt, device=dev)
     if need[2] and grad_w is None:
-        grad_w = torch.empty((E, plan.weight_numel), dtype=dt, device=dev)
+        grad_w = torch.empty(wshape, dtype=dt, device=dev)
     gx = grad_x if need[0] else None
     gy = grad_y if need[1] else None
     gw = grad_w if need[2] else None
+    if uvw:
+        nbytes = conv_backward_workspace_size(plan, N, E)
+        if workspace is None and nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        ws = ctypes.c_void_p(0) if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+        wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(lib().cgtp_conv_backward_ws(
+            plan.handle, N, E, _dev(row_ptr, "row_ptr", torch.int32), _dev(col, "col", torch.int32),
+            _ptr_or_null(order, "order", torch.int32, (N,)),
+            _dev(t_row_ptr, "t_row_ptr", torch.int32, (N + 1,)), _dev(t_edge, "t_edge", torch.int32, (E,)),
+            _dev(t_dst, "t_dst", torch.int32, (E,)), _dev(x, "x", dt, (N, plan.d_x)),
+            _dev(y, "y", dt, (E, plan.d_sh)), _dev(w, "w", dt, wshape), _dev(grad_out, "grad_out", dt, (N, plan.d_out)),
+            _ptr_or_null(gx, "grad_x", dt, (N, plan.d_x)), _ptr_or_null(gy, "grad_y", dt, (E, plan.d_sh)),
+            _ptr_or_null(gw, "grad_w", dt, wshape), ws, ctypes.c_size_t(wsb), _stream(stream, dev)))
+        return gx, gy, gw
     _check(lib().cgtp_conv_backward(
         plan.handle, N, E, _dev(row_ptr, "row_ptr", torch.int32), _dev(col, "col", torch.int32),
         _dev(t_row_ptr, "t_row_ptr", torch.int32, (N + 1,)), _dev(t_edge, "t_edge", torch.int32, (E,)),

@@ -67,12 +67,20 @@ def build(verbose: bool = False) -> str:
 
 
 def warm(names):
+    """Create the named workloads' plans (both dtypes) and build the modules that are otherwise
+    compiled on first use: the backward of uvw plans (batched or convolution)."""
     sys.path.insert(0, ROOT)
     from clebsch_gordan_tensor_cgtp_amd import binding, synth
     for name in names:
         for dtype in ("f32", "f64"):
             spec = {**synth.WORKLOADS, **synth.EXTRA_WORKLOADS}[name]
-            binding.plan_for(spec, dtype)
+            plan = binding.plan_for(spec, dtype)
+            if spec.mode != "uvw":
+                continue
+            if hasattr(spec, "n_edges"):
+                plan.conv_uvw_backward_source(0)
+            else:
+                plan.uvw_backward_source()
 
 
 def main():

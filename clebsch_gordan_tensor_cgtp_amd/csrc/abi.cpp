@@ -86,6 +86,49 @@ void check_graph_sizes(int64_t N, int64_t E)
     require(E >= 0 && E < INT_MAX, "E must be in [0, 2^31-1)");
 }
 
+// out[0, wn) = sum over nchunks chunks of the partials ws[chunk][wn] (cgtp_reduce_chunks: one
+// 16-wave workgroup per 64 elements)
+void launch_reduce(hipFunction_t f, int64_t wn, void *ws, long nchunks, void *out, void *stream)
+{
+    void *args[] = {&ws, &nchunks, &out};
+    check_hip(hipModuleLaunchKernel(f, (unsigned)((wn + 63) / 64), 1, 1, 1024, 1, 1, 0, static_cast<hipStream_t>(stream),
+                                    args, nullptr),
+              "hipModuleLaunchKernel");
+}
+
+// Sender pass of the backward (one launch per path group, in order): dx, dY and (uvu) dW from
+// the output gradient g; A is the plan itself or the uvw convolution's unit-weight plan.
+void sender_pass(cgtp::Plan &A, int64_t N, int64_t E, const int32_t *t_row_ptr, const int32_t *t_edge,
+                 const int32_t *t_dst, const void *x, const void *y, const void *w, const void *g, void *dx, void *dy,
+                 void *dw, void *stream)
+{
+    const auto &L = cgtp::module_for_current_device(A);
+    long nnodes = (long)N;
+    // waves per sender: split the sender's edges when the mean out-degree leaves enough
+    // edge groups per wave (the dx partials are then summed in a fixed order in LDS)
+    for (int grp = 0; grp < (int)A.bwd_groups.size(); ++grp) {
+        const double groups = (double)E / (double)N / A.bwd_groups[grp].es;
+        int wpr = groups >= 16 ? 4 : groups >= 8 ? 2 : 1;
+        if (const char *env = std::getenv("CGTP_BWD_WPR")) wpr = std::max(1, std::min(4, std::atoi(env)));
+        void *args[] = {&t_row_ptr, &t_edge, &t_dst, &x, &y, &w, &g, &dx, &dy, &dw, &nnodes, &wpr, &grp};
+        check_hip(hipModuleLaunchKernel(L.conv_bwd, (unsigned)N, 1, 1, 64 * wpr, 1, 1, 0,
+                                        static_cast<hipStream_t>(stream), args, nullptr),
+                  "hipModuleLaunchKernel");
+    }
+}
+
+// Workspace of the uvw convolution backward: G (N x sum_p mul_in(p) (2 l3 + 1), padded to 256
+// bytes), then one dW partial per 16-receiver tile.  Zero for uvu plans.
+size_t conv_uvw_workspace(const cgtp::Plan &P, int64_t N, size_t *g_bytes)
+{
+    if (g_bytes) *g_bytes = 0;
+    if (P.mode != CGTP_UVW || N == 0) return 0;
+    const size_t es = elem(P);
+    const size_t gb = ((size_t)N * cgtp::conv_uvw_g_width(P) * es + 255) / 256 * 256;
+    if (g_bytes) *g_bytes = gb;
+    return gb + (size_t)((N + 15) / 16) * P.w_numel * es;
+}
+
 }  // namespace
 
 extern "C" {
@@ -141,12 +184,7 @@ cgtp_status cgtp_plan_destroy(cgtp_plan *plan)
 {
     return guarded([&] {
         if (!plan) return;
-        int prev = 0;
-        bool have_prev = hipGetDevice(&prev) == hipSuccess;
-        for (auto &kv : plan->p.loaded) {
-            if (hipSetDevice(kv.first) == hipSuccess && kv.second.module) hipModuleUnload(kv.second.module);
-        }
-        if (have_prev && !plan->p.loaded.empty()) hipSetDevice(prev);
+        cgtp::unload_modules(plan->p);
         delete plan;
     });
 }
@@ -301,8 +339,17 @@ cgtp_status cgtp_tp_backward(const cgtp_plan *plan, int64_t B, const void *x, co
             require(shared_weights == 1, "uvw takes shared weights: shared_weights must be 1");
         if (uvw && !P.uvb_ok)
             throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw batched backward: every multiplicity must be <= 16");
-        if (B == 0 || (!grad_x && !grad_y && !grad_w)) return;
+        if (!grad_x && !grad_y && !grad_w) return;
         const size_t es = elem(P);
+        if (B == 0) {
+            if (uvw && grad_w) {
+                // no rows: the shared-weight gradient is zero
+                require_ptr(grad_w, "grad_w", es);
+                const auto &F = cgtp::uvw_backward_for_current_device(P);
+                launch_reduce(F.reduce, P.w_numel, workspace, 0, grad_w, stream);
+            }
+            return;
+        }
         require_ptr(x, "x", es);
         require_ptr(y, "y", es);
         require_ptr(w, "w", es);
@@ -351,10 +398,7 @@ cgtp_status cgtp_tp_backward(const cgtp_plan *plan, int64_t B, const void *x, co
             long nwaves = nchunks * (long)P.uvb_w_groups.size();
             void *args[] = {&x, &y, &grad_out, &workspace, &nrows, &nblocks, &bpc, &nchunks, &nwaves};
             launch(F.w, nwaves, args, stream);
-            void *rargs[] = {&workspace, &nchunks, &grad_w};
-            check_hip(hipModuleLaunchKernel(F.reduce, (unsigned)((P.w_numel + 255) / 256), 1, 1, 256, 1, 1, 0,
-                                            static_cast<hipStream_t>(stream), rargs, nullptr),
-                      "hipModuleLaunchKernel");
+            launch_reduce(F.reduce, P.w_numel, workspace, nchunks, grad_w, stream);
         }
     });
 }
@@ -536,7 +580,7 @@ cgtp_status cgtp_conv_backward(const cgtp_plan *plan, int64_t N, int64_t E, cons
         require(plan != nullptr, "plan is NULL");
         cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
         check_graph_sizes(N, E);
-        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw convolution is not built yet");
+        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw convolution backward: use cgtp_conv_backward_ws (it needs a workspace)");
         if (N == 0) return;
         if (!grad_x && !grad_y && !grad_w) return;
         const size_t es = elem(P);
@@ -566,21 +610,120 @@ cgtp_status cgtp_conv_backward(const cgtp_plan *plan, int64_t N, int64_t E, cons
             for (int b = a + 1; b < 3; ++b) require_disjoint(outs[a], outn[a], outm[a], outs[b], outn[b], outm[b]);
         }
         // with E == 0 the kernel still runs: every sender has an empty row and writes zeros to grad_x
-        const auto &L = cgtp::module_for_current_device(P);
-        long nnodes = (long)N;
-        // waves per sender: split the sender's edges when the mean out-degree leaves enough
-        // edge groups per wave (the dx partials are then summed in a fixed order in LDS)
-        for (int grp = 0; grp < (int)P.bwd_groups.size(); ++grp) {
-            const double groups = (double)E / (double)N / P.bwd_groups[grp].es;
-            int wpr = groups >= 16 ? 4 : groups >= 8 ? 2 : 1;
-            if (const char *env = std::getenv("CGTP_BWD_WPR")) wpr = std::max(1, std::min(4, std::atoi(env)));
-            void *args[] = {&t_row_ptr, &t_edge, &t_dst, &x, &y, &w, &grad_out, &grad_x, &grad_y, &grad_w,
-                            &nnodes, &wpr, &grp};
-            check_hip(hipModuleLaunchKernel(L.conv_bwd, (unsigned)N, 1, 1, 64 * wpr, 1, 1, 0,
-                                            static_cast<hipStream_t>(stream), args, nullptr),
-                      "hipModuleLaunchKernel");
+        sender_pass(P, N, E, t_row_ptr, t_edge, t_dst, x, y, w, grad_out, grad_x, grad_y, grad_w, stream);
+    });
+}
+
+cgtp_status cgtp_conv_backward_workspace_size(const cgtp_plan *plan, int64_t N, int64_t E, size_t *bytes)
+{
+    return guarded([&] {
+        require(plan != nullptr && bytes != nullptr, "plan and bytes must be non-NULL");
+        check_graph_sizes(N, E);
+        *bytes = conv_uvw_workspace(plan->p, N, nullptr);
+    });
+}
+
+cgtp_status cgtp_conv_backward_ws(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
+                                  const int32_t *col, const int32_t *order, const int32_t *t_row_ptr,
+                                  const int32_t *t_edge, const int32_t *t_dst, const void *x, const void *y,
+                                  const void *w, const void *grad_out, void *grad_x, void *grad_y, void *grad_w,
+                                  void *workspace, size_t workspace_bytes, void *stream)
+{
+    return guarded([&] {
+        require(plan != nullptr, "plan is NULL");
+        cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
+        check_graph_sizes(N, E);
+        if (P.mode == CGTP_UVU) {
+            const cgtp_status st = cgtp_conv_backward(plan, N, E, row_ptr, col, t_row_ptr, t_edge, t_dst, x, y, w,
+                                                      grad_out, grad_x, grad_y, grad_w, stream);
+            if (st != CGTP_OK) throw cgtp::Error(st, g_last_error);
+            return;
+        }
+        if (!grad_x && !grad_y && !grad_w) return;
+        const size_t es = elem(P);
+        if (grad_w) require_ptr(grad_w, "grad_w", es);
+        if (N == 0) {
+            // no receivers: dW is zero (grad_x and grad_y are empty)
+            if (grad_w) {
+                const auto &F = cgtp::conv_uvw_backward_for_current_device(P);
+                launch_reduce(F.reduce, P.w_numel, workspace, 0, grad_w, stream);
+            }
+            return;
+        }
+        require_ptr(row_ptr, "row_ptr", 4);
+        require_ptr(t_row_ptr, "t_row_ptr", 4);
+        require_ptr(x, "x", es);
+        require_ptr(w, "w", es);
+        require_ptr(grad_out, "grad_out", es);
+        if (E > 0) {
+            require_ptr(col, "col", 4);
+            require_ptr(t_edge, "t_edge", 4);
+            require_ptr(t_dst, "t_dst", 4);
+            require_ptr(y, "y", es);
+        }
+        if (grad_x) require_ptr(grad_x, "grad_x", es);
+        if (E > 0 && grad_y) require_ptr(grad_y, "grad_y", es);
+        if (order) require_ptr(order, "order", 4);
+        size_t g_bytes = 0;
+        const size_t ws_need = conv_uvw_workspace(P, N, &g_bytes);
+        require_ptr(workspace, "workspace", 256);
+        require(workspace_bytes >= ws_need, "workspace too small (see cgtp_conv_backward_workspace_size)");
+        const void *ins[] = {x, y, w, grad_out, row_ptr, col, t_row_ptr, t_edge, t_dst, order};
+        const size_t inn[] = {N * P.d_x * es, E * P.d_sh * es, P.w_numel * es, N * P.d_out * es,
+                              (size_t)(N + 1) * 4, (size_t)E * 4, (size_t)(N + 1) * 4, (size_t)E * 4,
+                              (size_t)E * 4, order ? (size_t)N * 4 : 0};
+        const char *inm[] = {"x", "y", "w", "grad_out", "row_ptr", "col", "t_row_ptr", "t_edge", "t_dst", "order"};
+        void *outs[] = {grad_x, grad_y, grad_w, workspace};
+        const size_t outn[] = {N * P.d_x * es, E * P.d_sh * es, P.w_numel * es, ws_need};
+        const char *outm[] = {"grad_x", "grad_y", "grad_w", "workspace"};
+        for (int a = 0; a < 4; ++a) {
+            for (int b = 0; b < 10; ++b) require_disjoint(outs[a], outn[a], outm[a], ins[b], inn[b], inm[b]);
+            for (int b = a + 1; b < 4; ++b) require_disjoint(outs[a], outn[a], outm[a], outs[b], outn[b], outm[b]);
+        }
+        const auto &F = cgtp::conv_uvw_backward_for_current_device(P);
+        long nrows = (long)N;
+        void *G = workspace;
+        if (grad_x || grad_y) {
+            // G_p = W_p^T g per receiver, then the sender pass of the unit-weight internal plan
+            long nwaves = (long)((N + 15) / 16) * (long)cgtp::conv_uvw_g_items(P, nullptr);
+            void *args[] = {&w, &grad_out, &G, &nrows, &nwaves};
+            launch(F.g, nwaves, args, stream);
+            cgtp::Plan &A = cgtp::conv_uvw_aux_plan(P);
+            sender_pass(A, N, E, t_row_ptr, t_edge, t_dst, x, y, nullptr, G, grad_x, grad_y, nullptr, stream);
+        }
+        if (grad_w) {
+            // per-tile partials of dW (one launch per path group), summed in tile order
+            void *part = static_cast<char *>(workspace) + g_bytes;
+            const unsigned tiles = (unsigned)((N + 15) / 16);
+            const unsigned threads = 1024u / (unsigned)P.uvc_rpw;
+            for (int grp = 0; grp < (int)P.uvc_groups.size(); ++grp) {
+                void *args[] = {&row_ptr, &col, &x, &y, &grad_out, &part, &nrows, &order, &grp};
+                check_hip(hipModuleLaunchKernel(F.w, tiles, 1, 1, threads, 1, 1, 0, static_cast<hipStream_t>(stream),
+                                                args, nullptr),
+                          "hipModuleLaunchKernel");
+            }
+            launch_reduce(F.reduce, P.w_numel, part, (long)tiles, grad_w, stream);
         }
     });
+}
+
+cgtp_status cgtp_plan_conv_uvw_backward_prepare(const cgtp_plan *plan)
+{
+    return guarded([&] {
+        require(plan != nullptr, "plan is NULL");
+        cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
+        if (P.mode != CGTP_UVW) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw convolution backward: uvw plans only");
+        cgtp::prepare_conv_uvw_backward(P);
+    });
+}
+
+const char *cgtp_plan_conv_uvw_backward_source(const cgtp_plan *plan, int32_t module)
+{
+    if (!plan || (module != 0 && module != 1)) return nullptr;
+    cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
+    std::lock_guard<std::mutex> lock(P.mu);
+    if (P.ucb.code.empty() || !P.aux) return nullptr;
+    return module == 0 ? P.ucb.source.c_str() : P.aux->source.c_str();
 }
 
 cgtp_status cgtp_conv_double_backward(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
@@ -594,7 +737,7 @@ cgtp_status cgtp_conv_double_backward(const cgtp_plan *plan, int64_t N, int64_t 
         require(plan != nullptr, "plan is NULL");
         cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
         check_graph_sizes(N, E);
-        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw convolution is not built yet");
+        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "double backward: uvu plans only");
         if (N == 0) return;
         const bool send = grad_x || grad_y || grad_w;
         if (!send && !grad_grad_out) return;

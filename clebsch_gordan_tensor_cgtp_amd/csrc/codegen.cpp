@@ -592,6 +592,7 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
                 o(Ty, pre, "y", b, "_", j, " = LD_STREAM(&y[(size_t)", ev, " * DSH + ", off + j, "]);");
         }
         for (int pi : g.paths) {
+            if (P.unit_weights) break;
             const Path &p = P.paths[pi];
             std::string wa = "LD_STREAM(&w[(size_t)" + ev + " * WROW + " + std::to_string(p.w_off) + " + u])";
             if (needs_mask(p.mul_in, g))
@@ -702,7 +703,7 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
         if (dbl) contract(rows, false, "gy", p.i2, "fxg");  // d/dx of the ggy term
         contract(cols, true, "x", p.i1, "fy");
         if (dbl) contract(cols, true, "gx", p.i1, "fyg");   // d/dy of the ggx term
-        {
+        if (!P.unit_weights) {
             // dW = sum_i x_i dF/dx_i   (double backward: sum_i ggx_i fx_i + x_i fxg_i)
             std::ostringstream e;
             bool first = true;
@@ -737,6 +738,9 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
             for (auto &kv : cols)
                 o("h", p.i2, "_", kv.first, " = FMA(w", pi, ", fyg", kv.first, ", FMA(gw", pi, ", fy", kv.first, ", h", p.i2,
                   "_", kv.first, "));");
+        } else if (P.unit_weights) {
+            for (auto &kv : rows) o("d", p.i1, "_", kv.first, " += fx", kv.first, ";");
+            for (auto &kv : cols) o("h", p.i2, "_", kv.first, " += fy", kv.first, ";");
         } else {
             for (auto &kv : rows)
                 o("d", p.i1, "_", kv.first, " = FMA(w", pi, ", fx", kv.first, ", d", p.i1, "_", kv.first, ");");
@@ -797,7 +801,8 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
     if (pf) {
         for (int b : t.i2)
             for (int j = 0; j < n_of(P.sh[b].l); ++j) o("y", b, "_", j, " = ny", b, "_", j, ";");
-        for (int pi : g.paths) o("w", pi, " = nw", pi, ";");
+        if (!P.unit_weights)
+            for (int pi : g.paths) o("w", pi, " = nw", pi, ";");
         for (int q : t.slots)
             for (int k = 0; k < n_of(P.out[q].l); ++k) o("g", q, "_", k, " = ng", q, "_", k, ";");
         if (dbl) {
@@ -926,7 +931,7 @@ void emit_bwd_kernel(Out &o, const Plan &P, bool dbl = false)
     for (int gi = 0; gi < (int)groups.size(); ++gi) emit_bwd_group(o, P, gi, dbl);
     o("// one workgroup of 64*wpr threads per sender; `group` selects the path group (launched in order)");
     o("extern \"C\" __global__ void __launch_bounds__(256, ", dbl ? P.dbl_bwd_waves_per_eu : P.bwd_waves_per_eu, ") ",
-      dbl ? "cgtp_conv_dbwd_send" : "cgtp_conv_bwd",
+      dbl ? "cgtp_conv_dbwd_send" : P.unit_weights ? "cgtp_conv_uvw_bwd_xy" : "cgtp_conv_bwd",
       "(const int* __restrict__ t_row_ptr, "
       "const int* __restrict__ t_edge, const int* __restrict__ t_dst, const T* __restrict__ x, "
       "const T* __restrict__ y, const T* __restrict__ w, const T* __restrict__ g, ",
@@ -1644,6 +1649,49 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
     o("");
 }
 
+// out[i] = sum over chunks of ws[chunk][i] (nchunks = 0 writes zeros).  One workgroup of 16
+// waves per 64 consecutive i: wave v sums the v-th contiguous sixteenth of the chunks in chunk
+// order (eight loads in flight), then wave 0 adds the sixteen partials in wave order; the order
+// of every sum is fixed by nchunks alone.
+void emit_reduce_chunks(Out &o)
+{
+    o("extern \"C\" __global__ void __launch_bounds__(1024) cgtp_reduce_chunks(const T* __restrict__ ws, long nchunks, "
+      "T* __restrict__ out)");
+    o("{");
+    o.ind++;
+    o("__shared__ T part[16 * 64];");
+    o("const int lane = threadIdx.x & 63;");
+    o("const int wv = threadIdx.x >> 6;");
+    o("const long i = (long)blockIdx.x * 64 + lane;");
+    o("const bool ok = i < WN;");
+    o("const long per = (nchunks + 15) / 16;");
+    o("const long c0 = wv * per;");
+    o("const long c1 = c0 + per < nchunks ? c0 + per : nchunks;");
+    o("const T* p = ws + (ok ? i : 0);");
+    o("T s = (T)0;");
+    o("long c = c0;");
+    o("for (; ok && c + 8 <= c1; c += 8) {");
+    o.ind++;
+    o("T v[8];");
+    o("for (int k = 0; k < 8; ++k) v[k] = p[(size_t)(c + k) * WN];");
+    o("for (int k = 0; k < 8; ++k) s += v[k];");
+    o.ind--;
+    o("}");
+    o("for (; ok && c < c1; ++c) s += p[(size_t)c * WN];");
+    o("part[wv * 64 + lane] = s;");
+    o("__syncthreads();");
+    o("if (wv == 0 && ok) {");
+    o.ind++;
+    o("T t = part[lane];");
+    o("for (int v = 1; v < 16; ++v) t += part[v * 64 + lane];");
+    o("out[i] = t;");
+    o.ind--;
+    o("}");
+    o.ind--;
+    o("}");
+    o("");
+}
+
 void emit_uvb_kernels(Out &o, const Plan &P)
 {
     if (!P.uvb_ok) {
@@ -1694,19 +1742,235 @@ void emit_uvb_kernels(Out &o, const Plan &P)
     o.ind--;
     o("}");
     o("");
-    o("// dW[i] = sum over chunks of the partials, in chunk order");
-    o("extern \"C\" __global__ void __launch_bounds__(256) cgtp_reduce_chunks(const T* __restrict__ ws, long nchunks, "
-      "T* __restrict__ out)");
+    emit_reduce_chunks(o);
+}
+
+// ------------------------------------------------------------------------------------------
+// uvw convolution backward.  With the receiver-side products
+//   G_p[n][u][k] = sum_w W_p[u][w] g[n][slot(p)][w][k]
+// (cgtp_conv_uvw_bwd_g, MFMA per 16-receiver tile), the input and SH gradients are those of a
+// uvu convolution with unit weights whose output has one block per path (mul_in(p) x l3): the
+// sender pass of that internal plan reads G in place of the output gradient.  The weight
+// gradient
+//   dW_p[u][w] = sum_n sum_k T_p[n][u][k] g[n][slot(p)][w][k],
+// T_p the unweighted per-receiver sums of the forward, reuses the forward's edge pass (T staged
+// in LDS for the tile's 16 receivers), then contracts over the 16 receivers on MFMA with the
+// receivers as the K dimension (A = T[u = lane % 16][row = 4m + lane / 16], B = g[row][w = lane %
+// 16][k]); every tile writes its partial, and cgtp_reduce_chunks sums them in tile order.
+// work items of the G kernel: (path, 16-channel block of u)
+int ucb_items(const Plan &P, std::vector<std::pair<int, int>> *items)
+{
+    int n = 0;
+    for (int pi = 0; pi < (int)P.paths.size(); ++pi)
+        for (int ut = 0; ut * 16 < P.paths[pi].mul_in; ++ut, ++n)
+            if (items) items->push_back({pi, ut});
+    return n;
+}
+
+void emit_ucb_g_kernel(Out &o, const Plan &P)
+{
+    const bool f64 = P.dtype == CGTP_F64;
+    std::vector<std::pair<int, int>> items;
+    const int nitems = ucb_items(P, &items);
+    std::vector<int> goff(P.paths.size());
+    for (int pi = 0, acc = 0; pi < (int)P.paths.size(); ++pi) {
+        goff[pi] = acc;
+        acc += P.paths[pi].mul_in * n_of(P.paths[pi].l3);
+    }
+    o("// one wave per (16-receiver tile, path, 16-channel block of u), tile-major");
+    o("extern \"C\" __global__ void __launch_bounds__(256) cgtp_conv_uvw_bwd_g(const T* __restrict__ w, "
+      "const T* __restrict__ g, T* __restrict__ G, long nrows, long nwaves)");
     o("{");
     o.ind++;
-    o("const long i = (long)blockIdx.x * 256 + threadIdx.x;");
-    o("if (i >= WN) return;");
-    o("T s = (T)0;");
-    o("for (long c = 0; c < nchunks; ++c) s += ws[(size_t)c * WN + i];");
-    o("out[i] = s;");
+    o("const long wave = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const int lane = threadIdx.x & 63;");
+    o("if (wave >= nwaves) return;");
+    o("const long tile = wave / ", nitems, ";");
+    o("const int item = (int)(wave - tile * ", nitems, ");");
+    o("const int usub = lane >> 4;");
+    o("const int row = lane & 15;");
+    o("const long n = tile * 16 + row;");
+    o("const bool live = n < nrows;");
+    o("const long nn = live ? n : nrows - 1;");
+    o("switch (item) {");
+    for (int it = 0; it < nitems; ++it) {
+        const int q = P.paths[items[it].first].slot, ut = items[it].second;
+        const Irrep &ir = P.out[q];
+        const int n3 = n_of(ir.l);
+        int ooff = 0;
+        for (int qq = 0; qq < q; ++qq) ooff += P.out[qq].dim();
+        const int cs = (ir.mul + 3) / 4;
+        o("case ", it, ": {");
+        o.ind++;
+        const std::vector<int> ps = {items[it].first};
+        // operands first (one wait for all of them): B = g[row = lane % 16][w = 4c + lane / 16][k]
+        // for every k, A = W_p[u = 16 ut + lane % 16][w = 4c + lane / 16]
+        for (int k = 0; k < n3; ++k)
+            for (int c = 0; c < cs; ++c) {
+                const std::string wv = "(" + std::to_string(4 * c) + " + usub)";
+                if (4 * c + 3 >= ir.mul)
+                    o("const T b", k, "_", c, " = ", wv, " < ", ir.mul, " ? g[(size_t)nn * DOUT + ", ooff, " + (", wv, " < ", ir.mul,
+                      " ? ", wv, " : 0) * ", n3, " + ", k, "] : (T)0;");
+                else
+                    o("const T b", k, "_", c, " = g[(size_t)nn * DOUT + ", ooff, " + ", wv, " * ", n3, " + ", k, "];");
+            }
+        const std::string u = "(" + std::to_string(16 * ut) + " + row)";
+        for (int pi : ps) {
+            const Path &p = P.paths[pi];
+            for (int c = 0; c < cs; ++c) {
+                const std::string wv = "(" + std::to_string(4 * c) + " + usub)";
+                if (16 * ut + 15 >= p.mul_in || 4 * c + 3 >= p.mul_out) {
+                    const std::string ok = "(" + u + " < " + std::to_string(p.mul_in) + " && " + wv + " < " +
+                                           std::to_string(p.mul_out) + ")";
+                    o("const T a", pi, "_", c, " = ", ok, " ? w[", p.w_off, " + (", ok, " ? ", u, " * ", p.mul_out, " + ", wv,
+                      " : 0)] : (T)0;");
+                } else {
+                    o("const T a", pi, "_", c, " = w[", p.w_off, " + ", u, " * ", p.mul_out, " + ", wv, "];");
+                }
+            }
+        }
+        for (int pi : ps)
+            for (int k = 0; k < n3; ++k) {
+                o("V4 d", pi, "_", k, " = {0, 0, 0, 0};");
+                for (int c = 0; c < cs; ++c) o("d", pi, "_", k, " = MFMA(a", pi, "_", c, ", b", k, "_", c, ", d", pi, "_", k, ");");
+            }
+        // lane holds G[u = 16 ut + U(v)][row = lane % 16]; one branch for all stores, so that
+        // the loads and MFMAs above form one scheduling region
+        o("if (live) {");
+        o.ind++;
+        for (int pi : ps) {
+            const Path &p = P.paths[pi];
+            for (int k = 0; k < n3; ++k)
+                for (int v = 0; v < 4; ++v) {
+                    const std::string uu = "(" + std::to_string(16 * ut) + " + " + uvb_u(f64, v) + ")";
+                    const std::string guard = 16 * ut + 15 >= p.mul_in ? "if (" + uu + " < " + std::to_string(p.mul_in) + ") " : "";
+                    o(guard, "G[(size_t)n * DG + ", goff[pi], " + ", uu, " * ", n3, " + ", k, "] = d", pi, "_", k, "[", v, "];");
+                }
+        }
+        o.ind--;
+        o("}");
+        o("break;");
+        o.ind--;
+        o("}");
+    }
+    o("default: break;");
+    o("}");
     o.ind--;
     o("}");
     o("");
+}
+
+void emit_ucb_w_group(Out &o, const Plan &P, int gi)
+{
+    const Group &g = P.uvc_groups[gi];
+    std::map<int, int> loff;
+    int lds_elems = 0;
+    for (int pi : g.paths) {
+        loff[pi] = lds_elems;
+        lds_elems += 16 * uvc_mu_pad(P.paths[pi]) * n_of(P.paths[pi].l3);
+    }
+    const bool f64 = P.dtype == CGTP_F64;
+    const int nw = 16 / P.uvc_rpw;
+    o("__device__ __forceinline__ void ucw_g", gi,
+      "(long tile, int wv, int lane, const int* __restrict__ row_ptr, const int* __restrict__ col, "
+      "const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ g, T* __restrict__ ws, long nrows, "
+      "const int* __restrict__ order, T* lds)");
+    o("{");
+    o.ind++;
+    emit_uvc_phase_a(o, P, g, loff);
+    o("__syncthreads();");
+    o("const int usub = lane >> 4;");
+    o("const int row = lane & 15;");
+    // receivers of the B rows 4m + lane / 16
+    for (int m = 0; m < 4; ++m) {
+        o("const long bi", m, " = tile * 16 + ", 4 * m, " + usub;");
+        o("const bool bl", m, " = bi", m, " < nrows;");
+        o("const long bn", m, " = bl", m, " ? (order ? (long)order[bi", m, "] : bi", m, ") : 0;");
+    }
+    int item = 0;
+    for (int pi : g.paths) {
+        const Path &p = P.paths[pi];
+        const int n3 = n_of(p.l3), mp = uvc_mu_pad(p);
+        const int uts = (p.mul_in + 15) / 16, wts = (p.mul_out + 15) / 16;
+        for (int wt = 0; wt < wts; ++wt, ++item) {
+            o("if (wv == ", item % nw, ") {");
+            o.ind++;
+            for (int ut = 0; ut < uts; ++ut) o("V4 D", ut, " = {0, 0, 0, 0};");
+            const std::string wcol = "(" + std::to_string(16 * wt) + " + row)";
+            const bool wmask = 16 * wt + 15 >= p.mul_out;
+            for (int k = 0; k < n3; ++k) {
+                o("{");
+                o.ind++;
+                for (int m = 0; m < 4; ++m) {
+                    if (wmask)
+                        o("const T b", m, " = (bl", m, " && ", wcol, " < ", p.mul_out, ") ? g[(size_t)bn", m, " * DOUT + ", p.o, " + (",
+                          wcol, " < ", p.mul_out, " ? ", wcol, " : 0) * ", n3, " + ", k, "] : (T)0;");
+                    else
+                        o("const T b", m, " = bl", m, " ? g[(size_t)bn", m, " * DOUT + ", p.o, " + ", wcol, " * ", n3, " + ", k,
+                          "] : (T)0;");
+                }
+                for (int ut = 0; ut < uts; ++ut) {
+                    const std::string u = "(" + std::to_string(16 * ut) + " + row)";
+                    const bool umask = 16 * ut + 15 >= mp;
+                    for (int m = 0; m < 4; ++m) {
+                        const std::string base = std::to_string(loff[pi] + 16 * mp * k + 4 * m);
+                        if (umask)
+                            o("D", ut, " = MFMA(", u, " < ", mp, " ? lds[", base, " + (", u, " < ", mp, " ? ", u, " : 0) * 16 + usub] : (T)0, b",
+                              m, ", D", ut, ");");
+                        else
+                            o("D", ut, " = MFMA(lds[", base, " + ", u, " * 16 + usub], b", m, ", D", ut, ");");
+                    }
+                }
+                o.ind--;
+                o("}");
+            }
+            // lane holds D[u = 16 ut + U(v)][w = 16 wt + lane % 16]
+            for (int ut = 0; ut < uts; ++ut)
+                for (int v = 0; v < 4; ++v) {
+                    const std::string uu = "(" + std::to_string(16 * ut) + " + " + uvb_u(f64, v) + ")";
+                    std::string guard;
+                    if (16 * ut + 15 >= p.mul_in) guard += uu + " < " + std::to_string(p.mul_in);
+                    if (wmask) guard += (guard.empty() ? "" : " && ") + wcol + " < " + std::to_string(p.mul_out);
+                    o(guard.empty() ? "" : "if (" + guard + ") ", "ws[(size_t)tile * WN + ", p.w_off, " + ", uu, " * ", p.mul_out, " + ", wcol,
+                      "] = D", ut, "[", v, "];");
+                }
+            o.ind--;
+            o("}");
+        }
+    }
+    o.ind--;
+    o("}");
+    o("");
+}
+
+void emit_ucb_kernels(Out &o, const Plan &P)
+{
+    o("#define WN ", P.w_numel, "L");
+    int dg = 0;
+    for (const Path &p : P.paths) dg += p.mul_in * n_of(p.l3);
+    o("#define DG ", dg);
+    emit_ucb_g_kernel(o, P);
+    for (int gi = 0; gi < (int)P.uvc_groups.size(); ++gi) emit_ucb_w_group(o, P, gi);
+    o("// one workgroup of ", 16 / P.uvc_rpw, " waves per 16 receivers; `group` selects the path group");
+    o("extern \"C\" __global__ void __launch_bounds__(", 1024 / P.uvc_rpw, ", ", P.uvc_waves_per_eu,
+      ") cgtp_conv_uvw_bwd_w(const int* __restrict__ row_ptr, const int* __restrict__ col, const T* __restrict__ x, "
+      "const T* __restrict__ y, const T* __restrict__ g, T* __restrict__ ws, long nrows, "
+      "const int* __restrict__ order, int group)");
+    o("{");
+    o.ind++;
+    o("__shared__ T lds[", uvc_lds_elems(P), "];  // T of the tile's 16 receivers, [p,k][u][row]");
+    o("const long tile = blockIdx.x;");
+    o("const int wv = threadIdx.x >> 6;");
+    o("const int lane = threadIdx.x & 63;");
+    o("switch (group) {");
+    for (int gi = 0; gi < (int)P.uvc_groups.size(); ++gi)
+        o("case ", gi, ": ucw_g", gi, "(tile, wv, lane, row_ptr, col, x, y, g, ws, nrows, order, lds); break;");
+    o("default: break;");
+    o("}");
+    o.ind--;
+    o("}");
+    o("");
+    emit_reduce_chunks(o);
 }
 
 }  // namespace
@@ -1720,6 +1984,26 @@ std::string generate_uvw_backward_source(const Plan &P)
     o("// @@section cgtp_tp_uvw_bwd");
     emit_uvb_kernels(o, P);
     return o.s.str();
+}
+
+std::string generate_conv_uvw_backward_source(const Plan &P)
+{
+    Out o;
+    o("// @@section common");
+    emit_preamble(o, P);
+    emit_mfma_defs(o, P);
+    o("// @@section cgtp_conv_uvw_bwd");
+    emit_ucb_kernels(o, P);
+    return o.s.str();
+}
+
+int conv_uvw_g_items(const Plan &P, std::vector<std::pair<int, int>> *items) { return ucb_items(P, items); }
+
+int64_t conv_uvw_g_width(const Plan &P)
+{
+    int64_t dg = 0;
+    for (const Path &p : P.paths) dg += (int64_t)p.mul_in * (2 * p.l3 + 1);
+    return dg;
 }
 
 std::string generate_radial_source(const Plan &P, int R)
@@ -1767,7 +2051,12 @@ std::string generate_source(const Plan &P)
     Out o;
     o("// @@section common");
     emit_preamble(o, P);
-    if (P.mode == CGTP_UVU) {
+    if (P.unit_weights) {
+        // internal plan of the uvw convolution backward: the sender pass only
+        emit_slot_sum(o, P);
+        o("// @@section cgtp_conv_uvw_bwd_xy");
+        emit_bwd_kernel(o, P);
+    } else if (P.mode == CGTP_UVU) {
         emit_slot_sum(o, P);
         o("// @@section cgtp_conv_fwd");
         for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi) emit_fwd_group(o, P, gi, false);

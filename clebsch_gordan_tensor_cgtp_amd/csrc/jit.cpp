@@ -120,7 +120,9 @@ const Plan::Loaded &module_for_current_device(Plan &P)
     if (it != P.loaded.end()) return it->second;
     Plan::Loaded L;
     check(hipModuleLoadData(&L.module, P.code.data()), "hipModuleLoadData");
-    if (P.mode == CGTP_UVU) {
+    if (P.unit_weights) {
+        check(hipModuleGetFunction(&L.conv_bwd, L.module, "cgtp_conv_uvw_bwd_xy"), "hipModuleGetFunction(uvw_bwd_xy)");
+    } else if (P.mode == CGTP_UVU) {
         check(hipModuleGetFunction(&L.conv_fwd, L.module, "cgtp_conv_fwd"), "hipModuleGetFunction(conv_fwd)");
         check(hipModuleGetFunction(&L.conv_bwd, L.module, "cgtp_conv_bwd"), "hipModuleGetFunction(conv_bwd)");
         check(hipModuleGetFunction(&L.tp_fwd, L.module, "cgtp_tp_fwd"), "hipModuleGetFunction(tp_fwd)");
@@ -201,6 +203,73 @@ const Plan::UvwBackward::Fns &uvw_backward_for_current_device(Plan &P)
     check(hipModuleGetFunction(&F.w, F.module, "cgtp_tp_uvw_bwd_w"), "hipModuleGetFunction(uvw_bwd_w)");
     check(hipModuleGetFunction(&F.reduce, F.module, "cgtp_reduce_chunks"), "hipModuleGetFunction(reduce)");
     return P.uvb.loaded.emplace(dev, F).first->second;
+}
+
+// uvw convolution backward: the G / dW module and the internal sender-pass plan; caller holds P.mu
+static void ucb_locked(Plan &P)
+{
+    if (P.ucb.code.empty()) {
+        P.ucb.source = generate_conv_uvw_backward_source(P);
+        P.ucb.code = compile_source(P.ucb.source);
+    }
+    if (!P.aux) {
+        std::unique_ptr<Plan> A = make_conv_uvw_aux(P);
+        A->source = generate_source(*A);
+        A->code = compile_source(A->source);
+        P.aux = std::move(A);
+    }
+}
+
+const std::string &prepare_conv_uvw_backward(Plan &P)
+{
+    std::lock_guard<std::mutex> lock(P.mu);
+    ucb_locked(P);
+    return P.ucb.source;
+}
+
+Plan &conv_uvw_aux_plan(Plan &P)
+{
+    std::lock_guard<std::mutex> lock(P.mu);
+    ucb_locked(P);
+    return *P.aux;
+}
+
+const Plan::ConvUvwBackward::Fns &conv_uvw_backward_for_current_device(Plan &P)
+{
+    int dev = 0;
+    check(hipGetDevice(&dev), "hipGetDevice");
+    std::lock_guard<std::mutex> lock(P.mu);
+    ucb_locked(P);
+    auto it = P.ucb.loaded.find(dev);
+    if (it != P.ucb.loaded.end()) return it->second;
+    Plan::ConvUvwBackward::Fns F;
+    check(hipModuleLoadData(&F.module, P.ucb.code.data()), "hipModuleLoadData");
+    check(hipModuleGetFunction(&F.g, F.module, "cgtp_conv_uvw_bwd_g"), "hipModuleGetFunction(conv_uvw_bwd_g)");
+    check(hipModuleGetFunction(&F.w, F.module, "cgtp_conv_uvw_bwd_w"), "hipModuleGetFunction(conv_uvw_bwd_w)");
+    check(hipModuleGetFunction(&F.reduce, F.module, "cgtp_reduce_chunks"), "hipModuleGetFunction(reduce)");
+    return P.ucb.loaded.emplace(dev, F).first->second;
+}
+
+// Unload every module of the plan (and of its internal plan) on the device it was loaded on.
+void unload_modules(Plan &P)
+{
+    std::vector<std::pair<int, hipModule_t>> mods;
+    for (auto &kv : P.loaded) mods.push_back({kv.first, kv.second.module});
+    for (auto &r : P.radial)
+        for (auto &kv : r.second.loaded) mods.push_back({kv.first, kv.second.first});
+    for (auto &kv : P.uvb.loaded) mods.push_back({kv.first, kv.second.module});
+    for (auto &kv : P.ucb.loaded) mods.push_back({kv.first, kv.second.module});
+    P.loaded.clear();
+    for (auto &r : P.radial) r.second.loaded.clear();
+    P.uvb.loaded.clear();
+    P.ucb.loaded.clear();
+    if (P.aux) unload_modules(*P.aux);
+    if (mods.empty()) return;
+    int prev = 0;
+    const bool have_prev = hipGetDevice(&prev) == hipSuccess;
+    for (auto &dm : mods)
+        if (dm.second && hipSetDevice(dm.first) == hipSuccess) hipModuleUnload(dm.second);
+    if (have_prev) hipSetDevice(prev);
 }
 
 }  // namespace cgtp

@@ -6,6 +6,7 @@
 
 #include <cstdint>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <stdexcept>
 #include <string>
@@ -68,6 +69,7 @@ struct Plan {
     std::vector<Group> uvb_x_groups;  // uvw batched backward, dx/dy: one input block per group (launched in order)
     std::vector<Group> uvb_w_groups;  // uvw batched backward, dW partials: up to 16 paths per group
     bool uvb_ok = false;            // uvw batched backward supported (every mul_in, mul_out <= 16)
+    bool unit_weights = false;      // internal plans: every weight is 1 (not read), only the sender pass
     int fwd_waves_per_eu = 4;       // occupancy target given to the compiler (min waves per SIMD)
     int bwd_waves_per_eu = 4;
     int uvw_waves_per_eu = 2;
@@ -108,6 +110,20 @@ struct Plan {
         };
         std::map<int, Fns> loaded;  // per device
     } uvb;
+
+    // uvw convolution backward: G = W^T g per receiver and the dW partials (own module, built
+    // on first use), and the sender pass of an internal uvu plan with one output block per path
+    // and unit weights, which turns G into dx and dY.
+    struct ConvUvwBackward {
+        std::string source;
+        std::vector<char> code;
+        struct Fns {
+            hipModule_t module = nullptr;
+            hipFunction_t g = nullptr, w = nullptr, reduce = nullptr;
+        };
+        std::map<int, Fns> loaded;  // per device
+    } ucb;
+    std::unique_ptr<Plan> aux;
 };
 
 // planner.cpp
@@ -129,5 +145,13 @@ const std::string &prepare_radial(Plan &plan, int R);
 std::string generate_uvw_backward_source(const Plan &plan);
 const std::string &prepare_uvw_backward(Plan &plan);
 const Plan::UvwBackward::Fns &uvw_backward_for_current_device(Plan &plan);
+std::string generate_conv_uvw_backward_source(const Plan &plan);
+const Plan::ConvUvwBackward::Fns &conv_uvw_backward_for_current_device(Plan &plan);
+Plan &conv_uvw_aux_plan(Plan &plan);
+const std::string &prepare_conv_uvw_backward(Plan &plan);
+std::unique_ptr<Plan> make_conv_uvw_aux(const Plan &plan);
+void unload_modules(Plan &plan);
+int64_t conv_uvw_g_width(const Plan &plan);
+int conv_uvw_g_items(const Plan &plan, std::vector<std::pair<int, int>> *items);
 
 }  // namespace cgtp

@@ -397,7 +397,8 @@ void schedule(Plan &P)
             return est_max <= 128 ? 1 : est_max <= 256 ? 2 : 4;
         };
         P.uvc_rpw = make(65536, P.uvc_groups);
-        if (P.uvc_rpw == 1) {
+        const char *wide_env = std::getenv("CGTP_UVC_WIDE");
+        if (P.uvc_rpw == 1 && (!wide_env || std::atoi(wide_env) != 0)) {
             std::vector<Group> wide;
             if (make(122880, wide) == 1) P.uvc_groups = wide;
         }
@@ -517,6 +518,43 @@ void schedule(Plan &P)
     P.uvc_waves_per_eu = 4 / P.uvc_rpw;  // the workgroup's 16 / rpw waves spread over 4 SIMDs
     if (const char *e = std::getenv("CGTP_UVW_WAVES")) P.uvw_waves_per_eu = std::max(1, std::atoi(e));
     if (const char *e = std::getenv("CGTP_BWD_SCHED_BARRIER")) P.bwd_sched_barrier = std::atoi(e) != 0;
+}
+
+// Internal plan of the uvw convolution backward: the paths and CG blocks of P, each path
+// feeding an output block of its own (mul_in x l3, in path order), uvu with unit weights.  Its
+// sender pass, given G_p = W_p^T g as the output gradient, yields the input and SH gradients.
+std::unique_ptr<Plan> make_conv_uvw_aux(const Plan &P)
+{
+    auto A = std::make_unique<Plan>();
+    A->mode = CGTP_UVU;
+    A->dtype = P.dtype;
+    A->ins = P.ins;
+    A->sh = P.sh;
+    A->paths = P.paths;
+    int off = 0;
+    int64_t w = 0;
+    for (size_t i = 0; i < A->paths.size(); ++i) {
+        Path &p = A->paths[i];
+        Irrep ir;
+        ir.mul = p.mul_in;
+        ir.l = p.l3;
+        ir.p = p.p3;
+        A->out.push_back(ir);
+        p.slot = (int)i;
+        p.o = off;
+        p.mul_out = p.mul_in;
+        p.w_off = w;
+        off += ir.dim();
+        w += p.mul_in;
+    }
+    A->d_x = P.d_x;
+    A->d_sh = P.d_sh;
+    A->d_out = off;
+    A->w_numel = w;
+    A->nnz_total = P.nnz_total;
+    A->unit_weights = true;
+    schedule(*A);
+    return A;
 }
 
 }  // namespace cgtp

@@ -33,10 +33,11 @@
  *
  * Memory and streams: every device buffer is owned by the caller, must be a
  * device pointer to contiguous row-major data of the plan's dtype, aligned
- * to its element size, and outputs must not alias inputs.  The library never allocates,
- * frees or synchronises device memory; the one entry point that needs
- * temporary memory (cgtp_tp_backward, uvw) takes it from the caller.  `stream` is a hipStream_t (NULL =
- * the default stream); all work is enqueued on it asynchronously.
+ * to its element size, and outputs must not alias inputs.  The library
+ * never allocates, frees or synchronises device memory; the entry points that
+ * need temporary memory (cgtp_tp_backward and cgtp_conv_backward_ws, uvw)
+ * take it from the caller.  `stream` is a hipStream_t (NULL = the default
+ * stream); all work is enqueued on it asynchronously.
  * Index arrays are int32 and N, E < 2^31.
  *
  * Errors: every entry point returns a cgtp_status; the message of the last
@@ -145,7 +146,7 @@ cgtp_status cgtp_tp_forward(const cgtp_plan *plan, int64_t B, const void *x, con
  *   0 for uvu, where workspace may be NULL) and are summed in chunk order.
  * Any of grad_x / grad_y / grad_w may be NULL to skip it; outputs are
  * overwritten, one owner per element, no atomics, bitwise deterministic.
- * B = 0 is a no-op.
+ * B = 0 writes nothing, except that a uvw grad_w is set to zero.
  */
 cgtp_status cgtp_tp_backward_workspace_size(const cgtp_plan *plan, int64_t B, size_t *bytes);
 /* uvw: the backward kernels form their own module, generated and compiled on the first call;
@@ -239,6 +240,43 @@ cgtp_status cgtp_conv_backward(const cgtp_plan *plan, int64_t N, int64_t E, cons
                                const int32_t *t_dst, const void *x, const void *y, const void *w,
                                const void *grad_out, void *grad_x, void *grad_y, void *grad_w,
                                void *stream);
+
+/*
+ * Fused convolution backward with a caller workspace; needed by uvw plans
+ * (shared [weight_numel] W, fully connected multiplicity mixing inside the
+ * convolution; Sobek page, Abstract: gradients of the same operator without
+ * edge-sized intermediates).  With g = grad_out [N][d_out] and, per receiver
+ * n and path p, G_p[n,u,k] = sum_w W_p[u][w] g[n, o_p + w(2l3+1) + k]:
+ *   grad_x[s, a_p + u(2l1+1) + i] = sum_{e: col[e]=s} sum_p sum_{jk} C y[e,j] G_p[n_e,u,k]
+ *   grad_y[e, b_p + j]            = sum_p sum_u sum_{ik} C x[col[e],u,i] G_p[n_e,u,k]
+ *   grad_w[w_p + u*mul_out + w]   = sum_n sum_k T_p[n,u,k] g[n, o_p + w(2l3+1) + k],
+ *     T_p[n,u,k] = sum_{e into n} sum_{ij} C x[col[e],u,i] y[e,j]
+ * (n_e the receiver of edge e).  G is computed per 16-receiver tile on MFMA
+ * into the workspace, then read by one sender-ordered pass over the transpose
+ * (grad_x, grad_y: one owner per row); grad_w is one partial per 16-receiver
+ * tile (the forward's edge pass, then MFMA over the tile's receivers) summed
+ * in tile order.  No atomics, bitwise deterministic.  `order` is the receiver
+ * schedule of the grad_w pass (as in cgtp_conv_forward_ordered, NULL =
+ * natural; results do not depend on it).  workspace: device memory of at
+ * least cgtp_conv_backward_workspace_size(plan, N, E) bytes, 256-byte
+ * aligned, caller-owned, disjoint from every argument; its contents on entry
+ * are ignored and on return unspecified.  Any of grad_x / grad_y / grad_w may
+ * be NULL to skip it; outputs are overwritten; N = 0 sets grad_w to zero.
+ * uvu plans: identical to cgtp_conv_backward (order and workspace unused,
+ * size 0).  The uvw backward kernels are generated and compiled on the first
+ * call (then cached); cgtp_plan_conv_uvw_backward_prepare does it ahead of
+ * time on the host, and cgtp_plan_conv_uvw_backward_source returns the
+ * sources (module 0: G and grad_w kernels; 1: the sender pass; owned by the
+ * plan, NULL before they exist).
+ */
+cgtp_status cgtp_conv_backward_workspace_size(const cgtp_plan *plan, int64_t N, int64_t E, size_t *bytes);
+cgtp_status cgtp_conv_backward_ws(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
+                                  const int32_t *col, const int32_t *order, const int32_t *t_row_ptr,
+                                  const int32_t *t_edge, const int32_t *t_dst, const void *x, const void *y,
+                                  const void *w, const void *grad_out, void *grad_x, void *grad_y, void *grad_w,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+cgtp_status cgtp_plan_conv_uvw_backward_prepare(const cgtp_plan *plan);
+const char *cgtp_plan_conv_uvw_backward_source(const cgtp_plan *plan, int32_t module);
 
 /*
  * Fused convolution double backward: the higher partial derivatives used for

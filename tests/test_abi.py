@@ -174,7 +174,47 @@ def test_call_errors_before_any_gpu_work():
                                 fake, fake, fake, s) == inval
     assert L.cgtp_conv_backward(uvw.handle, 4, 4, fake, fake, fake, fake, fake, fake, fake, fake, fake,
                                 fake, fake, fake, s) == unsup
+    # uvw convolution backward: the workspace is checked (size, alignment, overlap) before any GPU call
+    cuvw = cg.plan_for(synth.EXTRA_WORKLOADS["c2uvw"], "f32")
+    wsz = ctypes.c_size_t()
+    assert L.cgtp_conv_backward_workspace_size(cuvw.handle, 4, 4, ctypes.byref(wsz)) == 0 and wsz.value > 0
+    big = ctypes.c_void_p(1 << 30)
+
+    def ws_call(workspace, nbytes, grad_w=ctypes.c_void_p(1 << 28), order=null):
+        # plan, N, E, row_ptr, col, order, t_row_ptr, t_edge, t_dst, x, y, w, g, gx, gy, gw, ws, bytes, stream
+        st = L.cgtp_conv_backward_ws(cuvw.handle, 4, 4, fake, fake, order, fake, fake, fake, fake, fake, fake,
+                                     fake, null, null, grad_w, workspace, ctypes.c_size_t(nbytes), s)
+        return st, cg.last_error()
+    assert ws_call(big, wsz.value - 1) == (inval, "workspace too small (see cgtp_conv_backward_workspace_size)")
+    assert ws_call(null, wsz.value) == (inval, "workspace is NULL")
+    assert ws_call(ctypes.c_void_p((1 << 30) + 64), wsz.value) == (inval, "workspace is not aligned to 256 bytes")
+    assert ws_call(big, wsz.value, grad_w=ctypes.c_void_p((1 << 30) + 256)) == (inval, "grad_w overlaps workspace")
+    assert ws_call(big, wsz.value, order=ctypes.c_void_p((1 << 20) + 2)) == (inval, "order is not aligned to 4 bytes")
+    assert L.cgtp_conv_backward_ws(cuvw.handle, 4, 4, fake, fake, null, fake, fake, fake, fake, fake, fake, fake,
+                                   null, null, null, null, z, s) == 0            # nothing requested
     # zero-sized work is a no-op that succeeds without touching memory
     assert L.cgtp_tp_forward(plan.handle, 0, null, null, null, 0, null, s) == 0
     assert L.cgtp_spherical_harmonics(2, 0, 0, null, null, s) == 0
     assert L.cgtp_conv_forward(plan.handle, 0, 0, null, null, null, null, null, null, s) == 0
+
+
+def test_conv_uvw_backward_workspace_and_modules():
+    """Workspace of the uvw convolution backward: G (N x sum_p mul_in (2 l3 + 1), padded to 256
+    bytes) plus one dW partial per 16-receiver tile; its two modules build on the host."""
+    plan = cg.plan_for(synth.EXTRA_WORKLOADS["c2uvw"], "f32")
+    dg = sum(plan.path(p)["mul_in"] * (2 * plan.path(p)["l3"] + 1) for p in range(plan.num_paths))
+    for n in (1, 17, 5000):
+        want = -(-n * dg * 4 // 256) * 256 + -(-n // 16) * plan.weight_numel * 4
+        assert cg.conv_backward_workspace_size(plan, n, 40 * n) == want
+    assert cg.conv_backward_workspace_size(plan, 0, 0) == 0
+    assert cg.conv_backward_workspace_size(cg.plan_for(synth.WORKLOADS["c2"], "f32"), 5000, 200_000) == 0
+    with pytest.raises(cg.CgtpError, match="CGTP_ERR_UNSUPPORTED"):
+        cg.plan_for(synth.WORKLOADS["c2"], "f32").conv_uvw_backward_source(0)
+    src_gw = plan.conv_uvw_backward_source(0)
+    src_xy = plan.conv_uvw_backward_source(1)
+    assert "cgtp_conv_uvw_bwd_g" in src_gw and "cgtp_conv_uvw_bwd_w" in src_gw and "cgtp_reduce_chunks" in src_gw
+    assert "cgtp_conv_uvw_bwd_xy" in src_xy
+    # the sender pass has unit weights: it reads no weight and writes no weight gradient
+    assert "&w[" not in src_xy and "dw[" not in src_xy
+    for src in (src_gw, src_xy):
+        assert "atomic" not in src.lower()
