@@ -270,6 +270,23 @@ def conv_forward_radial_rows(tab: Tables, row_ptr, col, x, y, rho, theta, rows, 
                        np.asarray(y, np.float64)[eidx], w, n_threads)
 
 
+def conv_backward_radial_rows(tab: Tables, row_ptr, col, x, y, rho, theta, g, rows, senders, n_threads=None):
+    """Radial-projection convolution backward on a sample, from the explicit uvu backward loops
+    with W_e = rho[e] @ Theta formed per edge (a library matmul): dY and drho = dW_e Theta^T for
+    every edge of the receivers ``rows``, dx of the nodes ``senders`` and dTheta = sum over every
+    edge of rho[e]^T dW_e.  Returns (edge ids, dx, dy, drho, dtheta)."""
+    rho = np.asarray(rho, np.float64)
+    theta = np.asarray(theta, np.float64)
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    g = np.asarray(g, np.float64)
+    w = rho @ theta
+    eidx, dy, dw = conv_backward_edge_rows(tab, row_ptr, col, x, y, w, g, rows, n_threads)
+    _, _, dw_all = conv_backward_edge_rows(tab, row_ptr, col, x, y, w, g, np.arange(len(row_ptr) - 1), n_threads)
+    dx = conv_backward_x_rows(tab, row_ptr, col, y, w, g, senders, n_threads)
+    return eidx, dx, dy, dw @ theta.T, rho.T @ dw_all
+
+
 def conv_backward_uvw_rows(tab: Tables, row_ptr, col, x, y, w, g, edges, senders, n_threads=None):
     """uvw convolution backward on a sample: dY of the edges ``edges``, dx of the nodes
     ``senders`` (all their edges) and dW over every edge, from the explicit uvw backward loops

@@ -212,6 +212,19 @@ def conv_forward_radial(prob: Problem, row_ptr, col, x, y, rho, theta):
     return conv_forward(prob, row_ptr, col, x, y, w)
 
 
+def conv_backward_radial(prob: Problem, row_ptr, col, x, y, rho, theta, g):
+    """Gradients of sum(g * conv_forward_radial(x, y, rho, Theta)) with respect to x, y, rho and
+    Theta.
+
+    Sobek page, Abstract: the radial projection is reassociated through the backward as well.  The
+    plain definition is the chain rule through W = rho @ Theta (library matmuls):
+      (dx, dy, dW) = conv_backward(x, y, W, g),   drho = dW @ Theta^T,   dTheta = rho^T @ dW."""
+    rho = np.asarray(rho, np.float64)
+    theta = np.asarray(theta, np.float64)
+    dx, dy, dw = conv_backward(prob, row_ptr, col, x, y, rho @ theta, g)
+    return dx, dy, dw @ theta.T, rho.T @ dw
+
+
 def tp_backward(prob: Problem, x, y, w, g):
     """Gradients of sum(g * tp_forward(x, y, W)) for the batched product (use case A).
 

@@ -490,6 +490,58 @@ def test_cpu_loops_radial_match_numpy():
 
 
 
+def test_radial_conv_backward_matches_autograd_and_loops():
+    """dx, dy, drho, dTheta of sum(g * conv(x, y, rho Theta)): torch autograd (CPU, float64) through
+    the dense coupling with W = rho Theta written into the einsum, and the explicit loops."""
+    import torch
+    prob = problem("3x0e+2x1o+3x2e", 2, 2)
+    rng = np.random.default_rng(26)
+    row_ptr, col, x, vec, w, g = conv_inputs(prob, rng, 8, 33)
+    y = rng.standard_normal((33, prob.d_sh))
+    rho = rng.standard_normal((33, 5))
+    theta = rng.standard_normal((5, prob.weight_numel))
+    t = torch.from_numpy(dense_tensor(prob))
+    dst = torch.from_numpy(ref.receivers_of(row_ptr))
+    colt = torch.from_numpy(np.asarray(col, np.int64))
+    X, Y, Rho, Th = (torch.tensor(a, requires_grad=True) for a in (x, y, rho, theta))
+    msg = torch.einsum("abvo,ea,eb,er,rv->eo", t, X[colt], Y, Rho, Th)
+    out = torch.zeros(8, prob.d_out, dtype=torch.float64).index_add(0, dst, msg)
+    want = torch.autograd.grad((torch.from_numpy(g) * out).sum(), (X, Y, Rho, Th))
+    got = ref.conv_backward_radial(prob, row_ptr, col, x, y, rho, theta, g)
+    for a, b in zip(got, want):
+        assert np.allclose(a, b.numpy(), atol=1e-10)
+    rows, senders = np.array([6, 0, 3]), np.array([7, 2, 0, 5])
+    eidx, dx, dy, drho, dtheta = loops.conv_backward_radial_rows(loops.Tables(prob), row_ptr, col, x, y, rho, theta,
+                                                                 g, rows, senders)
+    assert np.allclose(dx, got[0][senders], atol=1e-11)
+    assert np.allclose(dy, got[1][eidx], atol=1e-11)
+    assert np.allclose(drho, got[2][eidx], atol=1e-11)
+    assert np.allclose(dtheta, got[3], atol=1e-10)
+
+
+def test_radial_conv_backward_one_hot_and_adjoint():
+    """A rho one-hot on channel r gives dTheta zero outside row r and equal there to the sum of the
+    stored-weight gradients over all edges, and drho[e][r] = <dW_e, Theta[r]>; for any direction V,
+    <dTheta, V> = <g, conv(x, y, rho V)> (the forward is linear in Theta)."""
+    prob = problem("2x0e+3x1o+2x2e", 2, 2)
+    rng = np.random.default_rng(27)
+    row_ptr, col, x, vec, w, g = conv_inputs(prob, rng, 6, 25)
+    y = rng.standard_normal((25, prob.d_sh))
+    theta = rng.standard_normal((4, prob.weight_numel))
+    onehot = np.zeros((25, 4))
+    onehot[:, 2] = 1.0
+    dx, dy, drho, dtheta = ref.conv_backward_radial(prob, row_ptr, col, x, y, onehot, theta, g)
+    _, _, dw = ref.conv_backward(prob, row_ptr, col, x, y, np.tile(theta[2], (25, 1)), g)
+    assert np.allclose(dtheta[[0, 1, 3]], 0.0) and np.allclose(dtheta[2], dw.sum(axis=0), atol=1e-11)
+    assert np.allclose(drho, dw @ theta.T, atol=1e-11)
+    rho = rng.standard_normal((25, 4))
+    v = rng.standard_normal(theta.shape)
+    _, _, _, dtheta = ref.conv_backward_radial(prob, row_ptr, col, x, y, rho, theta, g)
+    lhs = float(np.sum(dtheta * v))
+    rhs = float(np.sum(g * ref.conv_forward_radial(prob, row_ptr, col, x, y, rho, v)))
+    assert abs(lhs - rhs) <= 1e-10 * max(1.0, abs(rhs))
+
+
 # ------------------------------------------------------------------------------ batched backward
 
 def _uvw_tp_problem():
