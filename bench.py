@@ -326,9 +326,10 @@ def bench_conv_uvw(a, spec, plan, d, host_graph, device):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline_radial(spec, seed, host_graph, R, max_seconds=30.0):
+def cpu_baseline_radial(spec, seed, host_graph, R, max_seconds=30.0, backward=False):
     """The oracle (W = rho @ Theta for the slice's edges, then the explicit uvu loops) on a
-    contiguous receiver slice with ~5% of the edges; random values.  Rate = slice edges/s."""
+    contiguous receiver slice with ~5% of the edges (with ``backward`` also dx, dY, drho and dTheta
+    of that sub-graph); random values.  Rate = slice edges/s."""
     from oracle import irreps as oirreps
     from oracle import loops
     row_ptr, col = (np.asarray(a, dtype=np.int64) for a in host_graph)
@@ -349,17 +350,21 @@ def cpu_baseline_radial(spec, seed, host_graph, R, max_seconds=30.0):
     rho = rng.standard_normal((e1 - e0, R))
     theta = rng.standard_normal((R, prob.weight_numel))
     rows = np.arange(stop - start)
+    g = rng.standard_normal((stop - start, prob.d_out))
     t0 = time.perf_counter()
     reps = 0
     while True:
         loops.conv_forward_radial_rows(tab, sub_ptr, inv, x, y, rho, theta, rows, threads)
+        if backward:
+            loops.conv_backward_radial_rows(tab, sub_ptr, inv, x, y, rho, theta, g, rows, np.arange(len(uniq)), threads)
         reps += 1
         el = time.perf_counter() - t0
         if el >= 10.0 or el >= max_seconds:
             break
+    what = "forward and backward (dx, dY, drho, dTheta)" if backward else "forward"
     return {"value": (e1 - e0) * reps / el, "unit": "edges/s", "cores": threads, "kind": "oracle",
             "sample": f"receivers [{start},{stop}) = {e1 - e0} of {E} edges, R = {R}: W = rho @ Theta for those "
-                      f"edges, then the fp64 explicit loops; mean of {reps} rep(s)"}
+                      f"edges, then the fp64 explicit loops, {what}; mean of {reps} rep(s)"}
 
 
 def bench_radial(a, spec, plan, d, host_graph, device):
@@ -393,27 +398,51 @@ def bench_radial(a, spec, plan, d, host_graph, device):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / a.steps, (time.perf_counter() - t0) / a.steps
 
-    ms, wall = timed(lambda: cg.conv_forward_radial(plan, d["row_ptr"], d["col"], d["x"], y, rho, theta, out=out,
-                                                     order=order))
+    fwd = lambda: cg.conv_forward_radial(plan, d["row_ptr"], d["col"], d["x"], y, rho, theta, out=out, order=order)
+    ms, wall = timed(fwd)
     ms_w, _ = timed(lambda: cg.conv_forward(plan, d["row_ptr"], d["col"], d["x"], y, d["w"], out=out, order=order))
     alg = (N + 1) * 4 + E * 4 + es * (N * plan.d_x + E * plan.d_sh + E * R + R * plan.weight_numel + N * plan.d_out)
-    achieved = alg / (ms * 1e-3) / 1e9
+    config = {"workload": spec.name, "N": N, "E": E, "in_irreps": spec.in_irreps, "sh_lmax": spec.lmax_sh,
+              "paths": plan.num_paths, "d_out": plan.d_out, "radial_features": R,
+              "step": "conv_forward_radial (W_e = rho_e Theta rebuilt in registers, never stored)",
+              "receiver_schedule": "natural" if a.natural_order else "heavy-first", "fwd_ms": ms,
+              "materialised_weights_fwd_ms": ms_w}
+    dom = ("cgtp_conv_fwd_radial", ms, alg)
+    if a.backward:
+        tr = cg.graph_transpose(d["row_ptr"], d["col"])
+        ws = torch.empty(cg.conv_backward_radial_workspace_size(plan, N, E, R), dtype=torch.uint8, device=device)
+        outs = (torch.empty_like(d["x"]), torch.empty_like(y), torch.empty_like(rho), torch.empty_like(theta))
+        bwd = lambda: cg.conv_backward_radial(plan, d["row_ptr"], d["col"], tr, d["x"], y, rho, theta, d["g"],
+                                              outs=outs, workspace=ws)
+        bms, _ = timed(bwd)
+
+        def step():
+            fwd()
+            bwd()
+        _, wall = timed(step)
+        gw = (torch.empty_like(d["x"]), torch.empty_like(y), torch.empty_like(d["w"]))
+        bms_w, _ = timed(lambda: cg.conv_backward(plan, d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"], *gw))
+        # reads x, Y, rho, Theta, g and the transpose once; writes dx, dY, drho once (the dTheta
+        # partials are chunk-sized, not edge-sized)
+        alg_b = (N + 1) * 4 + 2 * E * 4 + es * (2 * N * plan.d_x + 2 * E * plan.d_sh + 2 * E * R
+                                               + 2 * R * plan.weight_numel + N * plan.d_out)
+        config.update({"step": "conv_forward_radial + conv_backward_radial (dx, dY, drho, dTheta; W_e and dW_e "
+                               "never stored)", "bwd_ms": bms, "materialised_weights_bwd_ms": bms_w,
+                       "bwd_launches": plan.radial_source(R).count("void rbw_g")})
+        if bms >= ms:
+            dom = ("cgtp_conv_bwd_radial", bms, alg_b)
+    achieved = dom[2] / (dom[1] * 1e-3) / 1e9
     line = {
         "metric": METRIC, "value": E / wall, "unit": "edges/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": wall * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": a.dtype, "data": "synthetic",
-        "config": {"workload": spec.name, "N": N, "E": E, "in_irreps": spec.in_irreps, "sh_lmax": spec.lmax_sh,
-                   "paths": plan.num_paths, "d_out": plan.d_out, "radial_features": R,
-                   "step": "conv_forward_radial (W_e = rho_e Theta rebuilt in registers, never stored)",
-                   "receiver_schedule": "natural" if a.natural_order else "heavy-first", "fwd_ms": ms,
-                   "materialised_weights_fwd_ms": ms_w},
-        "roofline": {"bound": "hbm", "kernel": "cgtp_conv_fwd_radial", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        "dtype": a.dtype, "data": "synthetic", "config": config,
+        "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "algorithmic_bytes_per_launch": alg, "avg_launch_ms": ms},
+                     "algorithmic_bytes_per_launch": dom[2], "avg_launch_ms": dom[1]},
         "cpu_baseline": None,
     }
     if not a.no_cpu:
-        line["cpu_baseline"] = cpu_baseline_radial(spec, a.seed, host_graph, R)
+        line["cpu_baseline"] = cpu_baseline_radial(spec, a.seed, host_graph, R, backward=a.backward)
     print(json.dumps(line), flush=True)
 
 

@@ -26,7 +26,7 @@ EXPORTS = ("cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info_get", "cgtp_
            "cgtp_conv_forward_radial", "cgtp_plan_radial_prepare", "cgtp_plan_radial_source",
            "cgtp_tp_backward_workspace_size", "cgtp_plan_uvw_backward_prepare", "cgtp_plan_uvw_backward_source",
            "cgtp_conv_backward_workspace_size", "cgtp_conv_backward_ws", "cgtp_plan_conv_uvw_backward_prepare",
-           "cgtp_plan_conv_uvw_backward_source")
+           "cgtp_plan_conv_uvw_backward_source", "cgtp_conv_backward_radial", "cgtp_conv_backward_radial_workspace_size")
 _STRING_RESULTS = ("cgtp_last_error", "cgtp_plan_source", "cgtp_plan_radial_source", "cgtp_plan_uvw_backward_source",
                    "cgtp_plan_conv_uvw_backward_source")
 
@@ -69,6 +69,8 @@ def lib():
         L.cgtp_plan_conv_uvw_backward_source.argtypes = [vp, i32]
         L.cgtp_conv_backward_workspace_size.argtypes = [vp, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
         L.cgtp_conv_backward_ws.argtypes = [vp, i64, i64] + [vp] * 14 + [ctypes.c_size_t, vp]
+        L.cgtp_conv_backward_radial_workspace_size.argtypes = [vp, i64, i64, i32, ctypes.POINTER(ctypes.c_size_t)]
+        L.cgtp_conv_backward_radial.argtypes = [vp, i64, i64] + [vp] * 7 + [i32] + [vp] * 8 + [ctypes.c_size_t, vp]
         L.cgtp_plan_source.argtypes = [vp]
         L.cgtp_plan_create.argtypes = [ctypes.c_char_p] * 3 + [ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp)]
         L.cgtp_plan_destroy.argtypes = [vp]
@@ -318,6 +320,42 @@ def conv_forward_radial(plan: Plan, row_ptr, col, x, y, rho, theta, out=None, or
                                           _dev(rho, "rho", dt, (E, R)), _dev(theta, "theta", dt, (R, plan.weight_numel)),
                                           _dev(out, "out", dt, (N, plan.d_out)), _stream(stream, x.device)))
     return out
+
+
+def conv_backward_radial_workspace_size(plan: Plan, N: int, E: int, R: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().cgtp_conv_backward_radial_workspace_size(plan.handle, N, E, R, ctypes.byref(n)))
+    return n.value
+
+
+def conv_backward_radial(plan: Plan, row_ptr, col, transpose, x, y, rho, theta, grad_out, outs=(None, None, None, None),
+                         need=(True, True, True, True), workspace=None, stream=None):
+    """Backward of the radial-projection convolution: (grad_x, grad_y, grad_rho, grad_theta); entries
+    not in ``need`` are None and not computed.  The dTheta workspace is allocated here unless given."""
+    import torch
+    N, E = row_ptr.shape[0] - 1, col.shape[0]
+    R = theta.shape[0]
+    dt = plan.torch_dtype
+    dev = x.device
+    shapes = ((N, plan.d_x), (E, plan.d_sh), (E, R), (R, plan.weight_numel))
+    res = [None if not nd else (torch.empty(sh, dtype=dt, device=dev) if o is None else o)
+           for o, nd, sh in zip(outs, need, shapes)]
+    nbytes = conv_backward_radial_workspace_size(plan, N, E, R) if res[3] is not None else 0
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ws = ctypes.c_void_p(0) if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    t_row_ptr, t_edge, t_dst = transpose
+    names = ("grad_x", "grad_y", "grad_rho", "grad_theta")
+    _check(lib().cgtp_conv_backward_radial(
+        plan.handle, N, E, _dev(row_ptr, "row_ptr", torch.int32), _dev(col, "col", torch.int32),
+        _dev(t_row_ptr, "t_row_ptr", torch.int32, (N + 1,)), _dev(t_edge, "t_edge", torch.int32, (E,)),
+        _dev(t_dst, "t_dst", torch.int32, (E,)), _dev(x, "x", dt, (N, plan.d_x)), _dev(y, "y", dt, (E, plan.d_sh)), R,
+        _dev(rho, "rho", dt, (E, R)), _dev(theta, "theta", dt, (R, plan.weight_numel)),
+        _dev(grad_out, "grad_out", dt, (N, plan.d_out)),
+        *[_ptr_or_null(r, nm, dt, sh) for r, nm, sh in zip(res, names, shapes)],
+        ws, ctypes.c_size_t(wsb), _stream(stream, dev)))
+    return tuple(res)
 
 
 def graph_transpose(row_ptr, col, t_row_ptr=None, t_edge=None, t_dst=None, stream=None):

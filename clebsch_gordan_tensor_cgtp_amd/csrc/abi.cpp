@@ -96,6 +96,15 @@ void launch_reduce(hipFunction_t f, int64_t wn, void *ws, long nchunks, void *ou
               "hipModuleLaunchKernel");
 }
 
+// Radial backward: chunks of spc consecutive senders, one workgroup and one dTheta partial each
+// (at most 1024 chunks)
+void radial_chunks(int64_t N, long &spc, long &nchunks)
+{
+    nchunks = (long)std::min<int64_t>(N, 1024);
+    spc = nchunks > 0 ? (long)((N + nchunks - 1) / nchunks) : 1;
+    nchunks = nchunks > 0 ? (long)((N + spc - 1) / spc) : 0;
+}
+
 // Sender pass of the backward (one launch per path group, in order): dx, dY and (uvu) dW from
 // the output gradient g; A is the plan itself or the uvw convolution's unit-weight plan.
 void sender_pass(cgtp::Plan &A, int64_t N, int64_t E, const int32_t *t_row_ptr, const int32_t *t_edge,
@@ -538,11 +547,103 @@ cgtp_status cgtp_conv_forward_radial(const cgtp_plan *plan, int64_t N, int64_t E
         require_disjoint(out, no, "out", row_ptr, (N + 1) * 4, "row_ptr");
         require_disjoint(out, no, "out", col, E * 4, "col");
         require_disjoint(out, no, "out", order, N * 4, "order");
-        hipFunction_t f = cgtp::radial_function_for_current_device(P, R);
+        hipFunction_t f = cgtp::radial_functions_for_current_device(P, R).fwd;
         int64_t waves = N * P.fwd_tasks;
         long nrows = (long)N, nwaves = (long)waves;
         void *args[] = {&row_ptr, &col, &x, &y, &rho, &theta, &out, &nrows, &nwaves, &order};
         launch(f, waves, args, stream);
+    });
+}
+
+cgtp_status cgtp_conv_backward_radial_workspace_size(const cgtp_plan *plan, int64_t N, int64_t E, int32_t R,
+                                                    size_t *bytes)
+{
+    return guarded([&] {
+        require(plan != nullptr && bytes != nullptr, "plan and bytes must be non-NULL");
+        check_graph_sizes(N, E);
+        require(R >= 1 && R <= 64, "R (radial features per edge) must be in [1, 64]");
+        long spc, nchunks;
+        radial_chunks(N, spc, nchunks);
+        *bytes = (size_t)nchunks * R * plan->p.w_numel * elem(plan->p);
+    });
+}
+
+cgtp_status cgtp_conv_backward_radial(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
+                                      const int32_t *col, const int32_t *t_row_ptr, const int32_t *t_edge,
+                                      const int32_t *t_dst, const void *x, const void *y, int32_t R, const void *rho,
+                                      const void *theta, const void *grad_out, void *grad_x, void *grad_y,
+                                      void *grad_rho, void *grad_theta, void *workspace, size_t workspace_bytes,
+                                      void *stream)
+{
+    return guarded([&] {
+        require(plan != nullptr, "plan is NULL");
+        cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
+        check_graph_sizes(N, E);
+        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "the radial projection takes uvu plans");
+        require(R >= 1 && R <= 64, "R (radial features per edge) must be in [1, 64]");
+        const size_t es = elem(P);
+        if ((size_t)R * P.w_numel * es > 65536)
+            throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "R * weight_numel must fit 64 KB of LDS (Theta is staged there)");
+        if (!grad_x && !grad_y && !grad_rho && !grad_theta) return;
+        const size_t nth = (size_t)R * P.w_numel * es;
+        if (grad_theta) require_ptr(grad_theta, "grad_theta", es);
+        long spc, nchunks;
+        radial_chunks(N, spc, nchunks);
+        const size_t ws_need = grad_theta ? (size_t)nchunks * nth : 0;
+        if (N > 0) {
+            require_ptr(row_ptr, "row_ptr", 4);
+            require_ptr(t_row_ptr, "t_row_ptr", 4);
+            require_ptr(x, "x", es);
+            require_ptr(theta, "theta", es);
+            if (E > 0) {
+                require_ptr(col, "col", 4);
+                require_ptr(t_edge, "t_edge", 4);
+                require_ptr(t_dst, "t_dst", 4);
+                require_ptr(y, "y", es);
+                require_ptr(rho, "rho", es);
+                require_ptr(grad_out, "grad_out", es);
+            }
+            if (grad_x) require_ptr(grad_x, "grad_x", es);
+            if (E > 0 && grad_y) require_ptr(grad_y, "grad_y", es);
+            if (E > 0 && grad_rho) require_ptr(grad_rho, "grad_rho", es);
+            if (ws_need) {
+                require_ptr(workspace, "workspace", 256);
+                require(workspace_bytes >= ws_need, "workspace too small (see cgtp_conv_backward_radial_workspace_size)");
+            }
+            const void *ins[] = {x, y, rho, theta, grad_out, row_ptr, col, t_row_ptr, t_edge, t_dst};
+            const size_t inn[] = {N * P.d_x * es, E * P.d_sh * es, E * (size_t)R * es, nth, N * P.d_out * es,
+                                  (size_t)(N + 1) * 4, (size_t)E * 4, (size_t)(N + 1) * 4, (size_t)E * 4, (size_t)E * 4};
+            const char *inm[] = {"x", "y", "rho", "theta", "grad_out", "row_ptr", "col", "t_row_ptr", "t_edge", "t_dst"};
+            void *outs[] = {grad_x, grad_y, grad_rho, grad_theta, ws_need ? workspace : nullptr};
+            const size_t outn[] = {N * P.d_x * es, E * P.d_sh * es, E * (size_t)R * es, nth, ws_need};
+            const char *outm[] = {"grad_x", "grad_y", "grad_rho", "grad_theta", "workspace"};
+            for (int a = 0; a < 5; ++a) {
+                for (int b = 0; b < 10; ++b) require_disjoint(outs[a], outn[a], outm[a], ins[b], inn[b], inm[b]);
+                for (int b = a + 1; b < 5; ++b) require_disjoint(outs[a], outn[a], outm[a], outs[b], outn[b], outm[b]);
+            }
+        }
+        const auto &F = cgtp::radial_functions_for_current_device(P, R);
+        if (!F.bwd)
+            throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "radial backward: Theta and the reduction buffer exceed the LDS");
+        if (N == 0) {
+            if (grad_theta) launch_reduce(F.reduce, (int64_t)R * P.w_numel, workspace, 0, grad_theta, stream);
+            return;
+        }
+        const std::vector<cgtp::Group> &groups = cgtp::radial_bwd_groups_of(P, R);
+        void *ws = ws_need ? workspace : nullptr;
+        long nnodes = (long)N;
+        // one launch per path group, in order (later groups add to dx, dY and drho)
+        for (int grp = 0; grp < (int)groups.size(); ++grp) {
+            const double eg = (double)E / (double)N / groups[grp].es;
+            int wpr = eg >= 16 ? 4 : eg >= 8 ? 2 : 1;
+            if (const char *env = std::getenv("CGTP_BWD_WPR")) wpr = std::max(1, std::min(4, std::atoi(env)));
+            void *args[] = {&t_row_ptr, &t_edge, &t_dst, &x, &y, &rho, &theta, &grad_out, &grad_x, &grad_y, &grad_rho,
+                            &ws, &nnodes, &spc, &wpr, &grp};
+            check_hip(hipModuleLaunchKernel(F.bwd, (unsigned)nchunks, 1, 1, 64 * wpr, 1, 1, 0,
+                                            static_cast<hipStream_t>(stream), args, nullptr),
+                      "hipModuleLaunchKernel");
+        }
+        if (grad_theta) launch_reduce(F.reduce, (int64_t)R * P.w_numel, workspace, nchunks, grad_theta, stream);
     });
 }
 

@@ -502,9 +502,14 @@ void emit_slot_sum(Out &o, const Plan &P)
 // and dY blocks are written by the first group that touches them (group 0 also
 // writes zeros for blocks no path touches) and accumulated by later groups;
 // the groups are separate launches in group order, so the sums are fixed.
-void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmode = false)
+// radial backward: dTheta sums reduced over the waves of a workgroup per round (bounds its LDS)
+constexpr int kRadialRound = 32;
+constexpr long kLdsBytes = 160 * 1024;  // LDS of one gfx950 workgroup
+
+void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmode = false, int radial = 0,
+                    const std::vector<Group> *radial_groups = nullptr)
 {
-    const std::vector<Group> &groups = dbl ? P.dbl_groups : P.bwd_groups;
+    const std::vector<Group> &groups = radial ? *radial_groups : dbl ? P.dbl_groups : P.bwd_groups;
     const Group &g = groups[gi];
     const bool f64 = P.dtype == CGTP_F64;
     const bool pf = g.prefetch && !rowmode;
@@ -543,6 +548,19 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
         o("const long row = blk * ", g.es, " + slot;");
         o("const bool live = row < nrows;");
         o("const long s = live ? row : nrows - 1;  // rows past the end read row nrows-1 and store nothing");
+    } else if (radial) {
+        // radial projection: a chunk of senders [c0, c1) per workgroup; dTheta partials of the
+        // chunk accumulate in registers and go to ws[chunk] at the end
+        o("__device__ __forceinline__ void rbw_g", gi,
+          "(long chunk, long c0, long c1, int wv, int lane, int wpr, T* red, const int* __restrict__ t_row_ptr, "
+          "const int* __restrict__ t_edge, const int* __restrict__ t_dst, const T* __restrict__ x, "
+          "const T* __restrict__ y, const T* __restrict__ rho, const T* th, const T* __restrict__ g, "
+          "T* __restrict__ dx, T* __restrict__ dy, T* __restrict__ drho, T* __restrict__ ws)");
+        o("{");
+        o.ind++;
+        o("const int slot = lane >> ", log2i(g.ct), ";");
+        o("const int ul = lane & ", g.ct - 1, ";");
+        o("const int stride = ", g.es, " * wpr;");
     } else {
     o("__device__ __forceinline__ void ", dbl ? "dbs" : "bwd", "_g", gi,
       "(long s, int wv, int lane, int wpr, T* red, const int* __restrict__ t_row_ptr, const int* __restrict__ t_edge, "
@@ -560,6 +578,13 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
     o("for (int tile = 0; tile < ", g.tiles, "; ++tile) {");
     o.ind++;
     o("const int u = tile * ", g.ct, " + ul;");
+    if (radial) {
+        for (int r = 0; r < radial; ++r)
+            for (int pi : g.paths) o("T ta", r, "_", pi, " = (T)0;  // dTheta[r][w_p + u] of the chunk");
+        o("for (long s = c0; s < c1; ++s) {");
+        o.ind++;
+        o("const int t0 = t_row_ptr[s], t1 = t_row_ptr[s + 1];");
+    }
     for (int b : xb) {
         const Irrep &ir = P.ins[b];
         int off = 0;
@@ -591,8 +616,9 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
             for (int j = 0; j < n_of(P.sh[b].l); ++j)
                 o(Ty, pre, "y", b, "_", j, " = LD_STREAM(&y[(size_t)", ev, " * DSH + ", off + j, "]);");
         }
+        for (int r = 0; r < radial; ++r) o(Ty, pre, "rho", r, " = LD_STREAM(&rho[(size_t)", ev, " * NRAD + ", r, "]);");
         for (int pi : g.paths) {
-            if (P.unit_weights) break;
+            if (P.unit_weights || radial) break;
             const Path &p = P.paths[pi];
             std::string wa = "LD_STREAM(&w[(size_t)" + ev + " * WROW + " + std::to_string(p.w_off) + " + u])";
             if (needs_mask(p.mul_in, g))
@@ -657,6 +683,7 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
     }
     for (int b : yb)
         for (int j = 0; j < n_of(P.sh[b].l); ++j) o("T h", b, "_", j, " = (T)0;");  // dF/dy partial of this lane
+    for (int r = 0; r < radial; ++r) o("T dr", r, " = (T)0;  // drho[e][r] partial of this lane");
     for (int pi : g.paths) {
         const Path &p = P.paths[pi];
         // B_ij = sum_k C_ijk g_k
@@ -664,6 +691,7 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
         for (const Nonzero &z : p.nz) byij[{z.i, z.j}].push_back(&z);
         o("{");
         o.ind++;
+        if (radial) emit_radial_weights(o, P, g, "", radial, pi);
         for (auto &kv : byij) {
             const auto &v = kv.second;
             std::ostringstream e;
@@ -726,9 +754,20 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
                     term("x" + b1 + "_" + i, "fx" + i);
                 }
             }
-            std::string guard = needs_mask(p.mul_in, g) ? "(u < " + std::to_string(p.mul_in) + ") && " : "";
-            if (rowmode) guard = "live && " + guard;
-            o("if (", guard, "dw) ST_STREAM(", e.str(), ", &dw[(size_t)e * WROW + ", p.w_off, " + u]);");
+            if (radial) {
+                // dW_e[p][u] is consumed at once: drho[e][r] += dW Theta[r][w_p + u] (summed over the
+                // lanes below), dTheta[r][w_p + u] += rho[e][r] dW (summed over the chunk's edges)
+                const std::string uu = needs_mask(p.mul_in, g) ? "(u < " + std::to_string(p.mul_in) + " ? u : 0)" : "u";
+                o("const T dwv = ", e.str(), ";");
+                for (int r = 0; r < radial; ++r) {
+                    o("dr", r, " = FMA(dwv, th[", (long)r * P.w_numel + p.w_off, " + ", uu, "], dr", r, ");");
+                    o("ta", r, "_", pi, " = FMA(rho", r, ", dwv, ta", r, "_", pi, ");");
+                }
+            } else {
+                std::string guard = needs_mask(p.mul_in, g) ? "(u < " + std::to_string(p.mul_in) + ") && " : "";
+                if (rowmode) guard = "live && " + guard;
+                o("if (", guard, "dw) ST_STREAM(", e.str(), ", &dw[(size_t)e * WROW + ", p.w_off, " + u]);");
+            }
         }
         if (dbl) {
             // d/dx = W fxg + ggw fx ; d/dy = W fyg + ggw fy
@@ -797,8 +836,33 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
     }
     o.ind--;
     o("}");
+    if (radial) {
+        // drho: sum over the slot's channel lanes; lane (r mod ct) of the slot writes (the first
+        // group's first tile) or adds r
+        o("if (drho) {");
+        o.ind++;
+        for (int r = 0; r < radial; ++r) o("dr", r, " = slot_sum<", g.ct, ">(dr", r, ");");
+        for (int lo = 0; lo < radial; lo += g.ct) {
+            o("{");
+            o.ind++;
+            o("T v = (T)0;");
+            o("int col = -1;");
+            for (int r = lo; r < std::min(radial, lo + g.ct); ++r) o("if (ul == ", r - lo, ") { v = dr", r, "; col = ", r, "; }");
+            o("if (col >= 0) {");
+            o.ind++;
+            o("T* p = &drho[(size_t)e * NRAD + col];");
+            o(gi == 0 ? "if (tile == 0) *p = v; else *p += v;" : "*p += v;");
+            o.ind--;
+            o("}");
+            o.ind--;
+            o("}");
+        }
+        o.ind--;
+        o("}");
+    }
     if (P.bwd_sched_barrier) o("__builtin_amdgcn_sched_barrier(0);");
     if (pf) {
+        for (int r = 0; r < radial; ++r) o("rho", r, " = nrho", r, ";");
         for (int b : t.i2)
             for (int j = 0; j < n_of(P.sh[b].l); ++j) o("y", b, "_", j, " = ny", b, "_", j, ";");
         if (!P.unit_weights)
@@ -880,6 +944,51 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
     }
     o.ind--;
     o("}");
+    if (radial) {
+        o.ind--;
+        o("}");  // senders of the chunk
+        // dTheta partial of the chunk: sum the edge slots, then the waves (fixed order), then store
+        std::vector<std::string> tas;
+        for (int r = 0; r < radial; ++r)
+            for (int pi : g.paths) tas.push_back("ta" + std::to_string(r) + "_" + std::to_string(pi));
+        const int nt = (int)tas.size();
+        for (int m = 32; m >= g.ct; m /= 2)
+            for (auto &v : tas) o(v, " += __shfl_xor(", v, ", ", m, ");");
+        o("if (wpr > 1) {");
+        o.ind++;
+        // in rounds of at most kRadialRound sums, so that the LDS buffer stays bounded
+        for (int k0 = 0; k0 < nt; k0 += kRadialRound) {
+            const int k1 = std::min(nt, k0 + kRadialRound), nk = k1 - k0;
+            o("if (wv > 0 && slot == 0) {");
+            o.ind++;
+            for (int k = k0; k < k1; ++k) o("red[(wv - 1) * ", nk * g.ct, " + ", (k - k0) * g.ct, " + ul] = ", tas[k], ";");
+            o.ind--;
+            o("}");
+            o("__syncthreads();");
+            o("if (wv == 0) {");
+            o.ind++;
+            o("for (int v = 1; v < wpr; ++v) {");
+            o.ind++;
+            for (int k = k0; k < k1; ++k) o(tas[k], " += red[(v - 1) * ", nk * g.ct, " + ", (k - k0) * g.ct, " + ul];");
+            o.ind--;
+            o("}");
+            o.ind--;
+            o("}");
+            o("__syncthreads();");
+        }
+        o.ind--;
+        o("}");
+        o("if (ws && wv == 0 && slot == 0) {");
+        o.ind++;
+        for (int r = 0; r < radial; ++r)
+            for (int pi : g.paths) {
+                const Path &p = P.paths[pi];
+                const std::string guard = needs_mask(p.mul_in, g) ? "if (u < " + std::to_string(p.mul_in) + ") " : "";
+                o(guard, "ws[(size_t)chunk * WN + ", (long)r * P.w_numel + p.w_off, " + u] = ta", r, "_", pi, ";");
+            }
+        o.ind--;
+        o("}");
+    }
     o.ind--;
     o("}");  // tile loop
     o.ind--;
@@ -2006,11 +2115,28 @@ int64_t conv_uvw_g_width(const Plan &P)
     return dg;
 }
 
-std::string generate_radial_source(const Plan &P, int R)
+long radial_bwd_red_size(const Plan &P, int R, const std::vector<Group> &bwd_groups)
+{
+    long red = bwd_red_size(bwd_groups, P);
+    for (const Group &g : bwd_groups) red = std::max<long>(red, 3L * std::min(kRadialRound, R * (int)g.paths.size()) * g.ct);
+    return red;
+}
+
+bool radial_bwd_fits(const Plan &P, int R, const std::vector<Group> &bwd_groups)
+{
+    return !bwd_groups.empty() &&
+           ((long)R * P.w_numel + radial_bwd_red_size(P, R, bwd_groups)) * (P.dtype == CGTP_F64 ? 8 : 4) <= kLdsBytes;
+}
+
+std::string generate_radial_source(const Plan &P, int R, const std::vector<Group> &bwd_groups, int bwd_waves)
 {
     Out o;
+    o("// @@section common");
     emit_preamble(o, P);
     o("#define NRAD ", R);
+    o("#define WN ((long)NRAD * WROW)");
+    emit_slot_sum(o, P);
+    o("// @@section cgtp_conv_fwd_radial");
     for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi) emit_fwd_group(o, P, gi, false, false, R);
     o("// one wave per (receiver, path group, channel tile); the workgroup first stages Theta in LDS");
     // the rebuilt weights and the double-buffered radial features need more registers than the
@@ -2040,6 +2166,47 @@ std::string generate_radial_source(const Plan &P, int R)
     o("}");
     o.ind--;
     o("}");
+    o("");
+    // backward: the sender pass with W rebuilt from rho and Theta and dW consumed into drho and
+    // the chunk's dTheta partial (Sobek page, Abstract: no edge-sized weights or adjoints)
+    o("// @@section cgtp_conv_bwd_radial");
+    const long red = radial_bwd_red_size(P, R, bwd_groups);
+    if (bwd_groups.empty() || ((long)R * P.w_numel + red) * (P.dtype == CGTP_F64 ? 8 : 4) > kLdsBytes) {
+        o("// backward not generated: Theta and the reduction buffer exceed the LDS of a workgroup");
+        return o.s.str();
+    }
+    for (int gi = 0; gi < (int)bwd_groups.size(); ++gi) emit_bwd_group(o, P, gi, false, false, R, &bwd_groups);
+    o("// one workgroup of 64*wpr threads per chunk of spc consecutive senders; `group` selects the path group");
+    o("extern \"C\" __global__ void __launch_bounds__(256, ", bwd_waves, ") cgtp_conv_bwd_radial("
+      "const int* __restrict__ t_row_ptr, const int* __restrict__ t_edge, const int* __restrict__ t_dst, "
+      "const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ rho, const T* __restrict__ theta, "
+      "const T* __restrict__ g, T* __restrict__ dx, T* __restrict__ dy, T* __restrict__ drho, T* __restrict__ ws, "
+      "long nnodes, long spc, int wpr, int group)");
+    o("{");
+    o.ind++;
+    o("__shared__ T thl[", (long)R * P.w_numel, "];  // Theta [r][w]");
+    o("__shared__ T red[", red, "];  // partial dx / dTheta of waves 1..3");
+    o("for (int i = threadIdx.x; i < ", (long)R * P.w_numel, "; i += blockDim.x) thl[i] = theta[i];");
+    o("__syncthreads();");
+    // an opaque zero offset keeps the compiler from hoisting every Theta read out of the edge loop
+    o("int zo = 0;");
+    o("asm volatile(\"\" : \"+v\"(zo));");
+    o("const T* th = thl + zo;");
+    o("const long chunk = blockIdx.x;");
+    o("const long c0 = chunk * spc;");
+    o("const long c1 = c0 + spc < nnodes ? c0 + spc : nnodes;");
+    o("const int wv = threadIdx.x >> 6;");
+    o("const int lane = threadIdx.x & 63;");
+    o("switch (group) {");
+    for (int gi = 0; gi < (int)bwd_groups.size(); ++gi)
+        o("case ", gi, ": rbw_g", gi, "(chunk, c0, c1, wv, lane, wpr, red, t_row_ptr, t_edge, t_dst, x, y, rho, th, g, dx, dy, "
+          "drho, ws); break;");
+    o("default: break;");
+    o("}");
+    o.ind--;
+    o("}");
+    o("");
+    emit_reduce_chunks(o);
     return o.s.str();
 }
 

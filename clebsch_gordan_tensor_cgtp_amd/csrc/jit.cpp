@@ -142,10 +142,18 @@ static Plan::Radial &radial_locked(Plan &P, int R)
 {
     Plan::Radial &rv = P.radial[R];
     if (rv.code.empty()) {
-        rv.source = generate_radial_source(P, R);
+        int waves = 1;
+        rv.bwd_groups = radial_bwd_groups(P, R, waves);
+        rv.source = generate_radial_source(P, R, rv.bwd_groups, waves);
         rv.code = compile_source(rv.source);
     }
     return rv;
+}
+
+const std::vector<Group> &radial_bwd_groups_of(Plan &P, int R)
+{
+    std::lock_guard<std::mutex> lock(P.mu);
+    return radial_locked(P, R).bwd_groups;
 }
 
 const std::string &prepare_radial(Plan &P, int R)
@@ -154,20 +162,22 @@ const std::string &prepare_radial(Plan &P, int R)
     return radial_locked(P, R).source;
 }
 
-hipFunction_t radial_function_for_current_device(Plan &P, int R)
+const Plan::Radial::Fns &radial_functions_for_current_device(Plan &P, int R)
 {
     int dev = 0;
     check(hipGetDevice(&dev), "hipGetDevice");
     std::lock_guard<std::mutex> lock(P.mu);
     Plan::Radial &rv = radial_locked(P, R);
     auto it = rv.loaded.find(dev);
-    if (it != rv.loaded.end()) return it->second.second;
-    hipModule_t m = nullptr;
-    hipFunction_t f = nullptr;
-    check(hipModuleLoadData(&m, rv.code.data()), "hipModuleLoadData");
-    check(hipModuleGetFunction(&f, m, "cgtp_conv_fwd_radial"), "hipModuleGetFunction(conv_fwd_radial)");
-    rv.loaded[dev] = {m, f};
-    return f;
+    if (it != rv.loaded.end()) return it->second;
+    Plan::Radial::Fns F;
+    check(hipModuleLoadData(&F.module, rv.code.data()), "hipModuleLoadData");
+    check(hipModuleGetFunction(&F.fwd, F.module, "cgtp_conv_fwd_radial"), "hipModuleGetFunction(conv_fwd_radial)");
+    if (radial_bwd_fits(P, R, rv.bwd_groups)) {
+        check(hipModuleGetFunction(&F.bwd, F.module, "cgtp_conv_bwd_radial"), "hipModuleGetFunction(conv_bwd_radial)");
+        check(hipModuleGetFunction(&F.reduce, F.module, "cgtp_reduce_chunks"), "hipModuleGetFunction(reduce)");
+    }
+    return rv.loaded.emplace(dev, F).first->second;
 }
 
 }  // namespace cgtp
@@ -256,7 +266,7 @@ void unload_modules(Plan &P)
     std::vector<std::pair<int, hipModule_t>> mods;
     for (auto &kv : P.loaded) mods.push_back({kv.first, kv.second.module});
     for (auto &r : P.radial)
-        for (auto &kv : r.second.loaded) mods.push_back({kv.first, kv.second.first});
+        for (auto &kv : r.second.loaded) mods.push_back({kv.first, kv.second.module});
     for (auto &kv : P.uvb.loaded) mods.push_back({kv.first, kv.second.module});
     for (auto &kv : P.ucb.loaded) mods.push_back({kv.first, kv.second.module});
     P.loaded.clear();

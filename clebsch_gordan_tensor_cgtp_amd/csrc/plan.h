@@ -92,11 +92,17 @@ struct Plan {
     };
     std::map<int, Loaded> loaded;
 
-    // Radial-projection forward, one module per number of radial features R (built on first use).
+    // Radial projection, one module per number of radial features R (built on first use): the
+    // forward, the backward's sender pass (dx, dY, drho, dTheta partials) and their reduction.
     struct Radial {
         std::string source;
         std::vector<char> code;
-        std::map<int, std::pair<hipModule_t, hipFunction_t>> loaded;  // per device
+        std::vector<Group> bwd_groups;  // sender-pass groups of the backward (R-dependent)
+        struct Fns {
+            hipModule_t module = nullptr;
+            hipFunction_t fwd = nullptr, bwd = nullptr, reduce = nullptr;
+        };
+        std::map<int, Fns> loaded;  // per device
     };
     std::map<int, Radial> radial;
 
@@ -134,13 +140,15 @@ void schedule(Plan &plan);
 
 // codegen.cpp
 std::string generate_source(const Plan &plan);
-std::string generate_radial_source(const Plan &plan, int R);
+std::string generate_radial_source(const Plan &plan, int R, const std::vector<Group> &bwd_groups, int bwd_waves);
+bool radial_bwd_fits(const Plan &plan, int R, const std::vector<Group> &bwd_groups);
 
 // jit.cpp
 void compile_module(Plan &plan);
 std::vector<char> compile_source(const std::string &source);
 const Plan::Loaded &module_for_current_device(Plan &plan);
-hipFunction_t radial_function_for_current_device(Plan &plan, int R);
+const Plan::Radial::Fns &radial_functions_for_current_device(Plan &plan, int R);
+const std::vector<Group> &radial_bwd_groups_of(Plan &plan, int R);
 const std::string &prepare_radial(Plan &plan, int R);
 std::string generate_uvw_backward_source(const Plan &plan);
 const std::string &prepare_uvw_backward(Plan &plan);
@@ -150,6 +158,7 @@ const Plan::ConvUvwBackward::Fns &conv_uvw_backward_for_current_device(Plan &pla
 Plan &conv_uvw_aux_plan(Plan &plan);
 const std::string &prepare_conv_uvw_backward(Plan &plan);
 std::unique_ptr<Plan> make_conv_uvw_aux(const Plan &plan);
+std::vector<Group> radial_bwd_groups(const Plan &plan, int R, int &waves_per_eu);
 void unload_modules(Plan &plan);
 int64_t conv_uvw_g_width(const Plan &plan);
 int conv_uvw_g_items(const Plan &plan, std::vector<std::pair<int, int>> *items);

@@ -261,6 +261,75 @@ static int getenv_int(const char *name, int dflt)
     return e && *e ? std::max(1, std::atoi(e)) : dflt;
 }
 
+// 32-bit registers per lane of one sender-pass group: dx accumulators and x per sender, the edge
+// operands (y, W, g), dY partials, the B block and its contractions; the double backward adds
+// ggx, ggy, ggw and a second contraction per line; the radial backward (R features) replaces W
+// by the R radial features and adds R dTheta sums per path and R drho partials.
+static int sender_estimate(const Plan &P, const std::vector<int> &ps, bool prefetch, bool dbl, int radial)
+{
+    const int word = P.dtype == CGTP_F64 ? 2 : 1;
+    std::set<int> i1s, i2s, slots;
+    int maxb = 0;
+    for (int pi : ps) {
+        std::set<std::pair<int, int>> ij;
+        for (const Nonzero &z : P.paths[pi].nz) ij.insert({z.i, z.j});
+        i1s.insert(P.paths[pi].i1);
+        i2s.insert(P.paths[pi].i2);
+        slots.insert(P.paths[pi].slot);
+        maxb = std::max(maxb, (int)ij.size() + (dbl ? 2 : 1) * (2 * P.paths[pi].l1 + 2 * P.paths[pi].l2 + 2));
+    }
+    int xs = 0, ys = 0, gs = 0;
+    for (int b : i1s) xs += 2 * P.ins[b].l + 1;
+    for (int b : i2s) ys += 2 * P.sh[b].l + 1;
+    for (int q : slots) gs += 2 * P.out[q].l + 1;
+    const int wregs = radial ? radial : (int)ps.size();
+    int edge = ys + wregs + gs + (dbl ? ys + (int)ps.size() : 0);
+    const int extra = radial ? radial * ((int)ps.size() + 1) : 0;
+    return word * ((dbl ? 3 : 2) * xs + edge + ys + maxb + extra + (prefetch ? edge : 0)) + 24;
+}
+
+// Radial-projection backward (R features): sender-pass groups packed per SH block while the
+// estimate fits the budget (a group holds at least one path); occupancy target from the largest.
+std::vector<Group> radial_bwd_groups(const Plan &P, int R, int &waves)
+{
+    // measured on the NequIP-like graph: 220 registers (fewer launches at 2 waves per SIMD) is best
+    // up to R = 8 (R = 8: 458 us against 570 us at 168), 168 above (R = 16: 797 us against 1185 us)
+    const int budget = getenv_int("CGTP_RAD_BUDGET", R <= 8 ? 220 : 168);
+    std::vector<Group> groups;
+    std::vector<int> all;
+    for (int i = 0; i < (int)P.paths.size(); ++i) all.push_back(i);
+    if (sender_estimate(P, all, false, false, R) <= budget) {
+        Group g;
+        g.paths = all;
+        groups.push_back(g);
+    } else {
+        for (int b = 0; b < (int)P.sh.size(); ++b) {
+            Group cur;
+            for (int i = 0; i < (int)P.paths.size(); ++i) {
+                if (P.paths[i].i2 != b) continue;
+                std::vector<int> trial = cur.paths;
+                trial.push_back(i);
+                if (!cur.paths.empty() && sender_estimate(P, trial, false, false, R) > budget) {
+                    groups.push_back(cur);
+                    cur = Group();
+                }
+                cur.paths.push_back(i);
+            }
+            if (!cur.paths.empty()) groups.push_back(cur);
+        }
+    }
+    int est_max = 0;
+    for (Group &g : groups) {
+        for (int pi : g.paths) g.mul = std::max(g.mul, P.paths[pi].mul_in);
+        finish_group(g);
+        g.prefetch = false;
+        est_max = std::max(est_max, sender_estimate(P, g.paths, false, false, R));
+    }
+    waves = std::max(1, std::min(4, 512 * 4 / (5 * std::max(est_max, 1))));
+    waves = getenv_int("CGTP_RAD_WAVES", waves);
+    return groups;
+}
+
 void schedule(Plan &P)
 {
     if (const char *e = std::getenv("CGTP_BWD_PREFETCH")) P.bwd_prefetch = std::atoi(e);
@@ -433,29 +502,8 @@ void schedule(Plan &P)
     // paths sharing an SH block (so that block's dY is complete in one group),
     // split when the register estimate exceeds the budget.
     {
-        auto nnz_b = [&](int pi) {
-            std::set<std::pair<int, int>> ij;
-            for (const Nonzero &z : P.paths[pi].nz) ij.insert({z.i, z.j});
-            return (int)ij.size();
-        };
-        // 32-bit registers per lane: dx accumulators and x per sender, the edge
-        // operands (y, W, g), dY partials, the B block and its contractions; the
-        // double backward adds ggx, ggy, ggw and a second contraction per line.
         auto estimate = [&](const std::vector<int> &ps, bool prefetch, bool dbl) {
-            std::set<int> i1s, i2s, slots;
-            int maxb = 0;
-            for (int pi : ps) {
-                i1s.insert(P.paths[pi].i1);
-                i2s.insert(P.paths[pi].i2);
-                slots.insert(P.paths[pi].slot);
-                maxb = std::max(maxb, nnz_b(pi) + (dbl ? 2 : 1) * (2 * P.paths[pi].l1 + 2 * P.paths[pi].l2 + 2));
-            }
-            int xs = 0, ys = 0, gs = 0;
-            for (int b : i1s) xs += 2 * P.ins[b].l + 1;
-            for (int b : i2s) ys += 2 * P.sh[b].l + 1;
-            for (int q : slots) gs += 2 * P.out[q].l + 1;
-            int edge = ys + (int)ps.size() + gs + (dbl ? ys + (int)ps.size() : 0);
-            return word * ((dbl ? 3 : 2) * xs + edge + ys + maxb + (prefetch ? edge : 0)) + 24;
+            return sender_estimate(P, ps, prefetch, dbl, 0);
         };
         // One group with every path is fastest when it fits (measured on the
         // NequIP-like graph: fewer launches and index loads, the g row read in

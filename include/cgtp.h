@@ -35,8 +35,8 @@
  * device pointer to contiguous row-major data of the plan's dtype, aligned
  * to its element size, and outputs must not alias inputs.  The library
  * never allocates, frees or synchronises device memory; the entry points that
- * need temporary memory (cgtp_tp_backward and cgtp_conv_backward_ws, uvw)
- * take it from the caller.  `stream` is a hipStream_t (NULL = the default
+ * need temporary memory (cgtp_tp_backward and cgtp_conv_backward_ws for uvw,
+ * cgtp_conv_backward_radial for dTheta) take it from the caller.  `stream` is a hipStream_t (NULL = the default
  * stream); all work is enqueued on it asynchronously.
  * Index arrays are int32 and N, E < 2^31.
  *
@@ -207,6 +207,36 @@ const char *cgtp_plan_radial_source(const cgtp_plan *plan, int32_t R);
 cgtp_status cgtp_conv_forward_radial(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
                                      const int32_t *col, const int32_t *order, const void *x, const void *y, int32_t R,
                                      const void *rho, const void *theta, void *out, void *stream);
+
+/*
+ * Backward of the radially projected convolution (Sobek page, Abstract: the
+ * reassociation extends through the backward; no edge-sized weights or
+ * adjoints).  With W_e = rho[e] @ Theta and (dx, dy, dW_e) the gradients of
+ * cgtp_conv_backward for that W:
+ *   grad_x [N][d_x], grad_y [E][d_sh]   as cgtp_conv_backward,
+ *   grad_rho [E][R]                     = dW_e Theta^T  (per edge),
+ *   grad_theta [R][weight_numel]        = sum_e rho[e]^T dW_e.
+ * One sender-ordered pass over the transpose (cgtp_graph_transpose) per path
+ * group: W_e is rebuilt from rho and the LDS copy of Theta, and dW_e is
+ * consumed at once into grad_rho (summed over the channel lanes) and into
+ * registers holding the dTheta sums of a chunk of consecutive senders.  Each
+ * chunk writes one partial to `workspace` (at least
+ * cgtp_conv_backward_radial_workspace_size bytes, 256-byte aligned,
+ * caller-owned, contents ignored on entry), summed in chunk order; neither W_e
+ * nor dW_e is stored.  Any output may be NULL to skip it (the workspace is
+ * needed only for grad_theta); outputs are overwritten, no atomics, bitwise
+ * deterministic.  N = 0 sets grad_theta to zero.  R and Theta limits as
+ * cgtp_conv_forward_radial; CGTP_ERR_UNSUPPORTED when Theta and the
+ * reduction buffer do not fit one workgroup's 160 KB of LDS.  uvu plans only.
+ */
+cgtp_status cgtp_conv_backward_radial_workspace_size(const cgtp_plan *plan, int64_t N, int64_t E, int32_t R,
+                                                    size_t *bytes);
+cgtp_status cgtp_conv_backward_radial(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
+                                      const int32_t *col, const int32_t *t_row_ptr, const int32_t *t_edge,
+                                      const int32_t *t_dst, const void *x, const void *y, int32_t R, const void *rho,
+                                      const void *theta, const void *grad_out, void *grad_x, void *grad_y,
+                                      void *grad_rho, void *grad_theta, void *workspace, size_t workspace_bytes,
+                                      void *stream);
 
 /*
  * Heavy-first receiver schedule, once per graph: order [N] (caller-owned)

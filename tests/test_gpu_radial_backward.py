@@ -1,0 +1,138 @@
+"""GPU parity of the radial-projection convolution backward (cgtp_conv_backward_radial).
+
+Bars: rel-L2 <= 1e-4 (fp32), <= 1e-10 (fp64) for dx, dY, drho and dTheta against the oracle
+(oracle.loops.conv_backward_radial_rows: the explicit uvu backward loops with W_e = rho_e Theta
+formed per edge, pinned against autograd through the dense einsum, one-hot and adjoint
+identities); repeated calls and skipped outputs change no bit of the others.  At the
+NequIP-like size (5000 receivers, 200k edges, R = 8) dTheta is checked in full, dY and drho on
+the edges of sampled receivers and dx on sampled senders.
+"""
+import numpy as np
+import pytest
+
+from clebsch_gordan_tensor_cgtp_amd import binding as cg
+from clebsch_gordan_tensor_cgtp_amd import synth
+from oracle import loops
+
+from cases import TOL, ConvCase, edge_case_graph, rel_l2, to_device
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    (synth.scaled(synth.CONV_NEQUIP, 300, 12_001), 8, "f32"),
+    (synth.scaled(synth.CONV_NEQUIP, 300, 12_001), 8, "f64"),
+    (synth.scaled(synth.CONV_NEQUIP, 300, 12_001), 4, "f32"),
+    (synth.scaled(synth.CONV_STREAM, 257, 9_001), 16, "f32"),
+    (synth.ConvSpec("mixed", 61, 1_777, "5x0e+3x1o+7x2e+2x3o", 3, 3), 5, "f64"),
+    (synth.ConvSpec("mul80", 41, 997, "80x0e+80x1o", 1, 1), 3, "f32"),
+    (synth.ConvSpec("mul4", 53, 1_201, "4x0e+4x1o", 2, 2), 1, "f32"),
+]
+
+
+def radial_inputs(case, R, seed):
+    npdt = np.float32 if case.dtype == "f32" else np.float64
+    st = synth.upstream_streams(seed)  # independent children for rho and Theta
+    rho = synth.normal(st["gg_y"], (case.E, R), dtype=npdt)
+    theta = synth.normal(st["gg_w"], (R, case.prob.weight_numel), 1.0 / np.sqrt(R * 40.0), dtype=npdt)
+    return rho, theta
+
+
+def run(case, device, rho, theta, need=(True, True, True, True), workspace=None):
+    import torch
+    plan = cg.plan_for(case.spec, case.dtype)
+    d = to_device(case, device)
+    y = cg.spherical_harmonics(case.spec.lmax_sh, d["vec"])
+    tr = cg.graph_transpose(d["row_ptr"], d["col"])
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    res = cg.conv_backward_radial(plan, d["row_ptr"], d["col"], tr, d["x"], y, t(rho), t(theta), d["g"], need=need,
+                                  workspace=workspace)
+    torch.cuda.synchronize()
+    return res
+
+
+def oracle(case, rho, theta, rows=None, senders=None):
+    rows = np.arange(case.N) if rows is None else rows
+    senders = np.arange(case.N) if senders is None else senders
+    return loops.conv_backward_radial_rows(case.tab, case.row_ptr, case.col, case.x, case.y_oracle(), rho, theta,
+                                           case.g, rows, senders)
+
+
+def check(case, got, rho, theta, dtype):
+    eidx, dx, dy, drho, dtheta = oracle(case, rho, theta)
+    for name, a, b in (("dx", got[0], dx), ("dy", got[1][eidx], dy), ("drho", got[2][eidx], drho),
+                       ("dtheta", got[3], dtheta)):
+        err = rel_l2(a, b)
+        assert err <= TOL[dtype], f"{name}: rel-L2 {err:.3e}"
+
+
+@pytest.mark.parametrize("spec,R,dtype", CASES, ids=[f"{c[0].name}-R{c[1]}-{c[2]}" for c in CASES])
+def test_radial_backward(device, spec, R, dtype):
+    case = ConvCase(spec, dtype, seed=61)
+    rho, theta = radial_inputs(case, R, 61)
+    got = [a.cpu().numpy() for a in run(case, device, rho, theta)]
+    check(case, got, rho, theta, dtype)
+
+
+@pytest.mark.parametrize("kind", ["empty", "heavy", "isolated", "selfdup"])
+def test_radial_backward_edge_cases(device, kind):
+    spec = synth.ConvSpec("radial-bwd-" + kind, 500, 0, "32x0e+32x1o+32x2e", 2, 2)
+    case = ConvCase(spec, "f32", seed=62, graph=edge_case_graph(kind, 500, np.random.default_rng(13)))
+    rho, theta = radial_inputs(case, 8, 62)
+    got = [a.cpu().numpy() for a in run(case, device, rho, theta)]
+    outdeg = np.bincount(case.col, minlength=case.N)
+    assert np.all(got[0][outdeg == 0] == 0)
+    if case.E == 0:
+        assert np.all(got[0] == 0) and np.all(got[3] == 0)
+    else:
+        check(case, got, rho, theta, "f32")
+
+
+def test_radial_backward_no_receivers(device):
+    """N = 0: the shared dTheta is zero."""
+    import torch
+    plan = cg.plan_for(synth.CONV_NEQUIP, "f32")
+    z = lambda *sh, dt=torch.float32: torch.zeros(sh, dtype=dt, device=device)
+    gt = torch.full((8, plan.weight_numel), 5.0, device=device)
+    i32 = torch.int32
+    cg.conv_backward_radial(plan, z(1, dt=i32), z(0, dt=i32), (z(1, dt=i32), z(0, dt=i32), z(0, dt=i32)),
+                            z(0, plan.d_x), z(0, plan.d_sh), z(0, 8), z(8, plan.weight_numel), z(0, plan.d_out),
+                            outs=(None, None, None, gt), need=(False, False, False, True))
+    torch.cuda.synchronize()
+    assert torch.all(gt == 0)
+
+
+def test_radial_backward_subsets_repeat_and_workspace(device):
+    import torch
+    case = ConvCase(synth.scaled(synth.CONV_STREAM, 800, 30_000), "f32", seed=63,
+                    graph=synth.powerlaw_graph(800, 30_000, 2.0, 300, np.random.default_rng(7)))
+    rho, theta = radial_inputs(case, 8, 63)
+    full = run(case, device, rho, theta)
+    again = run(case, device, rho, theta)
+    for a, b in zip(full, again):
+        assert torch.equal(a, b)
+    for k in range(4):
+        need = tuple(j == k for j in range(4))
+        part = run(case, device, rho, theta, need=need)
+        assert torch.equal(part[k], full[k]) and all(part[j] is None for j in range(4) if j != k)
+    plan = cg.plan_for(case.spec, "f32")
+    nbytes = cg.conv_backward_radial_workspace_size(plan, case.N, case.E, 8)
+    with pytest.raises(cg.CgtpError, match="workspace too small"):
+        run(case, device, rho, theta, workspace=torch.empty(nbytes - 256, dtype=torch.uint8, device=device))
+    exact = run(case, device, rho, theta, workspace=torch.empty(nbytes, dtype=torch.uint8, device=device))
+    assert torch.equal(exact[3], full[3])
+    check(case, [a.cpu().numpy() for a in full], rho, theta, "f32")
+
+
+def test_radial_backward_full_size_sampled(device):
+    """The NequIP-like graph (5000 receivers, 200k edges), R = 8, as the benchmark launches it."""
+    case = ConvCase(synth.CONV_NEQUIP, "f32", seed=0)
+    rho, theta = radial_inputs(case, 8, 0)
+    got = [a.cpu().numpy() for a in run(case, device, rho, theta)]
+    rs = np.random.default_rng(19)
+    rows = np.sort(rs.choice(case.N, 60, replace=False))
+    senders = np.sort(rs.choice(case.N, 300, replace=False))
+    eidx, dx, dy, drho, dtheta = oracle(case, rho, theta, rows, senders)
+    assert rel_l2(got[0][senders], dx) <= TOL["f32"]
+    assert rel_l2(got[1][eidx], dy) <= TOL["f32"]
+    assert rel_l2(got[2][eidx], drho) <= TOL["f32"]
+    assert rel_l2(got[3], dtheta) <= TOL["f32"]
