@@ -996,12 +996,24 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
     o("");
 }
 
+// LDS elements for the dx partials of waves 1..3 of a sender-pass workgroup: per group, the
+// components of the input blocks it writes or adds (its own blocks; group 0 also the blocks no
+// path touches) times its lanes per edge slot
 int bwd_red_size(const std::vector<Group> &groups, const Plan &P)
 {
+    std::set<int> touched_any;
+    for (const Group &g : groups)
+        for (int pi : g.paths) touched_any.insert(P.paths[pi].i1);
     int m = 1;
-    for (const Group &g : groups) {
+    for (size_t gi = 0; gi < groups.size(); ++gi) {
+        const Group &g = groups[gi];
+        std::set<int> blocks;
+        for (int pi : g.paths) blocks.insert(P.paths[pi].i1);
+        if (gi == 0)
+            for (int b = 0; b < (int)P.ins.size(); ++b)
+                if (!touched_any.count(b)) blocks.insert(b);
         int nx = 0;
-        for (const Irrep &ir : P.ins) nx += n_of(ir.l);  // upper bound over the group's blocks
+        for (int b : blocks) nx += n_of(P.ins[b].l);
         m = std::max(m, 3 * nx * g.ct);
     }
     return m;
