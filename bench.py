@@ -573,8 +573,9 @@ def tp_flops(plan_paths, mul, mode):
 
 def cpu_baseline_tp(spec, plan_paths, seed, max_seconds=30.0):
     """The oracle's explicit loops (fp64, OpenMP) on a bounded sample of rows of the same batch
-    (random values, timing only): the uvu forward (and backward with ``backward``) or the uvw
-    forward.  Rate = rows per second."""
+    (random values, timing only): the forward, and with ``plan_paths == "backward"`` also the
+    backward (uvu: per-row dY, dW and dx; uvw: dx, dY and the shared dW over the sample).
+    Rate = rows per second."""
     from oracle import irreps as oirreps
     from oracle import loops
     out_ir = spec.out_irreps if spec.mode == "uvw" else oirreps.per_path_out_irreps(spec.in_irreps, spec.lmax_sh,
@@ -594,6 +595,8 @@ def cpu_baseline_tp(spec, plan_paths, seed, max_seconds=30.0):
     while True:
         if spec.mode == "uvw":
             loops.uvw_forward(tab, x, y, w, threads)
+            if plan_paths == "backward":
+                loops.uvw_backward(tab, x, y, w, g, np.arange(n), np.arange(n), threads)
         else:
             loops.uvu_forward(tab, ident, np.arange(n), x, y, w, threads)
             if plan_paths == "backward":
@@ -603,15 +606,14 @@ def cpu_baseline_tp(spec, plan_paths, seed, max_seconds=30.0):
         el = time.perf_counter() - t0
         if el >= 10.0 or el >= max_seconds:
             break
-    what = "uvw forward" if spec.mode == "uvw" else ("uvu forward + backward" if plan_paths == "backward"
-                                                      else "uvu forward")
+    what = f"{spec.mode} forward + backward" if plan_paths == "backward" else f"{spec.mode} forward"
     return {"value": n * reps / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} of {spec.batch} rows, {what}; fp64 explicit loops, mean of {reps} rep(s)"}
 
 
 def bench_tp(a, spec, device):
     """Batched tensor product workloads: one step = one cgtp_tp_forward over the batch (with
-    --backward, uvu only: cgtp_tp_forward + cgtp_tp_backward)."""
+    --backward: cgtp_tp_forward + cgtp_tp_backward)."""
     import torch
     from clebsch_gordan_tensor_cgtp_amd import binding as cg
     from clebsch_gordan_tensor_cgtp_amd import synth

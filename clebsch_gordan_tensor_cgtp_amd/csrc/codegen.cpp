@@ -1558,9 +1558,27 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
             o("T d", v, "_", i, " = (T)0;");
         }
     }
+    // the (path, k) blocks in order; each block loads the next one's gradient values (the B
+    // operands of G) before its own work, so that their latency is covered by the block
+    std::vector<std::pair<int, int>> blocks;
+    for (int pi : g.paths) {
+        std::set<int> ks;
+        for (const Nonzero &z : P.paths[pi].nz) ks.insert(z.k);
+        for (int k : ks) blocks.push_back({pi, k});
+    }
+    auto load_next = [&](size_t bi) {
+        const Path &p = P.paths[blocks[bi].first];
+        const int k = blocks[bi].second, n3 = n_of(p.l3);
+        for (int c = 0; c < (p.mul_out + 3) / 4; ++c)
+            o("gq", c, " = ", 4 * c, " + usub < ", p.mul_out, " ? g[(size_t)rr * DOUT + ", p.o, " + (", 4 * c, " + usub < ", p.mul_out,
+              " ? ", 4 * c, " + usub : 0) * ", n3, " + ", k, "] : (T)0;");
+    };
+    for (int c = 0; c < 4; ++c) o("T gq", c, " = (T)0;");
+    if (!blocks.empty()) load_next(0);
+    size_t bidx = 0;
     for (int pi : g.paths) {
         const Path &p = P.paths[pi];
-        const int n3 = n_of(p.l3), n2 = n_of(p.l2);
+        const int n2 = n_of(p.l2);
         o("{");
         o.ind++;
         // A operands of G: W_p[u = lane % 16][w = 4c + lane / 16]
@@ -1577,9 +1595,10 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
             const int k = kk.first;
             o("{");
             o.ind++;
-            for (int c = 0; c < wch; ++c)
-                o("const T gb", c, " = ", 4 * c, " + usub < ", p.mul_out, " ? g[(size_t)rr * DOUT + ", p.o, " + (", 4 * c,
-                  " + usub < ", p.mul_out, " ? ", 4 * c, " + usub : 0) * ", n3, " + ", k, "] : (T)0;");
+            for (int c = 0; c < wch; ++c) o("const T gb", c, " = gq", c, ";");
+            if (bidx + 1 < blocks.size()) load_next(bidx + 1);
+            ++bidx;
+            (void)k;
             o("V4 G = {0, 0, 0, 0};");
             for (int c = 0; c < wch; ++c) o("G = MFMA(wa", c, ", gb", c, ", G);");
             for (auto &ii : kk.second) {
@@ -1687,6 +1706,33 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
     }
     std::map<int, std::vector<int>> by_i1;
     for (int pi : g.paths) by_i1[P.paths[pi].i1].push_back(pi);
+    // the (path, k) blocks in emission order; each block loads the next one's B operands (the
+    // gradient values of its four row groups) before its own work, so that their latency is
+    // covered by the block (one wave per SIMD leaves nothing else to hide it)
+    std::vector<std::pair<int, int>> blocks;
+    for (auto &kv : by_i1)
+        for (int pi : kv.second) {
+            std::set<int> ks;
+            for (const Nonzero &z : P.paths[pi].nz) ks.insert(z.k);
+            for (int k : ks) blocks.push_back({pi, k});
+        }
+    auto load_next = [&](size_t bi, bool declare) {
+        const Path &p = P.paths[blocks[bi].first];
+        const int k = blocks[bi].second, n3 = n_of(p.l3);
+        for (int m = 0; m < 4; ++m) {
+            o("{");
+            o.ind++;
+            o("const long br = blk * 16 + ", 4 * m, " + usub;");
+            o("const bool bok = br < nrows && rl < ", p.mul_out, ";");
+            o("gp", m, " = bok ? g[(size_t)br * DOUT + ", p.o, " + rl * ", n3, " + ", k, "] : (T)0;");
+            o.ind--;
+            o("}");
+        }
+        (void)declare;
+    };
+    for (int m = 0; m < 4; ++m) o("T gp", m, ";");
+    if (!blocks.empty()) load_next(0, true);
+    size_t bidx = 0;
     for (auto &kv : by_i1) {
         const Irrep &ir = P.ins[kv.first];
         const int n1 = n_of(ir.l);
@@ -1700,13 +1746,14 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
                   ir.mul, " ? ", 4 * c, " + usub : 0) * ", n1, " + ", i, "] : (T)0;");
         for (int pi : kv.second) {
             const Path &p = P.paths[pi];
-            const int n3 = n_of(p.l3);
             std::map<int, std::map<int, std::vector<const Nonzero *>>> byki;
             for (const Nonzero &z : p.nz) byki[z.k][z.i].push_back(&z);
             for (auto &kk : byki) {
-                const int k = kk.first;
                 o("{");
                 o.ind++;
+                for (int m = 0; m < 4; ++m) o("const T gc", m, " = gp", m, ";");
+                if (bidx + 1 < blocks.size()) load_next(bidx + 1, false);
+                ++bidx;
                 for (auto &ii : kk.second) {
                     const auto &v = ii.second;
                     std::ostringstream e;
@@ -1736,16 +1783,7 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
                 }
                 o("WAVE_SYNC();");
                 // rows are the MFMA K dimension: A = t[row = 4m + lane/16][u = lane%16], B = g[row][w = lane%16][k]
-                for (int m = 0; m < 4; ++m) {
-                    o("{");
-                    o.ind++;
-                    o("const long br = blk * 16 + ", 4 * m, " + usub;");
-                    o("const bool bok = br < nrows && rl < ", p.mul_out, ";");
-                    o("const T gv = g[bok ? (size_t)br * DOUT + ", p.o, " + rl * ", n3, " + ", k, " : 0];");
-                    o("D", pi, " = MFMA(tw[(", 4 * m, " + usub) * 17 + rl], bok ? gv : (T)0, D", pi, ");");
-                    o.ind--;
-                    o("}");
-                }
+                for (int m = 0; m < 4; ++m) o("D", pi, " = MFMA(tw[(", 4 * m, " + usub) * 17 + rl], gc", m, ", D", pi, ");");
                 o("__builtin_amdgcn_sched_barrier(0);");
                 o.ind--;
                 o("}");
@@ -1843,7 +1881,7 @@ void emit_uvb_kernels(Out &o, const Plan &P)
     o("");
     for (int gi = 0; gi < (int)P.uvb_w_groups.size(); ++gi) emit_uvb_w_group(o, P, gi);
     o("// one wave per (path group, chunk of row blocks), chunk-major within a group");
-    o("extern \"C\" __global__ void __launch_bounds__(256, 1) cgtp_tp_uvw_bwd_w(const T* __restrict__ x, "
+    o("extern \"C\" __global__ void __launch_bounds__(256, ", P.uvb_w_waves_per_eu, ") cgtp_tp_uvw_bwd_w(const T* __restrict__ x, "
       "const T* __restrict__ y, const T* __restrict__ g, T* __restrict__ ws, long nrows, long nblocks, long bpc, "
       "long nchunks, long nwaves)");
     o("{");

@@ -76,6 +76,7 @@ struct Plan {
     int dbl_fwd_waves_per_eu = 2;   // double backward, receiver pass (twice the forward's operands)
     int dbl_bwd_waves_per_eu = 2;   // double backward, sender pass
     int uvc_waves_per_eu = 2;       // uvw convolution
+    int uvb_w_waves_per_eu = 1;     // uvw batched backward, dW kernel
     int uvc_rpw = 4;                // uvw convolution: receivers per wave (16 / waves per workgroup)
     bool stream_hint = true;        // nontemporal loads/stores for once-touched per-edge rows
     bool bwd_sched_barrier = true;  // keep path blocks of the backward from interleaving
