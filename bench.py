@@ -47,6 +47,9 @@ def parse():
                     help="time the convolution double backward (both passes) instead of forward + backward")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates the HBM byte counters)")
+    ap.add_argument("--nodes", type=int, default=0,
+                    help="convolution workloads: the same recipe with this many receivers (sweeps; with --edges)")
+    ap.add_argument("--edges", type=int, default=0, help="convolution workloads: edge count of the --nodes variant")
     return ap.parse_args()
 
 
@@ -166,9 +169,9 @@ def bench_double_backward(a, spec, plan, d, host_graph, device):
     send_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     ms_per_step = wall * 1e3 / a.steps
     recv_b, send_b = algorithmic_bytes_dbl(plan, N, E, es)
-    dom = ("cgtp_conv_dbwd_send", send_ms, send_b) if send_ms >= recv_ms else ("cgtp_conv_dbwd_recv", recv_ms, recv_b)
-    oth = ("cgtp_conv_dbwd_recv", recv_ms, recv_b) if dom[0] == "cgtp_conv_dbwd_send" else \
-        ("cgtp_conv_dbwd_send", send_ms, send_b)
+    recv_k = split_kernel("cgtp_conv_dbwd_recv", plan.row_split(N, E, double_backward=True))
+    dom = ("cgtp_conv_dbwd_send", send_ms, send_b) if send_ms >= recv_ms else (recv_k, recv_ms, recv_b)
+    oth = (recv_k, recv_ms, recv_b) if dom[0] == "cgtp_conv_dbwd_send" else ("cgtp_conv_dbwd_send", send_ms, send_b)
     achieved = dom[2] / (dom[1] * 1e-3) / 1e9
     line = {
         "metric": METRIC, "value": E / (ms_per_step * 1e-3), "unit": "edges/s", "n_gpus": 1, "steps": a.steps,
@@ -446,10 +449,17 @@ def bench_radial(a, spec, plan, d, host_graph, device):
     print(json.dumps(line), flush=True)
 
 
+def split_kernel(base, split):
+    """Name of the receiver-owned kernel that gives each receiver row `split` waves."""
+    return base if split == 1 else f"{base}_split{split}"
+
+
 def kernel_digest(source, kernel):
     """SHA-1 of the generated code one kernel runs: the module's shared preamble plus that
-    kernel's own section (the generator marks sections with '// @@section NAME' lines)."""
+    kernel's own section (the generator marks sections with '// @@section NAME' lines); a
+    `_splitN` entry point also runs the code of its base kernel's section."""
     import hashlib
+    import re
     parts, name = {}, None
     for line in source.splitlines(keepends=True):
         if line.startswith("// @@section "):
@@ -457,7 +467,9 @@ def kernel_digest(source, kernel):
         parts[name] = parts.get(name, "") + line
     if "common" not in parts or kernel not in parts:
         return None
-    return hashlib.sha1((parts["common"] + parts[kernel]).encode()).hexdigest()
+    m = re.fullmatch(r"(.+)_split\d+", kernel)
+    base = parts.get(m.group(1), "") if m else ""
+    return hashlib.sha1((parts["common"] + base + parts[kernel]).encode()).hexdigest()
 
 
 def measured_traffic(plan, spec, dtype, kernel):
@@ -710,6 +722,11 @@ def main():
     spec = {**synth.WORKLOADS, **synth.EXTRA_WORKLOADS}[a.workload]
     if not hasattr(spec, "n_edges"):
         return bench_tp(a, spec, device)
+    if a.nodes or a.edges:
+        if a.nodes <= 0 or a.edges < 0:
+            print(json.dumps({"error": "--nodes needs a positive value and --edges a non-negative one"}))
+            sys.exit(2)
+        spec = synth.scaled(spec, a.nodes, a.edges)
     plan, d, host_graph = make_inputs(spec, a.dtype, a.seed, device)
     if spec.mode == "uvw":
         return bench_conv_uvw(a, spec, plan, d, host_graph, device)
@@ -751,7 +768,8 @@ def main():
     bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     ms_per_step = wall * 1e3 / a.steps
     fwd_b, bwd_b = algorithmic_bytes(plan, N, E, es)
-    dom = ("cgtp_conv_bwd", bwd_ms, bwd_b) if bwd_ms >= fwd_ms else ("cgtp_conv_fwd", fwd_ms, fwd_b)
+    fwd_k = split_kernel("cgtp_conv_fwd", plan.row_split(N, E))
+    dom = ("cgtp_conv_bwd", bwd_ms, bwd_b) if bwd_ms >= fwd_ms else (fwd_k, fwd_ms, fwd_b)
     achieved = dom[2] / (dom[1] * 1e-3) / 1e9
     traffic = measured_traffic(plan, spec, a.dtype, dom[0])
     line = {
@@ -776,7 +794,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": dom[2], "avg_launch_ms": dom[1],
-                     "other": {"kernel": "cgtp_conv_fwd" if dom[0] == "cgtp_conv_bwd" else "cgtp_conv_bwd",
+                     "other": {"kernel": fwd_k if dom[0] == "cgtp_conv_bwd" else "cgtp_conv_bwd",
                                "achieved": (fwd_b / (fwd_ms * 1e-3) if dom[0] == "cgtp_conv_bwd"
                                             else bwd_b / (bwd_ms * 1e-3)) / 1e9}},
         "cpu_baseline": None,

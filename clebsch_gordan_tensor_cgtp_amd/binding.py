@@ -26,7 +26,8 @@ EXPORTS = ("cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info_get", "cgtp_
            "cgtp_conv_forward_radial", "cgtp_plan_radial_prepare", "cgtp_plan_radial_source",
            "cgtp_tp_backward_workspace_size", "cgtp_plan_uvw_backward_prepare", "cgtp_plan_uvw_backward_source",
            "cgtp_conv_backward_workspace_size", "cgtp_conv_backward_ws", "cgtp_plan_conv_uvw_backward_prepare",
-           "cgtp_plan_conv_uvw_backward_source", "cgtp_conv_backward_radial", "cgtp_conv_backward_radial_workspace_size")
+           "cgtp_plan_conv_uvw_backward_source", "cgtp_conv_backward_radial", "cgtp_conv_backward_radial_workspace_size",
+           "cgtp_conv_row_split")
 _STRING_RESULTS = ("cgtp_last_error", "cgtp_plan_source", "cgtp_plan_radial_source", "cgtp_plan_uvw_backward_source",
                    "cgtp_plan_conv_uvw_backward_source")
 
@@ -72,6 +73,7 @@ def lib():
         L.cgtp_conv_backward_radial_workspace_size.argtypes = [vp, i64, i64, i32, ctypes.POINTER(ctypes.c_size_t)]
         L.cgtp_conv_backward_radial.argtypes = [vp, i64, i64] + [vp] * 7 + [i32] + [vp] * 8 + [ctypes.c_size_t, vp]
         L.cgtp_plan_source.argtypes = [vp]
+        L.cgtp_conv_row_split.argtypes = [vp, i64, i64, i32, ctypes.POINTER(i32)]
         L.cgtp_plan_create.argtypes = [ctypes.c_char_p] * 3 + [ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp)]
         L.cgtp_plan_destroy.argtypes = [vp]
         L.cgtp_plan_info_get.argtypes = [vp, ctypes.POINTER(PlanInfo)]
@@ -142,6 +144,13 @@ class Plan:
         _check(lib().cgtp_plan_path_coefficients(self._h, p, n.value, ijk.ctypes.data, vals.ctypes.data,
                                                  ctypes.byref(n)))
         return ijk, vals
+
+    def row_split(self, n_nodes: int, n_edges: int, double_backward: bool = False) -> int:
+        """Waves per receiver row (1, 2 or 4) of the forward (or of the double backward's receiver
+        pass) for a graph of this size; kernels of split rows carry the suffix _split2/_split4."""
+        v = ctypes.c_int32()
+        _check(lib().cgtp_conv_row_split(self._h, n_nodes, n_edges, 1 if double_backward else 0, ctypes.byref(v)))
+        return v.value
 
     @property
     def source(self) -> str:

@@ -69,16 +69,48 @@ void check_hip(hipError_t e, const char *what)
     if (e != hipSuccess) throw cgtp::Error(CGTP_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-void launch(hipFunction_t f, int64_t waves, void **args, void *stream)
+void launch(hipFunction_t f, int64_t waves, void **args, void *stream, unsigned lds_bytes = 0)
 {
     const int64_t blocks = (waves + 3) / 4;
     require(blocks <= INT_MAX, "problem too large for one launch");
-    check_hip(hipModuleLaunchKernel(f, (unsigned)blocks, 1, 1, 256, 1, 1, 0, static_cast<hipStream_t>(stream), args,
-                                    nullptr),
+    check_hip(hipModuleLaunchKernel(f, (unsigned)blocks, 1, 1, 256, 1, 1, lds_bytes, static_cast<hipStream_t>(stream),
+                                    args, nullptr),
               "hipModuleLaunchKernel");
 }
 
 size_t elem(const cgtp::Plan &P) { return P.dtype == CGTP_F64 ? 8 : 4; }
+
+// Waves per receiver row in the receiver-owned passes (forward, double backward's receiver
+// pass).  A graph with few receivers leaves most of the chip's wave slots (256 CUs x 4 SIMDs x
+// the occupancy target) idle once the first rows finish, and its longest row sets the end;
+// splitting each row over 2 or 4 waves of one workgroup (edge groups dealt round-robin, parts
+// summed in part order through LDS) shortens both.  The split doubles while the launch stays
+// under four waves per slot and every part keeps at least 8 edge groups of the mean row
+// (measured, 32 channels at 4 waves per SIMD: N = 5,000 with 40 edges per row 116 / 103 /
+// 108 us for 1 / 2 / 4 parts, with 160 edges per row 383 / 333 / 317 us; N = 20,000 with 40
+// edges per row even).  The choice depends only on N, E and the plan, so a given graph always
+// gets the same bits.  Single-task plans only.
+struct RowSplit {
+    int split = 1;
+    unsigned lds = 0;
+};
+
+RowSplit row_split(const cgtp::Plan &P, int64_t N, int64_t E, int waves_per_eu)
+{
+    RowSplit r;
+    if (!cgtp::fwd_splittable(P) || N <= 0) return r;
+    if (P.fwd_row_split > 0) {
+        r.split = P.fwd_row_split;
+    } else {
+        const int64_t slots = 1024LL * waves_per_eu;
+        const double groups = (double)E / (double)N / P.fwd_groups[0].es;  // edge groups per row
+        while (r.split < 4 && N * r.split < 4 * slots && groups / (2 * r.split) >= 8) r.split *= 2;
+    }
+    if (r.split > 1)
+        r.lds = (unsigned)((4 - 4 / r.split) * (size_t)cgtp::fwd_group_accs(P, 0) * P.fwd_groups[0].ct * elem(P));
+    if (r.lds > 65536) r = RowSplit{};
+    return r;
+}
 
 void check_graph_sizes(int64_t N, int64_t E)
 {
@@ -212,6 +244,18 @@ cgtp_status cgtp_plan_info_get(const cgtp_plan *plan, cgtp_plan_info *info)
         info->mode = P.mode;
         info->dtype = P.dtype;
         info->fwd_tasks = P.fwd_tasks;
+    });
+}
+
+cgtp_status cgtp_conv_row_split(const cgtp_plan *plan, int64_t N, int64_t E, int32_t pass, int32_t *split)
+{
+    return guarded([&] {
+        require(plan && split, "NULL argument to cgtp_conv_row_split");
+        require(pass == 0 || pass == 1, "pass must be 0 (forward) or 1 (double backward, receiver pass)");
+        check_graph_sizes(N, E);
+        const cgtp::Plan &P = plan->p;
+        *split = P.mode == CGTP_UVU ? row_split(P, N, E, pass == 0 ? P.fwd_waves_per_eu : P.dbl_fwd_waves_per_eu).split
+                                    : 1;
     });
 }
 
@@ -467,10 +511,10 @@ cgtp_status cgtp_conv_forward_ordered(const cgtp_plan *plan, int64_t N, int64_t 
             }
             return;
         }
-        int64_t waves = N * P.fwd_tasks;
-        long nrows = (long)N, nwaves = (long)waves;
+        const RowSplit rs = row_split(P, N, E, P.fwd_waves_per_eu);
+        long nrows = (long)N, nwaves = (long)(N * P.fwd_tasks);
         void *args[] = {&row_ptr, &col, &x, &y, &w, &out, &nrows, &nwaves, &order};
-        launch(L.conv_fwd, waves, args, stream);
+        launch(rs.split == 1 ? L.conv_fwd : L.conv_fwd_split[rs.split / 4], nwaves * rs.split, args, stream, rs.lds);
     });
 }
 
@@ -548,10 +592,11 @@ cgtp_status cgtp_conv_forward_radial(const cgtp_plan *plan, int64_t N, int64_t E
         require_disjoint(out, no, "out", col, E * 4, "col");
         require_disjoint(out, no, "out", order, N * 4, "order");
         hipFunction_t f = cgtp::radial_functions_for_current_device(P, R).fwd;
-        int64_t waves = N * P.fwd_tasks;
-        long nrows = (long)N, nwaves = (long)waves;
+        // one wave per row: splitting rows measured no faster here (each extra workgroup
+        // stages Theta again; N = 5,000, R = 8: 121 / 121 / 140 us for 1 / 2 / 4 parts)
+        long nrows = (long)N, nwaves = (long)(N * P.fwd_tasks);
         void *args[] = {&row_ptr, &col, &x, &y, &rho, &theta, &out, &nrows, &nwaves, &order};
-        launch(f, waves, args, stream);
+        launch(f, nwaves, args, stream);
     });
 }
 
@@ -880,10 +925,11 @@ cgtp_status cgtp_conv_double_backward(const cgtp_plan *plan, int64_t N, int64_t 
         const auto &L = cgtp::module_for_current_device(P);
         if (grad_grad_out) {
             // receiver pass: d/dg = conv(gg_x, y, w) + conv(x, gg_y, w) + conv(x, y, gg_w)
-            int64_t waves = N * P.fwd_tasks;
-            long nrows = (long)N, nwaves = (long)waves;
+            const RowSplit rs = row_split(P, N, E, P.dbl_fwd_waves_per_eu);
+            long nrows = (long)N, nwaves = (long)(N * P.fwd_tasks);
             void *args[] = {&row_ptr, &col, &x, &y, &w, &gg_x, &gg_y, &gg_w, &grad_grad_out, &nrows, &nwaves, &order};
-            launch(L.dbwd_recv, waves, args, stream);
+            launch(rs.split == 1 ? L.dbwd_recv : L.dbwd_recv_split[rs.split / 4], nwaves * rs.split, args, stream,
+                   rs.lds);
         }
         if (send) {
             // sender pass over the transpose: d/dx, d/dy, d/dW (one owner per output row)

@@ -15,6 +15,9 @@
 //                 works on 64/ct edges at once (edge slots) and sums the slots
 //                 at the end.  Accumulators stay in registers across the
 //                 receiver's CSR row; each output element is written once.
+//                 A launch may give each receiver `split` consecutive waves of
+//                 one workgroup (edge groups dealt round-robin); the parts are
+//                 summed through LDS in part order.
 //  cgtp_conv_bwd  one wave per sender over the sender-sorted transpose; every
 //                 path in one wave.  Per edge it forms B_ij = sum_k C_ijk g_k,
 //                 then dF/dx_i = sum_j B_ij y_j and dF/dy_j = sum_i B_ij x_i,
@@ -101,6 +104,8 @@ std::vector<std::pair<std::pair<int, int>, std::vector<int>>> pairs_of(const Pla
 
 // Is lane channel u possibly >= mul (masked) for a block of multiplicity mul?
 bool needs_mask(int mul, const Group &g) { return mul != g.tiles * g.ct; }
+
+
 
 // Emit loads of the sender row (x), the edge row (y) and the weights of edge index `ei`
 // and sender `si` into registers named <pre>x.., <pre>y.., <pre>w..
@@ -333,17 +338,53 @@ void emit_preamble(Out &o, const Plan &P)
 // Forward body of one group; `n` is the receiver (conv) or the row block (rows
 // mode).  With dbl, the same receiver-owned stream computes the double
 // backward's d/dg (emit_dbl_recv_math) from the extra operands ggx, ggy, ggw.
+// The parts of a split receiver row, summed in part order through LDS.  The part waves of one
+// receiver are consecutive waves of the workgroup, and every wave of the workgroup reaches the
+// barrier (split is uniform over the launch).
+void emit_part_sum(Out &o, const Plan &P, int gi, const Touch &t)
+{
+    const Group &g = P.fwd_groups[gi];
+    const long span = (long)fwd_group_accs(P, gi) * g.ct;
+    o("if constexpr (SPLIT > 1) {");
+    o.ind++;
+    o("T* red = pred + (long)((threadIdx.x >> 6) / SPLIT) * (SPLIT - 1) * ", span, " + (lane & ", g.ct - 1, ");");
+    o("if (part != 0 && slot == 0) {");
+    o.ind++;
+    o("T* r = red + (long)(part - 1) * ", span, ";");
+    int i = 0;
+    for (int q : t.slots)
+        for (int k = 0; k < n_of(P.out[q].l); ++k, ++i) o("r[", (long)i * g.ct, "] = a", q, "_", k, ";");
+    o.ind--;
+    o("}");
+    o("__syncthreads();");
+    o("if (part == 0 && slot == 0) {");
+    o.ind++;
+    o("for (int p = 1; p < SPLIT; ++p) {");
+    o.ind++;
+    o("const T* r = red + (long)(p - 1) * ", span, ";");
+    i = 0;
+    for (int q : t.slots)
+        for (int k = 0; k < n_of(P.out[q].l); ++k, ++i) o("a", q, "_", k, " += r[", (long)i * g.ct, "];");
+    o.ind--;
+    o("}");
+    o.ind--;
+    o("}");
+    o.ind--;
+    o("}");
+}
+
 void emit_fwd_group(Out &o, const Plan &P, int gi, bool rows, bool dbl = false, int radial = 0)
 {
     const Group &g = P.fwd_groups[gi];
     const bool f64 = P.dtype == CGTP_F64;
     Touch t = touched(P, g.paths);
+    if (!rows && fwd_splittable(P)) o("template <int SPLIT>  // waves per receiver row");
     o("__device__ __forceinline__ void ", rows ? "tp" : dbl ? "dbr" : radial ? "rad" : "fwd", "_g", gi,
       "(long n, int tile, int lane, const int* __restrict__ row_ptr, const int* __restrict__ col, "
       "const T* __restrict__ x, const T* __restrict__ y, ",
       radial ? "const T* __restrict__ rho, const T* thl, " : "const T* __restrict__ w, ",
       dbl ? "const T* __restrict__ ggx, const T* __restrict__ ggy, const T* __restrict__ ggw, " : "",
-      "T* __restrict__ out, long nrows)");
+      "T* __restrict__ out, long nrows", rows ? "" : ", int part, bool live, T* pred", ")");
     o("{");
     o.ind++;
     o("const int slot = lane >> ", log2i(g.ct), ";");
@@ -370,20 +411,28 @@ void emit_fwd_group(Out &o, const Plan &P, int gi, bool rows, bool dbl = false, 
         o.ind++;
         o("T* orow = out + (size_t)r * DOUT;");
     } else {
-        o("const int e0 = row_ptr[n], e1 = row_ptr[n + 1];");
+        // `split` waves share the receiver's row: part p takes edge groups p, p + split, ...
+        const bool splittable = fwd_splittable(P);
+        if (splittable) {
+            o("const int e0 = row_ptr[n], e1 = live ? row_ptr[n + 1] : e0;");
+            o("constexpr int stride = SPLIT * ", g.es, ";");
+        } else {
+            o("const int e0 = row_ptr[n], e1 = row_ptr[n + 1];");
+            o("constexpr int stride = ", g.es, ";");
+        }
         o("if (e0 < e1) {");
         o.ind++;
         // pipeline: senders (col) two edge groups ahead, operands one ahead, so
         // every wait is for loads issued a whole iteration earlier
-        o("int e = e0 + slot;");
+        o("int e = e0 + part * ", g.es, " + slot;");
         o("int ec = e < e1 ? e : e1 - 1;");
         o("int s = col[ec];");
-        o("int en = (e + ", g.es, " < e1) ? e + ", g.es, " : e1 - 1;");
+        o("int en = (e + stride < e1) ? e + stride : e1 - 1;");
         o("int sn = col[en];");
         emit_edge_loads(o, P, g, t, "c", "s", "ec", true, dbl, radial);
-        o("for (; e < e1; e += ", g.es, ") {");
+        o("for (; e < e1; e += stride) {");
         o.ind++;
-        o("const int enn = (e + ", 2 * g.es, " < e1) ? e + ", 2 * g.es, " : e1 - 1;");
+        o("const int enn = (e + 2 * stride < e1) ? e + 2 * stride : e1 - 1;");
         o("const int snn = col[enn];");
         emit_edge_loads(o, P, g, t, "n", "sn", "en", true, dbl, radial);
         if (radial) {
@@ -410,7 +459,12 @@ void emit_fwd_group(Out &o, const Plan &P, int gi, bool rows, bool dbl = false, 
         for (int m = 32; m >= g.ct; m /= 2)
             for (int q : t.slots)
                 for (int k = 0; k < n_of(P.out[q].l); ++k) o("a", q, "_", k, " += __shfl_xor(a", q, "_", k, ", ", m, ");");
-        o("if (slot == 0) {");
+        if (splittable) {
+            emit_part_sum(o, P, gi, t);
+            o("if (live && part == 0 && slot == 0) {");
+        } else {
+            o("if (slot == 0) {");
+        }
         o.ind++;
         o("T* orow = out + (size_t)n * DOUT;");
     }
@@ -434,10 +488,38 @@ void emit_fwd_group(Out &o, const Plan &P, int gi, bool rows, bool dbl = false, 
     o("");
 }
 
-void emit_fwd_kernel(Out &o, const Plan &P, bool rows, bool dbl = false)
+// Wave -> (receiver, task, part) of the receiver-owned passes.  `nwaves` counts (receiver, task)
+// units.  With split > 1 (single-task plans only) each receiver has `split` consecutive waves of
+// one workgroup, and the waves past the last receiver stay alive to the barrier of the part sum
+// without touching memory.
+void emit_fwd_unit(Out &o, const Plan &P, int split)
+{
+    if (split == 1) {
+        o("T* pred = nullptr;");
+        o("if (wave >= nwaves) return;");
+        o("const int part = 0;");
+        o("const bool live = true;");
+        o("const int task = (int)(wave % ", P.fwd_tasks, ");");
+        o("long n = wave / ", P.fwd_tasks, ";");
+        o("if (order) n = order[n];  // receiver schedule (heavy rows first), results unchanged");
+        return;
+    }
+    o("extern __shared__ T pred[];  // part sums: ", 4 - 4 / split, " waves x accumulators x lanes");
+    o("const long unit = wave / ", split, ";");
+    o("const int part = (int)(wave % ", split, ");");
+    o("const bool live = unit < nwaves;");
+    o("const int task = 0;");
+    o("long n = live ? unit : 0;");
+    o("if (live && order) n = order[n];  // receiver schedule (heavy rows first), results unchanged");
+}
+
+// Name suffix of the receiver-owned kernel that gives each row `split` waves.
+std::string split_suffix(int split) { return split == 1 ? "" : "_split" + std::to_string(split); }
+
+void emit_fwd_kernel(Out &o, const Plan &P, bool rows, bool dbl = false, int split = 1)
 {
     o("extern \"C\" __global__ void __launch_bounds__(256, ", dbl ? P.dbl_fwd_waves_per_eu : P.fwd_waves_per_eu, ") ",
-      rows ? "cgtp_tp_fwd" : dbl ? "cgtp_conv_dbwd_recv" : "cgtp_conv_fwd",
+      rows ? "cgtp_tp_fwd" : dbl ? "cgtp_conv_dbwd_recv" : "cgtp_conv_fwd", split_suffix(split),
       "(const int* __restrict__ row_ptr, const int* __restrict__ col, const T* __restrict__ x, "
       "const T* __restrict__ y, const T* __restrict__ w, ",
       dbl ? "const T* __restrict__ ggx, const T* __restrict__ ggy, const T* __restrict__ ggw, " : "",
@@ -446,16 +528,21 @@ void emit_fwd_kernel(Out &o, const Plan &P, bool rows, bool dbl = false)
     o.ind++;
     o("const long wave = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
     o("const int lane = threadIdx.x & 63;");
-    o("if (wave >= nwaves) return;");
-    o("const int task = (int)(wave % ", P.fwd_tasks, ");");
-    o("long n = wave / ", P.fwd_tasks, ";");
-    if (!rows) o("if (order) n = order[n];  // receiver schedule (heavy rows first), results unchanged");
+    if (rows) {
+        o("if (wave >= nwaves) return;");
+        o("const int task = (int)(wave % ", P.fwd_tasks, ");");
+        o("long n = wave / ", P.fwd_tasks, ";");
+    } else {
+        emit_fwd_unit(o, P, split);
+    }
+    const std::string targ = !rows && fwd_splittable(P) ? "<" + std::to_string(split) + ">" : "";
     o("switch (task) {");
     int task = 0;
     for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi)
         for (int tile = 0; tile < P.fwd_groups[gi].tiles; ++tile, ++task)
-            o("case ", task, ": ", rows ? "tp" : dbl ? "dbr" : "fwd", "_g", gi, "(n, ", tile,
-              ", lane, row_ptr, col, x, y, w, ", dbl ? "ggx, ggy, ggw, " : "", "out, nrows); break;");
+            o("case ", task, ": ", rows ? "tp" : dbl ? "dbr" : "fwd", "_g", gi, targ, "(n, ", tile,
+              ", lane, row_ptr, col, x, y, w, ", dbl ? "ggx, ggy, ggw, " : "", "out, nrows",
+              rows ? "" : ", part, live, pred", "); break;");
     o("default: break;");
     o("}");
     o.ind--;
@@ -2158,6 +2245,16 @@ std::string generate_conv_uvw_backward_source(const Plan &P)
 
 int conv_uvw_g_items(const Plan &P, std::vector<std::pair<int, int>> *items) { return ucb_items(P, items); }
 
+// receiver rows may be split over several waves only when one wave covers the whole receiver
+bool fwd_splittable(const Plan &P) { return P.fwd_tasks == 1 && P.fwd_groups.size() == 1; }
+
+int fwd_group_accs(const Plan &P, int gi)
+{
+    int n = 0;
+    for (int q : touched(P, P.fwd_groups[gi].paths).slots) n += n_of(P.out[q].l);
+    return n;
+}
+
 int64_t conv_uvw_g_width(const Plan &P)
 {
     int64_t dg = 0;
@@ -2203,15 +2300,14 @@ std::string generate_radial_source(const Plan &P, int R, const std::vector<Group
     o("__syncthreads();");
     o("const long wave = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
     o("const int lane = threadIdx.x & 63;");
-    o("if (wave >= nwaves) return;");
-    o("const int task = (int)(wave % ", P.fwd_tasks, ");");
-    o("long n = wave / ", P.fwd_tasks, ";");
-    o("if (order) n = order[n];  // receiver schedule (heavy rows first), results unchanged");
+    emit_fwd_unit(o, P, 1);
     o("switch (task) {");
     int task = 0;
+    const std::string targ = fwd_splittable(P) ? "<1>" : "";
     for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi)
         for (int tile = 0; tile < P.fwd_groups[gi].tiles; ++tile, ++task)
-            o("case ", task, ": rad_g", gi, "(n, ", tile, ", lane, row_ptr, col, x, y, rho, thl, out, nrows); break;");
+            o("case ", task, ": rad_g", gi, targ, "(n, ", tile,
+              ", lane, row_ptr, col, x, y, rho, thl, out, nrows, part, live, pred); break;");
     o("default: break;");
     o("}");
     o.ind--;
@@ -2278,6 +2374,13 @@ std::string generate_source(const Plan &P)
         o("// @@section cgtp_conv_fwd");
         for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi) emit_fwd_group(o, P, gi, false);
         emit_fwd_kernel(o, P, false);
+        // the same pass with each receiver row split over 2 or 4 waves (a `_splitN` section
+        // holds only the entry point; its code is the base section's template)
+        if (fwd_splittable(P))
+            for (int split : {2, 4}) {
+                o("// @@section cgtp_conv_fwd", split_suffix(split));
+                emit_fwd_kernel(o, P, false, false, split);
+            }
         o("// @@section cgtp_tp_fwd");
         for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi) emit_fwd_group(o, P, gi, true);
         emit_fwd_kernel(o, P, true);
@@ -2288,6 +2391,11 @@ std::string generate_source(const Plan &P)
         o("// @@section cgtp_conv_dbwd_recv");
         for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi) emit_fwd_group(o, P, gi, false, true);
         emit_fwd_kernel(o, P, false, true);
+        if (fwd_splittable(P))
+            for (int split : {2, 4}) {
+                o("// @@section cgtp_conv_dbwd_recv", split_suffix(split));
+                emit_fwd_kernel(o, P, false, true, split);
+            }
         o("// @@section cgtp_conv_dbwd_send");
         emit_bwd_kernel(o, P, true);
     } else {

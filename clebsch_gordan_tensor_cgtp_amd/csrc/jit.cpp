@@ -128,6 +128,14 @@ const Plan::Loaded &module_for_current_device(Plan &P)
         check(hipModuleGetFunction(&L.tp_fwd, L.module, "cgtp_tp_fwd"), "hipModuleGetFunction(tp_fwd)");
         check(hipModuleGetFunction(&L.dbwd_recv, L.module, "cgtp_conv_dbwd_recv"), "hipModuleGetFunction(dbwd_recv)");
         check(hipModuleGetFunction(&L.dbwd_send, L.module, "cgtp_conv_dbwd_send"), "hipModuleGetFunction(dbwd_send)");
+        if (fwd_splittable(P)) {
+            check(hipModuleGetFunction(&L.conv_fwd_split[0], L.module, "cgtp_conv_fwd_split2"), "hipModuleGetFunction");
+            check(hipModuleGetFunction(&L.conv_fwd_split[1], L.module, "cgtp_conv_fwd_split4"), "hipModuleGetFunction");
+            check(hipModuleGetFunction(&L.dbwd_recv_split[0], L.module, "cgtp_conv_dbwd_recv_split2"),
+                  "hipModuleGetFunction");
+            check(hipModuleGetFunction(&L.dbwd_recv_split[1], L.module, "cgtp_conv_dbwd_recv_split4"),
+                  "hipModuleGetFunction");
+        }
         check(hipModuleGetFunction(&L.tp_bwd, L.module, "cgtp_tp_bwd"), "hipModuleGetFunction(tp_bwd)");
     } else {
         check(hipModuleGetFunction(&L.tp_uvw, L.module, "cgtp_tp_uvw"), "hipModuleGetFunction(tp_uvw)");

@@ -82,6 +82,7 @@ struct Plan {
     bool bwd_sched_barrier = true;  // keep path blocks of the backward from interleaving
     int bwd_prefetch = -1;          // -1: per group by register estimate; 0/1 forced
     bool fwd_split_inputs = false;  // forward groups follow input-irrep classes (measured slower)
+    int fwd_row_split = 0;          // receiver-owned passes: waves per row forced (1, 2, 4); 0 = by N
     std::string source;             // generated HIP source
     std::vector<char> code;         // compiled gfx950 code object
 
@@ -90,6 +91,8 @@ struct Plan {
         hipModule_t module = nullptr;
         hipFunction_t conv_fwd = nullptr, conv_bwd = nullptr, tp_fwd = nullptr, tp_uvw = nullptr;
         hipFunction_t dbwd_recv = nullptr, dbwd_send = nullptr, conv_uvw = nullptr, tp_bwd = nullptr;
+        // receiver rows split over 2 / 4 waves (single-task plans; else null)
+        hipFunction_t conv_fwd_split[2] = {nullptr, nullptr}, dbwd_recv_split[2] = {nullptr, nullptr};
     };
     std::map<int, Loaded> loaded;
 
@@ -162,6 +165,10 @@ std::unique_ptr<Plan> make_conv_uvw_aux(const Plan &plan);
 std::vector<Group> radial_bwd_groups(const Plan &plan, int R, int &waves_per_eu);
 void unload_modules(Plan &plan);
 int64_t conv_uvw_g_width(const Plan &plan);
+// accumulators per lane of forward path group gi (the LDS words per lane of one split part)
+int fwd_group_accs(const Plan &plan, int gi);
+// whether the receiver-owned passes may split a receiver row over several waves
+bool fwd_splittable(const Plan &plan);
 int conv_uvw_g_items(const Plan &plan, std::vector<std::pair<int, int>> *items);
 
 }  // namespace cgtp

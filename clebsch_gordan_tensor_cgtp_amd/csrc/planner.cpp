@@ -356,12 +356,33 @@ void schedule(Plan &P)
         Group cur;
         std::vector<int> cur_inputs;
         int regs = 0;
-        for (int q : order) {
-            int need = word * (2 * P.out[q].l + 1);
+        auto need_of = [&](int q) { return word * (2 * P.out[q].l + 1); };
+        int total = 0;
+        for (int q : order) total += need_of(q);
+        // A plan that needs several groups anyway keeps each input class (consecutive slots
+        // fed by the same input blocks) whole where it fits: every group then gathers only
+        // its own blocks of the sender row instead of re-reading blocks that the previous
+        // group read too.
+        bool pack = total > budget && !P.fwd_split_inputs;
+        if (const char *e = std::getenv("CGTP_FWD_PACK_INPUTS")) pack = pack && std::atoi(e) != 0;
+        std::vector<int> class_need(order.size(), 0);  // need of the class starting at position k
+        for (int k = 0; k < (int)order.size();) {
+            int j = k, sum = 0;
+            while (j < (int)order.size() && inputs_of(order[j]) == inputs_of(order[k]) &&
+                   P.out[order[j]].mul == P.out[order[k]].mul)
+                sum += need_of(order[j++]);
+            class_need[k] = sum;
+            k = j;
+        }
+        for (int k = 0; k < (int)order.size(); ++k) {
+            const int q = order[k];
+            int need = need_of(q);
             int mul = P.out[q].mul;
             std::vector<int> ins = inputs_of(q);
-            if (!cur.paths.empty() &&
-                (regs + need > budget || mul != cur.mul || (P.fwd_split_inputs && ins != cur_inputs))) {
+            const bool class_start = class_need[k] > 0;
+            const bool keep_class = pack && class_start && class_need[k] <= budget && regs + class_need[k] > budget;
+            if (!cur.paths.empty() && (regs + need > budget || mul != cur.mul || keep_class ||
+                                       (P.fwd_split_inputs && ins != cur_inputs))) {
                 finish_group(cur);
                 P.fwd_groups.push_back(cur);
                 cur = Group();
@@ -556,6 +577,10 @@ void schedule(Plan &P)
     // CGTP_FWD_WAVES / CGTP_BWD_WAVES override (tuning).
     P.fwd_waves_per_eu = P.dtype == CGTP_F64 ? 2 : 4;
     if (const char *e = std::getenv("CGTP_FWD_WAVES")) P.fwd_waves_per_eu = std::max(1, std::atoi(e));
+    if (const char *e = std::getenv("CGTP_FWD_ROW_SPLIT")) {
+        const int v = std::atoi(e);
+        P.fwd_row_split = (v == 1 || v == 2 || v == 4) ? v : 0;
+    }
     // the double backward's receiver pass holds twice the forward's operands
     P.dbl_fwd_waves_per_eu = std::max(1, P.fwd_waves_per_eu / 2);
     if (const char *e = std::getenv("CGTP_DBL_FWD_WAVES")) P.dbl_fwd_waves_per_eu = std::max(1, std::atoi(e));

@@ -114,6 +114,18 @@ cgtp_status cgtp_plan_path_coefficients(const cgtp_plan *plan, int32_t path, int
                                         int32_t *ijk, double *values, int32_t *nnz);
 /* The generated HIP source of the plan's module (owned by the plan). */
 const char *cgtp_plan_source(const cgtp_plan *plan);
+/*
+ * Waves per receiver row that a receiver-owned pass launches for a graph of N
+ * receivers and E edges (LunaTP page, Abstract: node-centric execution; the
+ * split spreads one node's edges over several waves): pass 0 = the forward
+ * (cgtp_conv_forward, cgtp_conv_forward_ordered), pass 1 = the receiver pass
+ * of cgtp_conv_double_backward.  *split receives 1, 2 or 4; the kernel that
+ * runs is cgtp_conv_fwd / cgtp_conv_dbwd_recv with the suffix _split2 or
+ * _split4 when *split > 1.  The parts of a row are summed in part order, so
+ * the bits depend only on the plan, N and E.  Uses no device.
+ * Errors: CGTP_ERR_INVALID_ARG (NULL, pass not 0 or 1, N or E out of range).
+ */
+cgtp_status cgtp_conv_row_split(const cgtp_plan *plan, int64_t N, int64_t E, int32_t pass, int32_t *split);
 
 /*
  * Batched tensor product, use case A (sciencestack.ai page, Figure 4A):
@@ -166,7 +178,8 @@ cgtp_status cgtp_tp_backward(const cgtp_plan *plan, int64_t B, const void *x, co
  * non-decreasing, row_ptr[N] = E, 0 <= col < N); y [E][d_sh] and w
  * [E][weight_numel] are in CSR edge order; x [N][d_x]; out [N][d_out] is
  * overwritten, receivers without edges get zeros.  One owner per output row:
- * no atomics, bitwise deterministic.  uvw plans (fully connected multiplicity
+ * no atomics, bitwise deterministic (when a row is split over several waves,
+ * cgtp_conv_row_split, its parts are added in a fixed order).  uvw plans (fully connected multiplicity
  * mixing inside the convolution; Sobek page, Abstract): w is the shared
  * [weight_numel] block instead, out[n] = sum_e TP_uvw(x[col[e]], y[e], W),
  * the mixing running on MFMA per tile of 16 receivers.

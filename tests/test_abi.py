@@ -94,6 +94,32 @@ def test_generated_source_has_literal_nonzeros_and_no_atomics():
                 assert rnd(v) in lits, (dtype, p, v)
 
 
+def test_row_split_rule():
+    """Waves per receiver row: doubled while the launch has under four waves per wave slot
+    (1024 SIMDs x the occupancy target) and each part keeps >= 8 edge groups of the mean row;
+    plans with several path groups or channel tiles never split."""
+    c2 = cg.plan_for(synth.WORKLOADS["c2"], "f32")   # 32 channels: 2 edges per wave step, 4 waves/SIMD
+    assert c2.row_split(5000, 200_000) == 2
+    assert c2.row_split(601, 601 * 20) == 1 and c2.row_split(601, 601 * 40) == 2
+    assert c2.row_split(601, 601 * 160) == 4
+    assert c2.row_split(20_000, 800_000) == 1        # 20,000 waves already >= 4 x 4096 slots
+    assert c2.row_split(10_000, 400_000) == 2
+    assert c2.row_split(1, 0) == 1 and c2.row_split(0, 0) == 1
+    assert c2.row_split(5000, 200_000, double_backward=True) == 2   # 2 waves/SIMD: 8192 slots
+    assert c2.row_split(9000, 360_000, double_backward=True) == 1
+    c5 = cg.plan_for(synth.WORKLOADS["c5"], "f32")   # 64 channels: one edge per wave step
+    assert c5.row_split(200_000, 10_000_000) == 1
+    assert c5.row_split(2000, 100_000) == 4
+    c3 = cg.plan_for(synth.WORKLOADS["c3"], "f32")   # three path groups x two channel tiles
+    assert c3.row_split(100, 100_000) == 1
+    src = c2.source
+    assert "cgtp_conv_fwd_split2(" in src and "cgtp_conv_dbwd_recv_split4(" in src
+    assert "cgtp_conv_fwd_split2(" not in c3.source
+    with pytest.raises(cg.CgtpError, match="pass must be"):
+        v = ctypes.c_int32()
+        cg._check(cg.lib().cgtp_conv_row_split(c2.handle, 10, 10, 2, ctypes.byref(v)))
+
+
 # ---------------------------------------------------------------------------- error paths
 
 def test_plan_errors():
