@@ -11,7 +11,9 @@
 
 #include <cstdio>
 #include <cstdlib>
+#include <climits>
 #include <cstring>
+#include <type_traits>
 #include <fstream>
 #include <sstream>
 
@@ -66,16 +68,85 @@ static void write_file_atomic(const std::string &path, const std::vector<char> &
     std::rename(tmp.c_str(), path.c_str());
 }
 
+// The compiler.  A host process may already hold another hipRTC and code-object compiler
+// than the ROCm installation's (a framework loaded first can bring its own copies, and a
+// library with the same soname is then shared by everyone); their code for the same source can
+// differ (measured: a register spill in one and not the other).  So the installation's hipRTC is
+// loaded in a link namespace of its own (dlmopen), where it also finds the installation's
+// compiler library, and the cache key names the compiler that made each code object.  If that
+// load fails, the hipRTC the library was linked against is used.
+struct Rtc {
+    decltype(&hiprtcCreateProgram) create = hiprtcCreateProgram;
+    decltype(&hiprtcCompileProgram) compile = hiprtcCompileProgram;
+    decltype(&hiprtcGetProgramLogSize) log_size = hiprtcGetProgramLogSize;
+    decltype(&hiprtcGetProgramLog) log = hiprtcGetProgramLog;
+    decltype(&hiprtcGetCodeSize) code_size = hiprtcGetCodeSize;
+    decltype(&hiprtcGetCode) code = hiprtcGetCode;
+    decltype(&hiprtcDestroyProgram) destroy = hiprtcDestroyProgram;
+    decltype(&hiprtcGetErrorString) error_string = hiprtcGetErrorString;
+    decltype(&hiprtcVersion) version = hiprtcVersion;
+    std::string identity;  // which library compiles, for the cache key
+};
+
+static std::string real_path_of(void *sym)
+{
+    Dl_info info;
+    if (!dladdr(sym, &info) || !info.dli_fname) return "unknown";
+    char buf[4096];
+    return ::realpath(info.dli_fname, buf) ? std::string(buf) : std::string(info.dli_fname);
+}
+
+static const Rtc &rtc()
+{
+    static const Rtc r = [] {
+        Rtc x;
+        std::string path;
+        if (const char *e = std::getenv("CGTP_HIPRTC")) {
+            path = e;
+        } else {
+            const char *root = std::getenv("ROCM_PATH");
+            path = std::string(root && *root ? root : "/opt/rocm") + "/lib/libhiprtc.so.7";
+        }
+        void *h = path.empty() ? nullptr : ::dlmopen(LM_ID_NEWLM, path.c_str(), RTLD_NOW | RTLD_LOCAL);
+        bool ok = h != nullptr;
+        auto get = [&](auto &fn, const char *name) {
+            if (!ok) return;
+            void *p = ::dlsym(h, name);
+            if (p)
+                fn = reinterpret_cast<std::remove_reference_t<decltype(fn)>>(p);
+            else
+                ok = false;
+        };
+        Rtc y;
+        get(y.create, "hiprtcCreateProgram");
+        get(y.compile, "hiprtcCompileProgram");
+        get(y.log_size, "hiprtcGetProgramLogSize");
+        get(y.log, "hiprtcGetProgramLog");
+        get(y.code_size, "hiprtcGetCodeSize");
+        get(y.code, "hiprtcGetCode");
+        get(y.destroy, "hiprtcDestroyProgram");
+        get(y.error_string, "hiprtcGetErrorString");
+        get(y.version, "hiprtcVersion");
+        if (ok) x = y;
+        x.identity = real_path_of(reinterpret_cast<void *>(x.create));
+        int major = 0, minor = 0;
+        x.version(&major, &minor);
+        x.identity += " " + std::to_string(major) + "." + std::to_string(minor);
+        if (std::getenv("CGTP_LOG")) std::fprintf(stderr, "[cgtp] compiler: %s\n", x.identity.c_str());
+        return x;
+    }();
+    return r;
+}
+
 void compile_module(Plan &P) { P.code = compile_source(P.source); }
 
 std::vector<char> compile_source(const std::string &source)
 {
     std::vector<char> code;
-    int major = 0, minor = 0;
-    hiprtcVersion(&major, &minor);
+    const Rtc &R = rtc();
     std::string opts;
     for (const char *o : kOptions) opts += std::string(o) + " ";
-    std::string key_src = source + "\n//" + opts + std::to_string(major) + "." + std::to_string(minor);
+    std::string key_src = source + "\n//" + opts + R.identity;
     char name[64];
     std::snprintf(name, sizeof name, "cgtp_%016llx%016llx.hsaco",
                   (unsigned long long)fnv1a(key_src, 1469598103934665603ull),
@@ -85,22 +156,22 @@ std::vector<char> compile_source(const std::string &source)
     if (read_file(path, code)) return code;
 
     hiprtcProgram prog;
-    if (hiprtcCreateProgram(&prog, source.c_str(), "cgtp_module.hip", 0, nullptr, nullptr) != HIPRTC_SUCCESS)
+    if (R.create(&prog, source.c_str(), "cgtp_module.hip", 0, nullptr, nullptr) != HIPRTC_SUCCESS)
         throw Error(CGTP_ERR_COMPILE, "hiprtcCreateProgram failed");
-    hiprtcResult rc = hiprtcCompileProgram(prog, (int)(sizeof kOptions / sizeof kOptions[0]), kOptions);
+    hiprtcResult rc = R.compile(prog, (int)(sizeof kOptions / sizeof kOptions[0]), kOptions);
     if (rc != HIPRTC_SUCCESS) {
         size_t n = 0;
-        hiprtcGetProgramLogSize(prog, &n);
+        R.log_size(prog, &n);
         std::string log(n, '\0');
-        if (n) hiprtcGetProgramLog(prog, &log[0]);
-        hiprtcDestroyProgram(&prog);
-        throw Error(CGTP_ERR_COMPILE, std::string("hipRTC: ") + hiprtcGetErrorString(rc) + "\n" + log);
+        if (n) R.log(prog, &log[0]);
+        R.destroy(&prog);
+        throw Error(CGTP_ERR_COMPILE, std::string("hipRTC: ") + R.error_string(rc) + "\n" + log);
     }
     size_t n = 0;
-    hiprtcGetCodeSize(prog, &n);
+    R.code_size(prog, &n);
     code.resize(n);
-    hiprtcGetCode(prog, code.data());
-    hiprtcDestroyProgram(&prog);
+    R.code(prog, code.data());
+    R.destroy(&prog);
     ::mkdir(dir.c_str(), 0755);
     write_file_atomic(path, code);
     return code;
