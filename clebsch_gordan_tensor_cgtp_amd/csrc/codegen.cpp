@@ -1645,49 +1645,69 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
             o("T d", v, "_", i, " = (T)0;");
         }
     }
-    // the (path, k) blocks in order; each block loads the next one's gradient values (the B
-    // operands of G) before its own work, so that their latency is covered by the block
-    std::vector<std::pair<int, int>> blocks;
-    for (int pi : g.paths) {
+    // The (path, k) blocks in order, software-pipelined: block b issues the MFMAs of block b + 1's
+    // G (independent of its own) before its VALU work on G_b, so the MFMA chain runs under that
+    // work instead of stalling it; gradient values are loaded two blocks ahead (three register
+    // sets) and the W operands one path ahead (two sets, by path parity).
+    std::vector<std::pair<int, int>> blocks;  // (index into g.paths, k)
+    for (int q = 0; q < (int)g.paths.size(); ++q) {
         std::set<int> ks;
-        for (const Nonzero &z : P.paths[pi].nz) ks.insert(z.k);
-        for (int k : ks) blocks.push_back({pi, k});
+        for (const Nonzero &z : P.paths[g.paths[q]].nz) ks.insert(z.k);
+        for (int k : ks) blocks.push_back({q, k});
     }
-    auto load_next = [&](size_t bi) {
-        const Path &p = P.paths[blocks[bi].first];
+    const int nb = (int)blocks.size();
+    auto wch_of = [&](int q) { return (P.paths[g.paths[q]].mul_out + 3) / 4; };
+    auto load_g = [&](int bi) {
+        const Path &p = P.paths[g.paths[blocks[bi].first]];
         const int k = blocks[bi].second, n3 = n_of(p.l3);
-        for (int c = 0; c < (p.mul_out + 3) / 4; ++c)
-            o("gq", c, " = ", 4 * c, " + usub < ", p.mul_out, " ? g[(size_t)rr * DOUT + ", p.o, " + (", 4 * c, " + usub < ", p.mul_out,
-              " ? ", 4 * c, " + usub : 0) * ", n3, " + ", k, "] : (T)0;");
+        for (int c = 0; c < wch_of(blocks[bi].first); ++c)
+            o("gs", bi % 3, "_", c, " = ", 4 * c, " + usub < ", p.mul_out, " ? g[(size_t)rr * DOUT + ", p.o, " + (", 4 * c,
+              " + usub < ", p.mul_out, " ? ", 4 * c, " + usub : 0) * ", n3, " + ", k, "] : (T)0;");
     };
-    for (int c = 0; c < 4; ++c) o("T gq", c, " = (T)0;");
-    if (!blocks.empty()) load_next(0);
-    size_t bidx = 0;
-    for (int pi : g.paths) {
-        const Path &p = P.paths[pi];
+    // A operands of G: W_p[u = lane % 16][w = 4c + lane / 16]
+    auto load_w = [&](int q) {
+        const Path &p = P.paths[g.paths[q]];
+        for (int c = 0; c < wch_of(q); ++c) {
+            o("{");
+            o.ind++;
+            o("const bool wok = rl < ", p.mul_in, " && ", 4 * c, " + usub < ", p.mul_out, ";");
+            o("const T wv = w[", p.w_off, " + (wok ? rl * ", p.mul_out, " + ", 4 * c, " + usub : 0)];");
+            o("wa", q % 2, "_", c, " = wok ? wv : (T)0;");
+            o.ind--;
+            o("}");
+        }
+    };
+    auto issue_g = [&](int bi) {
+        const int q = blocks[bi].first;
+        o("G", bi, " = (V4){0, 0, 0, 0};");
+        for (int c = 0; c < wch_of(q); ++c) o("G", bi, " = MFMA(wa", q % 2, "_", c, ", gs", bi % 3, "_", c, ", G", bi, ");");
+    };
+    for (int set = 0; set < 3; ++set)
+        for (int c = 0; c < 4; ++c) o("T gs", set, "_", c, " = (T)0;");
+    for (int set = 0; set < 2; ++set)
+        for (int c = 0; c < 4; ++c) o("T wa", set, "_", c, " = (T)0;");
+    for (int bi = 0; bi < nb; ++bi) o("V4 G", bi, ";");
+    if (nb > 0) {
+        load_w(0);
+        if (g.paths.size() > 1) load_w(1);
+        load_g(0);
+        if (nb > 1) load_g(1);
+        issue_g(0);
+    }
+    int bi = 0;
+    for (int q = 0; q < (int)g.paths.size(); ++q) {
+        const Path &p = P.paths[g.paths[q]];
         const int n2 = n_of(p.l2);
         o("{");
         o.ind++;
-        // A operands of G: W_p[u = lane % 16][w = 4c + lane / 16]
-        const int wch = (p.mul_out + 3) / 4;
-        for (int c = 0; c < wch; ++c) {
-            o("const bool wok", c, " = rl < ", p.mul_in, " && ", 4 * c, " + usub < ", p.mul_out, ";");
-            o("const T wv", c, " = w[", p.w_off, " + (wok", c, " ? rl * ", p.mul_out, " + ", 4 * c, " + usub : 0)];");
-            o("const T wa", c, " = wok", c, " ? wv", c, " : (T)0;");
-        }
         for (int j = 0; j < n2; ++j) o("T h", j, " = (T)0;");
         std::map<int, std::map<int, std::vector<const Nonzero *>>> byki;  // k -> i -> nonzeros
         for (const Nonzero &z : p.nz) byki[z.k][z.i].push_back(&z);
         for (auto &kk : byki) {
-            const int k = kk.first;
             o("{");
             o.ind++;
-            for (int c = 0; c < wch; ++c) o("const T gb", c, " = gq", c, ";");
-            if (bidx + 1 < blocks.size()) load_next(bidx + 1);
-            ++bidx;
-            (void)k;
-            o("V4 G = {0, 0, 0, 0};");
-            for (int c = 0; c < wch; ++c) o("G = MFMA(wa", c, ", gb", c, ", G);");
+            if (bi + 2 < nb) load_g(bi + 2);
+            if (bi + 1 < nb) issue_g(bi + 1);
             for (auto &ii : kk.second) {
                 const int i = ii.first;
                 const auto &v = ii.second;
@@ -1701,18 +1721,23 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
                 o("{");
                 o.ind++;
                 o("const T A = ", e.str(), ";");
-                for (int vv = 0; vv < 4; ++vv) o("d", vv, "_", i, " = FMA(A, G[", vv, "], d", vv, "_", i, ");");
-                o("const T si = FMA(x0_", i, ", G[0], FMA(x1_", i, ", G[1], FMA(x2_", i, ", G[2], x3_", i, " * G[3])));");
+                for (int vv = 0; vv < 4; ++vv) o("d", vv, "_", i, " = FMA(A, G", bi, "[", vv, "], d", vv, "_", i, ");");
+                o("const T si = FMA(x0_", i, ", G", bi, "[0], FMA(x1_", i, ", G", bi, "[1], FMA(x2_", i, ", G", bi, "[2], x3_", i,
+                  " * G", bi, "[3])));");
                 for (const Nonzero *z : v) o("h", z->j, " = FMA(", lit(z->c, f64), ", si, h", z->j, ");");
                 o.ind--;
                 o("}");
             }
+            ++bi;
             // one output component at a time: without this the loads and MFMAs of every k of the
             // path are issued together and all of their results stay live
             o("__builtin_amdgcn_sched_barrier(0);");
             o.ind--;
             o("}");
         }
+        // this path's W set is free once its last G has been issued (one block ago): fetch the
+        // W of the path after next into it
+        if (q + 2 < (int)g.paths.size()) load_w(q + 2);
         // dY of this path: sum the row's four lanes, then lane usub == 0 adds into the wave's LDS rows
         for (int j = 0; j < n2; ++j) {
             o("h", j, " += __shfl_xor(h", j, ", 16);");
