@@ -244,3 +244,26 @@ def test_conv_uvw_backward_workspace_and_modules():
     assert "&w[" not in src_xy and "dw[" not in src_xy
     for src in (src_gw, src_xy):
         assert "atomic" not in src.lower()
+
+
+def test_compiled_code_does_not_depend_on_what_the_process_loaded_first(tmp_path):
+    """The generated module is compiled by the ROCm installation's hipRTC in a link namespace of
+    its own, so a process that imported torch first (which brings its own hipRTC and compiler
+    library under the same soname) writes the same code object under the same cache key."""
+    import subprocess
+    import sys
+    prog = ("import sys\n"
+            "if sys.argv[1] == 'torch': import torch\n"
+            "from clebsch_gordan_tensor_cgtp_amd import binding as cg\n"
+            "cg.Plan('4x0e+4x1o', cg.sh_irreps(2), cg.per_path_out_irreps('4x0e+4x1o', 2, 2), 'uvu', 'f32')\n")
+    dirs = []
+    for first in ("torch", "plain"):
+        d = tmp_path / first
+        d.mkdir()
+        env = dict(os.environ, CGTP_CACHE_DIR=str(d), PYTHONPATH=ROOT)
+        subprocess.run([sys.executable, "-c", prog, first], check=True, env=env, cwd=ROOT, timeout=600)
+        dirs.append(d)
+    a = sorted(p.name for p in dirs[0].iterdir() if p.suffix == ".hsaco")
+    b = sorted(p.name for p in dirs[1].iterdir() if p.suffix == ".hsaco")
+    assert a == b and len(a) == 1
+    assert (dirs[0] / a[0]).read_bytes() == (dirs[1] / b[0]).read_bytes()
