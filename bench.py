@@ -449,6 +449,32 @@ def bench_radial(a, spec, plan, d, host_graph, device):
     print(json.dumps(line), flush=True)
 
 
+def spread(evs):
+    """Median, min and max over the timed steps of the forward and backward launch times."""
+    f = [e[0].elapsed_time(e[1]) for e in evs]
+    b = [e[1].elapsed_time(e[2]) for e in evs]
+    return {"fwd": [float(np.median(f)), float(np.min(f)), float(np.max(f))],
+            "bwd": [float(np.median(b)), float(np.min(b)), float(np.max(b))], "order": "median, min, max"}
+
+
+def cold_cache_times(a, step, device):
+    """The same steps, each after writing a 1 GiB buffer (more than the 4 MB L2 of every XCD and
+    the 256 MB last-level cache) outside its timed region: the forward and backward launch times
+    with nothing of the step's inputs left in the caches.  Reported beside the warm figures; the
+    headline value is the warm K-step wall time."""
+    import torch
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=device)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    for k in range(a.steps):
+        scratch.fill_(float(k))
+        step(evs[k])
+    torch.cuda.synchronize()
+    del scratch
+    return {"fwd_ms": float(np.median([e[0].elapsed_time(e[1]) for e in evs])),
+            "bwd_ms": float(np.median([e[1].elapsed_time(e[2]) for e in evs])),
+            "flush": "1 GiB fill before each step, outside its events", "statistic": "median"}
+
+
 def split_kernel(base, split):
     """Name of the receiver-owned kernel that gives each receiver row `split` waves."""
     return base if split == 1 else f"{base}_split{split}"
@@ -767,6 +793,7 @@ def main():
     fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     ms_per_step = wall * 1e3 / a.steps
+    cold = cold_cache_times(a, step, device)
     fwd_b, bwd_b = algorithmic_bytes(plan, N, E, es)
     fwd_k = split_kernel("cgtp_conv_fwd", plan.row_split(N, E))
     dom = ("cgtp_conv_bwd", bwd_ms, bwd_b) if bwd_ms >= fwd_ms else (fwd_k, fwd_ms, fwd_b)
@@ -790,7 +817,8 @@ def main():
                    "step": "conv_forward + conv_backward (grad_x, grad_y, grad_w)",
                    "receiver_schedule": "natural" if a.natural_order else "heavy-first",
                    "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
-                   "fwd_edges_per_s": E / (fwd_ms * 1e-3), "bwd_edges_per_s": E / (bwd_ms * 1e-3)},
+                   "fwd_edges_per_s": E / (fwd_ms * 1e-3), "bwd_edges_per_s": E / (bwd_ms * 1e-3),
+                   "spread_ms": spread(evs), "cold_cache": cold},
         "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": dom[2], "avg_launch_ms": dom[1],
