@@ -337,10 +337,17 @@ void schedule(Plan &P)
     if (const char *e = std::getenv("CGTP_NT")) P.stream_hint = std::atoi(e) != 0;
     const int word = P.dtype == CGTP_F64 ? 2 : 1;
     // 32-bit registers per lane for the forward accumulators (CGTP_FWD_BUDGET overrides, tuning).
-    // fp64 runs at two waves per SIMD, which leaves room for twice the fp32 budget: on the
-    // MACE-like plan that is 3 path groups instead of 5 (fewer re-reads of the sender row),
-    // 232 VGPRs and no spill, 12.08 -> 10.68 ms.  fp32 with 128 at two waves: 5.20 against 4.63 ms.
-    const int budget = std::max(16, getenv_int("CGTP_FWD_BUDGET", word == 2 ? 128 : 64));
+    // An fp64 plan that needs more than two groups at 64 registers already runs at two waves per
+    // SIMD, which leaves room for twice that budget: on the MACE-like plan 3 path groups instead of
+    // 5 (fewer re-reads of the sender row), 232 VGPRs and no spill, 12.08 -> 10.6 ms.  A smaller
+    // plan keeps 64: the NequIP-like fp64 plan in one group needs 208 VGPRs (two waves per SIMD,
+    // 362 us) against two groups at 122 (four waves, 296 us).  fp32 with 128 at two waves on the
+    // MACE-like plan: 5.20 against 4.63 ms.
+    int total_need = 0;
+    if (P.mode == CGTP_UVU)
+        for (const Irrep &o : P.out) total_need += word * (2 * o.l + 1);
+    const int budget =
+        std::max(16, getenv_int("CGTP_FWD_BUDGET", word == 2 && total_need > 2 * 64 ? 128 : 64));
     P.fwd_groups.clear();
     if (P.mode == CGTP_UVU) {
         std::vector<std::vector<int>> slot_paths(P.out.size());
