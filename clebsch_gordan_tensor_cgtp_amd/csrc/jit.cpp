@@ -127,7 +127,10 @@ static const Rtc &rtc()
         get(y.destroy, "hiprtcDestroyProgram");
         get(y.error_string, "hiprtcGetErrorString");
         get(y.version, "hiprtcVersion");
-        if (ok) x = y;
+        if (ok)
+            x = y;
+        else if (h)
+            ::dlclose(h);
         x.identity = real_path_of(reinterpret_cast<void *>(x.create));
         int major = 0, minor = 0;
         x.version(&major, &minor);

@@ -97,9 +97,13 @@ typedef struct cgtp_path_info {
  * generate one gfx950 module with the nonzeros as compile-time constants
  * (sciencestack.ai page, TL;DR and Abstract: JIT generation with static
  * analysis; OpenEquivariance discussion: nonzeros in the instruction stream).
- * The module is compiled with hipRTC (or taken from the on-disk cache,
- * $CGTP_CACHE_DIR, default: a jit_cache folder next to the library) and
- * loaded on a device at its first launch there.  Allocates no device memory.
+ * The module is compiled with the ROCm installation's hipRTC
+ * ($ROCM_PATH/lib/libhiprtc.so.7, or $CGTP_HIPRTC), loaded into a link
+ * namespace of its own so that a hipRTC already in the process (one bundled
+ * with a framework) does not take its place, or taken from the on-disk cache
+ * ($CGTP_CACHE_DIR, default: a jit_cache folder next to the library; the key
+ * names the compiler).  The module is loaded on a device at its first launch
+ * there.  Allocates no device memory.
  * uvu needs mul_out == mul_in on every path; both modes need SH mul == 1.
  * Errors: CGTP_ERR_INVALID_ARG (null), CGTP_ERR_IRREPS, CGTP_ERR_COMPILE.
  */
