@@ -441,11 +441,9 @@ cgtp_status cgtp_tp_backward(const cgtp_plan *plan, int64_t B, const void *x, co
         }
         const auto &F = cgtp::uvw_backward_for_current_device(P);
         if (grad_x || grad_y) {
-            // one launch per input block, in order (dY is added over the launches)
-            for (int grp = 0; grp < (int)P.uvb_x_groups.size(); ++grp) {
-                void *args[] = {&x, &y, &w, &grad_out, &grad_x, &grad_y, &nrows, &nblocks, &grp};
-                launch(F.xy, nblocks, args, stream);
-            }
+            // one workgroup of four waves per 16-row block; the waves share the input blocks
+            void *args[] = {&x, &y, &w, &grad_out, &grad_x, &grad_y, &nrows, &nblocks};
+            launch(F.xy, nblocks * 4, args, stream);
         }
         if (grad_w) {
             long nwaves = nchunks * (long)P.uvb_w_groups.size();

@@ -1629,9 +1629,7 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
     o("const long row = blk * 16 + rl;");
     o("const bool live = row < nrows;");
     o("const long rr = live ? row : nrows - 1;  // rows past the end read row nrows-1 and store nothing");
-    o("T* dyw = dyl + wv * ", 16 * P.d_sh, ";  // this wave's dY rows");
-    o("for (int c = lane; c < ", 16 * P.d_sh, "; c += 64) dyw[c] = (T)0;");
-    o("WAVE_SYNC();");
+    o("T* dyw = dyl + wv * ", 16 * P.d_sh, ";  // this wave's dY rows (zeroed by the kernel)");
     for (int b : t.i2) {
         int off = 0;
         for (int bb = 0; bb < b; ++bb) off += P.sh[bb].dim();
@@ -1777,13 +1775,6 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
             off += P.ins[b].dim();
         }
     }
-    o.ind--;
-    o("}");
-    o("WAVE_SYNC();");
-    // dY of the rows: the first launch writes every column, later launches add theirs
-    o("if (live && dy) {");
-    o.ind++;
-    o("for (int j = usub; j < DSH; j += 4) dy[(size_t)rr * DSH + j] ", gi == 0 ? "=" : "+=", " dyw[rl * DSH + j];");
     o.ind--;
     o("}");
     o.ind--;
@@ -1973,20 +1964,58 @@ void emit_uvb_kernels(Out &o, const Plan &P)
     o("#define WAVE_SYNC() do { __builtin_amdgcn_fence(__ATOMIC_RELEASE, \"wavefront\"); "
       "__builtin_amdgcn_wave_barrier(); __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, \"wavefront\"); } while (0)");
     for (int gi = 0; gi < (int)P.uvb_x_groups.size(); ++gi) emit_uvb_xy_group(o, P, gi);
+    // One workgroup per 16-row block; its four waves share the input blocks (each wave its own
+    // list, balanced by a cost estimate, heaviest first), write the dx of their blocks, and add
+    // their dY rows in LDS; after the barrier the four waves' rows are summed in wave order.
+    std::vector<std::pair<long, int>> cost;
+    for (int gi = 0; gi < (int)P.uvb_x_groups.size(); ++gi) {
+        long c = 0;
+        for (int pi : P.uvb_x_groups[gi].paths) {
+            const Path &p = P.paths[pi];
+            c += (long)p.nz.size() * 6 + 16L * n_of(p.l3);
+        }
+        cost.push_back({c, gi});
+    }
+    std::stable_sort(cost.begin(), cost.end(), [](auto &a, auto &b) { return a.first > b.first; });
+    std::vector<std::vector<int>> lists(4);
+    std::vector<long> load(4, 0);
+    for (auto &cg : cost) {
+        const int wv = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+        lists[wv].push_back(cg.second);
+        load[wv] += cg.first;
+    }
     o("extern \"C\" __global__ void __launch_bounds__(256, 1) cgtp_tp_uvw_bwd_xy(const T* __restrict__ x, "
       "const T* __restrict__ y, const T* __restrict__ w, const T* __restrict__ g, T* __restrict__ dx, "
-      "T* __restrict__ dy, long nrows, long nblocks, int group)");
+      "T* __restrict__ dy, long nrows, long nblocks)");
     o("{");
     o.ind++;
     o("__shared__ T dyl[", 4 * 16 * P.d_sh, "];");
-    o("const long blk = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const long blk = blockIdx.x;");
     o("const int wv = threadIdx.x >> 6;");
     o("const int lane = threadIdx.x & 63;");
-    o("if (blk >= nblocks) return;");
-    o("switch (group) {");
-    for (int gi = 0; gi < (int)P.uvb_x_groups.size(); ++gi)
-        o("case ", gi, ": uvbx_g", gi, "(blk, wv, lane, x, y, w, g, dx, dy, nrows, dyl); break;");
+    o("for (int c = threadIdx.x; c < ", 4 * 16 * P.d_sh, "; c += 256) dyl[c] = (T)0;");
+    o("__syncthreads();");
+    o("switch (wv) {");
+    for (int wv = 0; wv < 4; ++wv) {
+        o("case ", wv, ":");
+        o.ind++;
+        for (int gi : lists[wv]) o("uvbx_g", gi, "(blk, wv, lane, x, y, w, g, dx, dy, nrows, dyl);");
+        o("break;");
+        o.ind--;
+    }
     o("default: break;");
+    o("}");
+    o("__syncthreads();");
+    o("if (dy) {");
+    o.ind++;
+    o("for (int c = threadIdx.x; c < ", 16 * P.d_sh, "; c += 256) {");
+    o.ind++;
+    o("const long row = blk * 16 + c / DSH;");
+    o("if (row < nrows) dy[(size_t)row * DSH + c % DSH] = ((dyl[c] + dyl[", 16 * P.d_sh, " + c]) + dyl[", 32 * P.d_sh,
+      " + c]) + dyl[", 48 * P.d_sh, " + c];");
+    o.ind--;
+    o("}");
+    o.ind--;
     o("}");
     o.ind--;
     o("}");
