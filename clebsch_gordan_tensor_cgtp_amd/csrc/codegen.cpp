@@ -1797,18 +1797,30 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
     for (int pi : g.paths) o("V4 D", pi, " = {0, 0, 0, 0};");
     o("const long b0 = chunk * bpc;");
     o("const long b1 = b0 + bpc < nblocks ? b0 + bpc : nblocks;");
-    o("for (long blk = b0; blk < b1; ++blk) {");
-    o.ind++;
-    o("const long row = blk * 16 + rl;");
-    o("const bool live = row < nrows;");
-    o("const long rr = live ? row : nrows - 1;");
-    for (int b : t.i2) {
-        int off = 0;
-        for (int bb = 0; bb < b; ++bb) off += P.sh[bb].dim();
-        for (int j = 0; j < n_of(P.sh[b].l); ++j) o("const T y", b, "_", j, " = y[(size_t)rr * DSH + ", off + j, "];");
-    }
     std::map<int, std::vector<int>> by_i1;
     for (int pi : g.paths) by_i1[P.paths[pi].i1].push_back(pi);
+    // Every load a row block needs is issued one step ahead: its y and the x of its first input
+    // block during the previous row block, the x of each later input block during the one
+    // before it, and the gradient values of its first (path, k) block during the previous row
+    // block's last one (one wave per SIMD: nothing else covers their latency).
+    auto y_loads = [&](const std::string &dst, const std::string &rrx) {
+        for (int b : t.i2) {
+            int off = 0;
+            for (int bb = 0; bb < b; ++bb) off += P.sh[bb].dim();
+            for (int j = 0; j < n_of(P.sh[b].l); ++j)
+                o(dst, b, "_", j, " = y[(size_t)", rrx, " * DSH + ", off + j, "];");
+        }
+    };
+    auto x_loads = [&](int i1, const std::string &rrx) {
+        const Irrep &ir = P.ins[i1];
+        const int n1 = n_of(ir.l);
+        const int a = P.paths[by_i1[i1][0]].a;
+        // x in the forward's layout: lane holds u = 4c + lane / 16
+        for (int c = 0; c < 4; ++c)
+            for (int i = 0; i < n1; ++i)
+                o("xp", c, "_", i, " = ", 4 * c, " + usub < ", ir.mul, " ? x[(size_t)", rrx, " * DX + ", a, " + (", 4 * c,
+                  " + usub < ", ir.mul, " ? ", 4 * c, " + usub : 0) * ", n1, " + ", i, "] : (T)0;");
+    };
     // the (path, k) blocks in emission order; each block loads the next one's B operands (the
     // gradient values of its four row groups) before its own work, so that their latency is
     // covered by the block (one wave per SIMD leaves nothing else to hide it)
@@ -1819,34 +1831,70 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
             for (const Nonzero &z : P.paths[pi].nz) ks.insert(z.k);
             for (int k : ks) blocks.push_back({pi, k});
         }
-    auto load_next = [&](size_t bi, bool declare) {
+    // gradient values of block bi of the row block starting at row `rb` (a variable name)
+    auto load_g = [&](size_t bi, const std::string &rb) {
         const Path &p = P.paths[blocks[bi].first];
         const int k = blocks[bi].second, n3 = n_of(p.l3);
         for (int m = 0; m < 4; ++m) {
             o("{");
             o.ind++;
-            o("const long br = blk * 16 + ", 4 * m, " + usub;");
+            o("const long br = ", rb, " * 16 + ", 4 * m, " + usub;");
             o("const bool bok = br < nrows && rl < ", p.mul_out, ";");
             o("gp", m, " = bok ? g[(size_t)br * DOUT + ", p.o, " + rl * ", n3, " + ", k, "] : (T)0;");
             o.ind--;
             o("}");
         }
-        (void)declare;
     };
-    for (int m = 0; m < 4; ++m) o("T gp", m, ";");
-    if (!blocks.empty()) load_next(0, true);
+    int n1max = 1;
+    for (auto &kv : by_i1) n1max = std::max(n1max, n_of(P.ins[kv.first].l));
+    for (int b : t.i2)
+        for (int j = 0; j < n_of(P.sh[b].l); ++j) o("T yp", b, "_", j, " = (T)0;");
+    for (int c = 0; c < 4; ++c)
+        for (int i = 0; i < n1max; ++i) o("T xp", c, "_", i, " = (T)0;");
+    for (int m = 0; m < 4; ++m) o("T gp", m, " = (T)0;");
+    o("if (b0 < b1) {");
+    o.ind++;
+    o("const long row0 = b0 * 16 + rl;");
+    o("const long rr0 = row0 < nrows ? row0 : nrows - 1;");
+    y_loads("yp", "rr0");
+    if (!by_i1.empty()) x_loads(by_i1.begin()->first, "rr0");
+    if (!blocks.empty()) load_g(0, "b0");
+    o.ind--;
+    o("}");
+    o("for (long blk = b0; blk < b1; ++blk) {");
+    o.ind++;
+    o("const long row = blk * 16 + rl;");
+    o("const bool live = row < nrows;");
+    o("const long rr = live ? row : nrows - 1;");
+    o("const bool more = blk + 1 < b1;");
+    o("const long rowx = (blk + 1) * 16 + rl;");
+    o("const long rrx = more ? (rowx < nrows ? rowx : nrows - 1) : rr;");
+    for (int b : t.i2)
+        for (int j = 0; j < n_of(P.sh[b].l); ++j) o("const T y", b, "_", j, " = yp", b, "_", j, ";");
+    o("if (more) {");
+    o.ind++;
+    y_loads("yp", "rrx");
+    o.ind--;
+    o("}");
     size_t bidx = 0;
+    size_t sec = 0;
     for (auto &kv : by_i1) {
         const Irrep &ir = P.ins[kv.first];
         const int n1 = n_of(ir.l);
-        const int a = P.paths[kv.second[0]].a;
         o("{");
         o.ind++;
-        // x in the forward's layout: lane holds u = 4c + lane / 16
         for (int c = 0; c < 4; ++c)
-            for (int i = 0; i < n1; ++i)
-                o("const T x", c, "_", i, " = ", 4 * c, " + usub < ", ir.mul, " ? x[(size_t)rr * DX + ", a, " + (", 4 * c, " + usub < ",
-                  ir.mul, " ? ", 4 * c, " + usub : 0) * ", n1, " + ", i, "] : (T)0;");
+            for (int i = 0; i < n1; ++i) o("const T x", c, "_", i, " = xp", c, "_", i, ";");
+        // the next input block's x: this row block's, or the next row block's first
+        if (++sec < by_i1.size()) {
+            x_loads(std::next(by_i1.begin(), (long)sec)->first, "rr");
+        } else {
+            o("if (more) {");
+            o.ind++;
+            x_loads(by_i1.begin()->first, "rrx");
+            o.ind--;
+            o("}");
+        }
         for (int pi : kv.second) {
             const Path &p = P.paths[pi];
             std::map<int, std::map<int, std::vector<const Nonzero *>>> byki;
@@ -1855,7 +1903,15 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
                 o("{");
                 o.ind++;
                 for (int m = 0; m < 4; ++m) o("const T gc", m, " = gp", m, ";");
-                if (bidx + 1 < blocks.size()) load_next(bidx + 1, false);
+                if (bidx + 1 < blocks.size()) {
+                    load_g(bidx + 1, "blk");
+                } else {
+                    o("if (more) {");
+                    o.ind++;
+                    load_g(0, "(blk + 1)");
+                    o.ind--;
+                    o("}");
+                }
                 ++bidx;
                 for (auto &ii : kk.second) {
                     const auto &v = ii.second;
