@@ -541,7 +541,7 @@ void schedule(Plan &P)
         // NequIP-like graph: fewer launches and index loads, the g row read in
         // one pass); larger problems are split so that no group spills.
         auto make_groups = [&](bool dbl, std::vector<Group> &groups, int &waves) {
-            const int split_budget = 168, one_group_limit = 200;
+            const int split_budget = getenv_int("CGTP_BWD_BUDGET", 168), one_group_limit = 200;
             groups.clear();
             std::vector<int> all_paths;
             for (int i = 0; i < (int)P.paths.size(); ++i) all_paths.push_back(i);
