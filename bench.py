@@ -696,10 +696,26 @@ def bench_tp(a, spec, device):
     wall = time.perf_counter() - t0
     fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) if backward else 0.0
+    # the same steps captured once in a HIP graph and replayed (the library allocates and
+    # synchronises nothing, so its launches can be captured): what a launch-bound caller gets
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(a.steps):
+            step()
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / a.steps
+    del graph
     paths = [plan.path(p) for p in range(plan.num_paths)]
     config = {"workload": spec.name, "B": B, "in_irreps": spec.in_irreps, "mode": spec.mode,
               "paths": plan.num_paths, "nnz": plan.nnz_total, "fwd_ms": fwd_ms,
-              "step": "tp_forward + tp_backward" if backward else "tp_forward"}
+              "step": "tp_forward + tp_backward" if backward else "tp_forward",
+              "graph_replay_ms_per_step": graph_ms, "graph_rows_per_s": B / (graph_ms * 1e-3)}
     if spec.mode == "uvw":
         flops = tp_flops(paths, None, spec.mode) * B
         peak = 157.3 if a.dtype == "f32" else 78.6
