@@ -541,7 +541,12 @@ void schedule(Plan &P)
         // NequIP-like graph: fewer launches and index loads, the g row read in
         // one pass); larger problems are split so that no group spills.
         auto make_groups = [&](bool dbl, std::vector<Group> &groups, int &waves) {
-            const int split_budget = getenv_int("CGTP_BWD_BUDGET", 168), one_group_limit = 200;
+            // split budget of the register estimate (measured on the MACE-like plan, first-order
+            // backward: fp32 at 140 gives six groups that need 232 VGPRs and no spill, 20.75 ms,
+            // against 256 VGPRs, a 128-byte spill and 21.8 ms at 168; fp64 at 140 took 56.8
+            // against 47.2 ms at 168).  The double backward's sender pass keeps 168.
+            const int split_budget = getenv_int("CGTP_BWD_BUDGET", dbl || P.dtype == CGTP_F64 ? 168 : 140);
+            const int one_group_limit = 200;
             groups.clear();
             std::vector<int> all_paths;
             for (int i = 0; i < (int)P.paths.size(); ++i) all_paths.push_back(i);
