@@ -324,15 +324,10 @@ cgtp_status cgtp_tp_forward(const cgtp_plan *plan, int64_t B, const void *x, con
         require_disjoint(out, B * P.d_out * es, "out", y, B * P.d_sh * es, "y");
         require_disjoint(out, B * P.d_out * es, "out", w, nw, "w");
         if (P.mode == CGTP_UVW) {
-            for (const cgtp::Irrep &o : P.out)
-                if (o.mul > 16)
-                    throw cgtp::Error(CGTP_ERR_UNSUPPORTED,
-                                      "uvw batched product: output multiplicities above 16 are not supported (one "
-                                      "MFMA tile of 16 output channels); the uvw convolution supports them");
             const auto &L = cgtp::module_for_current_device(P);
             long nrows = (long)B, nblocks = (long)((B + 15) / 16);
             void *args[] = {&x, &y, &w, &out, &nrows, &nblocks};
-            launch(L.tp_uvw, nblocks * (int64_t)P.uvw_groups.size(), args, stream);
+            launch(L.tp_uvw, nblocks * (int64_t)P.uvw_groups.size() * cgtp::uvw_out_tiles(P), args, stream);
             return;
         }
         const auto &L = cgtp::module_for_current_device(P);

@@ -1183,11 +1183,15 @@ void emit_uvw_group(Out &o, const Plan &P, int gi)
     Touch t = touched(P, g.paths);
     int chunks = 0;
     for (int pi : g.paths) chunks = std::max(chunks, (P.paths[pi].mul_in + 3) / 4);
+    // output multiplicities above 16 take one wave per 16-wide tile of output channels (wt);
+    // plans within one tile generate no tile index at all
+    const bool tiled = uvw_out_tiles(P) > 1;
     o("__device__ __forceinline__ void uvw_g", gi,
       "(long blk, int lane, const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, "
-      "T* __restrict__ out, long nrows)");
+      "T* __restrict__ out, long nrows", tiled ? ", int wt" : "", ")");
     o("{");
     o.ind++;
+    if (tiled) o("const int wcol = wt * 16 + (lane & 15);  // output channel of this lane's A operand");
     o("const long row = blk * 16 + (lane & 15);");
     o("const int usub = lane >> 4;");
     o("const bool live = row < nrows;");
@@ -1229,10 +1233,11 @@ void emit_uvw_group(Out &o, const Plan &P, int gi)
             // A operands: W_p[u][w] with u = 4c + lane/16, w = lane % 16 (zero outside the block)
             for (int c = 0; c < chunks; ++c) {
                 std::string u = "(" + std::to_string(4 * c) + " + usub)";
-                const bool wmask = 4 * c + 3 >= p.mul_in || p.mul_out < 16;
+                const bool wmask = 4 * c + 3 >= p.mul_in || p.mul_out < 16 || tiled;
+                const std::string wc = tiled ? "wcol" : "(lane & 15)";
                 if (wmask) {
-                    o("const bool wok", c, " = ", u, " < ", p.mul_in, " && (lane & 15) < ", p.mul_out, ";");
-                    o("const T wv", c, " = w[", p.w_off, " + (wok", c, " ? ", u, " * ", p.mul_out, " + (lane & 15) : 0)];");
+                    o("const bool wok", c, " = ", u, " < ", p.mul_in, " && ", wc, " < ", p.mul_out, ";");
+                    o("const T wv", c, " = w[", p.w_off, " + (wok", c, " ? ", u, " * ", p.mul_out, " + ", wc, " : 0)];");
                     o("const T wa", c, " = wok", c, " ? wv", c, " : (T)0;");
                 } else {
                     o("const T wa", c, " = w[", p.w_off, " + ", u, " * ", p.mul_out, " + (lane & 15)];");
@@ -1291,14 +1296,16 @@ void emit_uvw_group(Out &o, const Plan &P, int gi)
             o.ind++;
             // D row held in register v of this lane: 4 (lane / 16) + v for the fp32
             // instruction, lane / 16 + 4 v for the fp64 one
+            const std::string tile0 = tiled ? "wt * 16 + " : "";
             if (f64)
-                o("const int wo = usub + ", 4 * v, ";");
+                o("const int wo = ", tile0, "usub + ", 4 * v, ";");
             else
-                o("const int wo = 4 * usub + ", v, ";");
-            if (ir.mul < 16) o("if (wo < ", ir.mul, ") {");
+                o("const int wo = ", tile0, "4 * usub + ", v, ";");
+            const bool guard = ir.mul < 16 || tiled;
+            if (guard) o("if (wo < ", ir.mul, ") {");
             for (int k = 0; k < n_of(ir.l); ++k)
                 o("orow[", off, " + wo * ", n_of(ir.l), " + ", k, "] = a", q, "_", k, "[", v, "];");
-            if (ir.mul < 16) o("}");
+            if (guard) o("}");
             o.ind--;
             o("}");
         }
@@ -1332,11 +1339,21 @@ void emit_uvw_kernel(Out &o, const Plan &P)
     o.ind++;
     o("const long wave = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
     o("const int lane = threadIdx.x & 63;");
-    o("const int group = (int)(wave / nblocks);");
-    o("const long blk = wave - (long)group * nblocks;");
+    const int tiles = uvw_out_tiles(P);
+    if (tiles > 1) {
+        // waves are (group, output tile, block), block fastest
+        o("const long per_group = nblocks * ", tiles, ";");
+        o("const int group = (int)(wave / per_group);");
+        o("const long rest = wave - (long)group * per_group;");
+        o("const int wt = (int)(rest / nblocks);");
+        o("const long blk = rest - (long)wt * nblocks;");
+    } else {
+        o("const int group = (int)(wave / nblocks);");
+        o("const long blk = wave - (long)group * nblocks;");
+    }
     o("switch (group) {");
     for (int gi = 0; gi < (int)P.uvw_groups.size(); ++gi)
-        o("case ", gi, ": uvw_g", gi, "(blk, lane, x, y, w, out, nrows); break;");
+        o("case ", gi, ": uvw_g", gi, "(blk, lane, x, y, w, out, nrows", tiles > 1 ? ", wt" : "", "); break;");
     o("default: break;");
     o("}");
     o.ind--;
@@ -2357,6 +2374,13 @@ int conv_uvw_g_items(const Plan &P, std::vector<std::pair<int, int>> *items) { r
 
 // receiver rows may be split over several waves only when one wave covers the whole receiver
 bool fwd_splittable(const Plan &P) { return P.fwd_tasks == 1 && P.fwd_groups.size() == 1; }
+
+int uvw_out_tiles(const Plan &P)
+{
+    int m = 1;
+    for (const Irrep &o : P.out) m = std::max(m, o.mul);
+    return (m + 15) / 16;
+}
 
 int fwd_group_accs(const Plan &P, int gi)
 {

@@ -169,6 +169,8 @@ int64_t conv_uvw_g_width(const Plan &plan);
 int fwd_group_accs(const Plan &plan, int gi);
 // whether the receiver-owned passes may split a receiver row over several waves
 bool fwd_splittable(const Plan &plan);
+// batched uvw forward: 16-wide tiles of output channels (one wave per tile and 16-row block)
+int uvw_out_tiles(const Plan &plan);
 int conv_uvw_g_items(const Plan &plan, std::vector<std::pair<int, int>> *items);
 
 }  // namespace cgtp

@@ -137,9 +137,8 @@ cgtp_status cgtp_conv_row_split(const cgtp_plan *plan, int64_t N, int64_t E, int
  *                                   sum_{i,j} C[i,j,k] x[b, a + u(2l1+1) + i] y[b, b_p + j]
  *        w is [B][weight_numel], shared_weights must be 0;
  *   uvw: out[b, o + v(2l3+1) + k] = sum_paths sum_u W_p[u][v] * (same contraction)
- *        w is the shared [weight_numel] block, shared_weights must be 1; every
- *        output multiplicity must be <= 16 (one MFMA tile), else
- *        CGTP_ERR_UNSUPPORTED.
+ *        w is the shared [weight_numel] block, shared_weights must be 1; output
+ *        multiplicities above 16 run as 16-wide tiles of output channels.
  * x [B][d_x], y [B][d_sh], out [B][d_out] (overwritten).  B = 0 is a no-op.
  */
 cgtp_status cgtp_tp_forward(const cgtp_plan *plan, int64_t B, const void *x, const void *y,

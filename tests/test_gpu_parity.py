@@ -263,6 +263,9 @@ def _uvw_case(in_irreps, lmax, out_irreps, B, dtype, seed=13):
     (synth.TP_HIGHL.in_irreps, 7, synth.TP_HIGHL.out_irreps, 333),
     ("3x0e+5x1o+2x2e", 2, "4x0e+7x1o+3x2e+2x1e+16x2o", 77),
     ("16x0e+16x1o", 1, "16x0e+16x1o+16x1e", 1),
+    # output multiplicities above 16: 16-wide output tiles, ragged last tile, mixed tile counts
+    ("20x0e+5x1o", 1, "33x0e+17x1o+3x1e", 77),
+    ("8x0e+8x1o+8x2e", 2, "32x0e+32x1o+32x2e", 300),
 ])
 def test_tp_forward_uvw(device, dtype, in_irreps, lmax, out_irreps, B):
     import torch
