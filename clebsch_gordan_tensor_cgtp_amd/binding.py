@@ -277,9 +277,14 @@ def tp_backward(plan: Plan, x, y, w, grad_out, grad_x=None, grad_y=None, grad_w=
     shapes = ((B, plan.d_x), (B, plan.d_sh), wshape)
     res = [None if not nd else (torch.empty(sh, dtype=dt, device=dev) if o is None else o)
            for o, nd, sh in zip((grad_x, grad_y, grad_w), need, shapes)]
-    nbytes = tp_backward_workspace_size(plan, B) if res[2] is not None else 0
+    # uvw with every multiplicity <= 16 needs the workspace for grad_w only; wider uvw plans run
+    # the convolution backward on the identity graph, which needs it for every gradient
+    wide = shared and any(max(plan.path(p)["mul_in"], plan.path(p)["mul_out"]) > 16 for p in range(plan.num_paths))
+    wanted = res[2] is not None or (wide and any(r is not None for r in res))
+    nbytes = tp_backward_workspace_size(plan, B) if wanted else 0
     if workspace is None and nbytes:
-        workspace = torch.empty(nbytes // (4 if plan.dtype == "f32" else 8), dtype=dt, device=dev)
+        es = 4 if plan.dtype == "f32" else 8
+        workspace = torch.empty(-(-nbytes // es), dtype=dt, device=dev)
     ws = ctypes.c_void_p(0) if workspace is None else ctypes.c_void_p(workspace.data_ptr())
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().cgtp_tp_backward(plan.handle, B, _dev(x, "x", dt, shapes[0]), _dev(y, "y", dt, shapes[1]),

@@ -357,6 +357,14 @@ static void uvb_chunks(int64_t B, long &nblocks, long &bpc, long &nchunks)
     nchunks = nchunks > 0 ? (nblocks + bpc - 1) / bpc : 0;
 }
 
+// uvw batched backward with a multiplicity above 16: the uvw convolution backward on the identity
+// graph (row b is the edge from sender b to receiver b), whose one index array 0, 1, ..., B sits
+// in the workspace after the convolution's own part (padded to 256 bytes)
+static size_t identity_conv_part(const cgtp::Plan &P, int64_t B)
+{
+    return (conv_uvw_workspace(P, B, nullptr) + 255) / 256 * 256;
+}
+
 cgtp_status cgtp_tp_backward_workspace_size(const cgtp_plan *plan, int64_t B, size_t *bytes)
 {
     return guarded([&] {
@@ -364,7 +372,9 @@ cgtp_status cgtp_tp_backward_workspace_size(const cgtp_plan *plan, int64_t B, si
         const cgtp::Plan &P = plan->p;
         require(B >= 0 && B < INT_MAX, "B must be in [0, 2^31-1)");
         *bytes = 0;
-        if (P.mode == CGTP_UVW) {
+        if (P.mode == CGTP_UVW && !P.uvb_ok) {
+            *bytes = identity_conv_part(P, B) + (size_t)(B + 1) * 4;
+        } else if (P.mode == CGTP_UVW) {
             long nblocks, bpc, nchunks;
             uvb_chunks(B, nblocks, bpc, nchunks);
             *bytes = (size_t)nchunks * P.w_numel * elem(P);
@@ -385,9 +395,18 @@ cgtp_status cgtp_tp_backward(const cgtp_plan *plan, int64_t B, const void *x, co
             require(shared_weights == 0, "uvu takes per-row weights: shared_weights must be 0");
         else
             require(shared_weights == 1, "uvw takes shared weights: shared_weights must be 1");
-        if (uvw && !P.uvb_ok)
-            throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw batched backward: every multiplicity must be <= 16");
         if (!grad_x && !grad_y && !grad_w) return;
+        if (uvw && !P.uvb_ok) {
+            const size_t part = identity_conv_part(P, B), need = part + (size_t)(B + 1) * 4;
+            require_ptr(workspace, "workspace", 256);
+            require(workspace_bytes >= need, "workspace too small (see cgtp_tp_backward_workspace_size)");
+            int32_t *ids = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + part);
+            check_hip(cgtp::launch_iota(B + 1, ids, static_cast<hipStream_t>(stream)), "iota launch");
+            const cgtp_status st = cgtp_conv_backward_ws(plan, B, B, ids, ids, nullptr, ids, ids, ids, x, y, w,
+                                                         grad_out, grad_x, grad_y, grad_w, workspace, part, stream);
+            if (st != CGTP_OK) throw cgtp::Error(st, g_last_error);
+            return;
+        }
         const size_t es = elem(P);
         if (B == 0) {
             if (uvw && grad_w) {

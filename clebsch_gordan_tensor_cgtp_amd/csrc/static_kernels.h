@@ -11,5 +11,7 @@ hipError_t launch_spherical_harmonics(int lmax, bool f64, int64_t E, const void 
 hipError_t launch_degree_order(int64_t N, const int32_t *row_ptr, int32_t *order, hipStream_t st);
 hipError_t launch_transpose(int64_t N, int64_t E, const int32_t *row_ptr, const int32_t *col, int32_t *t_row_ptr,
                             int32_t *t_edge, int32_t *t_dst, hipStream_t st);
+// a[i] = i for i < n
+hipError_t launch_iota(int64_t n, int32_t *a, hipStream_t st);
 
 }  // namespace cgtp

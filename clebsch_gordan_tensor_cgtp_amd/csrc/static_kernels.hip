@@ -115,6 +115,12 @@ __global__ void __launch_bounds__(256) fill_zero(int32_t *a, int64_t n)
     if (i < n) a[i] = 0;
 }
 
+__global__ void __launch_bounds__(256) iota(int32_t *a, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) a[i] = (int32_t)i;
+}
+
 // count(s) lands at index s + 2 so that the inclusive scan leaves start(s) at s + 1
 __global__ void __launch_bounds__(256) count_senders(const int32_t *__restrict__ col, int64_t E, int64_t N,
                                                      int32_t *t_row_ptr)
@@ -293,6 +299,12 @@ hipError_t launch_transpose(int64_t N, int64_t E, const int32_t *row_ptr, const 
         if (N > 0) hipLaunchKernelGGL(sort_segments, blocks(N), dim3(256), 0, st, t_row_ptr, N, t_edge);
         hipLaunchKernelGGL(edge_receivers, blocks(E), dim3(256), 0, st, row_ptr, N, t_edge, E, t_dst);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_iota(int64_t n, int32_t *a, hipStream_t st)
+{
+    if (n > 0) hipLaunchKernelGGL(iota, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a, n);
     return hipGetLastError();
 }
 

@@ -151,14 +151,17 @@ cgtp_status cgtp_tp_forward(const cgtp_plan *plan, int64_t B, const void *x, con
  *     grad_w[b, w_p + u] = sum_{ijk} C x[b,u,i] y[b,j] g[b,u,k]
  *     grad_y[b, b_p + j] = sum_p sum_u W[b,p,u] sum_{ik} C x[b,u,i] g[b,u,k]
  *     grad_x[b, a_p + u(2l1+1) + i] = sum_p W[b,p,u] sum_{jk} C y[b,j] g[b,u,k]
- *   uvw (shared_weights = 1, every mul_in and mul_out <= 16, else
- *   CGTP_ERR_UNSUPPORTED), with G_p[b,u,k] = sum_w W_p[u][w] g[b, o_p + w(2l3+1) + k]:
+ *   uvw (shared_weights = 1), with G_p[b,u,k] = sum_w W_p[u][w] g[b, o_p + w(2l3+1) + k]:
  *     grad_x[b, a_p + u(2l1+1) + i] = sum_p sum_{jk} C y[b,j] G_p[b,u,k]
  *     grad_y[b, b_p + j] = sum_p sum_u sum_{ik} C x[b,u,i] G_p[b,u,k]
  *     grad_w[w_p + u*mul_out + w] = sum_b sum_{ijk} C x[b,u,i] y[b,j] g[b, o_p + w(2l3+1) + k]
  *   The shared-weight gradient sums over all rows: per-chunk partials go to
  *   the caller's `workspace` (workspace_bytes >= cgtp_tp_backward_workspace_size;
  *   0 for uvu, where workspace may be NULL) and are summed in chunk order.
+ *   A uvw plan with a multiplicity above 16 runs the uvw convolution backward
+ *   (cgtp_conv_backward_ws) on the identity graph, row b being the edge from
+ *   sender b to receiver b; its workspace (256-byte aligned) then holds that
+ *   call's workspace and the index array 0..B, and is needed for every gradient.
  * Any of grad_x / grad_y / grad_w may be NULL to skip it; outputs are
  * overwritten, one owner per element, no atomics, bitwise deterministic.
  * B = 0 writes nothing, except that a uvw grad_w is set to zero.

@@ -186,7 +186,13 @@ def test_call_errors_before_any_gpu_work():
     assert L.cgtp_tp_backward_workspace_size(plan.handle, 50_000, ctypes.byref(nb)) == 0 and nb.value == 0
     assert L.cgtp_tp_backward(uvw.handle, 4, fake, fake, fake, 1, ctypes.c_void_p(1 << 26), null, null,
                               ctypes.c_void_p(1 << 28), null, z, s) == inval
-    assert L.cgtp_tp_backward(wide, 4, fake, fake, fake, 1, fake, fake, fake, fake, null, z, s) == unsup
+    # wider plans run the convolution backward on the identity graph: the workspace holds its part
+    # (16x0e -> 32x0e, l = 0: G 4 x 16 floats padded to 256 bytes, one 512-weight dW partial) and
+    # the index array 0..B, and is needed for every gradient
+    assert L.cgtp_tp_backward_workspace_size(wide, 4, ctypes.byref(nb)) == 0 and nb.value == 256 + 2048 + 20
+    assert L.cgtp_tp_backward(wide, 4, fake, fake, fake, 1, fake, fake, fake, fake, null, z, s) == inval
+    assert L.cgtp_tp_backward(wide, 4, fake, fake, fake, 1, fake, fake, null, null, ctypes.c_void_p(1 << 28),
+                              ctypes.c_size_t(256 + 2048 + 19), s) == inval
     assert L.cgtp_plan_destroy(wide) == 0
     assert L.cgtp_tp_forward(plan.handle, 4, fake, fake, fake, 1, fake, s) == inval   # uvu needs shared=0
     assert L.cgtp_tp_forward(uvw.handle, 4, fake, fake, fake, 0, fake, s) == inval    # uvw needs shared=1

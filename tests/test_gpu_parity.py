@@ -304,7 +304,11 @@ UVB_CASES = [
     ("5x0e+3x1o+7x2e+2x3o", 3, "6x0e+4x1o+3x2e+2x1e+1x3o+9x2o", 301, ("f32",)),
     ("+".join(f"16x{l}{'e' if l % 2 == 0 else 'o'}" for l in range(6)), 5,
      "+".join(f"16x{l}{'e' if l % 2 == 0 else 'o'}" for l in range(6)), 200, ("f32",)),
+    # multiplicities above 16: the convolution backward on the identity graph
+    ("20x0e+5x1o", 1, "33x0e+17x1o+3x1e", 77, ("f32", "f64")),
+    ("32x0e+32x1o", 1, "32x0e+32x1o+32x1e", 300, ("f32",)),
 ]
+WIDE = UVB_CASES[-2]
 
 
 def _uvb_run(device, ins, lmax, outs, B, dtype, seed=61, need=(True, True, True)):
@@ -333,6 +337,25 @@ def test_tp_backward_uvw(device, ins, lmax, outs, B, dtype):
     assert rel_l2(gx.cpu().numpy(), dx) <= TOL[dtype]
     assert rel_l2(gy.cpu().numpy(), dy) <= TOL[dtype]
     assert rel_l2(gw.cpu().numpy(), dw) <= TOL[dtype]
+
+
+def test_tp_backward_uvw_wide_subsets_and_empty_batch(device):
+    """Multiplicities above 16: each gradient alone gives the bits of the full call, and an empty
+    batch gives a zero weight gradient."""
+    import torch
+    ins, lmax, outs, B, _ = WIDE
+    full = _uvb_run(device, ins, lmax, outs, B, "f32")[-1]
+    for k in range(3):
+        need = tuple(j == k for j in range(3))
+        part = _uvb_run(device, ins, lmax, outs, B, "f32", need=need)[-1]
+        assert torch.equal(part[k], full[k])
+    plan = cg.plan_create(ins, oirreps.sh_irreps(lmax), outs, "uvw", "f32")
+    e = lambda *sh: torch.empty(sh, device=device)
+    gw = torch.full((plan.weight_numel,), float("nan"), device=device)
+    cg.tp_backward(plan, e(0, plan.d_x), e(0, plan.d_sh), e(plan.weight_numel), e(0, plan.d_out),
+                   grad_w=gw, need=(False, False, True))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(gw).item() == 0
 
 
 def test_tp_backward_uvw_outputs_and_repeat_bitwise(device):
