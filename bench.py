@@ -1,7 +1,12 @@
 """Benchmark of the fused CGTP convolution on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c5] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5|c2|c3|...] [--no-cpu]
                     [--double-backward]
+
+The default workload is the largest single-GPU convolution: the power-law graph
+with 200,000 nodes and 10,000,000 edges, 64x(0e,1o,2e) features, SH l <= 2,
+fp32, forward + backward with no edge-sized intermediates (Sobek page,
+Abstract: the edge-scaling regime).
 
 One step = one pass of the hot path over the synthetic graph: the fused
 convolution forward (cgtp_conv_forward_ordered, heavy-first receiver schedule)
@@ -33,7 +38,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c2uvw", "c1big"])
+    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "c2uvw", "c1big"])
     ap.add_argument("--backward", action="store_true",
                     help="batched workloads: also time cgtp_tp_backward; uvw convolution: also cgtp_conv_backward_ws")
     ap.add_argument("--dtype", default="f32", choices=["f32", "f64"])
@@ -671,8 +676,13 @@ def bench_tp(a, spec, device):
     grads = (torch.empty_like(x), torch.empty_like(y), torch.empty_like(w)) if backward else None
     ws = None
     if backward and spec.mode == "uvw":
-        plan.uvw_backward_source()  # JIT outside the timed region
-        ws = torch.empty(cg.tp_backward_workspace_size(plan, B) // es, dtype=plan.torch_dtype, device=device)
+        # JIT outside the timed region: plans with a multiplicity above 16 run the uvw convolution
+        # backward on the identity graph, the others the batched backward's own module
+        if plan.wide_uvw:
+            plan.conv_uvw_backward_source(0)
+        else:
+            plan.uvw_backward_source()
+        ws = torch.empty(-(-cg.tp_backward_workspace_size(plan, B) // es), dtype=plan.torch_dtype, device=device)
 
     def step(ev=None):
         if ev is not None:

@@ -125,6 +125,15 @@ class Plan:
         return self._h
 
     @property
+    def wide_uvw(self) -> bool:
+        """A uvw plan with a multiplicity above 16: its batched backward runs the uvw convolution
+        backward on the identity graph (computed once per plan)."""
+        if not hasattr(self, "_wide_uvw"):
+            self._wide_uvw = self.mode == "uvw" and any(
+                max(self.path(p)["mul_in"], self.path(p)["mul_out"]) > 16 for p in range(self.num_paths))
+        return self._wide_uvw
+
+    @property
     def torch_dtype(self):
         import torch
         return torch.float32 if self.dtype == "f32" else torch.float64
@@ -279,7 +288,7 @@ def tp_backward(plan: Plan, x, y, w, grad_out, grad_x=None, grad_y=None, grad_w=
            for o, nd, sh in zip((grad_x, grad_y, grad_w), need, shapes)]
     # uvw with every multiplicity <= 16 needs the workspace for grad_w only; wider uvw plans run
     # the convolution backward on the identity graph, which needs it for every gradient
-    wide = shared and any(max(plan.path(p)["mul_in"], plan.path(p)["mul_out"]) > 16 for p in range(plan.num_paths))
+    wide = plan.wide_uvw
     wanted = res[2] is not None or (wide and any(r is not None for r in res))
     nbytes = tp_backward_workspace_size(plan, B) if wanted else 0
     if workspace is None and nbytes:

@@ -395,6 +395,9 @@ cgtp_status cgtp_tp_backward(const cgtp_plan *plan, int64_t B, const void *x, co
             require(shared_weights == 0, "uvu takes per-row weights: shared_weights must be 0");
         else
             require(shared_weights == 1, "uvw takes shared weights: shared_weights must be 1");
+        if (uvw && !P.uvb_ok && !P.uvc_ok)
+            throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw batched backward with a multiplicity above 16 runs the uvw "
+                                                    "convolution backward, which this plan cannot: " + P.uvc_why);
         if (!grad_x && !grad_y && !grad_w) return;
         if (uvw && !P.uvb_ok) {
             const size_t part = identity_conv_part(P, B), need = part + (size_t)(B + 1) * 4;
@@ -488,8 +491,9 @@ cgtp_status cgtp_conv_forward_ordered(const cgtp_plan *plan, int64_t N, int64_t 
         require(plan != nullptr, "plan is NULL");
         cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
         check_graph_sizes(N, E);
-        if (N == 0) return;
         const bool uvw = P.mode == CGTP_UVW;
+        if (uvw && !P.uvc_ok) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, P.uvc_why);
+        if (N == 0) return;
         const size_t es = elem(P);
         require_ptr(row_ptr, "row_ptr", 4);
         require_ptr(out, "out", es);
@@ -797,6 +801,7 @@ cgtp_status cgtp_conv_backward_ws(const cgtp_plan *plan, int64_t N, int64_t E, c
             if (st != CGTP_OK) throw cgtp::Error(st, g_last_error);
             return;
         }
+        if (!P.uvc_ok) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, P.uvc_why);
         if (!grad_x && !grad_y && !grad_w) return;
         const size_t es = elem(P);
         if (grad_w) require_ptr(grad_w, "grad_w", es);
@@ -871,6 +876,7 @@ cgtp_status cgtp_plan_conv_uvw_backward_prepare(const cgtp_plan *plan)
         require(plan != nullptr, "plan is NULL");
         cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
         if (P.mode != CGTP_UVW) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "uvw convolution backward: uvw plans only");
+        if (!P.uvc_ok) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, P.uvc_why);
         cgtp::prepare_conv_uvw_backward(P);
     });
 }

@@ -86,7 +86,14 @@ struct Rtc {
     decltype(&hiprtcGetErrorString) error_string = hiprtcGetErrorString;
     decltype(&hiprtcVersion) version = hiprtcVersion;
     std::string identity;  // which library compiles, for the cache key
+    // The C library of the private link namespace keeps its own `environ`, copied when the
+    // namespace was created.  A later setenv/putenv in the process may move the environment
+    // array and free the old one, leaving that copy dangling (hipRTC reads the environment):
+    // it is pointed at the process's current array before every call into hipRTC.
+    char ***ns_environ = nullptr;
 };
+
+extern "C" char **environ;
 
 static std::string real_path_of(void *sym)
 {
@@ -127,10 +134,15 @@ static const Rtc &rtc()
         get(y.destroy, "hiprtcDestroyProgram");
         get(y.error_string, "hiprtcGetErrorString");
         get(y.version, "hiprtcVersion");
-        if (ok)
+        if (ok) {
+            Lmid_t lmid;
+            if (::dlinfo(h, RTLD_DI_LMID, &lmid) == 0)
+                if (void *libc = ::dlmopen(lmid, "libc.so.6", RTLD_NOW | RTLD_NOLOAD))
+                    y.ns_environ = static_cast<char ***>(::dlsym(libc, "environ"));
             x = y;
-        else if (h)
+        } else if (h) {
             ::dlclose(h);
+        }
         x.identity = real_path_of(reinterpret_cast<void *>(x.create));
         int major = 0, minor = 0;
         x.version(&major, &minor);
@@ -159,6 +171,7 @@ std::vector<char> compile_source(const std::string &source)
     if (read_file(path, code)) return code;
 
     hiprtcProgram prog;
+    if (R.ns_environ && R.ns_environ != &environ) *R.ns_environ = environ;
     if (R.create(&prog, source.c_str(), "cgtp_module.hip", 0, nullptr, nullptr) != HIPRTC_SUCCESS)
         throw Error(CGTP_ERR_COMPILE, "hiprtcCreateProgram failed");
     hiprtcResult rc = R.compile(prog, (int)(sizeof kOptions / sizeof kOptions[0]), kOptions);

@@ -69,6 +69,8 @@ struct Plan {
     std::vector<Group> uvb_x_groups;  // uvw batched backward, dx/dy: one input block per group (launched in order)
     std::vector<Group> uvb_w_groups;  // uvw batched backward, dW partials: up to 16 paths per group
     bool uvb_ok = false;            // uvw batched backward supported (every mul_in, mul_out <= 16)
+    bool uvc_ok = false;            // uvw convolution supported (every path group's T staging fits LDS)
+    std::string uvc_why;            // why not, when uvc_ok is false
     bool unit_weights = false;      // internal plans: every weight is 1 (not read), only the sender pass
     int fwd_waves_per_eu = 4;       // occupancy target given to the compiler (min waves per SIMD)
     int bwd_waves_per_eu = 4;

@@ -503,6 +503,25 @@ void schedule(Plan &P)
             std::vector<Group> wide;
             if (make(122880, wide) == 1) P.uvc_groups = wide;
         }
+        // A group is split only between paths, so one path whose staging alone exceeds the
+        // workgroup's LDS (e.g. 128x7o in fp64) cannot run: such plans keep the batched product
+        // but the convolution kernels are not generated and their entry points report it.
+        const long lds_cap = 160L * 1024;  // LDS of one gfx950 workgroup
+        P.uvc_ok = true;
+        for (const Group &g : P.uvc_groups) {
+            long bytes = 0;
+            for (int pi : g.paths) {
+                const Path &p = P.paths[pi];
+                bytes += 16L * ((p.mul_in + 3) / 4 * 4) * (2 * p.l3 + 1) * 4 * word;
+            }
+            if (bytes > lds_cap && P.uvc_ok) {
+                P.uvc_ok = false;
+                P.uvc_why = "uvw convolution: path " + std::to_string(g.paths.front()) + " stages " +
+                            std::to_string(bytes) + " bytes of T for a 16-receiver tile, more than the " +
+                            std::to_string(lds_cap) + " bytes of LDS of one workgroup";
+            }
+        }
+        if (!P.uvc_ok) P.uvc_groups.clear();
     }
 
     // uvw batched backward: dx/dy groups are the input blocks (each block's dx is complete in one

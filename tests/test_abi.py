@@ -273,3 +273,52 @@ def test_compiled_code_does_not_depend_on_what_the_process_loaded_first(tmp_path
     b = sorted(p.name for p in dirs[1].iterdir() if p.suffix == ".hsaco")
     assert a == b and len(a) == 1
     assert (dirs[0] / a[0]).read_bytes() == (dirs[1] / b[0]).read_bytes()
+
+
+@pytest.mark.parametrize("irreps,dtype", [("128x7o", "f64"), ("256x7o", "f32")])
+def test_uvw_convolution_rejects_paths_beyond_workgroup_lds(irreps, dtype, tmp_path, monkeypatch):
+    """A uvw path whose T staging for one 16-receiver tile (16 x mul_in x (2 l3 + 1) elements)
+    exceeds the 160 KB of LDS of one workgroup cannot be split further: the plan still builds (the
+    batched forward tiles its output channels), while the convolution entry points return
+    CGTP_ERR_UNSUPPORTED with the reason before any GPU call."""
+    monkeypatch.setenv("CGTP_CACHE_DIR", str(tmp_path))
+    plan = cg.plan_create(irreps, "1x0e", irreps, "uvw", dtype)
+    L = cg.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    null = ctypes.c_void_p(0)
+    s = ctypes.c_void_p(0)
+    unsup = cg.STATUS_CODES["CGTP_ERR_UNSUPPORTED"]
+    assert L.cgtp_conv_forward(plan.handle, 4, 4, fake, fake, fake, fake, fake, fake, s) == unsup
+    assert "LDS" in cg.last_error()
+    assert L.cgtp_conv_backward_ws(plan.handle, 4, 4, fake, fake, null, fake, fake, fake, fake, fake, fake, fake,
+                                   fake, fake, fake, fake, ctypes.c_size_t(1 << 30), s) == unsup
+    assert L.cgtp_tp_backward(plan.handle, 4, fake, fake, fake, 1, fake, fake, fake, fake, fake,
+                              ctypes.c_size_t(1 << 30), s) == unsup
+    with pytest.raises(cg.CgtpError, match="CGTP_ERR_UNSUPPORTED"):
+        plan.conv_uvw_backward_source(0)
+    plan.close()
+
+
+def test_compile_after_the_environment_moved(tmp_path):
+    """hipRTC runs in a link namespace of its own, whose C library keeps its own pointer to the
+    environment.  A process that changes its environment after the first plan (here: enough new
+    variables to move the environment array) must still compile the next module."""
+    import subprocess
+    import sys
+    # the environment is moved once before the first plan (so the namespace copies a heap array)
+    # and many times after it (freeing that array); the freed memory is then overwritten
+    prog = ("import os, sys\n"
+            "from clebsch_gordan_tensor_cgtp_amd import binding as cg\n"
+            "for i in range(300): os.environ[f'CGTP_TEST_PRE_{i}'] = 'x'\n"
+            "cg.Plan('2x0e', '1x0e', '2x0e', 'uvu', 'f32')\n"
+            "for i in range(3000): os.environ[f'CGTP_TEST_PAD_{i}'] = 'x' * 64\n"
+            "junk = [bytearray(b'\\xff' * n) for n in range(1024, 65536, 512) for _ in range(4)]\n"
+            "os.environ['CGTP_CACHE_DIR'] = sys.argv[1]\n"
+            "p = cg.Plan('3x1o', '1x0e+1x1o', '3x1o+3x0e+3x1e+3x2e', 'uvu', 'f32')\n"
+            "print(p.num_paths)\n")
+    env = dict(os.environ, CGTP_CACHE_DIR=str(tmp_path / "first"), PYTHONPATH=ROOT)
+    r = subprocess.run([sys.executable, "-c", prog, str(tmp_path / "second")], env=env, cwd=ROOT, timeout=600,
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip() == "4"
+    assert any(p.suffix == ".hsaco" for p in (tmp_path / "second").iterdir())
