@@ -109,8 +109,29 @@ typedef struct cgtp_path_info {
  */
 cgtp_status cgtp_plan_create(const char *in_irreps, const char *sh_irreps, const char *out_irreps,
                              cgtp_mode mode, cgtp_dtype dtype, cgtp_plan **plan_out);
+/*
+ * Release a plan and the code objects it loaded on any device.  Not on the
+ * pages: every object that cgtp_plan_create hands out needs an owner-side
+ * release, and the only device resources a plan holds are its loaded modules
+ * (the OpenEquivariance discussion's rule that the library keeps no device
+ * buffers of its own).  The caller must not use the plan afterwards, and must
+ * first let every kernel launched with it finish (synchronise the streams it
+ * used): the code those kernels run is unloaded here.  NULL is accepted and
+ * ignored.  Unloading errors are not reported; always returns CGTP_OK.
+ */
 cgtp_status cgtp_plan_destroy(cgtp_plan *plan);
+/*
+ * Plan bookkeeping for sizing caller-owned buffers: widths d_x, d_sh, d_out,
+ * path count, weight count, CG nonzeros (sciencestack.ai page, Figure 1: the
+ * dense operands x, y, the output and the structured weight W whose sizes
+ * follow from the irreps; Figure 2: the sparse blocks).  The name carries
+ * `_get` because the C struct cgtp_plan_info already owns the plain name.
+ * Host only.  Errors: CGTP_ERR_INVALID_ARG (NULL).
+ */
 cgtp_status cgtp_plan_info_get(const cgtp_plan *plan, cgtp_plan_info *info);
+/* One path of the plan (input irrep, SH irrep, output block, degrees, offsets, nonzeros;
+ * sciencestack.ai page, Figure 1: one sparse block per coupling path).  Host only.
+ * Errors: CGTP_ERR_INVALID_ARG (NULL, path out of range). */
 cgtp_status cgtp_plan_path(const cgtp_plan *plan, int32_t path, cgtp_path_info *info);
 /* Copies up to `cap` nonzeros of one path's real CG block: ijk[3*n] (i, j, k)
  * and values[n] as float64.  *nnz receives the full count. */
@@ -258,17 +279,29 @@ cgtp_status cgtp_conv_backward_radial(const cgtp_plan *plan, int64_t N, int64_t 
                                       void *stream);
 
 /*
- * Heavy-first receiver schedule, once per graph: order [N] (caller-owned)
- * receives the receivers stably sorted by floor(log2(in-degree + 1)),
- * largest first (ties keep node order).  Integer result, deterministic.
+ * Heavy-first receiver schedule, once per graph (LunaTP page, Abstract:
+ * node-centric execution; here it orders which receivers the node-owned
+ * waves start first, so that the heaviest nodes of a power-law graph do not
+ * finish last).  order [N] (caller-owned) receives the receivers stably sorted
+ * by floor(log2(in-degree + 1)), largest first (ties keep node order).
+ * row_ptr as in cgtp_conv_forward.  Integer result, deterministic, enqueued on
+ * `stream`.  N = 0 is a no-op.  Errors: CGTP_ERR_INVALID_ARG (NULL,
+ * misaligned, N out of range), CGTP_ERR_HIP (launch).
  */
 cgtp_status cgtp_graph_order(int64_t N, const int32_t *row_ptr, int32_t *order, void *stream);
 
 /*
- * Sender-sorted transpose of a receiver CSR, once per graph: t_row_ptr [N+1],
- * t_edge [E] (edge ids grouped by sender, ascending edge id inside a sender:
- * a stable sort by col) and t_dst [E] (receiver of t_edge[t]).  Integer
- * results, bit-exact and deterministic.  All outputs caller-owned.
+ * Sender-sorted transpose of a receiver CSR, once per graph.  It is what
+ * makes the backward deterministic without atomics or input-sized scratch:
+ * the OpenEquivariance discussion contrasts an atomic fused convolution with a
+ * deterministic one that needs scratch space; here the gradient of each sender
+ * row has one owner that walks its edges through this index (Sobek page,
+ * Abstract: adjoints without edge-sized intermediates).  Outputs:
+ * t_row_ptr [N+1], t_edge [E] (edge ids grouped by sender, ascending edge id
+ * inside a sender: a stable sort by col) and t_dst [E] (receiver of
+ * t_edge[t]).  Integer results, bit-exact and deterministic, enqueued on
+ * `stream`.  All outputs caller-owned, disjoint from the inputs.  Errors:
+ * CGTP_ERR_INVALID_ARG (NULL, misaligned, N or E out of range), CGTP_ERR_HIP.
  */
 cgtp_status cgtp_graph_transpose(int64_t N, int64_t E, const int32_t *row_ptr, const int32_t *col,
                                  int32_t *t_row_ptr, int32_t *t_edge, int32_t *t_dst, void *stream);
@@ -367,7 +400,13 @@ cgtp_status cgtp_conv_double_backward(const cgtp_plan *plan, int64_t N, int64_t 
 cgtp_status cgtp_spherical_harmonics(int32_t lmax, cgtp_dtype dtype, int64_t E, const void *vec,
                                      void *y, void *stream);
 
-/* Message of the last failed call on this thread ("" if none). */
+/*
+ * Message of the last failed call on this thread ("" if none).  Not on the
+ * pages: a C ABI cannot carry exceptions, so every entry point returns a
+ * status and leaves its reason here (for CGTP_ERR_COMPILE, the hipRTC log).
+ * The string is owned by the library and valid until the next failing call on
+ * the same thread.
+ */
 const char *cgtp_last_error(void);
 
 #ifdef __cplusplus

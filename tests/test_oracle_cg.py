@@ -123,6 +123,29 @@ def test_sh_coupling_gaunt():
     assert np.allclose(np.einsum("ijk,ni,nj->nk", c, v, v), np.sqrt(3.0), atol=1e-13)
 
 
+# Signed coupling constants c of sum_ij C_ijk Y_l1,i(r) Y_l2,j(r) = c Y_l3,k(r) under the real basis
+# and first-nonzero-positive sign rule (values to 12 decimals; e.g. (1,1,2) = -sqrt(6)/5,
+# (2,2,2) = -sqrt(2/7), (1,2,3) = -3/7, (7,7,0) = sqrt(15)).  A sign error in the basis change or
+# the sign rule of either the CG block or the harmonics flips one of these.
+GAUNT_SIGNED = {
+    (1, 1, 0): 1.732050807569, (1, 1, 2): -0.489897948557, (2, 2, 0): 2.236067977500,
+    (2, 2, 2): -0.534522483825, (1, 2, 1): 0.816496580928, (1, 2, 3): -0.428571428571,
+    (2, 2, 4): 0.398409536445, (3, 3, 2): -0.611010092661, (7, 7, 0): 3.872983346207,
+}
+
+
+@pytest.mark.parametrize("triple", sorted(GAUNT_SIGNED))
+def test_sh_coupling_signed_constants(triple):
+    """G3 with signs: the coupling constant itself, not only its magnitude."""
+    l1, l2, l3 = triple
+    pts = np.random.default_rng(11).standard_normal((40, 3))
+    lhs = np.einsum("ijk,ni,nj->nk", cg.real_cg_block(l1, l2, l3), sh.real_sh(l1, pts), sh.real_sh(l2, pts))
+    y3 = sh.real_sh(l3, pts)
+    coef = float(np.sum(lhs * y3) / np.sum(y3 * y3))
+    assert np.abs(lhs - coef * y3).max() < 1e-11
+    assert abs(coef - GAUNT_SIGNED[triple]) < 1e-11
+
+
 def test_swap_symmetry():
     """G4: C^{l2 l1 l3}[j,i,k] = +-C^{l1 l2 l3}[i,j,k]."""
     for l1, l2, l3 in triples(6):
