@@ -31,6 +31,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "edges/sec fused CGTP conv fwd (+bwd) and % of HBM / FP32 roofline"
 HBM_PEAK_GBS = 8000.0
+# workspace of the receiver-order backward: a fixed bound, independent of the edge count (the edges
+# are taken in ranges of as many dx rows as it holds)
+RECEIVER_WORKSPACE_BYTES = 4 << 30
 
 
 def parse():
@@ -44,6 +47,9 @@ def parse():
     ap.add_argument("--dtype", default="f32", choices=["f32", "f64"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--backward-schedule", default="sender", choices=["receiver", "sender"],
+                    help="uvu convolution backward: receiver order with a bounded workspace "
+                         "(cgtp_conv_backward_receiver) or sender order (cgtp_conv_backward)")
     ap.add_argument("--natural-order", action="store_true",
                     help="start receivers in node order instead of the heavy-first schedule")
     ap.add_argument("--radial", type=int, default=0, metavar="R",
@@ -505,8 +511,12 @@ def kernel_digest(source, kernel):
 
 def measured_traffic(plan, spec, dtype, kernel):
     """HBM-side bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE record, scaled
-    by the copy-kernel calibration; None unless the record was taken on exactly this kernel's code."""
+    by the copy-kernel calibration; None unless the record was taken on exactly this kernel's code.
+    A tuple of kernels (one call made of several kernels) gives the sum, or None if any is missing."""
     import glob
+    if isinstance(kernel, tuple):
+        parts = [measured_traffic(plan, spec, dtype, k) for k in kernel]
+        return None if any(p is None for p in parts) else sum(parts)
     digest = kernel_digest(plan.source, kernel)
     for path in glob.glob(os.path.join(ROOT, "profiles", "*_hbm_counters.json")):
         rec = json.load(open(path))
@@ -796,13 +806,25 @@ def main():
     gy = torch.empty_like(y)
     gw = torch.empty_like(d["w"])
 
+    receiver = a.backward_schedule == "receiver"
+    ws = None
+    if receiver:
+        full, least = cg.conv_backward_receiver_workspace_size(plan, N, E)
+        ws = torch.empty(max(least, min(full, RECEIVER_WORKSPACE_BYTES)), dtype=torch.uint8, device=device)
+        row_bytes = plan.d_x * es
+        ranges = -(-E // (ws.numel() // row_bytes)) if E else 0
+
     def step(ev=None):
         if ev is not None:
             ev[0].record()
         cg.conv_forward(plan, d["row_ptr"], d["col"], d["x"], y, d["w"], out=out, order=order)
         if ev is not None:
             ev[1].record()
-        cg.conv_backward(plan, d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"], gx, gy, gw)
+        if receiver:
+            cg.conv_backward_receiver(plan, d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"], gx, gy, gw,
+                                      workspace=ws)
+        else:
+            cg.conv_backward(plan, d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"], gx, gy, gw)
         if ev is not None:
             ev[2].record()
 
@@ -822,7 +844,10 @@ def main():
     cold = cold_cache_times(a, step, device)
     fwd_b, bwd_b = algorithmic_bytes(plan, N, E, es)
     fwd_k = split_kernel("cgtp_conv_fwd", plan.row_split(N, E))
-    dom = ("cgtp_conv_bwd", bwd_ms, bwd_b) if bwd_ms >= fwd_ms else (fwd_k, fwd_ms, fwd_b)
+    # the receiver-order backward is one call of several launches (cgtp_conv_rbw per path group and
+    # edge range, cgtp_conv_rbw_dx per range); its time and bytes are those of the whole call
+    bwd_k = ("cgtp_conv_rbw", "cgtp_conv_rbw_dx") if receiver else "cgtp_conv_bwd"
+    dom = (bwd_k, bwd_ms, bwd_b) if bwd_ms >= fwd_ms else (fwd_k, fwd_ms, fwd_b)
     achieved = dom[2] / (dom[1] * 1e-3) / 1e9
     traffic = measured_traffic(plan, spec, a.dtype, dom[0])
     line = {
@@ -842,14 +867,18 @@ def main():
                    "sh_lmax": spec.lmax_sh, "paths": plan.num_paths, "d_out": plan.d_out,
                    "step": "conv_forward + conv_backward (grad_x, grad_y, grad_w)",
                    "receiver_schedule": "natural" if a.natural_order else "heavy-first",
+                   "backward_schedule": (f"receiver order, {ws.numel()} B workspace, {ranges} edge range(s), "
+                                         f"{plan.info.fwd_tasks} task(s)") if receiver else "sender order",
                    "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
                    "fwd_edges_per_s": E / (fwd_ms * 1e-3), "bwd_edges_per_s": E / (bwd_ms * 1e-3),
                    "spread_ms": spread(evs), "cold_cache": cold},
-        "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": achieved, "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": "+".join(dom[0]) if isinstance(dom[0], tuple) else dom[0],
+                     "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": dom[2], "avg_launch_ms": dom[1],
-                     "other": {"kernel": fwd_k if dom[0] == "cgtp_conv_bwd" else "cgtp_conv_bwd",
-                               "achieved": (fwd_b / (fwd_ms * 1e-3) if dom[0] == "cgtp_conv_bwd"
+                     "algorithmic_bytes_per_edge": dom[2] / E if E else None,
+                     "other": {"kernel": fwd_k if dom[0] == bwd_k else "+".join(bwd_k) if receiver else bwd_k,
+                               "achieved": (fwd_b / (fwd_ms * 1e-3) if dom[0] == bwd_k
                                             else bwd_b / (bwd_ms * 1e-3)) / 1e9}},
         "cpu_baseline": None,
     }

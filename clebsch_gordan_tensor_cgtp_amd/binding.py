@@ -27,7 +27,8 @@ EXPORTS = ("cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info_get", "cgtp_
            "cgtp_tp_backward_workspace_size", "cgtp_plan_uvw_backward_prepare", "cgtp_plan_uvw_backward_source",
            "cgtp_conv_backward_workspace_size", "cgtp_conv_backward_ws", "cgtp_plan_conv_uvw_backward_prepare",
            "cgtp_plan_conv_uvw_backward_source", "cgtp_conv_backward_radial", "cgtp_conv_backward_radial_workspace_size",
-           "cgtp_conv_row_split")
+           "cgtp_conv_row_split", "cgtp_conv_backward_receiver",
+           "cgtp_conv_backward_receiver_workspace_size")
 _STRING_RESULTS = ("cgtp_last_error", "cgtp_plan_source", "cgtp_plan_radial_source", "cgtp_plan_uvw_backward_source",
                    "cgtp_plan_conv_uvw_backward_source")
 
@@ -80,6 +81,18 @@ def lib():
         L.cgtp_plan_path.argtypes = [vp, i32, ctypes.POINTER(PathInfo)]
         L.cgtp_plan_path_coefficients.argtypes = [vp, i32, i32, vp, vp, ctypes.POINTER(i32)]
         L.cgtp_tp_forward.argtypes = [vp, i64, vp, vp, vp, ctypes.c_int, vp, vp]
+        L.cgtp_tp_backward.argtypes = [vp, i64, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.cgtp_tp_backward_workspace_size.argtypes = [vp, i64, ctypes.POINTER(ctypes.c_size_t)]
+        L.cgtp_conv_backward_receiver.argtypes = [vp, i64, i64] + [vp] * 12 + [ctypes.c_size_t, vp]
+        L.cgtp_conv_backward_receiver_workspace_size.argtypes = [vp, i64, i64, ctypes.POINTER(ctypes.c_size_t),
+                                                                 ctypes.POINTER(ctypes.c_size_t)]
+        L.cgtp_plan_uvw_backward_prepare.argtypes = [vp]
+        L.cgtp_plan_uvw_backward_source.argtypes = [vp]
+        L.cgtp_plan_conv_uvw_backward_prepare.argtypes = [vp]
+        L.cgtp_plan_radial_prepare.argtypes = [vp, i32]
+        L.cgtp_plan_radial_source.argtypes = [vp, i32]
+        L.cgtp_conv_forward_radial.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
+        L.cgtp_conv_double_backward.argtypes = [vp, i64, i64] + [vp] * 18
         L.cgtp_conv_forward.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         L.cgtp_conv_forward_ordered.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
         L.cgtp_graph_order.argtypes = [i64, vp, vp, vp]
@@ -444,6 +457,47 @@ def conv_backward(plan: Plan, row_ptr, col, transpose, x, y, w, grad_out, grad_x
         _dev(w, "w", dt, (E, plan.weight_numel)), _dev(grad_out, "grad_out", dt, (N, plan.d_out)),
         _ptr_or_null(gx, "grad_x", dt, (N, plan.d_x)), _ptr_or_null(gy, "grad_y", dt, (E, plan.d_sh)),
         _ptr_or_null(gw, "grad_w", dt, (E, plan.weight_numel)), _stream(stream, dev)))
+    return gx, gy, gw
+
+
+def conv_backward_receiver_workspace_size(plan: Plan, N: int, E: int):
+    """(bytes for one edge range holding every edge, the least workspace the call accepts)."""
+    full, least = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().cgtp_conv_backward_receiver_workspace_size(plan.handle, N, E, ctypes.byref(full), ctypes.byref(least)))
+    return full.value, least.value
+
+
+def conv_backward_receiver(plan: Plan, row_ptr, col, transpose, x, y, w, grad_out, grad_x=None, grad_y=None,
+                           grad_w=None, need=(True, True, True), workspace=None, stream=None):
+    """The convolution backward in receiver order (cgtp_conv_backward_receiver): returns (grad_x,
+    grad_y, grad_w); entries not in ``need`` are None and not computed.  grad_x needs a workspace
+    (uint8 device tensor); the edges are taken in ranges of as many dx rows as it holds.  One that
+    holds every edge is allocated here unless given."""
+    import torch
+    N, E = row_ptr.shape[0] - 1, col.shape[0]
+    dt = plan.torch_dtype
+    dev = x.device
+    t_row_ptr, t_edge, _ = transpose
+    if need[0] and grad_x is None:
+        grad_x = torch.empty((N, plan.d_x), dtype=dt, device=dev)
+    if need[1] and grad_y is None:
+        grad_y = torch.empty((E, plan.d_sh), dtype=dt, device=dev)
+    if need[2] and grad_w is None:
+        grad_w = torch.empty((E, plan.weight_numel), dtype=dt, device=dev)
+    gx = grad_x if need[0] else None
+    gy = grad_y if need[1] else None
+    gw = grad_w if need[2] else None
+    if gx is not None and workspace is None and E > 0:
+        workspace = torch.empty(conv_backward_receiver_workspace_size(plan, N, E)[0], dtype=torch.uint8, device=dev)
+    ws = ctypes.c_void_p(0) if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().cgtp_conv_backward_receiver(
+        plan.handle, N, E, _dev(row_ptr, "row_ptr", torch.int32), _dev(col, "col", torch.int32),
+        _dev(t_row_ptr, "t_row_ptr", torch.int32, (N + 1,)), _dev(t_edge, "t_edge", torch.int32, (E,)),
+        _dev(x, "x", dt, (N, plan.d_x)), _dev(y, "y", dt, (E, plan.d_sh)), _dev(w, "w", dt, (E, plan.weight_numel)),
+        _dev(grad_out, "grad_out", dt, (N, plan.d_out)), _ptr_or_null(gx, "grad_x", dt, (N, plan.d_x)),
+        _ptr_or_null(gy, "grad_y", dt, (E, plan.d_sh)), _ptr_or_null(gw, "grad_w", dt, (E, plan.weight_numel)),
+        ws, ctypes.c_size_t(wsb), _stream(stream, dev)))
     return gx, gy, gw
 
 

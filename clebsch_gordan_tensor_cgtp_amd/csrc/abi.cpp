@@ -776,6 +776,112 @@ cgtp_status cgtp_conv_backward(const cgtp_plan *plan, int64_t N, int64_t E, cons
     });
 }
 
+// Backward in receiver order: edges per wave (a multiple of the widest group's edge slots) and
+// the edges of one range [e_lo, e_hi) whose dx contributions fit the workspace.
+static long rbw_edges_per_wave(const cgtp::Plan &P, long range_edges)
+{
+    int es = 1;
+    for (const cgtp::Group &g : P.rbw_groups) es = std::max(es, g.es);
+    long k = (range_edges + 16383) / 16384;  // about 16k waves per launch
+    k = std::max<long>(4, std::min<long>(k, 256));
+    return (k + es - 1) / es * es;
+}
+
+cgtp_status cgtp_conv_backward_receiver_workspace_size(const cgtp_plan *plan, int64_t N, int64_t E, size_t *bytes,
+                                                       size_t *min_bytes)
+{
+    return guarded([&] {
+        require(plan != nullptr && bytes != nullptr, "plan and bytes must be non-NULL");
+        check_graph_sizes(N, E);
+        const cgtp::Plan &P = plan->p;
+        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "the receiver-order backward takes uvu plans");
+        const size_t row = (size_t)P.d_x * elem(P);
+        *bytes = (size_t)E * row;
+        if (min_bytes) *min_bytes = E > 0 ? (size_t)rbw_edges_per_wave(P, E) * row : 0;
+    });
+}
+
+cgtp_status cgtp_conv_backward_receiver(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
+                                        const int32_t *col, const int32_t *t_row_ptr, const int32_t *t_edge,
+                                        const void *x, const void *y, const void *w, const void *grad_out,
+                                        void *grad_x, void *grad_y, void *grad_w, void *workspace,
+                                        size_t workspace_bytes, void *stream)
+{
+    return guarded([&] {
+        require(plan != nullptr, "plan is NULL");
+        cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
+        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "the receiver-order backward takes uvu plans");
+        check_graph_sizes(N, E);
+        if (!grad_x && !grad_y && !grad_w) return;
+        if (N == 0) return;
+        const size_t es = elem(P);
+        const size_t row = (size_t)P.d_x * es;
+        require_ptr(row_ptr, "row_ptr", 4);
+        if (grad_x) {
+            require_ptr(t_row_ptr, "t_row_ptr", 4);
+            require_ptr(grad_x, "grad_x", es);
+        }
+        if (grad_y) require_ptr(grad_y, "grad_y", es);
+        if (grad_w) require_ptr(grad_w, "grad_w", es);
+        long range = E;
+        if (E > 0) {
+            require_ptr(col, "col", 4);
+            require_ptr(x, "x", es);
+            require_ptr(y, "y", es);
+            require_ptr(w, "w", es);
+            require_ptr(grad_out, "grad_out", es);
+            if (grad_x) {
+                require_ptr(t_edge, "t_edge", 4);
+                require_ptr(workspace, "workspace", 256);
+                const long kmin = rbw_edges_per_wave(P, E);
+                require(workspace_bytes >= (size_t)kmin * row,
+                        "workspace too small: it must hold the dx rows of at least " + std::to_string(kmin) +
+                            " edges (see cgtp_conv_backward_receiver_workspace_size)");
+                range = (long)std::min<size_t>((size_t)E, workspace_bytes / row);
+            }
+        }
+        const size_t nx = N * P.d_x * es, ny = E * P.d_sh * es, nw = E * (size_t)P.w_numel * es;
+        const size_t wsn = grad_x && E > 0 ? (size_t)range * row : 0;
+        const void *ins[] = {x, y, w, grad_out, row_ptr, col, t_row_ptr, t_edge};
+        const size_t inn[] = {E > 0 ? nx : 0, ny, nw, E > 0 ? N * P.d_out * es : 0, (size_t)(N + 1) * 4, (size_t)E * 4,
+                              grad_x ? (size_t)(N + 1) * 4 : 0, grad_x ? (size_t)E * 4 : 0};
+        const char *inm[] = {"x", "y", "w", "grad_out", "row_ptr", "col", "t_row_ptr", "t_edge"};
+        void *outs[] = {grad_x, grad_y, grad_w, wsn ? workspace : nullptr};
+        const size_t outn[] = {nx, ny, nw, wsn};
+        const char *outm[] = {"grad_x", "grad_y", "grad_w", "workspace"};
+        for (int a = 0; a < 4; ++a) {
+            for (int b = 0; b < 8; ++b) require_disjoint(outs[a], outn[a], outm[a], ins[b], inn[b], inm[b]);
+            for (int b = a + 1; b < 4; ++b) require_disjoint(outs[a], outn[a], outm[a], outs[b], outn[b], outm[b]);
+        }
+        const auto &L = cgtp::module_for_current_device(P);
+        long nrows = (long)N;
+        void *hb = grad_x ? workspace : nullptr;
+        if (E == 0) {
+            // no edges: dx is zero (the sum over an empty range, written by the first range)
+            long e_lo = 0, e_hi = 0;
+            int first = 1;
+            void *args[] = {&t_row_ptr, &t_edge, &hb, &grad_x, &nrows, &e_lo, &e_hi, &first};
+            if (grad_x) launch(L.rbw_dx, nrows, args, stream);
+            return;
+        }
+        for (long e_lo = 0; e_lo < E; e_lo += range) {
+            long e_hi = std::min<long>(E, e_lo + range);
+            long kper = rbw_edges_per_wave(P, e_hi - e_lo);
+            long nwaves = (e_hi - e_lo + kper - 1) / kper;
+            for (int grp = 0; grp < (int)P.rbw_groups.size(); ++grp) {
+                void *args[] = {&row_ptr, &col, &x, &y, &w, &grad_out, &grad_y, &grad_w, &hb,
+                                &nrows, &e_lo, &e_hi, &kper, &grp};
+                launch(L.rbw, nwaves, args, stream);
+            }
+            if (grad_x) {
+                int first = e_lo == 0 ? 1 : 0;
+                void *args[] = {&t_row_ptr, &t_edge, &hb, &grad_x, &nrows, &e_lo, &e_hi, &first};
+                launch(L.rbw_dx, nrows, args, stream);
+            }
+        }
+    });
+}
+
 cgtp_status cgtp_conv_backward_workspace_size(const cgtp_plan *plan, int64_t N, int64_t E, size_t *bytes)
 {
     return guarded([&] {

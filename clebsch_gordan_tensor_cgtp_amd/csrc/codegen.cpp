@@ -204,6 +204,19 @@ void emit_copy(Out &o, const Plan &P, const Group &g, const Touch &t, const std:
     for (int pi : g.paths) o(dst, "gw", pi, " = ", src, "gw", pi, ";");
 }
 
+// sum_n c_n * <prefix><k_n> over the nonzeros in v (the B_ij = sum_k C_ijk g_k of the backward)
+std::string cg_sum_k(const std::vector<const Nonzero *> &v, const std::string &prefix, bool f64)
+{
+    std::ostringstream e;
+    e << lit(v[0]->c, f64) << " * " << prefix << v[0]->k;
+    for (size_t n = 1; n < v.size(); ++n) {
+        std::ostringstream f;
+        f << "FMA(" << lit(v[n]->c, f64) << ", " << prefix << v[n]->k << ", " << e.str() << ")";
+        e.str(f.str());
+    }
+    return e.str();
+}
+
 // Linear combination sum_n c_n * <reg prefix><i>_<j> of the nonzeros in v, as nested FMAs.
 std::string cg_sum(const std::vector<const Nonzero *> &v, const std::string &reg, bool f64)
 {
@@ -1023,6 +1036,20 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
         const Irrep &ir = P.ins[b];
         int off = 0;
         for (int bb = 0; bb < b; ++bb) off += P.ins[bb].dim();
+        if (!t.i1.count(b)) {
+            // an input block no path reads: zero in every channel (its multiplicity may exceed the
+            // channels this group's tiles cover), written once
+            o("if (tile == 0) {");
+            o.ind++;
+            o("for (int uu = ul; uu < ", ir.mul, "; uu += ", g.ct, ") {");
+            o.ind++;
+            for (int i = 0; i < n_of(ir.l); ++i) o("dx[(size_t)s * DX + ", off, " + uu * ", n_of(ir.l), " + ", i, "] = (T)0;");
+            o.ind--;
+            o("}");
+            o.ind--;
+            o("}");
+            continue;
+        }
         bool add = first_i1(b) >= 0 && first_i1(b) < gi;
         std::string guard = needs_mask(ir.mul, g) ? "if (u < " + std::to_string(ir.mul) + ") " : "";
         for (int i = 0; i < n_of(ir.l); ++i)
@@ -1158,6 +1185,424 @@ void emit_bwd_kernel(Out &o, const Plan &P, bool dbl = false)
           dbl ? "ggx, ggy, ggw, " : "", "dx, dy, dw); break;");
     o("default: break;");
     o("}");
+    o.ind--;
+    o("}");
+    o("");
+}
+
+// ------------------------------------------------------------------------------------------
+// Backward in receiver order (cgtp_conv_backward_receiver).  The edges of a contiguous range
+// [e_lo, e_hi) of the receiver CSR are dealt to waves in blocks of `kper` consecutive edges, so
+// the work per wave does not depend on the degree law.  A wave holds the output gradient g[n] of
+// its current receiver in registers (reloaded when its edges cross into the next receiver) and
+// gathers the sender row x[col[e]] per edge: the row it gathers is d_x wide, where the sender
+// order gathers the d_out-wide gradient row.  Per edge and path, with B_ij = sum_k C_ijk g_k:
+//   dW[e,p,u] = sum_i x_i sum_j B_ij y_j          (written once)
+//   dY[e,j]  += W sum_i B_ij x_i, summed over the channel lanes (first writer stores, later add)
+//   h[e,a_p + u(2l1+1) + i] += W sum_j B_ij y_j   (the edge's contribution to dx[col[e]])
+// h goes to the caller's buffer (one row of d_x per edge of the range, only when dx is wanted);
+// cgtp_conv_rbw_dx then sums, for every sender, the rows of its edges in the range (ascending
+// edge id, from the transpose) into dx: the first range writes, later ranges add.  Every output
+// element has one owner and a fixed summation order; no atomics.  One launch per forward path
+// group (input blocks whole where they fit), in order; channel tiles are walked by the same wave.
+
+void emit_find_receiver(Out &o)
+{
+    o("// largest n in [0, nrows) with row_ptr[n] <= e (row_ptr[0] = 0 <= e < row_ptr[nrows]):");
+    o("// a 64-way search, all 64 lanes active, row_ptr non-decreasing so the probes that pass form a prefix");
+    o("__device__ __forceinline__ long find_receiver(const int* __restrict__ row_ptr, long nrows, long e, int lane)");
+    o("{");
+    o.ind++;
+    o("long lo = 0, hi = nrows;");
+    o("while (hi - lo > 1) {");
+    o.ind++;
+    o("const long step = (hi - lo + 63) / 64;");
+    o("const long p = lo + (long)lane * step;");
+    o("const bool ok = p < hi && (long)row_ptr[p] <= e;");
+    o("const unsigned long long m = __ballot(ok);");
+    o("const long last = 63 - __clzll(m);");
+    o("lo += last * step;");
+    o("hi = (lo + step < hi) ? lo + step : hi;");
+    o.ind--;
+    o("}");
+    o("return lo;");
+    o.ind--;
+    o("}");
+    o("");
+}
+
+void emit_rbw_group(Out &o, const Plan &P, int gi)
+{
+    const std::vector<Group> &groups = P.rbw_groups;
+    const Group &g = groups[gi];
+    const bool f64 = P.dtype == CGTP_F64;
+    Touch t = touched(P, g.paths);
+    auto first_i1 = [&](int b) {
+        for (int k = 0; k < (int)groups.size(); ++k)
+            for (int pi : groups[k].paths)
+                if (P.paths[pi].i1 == b) return k;
+        return -1;
+    };
+    auto first_i2 = [&](int b) {
+        for (int k = 0; k < (int)groups.size(); ++k)
+            for (int pi : groups[k].paths)
+                if (P.paths[pi].i2 == b) return k;
+        return -1;
+    };
+    std::vector<int> xb, xz;  // input blocks whose h this group writes or adds; untouched blocks (zeroed)
+    for (int b = 0; b < (int)P.ins.size(); ++b) {
+        if (t.i1.count(b)) xb.push_back(b);
+        if (gi == 0 && first_i1(b) < 0) xz.push_back(b);
+    }
+    std::vector<int> yb;  // SH blocks whose dY this group writes or adds
+    for (int b = 0; b < (int)P.sh.size(); ++b)
+        if (t.i2.count(b) || (gi == 0 && first_i2(b) < 0)) yb.push_back(b);
+    auto xoff = [&](int b) {
+        int off = 0;
+        for (int bb = 0; bb < b; ++bb) off += P.ins[bb].dim();
+        return off;
+    };
+    auto yoff = [&](int b) {
+        int off = 0;
+        for (int bb = 0; bb < b; ++bb) off += P.sh[bb].dim();
+        return off;
+    };
+    auto ooff = [&](int q) {
+        int off = 0;
+        for (int qq = 0; qq < q; ++qq) off += P.out[qq].dim();
+        return off;
+    };
+
+    o("__device__ __forceinline__ void rbw_g", gi,
+      "(long blk, int lane, const int* __restrict__ row_ptr, const int* __restrict__ col, const T* __restrict__ x, "
+      "const T* __restrict__ y, const T* __restrict__ w, const T* __restrict__ g, T* __restrict__ dy, "
+      "T* __restrict__ dw, T* __restrict__ hb, long nrows, long e_lo, long e_hi, long kper)");
+    o("{");
+    o.ind++;
+    o("const int slot = lane >> ", log2i(g.ct), ";");
+    o("const int ul = lane & ", g.ct - 1, ";");
+    o("const long eb0 = e_lo + blk * kper;");
+    o("const long eb1 = (eb0 + kper < e_hi) ? eb0 + kper : e_hi;");
+    o("const long n0 = find_receiver(row_ptr, nrows, eb0, lane);");
+    o("for (int tile = 0; tile < ", g.tiles, "; ++tile) {");
+    o.ind++;
+    o("const int u = tile * ", g.ct, " + ul;");
+    o("long e = eb0 + slot;");
+    o("if (e < eb1) {");
+    o.ind++;
+    o("long n = n0;");
+    o("long nend = row_ptr[n + 1];");
+    o("while (nend <= e) { ++n; nend = row_ptr[n + 1]; }");
+    auto load_g = [&](bool declare) {
+        for (int q : t.slots) {
+            const Irrep &ir = P.out[q];
+            for (int k = 0; k < n_of(ir.l); ++k) {
+                std::string ga = "g[(size_t)n * DOUT + " + std::to_string(ooff(q)) + " + u * " + std::to_string(n_of(ir.l)) +
+                                 " + " + std::to_string(k) + "]";
+                if (needs_mask(ir.mul, g))
+                    o(declare ? "T " : "", "g", q, "_", k, " = (u < ", ir.mul, ") ? ", ga, " : (T)0;");
+                else
+                    o(declare ? "T " : "", "g", q, "_", k, " = ", ga, ";");
+            }
+        }
+    };
+    load_g(true);
+    // operands of edge `ev` (sender `sv`) into registers <pre>x.., <pre>y.., <pre>w..
+    auto load_ops = [&](const std::string &pre, const std::string &sv, const std::string &ev, bool declare) {
+        const std::string Tq = declare ? "T " : "";
+        for (int b : t.i1) {
+            const Irrep &ir = P.ins[b];
+            for (int i = 0; i < n_of(ir.l); ++i) {
+                std::string addr = "x[(size_t)" + sv + " * DX + " + std::to_string(xoff(b)) + " + u * " +
+                                   std::to_string(n_of(ir.l)) + " + " + std::to_string(i) + "]";
+                if (needs_mask(ir.mul, g))
+                    o(Tq, pre, "x", b, "_", i, " = (u < ", ir.mul, ") ? ", addr, " : (T)0;");
+                else
+                    o(Tq, pre, "x", b, "_", i, " = ", addr, ";");
+            }
+        }
+        for (int b : t.i2)
+            for (int j = 0; j < n_of(P.sh[b].l); ++j)
+                o(Tq, pre, "y", b, "_", j, " = LD_STREAM(&y[(size_t)", ev, " * DSH + ", yoff(b) + j, "]);");
+        for (int pi : g.paths) {
+            const Path &p = P.paths[pi];
+            std::string wa = "LD_STREAM(&w[(size_t)" + ev + " * WROW + " + std::to_string(p.w_off) + " + u])";
+            if (needs_mask(p.mul_in, g))
+                o(Tq, pre, "w", pi, " = (u < ", p.mul_in, ") ? ", wa, " : (T)0;");
+            else
+                o(Tq, pre, "w", pi, " = ", wa, ";");
+        }
+    };
+    const bool pf = P.rbw_prefetch;
+    if (pf) {
+        // pipeline: sender ids two edges ahead, operands one ahead (indices clamped to the block)
+        o("long en = (e + ", g.es, " < eb1) ? e + ", g.es, " : e;");
+        o("long s = col[e], sn = col[en];");
+        load_ops("", "s", "e", true);
+    }
+    o("for (; e < eb1; e += ", g.es, ") {");
+    o.ind++;
+    if (pf) {
+        o("const long enn = (en + ", g.es, " < eb1) ? en + ", g.es, " : en;");
+        o("const long snn = col[enn];");
+        load_ops("n", "sn", "en", true);
+    }
+    o("if (e >= nend) {");
+    o.ind++;
+    o("do { ++n; nend = row_ptr[n + 1]; } while (nend <= e);");
+    load_g(false);
+    o.ind--;
+    o("}");
+    if (!pf) {
+        o("const long s = col[e];");
+        load_ops("", "s", "e", true);
+    }
+    for (int b : xb)
+        for (int i = 0; i < n_of(P.ins[b].l); ++i) o("T d", b, "_", i, " = (T)0;");
+    for (int b : yb)
+        for (int j = 0; j < n_of(P.sh[b].l); ++j) o("T h", b, "_", j, " = (T)0;");
+    for (int pi : g.paths) {
+        const Path &p = P.paths[pi];
+        std::map<std::pair<int, int>, std::vector<const Nonzero *>> byij;
+        for (const Nonzero &z : p.nz) byij[{z.i, z.j}].push_back(&z);
+        o("{");
+        o.ind++;
+        for (auto &kv : byij)
+            o("const T B", kv.first.first, "_", kv.first.second, " = ",
+              cg_sum_k(kv.second, "g" + std::to_string(p.slot) + "_", f64), ";");
+        std::map<int, std::vector<int>> rows, cols;
+        for (auto &kv : byij) {
+            rows[kv.first.first].push_back(kv.first.second);
+            cols[kv.first.second].push_back(kv.first.first);
+        }
+        // fx_i = sum_j B_ij y_j ; fy_j = sum_i B_ij x_i
+        for (auto &kv : rows) {
+            std::ostringstream e;
+            e << "B" << kv.first << "_" << kv.second[0] << " * y" << p.i2 << "_" << kv.second[0];
+            for (size_t m = 1; m < kv.second.size(); ++m) {
+                std::ostringstream f;
+                f << "FMA(B" << kv.first << "_" << kv.second[m] << ", y" << p.i2 << "_" << kv.second[m] << ", " << e.str()
+                  << ")";
+                e.str(f.str());
+            }
+            o("const T fx", kv.first, " = ", e.str(), ";");
+        }
+        for (auto &kv : cols) {
+            std::ostringstream e;
+            e << "B" << kv.second[0] << "_" << kv.first << " * x" << p.i1 << "_" << kv.second[0];
+            for (size_t m = 1; m < kv.second.size(); ++m) {
+                std::ostringstream f;
+                f << "FMA(B" << kv.second[m] << "_" << kv.first << ", x" << p.i1 << "_" << kv.second[m] << ", " << e.str()
+                  << ")";
+                e.str(f.str());
+            }
+            o("const T fy", kv.first, " = ", e.str(), ";");
+        }
+        {
+            // dW = sum_i x_i fx_i
+            std::ostringstream e;
+            bool first = true;
+            for (auto &kv : rows) {
+                if (first) {
+                    e << "x" << p.i1 << "_" << kv.first << " * fx" << kv.first;
+                    first = false;
+                } else {
+                    std::ostringstream f;
+                    f << "FMA(x" << p.i1 << "_" << kv.first << ", fx" << kv.first << ", " << e.str() << ")";
+                    e.str(f.str());
+                }
+            }
+            std::string guard = needs_mask(p.mul_in, g) ? "(u < " + std::to_string(p.mul_in) + ") && " : "";
+            o("if (", guard, "dw) ST_STREAM(", e.str(), ", &dw[(size_t)e * WROW + ", p.w_off, " + u]);");
+        }
+        for (auto &kv : rows)
+            o("d", p.i1, "_", kv.first, " = FMA(w", pi, ", fx", kv.first, ", d", p.i1, "_", kv.first, ");");
+        for (auto &kv : cols)
+            o("h", p.i2, "_", kv.first, " = FMA(w", pi, ", fy", kv.first, ", h", p.i2, "_", kv.first, ");");
+        o.ind--;
+        o("}");
+        // one path at a time: interleaving the paths' temporaries would multiply the live registers
+        if (P.rbw_sched_barrier) o("__builtin_amdgcn_sched_barrier(0);");
+    }
+    // the edge's contribution to dx of its sender: row (e - e_lo) of hb
+    o("if (hb) {");
+    o.ind++;
+    o("T* hr = hb + (size_t)(e - e_lo) * DX;");
+    if (!xz.empty()) {
+        // input blocks no path reads: their dx is zero (all channels, once)
+        o("if (tile == 0) {");
+        o.ind++;
+        for (int b : xz) {
+            o("for (int uu = ul; uu < ", P.ins[b].mul, "; uu += ", g.ct, ") {");
+            o.ind++;
+            for (int i = 0; i < n_of(P.ins[b].l); ++i) o("hr[", xoff(b), " + uu * ", n_of(P.ins[b].l), " + ", i, "] = (T)0;");
+            o.ind--;
+            o("}");
+        }
+        o.ind--;
+        o("}");
+    }
+    for (int b : xb) {
+        const Irrep &ir = P.ins[b];
+        const bool add = first_i1(b) >= 0 && first_i1(b) < gi;
+        std::string guard = needs_mask(ir.mul, g) ? "if (u < " + std::to_string(ir.mul) + ") " : "";
+        for (int i = 0; i < n_of(ir.l); ++i)
+            o(guard, "hr[", xoff(b), " + u * ", n_of(ir.l), " + ", i, "] ", add ? "+=" : "=", " d", b, "_", i, ";");
+    }
+    o.ind--;
+    o("}");
+    // dY: sum over the slot's channel lanes; lane (j mod ct) of the slot writes or adds column j
+    o("if (dy) {");
+    o.ind++;
+    std::vector<std::pair<int, std::string>> hs;
+    for (int b : yb)
+        for (int jj = 0; jj < n_of(P.sh[b].l); ++jj)
+            hs.push_back({yoff(b) + jj, "h" + std::to_string(b) + "_" + std::to_string(jj)});
+    for (auto &h : hs) o(h.second, " = slot_sum<", g.ct, ">(", h.second, ");");
+    for (size_t r = 0; r * g.ct < hs.size(); ++r) {
+        const size_t lo = r * g.ct, hi = std::min(hs.size(), (r + 1) * g.ct);
+        for (int add = 0; add < 2; ++add) {
+            std::vector<std::pair<size_t, int>> sel;
+            for (size_t c = lo; c < hi; ++c) {
+                int colj = hs[c].first, blk = 0, acc = 0;
+                for (int b = 0; b < (int)P.sh.size(); ++b) {
+                    if (colj < acc + P.sh[b].dim()) {
+                        blk = b;
+                        break;
+                    }
+                    acc += P.sh[b].dim();
+                }
+                bool is_add = first_i2(blk) >= 0 && first_i2(blk) < gi;
+                if ((int)is_add == add) sel.push_back({c - lo, colj});
+            }
+            if (sel.empty()) continue;
+            o("{");
+            o.ind++;
+            o("T v = (T)0;");
+            o("int cj = -1;");
+            for (auto &sc : sel) o("if (ul == ", sc.first, ") { v = ", hs[lo + sc.first].second, "; cj = ", sc.second, "; }");
+            o("if (cj >= 0) {");
+            o.ind++;
+            o("T* p = &dy[(size_t)e * DSH + cj];");
+            if (add)
+                o("*p += v;");
+            else
+                o("if (tile == 0) *p = v; else *p += v;");
+            o.ind--;
+            o("}");
+            o.ind--;
+            o("}");
+        }
+    }
+    o.ind--;
+    o("}");
+    if (pf) {
+        for (int b : t.i1)
+            for (int i = 0; i < n_of(P.ins[b].l); ++i) o("x", b, "_", i, " = nx", b, "_", i, ";");
+        for (int b : t.i2)
+            for (int j = 0; j < n_of(P.sh[b].l); ++j) o("y", b, "_", j, " = ny", b, "_", j, ";");
+        for (int pi : g.paths) o("w", pi, " = nw", pi, ";");
+        o("en = enn;");
+        o("sn = snn;");
+    }
+    o.ind--;
+    o("}");  // edge loop
+    o.ind--;
+    o("}");  // e < eb1
+    o.ind--;
+    o("}");  // tile loop
+    o.ind--;
+    o("}");
+    o("");
+}
+
+void emit_rbw_kernels(Out &o, const Plan &P)
+{
+    emit_find_receiver(o);
+    for (int gi = 0; gi < (int)P.rbw_groups.size(); ++gi) emit_rbw_group(o, P, gi);
+    o("// one wave per block of kper consecutive edges of [e_lo, e_hi); `group` selects the path group (in order)");
+    o("extern \"C\" __global__ void __launch_bounds__(256, ", P.rbw_waves_per_eu,
+      ") cgtp_conv_rbw(const int* __restrict__ row_ptr, const int* __restrict__ col, const T* __restrict__ x, "
+      "const T* __restrict__ y, const T* __restrict__ w, const T* __restrict__ g, T* __restrict__ dy, "
+      "T* __restrict__ dw, T* __restrict__ hb, long nrows, long e_lo, long e_hi, long kper, int group)");
+    o("{");
+    o.ind++;
+    o("const long blk = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const int lane = threadIdx.x & 63;");
+    o("if (e_lo + blk * kper >= e_hi) return;");
+    o("switch (group) {");
+    for (int gi = 0; gi < (int)P.rbw_groups.size(); ++gi)
+        o("case ", gi, ": rbw_g", gi, "(blk, lane, row_ptr, col, x, y, w, g, dy, dw, hb, nrows, e_lo, e_hi, kper); break;");
+    o("default: break;");
+    o("}");
+    o.ind--;
+    o("}");
+    o("");
+    // dx of every sender from the rows of its edges in [e_lo, e_hi): one wave per sender, lanes over
+    // columns; edge ids ascend inside a sender's part of the transpose, so the range is found with
+    // two counts over that part
+    const int nc = (P.d_x + 63) / 64;
+    o("// dx[s] (first range: =, later ranges: +=) sum of hb rows of the sender's edges in [e_lo, e_hi),");
+    o("// in ascending edge id; one wave per sender, lane c holds columns c, c + 64, ...");
+    o("extern \"C\" __global__ void __launch_bounds__(256) cgtp_conv_rbw_dx(const int* __restrict__ t_row_ptr, "
+      "const int* __restrict__ t_edge, const T* __restrict__ hb, T* __restrict__ dx, long nnodes, long e_lo, "
+      "long e_hi, int first)");
+    o("{");
+    o.ind++;
+    o("const long s = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const int lane = threadIdx.x & 63;");
+    o("if (s >= nnodes) return;");
+    o("const int t0 = t_row_ptr[s], t1 = t_row_ptr[s + 1];");
+    o("int ta = t0, tb = t0;");
+    o("for (int base = t0; base < t1; base += 64) {");
+    o.ind++;
+    o("const int tt = base + lane;");
+    o("const long ev = tt < t1 ? (long)t_edge[tt] : e_hi;");
+    o("ta += __popcll(__ballot(tt < t1 && ev < e_lo));");
+    o("tb += __popcll(__ballot(tt < t1 && ev < e_hi));");
+    o.ind--;
+    o("}");
+    o("if (!first && ta == tb) return;");
+    for (int m = 0; m < nc; ++m) o("T a", m, " = (T)0;");
+    // edge ids of 64 rows at a time, one per lane, then broadcast: the row loads of consecutive
+    // edges do not wait for a scalar index load each, and two rows are in flight per step
+    o("for (int base = ta; base < tb; base += 64) {");
+    o.ind++;
+    o("const int cnt = (tb - base < 64) ? tb - base : 64;");
+    o("const int ev = (lane < cnt) ? t_edge[base + lane] : 0;");
+    auto row_loads = [&](const std::string &r, const std::string &v) {
+        for (int m = 0; m < nc; ++m) {
+            if ((m + 1) * 64 <= P.d_x)
+                o("const T ", v, m, " = LD_STREAM(&", r, "[", m * 64, "]);");
+            else
+                o("const T ", v, m, " = (lane + ", m * 64, " < DX) ? LD_STREAM(&", r, "[", m * 64, "]) : (T)0;");
+        }
+    };
+    o("int j = 0;");
+    o("for (; j + 1 < cnt; j += 2) {");
+    o.ind++;
+    o("const T* r0 = hb + (size_t)(__builtin_amdgcn_readlane(ev, j) - e_lo) * DX + lane;");
+    o("const T* r1 = hb + (size_t)(__builtin_amdgcn_readlane(ev, j + 1) - e_lo) * DX + lane;");
+    row_loads("r0", "p");
+    row_loads("r1", "q");
+    for (int m = 0; m < nc; ++m) o("a", m, " += p", m, ";");
+    for (int m = 0; m < nc; ++m) o("a", m, " += q", m, ";");
+    o.ind--;
+    o("}");
+    o("if (j < cnt) {");
+    o.ind++;
+    o("const T* r0 = hb + (size_t)(__builtin_amdgcn_readlane(ev, j) - e_lo) * DX + lane;");
+    row_loads("r0", "p");
+    for (int m = 0; m < nc; ++m) o("a", m, " += p", m, ";");
+    o.ind--;
+    o("}");
+    o.ind--;
+    o("}");
+    o("T* d = dx + (size_t)s * DX + lane;");
+    for (int m = 0; m < nc; ++m) {
+        std::string guard = (m + 1) * 64 <= P.d_x ? "" : "if (lane + " + std::to_string(m * 64) + " < DX) ";
+        o(guard, "d[", m * 64, "] = first ? a", m, " : d[", m * 64, "] + a", m, ";");
+    }
     o.ind--;
     o("}");
     o("");
@@ -2520,6 +2965,8 @@ std::string generate_source(const Plan &P)
         emit_fwd_kernel(o, P, true);
         o("// @@section cgtp_conv_bwd");
         emit_bwd_kernel(o, P);
+        o("// @@section cgtp_conv_rbw");
+        emit_rbw_kernels(o, P);
         o("// @@section cgtp_tp_bwd");
         emit_tpb_kernel(o, P);
         o("// @@section cgtp_conv_dbwd_recv");

@@ -224,6 +224,8 @@ const Plan::Loaded &module_for_current_device(Plan &P)
                   "hipModuleGetFunction");
         }
         check(hipModuleGetFunction(&L.tp_bwd, L.module, "cgtp_tp_bwd"), "hipModuleGetFunction(tp_bwd)");
+        check(hipModuleGetFunction(&L.rbw, L.module, "cgtp_conv_rbw"), "hipModuleGetFunction(conv_rbw)");
+        check(hipModuleGetFunction(&L.rbw_dx, L.module, "cgtp_conv_rbw_dx"), "hipModuleGetFunction(conv_rbw_dx)");
     } else {
         check(hipModuleGetFunction(&L.tp_uvw, L.module, "cgtp_tp_uvw"), "hipModuleGetFunction(tp_uvw)");
         check(hipModuleGetFunction(&L.conv_uvw, L.module, "cgtp_conv_uvw"), "hipModuleGetFunction(conv_uvw)");

@@ -61,6 +61,7 @@ struct Plan {
     int nnz_total = 0;
 
     std::vector<Group> fwd_groups;  // forward: one wave per (receiver, group, tile)
+    std::vector<Group> rbw_groups;  // receiver-order backward: one launch per group, in order
     int fwd_tasks = 0;              // sum over groups of tiles
     std::vector<Group> bwd_groups;  // backward: one launch per group, in order
     std::vector<Group> uvw_groups;  // uvw batched product: one launch per group of output slots
@@ -77,11 +78,14 @@ struct Plan {
     int uvw_waves_per_eu = 2;
     int dbl_fwd_waves_per_eu = 2;   // double backward, receiver pass (twice the forward's operands)
     int dbl_bwd_waves_per_eu = 2;   // double backward, sender pass
+    int rbw_waves_per_eu = 2;       // backward in receiver order (cgtp_conv_rbw)
     int uvc_waves_per_eu = 2;       // uvw convolution
     int uvb_w_waves_per_eu = 1;     // uvw batched backward, dW kernel
     int uvc_rpw = 4;                // uvw convolution: receivers per wave (16 / waves per workgroup)
     bool stream_hint = true;        // nontemporal loads/stores for once-touched per-edge rows
     bool bwd_sched_barrier = true;  // keep path blocks of the backward from interleaving
+    bool rbw_sched_barrier = true;  // the same for the receiver-order backward, per path
+    bool rbw_prefetch = false;      // receiver-order backward: sender ids two edges ahead, operands one ahead
     int bwd_prefetch = -1;          // -1: per group by register estimate; 0/1 forced
     bool fwd_split_inputs = false;  // forward groups follow input-irrep classes (measured slower)
     int fwd_row_split = 0;          // receiver-owned passes: waves per row forced (1, 2, 4); 0 = by N
@@ -93,6 +97,7 @@ struct Plan {
         hipModule_t module = nullptr;
         hipFunction_t conv_fwd = nullptr, conv_bwd = nullptr, tp_fwd = nullptr, tp_uvw = nullptr;
         hipFunction_t dbwd_recv = nullptr, dbwd_send = nullptr, conv_uvw = nullptr, tp_bwd = nullptr;
+        hipFunction_t rbw = nullptr, rbw_dx = nullptr;  // backward in receiver order and its dx sum
         // receiver rows split over 2 / 4 waves (single-task plans; else null)
         hipFunction_t conv_fwd_split[2] = {nullptr, nullptr}, dbwd_recv_split[2] = {nullptr, nullptr};
     };

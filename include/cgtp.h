@@ -324,6 +324,49 @@ cgtp_status cgtp_conv_backward(const cgtp_plan *plan, int64_t N, int64_t E, cons
                                void *stream);
 
 /*
+ * Fused convolution backward in receiver order (uvu plans): the same results
+ * as cgtp_conv_backward, from a schedule whose per-edge gather is the sender
+ * row x[col[e]] (d_x wide) instead of the receiver's output-gradient row
+ * (d_out wide).  Sources: sciencestack.ai page, Abstract (gradient kernels
+ * that minimise global reads and writes); LunaTP page, Abstract
+ * (node-centric execution: the output gradient of a node stays in
+ * registers while its edges stream past); OpenEquivariance discussion
+ * (a deterministic convolution uses a bounded scratch buffer instead of
+ * atomics).  The edges are taken in contiguous ranges [e_lo, e_hi) of the
+ * receiver CSR; for each range:
+ *   1. one pass over its edges (one wave per block of consecutive edges, the
+ *      receiver's gradient row held in registers) writes grad_w and grad_y
+ *      of every edge (formulas of cgtp_conv_backward) and, when grad_x is
+ *      wanted, the edge's contribution to its sender's dx,
+ *        h[e - e_lo, a_p + u(2l1+1) + i] = sum_p W[e,p,u] sum_{jk} C y[e,j] g[n,u,k],
+ *      into `workspace` ([e_hi - e_lo][d_x] rows);
+ *   2. for every sender, the rows of its edges in the range are summed in
+ *      ascending edge id (from the transpose) into grad_x: the first range
+ *      writes, later ranges add.
+ * The range length is the number of rows the workspace holds (at most E):
+ * the workspace is a caller-chosen, bounded buffer, independent of E when
+ * the caller wants it to be; a smaller one means more ranges and more
+ * read-modify-write of grad_x.  cgtp_conv_backward_receiver_workspace_size
+ * gives *bytes = E * d_x * elem (one range) and *min_bytes, the least the call
+ * accepts (one block of edges).  workspace: 256-byte aligned, caller-owned,
+ * disjoint from every argument, contents ignored on entry, unspecified on
+ * return; needed only when grad_x is wanted and E > 0.  t_row_ptr and t_edge
+ * are those of cgtp_graph_transpose (t_dst is not needed); they may be NULL
+ * when grad_x is NULL.  Any gradient may be NULL to skip it; outputs are
+ * overwritten, each element has one owner, no atomics, bitwise deterministic
+ * for a given workspace size (the range boundaries group the dx sums).
+ * Errors: CGTP_ERR_INVALID_ARG (NULL, misaligned, overlapping, workspace
+ * below *min_bytes), CGTP_ERR_UNSUPPORTED (uvw plans), CGTP_ERR_HIP.
+ */
+cgtp_status cgtp_conv_backward_receiver_workspace_size(const cgtp_plan *plan, int64_t N, int64_t E, size_t *bytes,
+                                                       size_t *min_bytes);
+cgtp_status cgtp_conv_backward_receiver(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
+                                        const int32_t *col, const int32_t *t_row_ptr, const int32_t *t_edge,
+                                        const void *x, const void *y, const void *w, const void *grad_out,
+                                        void *grad_x, void *grad_y, void *grad_w, void *workspace,
+                                        size_t workspace_bytes, void *stream);
+
+/*
  * Fused convolution backward with a caller workspace; needed by uvw plans
  * (shared [weight_numel] W, fully connected multiplicity mixing inside the
  * convolution; Sobek page, Abstract: gradients of the same operator without

@@ -27,6 +27,26 @@ def test_header_declares_what_binding_knows():
     assert set(declared_functions()) == set(cg.EXPORTS)
 
 
+def declared_arities():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(?:cgtp_status|const char \*)\s*(cgtp_[a-z_]+)\s*\(([^)]*)\)", text):
+        args = [a for a in m.group(2).split(",") if a.strip() and a.strip() != "void"]
+        out[m.group(1)] = len(args)
+    return out
+
+
+def test_binding_declares_every_argument():
+    """Every export taking arguments has ctypes argtypes of the header's arity (so 64-bit sizes
+    are passed as 64-bit values, never as C int)."""
+    lib = cg.lib()
+    ar = declared_arities()
+    assert set(ar) == set(declared_functions())
+    for name, n in ar.items():
+        if n:
+            assert getattr(lib, name).argtypes is not None and len(getattr(lib, name).argtypes) == n, name
+
+
 def test_library_exports_every_declared_symbol():
     lib = cg.lib()
     for name in declared_functions():

@@ -46,7 +46,9 @@ class DeviceCase:
         }
         self.tab = loops.Tables(self.prob)
 
-    def run(self):
+    def run(self, receiver_ws=None):
+        """Forward, then the backward: sender order, or (receiver_ws = workspace bytes) receiver
+        order with a bounded workspace, as bench.py times it."""
         import torch
         d = self.d
         y = cg.spherical_harmonics(self.spec.lmax_sh, d["vec"])
@@ -57,7 +59,14 @@ class DeviceCase:
             assert torch.equal(out, natural)
             del natural
         tr = cg.graph_transpose(d["row_ptr"], d["col"])
-        gx, gy, gw = cg.conv_backward(self.plan, d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"])
+        if receiver_ws is None:
+            gx, gy, gw = cg.conv_backward(self.plan, d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"])
+        else:
+            full, least = cg.conv_backward_receiver_workspace_size(self.plan, self.N, self.E)
+            ws = torch.empty(max(least, min(full, receiver_ws)), dtype=torch.uint8, device=d["x"].device)
+            gx, gy, gw = cg.conv_backward_receiver(self.plan, d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"],
+                                                   workspace=ws)
+            del ws
         torch.cuda.synchronize()
         return out, gx, gy, gw
 
@@ -97,8 +106,8 @@ class DeviceCase:
         return loops.uvu_backward_x(self.tab, sptr, inv, y, w, g)
 
 
-def check_sampled(case, n_recv, n_send, seed=5):
-    out, gx, gy, gw = case.run()
+def check_sampled(case, n_recv, n_send, seed=5, receiver_ws=None):
+    out, gx, gy, gw = case.run(receiver_ws)
     rng = np.random.default_rng(seed)
     deg = np.diff(case.row_ptr)
     outdeg = np.bincount(case.col, minlength=case.N)
@@ -142,6 +151,38 @@ def test_full_stream_powerlaw_sampled(device):
     case = DeviceCase(synth.CONV_STREAM, "f32", device)
     assert int(np.diff(case.row_ptr).max()) == 2000
     check_sampled(case, 256, 256)
+    del case
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------------------ receiver-order backward
+
+def test_full_nequip_receiver_backward_all_rows(device):
+    """The NequIP-like graph in full, with a 64 MB workspace: four edge ranges, dx summed over them."""
+    case = DeviceCase(synth.CONV_NEQUIP, "f32", device)
+    out, gx, gy, gw = case.run(receiver_ws=64 << 20)
+    allr = np.arange(case.N)
+    edges, want_out, want_dy, want_dw = case.oracle_receivers(allr)
+    assert rel_l2(gy.cpu().numpy(), want_dy) <= TOL["f32"]
+    assert rel_l2(gw.cpu().numpy(), want_dw) <= TOL["f32"]
+    assert rel_l2(gx.cpu().numpy(), case.oracle_senders(allr)) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_full_mace_receiver_backward_sampled(device, dtype):
+    import torch
+    import bench
+    case = DeviceCase(synth.CONV_MACE, dtype, device)
+    check_sampled(case, 192, 128, receiver_ws=bench.RECEIVER_WORKSPACE_BYTES)
+    del case
+    torch.cuda.empty_cache()
+
+
+def test_full_stream_receiver_backward_sampled(device):
+    import torch
+    import bench
+    case = DeviceCase(synth.CONV_STREAM, "f32", device)
+    check_sampled(case, 256, 256, receiver_ws=bench.RECEIVER_WORKSPACE_BYTES)
     del case
     torch.cuda.empty_cache()
 
