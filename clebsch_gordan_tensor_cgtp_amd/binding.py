@@ -27,7 +27,7 @@ EXPORTS = ("cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info_get", "cgtp_
            "cgtp_tp_backward_workspace_size", "cgtp_plan_uvw_backward_prepare", "cgtp_plan_uvw_backward_source",
            "cgtp_conv_backward_workspace_size", "cgtp_conv_backward_ws", "cgtp_plan_conv_uvw_backward_prepare",
            "cgtp_plan_conv_uvw_backward_source", "cgtp_conv_backward_radial", "cgtp_conv_backward_radial_workspace_size",
-           "cgtp_conv_row_split", "cgtp_conv_backward_receiver",
+           "cgtp_conv_row_split", "cgtp_tp_backward_noalloc", "cgtp_conv_backward_receiver",
            "cgtp_conv_backward_receiver_workspace_size")
 _STRING_RESULTS = ("cgtp_last_error", "cgtp_plan_source", "cgtp_plan_radial_source", "cgtp_plan_uvw_backward_source",
                    "cgtp_plan_conv_uvw_backward_source")
@@ -82,6 +82,7 @@ def lib():
         L.cgtp_plan_path_coefficients.argtypes = [vp, i32, i32, vp, vp, ctypes.POINTER(i32)]
         L.cgtp_tp_forward.argtypes = [vp, i64, vp, vp, vp, ctypes.c_int, vp, vp]
         L.cgtp_tp_backward.argtypes = [vp, i64, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.cgtp_tp_backward_noalloc.argtypes = [vp, i64, vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp]
         L.cgtp_tp_backward_workspace_size.argtypes = [vp, i64, ctypes.POINTER(ctypes.c_size_t)]
         L.cgtp_conv_backward_receiver.argtypes = [vp, i64, i64] + [vp] * 12 + [ctypes.c_size_t, vp]
         L.cgtp_conv_backward_receiver_workspace_size.argtypes = [vp, i64, i64, ctypes.POINTER(ctypes.c_size_t),
@@ -315,6 +316,23 @@ def tp_backward(plan: Plan, x, y, w, grad_out, grad_x=None, grad_y=None, grad_w=
                                                                                    shapes)],
                                   ws, ctypes.c_size_t(wsb), _stream(stream, dev)))
     return tuple(res)
+
+
+def tp_backward_noalloc(plan: Plan, x, y, w, grad_out, grad_x, grad_y, grad_w, stream=None):
+    """cgtp_tp_backward_noalloc: the batched backward with its temporary memory in the library's
+    fixed device scratch.  Every output (or None to skip it) is given by the caller; nothing is
+    allocated here or in the library."""
+    B = x.shape[0]
+    dt = plan.torch_dtype
+    shared = 1 if plan.mode == "uvw" else 0
+    wshape = (plan.weight_numel,) if shared else (B, plan.weight_numel)
+    shapes = ((B, plan.d_x), (B, plan.d_sh), wshape)
+    _check(lib().cgtp_tp_backward_noalloc(
+        plan.handle, B, _dev(x, "x", dt, shapes[0]), _dev(y, "y", dt, shapes[1]), _dev(w, "w", dt, wshape), shared,
+        _dev(grad_out, "grad_out", dt, (B, plan.d_out)),
+        *[_ptr_or_null(r, n, dt, sh) for r, n, sh in zip((grad_x, grad_y, grad_w), ("grad_x", "grad_y", "grad_w"),
+                                                         shapes)], _stream(stream, x.device)))
+    return grad_x, grad_y, grad_w
 
 
 def graph_order(row_ptr, order=None, stream=None):

@@ -471,6 +471,29 @@ cgtp_status cgtp_tp_backward(const cgtp_plan *plan, int64_t B, const void *x, co
     });
 }
 
+cgtp_status cgtp_tp_backward_noalloc(const cgtp_plan *plan, int64_t B, const void *x, const void *y, const void *w,
+                                     int shared_weights, const void *grad_out, void *grad_x, void *grad_y,
+                                     void *grad_w, void *stream)
+{
+    return guarded([&] {
+        require(plan != nullptr, "plan is NULL");
+        size_t need = 0;
+        cgtp_status st = cgtp_tp_backward_workspace_size(plan, B, &need);
+        if (st != CGTP_OK) throw cgtp::Error(st, g_last_error);
+        if (need > cgtp::kScratchBytes)
+            throw cgtp::Error(CGTP_ERR_UNSUPPORTED,
+                              "cgtp_tp_backward_noalloc: this batch needs " + std::to_string(need) +
+                                  " bytes of workspace, more than the " + std::to_string(cgtp::kScratchBytes) +
+                                  " bytes of the library's fixed device scratch (use cgtp_tp_backward with a "
+                                  "caller workspace, or a smaller batch)");
+        void *ws = nullptr;
+        if (need > 0) check_hip(cgtp::scratch_for_current_device(&ws), "hipGetSymbolAddress(scratch)");
+        st = cgtp_tp_backward(plan, B, x, y, w, shared_weights, grad_out, grad_x, grad_y, grad_w, ws,
+                              need > 0 ? cgtp::kScratchBytes : 0, stream);
+        if (st != CGTP_OK) throw cgtp::Error(st, g_last_error);
+    });
+}
+
 cgtp_status cgtp_graph_order(int64_t N, const int32_t *row_ptr, int32_t *order, void *stream)
 {
     return guarded([&] {

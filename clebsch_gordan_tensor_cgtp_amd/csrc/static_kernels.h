@@ -14,4 +14,10 @@ hipError_t launch_transpose(int64_t N, int64_t E, const int32_t *row_ptr, const 
 // a[i] = i for i < n
 hipError_t launch_iota(int64_t n, int32_t *a, hipStream_t st);
 
+// Device scratch of the allocation-free entry point: a fixed array of this module, one copy per
+// device.  The first call on a device looks its address up (with that device current) and keeps
+// it; later calls return the kept address.  Every caller on one device shares the same memory.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t scratch_for_current_device(void **ptr);
+
 }  // namespace cgtp

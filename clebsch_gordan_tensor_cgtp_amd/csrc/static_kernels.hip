@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <map>
+#include <mutex>
 
 #include "static_kernels.h"
 
@@ -306,6 +308,34 @@ hipError_t launch_iota(int64_t n, int32_t *a, hipStream_t st)
 {
     if (n > 0) hipLaunchKernelGGL(iota, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a, n);
     return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// scratch of the allocation-free entry point (cgtp_tp_backward_noalloc): a file-scope device
+// array, so the library never has to allocate device memory for it.  In host code `scratch` is
+// only a handle for the runtime, never a device address: the device address is looked up once
+// per device and only that address is handed to kernels.
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_for_current_device(void **ptr)
+{
+    static std::mutex mu;
+    static std::map<int, void *> by_device;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = by_device.find(dev);
+    if (it == by_device.end()) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        it = by_device.emplace(dev, p).first;
+    }
+    *ptr = it->second;
+    return hipSuccess;
 }
 
 }  // namespace cgtp

@@ -198,6 +198,26 @@ cgtp_status cgtp_tp_backward(const cgtp_plan *plan, int64_t B, const void *x, co
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The batched backward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and bits as
+ * cgtp_tp_backward; the temporary memory it needs (the uvw shared-weight
+ * gradient's per-chunk partials, or the identity-graph route of plans with a
+ * multiplicity above 16) comes from a fixed 64 MiB device array inside the
+ * library, one per device, held until the process ends.  Calls whose
+ * workspace need (cgtp_tp_backward_workspace_size) exceeds 64 MiB return
+ * CGTP_ERR_UNSUPPORTED.  The first call on a device looks up that device's
+ * copy of the array (and, as for every entry point, loads the plan's code on
+ * the device); later calls allocate nothing.  Every call on one device shares
+ * the same array: calls that overlap in time on one device (different streams
+ * or threads) race and give unspecified results; calls ordered on one stream
+ * are safe.  uvu plans use no scratch.
+ */
+cgtp_status cgtp_tp_backward_noalloc(const cgtp_plan *plan, int64_t B, const void *x, const void *y, const void *w,
+                                     int shared_weights, const void *grad_out, void *grad_x, void *grad_y,
+                                     void *grad_w, void *stream);
+
+/*
  * Fused convolution forward, use case B (sciencestack.ai page, Figure 4B;
  * Sobek page, Abstract): for every receiver n,
  *   out[n] = sum_{e in [row_ptr[n], row_ptr[n+1])} TP_uvu(x[col[e]], y[e], W[e]).
