@@ -22,7 +22,7 @@ cg       exact Racah CG -> real basis -> Frobenius 1 -> sign rule -> nonzeros
 sh       real spherical harmonics (component normalisation)
 wigner   real Wigner D by least squares (for equivariance checks)
 ref      numpy definitions: batched TP (uvu, uvw) and its backward, conv forward,
-         backward and double backward (uvu), the uvw conv forward and backward,
+         backward and double backward (uvu and uvw), the uvw conv forward and backward,
          the radial-projection conv forward and backward (W = rho Theta)
 loops    ctypes front-end to ``cpu_loops.c`` (explicit fp64 loops, OpenMP), and
          the double backward, the uvw conv and the radial conv on sampled rows
@@ -30,9 +30,9 @@ loops    ctypes front-end to ``cpu_loops.c`` (explicit fp64 loops, OpenMP), and
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests
 (closed forms, orthogonality, a library CG/SH, brute force, equivariance,
-the trilinear identity and finite differences; the double backward against
-torch autograd applied twice to a dense einsum, finite differences of the
-first-order oracle, and its four Euler identities; the uvw and radial
+the trilinear identity and finite differences; the double backward (uvu and
+uvw) against torch autograd applied twice to a dense einsum, finite
+differences of the first-order oracle, and its four Euler identities; the uvw and radial
 backwards against torch autograd through a dense einsum, one-hot and adjoint
 identities).  No function is "parity unpinned".
 """

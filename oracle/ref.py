@@ -201,6 +201,57 @@ def conv_double_backward(prob: Problem, row_ptr, col, x, y, w, g, ggx, ggy, ggw)
     return dx, dy, dw, dg
 
 
+def conv_double_backward_uvw(prob: Problem, row_ptr, col, x, y, w, g, ggx, ggy, ggw):
+    """Second-order gradients of the convolution with shared weights (uvw).
+
+    Sources as for the uvu double backward; the Sobek page (Abstract) carries both operator
+    families, the fully connected one included, through the double backward.  With
+    (dx, dy, dW) = conv_backward_uvw(x, y, W, g) and upstream gradients (ggx, ggy, ggw),
+        L2 = <ggx, dx> + <ggy, dy> + <ggw, dW>
+           = sum over edges e = (s -> n), paths p, channels u, w, nonzeros (i, j, k, c) of
+             c * g[n,w,k] * (W_p[u,w] (ggx[s,u,i] y[e,j] + x[s,u,i] ggy[e,j]) + ggw_p[u,w] x[s,u,i] y[e,j])
+    and, term by term, with G_p[n,u,k] = sum_w W_p[u,w] g[n,w,k] and G'_p the same with ggw:
+      d/dx[s,u,i]    = sum c (ggy_j G_k + y_j G'_k)                 (summed over the edges of s)
+      d/dy[e,j]      = sum_u c (ggx_i G_k + x_i G'_k)
+      d/dW_p[u,w]    = sum_e c g[n,w,k] (ggx_i y_j + x_i ggy_j)
+      d/dg[n,w,k]    = sum_e c (sum_u W_p[u,w] (ggx_i y_j + x_i ggy_j) + sum_u ggw_p[u,w] x_i y_j)
+    Returns (dx, dy, dw, dg), float64, dw shaped like w."""
+    x, y, w, g, ggx, ggy, ggw = (np.asarray(a, np.float64) for a in (x, y, w, g, ggx, ggy, ggw))
+    col = np.asarray(col, np.int64)
+    dst = receivers_of(row_ptr)
+    n_edges = len(col)
+    xs, gxs, gs = x[col], ggx[col], g[dst]
+    dxs = np.zeros_like(xs)
+    dy = np.zeros_like(y)
+    dw = np.zeros_like(w)
+    dgs = np.zeros((n_edges, prob.d_out))
+    for p, a, b, o, mul_in, mul_out, nz in _path_terms(prob):
+        n1, n3 = 2 * p.l1 + 1, 2 * p.l3 + 1
+        xb = xs[:, a:a + mul_in * n1].reshape(n_edges, mul_in, n1)
+        gxb = gxs[:, a:a + mul_in * n1].reshape(n_edges, mul_in, n1)
+        dxb = dxs[:, a:a + mul_in * n1].reshape(n_edges, mul_in, n1)
+        gb = gs[:, o:o + mul_out * n3].reshape(n_edges, mul_out, n3)
+        dgb = dgs[:, o:o + mul_out * n3].reshape(n_edges, mul_out, n3)
+        wp = w[p.w_off:p.w_off + mul_in * mul_out].reshape(mul_in, mul_out)
+        gwp = ggw[p.w_off:p.w_off + mul_in * mul_out].reshape(mul_in, mul_out)
+        dwp = dw[p.w_off:p.w_off + mul_in * mul_out].reshape(mul_in, mul_out)
+        G = np.einsum("uw,ewk->euk", wp, gb)
+        Gp = np.einsum("uw,ewk->euk", gwp, gb)
+        for i, j, k, c in nz:
+            yj = y[:, b + j][:, None]
+            gyj = ggy[:, b + j][:, None]
+            dxb[:, :, i] += c * (gyj * G[:, :, k] + yj * Gp[:, :, k])
+            dy[:, b + j] += c * np.sum(gxb[:, :, i] * G[:, :, k] + xb[:, :, i] * Gp[:, :, k], axis=1)
+            mixed = gxb[:, :, i] * yj + xb[:, :, i] * gyj           # (e, u)
+            dwp += c * np.einsum("eu,ew->uw", mixed, gb[:, :, k])
+            dgb[:, :, k] += c * (mixed @ wp + (xb[:, :, i] * yj) @ gwp)
+    dx = np.zeros_like(x)
+    np.add.at(dx, col, dxs)
+    dg = np.zeros_like(g)
+    np.add.at(dg, dst, dgs)
+    return dx, dy, dw, dg
+
+
 def conv_forward_radial(prob: Problem, row_ptr, col, x, y, rho, theta):
     """Convolution whose per-edge weights are a radial projection: W_e = rho[e] @ Theta.
 

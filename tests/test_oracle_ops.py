@@ -634,3 +634,96 @@ def test_uvw_conv_backward_matches_autograd_and_loops():
     assert np.allclose(dx, got[0][senders], atol=1e-12)
     assert np.allclose(dy, got[1][edges], atol=1e-12)
     assert np.allclose(dw, got[2], atol=1e-11)
+
+
+# ------------------------------------------------------------------------------ uvw double backward
+
+def _uvw_dbl_inputs(prob, rng, n_nodes=7, n_edges=27):
+    row_ptr, col = small_graph(rng, n_nodes, n_edges)
+    x, ggx = rng.standard_normal((2, n_nodes, prob.d_in))
+    y, ggy = rng.standard_normal((2, n_edges, prob.d_sh))
+    w, ggw = rng.standard_normal((2, prob.weight_numel))
+    g = rng.standard_normal((n_nodes, prob.d_out))
+    return row_ptr, col, x, y, w, g, ggx, ggy, ggw
+
+
+@pytest.mark.parametrize("ins,lmax,outs", [
+    ("3x0e+2x1o+2x2e", 2, "2x0e+3x1o+2x2e+1x1e+2x2o"),
+    ("2x0e+1x1o+2x2e+1x3o", 3, "1x0e+2x1o+1x2e+2x3o+1x1e"),
+    ("17x0e+3x1o", 1, "18x1o+2x0e+19x1e")])
+def test_uvw_double_backward_matches_autograd_of_dense_einsum(ins, lmax, outs):
+    """Brute force: torch autograd (CPU, float64) differentiates twice through the dense coupling
+    of the uvw convolution (shared weights, multiplicity mixing inside the coupling tensor)."""
+    import torch
+    prob = irreps.build_problem(ins, irreps.sh_irreps(lmax), outs, "uvw")
+    rng = np.random.default_rng(41)
+    row_ptr, col, x, y, w, g, ggx, ggy, ggw = _uvw_dbl_inputs(prob, rng)
+    t = torch.from_numpy(dense_tensor(prob))
+    dst = torch.from_numpy(ref.receivers_of(row_ptr))
+    colt = torch.from_numpy(np.asarray(col, np.int64))
+    X, Y, W, G = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (x, y, w, g))
+
+    def forward(x_, y_, w_):
+        msg = torch.einsum("abvo,ea,eb,v->eo", t, x_[colt], y_, w_)
+        return torch.zeros(len(row_ptr) - 1, prob.d_out, dtype=torch.float64).index_add(0, dst, msg)
+
+    first = torch.autograd.grad((G * forward(X, Y, W)).sum(), (X, Y, W), create_graph=True)
+    l2 = sum((torch.from_numpy(u) * v).sum() for u, v in zip((ggx, ggy, ggw), first))
+    want = torch.autograd.grad(l2, (X, Y, W, G))
+    got = ref.conv_double_backward_uvw(prob, row_ptr, col, x, y, w, g, ggx, ggy, ggw)
+    for a, b in zip(got, want):
+        assert np.allclose(a, b.numpy(), atol=1e-11, rtol=1e-11)
+
+
+def test_uvw_double_backward_euler_identities_and_finite_differences():
+    """L2 = A + B + C with A = <ggx, dx>, B = <ggy, dy>, C = <ggw, dW> is linear in each operand:
+    <d/dx, x> = B + C, <d/dy, y> = A + C, <d/dW, W> = A + B, <d/dg, g> = A + B + C; and central
+    differences of L2 (through the first-order oracle) match the derivatives."""
+    prob = _uvw_conv_problem()
+    rng = np.random.default_rng(42)
+    row_ptr, col, x, y, w, g, ggx, ggy, ggw = _uvw_dbl_inputs(prob, rng, 6, 23)
+    dx1, dy1, dw1 = ref.conv_backward_uvw(prob, row_ptr, col, x, y, w, g)
+    A, B, C = np.sum(ggx * dx1), np.sum(ggy * dy1), np.sum(ggw * dw1)
+    got = ref.conv_double_backward_uvw(prob, row_ptr, col, x, y, w, g, ggx, ggy, ggw)
+    scale = max(1.0, abs(A) + abs(B) + abs(C))
+    for d, v, want in zip(got, (x, y, w, g), (B + C, A + C, A + B, A + B + C)):
+        assert abs(np.sum(d * v) - want) <= 1e-11 * scale
+
+    def l2(x_, y_, w_, g_):
+        a, b, c = ref.conv_backward_uvw(prob, row_ptr, col, x_, y_, w_, g_)
+        return np.sum(ggx * a) + np.sum(ggy * b) + np.sum(ggw * c)
+
+    h = 1e-6
+    base = [x, y, w, g]
+    for which in range(4):
+        for _ in range(4):
+            arr = base[which]
+            idx = tuple(rng.integers(0, s) for s in arr.shape)
+            plus, minus = list(base), list(base)
+            plus[which], minus[which] = arr.copy(), arr.copy()
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            fd = (l2(*plus) - l2(*minus)) / (2 * h)
+            assert abs(fd - got[which][idx]) < 1e-6 * max(1.0, abs(got[which][idx]))
+
+
+@pytest.mark.parametrize("improper", [False, True])
+def test_uvw_double_backward_equivariance(improper):
+    """Rotating x, the edge vectors and g (and the upstream gradients like what they multiply)
+    rotates d/dx, d/dy and d/dg and leaves d/dW unchanged."""
+    prob = _uvw_conv_problem()
+    rng = np.random.default_rng(43)
+    row_ptr, col, x, _, w, g, ggx, ggy, ggw = _uvw_dbl_inputs(prob, rng)
+    vec = rng.standard_normal((len(col), 3))
+    rot = wigner.random_rotation(rng)
+    lin = -rot if improper else rot
+    d_in, d_sh, d_out = (wigner.irreps_d(ir, rot, improper) for ir in (prob.ins, prob.sh, prob.out))
+    lmax = prob.sh[-1].l
+    y, y_rot = osh.real_sh_all(lmax, vec), osh.real_sh_all(lmax, vec @ lin.T)
+    a = ref.conv_double_backward_uvw(prob, row_ptr, col, x, y, w, g, ggx, ggy @ np.eye(prob.d_sh), ggw)
+    b = ref.conv_double_backward_uvw(prob, row_ptr, col, x @ d_in.T, y_rot, w, g @ d_out.T, ggx @ d_in.T,
+                                     ggy @ d_sh.T, ggw)
+    assert np.allclose(b[0], a[0] @ d_in.T, atol=1e-10)
+    assert np.allclose(b[1], a[1] @ d_sh.T, atol=1e-10)
+    assert np.allclose(b[2], a[2], atol=1e-10)
+    assert np.allclose(b[3], a[3] @ d_out.T, atol=1e-10)
