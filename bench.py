@@ -271,6 +271,8 @@ def bench_conv_uvw(a, spec, plan, d, host_graph, device):
     order = cg.graph_order(d["row_ptr"]) if not a.natural_order else None
     out = torch.empty((N, plan.d_out), dtype=plan.torch_dtype, device=device)
     backward = a.backward
+    if a.double_backward:
+        return bench_conv_uvw_double_backward(a, spec, plan, d, y, order, device)
     if backward:
         plan.conv_uvw_backward_source(0)  # JIT outside the timed region
         tr = cg.graph_transpose(d["row_ptr"], d["col"])
@@ -337,6 +339,65 @@ def bench_conv_uvw(a, spec, plan, d, host_graph, device):
     }
     if not a.no_cpu:
         line["cpu_baseline"] = cpu_baseline_uvw_conv(None, spec, a.seed, host_graph, backward=backward)
+    print(json.dumps(line), flush=True)
+
+
+def bench_conv_uvw_double_backward(a, spec, plan, d, y, order, device):
+    """uvw convolution double backward: one step = cgtp_conv_double_backward_ws with all four results
+    (G and G' on MFMA, the unit-weight sender pass twice, the dW pass twice and its reduction, the
+    forward three times), workspace preallocated."""
+    import torch
+    from clebsch_gordan_tensor_cgtp_amd import binding as cg
+    from clebsch_gordan_tensor_cgtp_amd import synth
+    N, E = d["row_ptr"].shape[0] - 1, d["col"].shape[0]
+    npdt = np.float32 if a.dtype == "f32" else np.float64
+    up = synth.upstream_streams(a.seed)
+    dev = lambda t: torch.from_numpy(np.ascontiguousarray(t)).to(device)
+    gg = (dev(synth.normal(up["gg_x"], (N, plan.d_x), dtype=npdt)),
+          dev(synth.normal(up["gg_y"], (E, plan.d_sh), dtype=npdt)),
+          dev(synth.normal(up["gg_w"], (plan.weight_numel,), 1.0 / np.sqrt(32.0), dtype=npdt)))
+    plan.conv_uvw_backward_source(0)  # JIT outside the timed region
+    tr = cg.graph_transpose(d["row_ptr"], d["col"])
+    ws = torch.empty(cg.conv_double_backward_workspace_size(plan, N, E), dtype=torch.uint8, device=device)
+    outs = (torch.empty_like(d["x"]), torch.empty_like(y), torch.empty_like(d["w"]),
+            torch.empty((N, plan.d_out), dtype=plan.torch_dtype, device=device))
+
+    def step():
+        cg.conv_double_backward(plan, d["row_ptr"], d["col"], tr, d["x"], y, d["w"], d["g"], *gg, order=order,
+                                outs=outs, workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(a.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / a.steps
+    ms = e0.elapsed_time(e1) / a.steps
+    sparse, dense = uvw_conv_flops(plan, N, E)
+    # fixed counting convention: d/dg = three forwards; d/dx, d/dy = G and G' (dense) + two
+    # sender passes (2 x sparse each); d/dW = two dW passes (sparse + dense each)
+    flops = 3 * (sparse + dense) + 2 * (dense + 2 * sparse) + 2 * (sparse + dense)
+    peak = 157.3 if a.dtype == "f32" else 78.6
+    tflops = flops / (ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC, "value": E / wall, "unit": "edges/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": wall * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": a.dtype, "data": "synthetic",
+        "config": {"workload": spec.name, "N": N, "E": E, "in_irreps": spec.in_irreps, "out_irreps": spec.out_irreps,
+                   "sh_lmax": spec.lmax_sh, "paths": plan.num_paths,
+                   "step": "conv_double_backward_ws (uvw: grad_x, grad_y, grad_w, grad_grad_out)",
+                   "receiver_schedule": "natural" if a.natural_order else "heavy-first", "dbl_ms": ms,
+                   "workspace_bytes": int(ws.numel())},
+        "roofline": {"bound": "alu", "kernel": "cgtp_conv_double_backward_ws (uvw, all launches of one call)",
+                     "achieved": tflops, "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak, "traffic": None,
+                     "flops_per_launch": flops, "avg_launch_ms": ms},
+        "cpu_baseline": None,
+    }
     print(json.dumps(line), flush=True)
 
 

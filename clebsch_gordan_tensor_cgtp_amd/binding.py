@@ -28,7 +28,8 @@ EXPORTS = ("cgtp_plan_create", "cgtp_plan_destroy", "cgtp_plan_info_get", "cgtp_
            "cgtp_conv_backward_workspace_size", "cgtp_conv_backward_ws", "cgtp_plan_conv_uvw_backward_prepare",
            "cgtp_plan_conv_uvw_backward_source", "cgtp_conv_backward_radial", "cgtp_conv_backward_radial_workspace_size",
            "cgtp_conv_row_split", "cgtp_tp_backward_noalloc", "cgtp_conv_backward_receiver",
-           "cgtp_conv_backward_receiver_workspace_size")
+           "cgtp_conv_backward_receiver_workspace_size", "cgtp_conv_double_backward_workspace_size",
+           "cgtp_conv_double_backward_ws")
 _STRING_RESULTS = ("cgtp_last_error", "cgtp_plan_source", "cgtp_plan_radial_source", "cgtp_plan_uvw_backward_source",
                    "cgtp_plan_conv_uvw_backward_source")
 
@@ -94,6 +95,8 @@ def lib():
         L.cgtp_plan_radial_source.argtypes = [vp, i32]
         L.cgtp_conv_forward_radial.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
         L.cgtp_conv_double_backward.argtypes = [vp, i64, i64] + [vp] * 18
+        L.cgtp_conv_double_backward_workspace_size.argtypes = [vp, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+        L.cgtp_conv_double_backward_ws.argtypes = [vp, i64, i64] + [vp] * 18 + [ctypes.c_size_t, vp]
         L.cgtp_conv_forward.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         L.cgtp_conv_forward_ordered.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
         L.cgtp_graph_order.argtypes = [i64, vp, vp, vp]
@@ -519,22 +522,46 @@ def conv_backward_receiver(plan: Plan, row_ptr, col, transpose, x, y, w, grad_ou
     return gx, gy, gw
 
 
+def conv_double_backward_workspace_size(plan: Plan, N: int, E: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().cgtp_conv_double_backward_workspace_size(plan.handle, N, E, ctypes.byref(n)))
+    return n.value
+
+
 def conv_double_backward(plan: Plan, row_ptr, col, transpose, x, y, w, grad_out, gg_x, gg_y, gg_w, order=None,
-                         outs=(None, None, None, None), need=(True, True, True, True), stream=None):
+                         outs=(None, None, None, None), need=(True, True, True, True), workspace=None, stream=None):
     """Second-order gradients (grad_x, grad_y, grad_w, grad_grad_out) of
     <gg_x, dx> + <gg_y, dy> + <gg_w, dW>, where (dx, dy, dW) = conv_backward(x, y, w, grad_out).
     An upstream gradient given as None is passed as zeros.  Entries not in ``need`` are None
-    and not computed."""
+    and not computed.  uvw plans (shared weights) run cgtp_conv_double_backward_ws with a
+    workspace, allocated here unless given."""
     import torch
     N, E = row_ptr.shape[0] - 1, col.shape[0]
     dt = plan.torch_dtype
     dev = x.device
-    shapes = ((N, plan.d_x), (E, plan.d_sh), (E, plan.weight_numel), (N, plan.d_out))
+    wshape = (plan.weight_numel,) if plan.mode == "uvw" else (E, plan.weight_numel)
+    shapes = ((N, plan.d_x), (E, plan.d_sh), wshape, (N, plan.d_out))
     gg = [torch.zeros(sh, dtype=dt, device=dev) if t is None else t for t, sh in zip((gg_x, gg_y, gg_w), shapes)]
     res = [None if not nd else (torch.empty(sh, dtype=dt, device=dev) if o is None else o)
            for o, nd, sh in zip(outs, need, shapes)]
     t_row_ptr, t_edge, t_dst = transpose
     names = ("grad_x", "grad_y", "grad_w", "grad_grad_out")
+    if plan.mode == "uvw":
+        nbytes = conv_double_backward_workspace_size(plan, N, E)
+        if workspace is None and nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        ws = ctypes.c_void_p(0) if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+        wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check(lib().cgtp_conv_double_backward_ws(
+            plan.handle, N, E, _dev(row_ptr, "row_ptr", torch.int32), _dev(col, "col", torch.int32),
+            _ptr_or_null(order, "order", torch.int32, (N,)),
+            _dev(t_row_ptr, "t_row_ptr", torch.int32, (N + 1,)), _dev(t_edge, "t_edge", torch.int32, (E,)),
+            _dev(t_dst, "t_dst", torch.int32, (E,)), _dev(x, "x", dt, shapes[0]), _dev(y, "y", dt, shapes[1]),
+            _dev(w, "w", dt, shapes[2]), _dev(grad_out, "grad_out", dt, shapes[3]),
+            _dev(gg[0], "gg_x", dt, shapes[0]), _dev(gg[1], "gg_y", dt, shapes[1]), _dev(gg[2], "gg_w", dt, shapes[2]),
+            *[_ptr_or_null(r, nm, dt, sh) for r, nm, sh in zip(res, names, shapes)], ws, ctypes.c_size_t(wsb),
+            _stream(stream, dev)))
+        return tuple(res)
     _check(lib().cgtp_conv_double_backward(
         plan.handle, N, E, _dev(row_ptr, "row_ptr", torch.int32), _dev(col, "col", torch.int32),
         _ptr_or_null(order, "order", torch.int32, (N,)),

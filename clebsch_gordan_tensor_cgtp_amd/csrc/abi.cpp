@@ -141,7 +141,7 @@ void radial_chunks(int64_t N, long &spc, long &nchunks)
 // the output gradient g; A is the plan itself or the uvw convolution's unit-weight plan.
 void sender_pass(cgtp::Plan &A, int64_t N, int64_t E, const int32_t *t_row_ptr, const int32_t *t_edge,
                  const int32_t *t_dst, const void *x, const void *y, const void *w, const void *g, void *dx, void *dy,
-                 void *dw, void *stream)
+                 void *dw, void *stream, int acc = 0)
 {
     const auto &L = cgtp::module_for_current_device(A);
     long nnodes = (long)N;
@@ -151,7 +151,8 @@ void sender_pass(cgtp::Plan &A, int64_t N, int64_t E, const int32_t *t_row_ptr, 
         const double groups = (double)E / (double)N / A.bwd_groups[grp].es;
         int wpr = groups >= 16 ? 4 : groups >= 8 ? 2 : 1;
         if (const char *env = std::getenv("CGTP_BWD_WPR")) wpr = std::max(1, std::min(4, std::atoi(env)));
-        void *args[] = {&t_row_ptr, &t_edge, &t_dst, &x, &y, &w, &g, &dx, &dy, &dw, &nnodes, &wpr, &grp};
+        // unit-weight plans (the uvw backward's sender pass) take `acc`: add to the outputs
+        void *args[] = {&t_row_ptr, &t_edge, &t_dst, &x, &y, &w, &g, &dx, &dy, &dw, &nnodes, &wpr, &grp, &acc};
         check_hip(hipModuleLaunchKernel(L.conv_bwd, (unsigned)N, 1, 1, 64 * wpr, 1, 1, 0,
                                         static_cast<hipStream_t>(stream), args, nullptr),
                   "hipModuleLaunchKernel");
@@ -1030,7 +1031,9 @@ cgtp_status cgtp_conv_double_backward(const cgtp_plan *plan, int64_t N, int64_t 
         require(plan != nullptr, "plan is NULL");
         cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
         check_graph_sizes(N, E);
-        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "double backward: uvu plans only");
+        if (P.mode != CGTP_UVU)
+            throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "double backward of uvw plans: use cgtp_conv_double_backward_ws "
+                                                    "(it needs a workspace)");
         if (N == 0) return;
         const bool send = grad_x || grad_y || grad_w;
         if (!send && !grad_grad_out) return;
@@ -1090,6 +1093,146 @@ cgtp_status cgtp_conv_double_backward(const cgtp_plan *plan, int64_t N, int64_t 
                 check_hip(hipModuleLaunchKernel(L.dbwd_send, (unsigned)N, 1, 1, 64 * wpr, 1, 1, 0,
                                                 static_cast<hipStream_t>(stream), args, nullptr),
                           "hipModuleLaunchKernel");
+            }
+        }
+    });
+}
+
+// Workspace of the uvw double backward: G = W^T g and G' = ggw^T g (each N x sum_p mul_in (2 l3 + 1),
+// padded to 256 bytes), then two dW partials per 16-receiver tile.  Zero for uvu plans.
+static size_t conv_uvw_dbl_workspace(const cgtp::Plan &P, int64_t N, size_t *g_bytes)
+{
+    size_t gb = 0;
+    const size_t one = conv_uvw_workspace(P, N, &gb);
+    if (g_bytes) *g_bytes = gb;
+    return one == 0 ? 0 : 2 * one;
+}
+
+cgtp_status cgtp_conv_double_backward_workspace_size(const cgtp_plan *plan, int64_t N, int64_t E, size_t *bytes)
+{
+    return guarded([&] {
+        require(plan != nullptr && bytes != nullptr, "plan and bytes must be non-NULL");
+        check_graph_sizes(N, E);
+        *bytes = conv_uvw_dbl_workspace(plan->p, N, nullptr);
+    });
+}
+
+cgtp_status cgtp_conv_double_backward_ws(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
+                                         const int32_t *col, const int32_t *order, const int32_t *t_row_ptr,
+                                         const int32_t *t_edge, const int32_t *t_dst, const void *x, const void *y,
+                                         const void *w, const void *grad_out, const void *gg_x, const void *gg_y,
+                                         const void *gg_w, void *grad_x, void *grad_y, void *grad_w,
+                                         void *grad_grad_out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return guarded([&] {
+        require(plan != nullptr, "plan is NULL");
+        cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
+        check_graph_sizes(N, E);
+        if (P.mode == CGTP_UVU) {
+            const cgtp_status st = cgtp_conv_double_backward(plan, N, E, row_ptr, col, order, t_row_ptr, t_edge, t_dst, x,
+                                                             y, w, grad_out, gg_x, gg_y, gg_w, grad_x, grad_y, grad_w,
+                                                             grad_grad_out, stream);
+            if (st != CGTP_OK) throw cgtp::Error(st, g_last_error);
+            return;
+        }
+        if (!P.uvc_ok) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, P.uvc_why);
+        if (!grad_x && !grad_y && !grad_w && !grad_grad_out) return;
+        const size_t es = elem(P);
+        if (grad_w) require_ptr(grad_w, "grad_w", es);
+        if (N == 0) {
+            // no receivers: d/dW is zero (every other result is empty)
+            if (grad_w) {
+                const auto &F = cgtp::conv_uvw_backward_for_current_device(P);
+                launch_reduce(F.reduce, P.w_numel, workspace, 0, grad_w, stream);
+            }
+            return;
+        }
+        require_ptr(row_ptr, "row_ptr", 4);
+        require_ptr(x, "x", es);
+        require_ptr(gg_x, "gg_x", es);
+        require_ptr(w, "w", es);
+        require_ptr(gg_w, "gg_w", es);
+        require_ptr(grad_out, "grad_out", es);
+        if (grad_x || grad_y) require_ptr(t_row_ptr, "t_row_ptr", 4);
+        if (E > 0) {
+            require_ptr(col, "col", 4);
+            require_ptr(y, "y", es);
+            require_ptr(gg_y, "gg_y", es);
+            if (grad_x || grad_y) {
+                require_ptr(t_edge, "t_edge", 4);
+                require_ptr(t_dst, "t_dst", 4);
+            }
+        }
+        if (grad_x) require_ptr(grad_x, "grad_x", es);
+        if (E > 0 && grad_y) require_ptr(grad_y, "grad_y", es);
+        if (grad_grad_out) require_ptr(grad_grad_out, "grad_grad_out", es);
+        if (order) require_ptr(order, "order", 4);
+        size_t g_bytes = 0;
+        const size_t ws_need = conv_uvw_dbl_workspace(P, N, &g_bytes);
+        const bool need_ws = grad_x || grad_y || grad_w;
+        if (need_ws) {
+            require_ptr(workspace, "workspace", 256);
+            require(workspace_bytes >= ws_need, "workspace too small (see cgtp_conv_double_backward_workspace_size)");
+        }
+        const size_t nx = N * P.d_x * es, ny = E * P.d_sh * es, nw = P.w_numel * es, no = N * P.d_out * es;
+        const void *ins[] = {x, y, w, grad_out, gg_x, gg_y, gg_w, row_ptr, col, t_row_ptr, t_edge, t_dst, order};
+        const size_t inn[] = {nx, ny, nw, no, nx, ny, nw, (size_t)(N + 1) * 4, (size_t)E * 4, (size_t)(N + 1) * 4,
+                              (size_t)E * 4, (size_t)E * 4, order ? (size_t)N * 4 : 0};
+        const char *inm[] = {"x", "y", "w", "grad_out", "gg_x", "gg_y", "gg_w", "row_ptr", "col", "t_row_ptr", "t_edge",
+                             "t_dst", "order"};
+        void *outs[] = {grad_x, grad_y, grad_w, grad_grad_out, need_ws ? workspace : nullptr};
+        const size_t outn[] = {nx, ny, nw, no, ws_need};
+        const char *outm[] = {"grad_x", "grad_y", "grad_w", "grad_grad_out", "workspace"};
+        for (int a = 0; a < 5; ++a) {
+            for (int b = 0; b < 13; ++b) require_disjoint(outs[a], outn[a], outm[a], ins[b], inn[b], inm[b]);
+            for (int b = a + 1; b < 5; ++b) require_disjoint(outs[a], outn[a], outm[a], outs[b], outn[b], outm[b]);
+        }
+        const auto &F = cgtp::conv_uvw_backward_for_current_device(P);
+        long nrows = (long)N;
+        const unsigned tiles = (unsigned)((N + 15) / 16);
+        const unsigned threads = 1024u / (unsigned)P.uvc_rpw;
+        if (grad_x || grad_y) {
+            // G = W^T g and G' = ggw^T g per receiver; d/dx = dx(ggy, G) + dx(y, G') and d/dy =
+            // dY(ggx, G) + dY(x, G'): the unit-weight sender pass twice, the second adding
+            void *G0 = workspace;
+            void *G1 = static_cast<char *>(workspace) + g_bytes;
+            long nwaves = (long)((N + 15) / 16) * (long)cgtp::conv_uvw_g_items(P, nullptr);
+            void *a0[] = {&w, &grad_out, &G0, &nrows, &nwaves};
+            launch(F.g, nwaves, a0, stream);
+            void *a1[] = {&gg_w, &grad_out, &G1, &nrows, &nwaves};
+            launch(F.g, nwaves, a1, stream);
+            cgtp::Plan &A = cgtp::conv_uvw_aux_plan(P);
+            sender_pass(A, N, E, t_row_ptr, t_edge, t_dst, gg_x, gg_y, nullptr, G0, grad_x, grad_y, nullptr, stream, 0);
+            sender_pass(A, N, E, t_row_ptr, t_edge, t_dst, x, y, nullptr, G1, grad_x, grad_y, nullptr, stream, 1);
+        }
+        if (grad_w) {
+            // d/dW = dW(T of (ggx, y)) + dW(T of (x, ggy)): the dW pass twice into consecutive
+            // per-tile partials, summed in order
+            void *part0 = static_cast<char *>(workspace) + 2 * g_bytes;
+            void *part1 = static_cast<char *>(part0) + (size_t)tiles * P.w_numel * es;
+            const void *xs[2] = {gg_x, x}, *ys[2] = {y, gg_y};
+            void *parts[2] = {part0, part1};
+            for (int r = 0; r < 2; ++r)
+                for (int grp = 0; grp < (int)P.uvc_groups.size(); ++grp) {
+                    void *args[] = {&row_ptr, &col, &xs[r], &ys[r], &grad_out, &parts[r], &nrows, &order, &grp};
+                    check_hip(hipModuleLaunchKernel(F.w, tiles, 1, 1, threads, 1, 1, 0,
+                                                    static_cast<hipStream_t>(stream), args, nullptr),
+                              "hipModuleLaunchKernel");
+                }
+            launch_reduce(F.reduce, P.w_numel, part0, 2 * (long)tiles, grad_w, stream);
+        }
+        if (grad_grad_out) {
+            // d/dg = conv(ggx, y, W) + conv(x, ggy, W) + conv(x, y, ggw): the forward three times,
+            // the later ones adding
+            const void *xs[3] = {gg_x, x, x}, *ys[3] = {y, gg_y, y}, *ws3[3] = {w, w, gg_w};
+            for (int r = 0; r < 3; ++r) {
+                int acc = r > 0 ? 1 : 0;
+                for (int grp = 0; grp < (int)P.uvc_groups.size(); ++grp) {
+                    void *args[] = {&row_ptr, &col, &xs[r], &ys[r], &ws3[r], &grad_grad_out, &nrows, &order, &grp, &acc};
+                    check_hip(hipModuleLaunchKernel(F.fwd_acc, tiles, 1, 1, threads, 1, 1, 0,
+                                                    static_cast<hipStream_t>(stream), args, nullptr),
+                              "hipModuleLaunchKernel");
+                }
             }
         }
     });

@@ -667,7 +667,7 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
       "const int* __restrict__ t_dst, const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, "
       "const T* __restrict__ g, ",
       dbl ? "const T* __restrict__ ggx, const T* __restrict__ ggy, const T* __restrict__ ggw, " : "",
-      "T* __restrict__ dx, T* __restrict__ dy, T* __restrict__ dw)");
+      "T* __restrict__ dx, T* __restrict__ dy, T* __restrict__ dw", P.unit_weights ? ", int acc" : "", ")");
     o("{");
     o.ind++;
     o("const int slot = lane >> ", log2i(g.ct), ";");
@@ -926,6 +926,8 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
             o("T* p = &dy[(size_t)e * DSH + col];");
             if (add)
                 o("*p += v;");
+            else if (P.unit_weights)
+                o("if (tile == 0 && !acc) *p = v; else *p += v;  // acc: add to an earlier call's dY");
             else
                 o("if (tile == 0) *p = v; else *p += v;");
             o.ind--;
@@ -1038,8 +1040,8 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
         for (int bb = 0; bb < b; ++bb) off += P.ins[bb].dim();
         if (!t.i1.count(b)) {
             // an input block no path reads: zero in every channel (its multiplicity may exceed the
-            // channels this group's tiles cover), written once
-            o("if (tile == 0) {");
+            // channels this group's tiles cover), written once (not when adding to an earlier call)
+            o(P.unit_weights ? "if (tile == 0 && !acc) {" : "if (tile == 0) {");
             o.ind++;
             o("for (int uu = ul; uu < ", ir.mul, "; uu += ", g.ct, ") {");
             o.ind++;
@@ -1052,9 +1054,16 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
         }
         bool add = first_i1(b) >= 0 && first_i1(b) < gi;
         std::string guard = needs_mask(ir.mul, g) ? "if (u < " + std::to_string(ir.mul) + ") " : "";
-        for (int i = 0; i < n_of(ir.l); ++i)
-            o(guard, "dx[(size_t)s * DX + ", off, " + u * ", n_of(ir.l), " + ", i, "] ", add ? "+=" : "=", " d", b, "_", i,
-              ";");
+        for (int i = 0; i < n_of(ir.l); ++i) {
+            const std::string dst = "dx[(size_t)s * DX + " + std::to_string(off) + " + u * " + std::to_string(n_of(ir.l)) +
+                                    " + " + std::to_string(i) + "]";
+            if (add)
+                o(guard, dst, " += d", b, "_", i, ";");
+            else if (P.unit_weights)
+                o(guard, "{ if (acc) ", dst, " += d", b, "_", i, "; else ", dst, " = d", b, "_", i, "; }");
+            else
+                o(guard, dst, " = d", b, "_", i, ";");
+        }
     }
     o.ind--;
     o("}");
@@ -1171,7 +1180,8 @@ void emit_bwd_kernel(Out &o, const Plan &P, bool dbl = false)
       "const int* __restrict__ t_edge, const int* __restrict__ t_dst, const T* __restrict__ x, "
       "const T* __restrict__ y, const T* __restrict__ w, const T* __restrict__ g, ",
       dbl ? "const T* __restrict__ ggx, const T* __restrict__ ggy, const T* __restrict__ ggw, " : "",
-      "T* __restrict__ dx, T* __restrict__ dy, T* __restrict__ dw, long nnodes, int wpr, int group)");
+      "T* __restrict__ dx, T* __restrict__ dy, T* __restrict__ dw, long nnodes, int wpr, int group",
+      P.unit_weights ? ", int acc" : "", ")");
     o("{");
     o.ind++;
     o("__shared__ T red[", bwd_red_size(groups, P), "];  // partial dx of waves 1..3");
@@ -1182,7 +1192,7 @@ void emit_bwd_kernel(Out &o, const Plan &P, bool dbl = false)
     o("switch (group) {");
     for (int gi = 0; gi < (int)groups.size(); ++gi)
         o("case ", gi, ": ", dbl ? "dbs" : "bwd", "_g", gi, "(s, wv, lane, wpr, red, t_row_ptr, t_edge, t_dst, x, y, w, g, ",
-          dbl ? "ggx, ggy, ggw, " : "", "dx, dy, dw); break;");
+          dbl ? "ggx, ggy, ggw, " : "", "dx, dy, dw", P.unit_weights ? ", acc" : "", "); break;");
     o("default: break;");
     o("}");
     o.ind--;
@@ -1930,7 +1940,7 @@ void emit_uvc_phase_a(Out &o, const Plan &P, const Group &g, std::map<int, int> 
     o("}");  // receivers of the wave
 }
 
-void emit_uvc_group(Out &o, const Plan &P, int gi)
+void emit_uvc_group(Out &o, const Plan &P, int gi, bool acc_variant = false)
 {
     const Group &g = P.uvc_groups[gi];
     const bool f64 = P.dtype == CGTP_F64;
@@ -1948,10 +1958,10 @@ void emit_uvc_group(Out &o, const Plan &P, int gi)
         loff[pi] = lds_elems;
         lds_elems += 16 * uvc_mu_pad(P.paths[pi]) * n_of(P.paths[pi].l3);
     }
-    o("__device__ __forceinline__ void uvc_g", gi,
+    o("__device__ __forceinline__ void ", acc_variant ? "uvca_g" : "uvc_g", gi,
       "(long tile, int wv, int lane, const int* __restrict__ row_ptr, const int* __restrict__ col, "
       "const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows, "
-      "const int* __restrict__ order, T* lds)");
+      "const int* __restrict__ order, T* lds", acc_variant ? ", int acc" : "", ")");
     o("{");
     o.ind++;
     const int nw = 16 / P.uvc_rpw;  // waves per workgroup
@@ -2011,8 +2021,16 @@ void emit_uvc_group(Out &o, const Plan &P, int gi)
                 std::string wo = f64 ? "(" + std::to_string(16 * wt + 4 * v) + " + usub)"
                                      : "(" + std::to_string(16 * wt + v) + " + 4 * usub)";
                 std::string guard = 16 * wt + 15 >= ir.mul ? "if (" + wo + " < " + std::to_string(ir.mul) + ") " : "";
-                for (int k = 0; k < n_of(ir.l); ++k)
-                    o(guard, "orow[", ooff, " + ", wo, " * ", n_of(ir.l), " + ", k, "] ", add ? "+=" : "=", " d", k, "[", v, "];");
+                for (int k = 0; k < n_of(ir.l); ++k) {
+                    std::ostringstream dst;
+                    dst << "orow[" << ooff << " + " << wo << " * " << n_of(ir.l) << " + " << k << "]";
+                    if (add)
+                        o(guard, dst.str(), " += d", k, "[", v, "];");
+                    else if (acc_variant)
+                        o(guard, "{ if (acc) ", dst.str(), " += d", k, "[", v, "]; else ", dst.str(), " = d", k, "[", v, "]; }");
+                    else
+                        o(guard, dst.str(), " = d", k, "[", v, "];");
+                }
             }
             o.ind--;
             o("}");
@@ -2053,6 +2071,31 @@ void emit_uvc_kernel(Out &o, const Plan &P)
     o("switch (group) {");
     for (int gi = 0; gi < (int)P.uvc_groups.size(); ++gi)
         o("case ", gi, ": uvc_g", gi, "(tile, wv, lane, row_ptr, col, x, y, w, out, nrows, order, lds); break;");
+    o("default: break;");
+    o("}");
+    o.ind--;
+    o("}");
+    o("");
+}
+
+// The uvw convolution forward with a runtime `acc` (0: write the output as the forward does; 1:
+// add to it), for the double backward's d/dgrad_out, a sum of three such convolutions.
+void emit_uvc_acc_kernel(Out &o, const Plan &P)
+{
+    for (int gi = 0; gi < (int)P.uvc_groups.size(); ++gi) emit_uvc_group(o, P, gi, true);
+    o("extern \"C\" __global__ void __launch_bounds__(", 1024 / P.uvc_rpw, ", ", P.uvc_waves_per_eu,
+      ") cgtp_conv_uvw_acc(const int* __restrict__ row_ptr, const int* __restrict__ col, const T* __restrict__ x, "
+      "const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows, "
+      "const int* __restrict__ order, int group, int acc)");
+    o("{");
+    o.ind++;
+    o("__shared__ T lds[", uvc_lds_elems(P), "];  // T of the tile's 16 receivers, [p,k][u][row]");
+    o("const long tile = blockIdx.x;");
+    o("const int wv = threadIdx.x >> 6;");
+    o("const int lane = threadIdx.x & 63;");
+    o("switch (group) {");
+    for (int gi = 0; gi < (int)P.uvc_groups.size(); ++gi)
+        o("case ", gi, ": uvca_g", gi, "(tile, wv, lane, row_ptr, col, x, y, w, out, nrows, order, lds, acc); break;");
     o("default: break;");
     o("}");
     o.ind--;
@@ -2812,6 +2855,8 @@ std::string generate_conv_uvw_backward_source(const Plan &P)
     emit_mfma_defs(o, P);
     o("// @@section cgtp_conv_uvw_bwd");
     emit_ucb_kernels(o, P);
+    o("// @@section cgtp_conv_uvw_acc");
+    emit_uvc_acc_kernel(o, P);
     return o.s.str();
 }
 

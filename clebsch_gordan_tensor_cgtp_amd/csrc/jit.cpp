@@ -354,6 +354,7 @@ const Plan::ConvUvwBackward::Fns &conv_uvw_backward_for_current_device(Plan &P)
     check(hipModuleGetFunction(&F.g, F.module, "cgtp_conv_uvw_bwd_g"), "hipModuleGetFunction(conv_uvw_bwd_g)");
     check(hipModuleGetFunction(&F.w, F.module, "cgtp_conv_uvw_bwd_w"), "hipModuleGetFunction(conv_uvw_bwd_w)");
     check(hipModuleGetFunction(&F.reduce, F.module, "cgtp_reduce_chunks"), "hipModuleGetFunction(reduce)");
+    check(hipModuleGetFunction(&F.fwd_acc, F.module, "cgtp_conv_uvw_acc"), "hipModuleGetFunction(conv_uvw_acc)");
     return P.ucb.loaded.emplace(dev, F).first->second;
 }
 

@@ -137,6 +137,7 @@ struct Plan {
         struct Fns {
             hipModule_t module = nullptr;
             hipFunction_t g = nullptr, w = nullptr, reduce = nullptr;
+            hipFunction_t fwd_acc = nullptr;  // the forward, adding to its output (double backward)
         };
         std::map<int, Fns> loaded;  // per device
     } ucb;

@@ -402,7 +402,8 @@ cgtp_status cgtp_conv_backward_receiver(const cgtp_plan *plan, int64_t N, int64_
  * tile (the forward's edge pass, then MFMA over the tile's receivers) summed
  * in tile order.  No atomics, bitwise deterministic.  `order` is the receiver
  * schedule of the grad_w pass (as in cgtp_conv_forward_ordered, NULL =
- * natural; results do not depend on it).  workspace: device memory of at
+ * natural); it decides which receivers share a tile, so grad_w's rounding (not
+ * its value) depends on it, while grad_x and grad_y do not.  workspace: device memory of at
  * least cgtp_conv_backward_workspace_size(plan, N, E) bytes, 256-byte
  * aligned, caller-owned, disjoint from every argument; its contents on entry
  * are ignored and on return unspecified.  Any of grad_x / grad_y / grad_w may
@@ -444,8 +445,8 @@ const char *cgtp_plan_conv_uvw_backward_source(const cgtp_plan *plan, int32_t mo
  * be NULL to skip it (a pass with no requested output is not launched);
  * outputs are overwritten, each row has one owner, no atomics, bitwise
  * deterministic.  Every input named in a requested pass must be non-NULL
- * (pass zeros for an absent upstream gradient); x and gg_x always.  uvu plans
- * only.
+ * (pass zeros for an absent upstream gradient); x and gg_x always.  uvu plans;
+ * uvw plans take cgtp_conv_double_backward_ws (CGTP_ERR_UNSUPPORTED here).
  */
 cgtp_status cgtp_conv_double_backward(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
                                       const int32_t *col, const int32_t *order, const int32_t *t_row_ptr,
@@ -453,6 +454,39 @@ cgtp_status cgtp_conv_double_backward(const cgtp_plan *plan, int64_t N, int64_t 
                                       const void *w, const void *grad_out, const void *gg_x, const void *gg_y,
                                       const void *gg_w, void *grad_x, void *grad_y, void *grad_w,
                                       void *grad_grad_out, void *stream);
+
+/*
+ * Convolution double backward with a caller workspace, for both operator
+ * families (Sobek page, Abstract: the fully connected multiplicity mixing is
+ * carried through forward, backward and double backward; sciencestack.ai
+ * page, Abstract: higher partial derivatives).  uvu plans: exactly
+ * cgtp_conv_double_backward (workspace unused, size 0).  uvw plans (shared W,
+ * gg_w shaped like W, grad_w [weight_numel]): with G_p = W_p^T g and
+ * G'_p = gg_w_p^T g per receiver (as in cgtp_conv_backward_ws),
+ *   grad_x         = dx(y -> gg_y, G) + dx(y, G')
+ *   grad_y         = dY(x -> gg_x, G) + dY(x, G')
+ *   grad_w         = dW(T of (gg_x, y)) + dW(T of (x, gg_y))
+ *   grad_grad_out  = conv(gg_x, y, W) + conv(x, gg_y, W) + conv(x, y, gg_w)
+ * where dx, dY, dW and T are those of cgtp_conv_backward_ws and conv is the
+ * uvw forward: the derivatives of <gg_x, dx> + <gg_y, dY> + <gg_w, dW>.  Each
+ * sum is formed in a fixed order (the second and third terms added by later
+ * launches of the same kernels; grad_w through per-tile partials summed in
+ * order): no atomics, bitwise deterministic.  workspace: at least
+ * cgtp_conv_double_backward_workspace_size bytes (G and G' for N receivers,
+ * then two dW partials per 16-receiver tile), 256-byte aligned, caller-owned,
+ * disjoint from every argument; needed unless only grad_grad_out is asked.
+ * Inputs: x, gg_x, w, gg_w and grad_out always, y and gg_y when E > 0; `order`
+ * is the receiver schedule of the receiver-tile passes (NULL = natural).  Any
+ * output may be NULL to skip it; N = 0 sets grad_w to zero.
+ * Errors: as cgtp_conv_backward_ws.
+ */
+cgtp_status cgtp_conv_double_backward_workspace_size(const cgtp_plan *plan, int64_t N, int64_t E, size_t *bytes);
+cgtp_status cgtp_conv_double_backward_ws(const cgtp_plan *plan, int64_t N, int64_t E, const int32_t *row_ptr,
+                                         const int32_t *col, const int32_t *order, const int32_t *t_row_ptr,
+                                         const int32_t *t_edge, const int32_t *t_dst, const void *x, const void *y,
+                                         const void *w, const void *grad_out, const void *gg_x, const void *gg_y,
+                                         const void *gg_w, void *grad_x, void *grad_y, void *grad_w,
+                                         void *grad_grad_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Real spherical harmonics of the edge vectors, component normalisation
