@@ -442,6 +442,18 @@ def cpu_baseline_radial(spec, seed, host_graph, R, max_seconds=30.0, backward=Fa
                       f"edges, then the fp64 explicit loops, {what}; mean of {reps} rep(s)"}
 
 
+def radial_flops(plan, E, R):
+    """Counting convention of the radial passes: per edge the uvu contraction
+    sum_p mul (2 nnz_p + 2 (2l3+1)) plus 2R flops per weight to rebuild W_e (forward); the
+    backward counts 3x the contraction plus 3 x 2R per weight (W_e rebuilt, drho, dTheta)."""
+    contr = 0
+    for p in range(plan.num_paths):
+        info = plan.path(p)
+        contr += info["mul_in"] * (2 * info["nnz"] + 2 * (2 * info["l3"] + 1))
+    radial = 2 * R * plan.weight_numel
+    return E * (contr + radial), E * (3 * contr + 3 * radial)
+
+
 def bench_radial(a, spec, plan, d, host_graph, device):
     import torch
     from clebsch_gordan_tensor_cgtp_amd import binding as cg
@@ -506,14 +518,22 @@ def bench_radial(a, spec, plan, d, host_graph, device):
                        "bwd_launches": plan.radial_source(R).count("void rbw_g")})
         if bms >= ms:
             dom = ("cgtp_conv_bwd_radial", bms, alg_b)
-    achieved = dom[2] / (dom[1] * 1e-3) / 1e9
+    # Rebuilding W (and consuming dW) costs R FMAs per weight and edge, against 4 or 8 bytes of W
+    # saved: the radial passes are bound by VALU issue, not by HBM.  Fixed counting convention:
+    # forward = the uvu contraction + 2R per weight; backward = 3x the contraction + 3 x 2R per
+    # weight (W rebuilt, drho, dTheta).
+    f_fwd, f_bwd = radial_flops(plan, E, R)
+    flops = f_bwd if dom[0] == "cgtp_conv_bwd_radial" else f_fwd
+    tflops = flops / (dom[1] * 1e-3) / 1e12
+    peak = 157.3 if a.dtype == "f32" else 78.6
     line = {
         "metric": METRIC, "value": E / wall, "unit": "edges/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": wall * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": a.dtype, "data": "synthetic", "config": config,
-        "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "algorithmic_bytes_per_launch": dom[2], "avg_launch_ms": dom[1]},
+        "roofline": {"bound": "alu", "kernel": dom[0], "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": tflops / peak, "traffic": None, "flops_per_launch": flops, "avg_launch_ms": dom[1],
+                     "hbm_algorithmic_bytes_per_launch": dom[2],
+                     "hbm_achieved_gbs": dom[2] / (dom[1] * 1e-3) / 1e9},
         "cpu_baseline": None,
     }
     if not a.no_cpu:

@@ -128,6 +128,15 @@ void launch_reduce(hipFunction_t f, int64_t wn, void *ws, long nchunks, void *ou
               "hipModuleLaunchKernel");
 }
 
+// Radial forward: the Theta columns of one path group's channel tile are copied to LDS
+void check_radial_fwd(const cgtp::Plan &P, int R)
+{
+    if (!cgtp::radial_fwd_fits(P, R))
+        throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "radial forward: R x (paths of a group) x (channels of a tile) Theta "
+                                                "elements exceed the 160 KB LDS of a workgroup (" +
+                                                    std::to_string(cgtp::radial_fwd_lds_bytes(P, R)) + " bytes)");
+}
+
 // Radial backward: chunks of spc consecutive senders, one workgroup and one dTheta partial each
 // (at most 1024 chunks)
 void radial_chunks(int64_t N, long &spc, long &nchunks)
@@ -584,8 +593,7 @@ cgtp_status cgtp_plan_radial_prepare(const cgtp_plan *plan, int32_t R)
         cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
         if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "the radial projection takes uvu plans");
         require(R >= 1 && R <= 64, "R (radial features per edge) must be in [1, 64]");
-        if ((size_t)R * P.w_numel * elem(P) > 65536)
-            throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "R * weight_numel must fit 64 KB of LDS (Theta is staged there)");
+        check_radial_fwd(P, R);
         cgtp::prepare_radial(P, R);
     });
 }
@@ -610,8 +618,7 @@ cgtp_status cgtp_conv_forward_radial(const cgtp_plan *plan, int64_t N, int64_t E
         if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "the radial projection takes uvu plans");
         require(R >= 1 && R <= 64, "R (radial features per edge) must be in [1, 64]");
         const size_t es = elem(P);
-        if ((size_t)R * P.w_numel * es > 65536)
-            throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "R * weight_numel must fit 64 KB of LDS (Theta is staged there)");
+        check_radial_fwd(P, R);
         if (N == 0) return;
         require_ptr(row_ptr, "row_ptr", 4);
         require_ptr(out, "out", es);
@@ -633,8 +640,9 @@ cgtp_status cgtp_conv_forward_radial(const cgtp_plan *plan, int64_t N, int64_t E
         require_disjoint(out, no, "out", order, N * 4, "order");
         hipFunction_t f = cgtp::radial_functions_for_current_device(P, R).fwd;
         // one wave per row: splitting rows measured no faster here (each extra workgroup
-        // stages Theta again; N = 5,000, R = 8: 121 / 121 / 140 us for 1 / 2 / 4 parts)
-        long nrows = (long)N, nwaves = (long)(N * P.fwd_tasks);
+        // stages Theta again; N = 5,000, R = 8: 121 / 121 / 140 us for 1 / 2 / 4 parts).
+        // Workgroups of 4 receivers, one (path group, channel tile) each: fwd_tasks * ceil(N / 4).
+        long nrows = (long)N, nwaves = (long)(P.fwd_tasks * ((N + 3) / 4) * 4);
         void *args[] = {&row_ptr, &col, &x, &y, &rho, &theta, &out, &nrows, &nwaves, &order};
         launch(f, nwaves, args, stream);
     });
@@ -667,8 +675,6 @@ cgtp_status cgtp_conv_backward_radial(const cgtp_plan *plan, int64_t N, int64_t 
         if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "the radial projection takes uvu plans");
         require(R >= 1 && R <= 64, "R (radial features per edge) must be in [1, 64]");
         const size_t es = elem(P);
-        if ((size_t)R * P.w_numel * es > 65536)
-            throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "R * weight_numel must fit 64 KB of LDS (Theta is staged there)");
         if (!grad_x && !grad_y && !grad_rho && !grad_theta) return;
         const size_t nth = (size_t)R * P.w_numel * es;
         if (grad_theta) require_ptr(grad_theta, "grad_theta", es);
@@ -709,7 +715,9 @@ cgtp_status cgtp_conv_backward_radial(const cgtp_plan *plan, int64_t N, int64_t 
         }
         const auto &F = cgtp::radial_functions_for_current_device(P, R);
         if (!F.bwd)
-            throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "radial backward: Theta and the reduction buffer exceed the LDS");
+            throw cgtp::Error(CGTP_ERR_UNSUPPORTED,
+                              "radial backward: a path group's R x mul_in Theta columns and the reduction buffer "
+                              "exceed the 160 KB LDS of a workgroup");
         if (N == 0) {
             if (grad_theta) launch_reduce(F.reduce, (int64_t)R * P.w_numel, workspace, 0, grad_theta, stream);
             return;

@@ -262,22 +262,70 @@ void emit_dbl_recv_math(Out &o, const Plan &P, const Group &g, bool f64, const s
 }
 
 // Radial projection (Sobek page, Abstract: reassociated radial projection): the edge's weights
-// W[p][u] = sum_r rho_r Theta[r][w_p + u] are rebuilt in registers from the R radial
-// features and the LDS copy of Theta ([r][w] layout: consecutive lanes read consecutive
-// words), never stored.
-void emit_radial_weights(Out &o, const Plan &P, const Group &g, const std::string &pre, int R, int only = -1)
+// W[p][u] = sum_r rho_r Theta[r][w_p + u] are rebuilt in registers from the R radial features
+// and an LDS copy of the Theta columns the launch unit reads, never stored.  The copy is compact,
+// [r][col] with the unit's paths side by side: a forward workgroup holds one channel tile of one
+// path group (ct columns per path, zero past the path's channels), a backward workgroup one whole
+// path group (mul_in columns per path).  Consecutive lanes read consecutive words.
+long theta_width(const Plan &P, const Group &g, bool per_tile)
+{
+    long w = 0;
+    for (int pi : g.paths) w += per_tile ? g.ct : P.paths[pi].mul_in;
+    return w;
+}
+
+// LDS index of Theta[r][w_p + u] in the unit's copy; `uu` is the (masked) channel
+std::string theta_index(const Plan &P, const Group &g, int pi, int r, bool per_tile, const std::string &uu)
+{
+    long off = 0;
+    for (int q : g.paths) {
+        if (q == pi) break;
+        off += per_tile ? g.ct : P.paths[q].mul_in;
+    }
+    const std::string col = per_tile ? "(lane & " + std::to_string(g.ct - 1) + ")" : uu;
+    return std::to_string((long)r * theta_width(P, g, per_tile) + off) + " + " + col;
+}
+
+// The workgroup copies the unit's Theta columns into `thl` (a barrier must follow); the forward
+// form needs `tile` in scope
+void emit_theta_stage(Out &o, const Plan &P, const Group &g, int R, bool per_tile, const std::string &nthreads)
+{
+    const long width = theta_width(P, g, per_tile);
+    long off = 0;
+    for (int pi : g.paths) {
+        const Path &p = P.paths[pi];
+        const int n = per_tile ? g.ct : p.mul_in;
+        o("for (int i = threadIdx.x; i < ", (long)R * n, "; i += ", nthreads, ") {");
+        o.ind++;
+        o("const int r = i / ", n, ", c = i - r * ", n, ";");
+        if (per_tile && needs_mask(p.mul_in, g)) {
+            o("const int uu = tile * ", g.ct, " + c;");
+            o("thl[r * ", width, " + ", off, " + c] = uu < ", p.mul_in, " ? theta[(size_t)r * WROW + ", p.w_off,
+              " + uu] : (T)0;");
+        } else if (per_tile) {
+            o("thl[r * ", width, " + ", off, " + c] = theta[(size_t)r * WROW + ", p.w_off, " + tile * ", g.ct, " + c];");
+        } else {
+            o("thl[r * ", width, " + ", off, " + c] = theta[(size_t)r * WROW + ", p.w_off, " + c];");
+        }
+        o.ind--;
+        o("}");
+        off += n;
+    }
+}
+
+void emit_radial_weights(Out &o, const Plan &P, const Group &g, const std::string &pre, int R, int only, bool per_tile)
 {
     for (int pi : g.paths) {
         if (only >= 0 && pi != only) continue;
         const Path &p = P.paths[pi];
         const bool m = needs_mask(p.mul_in, g);
-        // lanes past the block read column 0 (in bounds) and their weight is set to 0
+        // lanes past the block read an in-bounds column and their weight is set to 0
         const std::string uu = m ? "(u < " + std::to_string(p.mul_in) + " ? u : 0)" : "u";
         std::ostringstream e;
-        e << pre << "rho0 * th[" << p.w_off << " + " << uu << "]";
+        e << pre << "rho0 * th[" << theta_index(P, g, pi, 0, per_tile, uu) << "]";
         for (int r = 1; r < R; ++r) {
             std::ostringstream f;
-            f << "FMA(" << pre << "rho" << r << ", th[" << (long)r * P.w_numel + p.w_off << " + " << uu << "], " << e.str()
+            f << "FMA(" << pre << "rho" << r << ", th[" << theta_index(P, g, pi, r, per_tile, uu) << "], " << e.str()
               << ")";
             e.str(f.str());
         }
@@ -304,7 +352,7 @@ void emit_forward_math(Out &o, const Plan &P, const Group &g, bool f64, const st
               ij.second, ";");
         for (int pi : pr.second) {
             const Path &p = P.paths[pi];
-            if (radial) emit_radial_weights(o, P, g, pre, radial, pi);
+            if (radial) emit_radial_weights(o, P, g, pre, radial, pi, true);
             std::map<int, std::vector<const Nonzero *>> byk;
             for (const Nonzero &z : p.nz) byk[z.k].push_back(&z);
             for (auto &kv : byk) {
@@ -791,7 +839,7 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
         for (const Nonzero &z : p.nz) byij[{z.i, z.j}].push_back(&z);
         o("{");
         o.ind++;
-        if (radial) emit_radial_weights(o, P, g, "", radial, pi);
+        if (radial) emit_radial_weights(o, P, g, "", radial, pi, false);
         for (auto &kv : byij) {
             const auto &v = kv.second;
             std::ostringstream e;
@@ -860,7 +908,7 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
                 const std::string uu = needs_mask(p.mul_in, g) ? "(u < " + std::to_string(p.mul_in) + " ? u : 0)" : "u";
                 o("const T dwv = ", e.str(), ";");
                 for (int r = 0; r < radial; ++r) {
-                    o("dr", r, " = FMA(dwv, th[", (long)r * P.w_numel + p.w_off, " + ", uu, "], dr", r, ");");
+                    o("dr", r, " = FMA(dwv, th[", theta_index(P, g, pi, r, false, uu), "], dr", r, ");");
                     o("ta", r, "_", pi, " = FMA(rho", r, ", dwv, ta", r, "_", pi, ");");
                 }
             } else {
@@ -2893,10 +2941,34 @@ long radial_bwd_red_size(const Plan &P, int R, const std::vector<Group> &bwd_gro
     return red;
 }
 
+// LDS words of the compact Theta copies (the largest unit of the launch)
+long radial_fwd_theta_words(const Plan &P, int R)
+{
+    long m = 0;
+    for (const Group &g : P.fwd_groups) m = std::max(m, (long)R * theta_width(P, g, true));
+    return m;
+}
+
+long radial_bwd_theta_words(const Plan &P, int R, const std::vector<Group> &bwd_groups)
+{
+    long m = 0;
+    for (const Group &g : bwd_groups) m = std::max(m, (long)R * theta_width(P, g, false));
+    return m;
+}
+
+long radial_fwd_lds_bytes(const Plan &P, int R)
+{
+    return radial_fwd_theta_words(P, R) * (P.dtype == CGTP_F64 ? 8 : 4);
+}
+
+bool radial_fwd_fits(const Plan &P, int R) { return radial_fwd_lds_bytes(P, R) <= kLdsBytes; }
+
 bool radial_bwd_fits(const Plan &P, int R, const std::vector<Group> &bwd_groups)
 {
     return !bwd_groups.empty() &&
-           ((long)R * P.w_numel + radial_bwd_red_size(P, R, bwd_groups)) * (P.dtype == CGTP_F64 ? 8 : 4) <= kLdsBytes;
+           (radial_bwd_theta_words(P, R, bwd_groups) + radial_bwd_red_size(P, R, bwd_groups)) *
+                   (P.dtype == CGTP_F64 ? 8 : 4) <=
+               kLdsBytes;
 }
 
 std::string generate_radial_source(const Plan &P, int R, const std::vector<Group> &bwd_groups, int bwd_waves)
@@ -2908,45 +2980,62 @@ std::string generate_radial_source(const Plan &P, int R, const std::vector<Group
     o("#define WN ((long)NRAD * WROW)");
     emit_slot_sum(o, P);
     o("// @@section cgtp_conv_fwd_radial");
-    for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi) emit_fwd_group(o, P, gi, false, false, R);
-    o("// one wave per (receiver, path group, channel tile); the workgroup first stages Theta in LDS");
-    // the rebuilt weights and the double-buffered radial features need more registers than the
-    // forward's target leaves (measured: spills at 4 waves per SIMD)
-    const int waves = std::max(1, P.fwd_waves_per_eu - 1 - (R > 8 ? 1 : 0));
-    o("extern \"C\" __global__ void __launch_bounds__(256, ", waves, ") cgtp_conv_fwd_radial("
-      "const int* __restrict__ row_ptr, const int* __restrict__ col, const T* __restrict__ x, const T* __restrict__ y, "
-      "const T* __restrict__ rho, const T* __restrict__ theta, T* __restrict__ out, long nrows, long nwaves, "
-      "const int* __restrict__ order)");
-    o("{");
-    o.ind++;
-    o("__shared__ T thl[", (long)R * P.w_numel, "];  // Theta [r][w]");
-    o("for (int i = threadIdx.x; i < ", (long)R * P.w_numel, "; i += 256) thl[i] = theta[i];");
-    o("__syncthreads();");
-    o("const long wave = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
-    o("const int lane = threadIdx.x & 63;");
-    emit_fwd_unit(o, P, 1);
-    o("switch (task) {");
-    int task = 0;
-    const std::string targ = fwd_splittable(P) ? "<1>" : "";
-    for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi)
-        for (int tile = 0; tile < P.fwd_groups[gi].tiles; ++tile, ++task)
-            o("case ", task, ": rad_g", gi, targ, "(n, ", tile,
-              ", lane, row_ptr, col, x, y, rho, thl, out, nrows, part, live, pred); break;");
-    o("default: break;");
-    o("}");
-    o.ind--;
-    o("}");
-    o("");
+    if (!radial_fwd_fits(P, R)) {
+        o("// forward not generated: the Theta columns of one path group's channel tile exceed the LDS");
+    } else {
+        for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi) emit_fwd_group(o, P, gi, false, false, R);
+        o("// one wave per (receiver, path group, channel tile); the 4 waves of a workgroup share the");
+        o("// (group, tile), whose Theta columns the workgroup first copies to LDS: block b takes unit");
+        o("// b % units of receivers 4 (b / units) .. 4 (b / units) + 3, so a receiver's units run side by side");
+        // the rebuilt weights and the double-buffered radial features need more registers than the
+        // forward's target leaves (measured: spills at 4 waves per SIMD)
+        const int waves = std::max(1, P.fwd_waves_per_eu - 1 - (R > 8 ? 1 : 0));
+        o("extern \"C\" __global__ void __launch_bounds__(256, ", waves, ") cgtp_conv_fwd_radial("
+          "const int* __restrict__ row_ptr, const int* __restrict__ col, const T* __restrict__ x, const T* __restrict__ y, "
+          "const T* __restrict__ rho, const T* __restrict__ theta, T* __restrict__ out, long nrows, long nwaves, "
+          "const int* __restrict__ order)");
+        o("{");
+        o.ind++;
+        o("__shared__ T thl[", radial_fwd_theta_words(P, R), "];  // Theta columns of the unit, [r][col]");
+        o("const int task = (int)(blockIdx.x % ", P.fwd_tasks, ");");
+        o("const int lane = threadIdx.x & 63;");
+        o("long n = (long)(blockIdx.x / ", P.fwd_tasks, ") * 4 + (threadIdx.x >> 6);");
+        o("const bool live = n < nrows;");
+        o("if (live && order) n = order[n];  // receiver schedule (heavy rows first), results unchanged");
+        o("const int part = 0;");
+        o("T* pred = nullptr;");
+        o("switch (task) {");
+        int task = 0;
+        const std::string targ = fwd_splittable(P) ? "<1>" : "";
+        for (int gi = 0; gi < (int)P.fwd_groups.size(); ++gi)
+            for (int tile = 0; tile < P.fwd_groups[gi].tiles; ++tile, ++task) {
+                o("case ", task, ": {");
+                o.ind++;
+                o("const int tile = ", tile, ";");
+                emit_theta_stage(o, P, P.fwd_groups[gi], R, true, "256");
+                o("__syncthreads();");
+                o("if (live) rad_g", gi, targ, "(n, tile, lane, row_ptr, col, x, y, rho, thl, out, nrows, part, live, pred);");
+                o("break;");
+                o.ind--;
+                o("}");
+            }
+        o("default: break;");
+        o("}");
+        o.ind--;
+        o("}");
+        o("");
+    }
     // backward: the sender pass with W rebuilt from rho and Theta and dW consumed into drho and
     // the chunk's dTheta partial (Sobek page, Abstract: no edge-sized weights or adjoints)
     o("// @@section cgtp_conv_bwd_radial");
     const long red = radial_bwd_red_size(P, R, bwd_groups);
-    if (bwd_groups.empty() || ((long)R * P.w_numel + red) * (P.dtype == CGTP_F64 ? 8 : 4) > kLdsBytes) {
-        o("// backward not generated: Theta and the reduction buffer exceed the LDS of a workgroup");
+    if (!radial_bwd_fits(P, R, bwd_groups)) {
+        o("// backward not generated: a path group's Theta columns and the reduction buffer exceed the LDS");
         return o.s.str();
     }
     for (int gi = 0; gi < (int)bwd_groups.size(); ++gi) emit_bwd_group(o, P, gi, false, false, R, &bwd_groups);
-    o("// one workgroup of 64*wpr threads per chunk of spc consecutive senders; `group` selects the path group");
+    o("// one workgroup of 64*wpr threads per chunk of spc consecutive senders; `group` selects the path group,");
+    o("// whose Theta columns the workgroup first copies to LDS");
     o("extern \"C\" __global__ void __launch_bounds__(256, ", bwd_waves, ") cgtp_conv_bwd_radial("
       "const int* __restrict__ t_row_ptr, const int* __restrict__ t_edge, const int* __restrict__ t_dst, "
       "const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ rho, const T* __restrict__ theta, "
@@ -2954,10 +3043,8 @@ std::string generate_radial_source(const Plan &P, int R, const std::vector<Group
       "long nnodes, long spc, int wpr, int group)");
     o("{");
     o.ind++;
-    o("__shared__ T thl[", (long)R * P.w_numel, "];  // Theta [r][w]");
+    o("__shared__ T thl[", radial_bwd_theta_words(P, R, bwd_groups), "];  // Theta columns of the group, [r][col]");
     o("__shared__ T red[", red, "];  // partial dx / dTheta of waves 1..3");
-    o("for (int i = threadIdx.x; i < ", (long)R * P.w_numel, "; i += blockDim.x) thl[i] = theta[i];");
-    o("__syncthreads();");
     // an opaque zero offset keeps the compiler from hoisting every Theta read out of the edge loop
     o("int zo = 0;");
     o("asm volatile(\"\" : \"+v\"(zo));");
@@ -2968,9 +3055,16 @@ std::string generate_radial_source(const Plan &P, int R, const std::vector<Group
     o("const int wv = threadIdx.x >> 6;");
     o("const int lane = threadIdx.x & 63;");
     o("switch (group) {");
-    for (int gi = 0; gi < (int)bwd_groups.size(); ++gi)
-        o("case ", gi, ": rbw_g", gi, "(chunk, c0, c1, wv, lane, wpr, red, t_row_ptr, t_edge, t_dst, x, y, rho, th, g, dx, dy, "
-          "drho, ws); break;");
+    for (int gi = 0; gi < (int)bwd_groups.size(); ++gi) {
+        o("case ", gi, ": {");
+        o.ind++;
+        emit_theta_stage(o, P, bwd_groups[gi], R, false, "blockDim.x");
+        o("__syncthreads();");
+        o("rbw_g", gi, "(chunk, c0, c1, wv, lane, wpr, red, t_row_ptr, t_edge, t_dst, x, y, rho, th, g, dx, dy, drho, ws);");
+        o("break;");
+        o.ind--;
+        o("}");
+    }
     o("default: break;");
     o("}");
     o.ind--;

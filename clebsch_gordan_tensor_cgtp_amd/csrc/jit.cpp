@@ -269,7 +269,8 @@ const Plan::Radial::Fns &radial_functions_for_current_device(Plan &P, int R)
     if (it != rv.loaded.end()) return it->second;
     Plan::Radial::Fns F;
     check(hipModuleLoadData(&F.module, rv.code.data()), "hipModuleLoadData");
-    check(hipModuleGetFunction(&F.fwd, F.module, "cgtp_conv_fwd_radial"), "hipModuleGetFunction(conv_fwd_radial)");
+    if (radial_fwd_fits(P, R))
+        check(hipModuleGetFunction(&F.fwd, F.module, "cgtp_conv_fwd_radial"), "hipModuleGetFunction(conv_fwd_radial)");
     if (radial_bwd_fits(P, R, rv.bwd_groups)) {
         check(hipModuleGetFunction(&F.bwd, F.module, "cgtp_conv_bwd_radial"), "hipModuleGetFunction(conv_bwd_radial)");
         check(hipModuleGetFunction(&F.reduce, F.module, "cgtp_reduce_chunks"), "hipModuleGetFunction(reduce)");

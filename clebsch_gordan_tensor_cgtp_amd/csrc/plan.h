@@ -154,6 +154,9 @@ void schedule(Plan &plan);
 std::string generate_source(const Plan &plan);
 std::string generate_radial_source(const Plan &plan, int R, const std::vector<Group> &bwd_groups, int bwd_waves);
 bool radial_bwd_fits(const Plan &plan, int R, const std::vector<Group> &bwd_groups);
+// LDS bytes of the radial forward's Theta copy (one path group's channel tile) and whether it fits
+long radial_fwd_lds_bytes(const Plan &plan, int R);
+bool radial_fwd_fits(const Plan &plan, int R);
 
 // jit.cpp
 void compile_module(Plan &plan);

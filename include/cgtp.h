@@ -254,8 +254,9 @@ cgtp_status cgtp_conv_forward_ordered(const cgtp_plan *plan, int64_t N, int64_t 
  *   W_e = rho[e] @ Theta,   out[n] = sum_e TP_uvu(x[col[e]], y[e], W_e),
  * with rho [E][R] the edges' radial features (CSR edge order) and Theta
  * [R][weight_numel] shared.  Each edge reads R values instead of weight_numel;
- * Theta is staged in LDS (R * weight_numel elements must fit 64 KB, else
- * CGTP_ERR_UNSUPPORTED).  1 <= R <= 64.  The kernel for a given R is generated
+ * each workgroup copies to LDS the Theta columns of one path group's channel
+ * tile (R x paths x tile width elements must fit the 160 KB of a workgroup,
+ * else CGTP_ERR_UNSUPPORTED before any GPU work).  1 <= R <= 64.  The kernel for a given R is generated
  * and compiled on the first call with that R (then cached).  Everything else
  * (CSR, schedule `order`, layouts, determinism) as cgtp_conv_forward_ordered.
  */
@@ -285,9 +286,10 @@ cgtp_status cgtp_conv_forward_radial(const cgtp_plan *plan, int64_t N, int64_t E
  * caller-owned, contents ignored on entry), summed in chunk order; neither W_e
  * nor dW_e is stored.  Any output may be NULL to skip it (the workspace is
  * needed only for grad_theta); outputs are overwritten, no atomics, bitwise
- * deterministic.  N = 0 sets grad_theta to zero.  R and Theta limits as
- * cgtp_conv_forward_radial; CGTP_ERR_UNSUPPORTED when Theta and the
- * reduction buffer do not fit one workgroup's 160 KB of LDS.  uvu plans only.
+ * deterministic.  N = 0 sets grad_theta to zero.  1 <= R <= 64;
+ * CGTP_ERR_UNSUPPORTED when one path group's Theta columns (R x its channels)
+ * and the reduction buffer do not fit one workgroup's 160 KB of LDS.  uvu
+ * plans only.
  */
 cgtp_status cgtp_conv_backward_radial_workspace_size(const cgtp_plan *plan, int64_t N, int64_t E, int32_t R,
                                                     size_t *bytes);

@@ -342,3 +342,27 @@ def test_compile_after_the_environment_moved(tmp_path):
     assert r.returncode == 0, r.stderr[-2000:]
     assert r.stdout.strip() == "4"
     assert any(p.suffix == ".hsaco" for p in (tmp_path / "second").iterdir())
+
+
+def test_radial_theta_copies_fit_per_path_group(tmp_path, monkeypatch):
+    """The radial kernels copy to LDS only the Theta columns one workgroup reads: a channel tile
+    of one path group in the forward, one path group in the backward.  The MACE-like plan (4,352
+    weights per edge) at R = 8 needs 139 KB for the whole of Theta but a few tens of KB per
+    unit, so both kernels are generated; R = 64 overflows even one unit and is refused before
+    any code is generated or any GPU call is made."""
+    monkeypatch.setenv("CGTP_CACHE_DIR", str(tmp_path))
+    plan = cg.plan_for(synth.WORKLOADS["c3"], "f32")
+    src = plan.radial_source(8)
+    assert "cgtp_conv_fwd_radial(" in src and "cgtp_conv_bwd_radial(" in src
+    sizes = [int(n) for n in re.findall(r"__shared__ T thl\[(\d+)\]", src)]
+    assert len(sizes) == 2 and max(sizes) < 8 * plan.weight_numel
+    # every staged column is a Theta element of a path of the group (row r, column w_p + c)
+    assert "theta[(size_t)r * WROW + " in src
+    with pytest.raises(cg.CgtpError, match="CGTP_ERR_UNSUPPORTED"):
+        plan.radial_source(64)
+    assert "LDS" in cg.last_error()
+    fake = ctypes.c_void_p(1 << 20)
+    s = ctypes.c_void_p(0)
+    unsup = cg.STATUS_CODES["CGTP_ERR_UNSUPPORTED"]
+    assert cg.lib().cgtp_conv_forward_radial(plan.handle, 4, 4, fake, fake, None, fake, fake, 64, fake, fake,
+                                             ctypes.c_void_p(1 << 24), s) == unsup

@@ -26,6 +26,11 @@ CASES = [
     (synth.ConvSpec("mixed", 61, 1_777, "5x0e+3x1o+7x2e+2x3o", 3, 3), 5, "f64"),
     (synth.ConvSpec("mul80", 41, 997, "80x0e+80x1o", 1, 1), 3, "f32"),
     (synth.ConvSpec("mul4", 53, 1_201, "4x0e+4x1o", 2, 2), 1, "f32"),
+    # MACE-like irreps (4,352 weights per edge): Theta is copied to LDS per path group (and per
+    # channel tile in the forward), R * weight_numel alone would not fit a workgroup's LDS
+    (synth.scaled(synth.CONV_MACE, 97, 2_999), 8, "f32"),
+    (synth.scaled(synth.CONV_MACE, 97, 2_999), 8, "f64"),
+    (synth.scaled(synth.CONV_MACE, 61, 1_501), 16, "f32"),
 ]
 
 
