@@ -1870,12 +1870,25 @@ void emit_uvw_kernel(Out &o, const Plan &P)
 // channels (edge slots when there are fewer than 64), and per receiver the
 // unweighted sums T_p[u][k] = sum over its edges of sum_ij C_ijk x[s,u,i] y[e,j]
 // stay in registers (Sobek page, Abstract: edge-local products consumed into
-// bounded receiver-side state).  T is staged in LDS as [p,k][u][row].  Mixing:
+// bounded receiver-side state).  T is staged in LDS as [p,k][u][row], the 16 rows of each u
+// XOR-swizzled (see emit_tsw).  Mixing:
 // out[n, q, w, k] (+)= sum_p sum_u W_p[u][w] T_p[n][u][k] on MFMA 16x16x4 with
 // the 16 receivers as the B columns (A = W_p[u][w = lane % 16], B = T[row =
 // lane % 16][u = 4c + lane / 16][k]).  A slot's first group writes it, later
 // groups (later launches) add, so every sum has a fixed order.
 int uvc_mu_pad(const Path &p) { return (p.mul_in + 3) / 4 * 4; }
+
+// Position of T[u][row] inside a [u][row] block: the row index XOR ((u ^ (u >> 4)) & 15), so that
+// the three access patterns (the edge stream writing 64 consecutive u of one row, the forward's
+// MFMA reading 4 u x 16 rows, the dW pass reading 16 u x 4 rows) each touch distinct banks
+// (fp32; two words per fp64 element, the fewest possible).  Plain [u][row] strides the latter
+// two by 16 words.
+void emit_tsw(Out &o)
+{
+    o("#ifndef TSW");
+    o("#define TSW(u, r) ((u) * 16 + ((r) ^ (((u) ^ ((u) >> 4)) & 15)))");
+    o("#endif");
+}
 
 // uvw convolution, edge stream of one path group: each wave accumulates the unweighted per-path
 // sums T_p[u][k] of its receivers' edges (rows r of the tile `tile`) and stages them in LDS as
@@ -1978,7 +1991,7 @@ void emit_uvc_phase_a(Out &o, const Plan &P, const Group &g, std::map<int, int> 
         const Path &p = P.paths[pi];
         const int mp = uvc_mu_pad(p);
         for (int k = 0; k < n_of(p.l3); ++k)
-            o("if (u < ", mp, ") lds[", loff[pi] + 16 * mp * k, " + u * 16 + r] = t", pi, "_", k, ";");
+            o("if (u < ", mp, ") lds[", loff[pi] + 16 * mp * k, " + TSW(u, r)] = t", pi, "_", k, ";");
     }
     o.ind--;
     o("}");
@@ -2006,6 +2019,7 @@ void emit_uvc_group(Out &o, const Plan &P, int gi, bool acc_variant = false)
         loff[pi] = lds_elems;
         lds_elems += 16 * uvc_mu_pad(P.paths[pi]) * n_of(P.paths[pi].l3);
     }
+    emit_tsw(o);
     o("__device__ __forceinline__ void ", acc_variant ? "uvca_g" : "uvc_g", gi,
       "(long tile, int wv, int lane, const int* __restrict__ row_ptr, const int* __restrict__ col, "
       "const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows, "
@@ -2053,12 +2067,13 @@ void emit_uvc_group(Out &o, const Plan &P, int gi, bool acc_variant = false)
                 }
                 for (int k = 0; k < n_of(p.l3); ++k)
                     for (int c = 0; c < mp / 4; ++c) {
-                        const int base = loff[pi] + 16 * mp * k + 16 * 4 * c;
+                        const int base = loff[pi] + 16 * mp * k;
+                        const std::string at = "TSW(" + std::to_string(4 * c) + " + usub, row)";
                         if (4 * c + 3 >= p.mul_in)
-                            o("d", k, " = MFMA(wa", c, ", (", 4 * c, " + usub < ", p.mul_in, ") ? lds[", base, " + lane] : (T)0, d", k,
-                              ");");
+                            o("d", k, " = MFMA(wa", c, ", (", 4 * c, " + usub < ", p.mul_in, ") ? lds[", base, " + ", at,
+                              "] : (T)0, d", k, ");");
                         else
-                            o("d", k, " = MFMA(wa", c, ", lds[", base, " + lane], d", k, ");");
+                            o("d", k, " = MFMA(wa", c, ", lds[", base, " + ", at, "], d", k, ");");
                     }
                 o.ind--;
                 o("}");
@@ -2112,7 +2127,7 @@ void emit_uvc_kernel(Out &o, const Plan &P)
       "const int* __restrict__ order, int group)");
     o("{");
     o.ind++;
-    o("__shared__ T lds[", uvc_lds_elems(P), "];  // T of the tile's 16 receivers, [p,k][u][row]");
+    o("__shared__ T lds[", uvc_lds_elems(P), "];  // T of the tile's 16 receivers, [p,k][u][row] (rows swizzled)");
     o("const long tile = blockIdx.x;");
     o("const int wv = threadIdx.x >> 6;");
     o("const int lane = threadIdx.x & 63;");
@@ -2137,7 +2152,7 @@ void emit_uvc_acc_kernel(Out &o, const Plan &P)
       "const int* __restrict__ order, int group, int acc)");
     o("{");
     o.ind++;
-    o("__shared__ T lds[", uvc_lds_elems(P), "];  // T of the tile's 16 receivers, [p,k][u][row]");
+    o("__shared__ T lds[", uvc_lds_elems(P), "];  // T of the tile's 16 receivers, [p,k][u][row] (rows swizzled)");
     o("const long tile = blockIdx.x;");
     o("const int wv = threadIdx.x >> 6;");
     o("const int lane = threadIdx.x & 63;");
@@ -2161,6 +2176,10 @@ void emit_uvc_acc_kernel(Out &o, const Plan &P)
 //   dW_p[u][w] = sum_rows sum_k t_p[row][u][k] g[row][w][k],  t_p = sum_i A_p[i][k] x[row][u][i]
 // as per-chunk MFMA partials over row blocks (t transposed through LDS so that the rows are the
 // MFMA K dimension), summed in chunk order by cgtp_reduce_chunks.
+// Row stride of the dY rows staged in LDS by the dx/dY pass: odd, so that the 16 lanes adding one
+// component for their 16 rows hit 16 different banks (a stride of d_sh = 64 put them all on one).
+int uvb_dy_stride(const Plan &P) { return P.d_sh | 1; }
+
 std::string uvb_u(bool f64, int v) { return f64 ? "(usub + " + std::to_string(4 * v) + ")" : "(4 * usub + " + std::to_string(v) + ")"; }
 
 void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
@@ -2182,7 +2201,7 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
     o("const long row = blk * 16 + rl;");
     o("const bool live = row < nrows;");
     o("const long rr = live ? row : nrows - 1;  // rows past the end read row nrows-1 and store nothing");
-    o("T* dyw = dyl + wv * ", 16 * P.d_sh, ";  // this wave's dY rows (zeroed by the kernel)");
+    o("T* dyw = dyl + wv * ", 16 * uvb_dy_stride(P), ";  // this wave's dY rows (zeroed by the kernel)");
     for (int b : t.i2) {
         int off = 0;
         for (int bb = 0; bb < b; ++bb) off += P.sh[bb].dim();
@@ -2296,7 +2315,7 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
         }
         o("if (usub == 0) {");
         o.ind++;
-        for (int j = 0; j < n2; ++j) o("dyw[rl * DSH + ", p.b + j, "] += h", j, ";");
+        for (int j = 0; j < n2; ++j) o("dyw[rl * ", uvb_dy_stride(P), " + ", p.b + j, "] += h", j, ";");
         o.ind--;
         o("}");
         // The dx sums are only read by the conditional store at the end; left alone the compiler
@@ -2346,7 +2365,9 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
     o.ind++;
     o("const int rl = lane & 15;");
     o("const int usub = lane >> 4;");
-    o("T* tw = tl + wv * ", 16 * 17, ";  // this wave's transpose tile [row][u], rows padded to 17");
+    // this wave's transpose tile [row][u], u XOR row inside each row: the write (16 rows x 4 u) and
+    // the read (4 rows x 16 u) each touch distinct banks (rows padded to 17 left 2-way conflicts)
+    o("T* tw = tl + wv * 256;");
     for (int pi : g.paths) o("V4 D", pi, " = {0, 0, 0, 0};");
     o("const long b0 = chunk * bpc;");
     o("const long b1 = b0 + bpc < nblocks ? b0 + bpc : nblocks;");
@@ -2384,8 +2405,9 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
             for (const Nonzero &z : P.paths[pi].nz) ks.insert(z.k);
             for (int k : ks) blocks.push_back({pi, k});
         }
-    // gradient values of block bi of the row block starting at row `rb` (a variable name)
-    auto load_g = [&](size_t bi, const std::string &rb) {
+    // gradient values of block bi of the row block starting at row `rb` (a variable name), into
+    // register set `set`
+    auto load_g = [&](size_t bi, const std::string &rb, int set) {
         const Path &p = P.paths[blocks[bi].first];
         const int k = blocks[bi].second, n3 = n_of(p.l3);
         for (int m = 0; m < 4; ++m) {
@@ -2393,7 +2415,27 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
             o.ind++;
             o("const long br = ", rb, " * 16 + ", 4 * m, " + usub;");
             o("const bool bok = br < nrows && rl < ", p.mul_out, ";");
-            o("gp", m, " = bok ? g[(size_t)br * DOUT + ", p.o, " + rl * ", n3, " + ", k, "] : (T)0;");
+            o("gp", set, "_", m, " = bok ? g[(size_t)br * DOUT + ", p.o, " + rl * ", n3, " + ", k, "] : (T)0;");
+            o.ind--;
+            o("}");
+        }
+    };
+    // The gradient values run D blocks ahead in a ring of D register sets (a block's own work is
+    // a few hundred cycles, a gradient load under load a thousand or more).  The block stream of
+    // a row block is padded with D - 1 at most load-only steps to a multiple of D, so that block
+    // b always uses set b % D, also across row blocks.
+    const int nbk = (int)blocks.size();
+    const int D = std::max(1, P.uvb_w_prefetch);
+    const int padded = nbk == 0 ? 0 : (nbk + D - 1) / D * D;
+    // the load issued at stream position `pos` (consuming nothing at pad positions): block pos + D
+    auto ahead = [&](int pos) {
+        const int tgt = pos + D;
+        if (tgt < nbk) {
+            load_g((size_t)tgt, "blk", tgt % D);
+        } else if (tgt >= padded) {
+            o("if (more) {");
+            o.ind++;
+            load_g((size_t)(tgt - padded), "(blk + 1)", tgt % D);
             o.ind--;
             o("}");
         }
@@ -2404,14 +2446,15 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
         for (int j = 0; j < n_of(P.sh[b].l); ++j) o("T yp", b, "_", j, " = (T)0;");
     for (int c = 0; c < 4; ++c)
         for (int i = 0; i < n1max; ++i) o("T xp", c, "_", i, " = (T)0;");
-    for (int m = 0; m < 4; ++m) o("T gp", m, " = (T)0;");
+    for (int set = 0; set < D; ++set)
+        for (int m = 0; m < 4; ++m) o("T gp", set, "_", m, " = (T)0;");
     o("if (b0 < b1) {");
     o.ind++;
     o("const long row0 = b0 * 16 + rl;");
     o("const long rr0 = row0 < nrows ? row0 : nrows - 1;");
     y_loads("yp", "rr0");
     if (!by_i1.empty()) x_loads(by_i1.begin()->first, "rr0");
-    if (!blocks.empty()) load_g(0, "b0");
+    for (int b = 0; b < std::min(D, nbk); ++b) load_g((size_t)b, "b0", b % D);
     o.ind--;
     o("}");
     o("for (long blk = b0; blk < b1; ++blk) {");
@@ -2455,16 +2498,8 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
             for (auto &kk : byki) {
                 o("{");
                 o.ind++;
-                for (int m = 0; m < 4; ++m) o("const T gc", m, " = gp", m, ";");
-                if (bidx + 1 < blocks.size()) {
-                    load_g(bidx + 1, "blk");
-                } else {
-                    o("if (more) {");
-                    o.ind++;
-                    load_g(0, "(blk + 1)");
-                    o.ind--;
-                    o("}");
-                }
+                for (int m = 0; m < 4; ++m) o("const T gc", m, " = gp", (int)bidx % D, "_", m, ";");
+                ahead((int)bidx);
                 ++bidx;
                 for (auto &ii : kk.second) {
                     const auto &v = ii.second;
@@ -2491,11 +2526,12 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
                             e.str(f.str());
                         }
                     }
-                    o("tw[rl * 17 + ", 4 * c, " + usub] = live ? ", e.str(), " : (T)0;");
+                    o("tw[rl * 16 + ((", 4 * c, " + usub) ^ rl)] = live ? ", e.str(), " : (T)0;");
                 }
                 o("WAVE_SYNC();");
                 // rows are the MFMA K dimension: A = t[row = 4m + lane/16][u = lane%16], B = g[row][w = lane%16][k]
-                for (int m = 0; m < 4; ++m) o("D", pi, " = MFMA(tw[(", 4 * m, " + usub) * 17 + rl], gc", m, ", D", pi, ");");
+                for (int m = 0; m < 4; ++m)
+                    o("D", pi, " = MFMA(tw[(", 4 * m, " + usub) * 16 + (rl ^ (", 4 * m, " + usub))], gc", m, ", D", pi, ");");
                 o("__builtin_amdgcn_sched_barrier(0);");
                 o.ind--;
                 o("}");
@@ -2504,6 +2540,7 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
         o.ind--;
         o("}");
     }
+    for (int pos = nbk; pos < padded; ++pos) ahead(pos);  // load-only steps of the padding
     o.ind--;
     o("}");  // row blocks
     // lane holds D[u = U(v)][w = lane % 16]
@@ -2598,11 +2635,12 @@ void emit_uvb_kernels(Out &o, const Plan &P)
       "T* __restrict__ dy, long nrows, long nblocks)");
     o("{");
     o.ind++;
-    o("__shared__ T dyl[", 4 * 16 * P.d_sh, "];");
+    const int dsp = uvb_dy_stride(P);
+    o("__shared__ T dyl[", 4 * 16 * dsp, "];  // per wave 16 dY rows of stride ", dsp);
     o("const long blk = blockIdx.x;");
     o("const int wv = threadIdx.x >> 6;");
     o("const int lane = threadIdx.x & 63;");
-    o("for (int c = threadIdx.x; c < ", 4 * 16 * P.d_sh, "; c += 256) dyl[c] = (T)0;");
+    o("for (int c = threadIdx.x; c < ", 4 * 16 * dsp, "; c += 256) dyl[c] = (T)0;");
     o("__syncthreads();");
     o("switch (wv) {");
     for (int wv = 0; wv < 4; ++wv) {
@@ -2620,8 +2658,9 @@ void emit_uvb_kernels(Out &o, const Plan &P)
     o("for (int c = threadIdx.x; c < ", 16 * P.d_sh, "; c += 256) {");
     o.ind++;
     o("const long row = blk * 16 + c / DSH;");
-    o("if (row < nrows) dy[(size_t)row * DSH + c % DSH] = ((dyl[c] + dyl[", 16 * P.d_sh, " + c]) + dyl[", 32 * P.d_sh,
-      " + c]) + dyl[", 48 * P.d_sh, " + c];");
+    o("const int lc = (c / DSH) * ", dsp, " + c % DSH;");
+    o("if (row < nrows) dy[(size_t)row * DSH + c % DSH] = ((dyl[lc] + dyl[", 16 * dsp, " + lc]) + dyl[", 32 * dsp,
+      " + lc]) + dyl[", 48 * dsp, " + lc];");
     o.ind--;
     o("}");
     o.ind--;
@@ -2636,7 +2675,7 @@ void emit_uvb_kernels(Out &o, const Plan &P)
       "long nchunks, long nwaves)");
     o("{");
     o.ind++;
-    o("__shared__ T tl[", 4 * 16 * 17, "];");
+    o("__shared__ T tl[", 4 * 256, "];");
     o("const long wave = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
     o("const int wv = threadIdx.x >> 6;");
     o("const int lane = threadIdx.x & 63;");
@@ -2780,6 +2819,7 @@ void emit_ucb_w_group(Out &o, const Plan &P, int gi)
     }
     const bool f64 = P.dtype == CGTP_F64;
     const int nw = 16 / P.uvc_rpw;
+    emit_tsw(o);
     o("__device__ __forceinline__ void ucw_g", gi,
       "(long tile, int wv, int lane, const int* __restrict__ row_ptr, const int* __restrict__ col, "
       "const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ g, T* __restrict__ ws, long nrows, "
@@ -2822,12 +2862,13 @@ void emit_ucb_w_group(Out &o, const Plan &P, int gi)
                     const std::string u = "(" + std::to_string(16 * ut) + " + row)";
                     const bool umask = 16 * ut + 15 >= mp;
                     for (int m = 0; m < 4; ++m) {
-                        const std::string base = std::to_string(loff[pi] + 16 * mp * k + 4 * m);
+                        const std::string base = std::to_string(loff[pi] + 16 * mp * k);
+                        const std::string rr = "(" + std::to_string(4 * m) + " + usub)";
                         if (umask)
-                            o("D", ut, " = MFMA(", u, " < ", mp, " ? lds[", base, " + (", u, " < ", mp, " ? ", u, " : 0) * 16 + usub] : (T)0, b",
-                              m, ", D", ut, ");");
+                            o("D", ut, " = MFMA(", u, " < ", mp, " ? lds[", base, " + TSW((", u, " < ", mp, " ? ", u, " : 0), ", rr,
+                              ")] : (T)0, b", m, ", D", ut, ");");
                         else
-                            o("D", ut, " = MFMA(lds[", base, " + ", u, " * 16 + usub], b", m, ", D", ut, ");");
+                            o("D", ut, " = MFMA(lds[", base, " + TSW(", u, ", ", rr, ")], b", m, ", D", ut, ");");
                     }
                 }
                 o.ind--;
@@ -2867,7 +2908,7 @@ void emit_ucb_kernels(Out &o, const Plan &P)
       "const int* __restrict__ order, int group)");
     o("{");
     o.ind++;
-    o("__shared__ T lds[", uvc_lds_elems(P), "];  // T of the tile's 16 receivers, [p,k][u][row]");
+    o("__shared__ T lds[", uvc_lds_elems(P), "];  // T of the tile's 16 receivers, [p,k][u][row] (rows swizzled)");
     o("const long tile = blockIdx.x;");
     o("const int wv = threadIdx.x >> 6;");
     o("const int lane = threadIdx.x & 63;");

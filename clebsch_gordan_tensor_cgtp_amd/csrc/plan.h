@@ -81,6 +81,7 @@ struct Plan {
     int rbw_waves_per_eu = 2;       // backward in receiver order (cgtp_conv_rbw)
     int uvc_waves_per_eu = 2;       // uvw convolution
     int uvb_w_waves_per_eu = 1;     // uvw batched backward, dW kernel
+    int uvb_w_prefetch = 2;         // uvw batched backward, dW kernel: (path, k) blocks of gradients in flight
     int uvc_rpw = 4;                // uvw convolution: receivers per wave (16 / waves per workgroup)
     bool stream_hint = true;        // nontemporal loads/stores for once-touched per-edge rows
     bool bwd_sched_barrier = true;  // keep path blocks of the backward from interleaving

@@ -641,6 +641,7 @@ void schedule(Plan &P)
     P.uvc_waves_per_eu = 4 / P.uvc_rpw;  // the workgroup's 16 / rpw waves spread over 4 SIMDs
     if (const char *e = std::getenv("CGTP_UVW_WAVES")) P.uvw_waves_per_eu = std::max(1, std::atoi(e));
     if (const char *e = std::getenv("CGTP_UVB_W_WAVES")) P.uvb_w_waves_per_eu = std::max(1, std::atoi(e));
+    if (const char *e = std::getenv("CGTP_UVB_W_PREFETCH")) P.uvb_w_prefetch = std::max(1, std::min(8, std::atoi(e)));
     if (const char *e = std::getenv("CGTP_BWD_SCHED_BARRIER")) P.bwd_sched_barrier = std::atoi(e) != 0;
 }
 
