@@ -385,6 +385,11 @@ void emit_preamble(Out &o, const Plan &P)
     o("#define DOUT ", P.d_out);
     o("#define WROW ", P.w_numel, "L");
     o("typedef unsigned long size_t;");
+    // The wave's index in its workgroup, read from the first lane: the compiler then knows it is
+    // the same in every lane, so the receiver/sender/edge indices derived from it live in SGPRs
+    // and their row_ptr, col and y reads become scalar loads (fewer VGPRs, no per-lane address
+    // arithmetic).
+    o("#define WAVE_IN_BLOCK() ((int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6))");
     // per-edge rows read or written once (y, W, dW): streaming hint on the memory instructions
     if (P.stream_hint) {
         o("#define LD_STREAM(p) __builtin_nontemporal_load(p)");
@@ -496,6 +501,10 @@ void emit_fwd_group(Out &o, const Plan &P, int gi, bool rows, bool dbl = false, 
         o("const int enn = (e + 2 * stride < e1) ? e + 2 * stride : e1 - 1;");
         o("const int snn = col[enn];");
         emit_edge_loads(o, P, g, t, "n", "sn", "en", true, dbl, radial);
+        // keep the next edge's loads here, ahead of this edge's arithmetic: left alone the
+        // scheduler sinks them to the end of the iteration (fewer live registers), and each edge
+        // then waits for its own operands
+        if (P.fwd_sched_barrier) o("__builtin_amdgcn_sched_barrier(0);");
         if (radial) {
             // The Theta reads do not depend on the edge: left alone, the compiler hoists all
             // R * paths of them out of the loop and spills them.  An empty asm makes the base
@@ -587,7 +596,7 @@ void emit_fwd_kernel(Out &o, const Plan &P, bool rows, bool dbl = false, int spl
       "T* __restrict__ out, long nrows, long nwaves, const int* __restrict__ order)");
     o("{");
     o.ind++;
-    o("const long wave = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const long wave = (long)blockIdx.x * 4 + WAVE_IN_BLOCK();");
     o("const int lane = threadIdx.x & 63;");
     if (rows) {
         o("if (wave >= nwaves) return;");
@@ -1202,7 +1211,7 @@ void emit_tpb_kernel(Out &o, const Plan &P)
       "int group)");
     o("{");
     o.ind++;
-    o("const long blk = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const long blk = (long)blockIdx.x * 4 + WAVE_IN_BLOCK();");
     o("const int lane = threadIdx.x & 63;");
     o("if (blk >= nblocks) return;");
     o("switch (group) {");
@@ -1234,7 +1243,7 @@ void emit_bwd_kernel(Out &o, const Plan &P, bool dbl = false)
     o.ind++;
     o("__shared__ T red[", bwd_red_size(groups, P), "];  // partial dx of waves 1..3");
     o("const long s = blockIdx.x;");
-    o("const int wv = threadIdx.x >> 6;");
+    o("const int wv = WAVE_IN_BLOCK();");
     o("const int lane = threadIdx.x & 63;");
     o("if (s >= nnodes) return;");
     o("switch (group) {");
@@ -1585,7 +1594,7 @@ void emit_rbw_kernels(Out &o, const Plan &P)
       "T* __restrict__ dw, T* __restrict__ hb, long nrows, long e_lo, long e_hi, long kper, int group)");
     o("{");
     o.ind++;
-    o("const long blk = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const long blk = (long)blockIdx.x * 4 + WAVE_IN_BLOCK();");
     o("const int lane = threadIdx.x & 63;");
     o("if (e_lo + blk * kper >= e_hi) return;");
     o("switch (group) {");
@@ -1607,7 +1616,7 @@ void emit_rbw_kernels(Out &o, const Plan &P)
       "long e_hi, int first)");
     o("{");
     o.ind++;
-    o("const long s = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const long s = (long)blockIdx.x * 4 + WAVE_IN_BLOCK();");
     o("const int lane = threadIdx.x & 63;");
     o("if (s >= nnodes) return;");
     o("const int t0 = t_row_ptr[s], t1 = t_row_ptr[s + 1];");
@@ -1840,7 +1849,7 @@ void emit_uvw_kernel(Out &o, const Plan &P)
       "T* __restrict__ out, long nrows, long nblocks)");
     o("{");
     o.ind++;
-    o("const long wave = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const long wave = (long)blockIdx.x * 4 + WAVE_IN_BLOCK();");
     o("const int lane = threadIdx.x & 63;");
     const int tiles = uvw_out_tiles(P);
     if (tiles > 1) {
@@ -2129,7 +2138,7 @@ void emit_uvc_kernel(Out &o, const Plan &P)
     o.ind++;
     o("__shared__ T lds[", uvc_lds_elems(P), "];  // T of the tile's 16 receivers, [p,k][u][row] (rows swizzled)");
     o("const long tile = blockIdx.x;");
-    o("const int wv = threadIdx.x >> 6;");
+    o("const int wv = WAVE_IN_BLOCK();");
     o("const int lane = threadIdx.x & 63;");
     o("switch (group) {");
     for (int gi = 0; gi < (int)P.uvc_groups.size(); ++gi)
@@ -2154,7 +2163,7 @@ void emit_uvc_acc_kernel(Out &o, const Plan &P)
     o.ind++;
     o("__shared__ T lds[", uvc_lds_elems(P), "];  // T of the tile's 16 receivers, [p,k][u][row] (rows swizzled)");
     o("const long tile = blockIdx.x;");
-    o("const int wv = threadIdx.x >> 6;");
+    o("const int wv = WAVE_IN_BLOCK();");
     o("const int lane = threadIdx.x & 63;");
     o("switch (group) {");
     for (int gi = 0; gi < (int)P.uvc_groups.size(); ++gi)
@@ -2569,7 +2578,7 @@ void emit_reduce_chunks(Out &o)
     o.ind++;
     o("__shared__ T part[16 * 64];");
     o("const int lane = threadIdx.x & 63;");
-    o("const int wv = threadIdx.x >> 6;");
+    o("const int wv = WAVE_IN_BLOCK();");
     o("const long i = (long)blockIdx.x * 64 + lane;");
     o("const bool ok = i < WN;");
     o("const long per = (nchunks + 15) / 16;");
@@ -2638,7 +2647,7 @@ void emit_uvb_kernels(Out &o, const Plan &P)
     const int dsp = uvb_dy_stride(P);
     o("__shared__ T dyl[", 4 * 16 * dsp, "];  // per wave 16 dY rows of stride ", dsp);
     o("const long blk = blockIdx.x;");
-    o("const int wv = threadIdx.x >> 6;");
+    o("const int wv = WAVE_IN_BLOCK();");
     o("const int lane = threadIdx.x & 63;");
     o("for (int c = threadIdx.x; c < ", 4 * 16 * dsp, "; c += 256) dyl[c] = (T)0;");
     o("__syncthreads();");
@@ -2676,8 +2685,8 @@ void emit_uvb_kernels(Out &o, const Plan &P)
     o("{");
     o.ind++;
     o("__shared__ T tl[", 4 * 256, "];");
-    o("const long wave = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
-    o("const int wv = threadIdx.x >> 6;");
+    o("const long wave = (long)blockIdx.x * 4 + WAVE_IN_BLOCK();");
+    o("const int wv = WAVE_IN_BLOCK();");
     o("const int lane = threadIdx.x & 63;");
     o("if (wave >= nwaves) return;");
     o("const int group = (int)(wave / nchunks);");
@@ -2730,7 +2739,7 @@ void emit_ucb_g_kernel(Out &o, const Plan &P)
       "const T* __restrict__ g, T* __restrict__ G, long nrows, long nwaves)");
     o("{");
     o.ind++;
-    o("const long wave = ((long)blockIdx.x * 256 + threadIdx.x) >> 6;");
+    o("const long wave = (long)blockIdx.x * 4 + WAVE_IN_BLOCK();");
     o("const int lane = threadIdx.x & 63;");
     o("if (wave >= nwaves) return;");
     o("const long tile = wave / ", nitems, ";");
@@ -2910,7 +2919,7 @@ void emit_ucb_kernels(Out &o, const Plan &P)
     o.ind++;
     o("__shared__ T lds[", uvc_lds_elems(P), "];  // T of the tile's 16 receivers, [p,k][u][row] (rows swizzled)");
     o("const long tile = blockIdx.x;");
-    o("const int wv = threadIdx.x >> 6;");
+    o("const int wv = WAVE_IN_BLOCK();");
     o("const int lane = threadIdx.x & 63;");
     o("switch (group) {");
     for (int gi = 0; gi < (int)P.uvc_groups.size(); ++gi)
@@ -3040,7 +3049,7 @@ std::string generate_radial_source(const Plan &P, int R, const std::vector<Group
         o("__shared__ T thl[", radial_fwd_theta_words(P, R), "];  // Theta columns of the unit, [r][col]");
         o("const int task = (int)(blockIdx.x % ", P.fwd_tasks, ");");
         o("const int lane = threadIdx.x & 63;");
-        o("long n = (long)(blockIdx.x / ", P.fwd_tasks, ") * 4 + (threadIdx.x >> 6);");
+        o("long n = (long)(blockIdx.x / ", P.fwd_tasks, ") * 4 + WAVE_IN_BLOCK();");
         o("const bool live = n < nrows;");
         o("if (live && order) n = order[n];  // receiver schedule (heavy rows first), results unchanged");
         o("const int part = 0;");
@@ -3093,7 +3102,7 @@ std::string generate_radial_source(const Plan &P, int R, const std::vector<Group
     o("const long chunk = blockIdx.x;");
     o("const long c0 = chunk * spc;");
     o("const long c1 = c0 + spc < nnodes ? c0 + spc : nnodes;");
-    o("const int wv = threadIdx.x >> 6;");
+    o("const int wv = WAVE_IN_BLOCK();");
     o("const int lane = threadIdx.x & 63;");
     o("switch (group) {");
     for (int gi = 0; gi < (int)bwd_groups.size(); ++gi) {

@@ -85,6 +85,7 @@ struct Plan {
     int uvc_rpw = 4;                // uvw convolution: receivers per wave (16 / waves per workgroup)
     bool stream_hint = true;        // nontemporal loads/stores for once-touched per-edge rows
     bool bwd_sched_barrier = true;  // keep path blocks of the backward from interleaving
+    bool fwd_sched_barrier = false; // keep the receiver pass's next-edge loads ahead of its arithmetic
     bool rbw_sched_barrier = true;  // the same for the receiver-order backward, per path
     bool rbw_prefetch = false;      // receiver-order backward: sender ids two edges ahead, operands one ahead
     int bwd_prefetch = -1;          // -1: per group by register estimate; 0/1 forced

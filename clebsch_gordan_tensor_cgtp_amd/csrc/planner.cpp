@@ -643,6 +643,12 @@ void schedule(Plan &P)
     if (const char *e = std::getenv("CGTP_UVB_W_WAVES")) P.uvb_w_waves_per_eu = std::max(1, std::atoi(e));
     if (const char *e = std::getenv("CGTP_UVB_W_PREFETCH")) P.uvb_w_prefetch = std::max(1, std::min(8, std::atoi(e)));
     if (const char *e = std::getenv("CGTP_BWD_SCHED_BARRIER")) P.bwd_sched_barrier = std::atoi(e) != 0;
+    // Pinning the receiver pass's next-edge loads ahead of the arithmetic pays for plans split into
+    // several path groups, whose long per-edge arithmetic hides a whole load latency (MACE-like
+    // graph: fp32 4.27 -> 4.09 ms, fp64 9.52 -> 9.23 ms); single-group plans keep four waves per
+    // SIMD without it, and with it spill (NequIP-like graph: 107 -> 142 us).
+    P.fwd_sched_barrier = P.fwd_groups.size() > 1;
+    if (const char *e = std::getenv("CGTP_FWD_SCHED_BARRIER")) P.fwd_sched_barrier = std::atoi(e) != 0;
 }
 
 // Internal plan of the uvw convolution backward: the paths and CG blocks of P, each path
