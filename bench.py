@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "c2uvw", "c1big"])
+    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "c2uvw", "c1big", "c4wide"])
     ap.add_argument("--backward", action="store_true",
                     help="batched workloads: also time cgtp_tp_backward; uvw convolution: also cgtp_conv_backward_ws")
     ap.add_argument("--dtype", default="f32", choices=["f32", "f64"])

@@ -178,7 +178,11 @@ CONV_NEQUIP_UVW = ConvSpec("conv-uvw-N5000-E200k-32x(0e,1o,2e)-sh2", 5000, 200_0
 # A batched uvu product over as many rows as the streaming graph has nodes, with the NequIP-like
 # irreps (HBM-bound, unlike the 1,024-row batch that is launch-bound).
 TP_BIG = TPSpec("tp-uvu-B200k-32x(0e,1o,2e)-sh2", 200_000, _ladder(32, 2), 2, "uvu")
-EXTRA_WORKLOADS = {"c2uvw": CONV_NEQUIP_UVW, "c1big": TP_BIG}
+# A batched uvw product with multiplicities above 16 (32 channels in and out): its backward runs
+# through the uvw convolution's kernels on the identity graph.
+TP_WIDE_UVW = TPSpec("tp-uvw-B50000-32x(0e,1o,2e)-sh2", 50_000, _ladder(32, 2), 2, "uvw",
+                     "32x0e+32x1o+32x2e+32x1e+32x2o")
+EXTRA_WORKLOADS = {"c2uvw": CONV_NEQUIP_UVW, "c1big": TP_BIG, "c4wide": TP_WIDE_UVW}
 
 
 def conv_graph(spec: ConvSpec, seed: int = 0):
