@@ -389,7 +389,10 @@ void emit_preamble(Out &o, const Plan &P)
     // the same in every lane, so the receiver/sender/edge indices derived from it live in SGPRs
     // and their row_ptr, col and y reads become scalar loads (fewer VGPRs, no per-lane address
     // arithmetic).
-    o("#define WAVE_IN_BLOCK() ((int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6))");
+    if (P.scalar_wave)
+        o("#define WAVE_IN_BLOCK() ((int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6))");
+    else
+        o("#define WAVE_IN_BLOCK() ((int)(threadIdx.x >> 6))");
     // per-edge rows read or written once (y, W, dW): streaming hint on the memory instructions
     if (P.stream_hint) {
         o("#define LD_STREAM(p) __builtin_nontemporal_load(p)");

@@ -84,6 +84,7 @@ struct Plan {
     int uvb_w_prefetch = 2;         // uvw batched backward, dW kernel: (path, k) blocks of gradients in flight
     int uvc_rpw = 4;                // uvw convolution: receivers per wave (16 / waves per workgroup)
     bool stream_hint = true;        // nontemporal loads/stores for once-touched per-edge rows
+    bool scalar_wave = true;        // wave index read from the first lane (uniform, SGPR-held)
     bool bwd_sched_barrier = true;  // keep path blocks of the backward from interleaving
     bool fwd_sched_barrier = false; // keep the receiver pass's next-edge loads ahead of its arithmetic
     bool rbw_sched_barrier = true;  // the same for the receiver-order backward, per path

@@ -335,6 +335,7 @@ void schedule(Plan &P)
     if (const char *e = std::getenv("CGTP_BWD_PREFETCH")) P.bwd_prefetch = std::atoi(e);
     if (const char *e = std::getenv("CGTP_FWD_SPLIT_INPUTS")) P.fwd_split_inputs = std::atoi(e) != 0;
     if (const char *e = std::getenv("CGTP_NT")) P.stream_hint = std::atoi(e) != 0;
+    if (const char *e = std::getenv("CGTP_SCALAR_WAVE")) P.scalar_wave = std::atoi(e) != 0;
     const int word = P.dtype == CGTP_F64 ? 2 : 1;
     // 32-bit registers per lane for the forward accumulators (CGTP_FWD_BUDGET overrides, tuning).
     // An fp64 plan that needs more than two groups at 64 registers already runs at two waves per
