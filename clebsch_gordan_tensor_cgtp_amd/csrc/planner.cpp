@@ -574,9 +574,12 @@ void schedule(Plan &P)
         auto make_groups = [&](bool dbl, std::vector<Group> &groups, int &waves) {
             // split budget of the register estimate (measured on the MACE-like plan, first-order
             // backward: fp32 at 140 gives six groups that need 232 VGPRs and no spill, 20.75 ms,
-            // against 256 VGPRs, a 128-byte spill and 21.8 ms at 168; fp64 at 140 took 56.8
-            // against 47.2 ms at 168).  The double backward's sender pass keeps 168.
-            const int split_budget = getenv_int("CGTP_BWD_BUDGET", dbl || P.dtype == CGTP_F64 ? 168 : 140);
+            // against 256 VGPRs, a 128-byte spill and 21.8 ms at 168, and five spilling groups
+            // above 176; fp64 at 200 gives 11 groups at 247 VGPRs, two waves per SIMD and
+            // 38.8 ms, against 17 groups and 46.6 ms at 168, 56.8 ms at 140, and one wave per SIMD
+            // from 216 on (8 groups at 230: 48.1 ms)).  The double backward's sender pass keeps 168.
+            const int split_budget =
+                getenv_int("CGTP_BWD_BUDGET", dbl ? 168 : P.dtype == CGTP_F64 ? 200 : 140);
             const int one_group_limit = 200;
             groups.clear();
             std::vector<int> all_paths;
