@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--backward-schedule", default="sender", choices=["receiver", "sender"],
                     help="uvu convolution backward: receiver order with a bounded workspace "
                          "(cgtp_conv_backward_receiver) or sender order (cgtp_conv_backward)")
+    ap.add_argument("--receiver-workspace-gib", type=float, default=RECEIVER_WORKSPACE_BYTES / 2**30,
+                    help="workspace of the receiver-order backward (GiB; the call splits the edges into "
+                         "as many ranges as it needs)")
     ap.add_argument("--natural-order", action="store_true",
                     help="start receivers in node order instead of the heavy-first schedule")
     ap.add_argument("--radial", type=int, default=0, metavar="R",
@@ -891,7 +894,8 @@ def main():
     ws = None
     if receiver:
         full, least = cg.conv_backward_receiver_workspace_size(plan, N, E)
-        ws = torch.empty(max(least, min(full, RECEIVER_WORKSPACE_BYTES)), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(least, min(full, int(a.receiver_workspace_gib * 2**30))), dtype=torch.uint8,
+                         device=device)
         row_bytes = plan.d_x * es
         ranges = -(-E // (ws.numel() // row_bytes)) if E else 0
 
