@@ -2214,11 +2214,6 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
     o("const bool live = row < nrows;");
     o("const long rr = live ? row : nrows - 1;  // rows past the end read row nrows-1 and store nothing");
     o("T* dyw = dyl + wv * ", 16 * uvb_dy_stride(P), ";  // this wave's dY rows (zeroed by the kernel)");
-    for (int b : t.i2) {
-        int off = 0;
-        for (int bb = 0; bb < b; ++bb) off += P.sh[bb].dim();
-        for (int j = 0; j < n_of(P.sh[b].l); ++j) o("const T y", b, "_", j, " = y[(size_t)rr * DSH + ", off + j, "];");
-    }
     for (int v = 0; v < 4; ++v) {
         const std::string u = uvb_u(f64, v);
         for (int i = 0; i < n1; ++i) {
@@ -2282,6 +2277,13 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
         const int n2 = n_of(p.l2);
         o("{");
         o.ind++;
+        // this path's SH block, read here (an L1 hit after the first path of the row block):
+        // holding every block for the whole group took 64 registers at l <= 7 and spilled (52 and
+        // 148 bytes per lane for l1 = 6, 7; 0 and 20 this way, same time).  The opaque zero
+        // offset keeps the compiler from merging these reads across paths.
+        o("int zo = 0;");
+        o("asm volatile(\"\" : \"+v\"(zo));");
+        for (int j = 0; j < n2; ++j) o("const T y", p.i2, "_", j, " = y[(size_t)rr * DSH + zo + ", p.b + j, "];");
         for (int j = 0; j < n2; ++j) o("T h", j, " = (T)0;");
         std::map<int, std::map<int, std::vector<const Nonzero *>>> byki;  // k -> i -> nonzeros
         for (const Nonzero &z : p.nz) byki[z.k][z.i].push_back(&z);
