@@ -1721,6 +1721,29 @@ void emit_uvw_group(Out &o, const Plan &P, int gi)
     // paths grouped by input block: that block's x is loaded for all chunks once
     std::map<int, std::vector<int>> by_i1;
     for (int pi : g.paths) by_i1[P.paths[pi].i1].push_back(pi);
+    // A operands W_p[u][w] (u = 4c + lane/16, w = lane % 16) run one path ahead in two register
+    // sets: path t's are loaded when path t - 1 starts (unconditionally, from a clamped element;
+    // the mask is applied where they are used), so that their latency is covered by a path's work
+    std::vector<int> order;
+    for (auto &kv : by_i1)
+        for (int pi : kv.second) order.push_back(pi);
+    const std::string wc = tiled ? "wcol" : "(lane & 15)";
+    auto wmask_of = [&](const Path &p, int c) { return 4 * c + 3 >= p.mul_in || p.mul_out < 16 || tiled; };
+    auto load_w = [&](int t) {
+        const Path &p = P.paths[order[t]];
+        for (int c = 0; c < chunks; ++c) {
+            const std::string u = "(" + std::to_string(4 * c) + " + usub)";
+            if (wmask_of(p, c))
+                o("wv", t % 2, "_", c, " = w[", p.w_off, " + (", u, " < ", p.mul_in, " ? ", u, " : 0) * ", p.mul_out, " + (", wc,
+                  " < ", p.mul_out, " ? ", wc, " : 0)];");
+            else
+                o("wv", t % 2, "_", c, " = w[", p.w_off, " + ", u, " * ", p.mul_out, " + (lane & 15)];");
+        }
+    };
+    for (int set = 0; set < 2; ++set)
+        for (int c = 0; c < chunks; ++c) o("T wv", set, "_", c, " = (T)0;");
+    if (!order.empty()) load_w(0);
+    int tpath = 0;
     for (auto &kv : by_i1) {
         const int b = kv.first;
         const Irrep &ir = P.ins[b];
@@ -1743,20 +1766,20 @@ void emit_uvw_group(Out &o, const Plan &P, int gi)
         }
         for (int pi : kv.second) {
             const Path &p = P.paths[pi];
+            const int tp = tpath++;
             o("{");
             o.ind++;
-            // A operands: W_p[u][w] with u = 4c + lane/16, w = lane % 16 (zero outside the block)
+            // this path's A operands (zero outside the block), then the next path's loads
             for (int c = 0; c < chunks; ++c) {
-                std::string u = "(" + std::to_string(4 * c) + " + usub)";
-                const bool wmask = 4 * c + 3 >= p.mul_in || p.mul_out < 16 || tiled;
-                const std::string wc = tiled ? "wcol" : "(lane & 15)";
-                if (wmask) {
-                    o("const bool wok", c, " = ", u, " < ", p.mul_in, " && ", wc, " < ", p.mul_out, ";");
-                    o("const T wv", c, " = w[", p.w_off, " + (wok", c, " ? ", u, " * ", p.mul_out, " + ", wc, " : 0)];");
-                    o("const T wa", c, " = wok", c, " ? wv", c, " : (T)0;");
-                } else {
-                    o("const T wa", c, " = w[", p.w_off, " + ", u, " * ", p.mul_out, " + (lane & 15)];");
-                }
+                const std::string u = "(" + std::to_string(4 * c) + " + usub)";
+                if (wmask_of(p, c))
+                    o("const T wa", c, " = (", u, " < ", p.mul_in, " && ", wc, " < ", p.mul_out, ") ? wv", tp % 2, "_", c, " : (T)0;");
+                else
+                    o("const T wa", c, " = wv", tp % 2, "_", c, ";");
+            }
+            if (tp + 1 < (int)order.size()) {
+                load_w(tp + 1);
+                o("__builtin_amdgcn_sched_barrier(0);");
             }
             std::map<int, std::map<int, std::vector<const Nonzero *>>> byki;  // k -> i -> nonzeros
             for (const Nonzero &z : p.nz) byki[z.k][z.i].push_back(&z);
@@ -2224,8 +2247,10 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
     }
     // The (path, k) blocks in order, software-pipelined: block b issues the MFMAs of block b + 1's
     // G (independent of its own) before its VALU work on G_b, so the MFMA chain runs under that
-    // work instead of stalling it; gradient values are loaded two blocks ahead (three register
-    // sets) and the W operands one path ahead (two sets, by path parity).
+    // work instead of stalling it; gradient values are loaded PF blocks ahead (a ring of PF + 1
+    // register sets) and the W operands one path ahead (two sets, by path parity).  Loads are
+    // unconditional (clamped addresses) and masked where they are used: a load under a branch,
+    // or a select right after it, made the compiler wait for it at once.
     std::vector<std::pair<int, int>> blocks;  // (index into g.paths, k)
     for (int q = 0; q < (int)g.paths.size(); ++q) {
         std::set<int> ks;
@@ -2233,33 +2258,40 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
         for (int k : ks) blocks.push_back({q, k});
     }
     const int nb = (int)blocks.size();
+    const int PF = std::max(1, P.uvb_xy_prefetch), RS = PF + 1;
     auto wch_of = [&](int q) { return (P.paths[g.paths[q]].mul_out + 3) / 4; };
     auto load_g = [&](int bi) {
         const Path &p = P.paths[g.paths[blocks[bi].first]];
         const int k = blocks[bi].second, n3 = n_of(p.l3);
-        for (int c = 0; c < wch_of(blocks[bi].first); ++c)
-            o("gs", bi % 3, "_", c, " = ", 4 * c, " + usub < ", p.mul_out, " ? g[(size_t)rr * DOUT + ", p.o, " + (", 4 * c,
-              " + usub < ", p.mul_out, " ? ", 4 * c, " + usub : 0) * ", n3, " + ", k, "] : (T)0;");
+        for (int c = 0; c < wch_of(blocks[bi].first); ++c) {
+            const std::string wv = 4 * c + 3 < p.mul_out ? std::to_string(4 * c) + " + usub"
+                                                          : "(" + std::to_string(4 * c) + " + usub < " + std::to_string(p.mul_out) +
+                                                                " ? " + std::to_string(4 * c) + " + usub : 0)";
+            o("gs", bi % RS, "_", c, " = g[(size_t)rr * DOUT + ", p.o, " + (", wv, ") * ", n3, " + ", k, "];");
+        }
     };
-    // A operands of G: W_p[u = lane % 16][w = 4c + lane / 16]
+    // A operands of G: W_p[u = lane % 16][w = 4c + lane / 16] (rows and columns clamped)
     auto load_w = [&](int q) {
         const Path &p = P.paths[g.paths[q]];
-        for (int c = 0; c < wch_of(q); ++c) {
-            o("{");
-            o.ind++;
-            o("const bool wok = rl < ", p.mul_in, " && ", 4 * c, " + usub < ", p.mul_out, ";");
-            o("const T wv = w[", p.w_off, " + (wok ? rl * ", p.mul_out, " + ", 4 * c, " + usub : 0)];");
-            o("wa", q % 2, "_", c, " = wok ? wv : (T)0;");
-            o.ind--;
-            o("}");
-        }
+        for (int c = 0; c < wch_of(q); ++c)
+            o("wa", q % 2, "_", c, " = w[", p.w_off, " + (rl < ", p.mul_in, " ? rl : 0) * ", p.mul_out, " + (", 4 * c, " + usub < ",
+              p.mul_out, " ? ", 4 * c, " + usub : 0)];");
     };
     auto issue_g = [&](int bi) {
         const int q = blocks[bi].first;
+        const Path &p = P.paths[g.paths[q]];
         o("G", bi, " = (V4){0, 0, 0, 0};");
-        for (int c = 0; c < wch_of(q); ++c) o("G", bi, " = MFMA(wa", q % 2, "_", c, ", gs", bi % 3, "_", c, ", G", bi, ");");
+        for (int c = 0; c < wch_of(q); ++c) {
+            std::string wa = "wa" + std::to_string(q % 2) + "_" + std::to_string(c);
+            std::string gs = "gs" + std::to_string(bi % RS) + "_" + std::to_string(c);
+            const std::string wok = "(" + std::to_string(4 * c) + " + usub < " + std::to_string(p.mul_out) + ")";
+            if (p.mul_in < 16 || 4 * c + 3 >= p.mul_out)
+                wa = "((rl < " + std::to_string(p.mul_in) + " && " + wok + ") ? " + wa + " : (T)0)";
+            if (4 * c + 3 >= p.mul_out) gs = "(" + wok + " ? " + gs + " : (T)0)";
+            o("G", bi, " = MFMA(", wa, ", ", gs, ", G", bi, ");");
+        }
     };
-    for (int set = 0; set < 3; ++set)
+    for (int set = 0; set < RS; ++set)
         for (int c = 0; c < 4; ++c) o("T gs", set, "_", c, " = (T)0;");
     for (int set = 0; set < 2; ++set)
         for (int c = 0; c < 4; ++c) o("T wa", set, "_", c, " = (T)0;");
@@ -2267,8 +2299,7 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
     if (nb > 0) {
         load_w(0);
         if (g.paths.size() > 1) load_w(1);
-        load_g(0);
-        if (nb > 1) load_g(1);
+        for (int b = 0; b < std::min(PF, nb); ++b) load_g(b);
         issue_g(0);
     }
     int bi = 0;
@@ -2290,7 +2321,9 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
         for (auto &kk : byki) {
             o("{");
             o.ind++;
-            if (bi + 2 < nb) load_g(bi + 2);
+            if (bi + PF < nb) load_g(bi + PF);
+            // the loads first: left alone the scheduler moves them below this block's MFMAs
+            o("__builtin_amdgcn_sched_barrier(0);");
             if (bi + 1 < nb) issue_g(bi + 1);
             for (auto &ii : kk.second) {
                 const int i = ii.first;
@@ -2403,11 +2436,19 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
         const Irrep &ir = P.ins[i1];
         const int n1 = n_of(ir.l);
         const int a = P.paths[by_i1[i1][0]].a;
-        // x in the forward's layout: lane holds u = 4c + lane / 16
+        // x in the forward's layout: lane holds u = 4c + lane / 16.  Every load of this kernel is
+        // unconditional, from an element that exists (rows and channels clamped), and the
+        // masking waits for the use: a load under a branch made the compiler's wait counting
+        // fall back to waiting for every load in flight, and a select right after the load
+        // waits for it there; either defeated the prefetching below.
         for (int c = 0; c < 4; ++c)
-            for (int i = 0; i < n1; ++i)
-                o("xp", c, "_", i, " = ", 4 * c, " + usub < ", ir.mul, " ? x[(size_t)", rrx, " * DX + ", a, " + (", 4 * c,
-                  " + usub < ", ir.mul, " ? ", 4 * c, " + usub : 0) * ", n1, " + ", i, "] : (T)0;");
+            for (int i = 0; i < n1; ++i) {
+                if (4 * c + 3 < ir.mul)
+                    o("xp", c, "_", i, " = x[(size_t)", rrx, " * DX + ", a, " + (", 4 * c, " + usub) * ", n1, " + ", i, "];");
+                else
+                    o("xp", c, "_", i, " = x[(size_t)", rrx, " * DX + ", a, " + (", 4 * c, " + usub < ", ir.mul, " ? ", 4 * c,
+                      " + usub : 0) * ", n1, " + ", i, "];");
+            }
     };
     // the (path, k) blocks in emission order; each block loads the next one's B operands (the
     // gradient values of its four row groups) before its own work, so that their latency is
@@ -2428,8 +2469,8 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
             o("{");
             o.ind++;
             o("const long br = ", rb, " * 16 + ", 4 * m, " + usub;");
-            o("const bool bok = br < nrows && rl < ", p.mul_out, ";");
-            o("gp", set, "_", m, " = bok ? g[(size_t)br * DOUT + ", p.o, " + rl * ", n3, " + ", k, "] : (T)0;");
+            o("gp", set, "_", m, " = g[(size_t)(br < nrows ? br : nrows - 1) * DOUT + ", p.o, " + (rl < ", p.mul_out,
+              " ? rl : 0) * ", n3, " + ", k, "];");
             o.ind--;
             o("}");
         }
@@ -2447,11 +2488,7 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
         if (tgt < nbk) {
             load_g((size_t)tgt, "blk", tgt % D);
         } else if (tgt >= padded) {
-            o("if (more) {");
-            o.ind++;
-            load_g((size_t)(tgt - padded), "(blk + 1)", tgt % D);
-            o.ind--;
-            o("}");
+            load_g((size_t)(tgt - padded), "(blk + 1)", tgt % D);  // past the chunk: clamped, unused
         }
     };
     int n1max = 1;
@@ -2481,11 +2518,7 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
     o("const long rrx = more ? (rowx < nrows ? rowx : nrows - 1) : rr;");
     for (int b : t.i2)
         for (int j = 0; j < n_of(P.sh[b].l); ++j) o("const T y", b, "_", j, " = yp", b, "_", j, ";");
-    o("if (more) {");
-    o.ind++;
-    y_loads("yp", "rrx");
-    o.ind--;
-    o("}");
+    y_loads("yp", "rrx");  // rrx = rr after the last row block: loaded again, unused
     size_t bidx = 0;
     size_t sec = 0;
     for (auto &kv : by_i1) {
@@ -2494,16 +2527,17 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
         o("{");
         o.ind++;
         for (int c = 0; c < 4; ++c)
-            for (int i = 0; i < n1; ++i) o("const T x", c, "_", i, " = xp", c, "_", i, ";");
+            for (int i = 0; i < n1; ++i) {
+                if (4 * c + 3 < ir.mul)
+                    o("const T x", c, "_", i, " = xp", c, "_", i, ";");
+                else
+                    o("const T x", c, "_", i, " = ", 4 * c, " + usub < ", ir.mul, " ? xp", c, "_", i, " : (T)0;");
+            }
         // the next input block's x: this row block's, or the next row block's first
         if (++sec < by_i1.size()) {
             x_loads(std::next(by_i1.begin(), (long)sec)->first, "rr");
         } else {
-            o("if (more) {");
-            o.ind++;
             x_loads(by_i1.begin()->first, "rrx");
-            o.ind--;
-            o("}");
         }
         for (int pi : kv.second) {
             const Path &p = P.paths[pi];
@@ -2512,7 +2546,11 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
             for (auto &kk : byki) {
                 o("{");
                 o.ind++;
-                for (int m = 0; m < 4; ++m) o("const T gc", m, " = gp", (int)bidx % D, "_", m, ";");
+                // gradient values of rows past the end and of channels past mul_out are zero
+                const bool wmask = P.paths[pi].mul_out < 16;
+                for (int m = 0; m < 4; ++m)
+                    o("const T gc", m, " = (blk * 16 + ", 4 * m, " + usub < nrows", wmask ? " && rl < " + std::to_string(P.paths[pi].mul_out) : std::string(),
+                      ") ? gp", (int)bidx % D, "_", m, " : (T)0;");
                 ahead((int)bidx);
                 ++bidx;
                 for (auto &ii : kk.second) {
