@@ -1993,6 +1993,9 @@ void emit_uvc_phase_a(Out &o, const Plan &P, const Group &g, std::map<int, int> 
     o("const int enn = (e + ", 2 * g.es, " < e1) ? e + ", 2 * g.es, " : e1 - 1;");
     o("const int snn = col[enn];");
     loads("n", "sn", "en", true);
+    // keep the next edge's loads ahead of this edge's arithmetic (left alone, the scheduler sinks
+    // them to the end of the iteration and every edge waits for its own operands)
+    if (P.uvc_sched_barrier) o("__builtin_amdgcn_sched_barrier(0);");
     for (auto &pr : pairs_of(P, g.paths)) {
         int i1 = pr.first.first, i2 = pr.first.second;
         std::set<std::pair<int, int>> used;

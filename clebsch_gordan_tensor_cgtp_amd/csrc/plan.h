@@ -88,6 +88,7 @@ struct Plan {
     bool scalar_wave = true;        // wave index read from the first lane (uniform, SGPR-held)
     bool bwd_sched_barrier = true;  // keep path blocks of the backward from interleaving
     bool fwd_sched_barrier = false; // keep the receiver pass's next-edge loads ahead of its arithmetic
+    bool uvc_sched_barrier = true;  // the same in the uvw convolution's edge stream
     bool rbw_sched_barrier = true;  // the same for the receiver-order backward, per path
     bool rbw_prefetch = false;      // receiver-order backward: sender ids two edges ahead, operands one ahead
     int bwd_prefetch = -1;          // -1: per group by register estimate; 0/1 forced

@@ -654,6 +654,7 @@ void schedule(Plan &P)
     // SIMD without it, and with it spill (NequIP-like graph: 107 -> 142 us).
     P.fwd_sched_barrier = P.fwd_groups.size() > 1;
     if (const char *e = std::getenv("CGTP_FWD_SCHED_BARRIER")) P.fwd_sched_barrier = std::atoi(e) != 0;
+    if (const char *e = std::getenv("CGTP_UVC_SCHED_BARRIER")) P.uvc_sched_barrier = std::atoi(e) != 0;
 }
 
 // Internal plan of the uvw convolution backward: the paths and CG blocks of P, each path
