@@ -673,6 +673,17 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
     const Group &g = groups[gi];
     const bool f64 = P.dtype == CGTP_F64;
     const bool pf = g.prefetch && !rowmode;
+    // Rolling prefetch (first-order pass): an operand's next-edge value is loaded into its register
+    // right after the current edge's last use of it (a path's W after that path, a gradient or SH
+    // block after the last path reading it), so the next edge's loads stream in while this edge's
+    // later paths compute.  Registers are reused rather than doubled, but every operand now lives
+    // across the loop's back edge, which raises the count (it pays only for split plans).
+    const bool roll = P.bwd_rolling && !pf && !rowmode && !dbl && !radial;
+    std::map<int, int> last_of_slot, last_of_i2;  // operand block -> last path (emission order) using it
+    for (int pi : g.paths) {
+        last_of_slot[P.paths[pi].slot] = pi;
+        last_of_i2[P.paths[pi].i2] = pi;
+    }
     Touch t = touched(P, g.paths);
     // first group (in launch order) touching each input / SH block
     auto first_i1 = [&](int b) {
@@ -831,14 +842,14 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
     o("int e = t_edge[t], n = t_dst[t];");
     o("int tn = (t + stride < t1) ? t + stride : t;");
     o("int en = t_edge[tn], nn = t_dst[tn];");
-    if (pf) edge_loads("", "e", "n", true);
+    if (pf || roll) edge_loads("", "e", "n", true);
     o("for (; t < t1; t += stride) {");
     o.ind++;
     o("const int tnn = (t + 2 * stride < t1) ? t + 2 * stride : tn;");
     o("const int enn = t_edge[tnn], nnn = t_dst[tnn];");
     if (pf)
         edge_loads("n", "en", "nn", true);
-    else
+    else if (!roll)
         edge_loads("", "e", "n", true);
     }
     for (int b : yb)
@@ -945,6 +956,43 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
                 o("d", p.i1, "_", kv.first, " = FMA(w", pi, ", fx", kv.first, ", d", p.i1, "_", kv.first, ");");
             for (auto &kv : cols)
                 o("h", p.i2, "_", kv.first, " = FMA(w", pi, ", fy", kv.first, ", h", p.i2, "_", kv.first, ");");
+        }
+        if (roll) {
+            // this edge is done with these operands: load the next edge's into their registers.
+            // Barriers on both sides keep the loads after the last uses (so the registers are
+            // reused) and ahead of the next path's work.
+            if (P.bwd_rolling > 1) o("__builtin_amdgcn_sched_barrier(0);");
+            bool any = false;
+            if (!P.unit_weights) {
+                std::string wa = "LD_STREAM(&w[(size_t)en * WROW + " + std::to_string(p.w_off) + " + u])";
+                if (needs_mask(p.mul_in, g))
+                    o("w", pi, " = (u < ", p.mul_in, ") ? ", wa, " : (T)0;");
+                else
+                    o("w", pi, " = ", wa, ";");
+                any = true;
+            }
+            if (last_of_slot[p.slot] == pi) {
+                const Irrep &ir = P.out[p.slot];
+                int off = 0;
+                for (int qq = 0; qq < p.slot; ++qq) off += P.out[qq].dim();
+                for (int k = 0; k < n_of(ir.l); ++k) {
+                    std::string ga = "g[(size_t)nn * DOUT + " + std::to_string(off) + " + u * " + std::to_string(n_of(ir.l)) + " + " +
+                                     std::to_string(k) + "]";
+                    if (needs_mask(ir.mul, g))
+                        o("g", p.slot, "_", k, " = (u < ", ir.mul, ") ? ", ga, " : (T)0;");
+                    else
+                        o("g", p.slot, "_", k, " = ", ga, ";");
+                }
+                any = true;
+            }
+            if (last_of_i2[p.i2] == pi) {
+                int off = 0;
+                for (int bb = 0; bb < p.i2; ++bb) off += P.sh[bb].dim();
+                for (int j = 0; j < n_of(P.sh[p.i2].l); ++j)
+                    o("y", p.i2, "_", j, " = LD_STREAM(&y[(size_t)en * DSH + ", off + j, "]);");
+                any = true;
+            }
+            if (any && P.bwd_rolling > 1) o("__builtin_amdgcn_sched_barrier(0);");
         }
         o.ind--;
         o("}");

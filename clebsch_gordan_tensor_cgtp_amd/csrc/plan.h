@@ -87,6 +87,7 @@ struct Plan {
     bool stream_hint = true;        // nontemporal loads/stores for once-touched per-edge rows
     bool scalar_wave = true;        // wave index read from the first lane (uniform, SGPR-held)
     bool bwd_sched_barrier = true;  // keep path blocks of the backward from interleaving
+    int bwd_rolling = 0;            // sender pass: next edge's operands loaded as this edge frees them (2: pinned by barriers)
     bool fwd_sched_barrier = false; // keep the receiver pass's next-edge loads ahead of its arithmetic
     bool uvc_sched_barrier = true;  // the same in the uvw convolution's edge stream
     bool rbw_sched_barrier = true;  // the same for the receiver-order backward, per path
