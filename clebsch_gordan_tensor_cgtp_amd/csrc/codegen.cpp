@@ -2465,7 +2465,11 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
     o("const int usub = lane >> 4;");
     // this wave's transpose tile [row][u], u XOR row inside each row: the write (16 rows x 4 u) and
     // the read (4 rows x 16 u) each touch distinct banks (rows padded to 17 left 2-way conflicts)
-    o("T* tw = tl + wv * 256;");
+    // With the pipeline on, two tiles per wave: block b writes its t into tile b % 2 and, at its
+    // start, reads the tile block b - 1 wrote, whose MFMAs it issues after its own VALU work, so
+    // that the LDS round trip and the MFMA chain run under that work instead of stalling the wave.
+    const bool pipe = P.uvb_w_pipeline;
+    o("T* tw = tl + wv * ", pipe ? 512 : 256, ";");
     for (int pi : g.paths) o("V4 D", pi, " = {0, 0, 0, 0};");
     o("const long b0 = chunk * bpc;");
     o("const long b1 = b0 + bpc < nblocks ? b0 + bpc : nblocks;");
@@ -2550,6 +2554,9 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
         for (int i = 0; i < n1max; ++i) o("T xp", c, "_", i, " = (T)0;");
     for (int set = 0; set < D; ++set)
         for (int m = 0; m < 4; ++m) o("T gp", set, "_", m, " = (T)0;");
+    if (pipe)
+        for (int par = 0; par < 2; ++par)
+            for (int m = 0; m < 4; ++m) o("T gq", par, "_", m, " = (T)0;");
     o("if (b0 < b1) {");
     o.ind++;
     o("const long row0 = b0 * 16 + rl;");
@@ -2572,6 +2579,15 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
     y_loads("yp", "rrx");  // rrx = rr after the last row block: loaded again, unused
     size_t bidx = 0;
     size_t sec = 0;
+    int prev_pi = -1, par = 0;  // pipeline: the block whose MFMAs are pending, and this block's tile
+    // MFMAs of the pending block: A = t[row = 4m + lane/16][u = lane%16] from its tile
+    auto pending_mfma = [&](const std::string &ta) {
+        for (int m = 0; m < 4; ++m)
+            o("D", prev_pi, " = MFMA(", ta, m, ", gq", par ^ 1, "_", m, ", D", prev_pi, ");");
+    };
+    auto tile_read = [&](int tile, int m) {
+        return "tw[" + std::to_string(tile * 256 + 64 * m) + " + usub * 16 + (rl ^ (" + std::to_string(4 * m) + " + usub))]";
+    };
     for (auto &kv : by_i1) {
         const Irrep &ir = P.ins[kv.first];
         const int n1 = n_of(ir.l);
@@ -2599,9 +2615,17 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
                 o.ind++;
                 // gradient values of rows past the end and of channels past mul_out are zero
                 const bool wmask = P.paths[pi].mul_out < 16;
+                if (pipe) {
+                    // the pending block's t, read before this block's work (pinned here)
+                    o("WAVE_SYNC();");
+                    if (prev_pi >= 0) {
+                        for (int m = 0; m < 4; ++m) o("const T ta", m, " = ", tile_read(par ^ 1, m), ";");
+                        o("__builtin_amdgcn_sched_barrier(0);");
+                    }
+                }
                 for (int m = 0; m < 4; ++m)
-                    o("const T gc", m, " = (blk * 16 + ", 4 * m, " + usub < nrows", wmask ? " && rl < " + std::to_string(P.paths[pi].mul_out) : std::string(),
-                      ") ? gp", (int)bidx % D, "_", m, " : (T)0;");
+                    o(pipe ? "gq" + std::to_string(par) + "_" : std::string("const T gc"), m, " = (blk * 16 + ", 4 * m, " + usub < nrows",
+                      wmask ? " && rl < " + std::to_string(P.paths[pi].mul_out) : std::string(), ") ? gp", (int)bidx % D, "_", m, " : (T)0;");
                 ahead((int)bidx);
                 ++bidx;
                 for (auto &ii : kk.second) {
@@ -2615,7 +2639,7 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
                     }
                     o("const T A", ii.first, " = ", e.str(), ";");
                 }
-                o("WAVE_SYNC();");
+                if (!pipe) o("WAVE_SYNC();");
                 for (int c = 0; c < 4; ++c) {
                     std::ostringstream e;
                     bool first = true;
@@ -2629,12 +2653,17 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
                             e.str(f.str());
                         }
                     }
-                    o("tw[rl * 16 + ((", 4 * c, " + usub) ^ rl)] = live ? ", e.str(), " : (T)0;");
+                    o("tw[", pipe ? par * 256 : 0, " + rl * 16 + ((", 4 * c, " + usub) ^ rl)] = live ? ", e.str(), " : (T)0;");
                 }
-                o("WAVE_SYNC();");
-                // rows are the MFMA K dimension: A = t[row = 4m + lane/16][u = lane%16], B = g[row][w = lane%16][k]
-                for (int m = 0; m < 4; ++m)
-                    o("D", pi, " = MFMA(tw[(", 4 * m, " + usub) * 16 + (rl ^ (", 4 * m, " + usub))], gc", m, ", D", pi, ");");
+                if (pipe) {
+                    if (prev_pi >= 0) pending_mfma("ta");
+                    prev_pi = pi;
+                    par ^= 1;
+                } else {
+                    o("WAVE_SYNC();");
+                    // rows are the MFMA K dimension: A = t[row = 4m + lane/16][u = lane%16], B = g[row][w = lane%16][k]
+                    for (int m = 0; m < 4; ++m) o("D", pi, " = MFMA(", tile_read(0, m), ", gc", m, ", D", pi, ");");
+                }
                 o("__builtin_amdgcn_sched_barrier(0);");
                 o.ind--;
                 o("}");
@@ -2644,6 +2673,17 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
         o("}");
     }
     for (int pos = nbk; pos < padded; ++pos) ahead(pos);  // load-only steps of the padding
+    if (pipe && prev_pi >= 0) {
+        // the row block's last block
+        o("{");
+        o.ind++;
+        o("WAVE_SYNC();");
+        for (int m = 0; m < 4; ++m) o("const T ta", m, " = ", tile_read(par ^ 1, m), ";");
+        pending_mfma("ta");
+        o("WAVE_SYNC();");
+        o.ind--;
+        o("}");
+    }
     o.ind--;
     o("}");  // row blocks
     // lane holds D[u = U(v)][w = lane % 16]
@@ -2778,7 +2818,7 @@ void emit_uvb_kernels(Out &o, const Plan &P)
       "long nchunks, long nwaves)");
     o("{");
     o.ind++;
-    o("__shared__ T tl[", 4 * 256, "];");
+    o("__shared__ T tl[", 4 * (P.uvb_w_pipeline ? 512 : 256), "];");
     o("const long wave = (long)blockIdx.x * 4 + WAVE_IN_BLOCK();");
     o("const int wv = WAVE_IN_BLOCK();");
     o("const int lane = threadIdx.x & 63;");

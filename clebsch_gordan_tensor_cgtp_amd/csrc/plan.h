@@ -82,6 +82,7 @@ struct Plan {
     int uvc_waves_per_eu = 2;       // uvw convolution
     int uvb_w_waves_per_eu = 1;     // uvw batched backward, dW kernel
     int uvb_w_prefetch = 2;         // uvw batched backward, dW kernel: (path, k) blocks of gradients in flight
+    bool uvb_w_pipeline = true;     // uvw batched backward, dW kernel: a block's MFMAs issued during the next block
     int uvb_xy_prefetch = 2;        // uvw batched backward, dx/dY kernel: (path, k) blocks of gradients in flight
     int uvc_rpw = 4;                // uvw convolution: receivers per wave (16 / waves per workgroup)
     bool stream_hint = true;        // nontemporal loads/stores for once-touched per-edge rows

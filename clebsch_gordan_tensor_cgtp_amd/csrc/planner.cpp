@@ -646,6 +646,7 @@ void schedule(Plan &P)
     if (const char *e = std::getenv("CGTP_UVW_WAVES")) P.uvw_waves_per_eu = std::max(1, std::atoi(e));
     if (const char *e = std::getenv("CGTP_UVB_W_WAVES")) P.uvb_w_waves_per_eu = std::max(1, std::atoi(e));
     if (const char *e = std::getenv("CGTP_UVB_W_PREFETCH")) P.uvb_w_prefetch = std::max(1, std::min(8, std::atoi(e)));
+    if (const char *e = std::getenv("CGTP_UVB_W_PIPELINE")) P.uvb_w_pipeline = std::atoi(e) != 0;
     if (const char *e = std::getenv("CGTP_UVB_XY_PREFETCH")) P.uvb_xy_prefetch = std::max(1, std::min(8, std::atoi(e)));
     if (const char *e = std::getenv("CGTP_BWD_SCHED_BARRIER")) P.bwd_sched_barrier = std::atoi(e) != 0;
     // Rolling prefetch in the first-order sender pass pays where the plan is split into several
