@@ -2452,6 +2452,38 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
     o("");
 }
 
+// Gradient staging of the dW kernel: the block g[16 rows][slot of path p] (S = mul_out (2 l3 + 1)
+// values per row, contiguous in memory) is loaded whole, `cp` consecutive columns of 64 / cp rows
+// per load instruction (so that each instruction reads whole lines), and written to LDS rows of
+// stride T, T = 16 (mod 32): the MFMA B reads (16 channels at stride 2 l3 + 1, odd, times two rows
+// T apart) then fall on distinct banks.
+struct UvbStage {
+    int S, cp, rp, ncol, loads, T;
+};
+UvbStage uvb_stage(const Path &p)
+{
+    UvbStage st;
+    st.S = p.mul_out * n_of(p.l3);
+    st.cp = st.S > 16 ? 32 : 16;
+    st.rp = 64 / st.cp;
+    st.ncol = (st.S + st.cp - 1) / st.cp;
+    st.loads = (16 / st.rp) * st.ncol;
+    st.T = (st.cp * st.ncol + 15) / 32 * 32 + 16;
+    return st;
+}
+int uvb_stage_words(const Plan &P, const Group &g)
+{
+    int w = 0;
+    for (int pi : g.paths) w = std::max(w, 16 * uvb_stage(P.paths[pi]).T);
+    return w;
+}
+int uvb_stage_words(const Plan &P)
+{
+    int w = 0;
+    for (const Group &g : P.uvb_w_groups) w = std::max(w, uvb_stage_words(P, g));
+    return w;
+}
+
 void emit_uvb_w_group(Out &o, const Plan &P, int gi)
 {
     const Group &g = P.uvb_w_groups[gi];
@@ -2469,7 +2501,9 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
     // start, reads the tile block b - 1 wrote, whose MFMAs it issues after its own VALU work, so
     // that the LDS round trip and the MFMA chain run under that work instead of stalling the wave.
     const bool pipe = P.uvb_w_pipeline;
+    const bool gst = P.uvb_w_stage;
     o("T* tw = tl + wv * ", pipe ? 512 : 256, ";");
+    if (gst) o("T* gb = tl + ", 4 * (pipe ? 512 : 256), " + wv * ", uvb_stage_words(P), ";  // this wave's staged gradient block");
     for (int pi : g.paths) o("V4 D", pi, " = {0, 0, 0, 0};");
     o("const long b0 = chunk * bpc;");
     o("const long b1 = b0 + bpc < nblocks ? b0 + bpc : nblocks;");
@@ -2487,7 +2521,8 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
                 o(dst, b, "_", j, " = y[(size_t)", rrx, " * DSH + ", off + j, "];");
         }
     };
-    auto x_loads = [&](int i1, const std::string &rrx) {
+    auto x_loads = [&](int i1, const std::string &rrx, bool declare = false) {
+        const std::string Ty = declare ? "const T " : "";
         const Irrep &ir = P.ins[i1];
         const int n1 = n_of(ir.l);
         const int a = P.paths[by_i1[i1][0]].a;
@@ -2499,9 +2534,9 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
         for (int c = 0; c < 4; ++c)
             for (int i = 0; i < n1; ++i) {
                 if (4 * c + 3 < ir.mul)
-                    o("xp", c, "_", i, " = x[(size_t)", rrx, " * DX + ", a, " + (", 4 * c, " + usub) * ", n1, " + ", i, "];");
+                    o(Ty, "xp", c, "_", i, " = x[(size_t)", rrx, " * DX + ", a, " + (", 4 * c, " + usub) * ", n1, " + ", i, "];");
                 else
-                    o("xp", c, "_", i, " = x[(size_t)", rrx, " * DX + ", a, " + (", 4 * c, " + usub < ", ir.mul, " ? ", 4 * c,
+                    o(Ty, "xp", c, "_", i, " = x[(size_t)", rrx, " * DX + ", a, " + (", 4 * c, " + usub < ", ir.mul, " ? ", 4 * c,
                       " + usub : 0) * ", n1, " + ", i, "];");
             }
     };
@@ -2546,14 +2581,64 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
             load_g((size_t)(tgt - padded), "(blk + 1)", tgt % D);  // past the chunk: clamped, unused
         }
     };
+    // staged mode: paths in emission order; each path's block is loaded (into gr registers) while
+    // the path before it computes, and written to LDS where the path starts
+    std::vector<int> porder;
+    for (auto &kv : by_i1)
+        for (int pi : kv.second) porder.push_back(pi);
+    int gr_max = 0;
+    for (int pi : g.paths) gr_max = std::max(gr_max, uvb_stage(P.paths[pi]).loads);
+    auto stage_load = [&](int pi, const std::string &rb) {
+        const Path &p = P.paths[pi];
+        const UvbStage st = uvb_stage(p);
+        const int lsh = st.cp == 32 ? 5 : 4;
+        // one (wave-uniform) base per row block and unsigned 32-bit offsets from it; rows past the
+        // end read row nrows - 1 (rb is a block of the tensor: rb * 16 <= nrows - 1)
+        o("{");
+        o.ind++;
+        o("const T* gs = g + (size_t)(", rb, ") * 16 * DOUT + ", p.o, ";");
+        o("const unsigned lim = (unsigned)(nrows - 1 - (", rb, ") * 16);");
+        for (int r = 0; r < 16 / st.rp; ++r) {
+            o("{");
+            o.ind++;
+            o("const unsigned sr = ", st.rp * r, "u + (lane >> ", lsh, ") < lim ? ", st.rp * r, "u + (lane >> ", lsh, ") : lim;");
+            for (int c = 0; c < st.ncol; ++c) {
+                const std::string col = std::to_string(st.cp * c) + " + (lane & " + std::to_string(st.cp - 1) + ")";
+                const std::string cl = st.cp * (c + 1) > st.S ? "(" + col + " < " + std::to_string(st.S) + " ? " + col + " : " +
+                                                                   std::to_string(st.S - 1) + ")"
+                                                             : "(" + col + ")";
+                o("gr", r * st.ncol + c, " = gs[sr * (unsigned)DOUT + (unsigned)", cl, "];");
+            }
+            o.ind--;
+            o("}");
+        }
+        o.ind--;
+        o("}");
+    };
+    auto stage_store = [&](int pi) {
+        const UvbStage st = uvb_stage(P.paths[pi]);
+        const int lsh = st.cp == 32 ? 5 : 4;
+        for (int r = 0; r < 16 / st.rp; ++r)
+            for (int c = 0; c < st.ncol; ++c)
+                o("gb[(", st.rp * r, " + (lane >> ", lsh, ")) * ", st.T, " + ", st.cp * c, " + (lane & ", st.cp - 1, ")] = gr",
+                  r * st.ncol + c, ";");
+    };
     int n1max = 1;
     for (auto &kv : by_i1) n1max = std::max(n1max, n_of(P.ins[kv.first].l));
-    for (int b : t.i2)
-        for (int j = 0; j < n_of(P.sh[b].l); ++j) o("T yp", b, "_", j, " = (T)0;");
-    for (int c = 0; c < 4; ++c)
-        for (int i = 0; i < n1max; ++i) o("T xp", c, "_", i, " = (T)0;");
-    for (int set = 0; set < D; ++set)
-        for (int m = 0; m < 4; ++m) o("T gp", set, "_", m, " = (T)0;");
+    // The staged blocks take 64 registers per lane at l = 7; to make room, that mode reads each
+    // path's SH block where the path starts (L1 hits after the row block's first path) instead of
+    // holding every block and the next row block's, and loads x where its section starts.
+    if (!gst) {
+        for (int b : t.i2)
+            for (int j = 0; j < n_of(P.sh[b].l); ++j) o("T yp", b, "_", j, " = (T)0;");
+        for (int c = 0; c < 4; ++c)
+            for (int i = 0; i < n1max; ++i) o("T xp", c, "_", i, " = (T)0;");
+    }
+    if (gst)
+        for (int i = 0; i < gr_max; ++i) o("T gr", i, " = (T)0;");
+    else
+        for (int set = 0; set < D; ++set)
+            for (int m = 0; m < 4; ++m) o("T gp", set, "_", m, " = (T)0;");
     if (pipe)
         for (int par = 0; par < 2; ++par)
             for (int m = 0; m < 4; ++m) o("T gq", par, "_", m, " = (T)0;");
@@ -2561,9 +2646,15 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
     o.ind++;
     o("const long row0 = b0 * 16 + rl;");
     o("const long rr0 = row0 < nrows ? row0 : nrows - 1;");
-    y_loads("yp", "rr0");
-    if (!by_i1.empty()) x_loads(by_i1.begin()->first, "rr0");
-    for (int b = 0; b < std::min(D, nbk); ++b) load_g((size_t)b, "b0", b % D);
+    if (!gst) {
+        y_loads("yp", "rr0");
+        if (!by_i1.empty()) x_loads(by_i1.begin()->first, "rr0");
+    }
+    if (gst) {
+        if (!porder.empty()) stage_load(porder[0], "b0");
+    } else {
+        for (int b = 0; b < std::min(D, nbk); ++b) load_g((size_t)b, "b0", b % D);
+    }
     o.ind--;
     o("}");
     o("for (long blk = b0; blk < b1; ++blk) {");
@@ -2574,9 +2665,11 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
     o("const bool more = blk + 1 < b1;");
     o("const long rowx = (blk + 1) * 16 + rl;");
     o("const long rrx = more ? (rowx < nrows ? rowx : nrows - 1) : rr;");
-    for (int b : t.i2)
-        for (int j = 0; j < n_of(P.sh[b].l); ++j) o("const T y", b, "_", j, " = yp", b, "_", j, ";");
-    y_loads("yp", "rrx");  // rrx = rr after the last row block: loaded again, unused
+    if (!gst) {
+        for (int b : t.i2)
+            for (int j = 0; j < n_of(P.sh[b].l); ++j) o("const T y", b, "_", j, " = yp", b, "_", j, ";");
+        y_loads("yp", "rrx");  // rrx = rr after the last row block: loaded again, unused
+    }
     size_t bidx = 0;
     size_t sec = 0;
     int prev_pi = -1, par = 0;  // pipeline: the block whose MFMAs are pending, and this block's tile
@@ -2593,6 +2686,7 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
         const int n1 = n_of(ir.l);
         o("{");
         o.ind++;
+        if (gst) x_loads(kv.first, "rr", true);
         for (int c = 0; c < 4; ++c)
             for (int i = 0; i < n1; ++i) {
                 if (4 * c + 3 < ir.mul)
@@ -2601,7 +2695,8 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
                     o("const T x", c, "_", i, " = ", 4 * c, " + usub < ", ir.mul, " ? xp", c, "_", i, " : (T)0;");
             }
         // the next input block's x: this row block's, or the next row block's first
-        if (++sec < by_i1.size()) {
+        if (gst) {
+        } else if (++sec < by_i1.size()) {
             x_loads(std::next(by_i1.begin(), (long)sec)->first, "rr");
         } else {
             x_loads(by_i1.begin()->first, "rrx");
@@ -2610,6 +2705,28 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
             const Path &p = P.paths[pi];
             std::map<int, std::map<int, std::vector<const Nonzero *>>> byki;
             for (const Nonzero &z : p.nz) byki[z.k][z.i].push_back(&z);
+            const UvbStage st = uvb_stage(p);
+            o("{");
+            o.ind++;
+            if (gst) {
+                // opaque zero offset: keeps the compiler from merging these reads across paths
+                int off = 0;
+                for (int bb = 0; bb < p.i2; ++bb) off += P.sh[bb].dim();
+                o("int zo = 0;");
+                o("asm volatile(\"\" : \"+v\"(zo));");
+                for (int j = 0; j < n_of(p.l2); ++j) o("const T y", p.i2, "_", j, " = y[(size_t)rr * DSH + zo + ", off + j, "];");
+                // this path's gradient block into LDS (the reads of the path before it are
+                // issued, and the wave's LDS accesses complete in order), then the next path's
+                // loads: that of the next row block after the last path (clamped past the end)
+                const size_t at = (size_t)(std::find(porder.begin(), porder.end(), pi) - porder.begin());
+                o("WAVE_SYNC();");
+                stage_store(pi);
+                if (at + 1 < porder.size())
+                    stage_load(porder[at + 1], "blk");
+                else
+                    stage_load(porder[0], "(blk + 1 < b1 ? blk + 1 : blk)");  // the chunk's last: loaded again, unused
+                o("WAVE_SYNC();");
+            }
             for (auto &kk : byki) {
                 o("{");
                 o.ind++;
@@ -2623,10 +2740,16 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
                         o("__builtin_amdgcn_sched_barrier(0);");
                     }
                 }
-                for (int m = 0; m < 4; ++m)
+                for (int m = 0; m < 4; ++m) {
+                    const std::string src =
+                        gst ? "gb[" + std::to_string(4 * m * st.T) + " + usub * " + std::to_string(st.T) + " + " +
+                                  (wmask ? "(rl < " + std::to_string(p.mul_out) + " ? rl : 0)" : std::string("rl")) + " * " +
+                                  std::to_string(n_of(p.l3)) + " + " + std::to_string(kk.first) + "]"
+                            : "gp" + std::to_string((int)bidx % D) + "_" + std::to_string(m);
                     o(pipe ? "gq" + std::to_string(par) + "_" : std::string("const T gc"), m, " = (blk * 16 + ", 4 * m, " + usub < nrows",
-                      wmask ? " && rl < " + std::to_string(P.paths[pi].mul_out) : std::string(), ") ? gp", (int)bidx % D, "_", m, " : (T)0;");
-                ahead((int)bidx);
+                      wmask ? " && rl < " + std::to_string(P.paths[pi].mul_out) : std::string(), ") ? ", src, " : (T)0;");
+                }
+                if (!gst) ahead((int)bidx);
                 ++bidx;
                 for (auto &ii : kk.second) {
                     const auto &v = ii.second;
@@ -2668,11 +2791,14 @@ void emit_uvb_w_group(Out &o, const Plan &P, int gi)
                 o.ind--;
                 o("}");
             }
+            o.ind--;
+            o("}");  // path
         }
         o.ind--;
         o("}");
     }
-    for (int pos = nbk; pos < padded; ++pos) ahead(pos);  // load-only steps of the padding
+    if (!gst)
+        for (int pos = nbk; pos < padded; ++pos) ahead(pos);  // load-only steps of the padding
     if (pipe && prev_pi >= 0) {
         // the row block's last block
         o("{");
@@ -2818,7 +2944,7 @@ void emit_uvb_kernels(Out &o, const Plan &P)
       "long nchunks, long nwaves)");
     o("{");
     o.ind++;
-    o("__shared__ T tl[", 4 * (P.uvb_w_pipeline ? 512 : 256), "];");
+    o("__shared__ T tl[", 4 * (P.uvb_w_pipeline ? 512 : 256) + (P.uvb_w_stage ? 4 * uvb_stage_words(P) : 0), "];");
     o("const long wave = (long)blockIdx.x * 4 + WAVE_IN_BLOCK();");
     o("const int wv = WAVE_IN_BLOCK();");
     o("const int lane = threadIdx.x & 63;");

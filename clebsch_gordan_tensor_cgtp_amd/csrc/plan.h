@@ -83,6 +83,7 @@ struct Plan {
     int uvb_w_waves_per_eu = 1;     // uvw batched backward, dW kernel
     int uvb_w_prefetch = 2;         // uvw batched backward, dW kernel: (path, k) blocks of gradients in flight
     bool uvb_w_pipeline = true;     // uvw batched backward, dW kernel: a block's MFMAs issued during the next block
+    bool uvb_w_stage = true;        // uvw batched backward, dW kernel: per-path gradient blocks staged in LDS
     int uvb_xy_prefetch = 2;        // uvw batched backward, dx/dY kernel: (path, k) blocks of gradients in flight
     int uvc_rpw = 4;                // uvw convolution: receivers per wave (16 / waves per workgroup)
     bool stream_hint = true;        // nontemporal loads/stores for once-touched per-edge rows

@@ -647,6 +647,10 @@ void schedule(Plan &P)
     if (const char *e = std::getenv("CGTP_UVB_W_WAVES")) P.uvb_w_waves_per_eu = std::max(1, std::atoi(e));
     if (const char *e = std::getenv("CGTP_UVB_W_PREFETCH")) P.uvb_w_prefetch = std::max(1, std::min(8, std::atoi(e)));
     if (const char *e = std::getenv("CGTP_UVB_W_PIPELINE")) P.uvb_w_pipeline = std::atoi(e) != 0;
+    // the staged gradient blocks hold one path's block per lane in registers (64 values at l = 7):
+    // fp32 only (fp64 doubles that)
+    P.uvb_w_stage = P.dtype == CGTP_F32;
+    if (const char *e = std::getenv("CGTP_UVB_W_STAGE")) P.uvb_w_stage = std::atoi(e) != 0;
     if (const char *e = std::getenv("CGTP_UVB_XY_PREFETCH")) P.uvb_xy_prefetch = std::max(1, std::min(8, std::atoi(e)));
     if (const char *e = std::getenv("CGTP_BWD_SCHED_BARRIER")) P.bwd_sched_barrier = std::atoi(e) != 0;
     // Rolling prefetch in the first-order sender pass pays where the plan is split into several
