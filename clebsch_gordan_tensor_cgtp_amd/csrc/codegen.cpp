@@ -591,7 +591,8 @@ std::string split_suffix(int split) { return split == 1 ? "" : "_split" + std::t
 
 void emit_fwd_kernel(Out &o, const Plan &P, bool rows, bool dbl = false, int split = 1)
 {
-    o("extern \"C\" __global__ void __launch_bounds__(256, ", dbl ? P.dbl_fwd_waves_per_eu : P.fwd_waves_per_eu, ") ",
+    const int waves = dbl ? P.dbl_fwd_waves_per_eu : !rows && P.conv_fwd_waves ? P.conv_fwd_waves : P.fwd_waves_per_eu;
+    o("extern \"C\" __global__ void __launch_bounds__(256, ", waves, ") ",
       rows ? "cgtp_tp_fwd" : dbl ? "cgtp_conv_dbwd_recv" : "cgtp_conv_fwd", split_suffix(split),
       "(const int* __restrict__ row_ptr, const int* __restrict__ col, const T* __restrict__ x, "
       "const T* __restrict__ y, const T* __restrict__ w, ",

@@ -74,6 +74,7 @@ struct Plan {
     std::string uvc_why;            // why not, when uvc_ok is false
     bool unit_weights = false;      // internal plans: every weight is 1 (not read), only the sender pass
     int fwd_waves_per_eu = 4;       // occupancy target given to the compiler (min waves per SIMD)
+    int conv_fwd_waves = 0;         // the convolution's receiver pass, when it differs (0: fwd_waves_per_eu)
     int bwd_waves_per_eu = 4;
     int uvw_waves_per_eu = 2;
     int dbl_fwd_waves_per_eu = 2;   // double backward, receiver pass (twice the forward's operands)

@@ -664,6 +664,11 @@ void schedule(Plan &P)
     // SIMD without it, and with it spill (NequIP-like graph: 107 -> 142 us).
     P.fwd_sched_barrier = P.fwd_groups.size() > 1;
     if (const char *e = std::getenv("CGTP_FWD_SCHED_BARRIER")) P.fwd_sched_barrier = std::atoi(e) != 0;
+    // With the next edge's operands pinned ahead, the fp32 receiver pass of a split plan needs a few
+    // registers more than four waves per SIMD allow (MACE-like graph: 128 VGPRs and a 6-register
+    // spill at 4, 130 and none at 3: 4.07 against 4.03-4.04 ms, alternating runs on one box).
+    P.conv_fwd_waves = P.dtype == CGTP_F32 && P.fwd_sched_barrier && P.fwd_waves_per_eu == 4 ? 3 : 0;
+    if (const char *e = std::getenv("CGTP_CONV_FWD_WAVES")) P.conv_fwd_waves = std::max(0, std::atoi(e));
     if (const char *e = std::getenv("CGTP_UVC_SCHED_BARRIER")) P.uvc_sched_barrier = std::atoi(e) != 0;
 }
 
