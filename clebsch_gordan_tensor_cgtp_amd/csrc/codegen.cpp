@@ -507,7 +507,12 @@ void emit_fwd_group(Out &o, const Plan &P, int gi, bool rows, bool dbl = false, 
         // keep the next edge's loads here, ahead of this edge's arithmetic: left alone the
         // scheduler sinks them to the end of the iteration (fewer live registers), and each edge
         // then waits for its own operands
-        if (P.fwd_sched_barrier) o("__builtin_amdgcn_sched_barrier(0);");
+        if (P.fwd_sched_barrier)
+            o("__builtin_amdgcn_sched_barrier(0);");
+        else if (splittable && !dbl && !radial && P.split_sched_barrier)
+            // rows split over several waves only where receivers are few against the wave slots:
+            // there the few resident waves cannot hide each edge's wait, and the pinned loads pay
+            o("if constexpr (SPLIT > 1) __builtin_amdgcn_sched_barrier(0);");
         if (radial) {
             // The Theta reads do not depend on the edge: left alone, the compiler hoists all
             // R * paths of them out of the loop and spills them.  An empty asm makes the base
@@ -591,7 +596,8 @@ std::string split_suffix(int split) { return split == 1 ? "" : "_split" + std::t
 
 void emit_fwd_kernel(Out &o, const Plan &P, bool rows, bool dbl = false, int split = 1)
 {
-    const int waves = dbl ? P.dbl_fwd_waves_per_eu : !rows && P.conv_fwd_waves ? P.conv_fwd_waves : P.fwd_waves_per_eu;
+    int waves = dbl ? P.dbl_fwd_waves_per_eu : !rows && P.conv_fwd_waves ? P.conv_fwd_waves : P.fwd_waves_per_eu;
+    if (!rows && !dbl && split > 1 && P.split_sched_barrier && P.split_fwd_waves) waves = P.split_fwd_waves;
     o("extern \"C\" __global__ void __launch_bounds__(256, ", waves, ") ",
       rows ? "cgtp_tp_fwd" : dbl ? "cgtp_conv_dbwd_recv" : "cgtp_conv_fwd", split_suffix(split),
       "(const int* __restrict__ row_ptr, const int* __restrict__ col, const T* __restrict__ x, "

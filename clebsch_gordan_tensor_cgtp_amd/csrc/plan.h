@@ -75,6 +75,7 @@ struct Plan {
     bool unit_weights = false;      // internal plans: every weight is 1 (not read), only the sender pass
     int fwd_waves_per_eu = 4;       // occupancy target given to the compiler (min waves per SIMD)
     int conv_fwd_waves = 0;         // the convolution's receiver pass, when it differs (0: fwd_waves_per_eu)
+    int split_fwd_waves = 0;        // its row-split kernels, when they differ (0: as the receiver pass)
     int bwd_waves_per_eu = 4;
     int uvw_waves_per_eu = 2;
     int dbl_fwd_waves_per_eu = 2;   // double backward, receiver pass (twice the forward's operands)
@@ -92,6 +93,7 @@ struct Plan {
     bool bwd_sched_barrier = true;  // keep path blocks of the backward from interleaving
     int bwd_rolling = 0;            // sender pass: next edge's operands loaded as this edge frees them (2: pinned by barriers)
     bool fwd_sched_barrier = false; // keep the receiver pass's next-edge loads ahead of its arithmetic
+    bool split_sched_barrier = true; // the same in the row-split forward kernels of single-group plans
     bool uvc_sched_barrier = true;  // the same in the uvw convolution's edge stream
     bool rbw_sched_barrier = true;  // the same for the receiver-order backward, per path
     bool rbw_prefetch = false;      // receiver-order backward: sender ids two edges ahead, operands one ahead

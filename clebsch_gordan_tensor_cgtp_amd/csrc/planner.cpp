@@ -664,6 +664,15 @@ void schedule(Plan &P)
     // SIMD without it, and with it spill (NequIP-like graph: 107 -> 142 us).
     P.fwd_sched_barrier = P.fwd_groups.size() > 1;
     if (const char *e = std::getenv("CGTP_FWD_SCHED_BARRIER")) P.fwd_sched_barrier = std::atoi(e) != 0;
+    // Single-group plans split rows over 2 or 4 waves on graphs with few receivers against the wave
+    // slots; the barrier pays there and not on large graphs (one wave per row), so those kernels
+    // alone take it (NequIP-like graph: 102 -> 97 us; the 10M-edge plan on a 5,000-node graph 0.59
+    // -> 0.44 ms; on 200,000-node graphs 4.61 -> 4.64 and 9.82 -> 10.04 ms with it everywhere).
+    if (const char *e = std::getenv("CGTP_SPLIT_SCHED_BARRIER")) P.split_sched_barrier = std::atoi(e) != 0;
+    // with the barrier those kernels need a few registers more than four waves allow in fp32 (the
+    // NequIP-like plan: 134 and no spill at three, a 7-register spill at four)
+    P.split_fwd_waves = P.dtype == CGTP_F32 && P.fwd_waves_per_eu == 4 ? 3 : 0;
+    if (const char *e = std::getenv("CGTP_SPLIT_FWD_WAVES")) P.split_fwd_waves = std::max(0, std::atoi(e));
     // With the next edge's operands pinned ahead, the fp32 receiver pass of a split plan needs a few
     // registers more than four waves per SIMD allow (MACE-like graph: 128 VGPRs and a 6-register
     // spill at 4, 130 and none at 3: 4.07 against 4.03-4.04 ms, alternating runs on one box).
