@@ -84,6 +84,13 @@ Touch touched(const Plan &P, const std::vector<int> &paths)
 
 int n_of(int l) { return 2 * l + 1; }
 
+// v += v(lane ^ m): the permlane exchange for m = 16, 32, a lane shuffle below
+std::string xadd(const std::string &v, int m)
+{
+    if (m == 16 || m == 32) return v + " = xsum" + std::to_string(m) + "(" + v + ");";
+    return v + " += __shfl_xor(" + v + ", " + std::to_string(m) + ");";
+}
+
 // (i1, i2) pairs in order of their first path, each with its paths.
 std::vector<std::pair<std::pair<int, int>, std::vector<int>>> pairs_of(const Plan &P, const std::vector<int> &paths)
 {
@@ -393,6 +400,38 @@ void emit_preamble(Out &o, const Plan &P)
         o("#define WAVE_IN_BLOCK() ((int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6))");
     else
         o("#define WAVE_IN_BLOCK() ((int)(threadIdx.x >> 6))");
+    // v(l) + v(l ^ 16) and v(l) + v(l ^ 32) in every lane l.  A v_permlane16_swap of v with itself
+    // returns two registers holding the 16-lane rows (0, 0, 2, 2) and (1, 1, 3, 3) of v, a
+    // v_permlane32_swap the halves (lo, lo) and (hi, hi); the sum of the two is the xor butterfly's
+    // value bit for bit (IEEE addition commutes), from a VALU exchange instead of the LDS round
+    // trip of a lane shuffle
+    if (P.permlane_sums) {
+        for (int m : {16, 32}) {
+            o("__device__ __forceinline__ T xsum", m, "(T v)");
+            o("{");
+            o.ind++;
+            // the two results are copied into plain variables first: bit-casting the builtin's
+            // vector elements directly made the front end read element 0 for both
+            if (f64) {
+                o("const unsigned long long b = __builtin_bit_cast(unsigned long long, v);");
+                o("const auto lo = __builtin_amdgcn_permlane", m, "_swap((unsigned)b, (unsigned)b, false, false);");
+                o("const auto hi = __builtin_amdgcn_permlane", m, "_swap((unsigned)(b >> 32), (unsigned)(b >> 32), false, false);");
+                o("const unsigned l0 = lo[0], l1 = lo[1], h0 = hi[0], h1 = hi[1];");
+                o("return __builtin_bit_cast(double, ((unsigned long long)h0 << 32) | l0) + "
+                  "__builtin_bit_cast(double, ((unsigned long long)h1 << 32) | l1);");
+            } else {
+                o("const unsigned a = __builtin_bit_cast(unsigned, v);");
+                o("const auto r = __builtin_amdgcn_permlane", m, "_swap(a, a, false, false);");
+                o("const unsigned r0 = r[0], r1 = r[1];");
+                o("return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);");
+            }
+            o.ind--;
+            o("}");
+        }
+    } else {
+        o("#define xsum16(v) ((v) + __shfl_xor((v), 16))");
+        o("#define xsum32(v) ((v) + __shfl_xor((v), 32))");
+    }
     // per-edge rows read or written once (y, W, dW): streaming hint on the memory instructions
     if (P.stream_hint) {
         o("#define LD_STREAM(p) __builtin_nontemporal_load(p)");
@@ -536,7 +575,7 @@ void emit_fwd_group(Out &o, const Plan &P, int gi, bool rows, bool dbl = false, 
         // sum the edge slots (fixed butterfly order, identical in every run)
         for (int m = 32; m >= g.ct; m /= 2)
             for (int q : t.slots)
-                for (int k = 0; k < n_of(P.out[q].l); ++k) o("a", q, "_", k, " += __shfl_xor(a", q, "_", k, ", ", m, ");");
+                for (int k = 0; k < n_of(P.out[q].l); ++k) o(xadd("a" + std::to_string(q) + "_" + std::to_string(k), m));
         if (splittable) {
             emit_part_sum(o, P, gi, t);
             o("if (live && part == 0 && slot == 0) {");
@@ -657,8 +696,8 @@ void emit_slot_sum(Out &o, const Plan &P)
         o.ind--;
         o("}");
     }
-    o("if constexpr (CT >= 32) v += __shfl_xor(v, 16);");
-    o("if constexpr (CT >= 64) v += __shfl_xor(v, 32);");
+    o("if constexpr (CT >= 32) v = xsum16(v);");
+    o("if constexpr (CT >= 64) v = xsum32(v);");
     o("return v;");
     o.ind--;
     o("}");
@@ -1115,7 +1154,7 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
     // sum the edge slots of the wave, then the waves of the workgroup (fixed order)
     for (int m = 32; m >= g.ct; m /= 2)
         for (int b : xb)
-            for (int i = 0; i < n_of(P.ins[b].l); ++i) o("d", b, "_", i, " += __shfl_xor(d", b, "_", i, ", ", m, ");");
+            for (int i = 0; i < n_of(P.ins[b].l); ++i) o(xadd("d" + std::to_string(b) + "_" + std::to_string(i), m));
     o("if (wpr > 1) {");
     o.ind++;
     o("if (wv > 0 && slot == 0) {");
@@ -1191,7 +1230,7 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
             for (int pi : g.paths) tas.push_back("ta" + std::to_string(r) + "_" + std::to_string(pi));
         const int nt = (int)tas.size();
         for (int m = 32; m >= g.ct; m /= 2)
-            for (auto &v : tas) o(v, " += __shfl_xor(", v, ", ", m, ");");
+            for (auto &v : tas) o(xadd(v, m));
         o("if (wpr > 1) {");
         o.ind++;
         // in rounds of at most kRadialRound sums, so that the LDS buffer stays bounded
@@ -2077,7 +2116,7 @@ void emit_uvc_phase_a(Out &o, const Plan &P, const Group &g, std::map<int, int> 
     o("}");  // e0 < e1
     for (int m = 32; m >= g.ct; m /= 2)
         for (int pi : g.paths)
-            for (int k = 0; k < n_of(P.paths[pi].l3); ++k) o("t", pi, "_", k, " += __shfl_xor(t", pi, "_", k, ", ", m, ");");
+            for (int k = 0; k < n_of(P.paths[pi].l3); ++k) o(xadd("t" + std::to_string(pi) + "_" + std::to_string(k), m));
     o("if (slot == 0) {");
     o.ind++;
     for (int pi : g.paths) {
@@ -2415,12 +2454,17 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
         if (q + 2 < (int)g.paths.size()) load_w(q + 2);
         // dY of this path: sum the row's four lanes, then lane usub == 0 adds into the wave's LDS rows
         for (int j = 0; j < n2; ++j) {
-            o("h", j, " += __shfl_xor(h", j, ", 16);");
-            o("h", j, " += __shfl_xor(h", j, ", 32);");
+            o(xadd("h" + std::to_string(j), 16));
+            o(xadd("h" + std::to_string(j), 32));
         }
+        // LDS adds without return: nothing waits for them, and the wave's own adds to its rows
+        // complete in issue order (each instruction's 16 lanes add to distinct rows), so the sums
+        // keep a fixed order
         o("if (usub == 0) {");
         o.ind++;
-        for (int j = 0; j < n2; ++j) o("dyw[rl * ", uvb_dy_stride(P), " + ", p.b + j, "] += h", j, ";");
+        for (int j = 0; j < n2; ++j)
+            o("__hip_atomic_fetch_add(&dyw[rl * ", uvb_dy_stride(P), " + ", p.b + j, "], h", j,
+              ", __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);");
         o.ind--;
         o("}");
         // The dx sums are only read by the conditional store at the end; left alone the compiler

@@ -658,6 +658,7 @@ void schedule(Plan &P)
     // the extra live range (NequIP-like graph: 0.30 -> 0.68 ms, streaming graph: 29.1 -> 30.6 ms).
     P.bwd_rolling = P.dtype == CGTP_F32 && P.bwd_groups.size() > 1 ? 1 : 0;
     if (const char *e = std::getenv("CGTP_BWD_ROLLING")) P.bwd_rolling = std::atoi(e);
+    if (const char *e = std::getenv("CGTP_PERMLANE_SUMS")) P.permlane_sums = std::atoi(e) != 0;
     // Pinning the receiver pass's next-edge loads ahead of the arithmetic pays for plans split into
     // several path groups, whose long per-edge arithmetic hides a whole load latency (MACE-like
     // graph: fp32 4.27 -> 4.09 ms, fp64 9.52 -> 9.23 ms); single-group plans keep four waves per
