@@ -2413,6 +2413,10 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
         o("asm volatile(\"\" : \"+v\"(zo));");
         for (int j = 0; j < n2; ++j) o("const T y", p.i2, "_", j, " = y[(size_t)rr * DSH + zo + ", p.b + j, "];");
         for (int j = 0; j < n2; ++j) o("T h", j, " = (T)0;");
+        // the wave's dY row values this path adds to, read now: the add at the path's end then
+        // finds them in registers instead of waiting for an LDS read (the wave alone writes these
+        // rows, and its LDS accesses complete in issue order, after the previous path's writes)
+        for (int j = 0; j < n2; ++j) o("const T dyo", j, " = dyw[rl * ", uvb_dy_stride(P), " + ", p.b + j, "];");
         std::map<int, std::map<int, std::vector<const Nonzero *>>> byki;  // k -> i -> nonzeros
         for (const Nonzero &z : p.nz) byki[z.k][z.i].push_back(&z);
         for (auto &kk : byki) {
@@ -2457,14 +2461,9 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
             o(xadd("h" + std::to_string(j), 16));
             o(xadd("h" + std::to_string(j), 32));
         }
-        // LDS adds without return: nothing waits for them, and the wave's own adds to its rows
-        // complete in issue order (each instruction's 16 lanes add to distinct rows), so the sums
-        // keep a fixed order
         o("if (usub == 0) {");
         o.ind++;
-        for (int j = 0; j < n2; ++j)
-            o("__hip_atomic_fetch_add(&dyw[rl * ", uvb_dy_stride(P), " + ", p.b + j, "], h", j,
-              ", __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);");
+        for (int j = 0; j < n2; ++j) o("dyw[rl * ", uvb_dy_stride(P), " + ", p.b + j, "] = dyo", j, " + h", j, ";");
         o.ind--;
         o("}");
         // The dx sums are only read by the conditional store at the end; left alone the compiler
