@@ -272,6 +272,18 @@ def test_conv_uvw_backward_workspace_and_modules():
         assert "atomic" not in src.lower()
 
 
+def test_uvw_batched_backward_module_has_no_atomics_and_no_lane_shuffles():
+    """The batched uvw backward (dx/dY and dW kernels) builds on the host; like every generated
+    kernel it issues no atomic, and its lane sums over xor 16 / 32 are permlane exchanges."""
+    plan = cg.Plan("4x0e+3x1o+2x2e", cg.sh_irreps(2), "5x0e+3x1o+2x2e+1x1e", "uvw", "f32")
+    src = plan.uvw_backward_source()
+    assert "cgtp_tp_uvw_bwd_xy" in src and "cgtp_tp_uvw_bwd_w" in src
+    # (its wave-scope fences name memory orders, __ATOMIC_RELEASE / _ACQUIRE, and order nothing
+    # but the compiler's placement of the LDS transpose)
+    assert not re.search(r"__hip_atomic|atomic(add|sub|cas|exch|max|min|inc|dec|and|or|xor)|atomic_fetch", src, re.I)
+    assert "xsum16(" in src and "xsum32(" in src and "__shfl" not in src
+
+
 def test_compiled_code_does_not_depend_on_what_the_process_loaded_first(tmp_path):
     """The generated module is compiled by the ROCm installation's hipRTC in a link namespace of
     its own, so a process that imported torch first (which brings its own hipRTC and compiler
