@@ -2102,7 +2102,14 @@ void emit_uvc_phase_a(Out &o, const Plan &P, const Group &g, std::map<int, int> 
         for (int pi : pr.second) {
             std::map<int, std::vector<const Nonzero *>> byk;
             for (const Nonzero &z : P.paths[pi].nz) byk[z.k].push_back(&z);
-            for (auto &kv : byk) o("t", pi, "_", kv.first, " += ", cg_sum(kv.second, "q", f64), ";");
+            // the running sum is the innermost addend of the chain: one FMA per nonzero and no
+            // separate add per (path, k) block
+            for (auto &kv : byk) {
+                std::string e = "t" + std::to_string(pi) + "_" + std::to_string(kv.first);
+                for (const Nonzero *z : kv.second)
+                    e = "FMA(" + lit(z->c, f64) + ", q" + std::to_string(z->i) + "_" + std::to_string(z->j) + ", " + e + ")";
+                o("t", pi, "_", kv.first, " = ", e, ";");
+            }
         }
         o.ind--;
         o("}");
