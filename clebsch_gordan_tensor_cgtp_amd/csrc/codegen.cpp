@@ -944,9 +944,29 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
                 o("const T ", name, kv.first, " = ", e.str(), ";");
             }
         };
-        contract(rows, false, "y", p.i2, "fx");
+        // unit weights (the uvw convolution's sender pass): dx_i and dY_j take their terms as one
+        // FMA chain each, the running sum innermost (no separate add per row or column)
+        auto fold = [&](const std::map<int, std::vector<int>> &lines, bool by_col, const std::string &v, int blk,
+                        const std::string &acc) {
+            for (auto &kv : lines) {
+                std::string e = acc + std::to_string(kv.first);
+                for (int m : kv.second) {
+                    const std::string b = by_col ? "B" + std::to_string(m) + "_" + std::to_string(kv.first)
+                                                 : "B" + std::to_string(kv.first) + "_" + std::to_string(m);
+                    e = "FMA(" + b + ", " + v + std::to_string(blk) + "_" + std::to_string(m) + ", " + e + ")";
+                }
+                o(acc, kv.first, " = ", e, ";");
+            }
+        };
+        const bool folded = P.unit_weights && !dbl && !radial;
+        if (folded) {
+            fold(rows, false, "y", p.i2, "d" + std::to_string(p.i1) + "_");
+            fold(cols, true, "x", p.i1, "h" + std::to_string(p.i2) + "_");
+        } else {
+            contract(rows, false, "y", p.i2, "fx");
+            contract(cols, true, "x", p.i1, "fy");
+        }
         if (dbl) contract(rows, false, "gy", p.i2, "fxg");  // d/dx of the ggy term
-        contract(cols, true, "x", p.i1, "fy");
         if (dbl) contract(cols, true, "gx", p.i1, "fyg");   // d/dy of the ggx term
         if (!P.unit_weights) {
             // dW = sum_i x_i dF/dx_i   (double backward: sum_i ggx_i fx_i + x_i fxg_i)
@@ -995,8 +1015,10 @@ void emit_bwd_group(Out &o, const Plan &P, int gi, bool dbl = false, bool rowmod
                 o("h", p.i2, "_", kv.first, " = FMA(w", pi, ", fyg", kv.first, ", FMA(gw", pi, ", fy", kv.first, ", h", p.i2,
                   "_", kv.first, "));");
         } else if (P.unit_weights) {
-            for (auto &kv : rows) o("d", p.i1, "_", kv.first, " += fx", kv.first, ";");
-            for (auto &kv : cols) o("h", p.i2, "_", kv.first, " += fy", kv.first, ";");
+            if (!folded) {
+                for (auto &kv : rows) o("d", p.i1, "_", kv.first, " += fx", kv.first, ";");
+                for (auto &kv : cols) o("h", p.i2, "_", kv.first, " += fy", kv.first, ";");
+            }
         } else {
             for (auto &kv : rows)
                 o("d", p.i1, "_", kv.first, " = FMA(w", pi, ", fx", kv.first, ", d", p.i1, "_", kv.first, ");");
