@@ -577,9 +577,10 @@ void schedule(Plan &P)
             // against 256 VGPRs, a 128-byte spill and 21.8 ms at 168, and five spilling groups
             // above 176; fp64 at 200 gives 11 groups at 247 VGPRs, two waves per SIMD and
             // 38.8 ms, against 17 groups and 46.6 ms at 168, 56.8 ms at 140, and one wave per SIMD
-            // from 216 on (8 groups at 230: 48.1 ms)).  The double backward's sender pass keeps 168.
+            // from 216 on (8 groups at 230: 48.1 ms); with the rolling prefetch below 180 fits it in
+            // 247 VGPRs: 38.1 against 38.7 ms).  The double backward's sender pass keeps 168.
             const int split_budget =
-                getenv_int("CGTP_BWD_BUDGET", dbl ? 168 : P.dtype == CGTP_F64 ? 200 : 140);
+                getenv_int("CGTP_BWD_BUDGET", dbl ? 168 : P.dtype == CGTP_F64 ? 180 : 140);
             const int one_group_limit = 200;
             groups.clear();
             std::vector<int> all_paths;
@@ -654,9 +655,10 @@ void schedule(Plan &P)
     if (const char *e = std::getenv("CGTP_UVB_XY_PREFETCH")) P.uvb_xy_prefetch = std::max(1, std::min(8, std::atoi(e)));
     if (const char *e = std::getenv("CGTP_BWD_SCHED_BARRIER")) P.bwd_sched_barrier = std::atoi(e) != 0;
     // Rolling prefetch in the first-order sender pass pays where the plan is split into several
-    // path groups in fp32 (MACE-like graph: 20.1 -> 17.6 ms); single-group plans lose occupancy to
-    // the extra live range (NequIP-like graph: 0.30 -> 0.68 ms, streaming graph: 29.1 -> 30.6 ms).
-    P.bwd_rolling = P.dtype == CGTP_F32 && P.bwd_groups.size() > 1 ? 1 : 0;
+    // path groups (MACE-like graph: fp32 20.1 -> 17.6 ms; fp64 at the split budget of 180 38.7 ->
+    // 38.1 ms); single-group plans lose occupancy to the extra live range (NequIP-like graph: 0.30
+    // -> 0.68 ms, streaming graph: 29.1 -> 30.6 ms).
+    P.bwd_rolling = P.bwd_groups.size() > 1 ? 1 : 0;
     if (const char *e = std::getenv("CGTP_BWD_ROLLING")) P.bwd_rolling = std::atoi(e);
     if (const char *e = std::getenv("CGTP_PERMLANE_SUMS")) P.permlane_sums = std::atoi(e) != 0;
     // Pinning the receiver pass's next-edge loads ahead of the arithmetic pays for plans split into
