@@ -538,38 +538,72 @@ void emit_fwd_group(Out &o, const Plan &P, int gi, bool rows, bool dbl = false, 
         o("int en = (e + stride < e1) ? e + stride : e1 - 1;");
         o("int sn = col[en];");
         emit_edge_loads(o, P, g, t, "c", "s", "ec", true, dbl, radial);
-        o("for (; e < e1; e += stride) {");
-        o.ind++;
-        o("const int enn = (e + 2 * stride < e1) ? e + 2 * stride : e1 - 1;");
-        o("const int snn = col[enn];");
-        emit_edge_loads(o, P, g, t, "n", "sn", "en", true, dbl, radial);
-        // keep the next edge's loads here, ahead of this edge's arithmetic: left alone the
-        // scheduler sinks them to the end of the iteration (fewer live registers), and each edge
-        // then waits for its own operands
-        if (P.fwd_sched_barrier)
-            o("__builtin_amdgcn_sched_barrier(0);");
-        else if (splittable && !dbl && !radial && P.split_sched_barrier)
-            // rows split over several waves only where receivers are few against the wave slots:
-            // there the few resident waves cannot hide each edge's wait, and the pinned loads pay
-            o("if constexpr (SPLIT > 1) __builtin_amdgcn_sched_barrier(0);");
-        if (radial) {
-            // The Theta reads do not depend on the edge: left alone, the compiler hoists all
-            // R * paths of them out of the loop and spills them.  An empty asm makes the base
-            // offset (always 0) opaque per iteration, so each read stays next to its use.
-            o("int zo = 0;");
-            o("asm volatile(\"\" : \"+v\"(zo));");
-            o("const T* th = thl + zo;");
-            emit_forward_math(o, P, g, f64, "c", radial);
-        } else if (dbl) {
-            emit_dbl_recv_math(o, P, g, f64, "c");
+        // keep the next edge's loads ahead of this edge's arithmetic: left alone the scheduler
+        // sinks them to the end of the iteration (fewer live registers), and each edge then waits
+        // for its own operands
+        auto barrier = [&]() {
+            if (P.fwd_sched_barrier)
+                o("__builtin_amdgcn_sched_barrier(0);");
+            else if (splittable && !dbl && !radial && P.split_sched_barrier)
+                // rows split over several waves only where receivers are few against the wave
+                // slots: there the few resident waves cannot hide each edge's wait, and the pinned
+                // loads pay
+                o("if constexpr (SPLIT > 1) __builtin_amdgcn_sched_barrier(0);");
+        };
+        auto math = [&](const std::string &pre) {
+            if (radial) {
+                // The Theta reads do not depend on the edge: left alone, the compiler hoists all
+                // R * paths of them out of the loop and spills them.  An empty asm makes the base
+                // offset (always 0) opaque per iteration, so each read stays next to its use.
+                o("{");
+                o.ind++;
+                o("int zo = 0;");
+                o("asm volatile(\"\" : \"+v\"(zo));");
+                o("const T* th = thl + zo;");
+                emit_forward_math(o, P, g, f64, pre, radial);
+                o.ind--;
+                o("}");
+            } else if (dbl) {
+                emit_dbl_recv_math(o, P, g, f64, pre);
+            } else {
+                emit_forward_math(o, P, g, f64, pre);
+            }
+        };
+        if (P.fwd_unroll > 1) {
+            // two edges per iteration, the operand sets alternating: the first half computes on
+            // the c set and loads the n set, the second computes on n and reloads c, so no operand
+            // is copied from one set to the other
+            o("for (; e < e1; e += 2 * stride) {");
+            o.ind++;
+            o("const int enn = (e + 2 * stride < e1) ? e + 2 * stride : e1 - 1;");
+            o("const int snn = col[enn];");
+            emit_edge_loads(o, P, g, t, "n", "sn", "en", true, dbl, radial);
+            barrier();
+            math("c");
+            o("if (e + stride >= e1) break;");
+            o("const int e3 = (e + 3 * stride < e1) ? e + 3 * stride : e1 - 1;");
+            o("const int s3 = col[e3];");
+            emit_edge_loads(o, P, g, t, "c", "snn", "enn", false, dbl, radial);
+            barrier();
+            math("n");
+            o("en = e3;");
+            o("sn = s3;");
+            o.ind--;
+            o("}");
         } else {
-            emit_forward_math(o, P, g, f64, "c");
+            o("for (; e < e1; e += stride) {");
+            o.ind++;
+            o("const int enn = (e + 2 * stride < e1) ? e + 2 * stride : e1 - 1;");
+            o("const int snn = col[enn];");
+            emit_edge_loads(o, P, g, t, "n", "sn", "en", true, dbl, radial);
+            barrier();
+            math("c");
+            emit_copy(o, P, g, t, "c", "n", dbl, radial);
+            o("en = enn;");
+            o("sn = snn;");
+            o.ind--;
+            o("}");
         }
-        emit_copy(o, P, g, t, "c", "n", dbl, radial);
-        o("en = enn;");
-        o("sn = snn;");
-        o.ind--;
-        o("}");
         o.ind--;
         o("}");
         // sum the edge slots (fixed butterfly order, identical in every run)

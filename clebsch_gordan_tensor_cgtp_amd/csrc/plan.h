@@ -91,6 +91,7 @@ struct Plan {
     bool stream_hint = true;        // nontemporal loads/stores for once-touched per-edge rows
     bool scalar_wave = true;        // wave index read from the first lane (uniform, SGPR-held)
     bool permlane_sums = true;      // lane sums over xor 16 / 32 by v_permlane*_swap instead of shuffles
+    int fwd_unroll = 1;             // receiver pass: edges per loop iteration (2: operand sets alternate, no copies)
     bool bwd_sched_barrier = true;  // keep path blocks of the backward from interleaving
     int bwd_rolling = 0;            // sender pass: next edge's operands loaded as this edge frees them (2: pinned by barriers)
     bool fwd_sched_barrier = false; // keep the receiver pass's next-edge loads ahead of its arithmetic

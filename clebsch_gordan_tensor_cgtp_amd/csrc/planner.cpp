@@ -671,6 +671,11 @@ void schedule(Plan &P)
     // slots; the barrier pays there and not on large graphs (one wave per row), so those kernels
     // alone take it (NequIP-like graph: 102 -> 97 us; the 10M-edge plan on a 5,000-node graph 0.59
     // -> 0.44 ms; on 200,000-node graphs 4.61 -> 4.64 and 9.82 -> 10.04 ms with it everywhere).
+    // Split plans' receiver passes take two edges per loop iteration with alternating operand sets
+    // (no operand copies; MACE-like graph: fp32 4.02 -> 4.00 ms, fp64 8.98 -> 8.86-8.95 ms; the
+    // single-group plans measured the same either way and keep one)
+    P.fwd_unroll = P.fwd_sched_barrier ? 2 : 1;
+    if (const char *e = std::getenv("CGTP_FWD_UNROLL")) P.fwd_unroll = std::atoi(e) > 1 ? 2 : 1;
     if (const char *e = std::getenv("CGTP_SPLIT_SCHED_BARRIER")) P.split_sched_barrier = std::atoi(e) != 0;
     // with the barrier those kernels need a few registers more than four waves allow in fp32 (the
     // NequIP-like plan: 134 and no spill at three, a 7-register spill at four)
