@@ -2375,6 +2375,20 @@ void emit_uvc_acc_kernel(Out &o, const Plan &P)
 // component for their 16 rows hit 16 different banks (a stride of d_sh = 64 put them all on one).
 int uvb_dy_stride(const Plan &P) { return P.d_sh | 1; }
 
+// LDS words of the dx/dY kernel: the four waves' dY rows, then one [16][16 (2 l1 + 1) + 1] block
+// per half of a split input block
+int uvb_part_words(const Plan &P, int gi)
+{
+    const Group &g = P.uvb_x_groups[gi];
+    return g.part ? 16 * (16 * (2 * P.ins[P.paths[g.paths[0]].i1].l + 1) + 1) : 0;
+}
+int uvb_part_offset(const Plan &P, int gi)
+{
+    int off = 4 * 16 * uvb_dy_stride(P);
+    for (int k = 0; k < gi; ++k) off += uvb_part_words(P, k);
+    return off;
+}
+
 std::string uvb_u(bool f64, int v) { return f64 ? "(usub + " + std::to_string(4 * v) + ")" : "(4 * usub + " + std::to_string(v) + ")"; }
 
 void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
@@ -2538,9 +2552,19 @@ void emit_uvb_xy_group(Out &o, const Plan &P, int gi)
         o.ind--;
         o("}");
     }
+    if (g.part) {
+        // one half of a split input block: its dx partial goes to the group's LDS rows (row r,
+        // column u (2 l1 + 1) + i), which the kernel adds to the other half's after its barrier
+        const int off = uvb_part_offset(P, gi);
+        for (int v = 0; v < 4; ++v) {
+            const std::string u = uvb_u(f64, v);
+            for (int i = 0; i < n1; ++i)
+                o("dyl[", off, " + rl * ", 16 * n1 + 1, " + ", u, " * ", n1, " + ", i, "] = d", v, "_", i, ";");
+        }
+    }
     o("if (live && dx) {");
     o.ind++;
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < 4 && !g.part; ++v) {
         const std::string u = uvb_u(f64, v);
         o("if (", u, " < ", ir.mul, ") {");
         o.ind++;
@@ -3018,7 +3042,9 @@ void emit_uvb_kernels(Out &o, const Plan &P)
     o("{");
     o.ind++;
     const int dsp = uvb_dy_stride(P);
-    o("__shared__ T dyl[", 4 * 16 * dsp, "];  // per wave 16 dY rows of stride ", dsp);
+    const int nx = (int)P.uvb_x_groups.size();
+    const int lds_words = uvb_part_offset(P, nx);
+    o("__shared__ T dyl[", lds_words, "];  // per wave 16 dY rows of stride ", dsp, ", then the dx halves of split input blocks");
     o("const long blk = blockIdx.x;");
     o("const int wv = WAVE_IN_BLOCK();");
     o("const int lane = threadIdx.x & 63;");
@@ -3047,6 +3073,27 @@ void emit_uvb_kernels(Out &o, const Plan &P)
     o("}");
     o.ind--;
     o("}");
+    // dx of each split input block: first half + second half, stored by all 256 threads
+    for (int gi = 0; gi + 1 < nx; ++gi) {
+        const Group &h1 = P.uvb_x_groups[gi];
+        if (h1.part != 1) continue;
+        const Path &p0 = P.paths[h1.paths[0]];
+        const Irrep &ir = P.ins[p0.i1];
+        const int n1 = n_of(ir.l), cols = ir.mul * n1, rs = 16 * n1 + 1;
+        const int o1 = uvb_part_offset(P, gi), o2 = uvb_part_offset(P, gi + 1);
+        o("if (dx) {");
+        o.ind++;
+        o("for (int c = threadIdx.x; c < ", 16 * cols, "; c += 256) {");
+        o.ind++;
+        o("const int r = c / ", cols, ", col = c - r * ", cols, ";");
+        o("const long row = blk * 16 + r;");
+        o("if (row < nrows) dx[(size_t)row * DX + ", p0.a, " + col] = dyl[", o1, " + r * ", rs, " + col] + dyl[", o2, " + r * ", rs,
+          " + col];");
+        o.ind--;
+        o("}");
+        o.ind--;
+        o("}");
+    }
     o.ind--;
     o("}");
     o("");

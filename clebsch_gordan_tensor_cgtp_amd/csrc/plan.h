@@ -49,6 +49,7 @@ struct Group {
     int es = 1;              // edge slots per wave = 64 / ct
     int tiles = 1;           // channel tiles of width ct covering mul
     bool prefetch = false;   // backward: double-buffer the next edge's operands in registers
+    int part = 0;            // batched uvw dx/dY: 0 the whole input block, 1 / 2 the halves of a split one
 };
 
 struct Plan {

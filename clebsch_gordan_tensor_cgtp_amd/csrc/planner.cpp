@@ -550,6 +550,51 @@ void schedule(Plan &P)
                 if (P.paths[i].i1 == b) g.paths.push_back(i);
             if (!g.paths.empty()) P.uvb_x_groups.push_back(g);
         }
+        // The kernel's four waves per 16-row block take the input blocks by cost; a block heavier
+        // than an eighth of the whole is split into two path halves of about equal cost, which
+        // two waves run (each adds its dx partial in LDS, summed in fixed order at the end), so
+        // that no wave carries much more than a quarter.
+        if (getenv_int("CGTP_UVB_XY_SPLIT", 1)) {
+            auto cost = [&](int pi) {
+                const Path &p = P.paths[pi];
+                return (long)p.nz.size() * 6 + 16L * (2 * p.l3 + 1);
+            };
+            long total = 0;
+            for (const Group &g : P.uvb_x_groups)
+                for (int pi : g.paths) total += cost(pi);
+            std::vector<Group> out;
+            for (const Group &g : P.uvb_x_groups) {
+                long c = 0;
+                for (int pi : g.paths) c += cost(pi);
+                if (g.paths.size() < 2 || 8 * c <= total) {
+                    out.push_back(g);
+                    continue;
+                }
+                Group h1, h2;
+                h1.part = 1;
+                h2.part = 2;
+                long acc = 0;
+                for (int pi : g.paths) {
+                    if (2 * (acc + cost(pi)) <= c || h1.paths.empty())
+                        h1.paths.push_back(pi), acc += cost(pi);
+                    else
+                        h2.paths.push_back(pi);
+                }
+                if (h2.paths.empty()) {
+                    out.push_back(g);
+                    continue;
+                }
+                out.push_back(h1);
+                out.push_back(h2);
+            }
+            // the halves' dx partials live in LDS next to the dY rows: 16 x (16 (2 l1 + 1) + 1)
+            // words per half, within the 160 KB of a workgroup (the fp64 l <= 7 plan does not fit
+            // and keeps its blocks whole)
+            long words = 4L * 16 * (P.d_sh | 1);
+            for (const Group &g : out)
+                if (g.part) words += 16L * (16 * (2 * P.ins[P.paths[g.paths[0]].i1].l + 1) + 1);
+            if (words * (P.dtype == CGTP_F64 ? 8 : 4) <= 160L * 1024) P.uvb_x_groups = out;
+        }
         Group cur;
         for (int i = 0; i < (int)P.paths.size(); ++i) {
             if ((int)cur.paths.size() == (getenv_int("CGTP_UVB_W_PATHS", 8))) {
