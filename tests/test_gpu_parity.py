@@ -132,6 +132,32 @@ def test_conv_edge_cases(device, kind):
     assert rel_l2(gw.cpu().numpy(), dw) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("kind", ["empty", "heavy", "isolated", "selfdup"])
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_split_plan_edge_cases(device, kind, dtype):
+    """A plan split into several path groups (128 channels of l <= 3, SH l <= 3): its receiver
+    pass takes two edges per loop iteration and its sender pass loads the next edge's operands as
+    the current edge frees them; rows of 0, 1 and 2 edges, a 5,000-edge row, self-loops and
+    duplicates exercise the ends of both loops."""
+    spec = synth.ConvSpec("split-edge-" + kind, 300, 0, "128x0e+128x1o+128x2e+128x3o", 3, 3)
+    graph = edge_case_graph(kind, 300, np.random.default_rng(6))
+    case = ConvCase(spec, dtype, seed=3, graph=graph)
+    assert "e += 2 * stride" in cg.plan_for(spec, dtype).source  # the two-edge receiver loop
+    print(f"[split edge] {kind} {dtype} E={case.E}", flush=True)
+    d, y, out, tr, (gx, gy, gw) = run_gpu(case, device)
+    out_h = out.cpu().numpy()
+    deg = np.diff(case.row_ptr)
+    assert np.all(out_h[deg == 0] == 0)
+    if case.E == 0:
+        assert np.all(out_h == 0) and np.all(gx.cpu().numpy() == 0)
+        return
+    assert rel_l2(out_h, case.oracle_forward()) <= TOL[dtype]
+    dx, _, dy, dw = case.oracle_backward()
+    assert rel_l2(gx.cpu().numpy(), dx) <= TOL[dtype]
+    assert rel_l2(gy.cpu().numpy(), dy) <= TOL[dtype]
+    assert rel_l2(gw.cpu().numpy(), dw) <= TOL[dtype]
+
+
 def test_backward_optional_outputs(device):
     import torch
     case = ConvCase(synth.scaled(synth.CONV_NEQUIP, 100, 3_000), "f32", seed=4)
