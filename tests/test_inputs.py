@@ -44,9 +44,9 @@ def test_powerlaw_degrees_full_size():
 def test_powerlaw_graph_exact_draw():
     """The 10M-edge graph is pinned exactly (min 12, max 2,000, 749 capped receivers, median 13,
     99th percentile 743, and a digest of the degree array), so a change to the draw order or to
-    the water-filling rounding is noticed.  (The survey's own derivation of the same rule reports
-    737 capped receivers; its draw is not specified closely enough to reproduce, and the count
-    depends on the raw Zipf draws.)"""
+    the water-filling rounding is noticed.  (Another derivation of the same rule, with its own raw
+    Zipf draws, counts 737 capped receivers: the count depends on the draws, not only on the
+    rule.)"""
     import hashlib
     deg = synth.powerlaw_degrees(200_000, 10_000_000, 2.0, 2000, synth.rng(synth.streams(0)["graph"]))
     assert (int(deg.min()), int(deg.max()), int((deg == 2000).sum())) == (12, 2000, 749)
