@@ -23,7 +23,8 @@ sh       real spherical harmonics (component normalisation)
 wigner   real Wigner D by least squares (for equivariance checks)
 ref      numpy definitions: batched TP (uvu, uvw) and its backward, conv forward,
          backward and double backward (uvu and uvw), the uvw conv forward and backward,
-         the radial-projection conv forward and backward (W = rho Theta)
+         the radial-projection conv forward and backward (W = rho Theta; uvu, and uvw
+         with each edge's own W_p blocks)
 loops    ctypes front-end to ``cpu_loops.c`` (explicit fp64 loops, OpenMP), and
          the double backward, the uvw conv and the radial conv on sampled rows
          composed from those loops

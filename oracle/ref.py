@@ -252,15 +252,67 @@ def conv_double_backward_uvw(prob: Problem, row_ptr, col, x, y, w, g, ggx, ggy, 
     return dx, dy, dw, dg
 
 
+def edge_messages_uvw(prob: Problem, xs: np.ndarray, y: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Per-row uvw tensor product with a weight block of its own per row: w (rows, weight_numel),
+    row r's W_p[u, w] at w[r, w_p + u * mul_out + w] (the fully connected family of the Sobek
+    page, Abstract, with edge-conditioned weights)."""
+    assert prob.mode == "uvw"
+    rows = xs.shape[0]
+    msg = np.zeros((rows, prob.d_out))
+    for p, a, b, o, mul_in, mul_out, nz in _path_terms(prob):
+        n1, n3 = 2 * p.l1 + 1, 2 * p.l3 + 1
+        xb = xs[:, a:a + mul_in * n1].reshape(rows, mul_in, n1)
+        wp = w[:, p.w_off:p.w_off + mul_in * mul_out].reshape(rows, mul_in, mul_out)
+        t = np.zeros((rows, mul_in, n3))
+        for i, j, k, c in nz:
+            t[:, :, k] += c * xb[:, :, i] * y[:, b + j][:, None]
+        msg[:, o:o + mul_out * n3].reshape(rows, mul_out, n3)[...] += np.einsum("ruk,ruw->rwk", t, wp)
+    return msg
+
+
+def edge_backward_uvw(prob: Problem, xs: np.ndarray, y: np.ndarray, w: np.ndarray, gr: np.ndarray):
+    """Gradients of sum(gr * edge_messages_uvw(xs, y, w)) with respect to xs, y and the per-row w.
+    For each path and nonzero (i, j, k, c), with h[r, u, k] = sum_w W_r,p[u, w] gr[r, w, k]:
+      dxs[r, u, i] += c * y[r, j] * h[r, u, k]
+      dy[r, j]     += c * sum_u xs[r, u, i] * h[r, u, k]
+      dW_r,p[u, w] += c * xs[r, u, i] * y[r, j] * gr[r, w, k]"""
+    assert prob.mode == "uvw"
+    rows = xs.shape[0]
+    dxs = np.zeros_like(xs)
+    dy = np.zeros_like(y)
+    dw = np.zeros_like(w)
+    for p, a, b, o, mul_in, mul_out, nz in _path_terms(prob):
+        n1, n3 = 2 * p.l1 + 1, 2 * p.l3 + 1
+        xb = xs[:, a:a + mul_in * n1].reshape(rows, mul_in, n1)
+        dxb = dxs[:, a:a + mul_in * n1].reshape(rows, mul_in, n1)
+        wp = w[:, p.w_off:p.w_off + mul_in * mul_out].reshape(rows, mul_in, mul_out)
+        gb = gr[:, o:o + mul_out * n3].reshape(rows, mul_out, n3)
+        h = np.einsum("ruw,rwk->ruk", wp, gb)
+        t = np.zeros((rows, mul_in, n3))
+        for i, j, k, c in nz:
+            dxb[:, :, i] += c * y[:, b + j][:, None] * h[:, :, k]
+            dy[:, b + j] += c * np.sum(xb[:, :, i] * h[:, :, k], axis=1)
+            t[:, :, k] += c * xb[:, :, i] * y[:, b + j][:, None]
+        dw[:, p.w_off:p.w_off + mul_in * mul_out] += np.einsum("ruk,rwk->ruw", t, gb).reshape(rows, -1)
+    return dxs, dy, dw
+
+
 def conv_forward_radial(prob: Problem, row_ptr, col, x, y, rho, theta):
     """Convolution whose per-edge weights are a radial projection: W_e = rho[e] @ Theta.
 
     Source: Sobek page, Abstract (edge-conditioned weights from a radial projection, which the
     streaming formulation reassociates with the coupling and the aggregation so that W_e is
-    never stored).  rho [E][R] holds each edge's radial features, Theta [R][weight_numel] is
-    shared.  The plain definition: form W = rho @ Theta, then the uvu convolution."""
+    never stored; both operator families).  rho [E][R] holds each edge's radial features, Theta
+    [R][weight_numel] is shared.  The plain definition: form W = rho @ Theta, then the convolution
+    with those per-edge weights (uvu: conv_forward; uvw: each edge's own W_p blocks)."""
     w = np.asarray(rho, np.float64) @ np.asarray(theta, np.float64)
-    return conv_forward(prob, row_ptr, col, x, y, w)
+    if prob.mode == "uvu":
+        return conv_forward(prob, row_ptr, col, x, y, w)
+    x = np.asarray(x, np.float64)
+    col = np.asarray(col, np.int64)
+    out = np.zeros((len(row_ptr) - 1, prob.d_out))
+    np.add.at(out, receivers_of(row_ptr), edge_messages_uvw(prob, x[col], np.asarray(y, np.float64), w))
+    return out
 
 
 def conv_backward_radial(prob: Problem, row_ptr, col, x, y, rho, theta, g):
@@ -269,10 +321,18 @@ def conv_backward_radial(prob: Problem, row_ptr, col, x, y, rho, theta, g):
 
     Sobek page, Abstract: the radial projection is reassociated through the backward as well.  The
     plain definition is the chain rule through W = rho @ Theta (library matmuls):
-      (dx, dy, dW) = conv_backward(x, y, W, g),   drho = dW @ Theta^T,   dTheta = rho^T @ dW."""
+      (dx, dy, dW) = the convolution's gradients with per-edge weights W,
+      drho = dW @ Theta^T,   dTheta = rho^T @ dW."""
     rho = np.asarray(rho, np.float64)
     theta = np.asarray(theta, np.float64)
-    dx, dy, dw = conv_backward(prob, row_ptr, col, x, y, rho @ theta, g)
+    if prob.mode == "uvu":
+        dx, dy, dw = conv_backward(prob, row_ptr, col, x, y, rho @ theta, g)
+    else:
+        x, y, g = (np.asarray(a, np.float64) for a in (x, y, g))
+        col = np.asarray(col, np.int64)
+        dxs, dy, dw = edge_backward_uvw(prob, x[col], y, rho @ theta, g[receivers_of(row_ptr)])
+        dx = np.zeros_like(x)
+        np.add.at(dx, col, dxs)
     return dx, dy, dw @ theta.T, rho.T @ dw
 
 

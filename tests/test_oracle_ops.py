@@ -542,6 +542,65 @@ def test_radial_conv_backward_one_hot_and_adjoint():
     assert abs(lhs - rhs) <= 1e-10 * max(1.0, abs(rhs))
 
 
+def _uvw_radial_case(seed, n_nodes, n_edges, R):
+    prob = _uvw_conv_problem()
+    rng = np.random.default_rng(seed)
+    row_ptr, col = small_graph(rng, n_nodes, n_edges)
+    x = rng.standard_normal((n_nodes, prob.d_in))
+    y = rng.standard_normal((n_edges, prob.d_sh))
+    rho = rng.standard_normal((n_edges, R))
+    theta = rng.standard_normal((R, prob.weight_numel))
+    g = rng.standard_normal((n_nodes, prob.d_out))
+    return prob, rng, row_ptr, col, x, y, rho, theta, g
+
+
+def test_radial_uvw_conv_brute_force_linearity_and_one_hot():
+    """uvw with W_e = rho_e Theta (each edge its own W_p[u][w] blocks): the dense einsum with that W,
+    linear in Theta, and a rho one-hot on channel r equals the shared-weight uvw convolution with
+    Theta's row r."""
+    prob, rng, row_ptr, col, x, y, rho, theta, g = _uvw_radial_case(28, 7, 31, 4)
+    got = ref.conv_forward_radial(prob, row_ptr, col, x, y, rho, theta)
+    msg = np.einsum("abvo,ea,eb,er,rv->eo", dense_tensor(prob), x[col], y, rho, theta)
+    want = np.zeros((7, prob.d_out))
+    np.add.at(want, ref.receivers_of(row_ptr), msg)
+    assert np.allclose(got, want, atol=1e-12)
+    theta2 = rng.standard_normal(theta.shape)
+    both = ref.conv_forward_radial(prob, row_ptr, col, x, y, rho, theta - 3.0 * theta2)
+    assert np.allclose(both, got - 3.0 * ref.conv_forward_radial(prob, row_ptr, col, x, y, rho, theta2), atol=1e-11)
+    onehot = np.zeros_like(rho)
+    onehot[:, 1] = 1.0
+    assert np.allclose(ref.conv_forward_radial(prob, row_ptr, col, x, y, onehot, theta),
+                       ref.conv_forward(prob, row_ptr, col, x, y, theta[1]), atol=1e-12)
+
+
+def test_radial_uvw_conv_backward_matches_autograd_one_hot_and_adjoint():
+    """dx, dy, drho, dTheta of sum(g * conv(x, y, rho Theta)) in uvw mode: torch autograd (CPU,
+    float64) through the dense coupling; a rho one-hot on channel r gives the shared-weight uvw
+    gradients (dTheta zero outside row r); <dTheta, V> = <g, conv(x, y, rho V)>."""
+    import torch
+    prob, rng, row_ptr, col, x, y, rho, theta, g = _uvw_radial_case(29, 8, 33, 5)
+    t = torch.from_numpy(dense_tensor(prob))
+    dst = torch.from_numpy(ref.receivers_of(row_ptr))
+    colt = torch.from_numpy(np.asarray(col, np.int64))
+    X, Y, Rho, Th = (torch.tensor(a, requires_grad=True) for a in (x, y, rho, theta))
+    msg = torch.einsum("abvo,ea,eb,er,rv->eo", t, X[colt], Y, Rho, Th)
+    out = torch.zeros(8, prob.d_out, dtype=torch.float64).index_add(0, dst, msg)
+    want = torch.autograd.grad((torch.from_numpy(g) * out).sum(), (X, Y, Rho, Th))
+    got = ref.conv_backward_radial(prob, row_ptr, col, x, y, rho, theta, g)
+    for a, b in zip(got, want):
+        assert np.allclose(a, b.numpy(), atol=1e-10)
+    onehot = np.zeros_like(rho)
+    onehot[:, 3] = 1.0
+    dx, dy, drho, dtheta = ref.conv_backward_radial(prob, row_ptr, col, x, y, onehot, theta, g)
+    sx, sy, sw = ref.conv_backward_uvw(prob, row_ptr, col, x, y, theta[3], g)
+    assert np.allclose(dx, sx, atol=1e-11) and np.allclose(dy, sy, atol=1e-11)
+    assert np.allclose(dtheta[[0, 1, 2, 4]], 0.0) and np.allclose(dtheta[3], sw, atol=1e-11)
+    v = rng.standard_normal(theta.shape)
+    lhs = float(np.sum(got[3] * v))
+    rhs = float(np.sum(g * ref.conv_forward_radial(prob, row_ptr, col, x, y, rho, v)))
+    assert abs(lhs - rhs) <= 1e-10 * max(1.0, abs(rhs))
+
+
 # ------------------------------------------------------------------------------ batched backward
 
 def _uvw_tp_problem():
