@@ -544,6 +544,122 @@ def bench_radial(a, spec, plan, d, host_graph, device):
     print(json.dumps(line), flush=True)
 
 
+def cpu_baseline_radial_uvw(spec, seed, host_graph, R, max_seconds=30.0, backward=False):
+    """The oracle (oracle.ref: W_e = rho_e Theta formed per edge, then each edge's fully connected
+    product, summed per receiver; with ``backward`` also dx, dY, drho and dTheta) on a contiguous
+    receiver slice of about 2,000 edges (the formed W_e take E x weight_numel values); random
+    values.  Rate = slice edges/s."""
+    from oracle import irreps as oirreps
+    from oracle import ref
+    row_ptr, col = (np.asarray(a, dtype=np.int64) for a in host_graph)
+    N, E = len(row_ptr) - 1, len(col)
+    prob = oirreps.build_problem(spec.in_irreps, oirreps.sh_irreps(spec.lmax_sh), spec.out_irreps, "uvw")
+    rng = np.random.default_rng(seed + 96)
+    start = int(rng.integers(0, max(1, N // 2)))
+    stop = min(max(int(np.searchsorted(row_ptr, row_ptr[start] + 2_000)), start + 1), N)
+    e0, e1 = int(row_ptr[start]), int(row_ptr[stop])
+    sub_ptr = row_ptr[start:stop + 1] - e0
+    uniq, inv = np.unique(col[e0:e1], return_inverse=True)
+    x = rng.standard_normal((len(uniq), prob.d_in))
+    y = rng.standard_normal((e1 - e0, prob.d_sh))
+    rho = rng.standard_normal((e1 - e0, R))
+    theta = rng.standard_normal((R, prob.weight_numel))
+    g = rng.standard_normal((stop - start, prob.d_out))
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):  # numpy's BLAS on one thread, so that `cores` is what ran
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            ref.conv_forward_radial(prob, sub_ptr, inv, x, y, rho, theta)
+            if backward:
+                ref.conv_backward_radial(prob, sub_ptr, inv, x, y, rho, theta, g)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= 10.0 or el >= max_seconds:
+                break
+    what = "forward and backward (dx, dY, drho, dTheta)" if backward else "forward"
+    return {"value": (e1 - e0) * reps / el, "unit": "edges/s", "cores": 1, "kind": "oracle",
+            "sample": f"receivers [{start},{stop}) = {e1 - e0} of {E} edges, R = {R}: W_e = rho_e Theta formed "
+                      f"for those edges, then the fp64 numpy definition, {what}; mean of {reps} rep(s)"}
+
+
+def bench_radial_uvw(a, spec, plan, d, host_graph, device):
+    """uvw convolution with per-edge weights W_e = rho_e Theta: one step = conv_forward_radial (with
+    --backward: + conv_backward_radial for dx, dY, drho, dTheta).  Each radial channel r runs the
+    shared-weight uvw kernels on rho[:, r] * Y with Theta's row r; W_e is never formed."""
+    import torch
+    from clebsch_gordan_tensor_cgtp_amd import binding as cg
+    from clebsch_gordan_tensor_cgtp_amd import synth
+    R = a.radial
+    N, E = d["row_ptr"].shape[0] - 1, d["col"].shape[0]
+    npdt = np.float32 if a.dtype == "f32" else np.float64
+    up = synth.upstream_streams(a.seed)
+    rho = torch.from_numpy(synth.normal(up["gg_y"], (E, R), dtype=npdt)).to(device)
+    theta = torch.from_numpy(synth.normal(up["gg_w"], (R, plan.weight_numel), 1.0 / np.sqrt(R * E / N),
+                                          dtype=npdt)).to(device)
+    y = cg.spherical_harmonics(spec.lmax_sh, d["vec"])
+    order = cg.graph_order(d["row_ptr"]) if not a.natural_order else None
+    out = torch.empty((N, plan.d_out), dtype=plan.torch_dtype, device=device)
+    plan.radial_source(R)  # JIT outside the timed region
+    tr = cg.graph_transpose(d["row_ptr"], d["col"])
+    ws = torch.empty(max(1, cg.conv_backward_radial_workspace_size(plan, N, E, R)), dtype=torch.uint8, device=device)
+    outs = (torch.empty_like(d["x"]), torch.empty_like(y), torch.empty_like(rho), torch.empty_like(theta))
+    fwd = lambda: cg.conv_forward_radial(plan, d["row_ptr"], d["col"], d["x"], y, rho, theta, out=out, order=order)
+    bwd = lambda: cg.conv_backward_radial(plan, d["row_ptr"], d["col"], tr, d["x"], y, rho, theta, d["g"],
+                                          outs=outs, workspace=ws)
+
+    def step(ev):
+        ev[0].record()
+        fwd()
+        ev[1].record()
+        if a.backward:
+            bwd()
+        ev[2].record()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(max(a.steps, a.warmup))]
+    for k in range(a.warmup):
+        step(evs[k])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(a.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / a.steps
+    evs = evs[:a.steps]
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    sparse, dense = uvw_conv_flops(plan, N, E)
+    # counting convention: R times the shared-weight uvw passes (forward sparse + dense; backward
+    # dx/dY (dense + 2 sparse) and dTheta (sparse + dense)); the SH scaling and the fold are E d_sh
+    # multiplies per channel, not counted
+    phases = [("conv_forward_radial (R x cgtp_conv_uvw_rad)", ms, R * (sparse + dense))]
+    config = {"workload": spec.name, "N": N, "E": E, "in_irreps": spec.in_irreps, "out_irreps": spec.out_irreps,
+              "sh_lmax": spec.lmax_sh, "paths": plan.num_paths, "d_out": plan.d_out, "radial_features": R,
+              "step": "conv_forward_radial (uvw; W_e = rho_e Theta never formed)",
+              "receiver_schedule": "natural" if a.natural_order else "heavy-first", "fwd_ms": ms,
+              "formed_weights_bytes_avoided": E * plan.weight_numel * (4 if a.dtype == "f32" else 8)}
+    if a.backward:
+        bms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        phases.append(("conv_backward_radial (per channel: scale, G, sender pass, fold, dW pass)", bms,
+                       R * (3 * sparse + 2 * dense)))
+        config.update({"step": "conv_forward_radial + conv_backward_radial (uvw; dx, dY, drho, dTheta)",
+                       "bwd_ms": bms, "workspace_bytes": int(ws.numel())})
+    dom = max(phases, key=lambda p: p[1])
+    tflops = dom[2] / (dom[1] * 1e-3) / 1e12
+    peak = 157.3 if a.dtype == "f32" else 78.6
+    line = {
+        "metric": METRIC, "value": E / wall, "unit": "edges/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": wall * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": a.dtype, "data": "synthetic", "config": config,
+        "roofline": {"bound": "alu", "kernel": dom[0], "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": tflops / peak, "traffic": None, "flops_per_launch": dom[2], "avg_launch_ms": dom[1],
+                     "phases": [{"kernel": p[0], "avg_ms": p[1], "flops": p[2]} for p in phases]},
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_radial_uvw(spec, a.seed, host_graph, R, backward=a.backward)
+    print(json.dumps(line), flush=True)
+
+
 def spread(evs):
     """Median, min and max over the timed steps of the forward and backward launch times."""
     f = [e[0].elapsed_time(e[1]) for e in evs]
@@ -875,6 +991,8 @@ def main():
         spec = synth.scaled(spec, a.nodes, a.edges)
     plan, d, host_graph = make_inputs(spec, a.dtype, a.seed, device)
     if spec.mode == "uvw":
+        if a.radial:
+            return bench_radial_uvw(a, spec, plan, d, host_graph, device)
         return bench_conv_uvw(a, spec, plan, d, host_graph, device)
     if a.radial:
         return bench_radial(a, spec, plan, d, host_graph, device)

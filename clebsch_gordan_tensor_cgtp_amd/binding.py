@@ -388,7 +388,8 @@ def conv_backward_radial_workspace_size(plan: Plan, N: int, E: int, R: int) -> i
 def conv_backward_radial(plan: Plan, row_ptr, col, transpose, x, y, rho, theta, grad_out, outs=(None, None, None, None),
                          need=(True, True, True, True), workspace=None, stream=None):
     """Backward of the radial-projection convolution: (grad_x, grad_y, grad_rho, grad_theta); entries
-    not in ``need`` are None and not computed.  The dTheta workspace is allocated here unless given."""
+    not in ``need`` are None and not computed.  The workspace (uvu: dTheta partials; uvw: those,
+    G and two SH-sized rows per edge) is allocated here unless given."""
     import torch
     N, E = row_ptr.shape[0] - 1, col.shape[0]
     R = theta.shape[0]
@@ -397,7 +398,7 @@ def conv_backward_radial(plan: Plan, row_ptr, col, transpose, x, y, rho, theta, 
     shapes = ((N, plan.d_x), (E, plan.d_sh), (E, R), (R, plan.weight_numel))
     res = [None if not nd else (torch.empty(sh, dtype=dt, device=dev) if o is None else o)
            for o, nd, sh in zip(outs, need, shapes)]
-    nbytes = conv_backward_radial_workspace_size(plan, N, E, R) if res[3] is not None else 0
+    nbytes = conv_backward_radial_workspace_size(plan, N, E, R) if res[3] is not None or plan.mode == "uvw" else 0
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     ws = ctypes.c_void_p(0) if workspace is None else ctypes.c_void_p(workspace.data_ptr())

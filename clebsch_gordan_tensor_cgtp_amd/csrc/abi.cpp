@@ -180,6 +180,84 @@ size_t conv_uvw_workspace(const cgtp::Plan &P, int64_t N, size_t *g_bytes)
     return gb + (size_t)((N + 15) / 16) * P.w_numel * es;
 }
 
+// Workspace of the uvw radial backward, each part 256-byte aligned: G (as the uvw backward), the
+// dTheta partials of every radial channel (R x 16-receiver tiles x weight_numel), the scaled SH
+// rows rho[:, r] y of the current channel and that channel's SH-row gradient (E x d_sh each).
+struct uvw_radial_parts {
+    size_t g = 0, part = 0, ys = 0, t = 0;
+};
+
+size_t uvw_radial_workspace(const cgtp::Plan &P, int64_t N, int64_t E, int R, uvw_radial_parts *parts)
+{
+    if (N == 0) return 0;
+    const size_t es = elem(P);
+    auto pad = [](size_t b) { return (b + 255) / 256 * 256; };
+    size_t gb = 0;
+    conv_uvw_workspace(P, N, &gb);
+    uvw_radial_parts q;
+    q.g = 0;
+    q.part = gb;
+    q.ys = q.part + pad((size_t)R * ((N + 15) / 16) * P.w_numel * es);
+    q.t = q.ys + pad((size_t)E * P.d_sh * es);
+    if (parts) *parts = q;
+    return q.t + pad((size_t)E * P.d_sh * es);
+}
+
+// The uvw radial backward, channel by channel: with ys = rho[:, r] y and G_r = Theta_r^T g,
+// dTheta_r is the uvw dW pass on (x, ys); the unit-weight sender pass on (x, ys, G_r) adds channel
+// r's share to dx and yields t = d/dys, which the fold turns into dY += rho[:, r] t and
+// drho[:, r] = <y, t>.  Channel 0 writes dx and dY, later channels add; dTheta_r is the sum of its
+// tile partials in tile order.
+void uvw_radial_backward(cgtp::Plan &P, int64_t N, int64_t E, const int32_t *row_ptr, const int32_t *col,
+                         const int32_t *t_row_ptr, const int32_t *t_edge, const int32_t *t_dst, const void *x,
+                         const void *y, int R, const void *rho, const void *theta, const void *grad_out, void *grad_x,
+                         void *grad_y, void *grad_rho, void *grad_theta, void *workspace, const uvw_radial_parts &q,
+                         void *stream)
+{
+    const auto &F = cgtp::conv_uvw_backward_for_current_device(P);
+    const size_t es = elem(P);
+    const bool f64 = P.dtype == CGTP_F64;
+    if (N == 0) {
+        if (grad_theta) launch_reduce(F.reduce, (int64_t)R * P.w_numel, workspace, 0, grad_theta, stream);
+        return;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    void *G = ws + q.g, *ys = ws + q.ys, *t = ws + q.t;
+    long nrows = (long)N;
+    const unsigned tiles = (unsigned)((N + 15) / 16);
+    const unsigned threads = 1024u / (unsigned)P.uvc_rpw;
+    const bool need_t = grad_y || grad_rho;
+    const int32_t *order = nullptr;
+    for (int r = 0; r < R; ++r) {
+        const void *th = static_cast<const char *>(theta) + (size_t)r * P.w_numel * es;
+        check_hip(cgtp::launch_radial_scale(f64, E, P.d_sh, R, r, y, rho, ys, st), "radial scale");
+        if (grad_theta) {
+            void *part = ws + q.part + (size_t)r * tiles * P.w_numel * es;
+            for (int grp = 0; grp < (int)P.uvc_groups.size(); ++grp) {
+                void *args[] = {&row_ptr, &col, &x, &ys, &grad_out, &part, &nrows, &order, &grp};
+                check_hip(hipModuleLaunchKernel(F.w, tiles, 1, 1, threads, 1, 1, 0, st, args, nullptr),
+                          "hipModuleLaunchKernel");
+            }
+        }
+        if (grad_x || need_t) {
+            long nwaves = (long)tiles * (long)cgtp::conv_uvw_g_items(P, nullptr);
+            void *gargs[] = {&th, &grad_out, &G, &nrows, &nwaves};
+            launch(F.g, nwaves, gargs, stream);
+            cgtp::Plan &A = cgtp::conv_uvw_aux_plan(P);
+            sender_pass(A, N, E, t_row_ptr, t_edge, t_dst, x, ys, nullptr, G, grad_x, need_t ? t : nullptr, nullptr,
+                        stream, r > 0 ? 1 : 0);
+            if (need_t)
+                check_hip(cgtp::launch_radial_fold(f64, E, P.d_sh, R, r, y, rho, t, grad_y, grad_rho, r > 0 ? 1 : 0, st),
+                          "radial fold");
+        }
+    }
+    if (grad_theta)
+        for (int r = 0; r < R; ++r)
+            launch_reduce(F.reduce, P.w_numel, ws + q.part + (size_t)r * tiles * P.w_numel * es, (long)tiles,
+                          static_cast<char *>(grad_theta) + (size_t)r * P.w_numel * es, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -591,8 +669,13 @@ cgtp_status cgtp_plan_radial_prepare(const cgtp_plan *plan, int32_t R)
     return guarded([&] {
         require(plan != nullptr, "plan is NULL");
         cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
-        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "the radial projection takes uvu plans");
         require(R >= 1 && R <= 64, "R (radial features per edge) must be in [1, 64]");
+        if (P.mode == CGTP_UVW) {
+            // uvw: the kernels of the shared-weight uvw convolution module, one launch per channel
+            if (!P.uvc_ok) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, P.uvc_why);
+            cgtp::prepare_conv_uvw_backward(P);
+            return;
+        }
         check_radial_fwd(P, R);
         cgtp::prepare_radial(P, R);
     });
@@ -603,6 +686,7 @@ const char *cgtp_plan_radial_source(const cgtp_plan *plan, int32_t R)
     if (!plan) return nullptr;
     cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
     std::lock_guard<std::mutex> lock(P.mu);
+    if (P.mode == CGTP_UVW) return P.ucb.code.empty() ? nullptr : P.ucb.source.c_str();
     auto it = P.radial.find(R);
     return it == P.radial.end() ? nullptr : it->second.source.c_str();
 }
@@ -615,10 +699,11 @@ cgtp_status cgtp_conv_forward_radial(const cgtp_plan *plan, int64_t N, int64_t E
         require(plan != nullptr, "plan is NULL");
         cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
         check_graph_sizes(N, E);
-        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "the radial projection takes uvu plans");
         require(R >= 1 && R <= 64, "R (radial features per edge) must be in [1, 64]");
+        const bool uvw = P.mode == CGTP_UVW;
         const size_t es = elem(P);
-        check_radial_fwd(P, R);
+        if (uvw && !P.uvc_ok) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, P.uvc_why);
+        if (!uvw) check_radial_fwd(P, R);
         if (N == 0) return;
         require_ptr(row_ptr, "row_ptr", 4);
         require_ptr(out, "out", es);
@@ -638,6 +723,26 @@ cgtp_status cgtp_conv_forward_radial(const cgtp_plan *plan, int64_t N, int64_t E
         require_disjoint(out, no, "out", row_ptr, (N + 1) * 4, "row_ptr");
         require_disjoint(out, no, "out", col, E * 4, "col");
         require_disjoint(out, no, "out", order, N * 4, "order");
+        if (uvw) {
+            // channel r: the uvw convolution of (rho[:, r] y) with Theta's row r; channel 0 writes,
+            // the others add, each one launch per path group in order
+            const auto &F = cgtp::conv_uvw_backward_for_current_device(P);
+            long nrows = (long)N;
+            const unsigned tiles = (unsigned)((N + 15) / 16);
+            const unsigned threads = 1024u / (unsigned)P.uvc_rpw;
+            int nrad = R;
+            for (int r = 0; r < R; ++r) {
+                int acc = r > 0 ? 1 : 0, rr = r;
+                const void *th = static_cast<const char *>(theta) + (size_t)r * P.w_numel * es;
+                for (int grp = 0; grp < (int)P.uvc_groups.size(); ++grp) {
+                    void *args[] = {&row_ptr, &col, &x, &y, &th, &out, &nrows, &order, &grp, &acc, &rho, &nrad, &rr};
+                    check_hip(hipModuleLaunchKernel(F.fwd_rad, tiles, 1, 1, threads, 1, 1, 0,
+                                                    static_cast<hipStream_t>(stream), args, nullptr),
+                              "hipModuleLaunchKernel");
+                }
+            }
+            return;
+        }
         hipFunction_t f = cgtp::radial_functions_for_current_device(P, R).fwd;
         // one wave per row: splitting rows measured no faster here (each extra workgroup
         // stages Theta again; N = 5,000, R = 8: 121 / 121 / 140 us for 1 / 2 / 4 parts).
@@ -655,6 +760,10 @@ cgtp_status cgtp_conv_backward_radial_workspace_size(const cgtp_plan *plan, int6
         require(plan != nullptr && bytes != nullptr, "plan and bytes must be non-NULL");
         check_graph_sizes(N, E);
         require(R >= 1 && R <= 64, "R (radial features per edge) must be in [1, 64]");
+        if (plan->p.mode == CGTP_UVW) {
+            *bytes = uvw_radial_workspace(plan->p, N, E, R, nullptr);
+            return;
+        }
         long spc, nchunks;
         radial_chunks(N, spc, nchunks);
         *bytes = (size_t)nchunks * R * plan->p.w_numel * elem(plan->p);
@@ -672,15 +781,18 @@ cgtp_status cgtp_conv_backward_radial(const cgtp_plan *plan, int64_t N, int64_t 
         require(plan != nullptr, "plan is NULL");
         cgtp::Plan &P = const_cast<cgtp_plan *>(plan)->p;
         check_graph_sizes(N, E);
-        if (P.mode != CGTP_UVU) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, "the radial projection takes uvu plans");
         require(R >= 1 && R <= 64, "R (radial features per edge) must be in [1, 64]");
+        const bool uvw = P.mode == CGTP_UVW;
+        if (uvw && !P.uvc_ok) throw cgtp::Error(CGTP_ERR_UNSUPPORTED, P.uvc_why);
         const size_t es = elem(P);
         if (!grad_x && !grad_y && !grad_rho && !grad_theta) return;
         const size_t nth = (size_t)R * P.w_numel * es;
         if (grad_theta) require_ptr(grad_theta, "grad_theta", es);
         long spc, nchunks;
         radial_chunks(N, spc, nchunks);
-        const size_t ws_need = grad_theta ? (size_t)nchunks * nth : 0;
+        uvw_radial_parts parts{};
+        const size_t ws_need = uvw ? (N > 0 ? uvw_radial_workspace(P, N, E, R, &parts) : 0)
+                                   : grad_theta ? (size_t)nchunks * nth : 0;
         if (N > 0) {
             require_ptr(row_ptr, "row_ptr", 4);
             require_ptr(t_row_ptr, "t_row_ptr", 4);
@@ -712,6 +824,11 @@ cgtp_status cgtp_conv_backward_radial(const cgtp_plan *plan, int64_t N, int64_t 
                 for (int b = 0; b < 10; ++b) require_disjoint(outs[a], outn[a], outm[a], ins[b], inn[b], inm[b]);
                 for (int b = a + 1; b < 5; ++b) require_disjoint(outs[a], outn[a], outm[a], outs[b], outn[b], outm[b]);
             }
+        }
+        if (uvw) {
+            uvw_radial_backward(P, N, E, row_ptr, col, t_row_ptr, t_edge, t_dst, x, y, R, rho, theta, grad_out,
+                                grad_x, grad_y, grad_rho, grad_theta, workspace, parts, stream);
+            return;
         }
         const auto &F = cgtp::radial_functions_for_current_device(P, R);
         if (!F.bwd)

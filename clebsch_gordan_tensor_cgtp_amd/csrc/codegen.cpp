@@ -2078,7 +2078,7 @@ void emit_tsw(Out &o)
 // uvw convolution, edge stream of one path group: each wave accumulates the unweighted per-path
 // sums T_p[u][k] of its receivers' edges (rows r of the tile `tile`) and stages them in LDS as
 // [p,k][u][row] at the offsets `loff`.  Shared by the forward and the dW pass.
-void emit_uvc_phase_a(Out &o, const Plan &P, const Group &g, std::map<int, int> &loff)
+void emit_uvc_phase_a(Out &o, const Plan &P, const Group &g, std::map<int, int> &loff, bool rad = false)
 {
     Touch t = touched(P, g.paths);
     const bool f64 = P.dtype == CGTP_F64;
@@ -2118,12 +2118,14 @@ void emit_uvc_phase_a(Out &o, const Plan &P, const Group &g, std::map<int, int> 
                     o(Ty, pre, "x", b, "_", i, " = ", addr.str(), ";");
             }
         }
+        // radial variant: the edge's SH values scaled by its radial feature rr (rho_e[rr] y_e)
+        if (rad) o("const T ", pre, "rs = rho[(size_t)", ei, " * nrad + rr];");
         for (int b : t.i2) {
             int off = 0;
             for (int pi : g.paths)
                 if (P.paths[pi].i2 == b) off = P.paths[pi].b;
             for (int j = 0; j < n_of(P.sh[b].l); ++j)
-                o(Ty, pre, "y", b, "_", j, " = y[(size_t)", ei, " * DSH + ", off + j, "];");
+                o(Ty, pre, "y", b, "_", j, " = y[(size_t)", ei, " * DSH + ", off + j, "]", rad ? " * " + pre + "rs" : "", ";");
         }
     };
     auto copy = [&]() {
@@ -2196,8 +2198,9 @@ void emit_uvc_phase_a(Out &o, const Plan &P, const Group &g, std::map<int, int> 
     o("}");  // receivers of the wave
 }
 
-void emit_uvc_group(Out &o, const Plan &P, int gi, bool acc_variant = false)
+void emit_uvc_group(Out &o, const Plan &P, int gi, int variant = 0)
 {
+    const bool acc_variant = variant > 0, rad = variant == 2;
     const Group &g = P.uvc_groups[gi];
     const bool f64 = P.dtype == CGTP_F64;
     Touch t = touched(P, g.paths);
@@ -2215,14 +2218,15 @@ void emit_uvc_group(Out &o, const Plan &P, int gi, bool acc_variant = false)
         lds_elems += 16 * uvc_mu_pad(P.paths[pi]) * n_of(P.paths[pi].l3);
     }
     emit_tsw(o);
-    o("__device__ __forceinline__ void ", acc_variant ? "uvca_g" : "uvc_g", gi,
+    o("__device__ __forceinline__ void ", rad ? "uvcr_g" : acc_variant ? "uvca_g" : "uvc_g", gi,
       "(long tile, int wv, int lane, const int* __restrict__ row_ptr, const int* __restrict__ col, "
       "const T* __restrict__ x, const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows, "
-      "const int* __restrict__ order, T* lds", acc_variant ? ", int acc" : "", ")");
+      "const int* __restrict__ order, T* lds", acc_variant ? ", int acc" : "",
+      rad ? ", const T* __restrict__ rho, int nrad, int rr" : "", ")");
     o("{");
     o.ind++;
     const int nw = 16 / P.uvc_rpw;  // waves per workgroup
-    emit_uvc_phase_a(o, P, g, loff);
+    emit_uvc_phase_a(o, P, g, loff, rad);
     o("__syncthreads();");
     // mixing on MFMA: items (slot q, 16-wide block of output channels), round-robin over the waves
     o("const int usub = lane >> 4;");
@@ -2340,7 +2344,7 @@ void emit_uvc_kernel(Out &o, const Plan &P)
 // add to it), for the double backward's d/dgrad_out, a sum of three such convolutions.
 void emit_uvc_acc_kernel(Out &o, const Plan &P)
 {
-    for (int gi = 0; gi < (int)P.uvc_groups.size(); ++gi) emit_uvc_group(o, P, gi, true);
+    for (int gi = 0; gi < (int)P.uvc_groups.size(); ++gi) emit_uvc_group(o, P, gi, 1);
     o("extern \"C\" __global__ void __launch_bounds__(", 1024 / P.uvc_rpw, ", ", P.uvc_waves_per_eu,
       ") cgtp_conv_uvw_acc(const int* __restrict__ row_ptr, const int* __restrict__ col, const T* __restrict__ x, "
       "const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows, "
@@ -2354,6 +2358,33 @@ void emit_uvc_acc_kernel(Out &o, const Plan &P)
     o("switch (group) {");
     for (int gi = 0; gi < (int)P.uvc_groups.size(); ++gi)
         o("case ", gi, ": uvca_g", gi, "(tile, wv, lane, row_ptr, col, x, y, w, out, nrows, order, lds, acc); break;");
+    o("default: break;");
+    o("}");
+    o.ind--;
+    o("}");
+    o("");
+}
+
+// The uvw convolution with radially projected weights, one radial channel per launch: the edge's
+// SH values enter scaled by rho[e][rr] and the mixing uses Theta's row rr as W (by linearity the
+// sum over rr of these launches is the convolution with W_e = rho_e Theta, whose per-edge blocks
+// are never formed); `acc` as in cgtp_conv_uvw_acc.
+void emit_uvc_rad_kernel(Out &o, const Plan &P)
+{
+    for (int gi = 0; gi < (int)P.uvc_groups.size(); ++gi) emit_uvc_group(o, P, gi, 2);
+    o("extern \"C\" __global__ void __launch_bounds__(", 1024 / P.uvc_rpw, ", ", P.uvc_waves_per_eu,
+      ") cgtp_conv_uvw_rad(const int* __restrict__ row_ptr, const int* __restrict__ col, const T* __restrict__ x, "
+      "const T* __restrict__ y, const T* __restrict__ w, T* __restrict__ out, long nrows, "
+      "const int* __restrict__ order, int group, int acc, const T* __restrict__ rho, int nrad, int rr)");
+    o("{");
+    o.ind++;
+    o("__shared__ T lds[", uvc_lds_elems(P), "];  // T of the tile's 16 receivers, [p,k][u][row] (rows swizzled)");
+    o("const long tile = blockIdx.x;");
+    o("const int wv = WAVE_IN_BLOCK();");
+    o("const int lane = threadIdx.x & 63;");
+    o("switch (group) {");
+    for (int gi = 0; gi < (int)P.uvc_groups.size(); ++gi)
+        o("case ", gi, ": uvcr_g", gi, "(tile, wv, lane, row_ptr, col, x, y, w, out, nrows, order, lds, acc, rho, nrad, rr); break;");
     o("default: break;");
     o("}");
     o.ind--;
@@ -3375,6 +3406,8 @@ std::string generate_conv_uvw_backward_source(const Plan &P)
     emit_ucb_kernels(o, P);
     o("// @@section cgtp_conv_uvw_acc");
     emit_uvc_acc_kernel(o, P);
+    o("// @@section cgtp_conv_uvw_rad");
+    emit_uvc_rad_kernel(o, P);
     return o.s.str();
 }
 

@@ -356,6 +356,7 @@ const Plan::ConvUvwBackward::Fns &conv_uvw_backward_for_current_device(Plan &P)
     check(hipModuleGetFunction(&F.w, F.module, "cgtp_conv_uvw_bwd_w"), "hipModuleGetFunction(conv_uvw_bwd_w)");
     check(hipModuleGetFunction(&F.reduce, F.module, "cgtp_reduce_chunks"), "hipModuleGetFunction(reduce)");
     check(hipModuleGetFunction(&F.fwd_acc, F.module, "cgtp_conv_uvw_acc"), "hipModuleGetFunction(conv_uvw_acc)");
+    check(hipModuleGetFunction(&F.fwd_rad, F.module, "cgtp_conv_uvw_rad"), "hipModuleGetFunction(conv_uvw_rad)");
     return P.ucb.loaded.emplace(dev, F).first->second;
 }
 

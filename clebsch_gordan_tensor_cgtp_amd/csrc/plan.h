@@ -152,6 +152,7 @@ struct Plan {
             hipModule_t module = nullptr;
             hipFunction_t g = nullptr, w = nullptr, reduce = nullptr;
             hipFunction_t fwd_acc = nullptr;  // the forward, adding to its output (double backward)
+            hipFunction_t fwd_rad = nullptr;  // the forward for one radial channel (radial projection)
         };
         std::map<int, Fns> loaded;  // per device
     } ucb;

@@ -311,6 +311,72 @@ hipError_t launch_iota(int64_t n, int32_t *a, hipStream_t st)
 }
 
 // ------------------------------------------------------------------------------------------
+// radial projection of the uvw convolution, one radial channel r at a time (Sobek page,
+// Abstract: W_e = rho_e Theta reassociated with the coupling, so that per-edge W blocks are never
+// formed).  The coupling is linear in Y, so channel r's share of the convolution is the
+// shared-weight convolution of rho[:, r] * Y with Theta's row r.
+
+// ys[e][j] = y[e][j] * rho[e][r]
+template <typename T>
+__global__ void __launch_bounds__(256) radial_scale_rows(int64_t E, int D, int R, int r, const T *__restrict__ y,
+                                                         const T *__restrict__ rho, T *__restrict__ ys)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= E * D) return;
+    ys[i] = y[i] * rho[(i / D) * R + r];
+}
+
+// With t[e] the gradient of channel r's convolution with respect to its scaled SH row:
+// gy[e] (+)= rho[e][r] t[e] (the chain rule through ys = rho y; `acc` 0 writes), grho[e][r] =
+// sum_j y[e][j] t[e][j] (j ascending), then t[e] = 0 for the next channel's accumulation.
+template <typename T>
+__global__ void __launch_bounds__(256) radial_fold_rows(int64_t E, int D, int R, int r, const T *__restrict__ y,
+                                                        const T *__restrict__ rho, T *__restrict__ t,
+                                                        T *__restrict__ gy, T *__restrict__ grho, int acc)
+{
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= E) return;
+    const T s = rho[e * R + r];
+    T d = 0;
+    for (int j = 0; j < D; ++j) {
+        const T v = t[e * D + j];
+        if (gy) gy[e * D + j] = acc ? gy[e * D + j] + s * v : s * v;
+        d += y[e * D + j] * v;
+        t[e * D + j] = 0;
+    }
+    if (grho) grho[e * R + r] = d;
+}
+
+hipError_t launch_radial_scale(bool f64, int64_t E, int D, int R, int r, const void *y, const void *rho, void *ys,
+                               hipStream_t st)
+{
+    const int64_t n = E * D;
+    if (n == 0) return hipSuccess;
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (f64)
+        hipLaunchKernelGGL(radial_scale_rows<double>, grid, dim3(256), 0, st, E, D, R, r, (const double *)y,
+                           (const double *)rho, (double *)ys);
+    else
+        hipLaunchKernelGGL(radial_scale_rows<float>, grid, dim3(256), 0, st, E, D, R, r, (const float *)y,
+                           (const float *)rho, (float *)ys);
+    return hipGetLastError();
+}
+
+hipError_t launch_radial_fold(bool f64, int64_t E, int D, int R, int r, const void *y, const void *rho, void *t,
+                              void *gy, void *grho, int acc, hipStream_t st)
+{
+    if (E == 0) return hipSuccess;
+    const dim3 grid((unsigned)((E + 255) / 256));
+    if (f64)
+        hipLaunchKernelGGL(radial_fold_rows<double>, grid, dim3(256), 0, st, E, D, R, r, (const double *)y,
+                           (const double *)rho, (double *)t, (double *)gy, (double *)grho, acc);
+    else
+        hipLaunchKernelGGL(radial_fold_rows<float>, grid, dim3(256), 0, st, E, D, R, r, (const float *)y,
+                           (const float *)rho, (float *)t, (float *)gy, (float *)grho, acc);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
 // scratch of the allocation-free entry point (cgtp_tp_backward_noalloc): a file-scope device
 // array, so the library never has to allocate device memory for it.  In host code `scratch` is
 // only a handle for the runtime, never a device address: the device address is looked up once

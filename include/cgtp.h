@@ -259,6 +259,18 @@ cgtp_status cgtp_conv_forward_ordered(const cgtp_plan *plan, int64_t N, int64_t 
  * else CGTP_ERR_UNSUPPORTED before any GPU work).  1 <= R <= 64.  The kernel for a given R is generated
  * and compiled on the first call with that R (then cached).  Everything else
  * (CSR, schedule `order`, layouts, determinism) as cgtp_conv_forward_ordered.
+ *
+ * For a uvw plan (the fully connected family of the same passage) each edge
+ * has its own blocks W_e,p[u][w] = sum_r rho[e][r] Theta[r][w_p + u mul_out + w],
+ * out[n] = sum_e TP_uvw(x[col[e]], y[e], W_e).  The coupling is linear in y, so
+ * radial channel r contributes the shared-weight uvw convolution of
+ * rho[:, r] * y with Theta's row r: R launch rounds of the uvw convolution
+ * kernel (the scaling done as each edge's SH values are loaded; channel 0
+ * writes `out`, the others add, in order), with no per-edge weights formed
+ * and no workspace.  CGTP_ERR_UNSUPPORTED when the plan's uvw convolution is
+ * unsupported (cgtp_conv_forward_ordered's LDS limit).  cgtp_plan_radial_prepare then
+ * compiles the uvw convolution module (any R) and cgtp_plan_radial_source
+ * returns its source.
  */
 /* Generate and compile the radial kernel for R now (host only, no device needed), e.g. to
  * move the JIT cost out of the first call; its source is then cgtp_plan_radial_source (owned
@@ -288,8 +300,17 @@ cgtp_status cgtp_conv_forward_radial(const cgtp_plan *plan, int64_t N, int64_t E
  * needed only for grad_theta); outputs are overwritten, no atomics, bitwise
  * deterministic.  N = 0 sets grad_theta to zero.  1 <= R <= 64;
  * CGTP_ERR_UNSUPPORTED when one path group's Theta columns (R x its channels)
- * and the reduction buffer do not fit one workgroup's 160 KB of LDS.  uvu
- * plans only.
+ * and the reduction buffer do not fit one workgroup's 160 KB of LDS.
+ *
+ * uvw plans, radial channel by channel (ys = rho[:, r] * y, G_r = Theta_r^T g
+ * per receiver): dTheta_r is the uvw weight-gradient pass on (x, ys) (tile
+ * partials summed in tile order), the unit-weight sender pass on (x, ys, G_r)
+ * adds channel r's share to grad_x and yields t = d/dys, folded into
+ * grad_y += rho[:, r] t and grad_rho[:, r] = <y, t> (channel 0 writes).  The
+ * workspace is needed whenever N > 0 (any output requested): G, R x
+ * ceil(N / 16) dTheta partials and two E x d_sh rows (the scaled SH and t),
+ * each part 256-byte aligned; cgtp_conv_backward_radial_workspace_size gives
+ * the total.  No per-edge weight or weight gradient is formed.
  */
 cgtp_status cgtp_conv_backward_radial_workspace_size(const cgtp_plan *plan, int64_t N, int64_t E, int32_t R,
                                                     size_t *bytes);
