@@ -270,6 +270,17 @@ def test_conv_uvw_backward_workspace_and_modules():
     assert "&w[" not in src_xy and "dw[" not in src_xy
     for src in (src_gw, src_xy):
         assert "atomic" not in src.lower()
+    # the radial projection in uvw mode: the forward kernel of radial channel rr scales the SH
+    # values by rho as it loads them; its backward workspace is G, R x tiles dTheta partials and
+    # two SH-sized rows per edge, each part 256-byte aligned
+    assert "cgtp_conv_uvw_rad" in src_gw and "rho[(size_t)" in src_gw
+    pad = lambda b: (b + 255) // 256 * 256
+    N, E, R = 5000, 200_000, 8
+    tiles, es = (N + 15) // 16, 4
+    gb = cg.conv_backward_workspace_size(plan, N, E) - tiles * plan.weight_numel * es
+    assert cg.conv_backward_radial_workspace_size(plan, N, E, R) == (
+        gb + pad(R * tiles * plan.weight_numel * es) + 2 * pad(E * plan.d_sh * es))
+    assert cg.conv_backward_radial_workspace_size(plan, 0, 0, R) == 0
 
 
 def test_uvw_batched_backward_module_has_no_atomics_and_no_lane_shuffles():
