@@ -329,22 +329,36 @@ __global__ void __launch_bounds__(256) radial_scale_rows(int64_t E, int D, int R
 // With t[e] the gradient of channel r's convolution with respect to its scaled SH row:
 // gy[e] (+)= rho[e][r] t[e] (the chain rule through ys = rho y; `acc` 0 writes), grho[e][r] =
 // sum_j y[e][j] t[e][j] (j ascending), then t[e] = 0 for the next channel's accumulation.
+// A workgroup takes 64 consecutive edges: their rows of t and y are contiguous (64 D values), so
+// they are staged through LDS with consecutive threads on consecutive words, and the per-edge dot
+// products read them from there.
 template <typename T>
 __global__ void __launch_bounds__(256) radial_fold_rows(int64_t E, int D, int R, int r, const T *__restrict__ y,
                                                         const T *__restrict__ rho, T *__restrict__ t,
                                                         T *__restrict__ gy, T *__restrict__ grho, int acc)
 {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= E) return;
-    const T s = rho[e * R + r];
-    T d = 0;
-    for (int j = 0; j < D; ++j) {
-        const T v = t[e * D + j];
-        if (gy) gy[e * D + j] = acc ? gy[e * D + j] + s * v : s * v;
-        d += y[e * D + j] * v;
-        t[e * D + j] = 0;
+    extern __shared__ __align__(16) unsigned char fold_lds[];
+    T *ts = reinterpret_cast<T *>(fold_lds);  // [64 * D]
+    T *yl = ts + 64 * D;                       // [64 * D]
+    const int64_t e0 = (int64_t)blockIdx.x * 64;
+    const int ne = (int)(E - e0 < 64 ? E - e0 : 64);
+    const int n = ne * D;
+    const int64_t base = e0 * D;
+    for (int i = threadIdx.x; i < n; i += 256) {
+        ts[i] = t[base + i];
+        yl[i] = y[base + i];
     }
-    if (grho) grho[e * R + r] = d;
+    __syncthreads();
+    if (grho && (int)threadIdx.x < ne) {
+        T d = 0;
+        for (int j = 0; j < D; ++j) d += yl[threadIdx.x * D + j] * ts[threadIdx.x * D + j];
+        grho[(e0 + threadIdx.x) * R + r] = d;
+    }
+    for (int i = threadIdx.x; i < n; i += 256) {
+        const T s = rho[(e0 + i / D) * R + r];
+        if (gy) gy[base + i] = acc ? gy[base + i] + s * ts[i] : s * ts[i];
+        t[base + i] = 0;
+    }
 }
 
 hipError_t launch_radial_scale(bool f64, int64_t E, int D, int R, int r, const void *y, const void *rho, void *ys,
@@ -366,12 +380,14 @@ hipError_t launch_radial_fold(bool f64, int64_t E, int D, int R, int r, const vo
                               void *gy, void *grho, int acc, hipStream_t st)
 {
     if (E == 0) return hipSuccess;
-    const dim3 grid((unsigned)((E + 255) / 256));
+    if (D < 1 || D > 64) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((E + 63) / 64));
+    const size_t lds = 2 * 64 * (size_t)D * (f64 ? 8 : 4);  // at most 64 KB
     if (f64)
-        hipLaunchKernelGGL(radial_fold_rows<double>, grid, dim3(256), 0, st, E, D, R, r, (const double *)y,
+        hipLaunchKernelGGL(radial_fold_rows<double>, grid, dim3(256), lds, st, E, D, R, r, (const double *)y,
                            (const double *)rho, (double *)t, (double *)gy, (double *)grho, acc);
     else
-        hipLaunchKernelGGL(radial_fold_rows<float>, grid, dim3(256), 0, st, E, D, R, r, (const float *)y,
+        hipLaunchKernelGGL(radial_fold_rows<float>, grid, dim3(256), lds, st, E, D, R, r, (const float *)y,
                            (const float *)rho, (float *)t, (float *)gy, (float *)grho, acc);
     return hipGetLastError();
 }
