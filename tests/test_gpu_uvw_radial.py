@@ -149,3 +149,57 @@ def test_uvw_radial_one_hot_is_shared_weight_convolution(device):
     assert rel_l2(gx, sx.cpu().numpy()) <= 1e-6 and rel_l2(gy, sy.cpu().numpy()) <= 1e-6
     assert np.all(gth[[0, 1, 3]] == 0) and rel_l2(gth[2], sw.cpu().numpy()) <= 1e-6
     assert rel_l2(grho, oracle_bwd(c)[2]) <= TOL["f32"]
+
+
+def test_uvw_radial_full_nequip_size_sampled(device):
+    """The bench configuration (N = 5,000, E = 200,000, 32x(0e,1o,2e) into 32x(0e,1o,2e,1e,2o),
+    R = 8, fp32, heavy-first schedule): the output on sampled receivers, dY and drho on their
+    edges and dx on sampled senders against the oracle on those pieces; dTheta, whose oracle would
+    form all 200,000 x 15,360 weights, through the adjoint identity <dTheta, V> = <g, conv(x, y,
+    rho V)> with the library's own forward."""
+    import torch
+    spec = synth.EXTRA_WORKLOADS["c2uvw"]
+    R = 8
+    prob = oirreps.build_problem(spec.in_irreps, oirreps.sh_irreps(spec.lmax_sh), spec.out_irreps, "uvw")
+    row_ptr, col = synth.conv_graph(spec, 0)
+    N, E = len(row_ptr) - 1, len(col)
+    st, up = synth.streams(71), synth.upstream_streams(71)
+    f32 = np.float32
+    c = {"row_ptr": row_ptr, "col": col,
+         "x": synth.normal(st["x"], (N, prob.d_in), dtype=f32), "y": synth.normal(st["vec"], (E, prob.d_sh), dtype=f32),
+         "rho": synth.normal(up["gg_y"], (E, R), dtype=f32),
+         "theta": synth.normal(st["w"], (R, prob.weight_numel), 1.0 / np.sqrt(R * E / N), dtype=f32),
+         "g": synth.normal(st["sample"], (N, prob.d_out), dtype=f32)}
+    print(f"[uvw radial] full NequIP size N={N} E={E} R={R}", flush=True)
+    t = to_gpu(c, device)
+    plan = cg.Plan(spec.in_irreps, cg.sh_irreps(spec.lmax_sh), spec.out_irreps, "uvw", "f32")
+    order = cg.graph_order(t["row_ptr"])
+    out = cg.conv_forward_radial(plan, t["row_ptr"], t["col"], t["x"], t["y"], t["rho"], t["theta"], order=order)
+    tr = cg.graph_transpose(t["row_ptr"], t["col"])
+    gx, gy, grho, gth = cg.conv_backward_radial(plan, t["row_ptr"], t["col"], tr, t["x"], t["y"], t["rho"],
+                                                t["theta"], t["g"])
+    v = torch.from_numpy(synth.normal(up["gg_w"], (R, prob.weight_numel), dtype=f32)).to(device)
+    out_v = cg.conv_forward_radial(plan, t["row_ptr"], t["col"], t["x"], t["y"], t["rho"], v, order=order)
+    torch.cuda.synchronize()
+    out, gx, gy, grho, gth = (a.cpu().numpy() for a in (out, gx, gy, grho, gth))
+    rng = np.random.default_rng(5)
+    recv = np.sort(rng.choice(N, 12, replace=False))
+    edges = np.concatenate([np.arange(row_ptr[n], row_ptr[n + 1]) for n in recv])
+    sub_ptr = np.concatenate([[0], np.cumsum(np.diff(row_ptr)[recv])])
+    pieces = [c[k].astype(np.float64) for k in ("x", "y", "rho", "theta", "g")]
+    x64, y64, rho64, th64, g64 = pieces
+    want = ref.conv_forward_radial(prob, sub_ptr, col[edges], x64, y64[edges], rho64[edges], th64)
+    assert rel_l2(out[recv], want) <= TOL["f32"]
+    _, dy, drho, _ = ref.conv_backward_radial(prob, sub_ptr, col[edges], x64, y64[edges], rho64[edges], th64,
+                                              g64[recv])
+    assert rel_l2(gy[edges], dy) <= TOL["f32"] and rel_l2(grho[edges], drho) <= TOL["f32"]
+    senders = rng.choice(np.unique(col), 6, replace=False)
+    recv_of = ref.receivers_of(row_ptr)
+    for s in senders:
+        es = np.nonzero(col == s)[0]
+        dxs, _, _ = ref.edge_backward_uvw(prob, np.repeat(x64[s][None], len(es), 0), y64[es], rho64[es] @ th64,
+                                          g64[recv_of[es]])
+        assert rel_l2(gx[s], dxs.sum(axis=0)) <= TOL["f32"]
+    lhs = float(np.sum(gth.astype(np.float64) * v.cpu().numpy()))
+    rhs = float(np.sum(g64 * out_v.cpu().numpy().astype(np.float64)))
+    assert abs(lhs - rhs) <= 1e-4 * max(abs(rhs), 1.0)
