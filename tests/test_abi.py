@@ -339,6 +339,13 @@ def test_uvw_convolution_rejects_paths_beyond_workgroup_lds(irreps, dtype, tmp_p
                               ctypes.c_size_t(1 << 30), s) == unsup
     with pytest.raises(cg.CgtpError, match="CGTP_ERR_UNSUPPORTED"):
         plan.conv_uvw_backward_source(0)
+    # the uvw radial projection runs on the same convolution kernels: refused the same way
+    assert L.cgtp_conv_forward_radial(plan.handle, 4, 4, fake, fake, null, fake, fake, 2, fake, fake, fake, s) == unsup
+    assert "LDS" in cg.last_error()
+    assert L.cgtp_conv_backward_radial(plan.handle, 4, 4, fake, fake, fake, fake, fake, fake, fake, 2, fake, fake,
+                                       fake, fake, fake, fake, fake, fake, ctypes.c_size_t(1 << 30), s) == unsup
+    with pytest.raises(cg.CgtpError, match="CGTP_ERR_UNSUPPORTED"):
+        plan.radial_source(2)
     plan.close()
 
 
